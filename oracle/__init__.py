@@ -1,0 +1,228 @@
+"""fp64 CPU oracle for causal linear attention -- TEST INFRASTRUCTURE ONLY.
+
+Only `tests/`, `__graft_entry__.smoke()` and the CPU-baseline leg of
+`bench.py` may import this package.  It shares no code with the HIP library
+under `chunkwise_recurrence_amd/` and never imports it.
+
+Three independent ways to compute the same thing, each in float64:
+
+* `recurrent`   -- the plain definition, token by token (C, `la_oracle.c`).
+  This is THE oracle the GPU is compared with.
+* `parallel`    -- the fully parallel masked form Y = ((Q K^T) o D) V with
+  D[t,s] = prod_{r=s+1..t} a_r for s <= t and 0 above the diagonal
+  (CS336 lecture 4 code 1, `causal_linear_attention_parallel` and
+  `gated_linear_attention_parallel`, whose derivation expands the recurrence
+  into exactly this sum).  Here D is built from explicit products, not from
+  the log-space cumsum, so that it is a different computation path.
+* `chunkwise`   -- the chunkwise form: per chunk, inter = diag(e^b) Q_c S_c,
+  intra = ((Q_c K_c^T) o D_c) V_c, S_{c+1} = e^{b_last} S_c +
+  (diag(e^{b_last - b}) K_c)^T V_c, with b the in-chunk inclusive cumsum of
+  log a ("Linear / Sparse Attention" `linear_attn_chunkwise` for the
+  undecayed skeleton; tutorial section 6.2 says decayed variants fold the
+  cumulative decay into S_c and the in-chunk mask; the decayed formulas are
+  obtained by expanding the recurrence over one chunk).
+
+`parallel` and `chunkwise` exist to pin `recurrent` (they are never compared
+with the GPU).  All three take the decay as a per-token multiplier array
+`a` [.., L] produced by `decay_multipliers`, which turns the library's decay
+parameters into a_t exactly as the pages define them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+PHI_IDENTITY = 0
+PHI_ELU1 = 1
+DECAY_NONE = 0
+DECAY_HEAD = 1
+DECAY_LOG = 2
+DECAY_GATE = 3
+
+_libs: dict = {}
+
+
+def _load(path: str | None = None):
+    path = LIB_PATH if path is None else path
+    if path not in _libs:
+        if path == LIB_PATH and not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(path)
+        d = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_recurrent.restype = ctypes.c_int
+        lib.oracle_recurrent.argtypes = [ctypes.c_int] * 5 + [d, d, d, ctypes.c_int, ctypes.c_int,
+                                                             d, d, d, ctypes.c_int]
+        _libs[path] = lib
+    return _libs[path]
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def host_threads() -> int:
+    """Host cores available to this process (sched_getaffinity)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# --------------------------------------------------------------------------
+# the oracle proper
+# --------------------------------------------------------------------------
+def recurrent(q, k, v, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, decay=None,
+              state=None, nthreads: int | None = None, lib_path: str | None = None):
+    """Token-by-token fp64 recurrence (`la_oracle.c`).
+
+    q, k: [B,H,L,dk]; v: [B,H,L,dv]; decay: None | gamma[H] | log_a or g [B,H,L];
+    state: [B,H,dk,dv] initial state (zeros if None).
+    lib_path: another build of `la_oracle.c` to run instead of the default one
+    (the tests use it to check that deliberately broken copies get caught).
+    Returns (out [B,H,L,dv], final state [B,H,dk,dv]) as float64 arrays.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, H, L, dk) and v.shape == (B, H, L, dv)
+    S = np.zeros((B, H, dk, dv)) if state is None else _f64(state).copy()
+    assert S.shape == (B, H, dk, dv)
+    out = np.zeros((B, H, L, dv))
+    if decay_kind == DECAY_NONE:
+        dec = np.zeros(1)
+    elif decay_kind == DECAY_HEAD:
+        dec = _f64(decay).reshape(H)
+    else:
+        dec = _f64(decay).reshape(B, H, L)
+    if B * H == 0 or L == 0:
+        return out, S
+    n = host_threads() if nthreads is None else nthreads
+    _load(lib_path).oracle_recurrent(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), phi,
+                                     decay_kind, _ptr(dec), _ptr(S), _ptr(out), n)
+    return out, S
+
+
+def decode_step(q, k, v, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, decay=None,
+                state=None, lib_path: str | None = None):
+    """One recurrent step for N sequences x H heads: the same definition with L = 1.
+
+    q, k: [N,H,dk]; v: [N,H,dv]; decay: None | gamma[H] | [N,H]; state [N,H,dk,dv].
+    Returns (o [N,H,dv], new state).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, H, _ = q.shape
+    dec = decay
+    if decay_kind in (DECAY_LOG, DECAY_GATE):
+        dec = _f64(decay).reshape(N, H, 1)
+    o, S = recurrent(q[:, :, None, :], k[:, :, None, :], v[:, :, None, :], phi, decay_kind,
+                     dec, state, lib_path=lib_path)
+    return o[:, :, 0, :], S
+
+
+# --------------------------------------------------------------------------
+# helpers shared by the two pinning forms below (not used by `recurrent`)
+# --------------------------------------------------------------------------
+def feature_map(x, phi: int) -> np.ndarray:
+    """phi(x) = elu(x) + 1 (alpha = 1) or the identity, in fp64."""
+    x = _f64(x)
+    if phi == PHI_ELU1:
+        return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+    return x
+
+
+def decay_multipliers(B: int, H: int, L: int, decay_kind: int, decay) -> np.ndarray:
+    """a_t for every (b, h, t) as fp64 [B,H,L] (1 for no decay)."""
+    if decay_kind == DECAY_NONE:
+        return np.ones((B, H, L))
+    if decay_kind == DECAY_HEAD:
+        g = _f64(decay).reshape(1, H, 1)
+        return np.broadcast_to(g, (B, H, L)).copy()
+    x = _f64(decay).reshape(B, H, L)
+    if decay_kind == DECAY_LOG:
+        return np.exp(x)
+    # exp(-softplus(g)) = 1 / (1 + e^g), evaluated without overflow
+    return np.exp(-(np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))))
+
+
+def parallel(q, k, v, a, phi: int = PHI_IDENTITY, state=None):
+    """Fully parallel masked form, one [L,L] product per head (O(L^2)).
+
+    o_t = sum_{s<=t} D[t,s] (phi(q_t).phi(k_s)) v_s + (prod_{r<=t} a_r) phi(q_t)^T S_0,
+    D[t,s] = prod_{r=s+1..t} a_r (an explicit running product, no logs).
+    Returns (out, final state) with S_L = sum_s D[L-1,s] phi(k_s) v_s^T + prod(a) S_0.
+    """
+    fq, fk, v, a = feature_map(q, phi), feature_map(k, phi), _f64(v), _f64(a)
+    B, H, L, dk = fq.shape
+    dv = v.shape[-1]
+    S0 = np.zeros((B, H, dk, dv)) if state is None else _f64(state)
+    out = np.zeros((B, H, L, dv))
+    SL = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            D = np.zeros((L, L))
+            for s in range(L):
+                p = 1.0
+                D[s, s] = 1.0
+                for t in range(s + 1, L):
+                    p *= a[b, h, t]
+                    D[t, s] = p
+            head = np.cumprod(a[b, h])  # prod_{r<=t} a_r: decay of S_0 seen at token t
+            scores = fq[b, h] @ fk[b, h].T
+            out[b, h] = (scores * D) @ v[b, h] + head[:, None] * (fq[b, h] @ S0[b, h])
+            if L:
+                SL[b, h] = (fk[b, h] * D[L - 1][:, None]).T @ v[b, h] + head[-1] * S0[b, h]
+            else:
+                SL[b, h] = S0[b, h]
+    return out, SL
+
+
+def chunkwise(q, k, v, a, C: int, phi: int = PHI_IDENTITY, state=None, dtype=np.float64):
+    """Chunkwise form with decay folded in (log-space, every factor exp(<= 0)).
+
+    Per chunk of c <= C tokens with b = inclusive cumsum of log a inside the chunk:
+      O_c     = diag(e^b) Q_c S_c + ((Q_c K_c^T) o D_c) V_c,  D_c[i,j] = e^{b_i - b_j} [j <= i]
+      S_{c+1} = e^{b_last} S_c + (diag(e^{b_last - b}) K_c)^T V_c
+    A ragged last chunk simply has c < C rows.
+    `dtype` is the working precision (float64 by default; float32 reproduces
+    the magnitude of rounding error the pages print for their fp32 run).
+    """
+    fq, fk = feature_map(q, phi).astype(dtype), feature_map(k, phi).astype(dtype)
+    v, a = _f64(v).astype(dtype), _f64(a)
+    B, H, L, dk = fq.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv), dtype) if state is None else _f64(state).astype(dtype)
+    out = np.zeros((B, H, L, dv), dtype)
+    with np.errstate(divide="ignore"):
+        la = np.log(a)
+    for b in range(B):
+        for h in range(H):
+            Sh = S[b, h]
+            for s in range(0, L, C):
+                e = min(s + C, L)
+                Qc, Kc, Vc = fq[b, h, s:e], fk[b, h, s:e], v[b, h, s:e]
+                bc = np.cumsum(la[b, h, s:e]).astype(dtype)
+                diff = bc[:, None] - bc[None, :]
+                mask = np.tril(np.ones((e - s, e - s), dtype=bool))
+                Dc = np.where(mask, np.exp(np.where(mask, diff, 0.0)), 0.0).astype(dtype)
+                out[b, h, s:e] = np.exp(bc)[:, None] * (Qc @ Sh) + ((Qc @ Kc.T) * Dc) @ Vc
+                Sh = np.exp(bc[-1]) * Sh + (Kc * np.exp(bc[-1] - bc)[:, None]).T @ Vc
+            S[b, h] = Sh
+    return out, S
+
+
+def rel_err(x, ref) -> float:
+    """max|x - ref| / max|ref| (the pages' 'max relative difference')."""
+    x, ref = _f64(x), _f64(ref)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    num = np.max(np.abs(x - ref)) if ref.size else 0.0
+    return float(num / den) if den > 0 else float(num)
