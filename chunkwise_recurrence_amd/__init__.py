@@ -1,0 +1,13 @@
+"""Chunkwise causal linear attention on AMD MI355X (gfx950).
+
+The compute lives in `liblinattn.so` (hand-written HIP kernels behind a C
+ABI, declared in include/la.h).  This package is a thin ctypes binding over
+it: every function marshals torch tensors into device pointers and a stream,
+and the library does all of the work on the GPU.  There is no CPU fallback:
+if the library cannot be loaded, calls raise.
+"""
+from .binding import (  # noqa: F401
+    DECAY_GATE, DECAY_HEAD, DECAY_LOG, DECAY_NONE, PHI_ELU1, PHI_IDENTITY, LAError,
+    EXPORTS, LA_BF16, LA_F32, chunk_fwd, chunk_fwd_workspace_bytes, decode_step, lib_path, load,
+    plan, set_plan, state_init, status_string,
+)

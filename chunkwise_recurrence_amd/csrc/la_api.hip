@@ -1,0 +1,221 @@
+// la_api.hip -- the C ABI of liblinattn.so (declared in include/la.h):
+// argument validation on the host, the launch plan, and the launches.
+//
+// Validation happens before any HIP call, so every error path can be
+// exercised on a machine without a GPU.
+#include <atomic>
+#include <stdint.h>
+
+#include "../../include/la.h"
+#include "la_internal.h"
+
+namespace {
+
+// Workgroups the bf16 plan aims for: one per compute unit of an MI355X.
+constexpr int kTargetWorkgroups = 256;
+// A segment of the sequence keeps at least this many chunks.
+constexpr int kMinSegmentChunks = 4;
+
+std::atomic<int> g_plan_tv{0};
+std::atomic<int> g_plan_segments{0};
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+struct Plan {
+  int tv = 0;        // value-tile width of one workgroup (bf16 path)
+  int P = 1;         // sequence segments per head
+  int seg_chunks = 0;
+  size_t ws_bytes = 0;
+  size_t ws_S_off = 0, ws_logA_off = 0;
+};
+
+la_status check_chunk_shape(int dtype, int B, int H, int L, int d_k, int d_v, int C) {
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || L < 0 || C < 1) return LA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v) || !dim_ok(C)) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
+  Plan p;
+  const int heads = B * H;
+  const int nchunks = L > 0 ? (L + C - 1) / C : 0;
+  if (dtype == LA_F32) {
+    p.tv = d_v < 32 ? d_v : 32;
+    p.P = 1;
+    p.seg_chunks = nchunks;
+    return p;
+  }
+  // value tile: the widest that still gives enough workgroups, not below 32
+  int tv = d_v;
+  while ((long long)heads * (d_v / tv) < kTargetWorkgroups && tv > 32) tv /= 2;
+  const int forced_tv = g_plan_tv.load();
+  if (forced_tv > 0) {
+    tv = forced_tv;
+    while (tv > d_v) tv /= 2;
+  }
+  while (tv > 16 && !la::chunk_bf16_supported(d_k, tv, C)) tv /= 2;
+  p.tv = tv;
+  // sequence segments: split further only while workgroups are short and every
+  // segment keeps a few chunks
+  int P = 1;
+  const long long units = (long long)heads * (d_v / tv);
+  while (units * P < kTargetWorkgroups && (long long)P * 2 * kMinSegmentChunks <= nchunks) P *= 2;
+  const int forced_P = g_plan_segments.load();
+  if (forced_P > 0) P = forced_P;
+  if (P > nchunks) P = nchunks;
+  if (P < 1) P = 1;
+  p.seg_chunks = nchunks > 0 ? (nchunks + P - 1) / P : 0;
+  p.P = p.seg_chunks > 0 ? (nchunks + p.seg_chunks - 1) / p.seg_chunks : 1;
+  if (p.P > 1) {
+    const size_t s_bytes = (size_t)heads * p.P * d_k * d_v * sizeof(float);
+    const size_t a_bytes = (size_t)heads * p.P * sizeof(float);
+    p.ws_S_off = 0;
+    p.ws_logA_off = (s_bytes + 255) & ~(size_t)255;
+    p.ws_bytes = p.ws_logA_off + ((a_bytes + 255) & ~(size_t)255);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_string(int s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_NULL: return "LA_ERR_NULL: a required pointer is NULL";
+    case LA_ERR_SHAPE: return "LA_ERR_SHAPE: B, H or N < 1, L < 0 or C < 1";
+    case LA_ERR_UNSUPPORTED:
+      return "LA_ERR_UNSUPPORTED: d_k, d_v or C not in {16,32,64,128}, or an unknown dtype/phi/decay";
+    case LA_ERR_ALIGN: return "LA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
+    case LA_ERR_DEVICE: return "LA_ERR_DEVICE: a HIP call or kernel launch failed";
+  }
+  return "unknown la_status";
+}
+
+la_status la_set_plan(int dv_tile, int segments) {
+  if (dv_tile != 0 && !dim_ok(dv_tile)) return LA_ERR_UNSUPPORTED;
+  if (segments < 0) return LA_ERR_SHAPE;
+  g_plan_tv.store(dv_tile);
+  g_plan_segments.store(segments);
+  return LA_OK;
+}
+
+la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int* dv_tile,
+                            int* segments) {
+  const la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
+  if (st != LA_OK) return st;
+  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype);
+  if (dv_tile) *dv_tile = p.tv;
+  if (segments) *segments = p.P;
+  return LA_OK;
+}
+
+size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
+  if (check_chunk_shape(dtype, B, H, L, d_k, d_v, C) != LA_OK || L == 0) return 0;
+  return make_plan(B, H, L, d_k, d_v, C, dtype).ws_bytes;
+}
+
+la_status la_state_init(float* state, int B, int H, int d_k, int d_v, void* stream) {
+  if (B < 1 || H < 1) return LA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return LA_ERR_UNSUPPORTED;
+  if (!state) return LA_ERR_NULL;
+  if (!aligned(state, 16)) return LA_ERR_ALIGN;
+  const size_t n = (size_t)B * H * d_k * d_v;
+  return la::launch_fill_zero(state, n, as_stream(stream)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+}
+
+la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                       int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                       const float* decay_data, float* state, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
+  if (st != LA_OK) return st;
+  if (phi != LA_PHI_IDENTITY && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return LA_ERR_UNSUPPORTED;
+  if (L == 0) return LA_OK;
+  if (!q || !k || !v || !out) return LA_ERR_NULL;
+  if (decay_kind != LA_DECAY_NONE && !decay_data) return LA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      (state && !aligned(state, 16)) || (decay_data && !aligned(decay_data, 4)))
+    return LA_ERR_ALIGN;
+  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype);
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return LA_ERR_ALIGN;
+  }
+
+  la::ChunkArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.state = state;
+  a.decay = decay_kind == LA_DECAY_NONE ? nullptr : decay_data;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.DK = d_k;
+  a.DV = d_v;
+  a.C = C;
+  a.phi = phi;
+  a.decay_kind = decay_kind;
+  a.tv = p.tv;
+  a.n_v = d_v / p.tv;
+  a.P = p.P;
+  a.seg_chunks = p.seg_chunks;
+  const hipStream_t s = as_stream(stream);
+
+  hipError_t e;
+  if (dtype == LA_F32) {
+    a.n_units = B * H;
+    e = la::launch_chunk_f32(a, s);
+  } else {
+    if (p.P > 1) {
+      char* ws = static_cast<char*>(workspace);
+      a.ws_S = reinterpret_cast<float*>(ws + p.ws_S_off);
+      a.ws_logA = reinterpret_cast<float*>(ws + p.ws_logA_off);
+      a.n_units = B * H * (p.P - 1);
+      e = la::launch_chunk_bf16(a, /*state_only=*/true, s);
+      if (e != hipSuccess) return LA_ERR_DEVICE;
+    }
+    a.n_units = B * H * p.P;
+    e = la::launch_chunk_bf16(a, /*state_only=*/false, s);
+  }
+  return e == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+}
+
+la_status la_decode_step(const void* q, const void* k, const void* v, int dtype, int N, int H,
+                         int d_k, int d_v, int phi, int decay_kind, const float* decay_data,
+                         float* state, void* out, void* stream) {
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (N < 1 || H < 1) return LA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return LA_ERR_UNSUPPORTED;
+  if (phi != LA_PHI_IDENTITY && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return LA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !state || !out) return LA_ERR_NULL;
+  if (decay_kind != LA_DECAY_NONE && !decay_data) return LA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(state, 16) || (decay_data && !aligned(decay_data, 4)))
+    return LA_ERR_ALIGN;
+  la::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.state = state;
+  a.decay = decay_kind == LA_DECAY_NONE ? nullptr : decay_data;
+  a.N = N;
+  a.H = H;
+  a.DK = d_k;
+  a.DV = d_v;
+  a.phi = phi;
+  a.decay_kind = decay_kind;
+  return la::launch_decode(a, dtype, as_stream(stream)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+}
+
+}  // extern "C"

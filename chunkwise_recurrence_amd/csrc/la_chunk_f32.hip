@@ -1,0 +1,117 @@
+// la_chunk_f32.hip -- chunkwise causal linear attention with fp32 inputs and
+// fp32 arithmetic throughout (no bf16 rounding anywhere).
+//
+// Same chunkwise form as the bf16 kernel (per chunk: inter-chunk term
+// diag(e^b) Q_c S_c, intra-chunk term ((Q_c K_c^T) o D_c) V_c, then
+// S <- e^{b_last} S + (diag(e^{b_last - b}) K_c)^T V_c), written for
+// exactness rather than speed: plain fp32 FMA, the decayed score block and the
+// state tile in LDS, q and k read through the caches with phi applied on the
+// fly.  One workgroup per (head, 32-column value tile), chunks in sequence.
+// It serves small fp32 problems such as the 300 x 16 demo.
+#include "la_device.h"
+
+namespace la {
+namespace {
+
+constexpr int kTileF32 = 32;   // value columns per workgroup
+constexpr int kMaxC = 128;
+
+__device__ __forceinline__ float phi_f32(bool elu, float x) {
+  return elu ? feature_elu1_accurate(x) : x;
+}
+
+__global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / a.n_v, vt = blockIdx.x % a.n_v;
+  const int h = bh % a.H;
+  const int L = a.L, DK = a.DK, DV = a.DV, C = a.C;
+  const int tv = min(kTileF32, DV);
+  const int dv0 = vt * tv;
+  const bool elu = a.phi == kPhiElu1;
+  const int kind = a.decay_kind;
+
+  __shared__ float sP[kMaxC * kMaxC];
+  __shared__ float sS[128 * kTileF32];
+  __shared__ float sB[kMaxC];
+
+  const float* qh = static_cast<const float*>(a.q) + (size_t)bh * L * DK;
+  const float* kh = static_cast<const float*>(a.k) + (size_t)bh * L * DK;
+  const float* vh = static_cast<const float*>(a.v) + (size_t)bh * L * DV + dv0;
+  float* oh = static_cast<float*>(a.out) + (size_t)bh * L * DV + dv0;
+  const float* dtok = (kind == kDecayLog || kind == kDecayGate) ? a.decay + (size_t)bh * L : nullptr;
+  const float lg = (kind == kDecayHead) ? logf(a.decay[h]) : 0.0f;
+
+  for (int i = tid; i < DK * tv; i += 256) {
+    const int d = i / tv, v = i % tv;
+    sS[i] = a.state ? a.state[((size_t)bh * DK + d) * DV + dv0 + v] : 0.0f;
+  }
+
+  for (int t0 = 0; t0 < L; t0 += C) {
+    const int n = min(C, L - t0);
+    __syncthreads();  // previous chunk's readers of sB / sP are done
+    if (tid == 0) {
+      float b = 0.0f;
+      for (int i = 0; i < n; ++i) {
+        if (kind == kDecayHead) b += lg;
+        else if (dtok) b += token_log_decay(kind, dtok[t0 + i]);
+        sB[i] = b;
+      }
+    }
+    __syncthreads();
+    const float bL = sB[n - 1];
+    // decayed scores P[i][j] = (phi(q_i).phi(k_j)) e^{b_i - b_j}, j <= i
+    for (int idx = tid; idx < n * n; idx += 256) {
+      const int i = idx / n, j = idx % n;
+      float p = 0.0f;
+      if (j <= i) {
+        const float* qi = qh + (size_t)(t0 + i) * DK;
+        const float* kj = kh + (size_t)(t0 + j) * DK;
+        for (int d = 0; d < DK; ++d) p = fmaf(phi_f32(elu, qi[d]), phi_f32(elu, kj[d]), p);
+        p *= expf(sB[i] - sB[j]);
+      }
+      sP[i * kMaxC + j] = p;
+    }
+    __syncthreads();
+    // o_i = e^{b_i} phi(q_i)^T S + sum_{j<=i} P[i][j] v_j
+    for (int idx = tid; idx < n * tv; idx += 256) {
+      const int i = idx / tv, v = idx % tv;
+      const float* qi = qh + (size_t)(t0 + i) * DK;
+      float inter = 0.0f;
+      for (int d = 0; d < DK; ++d) inter = fmaf(phi_f32(elu, qi[d]), sS[d * tv + v], inter);
+      float intra = 0.0f;
+      for (int j = 0; j <= i; ++j) intra = fmaf(sP[i * kMaxC + j], vh[(size_t)(t0 + j) * DV + v], intra);
+      oh[(size_t)(t0 + i) * DV + v] = expf(sB[i]) * inter + intra;
+    }
+    __syncthreads();
+    // S <- e^{b_last} S + sum_j e^{b_last - b_j} phi(k_j) v_j^T
+    for (int idx = tid; idx < DK * tv; idx += 256) {
+      const int d = idx / tv, v = idx % tv;
+      float acc = 0.0f;
+      for (int j = 0; j < n; ++j)
+        acc = fmaf(expf(bL - sB[j]) * phi_f32(elu, kh[(size_t)(t0 + j) * DK + d]),
+                   vh[(size_t)(t0 + j) * DV + v], acc);
+      sS[idx] = expf(bL) * sS[idx] + acc;
+    }
+  }
+  __syncthreads();
+  if (a.state) {
+    for (int i = tid; i < DK * tv; i += 256) {
+      const int d = i / tv, v = i % tv;
+      a.state[((size_t)bh * DK + d) * DV + dv0 + v] = sS[i];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t s) {
+  ChunkArgs b = a;
+  const int tv = a.DV < kTileF32 ? a.DV : kTileF32;
+  b.n_v = a.DV / tv;
+  b.tv = tv;
+  const dim3 grid(a.B * a.H * b.n_v), block(256);
+  hipLaunchKernelGGL(chunk_f32_kernel, grid, block, 0, s, b);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,54 @@
+// la_device.h -- small device helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "la_internal.h"
+
+namespace la {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// phi(x) = elu(x) + 1 (alpha = 1): x + 1 for x > 0, e^x otherwise.
+__device__ __forceinline__ float feature_elu1(float x) {
+  return x > 0.0f ? x + 1.0f : __expf(x);
+}
+
+__device__ __forceinline__ float feature_elu1_accurate(float x) {
+  return x > 0.0f ? x + 1.0f : expf(x);
+}
+
+// log a_t for the token-dependent decay kinds (0 for none).
+//   log:  the value itself;  gate: -softplus(g) = -(max(g,0) + log1p(e^-|g|)).
+__device__ __forceinline__ float token_log_decay(int kind, float x) {
+  if (kind == kDecayLog) return x;
+  if (kind == kDecayGate) return -(fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
+  return 0.0f;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+}  // namespace la

@@ -1,0 +1,54 @@
+// la_internal.h -- launch descriptors shared by the host API (la_api.hip) and
+// the kernel files.  Not part of the public ABI (that is include/la.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace la {
+
+// Public enum values, mirrored for device code.
+enum { kF32 = 0, kBF16 = 1 };
+enum { kPhiIdentity = 0, kPhiElu1 = 1 };
+enum { kDecayNone = 0, kDecayHead = 1, kDecayLog = 2, kDecayGate = 3 };
+
+// One la_chunk_fwd launch (main pass or segment-state pass).
+struct ChunkArgs {
+  const void* q;        // [B,H,L,DK]
+  const void* k;        // [B,H,L,DK]
+  const void* v;        // [B,H,L,DV]
+  void* out;            // [B,H,L,DV]
+  float* state;         // [B,H,DK,DV] or nullptr
+  const float* decay;   // nullptr | gamma[H] | [B,H,L]
+  float* ws_S;          // [B*H, P, DK, DV] per-segment state increments
+  float* ws_logA;       // [B*H, P] per-segment total log decay
+  int B, H, L, DK, DV, C;
+  int P;                // sequence segments per head
+  int seg_chunks;       // chunks per segment (the last one may hold fewer)
+  int n_units;          // work units: B*H*P (main) or B*H*(P-1) (state pass)
+  int n_v;              // d_v tiles per head
+  int tv;               // d_v tile width
+  int phi, decay_kind;
+};
+
+struct DecodeArgs {
+  const void* q;        // [N,H,DK]
+  const void* k;        // [N,H,DK]
+  const void* v;        // [N,H,DV]
+  void* out;            // [N,H,DV]
+  float* state;         // [N,H,DK,DV]
+  const float* decay;   // nullptr | gamma[H] | [N,H]
+  int N, H, DK, DV;
+  int phi, decay_kind;
+};
+
+// Launchers (return the launch error, hipSuccess when enqueued).
+hipError_t launch_chunk_bf16(const ChunkArgs& a, bool state_only, hipStream_t s);
+hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
+
+// Whether a bf16 (DK, TV, C) combination has a compiled kernel.
+bool chunk_bf16_supported(int DK, int TV, int C);
+
+}  // namespace la

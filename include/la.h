@@ -1,0 +1,161 @@
+/*
+ * la.h -- C ABI of liblinattn.so: chunkwise causal linear attention on
+ * AMD MI355X (gfx950).
+ *
+ * The operation (one head; every head of a [B, H] batch is independent):
+ *
+ *   S_t = a_t S_{t-1} + phi(k_t) v_t^T        S is d_k x d_v (rows = key dim)
+ *   o_t = phi(q_t)^T S_t                      read after the write
+ *
+ * - The state, the outer-product write k v^T and the update-then-read order
+ *   follow "Linear / Sparse Attention - minimal runnable implementation"
+ *   (linear_attn_recurrent), whose chunkwise form (linear_attn_chunkwise) is
+ *   what la_chunk_fwd computes: per chunk of C tokens, an inter-chunk term
+ *   Q_c S_c, an intra-chunk term ((Q_c K_c^T) masked by tril incl. the
+ *   diagonal) V_c, then S_{c+1} = S_c + K_c^T V_c; the last chunk may be short.
+ * - The decay a_t follows CS336 lecture 4 code 1, section 4
+ *   (gated_linear_attention_recurrent): S_t = gamma_t S_{t-1} + k_t v_t^T with
+ *   gamma_t in (0, 1], constant per head (RetNet, tutorial section 2.4) or
+ *   token dependent; the gated kind uses a_t = exp(-softplus(g_t)), the
+ *   Mamba-style discretised decay exp(Delta A) with Delta = softplus(g) and
+ *   A = -1 (tutorial sections 3.3 and 4.2).  The tutorial's section 6.2 says
+ *   the chunkwise form folds the cumulative decay into S_c and the in-chunk
+ *   mask; the library does so in log space, so every factor is exp(<= 0).
+ * - phi is the identity or elu(x) + 1 with alpha = 1, applied to q and k,
+ *   never to v ("adv13 -- Linear Attention / SSM", sections 3.1-4.3).
+ * - No normaliser phi(q)^T z_t: this is the un-normalised form whose
+ *   recurrent == chunkwise equivalence the tutorial's section 6.2 states.
+ *
+ * Conventions for every entry point
+ * - Tensor pointers are DEVICE pointers (hipMalloc'd or torch tensors on the
+ *   GPU), contiguous, row-major, 16-byte aligned.  The caller owns and frees
+ *   all memory, including the workspace; the library allocates nothing.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *   and the call returns without synchronising.  Results are valid once the
+ *   caller has synchronised that stream.
+ * - Every argument is validated on the host before anything is launched, so
+ *   a call that returns an error has not touched device memory.  Values that
+ *   live on the device (decay parameters, NaN/Inf in inputs) are not
+ *   checked: NaN and Inf propagate.
+ * - Outputs must not alias inputs or the state (not checked).
+ * - Calls are thread-safe; calls that share output buffers must be ordered
+ *   by the caller.
+ */
+#ifndef LA_H_
+#define LA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  LA_ERR_SHAPE = 2,       /* B, H or N < 1, L < 0, C < 1                         */
+  LA_ERR_UNSUPPORTED = 3, /* d_k, d_v or C outside {16,32,64,128}; unknown enum  */
+  LA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                    */
+  LA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required            */
+  LA_ERR_DEVICE = 6       /* a HIP call or kernel launch failed                  */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1 } la_phi;
+
+typedef enum {
+  LA_DECAY_NONE = 0,       /* a_t = 1; decay_data ignored (may be NULL)          */
+  LA_DECAY_HEAD = 1,       /* a_t = gamma[h]; decay_data = float gamma[H], 0<gamma<=1 */
+  LA_DECAY_TOKEN_LOG = 2,  /* a_t = exp(log_a[b,h,t]); decay_data = float [B,H,L], <= 0 */
+  LA_DECAY_TOKEN_GATE = 3  /* a_t = exp(-softplus(g[b,h,t])); decay_data = float [B,H,L] */
+} la_decay_kind;
+
+/*
+ * la_state_init -- zero the recurrent state.
+ *   state : float [B, H, d_k, d_v], device, written.
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE (B or H < 1), LA_ERR_UNSUPPORTED (d_k, d_v),
+ *         LA_ERR_ALIGN, LA_ERR_DEVICE.
+ * A fill kernel (not hipMemsetAsync), so the call may be captured in a HIP graph.
+ */
+la_status la_state_init(float* state, int B, int H, int d_k, int d_v, void* stream);
+
+/*
+ * la_chunk_fwd_workspace_bytes -- bytes of device workspace la_chunk_fwd needs
+ * for this problem (0 when none is needed).  Pure host function; returns 0 for
+ * arguments la_chunk_fwd would reject.
+ */
+size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype);
+
+/*
+ * la_chunk_fwd -- the chunkwise-parallel forward over a whole sequence.
+ *
+ *   q, k       : [B, H, L, d_k], dtype          (device, read)
+ *   v          : [B, H, L, d_v], dtype          (device, read)
+ *   dtype      : LA_F32 (fp32 in, fp32 arithmetic throughout) or
+ *                LA_BF16 (bf16 in, bf16 matrix-core products, fp32 accumulation
+ *                and fp32 state)
+ *   C          : chunk size, one of 16, 32, 64, 128.  A performance knob only:
+ *                the result does not depend on C beyond rounding.  C >= L means
+ *                one chunk.  The requested C is honoured, never replaced.
+ *   phi        : la_phi
+ *   decay_kind : la_decay_kind; decay_data as described there (device, read)
+ *   state      : float [B, H, d_k, d_v] (device) or NULL.  In: S_0; out: S_L.
+ *                NULL means S_0 = 0 and the final state is dropped.
+ *   out        : [B, H, L, d_v], same dtype as q (device, written)
+ *   workspace  : device scratch of at least la_chunk_fwd_workspace_bytes(...)
+ *                bytes (may be NULL when that is 0); contents need no
+ *                initialisation and are garbage afterwards.
+ * L == 0 is a no-op that returns LA_OK (the state is left as is).
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN,
+ *         LA_ERR_WORKSPACE, LA_ERR_DEVICE.
+ */
+la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                       int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                       const float* decay_data, float* state, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * la_decode_step -- one recurrent token for N sequences x H heads, in place on
+ * the state (the recurrent form "linear_attn_recurrent" applied once; the
+ * state a prefill left behind is the S_{t-1} of the first step).
+ *
+ *   q, k       : [N, H, d_k], dtype     v : [N, H, d_v], dtype   (device, read)
+ *   decay_data : NULL | float gamma[H] | float [N, H] (this step's log a or g)
+ *   state      : float [N, H, d_k, d_v] (device, read and written; required)
+ *   out        : [N, H, d_v], same dtype as q (device, written)
+ * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN, LA_ERR_DEVICE.
+ */
+la_status la_decode_step(const void* q, const void* k, const void* v, int dtype, int N, int H,
+                         int d_k, int d_v, int phi, int decay_kind, const float* decay_data,
+                         float* state, void* out, void* stream);
+
+/* la_status_string -- a static, human-readable name for a status code. */
+const char* la_status_string(int status);
+
+/*
+ * la_chunk_fwd_plan -- the launch plan la_chunk_fwd would use (host only,
+ * for tests and benchmarks): the d_v tile width of one workgroup and the
+ * number of sequence segments each head is split into.  Returns LA_OK or the
+ * error la_chunk_fwd would return for these arguments.
+ */
+la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                            int* dv_tile, int* segments);
+
+/*
+ * la_set_plan -- override the launch plan la_chunk_fwd chooses for the bf16
+ * path: the d_v tile width of one workgroup (16, 32, 64 or 128; must divide
+ * d_v) and the number of sequence segments per head (>= 1).  0 restores the
+ * automatic choice for that field; values that do not fit a given call are
+ * clamped to the nearest valid ones for that call.  Results do not depend on
+ * the plan beyond rounding; tests use it to check exactly that.
+ * Process-wide; returns LA_ERR_UNSUPPORTED for an invalid tile, LA_ERR_SHAPE
+ * for a negative segment count.
+ */
+la_status la_set_plan(int dv_tile, int segments);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H_ */

@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/la.h
+declares, and rejects bad arguments with the documented status codes before
+touching the GPU (so these run on a machine without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_recurrence_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+P16 = ctypes.c_void_p(1 << 20)        # 16-byte aligned fake device address (never dereferenced)
+P8 = ctypes.c_void_p((1 << 20) + 8)   # misaligned
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:la_status|size_t|const char\*)\s+(la_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.load()
+    names = _declared()
+    assert set(names) == set(la.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(7):
+        assert la.status_string(s).startswith("LA_")
+    assert "unknown" in la.status_string(99)
+
+
+def _fwd(**kw):
+    a = dict(q=P16, k=P16, v=P16, dtype=1, B=1, H=1, L=64, dk=64, dv=64, C=64, phi=0, kind=0,
+             decay=None, state=None, out=P16, ws=None, ws_bytes=0)
+    a.update(kw)
+    return la.load().la_chunk_fwd(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["H"], a["L"],
+                                  a["dk"], a["dv"], a["C"], a["phi"], a["kind"], a["decay"],
+                                  a["state"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(out=None), NULL),
+    (dict(kind=1, decay=None), NULL), (dict(kind=3, decay=None), NULL),
+    (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(L=-5), SHAPE), (dict(C=0), SHAPE),
+    (dict(dk=48), UNSUP), (dict(dv=256), UNSUP), (dict(dk=8), UNSUP), (dict(C=256), UNSUP),
+    (dict(C=48), UNSUP), (dict(dtype=2), UNSUP), (dict(phi=2), UNSUP), (dict(kind=4), UNSUP),
+    (dict(kind=-1), UNSUP),
+    (dict(q=P8), ALIGN), (dict(out=P8), ALIGN), (dict(state=P8), ALIGN),
+    (dict(kind=1, decay=ctypes.c_void_p((1 << 20) + 2)), ALIGN),
+])
+def test_chunk_fwd_rejects(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_zero_length_is_ok_without_touching_memory():
+    assert _fwd(L=0, q=None, k=None, v=None, out=None) == OK
+
+
+def test_workspace_is_required_when_the_plan_splits_the_sequence():
+    # 1 head of 64 x 64 over 64K tokens: the plan splits the sequence
+    tv, P = la.plan(1, 1, 65536, 64, 64, 64)
+    assert P > 1
+    need = la.chunk_fwd_workspace_bytes(1, 1, 65536, 64, 64, 64)
+    assert need >= P * 64 * 64 * 4
+    assert _fwd(L=65536, ws=None, ws_bytes=0) == WS
+    assert _fwd(L=65536, ws=P16, ws_bytes=need - 1) == WS
+    assert _fwd(L=65536, ws=P8, ws_bytes=need) == ALIGN
+
+
+def test_plans_of_the_workloads():
+    # retnet: 64 heads x 4 value tiles of 32 = 256 workgroups, one segment
+    assert la.plan(2, 32, 16384, 128, 128, 64) == (32, 1)
+    # gated: 16 heads x 4 tiles x 4 segments = 256 workgroups
+    assert la.plan(1, 16, 65536, 128, 128, 64) == (32, 4)
+    # elu: 64 heads x 2 tiles x 2 segments
+    assert la.plan(4, 16, 4096, 64, 64, 64) == (32, 2)
+    # fp32: one segment, 16- or 32-wide tiles
+    assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32) == (16, 1)
+    assert la.chunk_fwd_workspace_bytes(1, 1, 300, 16, 16, 64, la.LA_F32) == 0
+
+
+def test_plan_override_and_clamping():
+    try:
+        la.set_plan(64, 3)
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (64, 3)
+        assert la.plan(1, 1, 64 * 2, 128, 32, 64) == (32, 2)   # tile clamped to d_v, P to chunks
+        with pytest.raises(la.LAError):
+            la.set_plan(48, 0)
+        with pytest.raises(la.LAError):
+            la.set_plan(0, -1)
+    finally:
+        la.set_plan(0, 0)
+    assert la.plan(2, 32, 16384, 128, 128, 64) == (32, 1)
+
+
+def _dec(**kw):
+    a = dict(q=P16, k=P16, v=P16, dtype=1, N=2, H=2, dk=128, dv=128, phi=0, kind=0, decay=None,
+             state=P16, out=P16)
+    a.update(kw)
+    return la.load().la_decode_step(a["q"], a["k"], a["v"], a["dtype"], a["N"], a["H"], a["dk"],
+                                    a["dv"], a["phi"], a["kind"], a["decay"], a["state"],
+                                    a["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), NULL), (dict(out=None), NULL), (dict(q=None), NULL),
+    (dict(kind=2, decay=None), NULL), (dict(N=0), SHAPE), (dict(H=0), SHAPE),
+    (dict(dk=100), UNSUP), (dict(dtype=7), UNSUP), (dict(phi=5), UNSUP), (dict(kind=9), UNSUP),
+    (dict(state=P8), ALIGN), (dict(v=P8), ALIGN),
+])
+def test_decode_step_rejects(kw, code):
+    assert _dec(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 1, 1, 64, 64), NULL), ((P16, 0, 1, 64, 64), SHAPE), ((P16, 1, 1, 64, 20), UNSUP),
+    ((P8, 1, 1, 64, 64), ALIGN),
+])
+def test_state_init_rejects(args, code):
+    assert la.load().la_state_init(*args, None) == code
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        la.chunk_fwd(x, x, x)
