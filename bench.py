@@ -48,7 +48,7 @@ def bench_chunk(la, torch, W, steps, warmup):
     q, k, v, gamma = q.to(dev), k.to(dev), v.to(dev), gamma.to(dev)
     S = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
     out = torch.empty_like(v)
-    need = la.chunk_fwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, w.C)
+    need = la.chunk_fwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, w.C, la.LA_BF16, w.decay_kind)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 

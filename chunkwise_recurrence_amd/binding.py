@@ -48,7 +48,7 @@ def load():
     lib.la_state_init.restype = i
     lib.la_state_init.argtypes = [vp, i, i, i, i, vp]
     lib.la_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.la_chunk_fwd_workspace_bytes.argtypes = [i] * 7
+    lib.la_chunk_fwd_workspace_bytes.argtypes = [i] * 8
     lib.la_chunk_fwd.restype = i
     lib.la_chunk_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp, vp, vp,
                                  ctypes.c_size_t, vp]
@@ -116,8 +116,8 @@ def set_plan(dv_tile: int = 0, segments: int = 0):
 
 
 def chunk_fwd_workspace_bytes(B: int, H: int, L: int, dk: int, dv: int, C: int,
-                              dtype: int = LA_BF16) -> int:
-    return int(load().la_chunk_fwd_workspace_bytes(B, H, L, dk, dv, C, dtype))
+                              dtype: int = LA_BF16, decay_kind: int = DECAY_NONE) -> int:
+    return int(load().la_chunk_fwd_workspace_bytes(B, H, L, dk, dv, C, dtype, decay_kind))
 
 
 def state_init(state: torch.Tensor, stream=None) -> torch.Tensor:
@@ -153,7 +153,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, C: int = 64,
         raise ValueError("decay data must be float32")
     if state is not None and (state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv)):
         raise ValueError("state must be float32 [B,H,dk,dv]")
-    need = chunk_fwd_workspace_bytes(B, H, L, dk, dv, C, dt)
+    need = chunk_fwd_workspace_bytes(B, H, L, dk, dv, C, dt, decay_kind)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -6,13 +6,15 @@
 #include <atomic>
 #include <stdint.h>
 
-#include "../../include/la.h"
+#include "la.h"
 #include "la_internal.h"
 
 namespace {
 
 // Workgroups the bf16 plan aims for: one per compute unit of an MI355X.
 constexpr int kTargetWorkgroups = 256;
+// Widest value tile of one bf16 workgroup.
+constexpr int kMaxTile = 64;
 // A segment of the sequence keeps at least this many chunks.
 constexpr int kMinSegmentChunks = 4;
 
@@ -28,8 +30,11 @@ struct Plan {
   int P = 1;         // sequence segments per head
   int seg_chunks = 0;
   size_t ws_bytes = 0;
-  size_t ws_S_off = 0, ws_logA_off = 0;
+  size_t ws_S_off = 0, ws_logA_off = 0, ws_b_off = 0;
+  bool prefix = false;  // token decays: in-chunk prefix sums of log a in the workspace
 };
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 la_status check_chunk_shape(int dtype, int B, int H, int L, int d_k, int d_v, int C) {
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
@@ -38,7 +43,7 @@ la_status check_chunk_shape(int dtype, int B, int H, int L, int d_k, int d_v, in
   return LA_OK;
 }
 
-Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
+Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int decay_kind) {
   Plan p;
   const int heads = B * H;
   const int nchunks = L > 0 ? (L + C - 1) / C : 0;
@@ -48,13 +53,13 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
     p.seg_chunks = nchunks;
     return p;
   }
-  // value tile: the widest that still gives enough workgroups, not below 32
-  int tv = d_v;
+  // value tile: the widest (at most 64) that still gives enough workgroups, not below 32
+  int tv = d_v < kMaxTile ? d_v : kMaxTile;
   while ((long long)heads * (d_v / tv) < kTargetWorkgroups && tv > 32) tv /= 2;
   const int forced_tv = g_plan_tv.load();
   if (forced_tv > 0) {
     tv = forced_tv;
-    while (tv > d_v) tv /= 2;
+    while (tv > d_v || tv > kMaxTile) tv /= 2;
   }
   while (tv > 16 && !la::chunk_bf16_supported(d_k, tv, C)) tv /= 2;
   p.tv = tv;
@@ -69,13 +74,19 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
   if (P < 1) P = 1;
   p.seg_chunks = nchunks > 0 ? (nchunks + P - 1) / P : 0;
   p.P = p.seg_chunks > 0 ? (nchunks + p.seg_chunks - 1) / p.seg_chunks : 1;
+  size_t off = 0;
   if (p.P > 1) {
-    const size_t s_bytes = (size_t)heads * p.P * d_k * d_v * sizeof(float);
-    const size_t a_bytes = (size_t)heads * p.P * sizeof(float);
-    p.ws_S_off = 0;
-    p.ws_logA_off = (s_bytes + 255) & ~(size_t)255;
-    p.ws_bytes = p.ws_logA_off + ((a_bytes + 255) & ~(size_t)255);
+    p.ws_S_off = off;
+    off += round256((size_t)heads * p.P * d_k * d_v * sizeof(float));
+    p.ws_logA_off = off;
+    off += round256((size_t)heads * p.P * sizeof(float));
   }
+  if (decay_kind == LA_DECAY_TOKEN_LOG || decay_kind == LA_DECAY_TOKEN_GATE) {
+    p.prefix = true;
+    p.ws_b_off = off;
+    off += round256((size_t)heads * L * sizeof(float));
+  }
+  p.ws_bytes = off;
   return p;
 }
 
@@ -109,15 +120,17 @@ la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dt
                             int* segments) {
   const la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
   if (st != LA_OK) return st;
-  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype);
+  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, LA_DECAY_NONE);
   if (dv_tile) *dv_tile = p.tv;
   if (segments) *segments = p.P;
   return LA_OK;
 }
 
-size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
+size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                                    int decay_kind) {
   if (check_chunk_shape(dtype, B, H, L, d_k, d_v, C) != LA_OK || L == 0) return 0;
-  return make_plan(B, H, L, d_k, d_v, C, dtype).ws_bytes;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return 0;
+  return make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind).ws_bytes;
 }
 
 la_status la_state_init(float* state, int B, int H, int d_k, int d_v, void* stream) {
@@ -143,7 +156,7 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
       (state && !aligned(state, 16)) || (decay_data && !aligned(decay_data, 4)))
     return LA_ERR_ALIGN;
-  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype);
+  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind);
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return LA_ERR_ALIGN;
@@ -175,8 +188,13 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
     a.n_units = B * H;
     e = la::launch_chunk_f32(a, s);
   } else {
+    char* ws = static_cast<char*>(workspace);
+    if (p.prefix) {
+      a.ws_b = reinterpret_cast<float*>(ws + p.ws_b_off);
+      e = la::launch_decay_prefix(a, s);
+      if (e != hipSuccess) return LA_ERR_DEVICE;
+    }
     if (p.P > 1) {
-      char* ws = static_cast<char*>(workspace);
       a.ws_S = reinterpret_cast<float*>(ws + p.ws_S_off);
       a.ws_logA = reinterpret_cast<float*>(ws + p.ws_logA_off);
       a.n_units = B * H * (p.P - 1);

@@ -1,0 +1,567 @@
+// la_chunk_bf16.h -- chunkwise causal linear attention, bf16 in, gfx950 MFMA.
+// Kernel template; one translation unit per key dimension instantiates it.
+//
+// What one workgroup computes.  A work unit is one head (b, h), one tile of
+// TV value columns [dv0, dv0 + TV) and one segment of consecutive chunks of
+// the sequence.  For every chunk of C tokens, with b_i the inclusive prefix
+// sum of log a over the chunk (every factor below is exp of a value <= 0):
+//
+//   O_c     = diag(e^b) Q_c S_c + ((Q_c K_c^T) o D_c) V_c,   D_c[i,j] = e^{b_i - b_j} [j <= i]
+//   S_{c+1} = e^{b_last} S_c + K_c^T diag(e^{b_last - b}) V_c
+//
+// This is the chunkwise form of "Linear / Sparse Attention - minimal runnable
+// implementation" (linear_attn_chunkwise: inter = Q_c S, intra = masked
+// (Q_c K_c^T) V_c, then S += K_c^T V_c, ragged last chunk) with the decay
+// folded into S_c and the in-chunk mask, as the linear/sparse attention
+// tutorial's section 6.2 says the gated variants do; the per-element decay is
+// the log-space construction of CS336 lecture 4 code 1,
+// gated_linear_attention_parallel (log D[t,s] = cumsum[t] - cumsum[s]).
+//
+// Mapping onto gfx950 (4 waves of 64 lanes, v_mfma_f32_16x16x32_bf16):
+//   * K and V tiles of a chunk go from HBM straight into LDS with
+//     global_load_lds_dwordx4 (no register staging), double-buffered: the
+//     next chunk streams in while the current one computes.  Rows are stored
+//     with an XOR swizzle of their 16-byte chunks so that 16 lanes reading 16
+//     rows at one column hit 16 different bank groups.
+//   * K^T and V^T operands (8 consecutive tokens of one key/value column per
+//     lane) come from the row-major tiles through ds_read_b64_tr_b16, the
+//     LDS transpose read: no transposed copies.
+//   * the C query rows of a chunk are split into 16-row strips, strip st
+//     belongs to wave st % 4.  A wave computes its strip's scores against key
+//     blocks 0..st only (the causal upper blocks are skipped), masks and
+//     decays them in fp32 registers, and uses them straight from registers as
+//     the B operand of the P.V product: the scores come out of the QK^T MFMA
+//     transposed (K is the A operand), which is already the operand layout;
+//     the V^T operand reads the matching two runs of 4 tokens.
+//   * the state tile S[:, dv0:dv0+TV] lives in fp32 MFMA accumulators, split
+//     over the 4 waves by 16x16 tile; after each update a bf16 copy S^T is
+//     written to LDS (double-buffered) for the next chunk's inter-chunk term.
+//   * Q goes straight from HBM into the B-operand registers of its wave.
+//   * one workgroup barrier per chunk.
+//   * the workgroups of one (head, segment) that differ only in the value
+//     tile are numbered so that they land on one XCD and share Q and K
+//     through that XCD's L2.
+//
+// A state-only variant (STATE_ONLY) computes, for one segment, the state
+// increment dS = sum_t e^{B_end - B_t} k_t v_t^T from a zero state and the
+// segment's total log decay; the main pass then starts every segment from
+// S_in = e^{A_{s-1}} (... (e^{A_0} S_0 + dS_0) ...) + dS_{s-1}, the prefix of
+// the associative (decay, state) composition (the parallel / associative
+// scan idea of the tutorial's section 3.3 applied to these pairs).
+#pragma once
+#include "la_device.h"
+
+namespace la {
+namespace bf16k {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int DK, int TV, int C>
+struct Geo {
+  static constexpr int CP = C < 32 ? 32 : C;       // chunk padded to whole MFMA k-steps
+  static constexpr int KSTEPS = DK < 32 ? 1 : DK / 32;  // k-steps over the key dim
+  static constexpr int CSTEPS = CP / 32;           // k-steps over the chunk's tokens
+  static constexpr int WCK = DK / 8;               // 16-byte chunks per K row
+  static constexpr int WCV = TV / 8;               // 16-byte chunks per V row
+  static constexpr int NSTRIP = C / 16;            // 16-row query strips per chunk
+  static constexpr int SPW = (NSTRIP + 3) / 4;     // strips per wave
+  static constexpr int NTV = TV / 16;              // 16-wide value tiles
+  static constexpr int NMK = DK / 16;              // 16-wide key tiles
+  static constexpr int NT_S = NMK * NTV;           // 16x16 tiles of the state
+  static constexpr int TPW = (NT_S + 3) / 4;       // state tiles per wave
+  static constexpr int K_TILE = C * DK;            // elements of one K tile
+  static constexpr int V_TILE = C * TV;
+  static constexpr int S_TILE = TV * DK;
+  static constexpr int NK_CHUNKS = C * WCK;        // 16-byte chunks of one K tile
+  static constexpr int NV_CHUNKS = C * WCV;
+  static constexpr size_t LDS_MAIN = 2 * (2 * (size_t)K_TILE + 2 * (size_t)V_TILE +
+                                          2 * (size_t)S_TILE) + 2 * 4 * (size_t)CP;
+};
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+// Byte offset of element (row, col) in a row-major bf16 tile of WC 16-byte
+// chunks per row whose chunks are XOR-swizzled by the row's position in its
+// 256-byte bank line: 16 consecutive rows read at one logical column land in
+// 16 distinct bank groups.
+template <int WC>
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int R = WC >= 16 ? 1 : 16 / WC;  // rows per 256-byte bank line
+  const int chunk = (col >> 3) ^ ((row / R) & (WC - 1));
+  return row * (WC * 16) + (chunk << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ u32x4 lds_b128(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+// Two LDS transpose reads: lane i of each 16-lane group receives column
+// (col0 + i) of rows k0a..k0a+3 (elements 0-3) and k0b..k0b+3 (elements 4-7)
+// of a swizzled row-major tile; each source lane s addresses row k0 + s/4,
+// columns col0 + 4 (s%4) .. +3.
+template <int WC>
+__device__ __forceinline__ u32x4 lds_tr8(const char* base, int k0a, int k0b, int col0, int l16) {
+  const int j = l16 >> 2, m = l16 & 3;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + swz<WC>(k0a + j, col0 + 4 * m)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + swz<WC>(k0b + j, col0 + 4 * m)));
+  u32x4 r;
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  r[0] = a[0];
+  r[1] = a[1];
+  r[2] = b[0];
+  r[3] = b[1];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// phi = elu + 1 on 8 packed bf16 values.
+__device__ __forceinline__ u32x4 elu1_x8(u32x4 w) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = cvt2(feature_elu1(bf16_to_f32(w[e] & 0xffffu)), feature_elu1(bf16_to_f32(w[e] >> 16)));
+  return w;
+}
+
+// Global -> LDS copy of one 16-byte chunk per lane; `dst` is wave-uniform and
+// lane l's chunk lands at dst + 16 l.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
+// Decay category of a launch (a template parameter, so the kernel has no
+// per-element branches on it): none, one constant per head, or per token
+// (log a given, or the gate a = exp(-softplus(g)); both arrive as in-chunk
+// prefix sums from the prefix pass).
+enum { kCatNone = 0, kCatHead = 1, kCatToken = 2 };
+
+template <int DK, int TV, int C, int CAT, bool STATE_ONLY>
+__global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
+  using G = Geo<DK, TV, C>;
+  static_assert(G::NTV <= 4, "a wave's state tiles must share one value tile");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < 4);
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // workgroup -> (unit, value tile); the tiles of one unit share an XCD
+  const int f = blockIdx.x;
+  const int slot = f >> 3;
+  const int vt = slot % a.n_v;
+  const int u = (slot / a.n_v) * 8 + (f & 7);
+  if (u >= a.n_units) return;
+  const int segs = STATE_ONLY ? a.P - 1 : a.P;
+  const int bh = u / segs, sigma = u % segs;
+  const int h = bh % a.H;
+  const int dv0 = vt * TV;
+  const int L = a.L, DV = a.DV;
+  const int nchunks = (L + C - 1) / C;
+  const int c_begin = sigma * a.seg_chunks;
+  const int c_end = min(c_begin + a.seg_chunks, nchunks);
+  constexpr bool decayed = CAT != kCatNone;
+  const bool elu = a.phi == kPhiElu1;
+
+  __shared__ __align__(16) char sK[2][G::K_TILE * 2];
+  __shared__ __align__(16) char sV[2][G::V_TILE * 2];
+  __shared__ __align__(16) char sST[2][STATE_ONLY ? 16 : G::S_TILE * 2];
+  __shared__ __align__(16) float sB[2][CAT == kCatToken ? G::CP : 4];
+
+  const size_t head_k = (size_t)bh * L * DK;
+  const size_t head_v = (size_t)bh * L * DV;
+  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + head_k;
+  const uint16_t* kh = static_cast<const uint16_t*>(a.k) + head_k;
+  const uint16_t* vh = static_cast<const uint16_t*>(a.v) + head_v + dv0;
+  uint16_t* oh = static_cast<uint16_t*>(a.out) + head_v + dv0;
+  const float* bws = CAT == kCatToken ? a.ws_b + (size_t)bh * L : nullptr;
+  const float lg = CAT == kCatHead ? logf(a.decay[h]) : 0.0f;
+
+  // state tiles of this wave: one value tile nt, key tiles mt = (wave + 4 t) / NTV
+  const int nt_w = wave % G::NTV;
+
+  // ---- initial state of this unit --------------------------------------
+  f32x4 accS[G::TPW];
+#pragma unroll
+  for (int t = 0; t < G::TPW; ++t) accS[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (!STATE_ONLY) {
+#pragma unroll
+    for (int t = 0; t < G::TPW; ++t) {
+      const int tau = wave + 4 * t;
+      if (tau < G::NT_S) {
+        const int mt = tau / G::NTV;
+        const int dv = dv0 + 16 * nt_w + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dk = 16 * mt + 4 * g4 + i;
+          float s = a.state ? a.state[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
+          for (int p = 0; p < sigma; ++p) {
+            const size_t seg = (size_t)bh * a.P + p;
+            s = expf(a.ws_logA[seg]) * s + a.ws_S[(seg * DK + dk) * DV + dv];
+          }
+          accS[t][i] = s;
+        }
+        u32x2 w;
+        w[0] = cvt2(accS[t][0], accS[t][1]);
+        w[1] = cvt2(accS[t][2], accS[t][3]);
+        *reinterpret_cast<u32x2*>(&sST[0][swz<G::WCK>(16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
+      }
+    }
+  }
+
+  // ---- loads of one chunk: K, V tiles and b into LDS, Q into registers ----
+  u32x4 qnext[G::SPW][G::KSTEPS];
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+
+  auto issue_loads = [&](int c, int buf) {
+    const int t0 = c * C;
+#pragma unroll
+    for (int i = 0; i < (G::NK_CHUNKS + 255) / 256; ++i) {
+      const int idx = wave + 4 * i;              // 64-chunk block of the tile
+      const int q = 64 * idx + lane;
+      if (64 * idx < G::NK_CHUNKS && q < G::NK_CHUNKS) {
+        const int r = q / G::WCK, p = q % G::WCK;
+        const int cc = p ^ ((r / (G::WCK >= 16 ? 1 : 16 / G::WCK)) & (G::WCK - 1));
+        const int t = min(t0 + r, L - 1);
+        dma16(kh + (size_t)t * DK + 8 * cc, &sK[buf][1024 * idx]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (G::NV_CHUNKS + 255) / 256; ++i) {
+      const int idx = wave + 4 * i;
+      const int q = 64 * idx + lane;
+      if (64 * idx < G::NV_CHUNKS && q < G::NV_CHUNKS) {
+        const int r = q / G::WCV, p = q % G::WCV;
+        const int cc = p ^ ((r / (G::WCV >= 16 ? 1 : 16 / G::WCV)) & (G::WCV - 1));
+        const int t = min(t0 + r, L - 1);
+        dma16(vh + (size_t)t * DV + 8 * cc, &sV[buf][1024 * idx]);
+      }
+    }
+    if constexpr (CAT == kCatToken) {
+#pragma unroll
+      for (int i = 0; i < (C + 63) / 64; ++i) {
+        if (wave == i && 64 * i + lane < C) {
+          const int t = min(t0 + 64 * i + lane, L - 1);
+          dma4(bws + t, &sB[buf][64 * i]);
+        }
+      }
+    }
+    if constexpr (!STATE_ONLY) {
+#pragma unroll
+      for (int j = 0; j < G::SPW; ++j) {
+        const int st = wave + 4 * j;
+        const int t = t0 + 16 * st + l16;
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; ++s) {
+          const int col = 32 * s + 8 * g4;
+          qnext[j][s] = (st < G::NSTRIP && t < L && col < DK)
+                            ? *reinterpret_cast<const u32x4*>(qh + (size_t)t * DK + col)
+                            : zero4;
+        }
+      }
+    }
+  };
+
+  float logA = 0.0f;
+  issue_loads(c_begin, 0);
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int buf = (c - c_begin) & 1;
+    const int t0 = c * C;
+    const int nvalid = min(C, L - t0);
+    char* kb = sK[buf];
+    char* vb = sV[buf];
+    const float* sb = sB[buf];
+
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c have landed
+    __syncthreads();                // ... and everybody's; chunk c-1 is finished
+    u32x4 qcur[G::SPW][G::KSTEPS];
+    if constexpr (!STATE_ONLY) {
+#pragma unroll
+      for (int j = 0; j < G::SPW; ++j)
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = elu ? elu1_x8(qnext[j][s]) : qnext[j][s];
+    }
+    if (c + 1 < c_end) issue_loads(c + 1, buf ^ 1);
+
+    // a short last chunk: zero the rows past the sequence (they hold clamped copies)
+    if (nvalid < C) {
+      for (int q = tid; q < (C - nvalid) * G::WCK; q += 256)
+        *reinterpret_cast<u32x4*>(kb + 16 * (nvalid * G::WCK + q)) = zero4;
+      for (int q = tid; q < (C - nvalid) * G::WCV; q += 256)
+        *reinterpret_cast<u32x4*>(vb + 16 * (nvalid * G::WCV + q)) = zero4;
+      __syncthreads();
+    }
+    // feature map on the staged keys, in place
+    if (elu) {
+      for (int q = tid; q < G::NK_CHUNKS; q += 256) {
+        u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
+        *p = elu1_x8(*p);
+      }
+      __syncthreads();
+    }
+
+    // b_i of this chunk (inclusive prefix of log a; per-head decay in closed form)
+    auto bval = [&](int i) -> float {
+      if constexpr (CAT == kCatHead) return (float)(min(i, nvalid - 1) + 1) * lg;
+      else if constexpr (CAT == kCatToken) return sb[i];
+      else return 0.0f;
+    };
+    const float bL = bval(nvalid - 1);
+
+    // (a) outputs of this chunk's query strips.  Every strip computes scores
+    // against all key blocks; the causal mask zeroes the blocks past the
+    // diagonal.  The slowest wave (the last strip) needs all of them anyway.
+    if constexpr (!STATE_ONLY) {
+      const char* stc = sST[buf];
+#pragma unroll
+      for (int j = 0; j < G::SPW; ++j) {
+        const int st = wave + 4 * j;
+        if (G::NSTRIP >= 4 * (j + 1) || st < G::NSTRIP) {
+          // all K operands of the strip's scores, then the MFMAs interleaved over key blocks
+          u32x4 kA[G::NSTRIP][G::KSTEPS];
+#pragma unroll
+          for (int jj = 0; jj < G::NSTRIP; ++jj)
+#pragma unroll
+            for (int s = 0; s < G::KSTEPS; ++s)
+              kA[jj][s] = (DK >= 32 || g4 < 2)
+                              ? lds_b128(kb, swz<G::WCK>(16 * jj + l16, 32 * s + 8 * g4))
+                              : zero4;
+          f32x4 pt[G::NSTRIP];
+#pragma unroll
+          for (int jj = 0; jj < G::NSTRIP; ++jj) pt[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < G::KSTEPS; ++s)
+#pragma unroll
+            for (int jj = 0; jj < G::NSTRIP; ++jj)
+              pt[jj] = mfma16x16x32(kA[jj][s], qcur[j][s], pt[jj]);
+          // operands of the inter- and intra-chunk products
+          u32x4 sA[G::NTV][G::KSTEPS];
+          u32x4 vA[G::NTV][G::CSTEPS];
+#pragma unroll
+          for (int mo = 0; mo < G::NTV; ++mo) {
+#pragma unroll
+            for (int s = 0; s < G::KSTEPS; ++s)
+              sA[mo][s] = (DK >= 32 || g4 < 2)
+                              ? lds_b128(stc, swz<G::WCK>(16 * mo + l16, 32 * s + 8 * g4))
+                              : zero4;
+#pragma unroll
+            for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
+              if constexpr (C >= 32) {
+                // V^T rows for tokens 32 s2 + 4 g4 + (0..3) and 32 s2 + 16 + 4 g4 + (0..3)
+                vA[mo][s2] = lds_tr8<G::WCV>(vb, 32 * s2 + 4 * g4, 32 * s2 + 16 + 4 * g4,
+                                             16 * mo, l16);
+              } else {
+                // a 16-token chunk: the second run of 4 tokens lies past the chunk
+                const int j2 = l16 >> 2, m2 = l16 & 3;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(vb + swz<G::WCV>(4 * g4 + j2, 16 * mo + 4 * m2)));
+                const u32x2 lw = __builtin_bit_cast(u32x2, lo);
+                vA[mo][s2] = u32x4{lw[0], lw[1], 0u, 0u};
+              }
+            }
+          }
+          // pt[jj][i] = score of query row r against key 16 jj + 4 g4 + i: mask and decay
+          const int r = 16 * st + l16;
+          const float br = bval(r);
+#pragma unroll
+          for (int jj = 0; jj < G::NSTRIP; ++jj) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int cc = 16 * jj + 4 * g4 + i;
+              float x = pt[jj][i];
+              if constexpr (decayed) x *= __expf(br - bval(cc));
+              pt[jj][i] = cc <= r ? x : 0.0f;
+            }
+          }
+          u32x4 pb[G::CSTEPS];
+#pragma unroll
+          for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
+            const f32x4 lo = pt[2 * s2];
+            const f32x4 hi = (2 * s2 + 1 < G::NSTRIP) ? pt[2 * s2 + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+            pb[s2][0] = cvt2(lo[0], lo[1]);
+            pb[s2][1] = cvt2(lo[2], lo[3]);
+            pb[s2][2] = cvt2(hi[0], hi[1]);
+            pb[s2][3] = cvt2(hi[2], hi[3]);
+          }
+          f32x4 acc[G::NTV];
+#pragma unroll
+          for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < G::KSTEPS; ++s)
+#pragma unroll
+            for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = mfma16x16x32(sA[mo][s], qcur[j][s], acc[mo]);
+          const float erow = decayed ? __expf(br) : 1.0f;
+#pragma unroll
+          for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = acc[mo] * erow;
+#pragma unroll
+          for (int s2 = 0; s2 < G::CSTEPS; ++s2)
+#pragma unroll
+            for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = mfma16x16x32(vA[mo][s2], pb[s2], acc[mo]);
+          if (r < nvalid) {
+#pragma unroll
+            for (int mo = 0; mo < G::NTV; ++mo) {
+              u32x2 w;
+              w[0] = cvt2(acc[mo][0], acc[mo][1]);
+              w[1] = cvt2(acc[mo][2], acc[mo][3]);
+              *reinterpret_cast<u32x2*>(oh + (size_t)(t0 + r) * DV + 16 * mo + 4 * g4) = w;
+            }
+          }
+        }
+      }
+    }
+
+    // (b) state update S <- e^{b_last} S + K^T diag(e^{b_last - b}) V.  The
+    // transpose reads take every lane of the wave (they exchange data within
+    // each 16-lane group); for a 16-token chunk the lane groups past the chunk
+    // read rows 0..15 again and are zeroed afterwards.
+    if (G::TPW > 1 || wave < G::NT_S) {
+      const float eL = decayed ? __expf(bL) : 1.0f;
+      char* stn = sST[buf ^ 1];
+      u32x4 vB[G::CSTEPS];
+#pragma unroll
+      for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
+        const int k0 = (C >= 32) ? 32 * s2 + 8 * g4 : (8 * g4) & 15;
+        u32x4 w = lds_tr8<G::WCV>(vb, k0, k0 + 4, 16 * nt_w, l16);
+        if constexpr (decayed) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {  // word e holds tokens k0 + 2e, k0 + 2e + 1
+            const int t_lo = k0 + 2 * e;
+            w[e] = cvt2(bf16_to_f32(w[e] & 0xffffu) * __expf(bL - bval(min(t_lo, C - 1))),
+                        bf16_to_f32(w[e] >> 16) * __expf(bL - bval(min(t_lo + 1, C - 1))));
+          }
+        }
+        vB[s2] = (C < 32 && g4 >= 2) ? zero4 : w;
+      }
+      u32x4 kA2[G::TPW][G::CSTEPS];
+#pragma unroll
+      for (int t = 0; t < G::TPW; ++t) {
+        const int mt = min((wave + 4 * t) / G::NTV, G::NMK - 1);
+#pragma unroll
+        for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
+          const int k0 = (C >= 32) ? 32 * s2 + 8 * g4 : (8 * g4) & 15;
+          const u32x4 w = lds_tr8<G::WCK>(kb, k0, k0 + 4, 16 * mt, l16);
+          kA2[t][s2] = (C < 32 && g4 >= 2) ? zero4 : w;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < G::TPW; ++t) accS[t] = accS[t] * eL;
+#pragma unroll
+      for (int s2 = 0; s2 < G::CSTEPS; ++s2)
+#pragma unroll
+        for (int t = 0; t < G::TPW; ++t) accS[t] = mfma16x16x32(kA2[t][s2], vB[s2], accS[t]);
+      if constexpr (!STATE_ONLY) {
+#pragma unroll
+        for (int t = 0; t < G::TPW; ++t) {
+          const int tau = wave + 4 * t;
+          if (tau < G::NT_S) {
+            const int mt = tau / G::NTV;
+            u32x2 w;
+            w[0] = cvt2(accS[t][0], accS[t][1]);
+            w[1] = cvt2(accS[t][2], accS[t][3]);
+            *reinterpret_cast<u32x2*>(&stn[swz<G::WCK>(16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
+          }
+        }
+      }
+    }
+    logA += bL;
+  }
+
+  // ---- epilogue ---------------------------------------------------------
+  float* dst = nullptr;
+  if constexpr (STATE_ONLY) {
+    dst = a.ws_S + ((size_t)bh * a.P + sigma) * DK * DV;
+    if (vt == 0 && tid == 0) a.ws_logA[(size_t)bh * a.P + sigma] = logA;
+  } else {
+    if (sigma == a.P - 1 && a.state != nullptr) dst = a.state + (size_t)bh * DK * DV;
+  }
+  if (dst != nullptr) {
+#pragma unroll
+    for (int t = 0; t < G::TPW; ++t) {
+      const int tau = wave + 4 * t;
+      if (tau < G::NT_S) {
+        const int mt = tau / G::NTV;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[(size_t)(16 * mt + 4 * g4 + i) * DV + dv0 + 16 * nt_w + l16] = accS[t][i];
+      }
+    }
+  }
+}
+
+template <int DK, int TV, int C, int CAT>
+hipError_t launch_one(const ChunkArgs& a, bool state_only, hipStream_t s) {
+  const int groups = (a.n_units + 7) / 8;
+  const dim3 grid(groups * 8 * a.n_v), block(256);
+  if (state_only)
+    hipLaunchKernelGGL((chunk_bf16_kernel<DK, TV, C, CAT, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((chunk_bf16_kernel<DK, TV, C, CAT, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DK, int TV, int CAT>
+hipError_t dispatch_c(const ChunkArgs& a, bool so, hipStream_t s) {
+  switch (a.C) {
+    case 16: return launch_one<DK, TV, 16, CAT>(a, so, s);
+    case 32: return launch_one<DK, TV, 32, CAT>(a, so, s);
+    case 64: return launch_one<DK, TV, 64, CAT>(a, so, s);
+    case 128:
+      if constexpr (Geo<DK, TV, 128>::LDS_MAIN <= kMaxLds) return launch_one<DK, TV, 128, CAT>(a, so, s);
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DK, int CAT>
+hipError_t dispatch_tv(const ChunkArgs& a, bool so, hipStream_t s) {
+  switch (a.tv) {
+    case 16: return dispatch_c<DK, 16, CAT>(a, so, s);
+    case 32: return dispatch_c<DK, 32, CAT>(a, so, s);
+    case 64: return dispatch_c<DK, 64, CAT>(a, so, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DK>
+hipError_t dispatch_cat(const ChunkArgs& a, bool so, hipStream_t s) {
+  switch (a.decay_kind) {
+    case kDecayNone: return dispatch_tv<DK, kCatNone>(a, so, s);
+    case kDecayHead: return dispatch_tv<DK, kCatHead>(a, so, s);
+    default: return dispatch_tv<DK, kCatToken>(a, so, s);
+  }
+}
+
+template <int DK, int TV>
+constexpr size_t lds_of(int C) {
+  return C == 16    ? Geo<DK, TV, 16>::LDS_MAIN
+         : C == 32  ? Geo<DK, TV, 32>::LDS_MAIN
+         : C == 64  ? Geo<DK, TV, 64>::LDS_MAIN
+                    : Geo<DK, TV, 128>::LDS_MAIN;
+}
+
+template <int DK>
+constexpr size_t lds_tv(int TV, int C) {
+  return TV == 16 ? lds_of<DK, 16>(C) : TV == 32 ? lds_of<DK, 32>(C) : lds_of<DK, 64>(C);
+}
+
+}  // namespace bf16k
+
+// One per key dimension, each in its own translation unit.
+hipError_t launch_chunk_bf16_dk16(const ChunkArgs& a, bool state_only, hipStream_t s);
+hipError_t launch_chunk_bf16_dk32(const ChunkArgs& a, bool state_only, hipStream_t s);
+hipError_t launch_chunk_bf16_dk64(const ChunkArgs& a, bool state_only, hipStream_t s);
+hipError_t launch_chunk_bf16_dk128(const ChunkArgs& a, bool state_only, hipStream_t s);
+
+}  // namespace la

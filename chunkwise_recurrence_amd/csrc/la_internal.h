@@ -22,6 +22,7 @@ struct ChunkArgs {
   const float* decay;   // nullptr | gamma[H] | [B,H,L]
   float* ws_S;          // [B*H, P, DK, DV] per-segment state increments
   float* ws_logA;       // [B*H, P] per-segment total log decay
+  float* ws_b;          // [B*H, L] in-chunk inclusive prefix of log a (token decays)
   int B, H, L, DK, DV, C;
   int P;                // sequence segments per head
   int seg_chunks;       // chunks per segment (the last one may hold fewer)
@@ -44,6 +45,7 @@ struct DecodeArgs {
 
 // Launchers (return the launch error, hipSuccess when enqueued).
 hipError_t launch_chunk_bf16(const ChunkArgs& a, bool state_only, hipStream_t s);
+hipError_t launch_decay_prefix(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);

@@ -82,10 +82,13 @@ la_status la_state_init(float* state, int B, int H, int d_k, int d_v, void* stre
 
 /*
  * la_chunk_fwd_workspace_bytes -- bytes of device workspace la_chunk_fwd needs
- * for this problem (0 when none is needed).  Pure host function; returns 0 for
- * arguments la_chunk_fwd would reject.
+ * for this problem (0 when none is needed): per-segment state increments when
+ * the sequence is split into segments, and the in-chunk prefix sums of log a
+ * (4 bytes per head-token) for the token-dependent decays.  Pure host
+ * function; returns 0 for arguments la_chunk_fwd would reject.
  */
-size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype);
+size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                                    int decay_kind);
 
 /*
  * la_chunk_fwd -- the chunkwise-parallel forward over a whole sequence.

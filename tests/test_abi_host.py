@@ -70,6 +70,9 @@ def test_workspace_is_required_when_the_plan_splits_the_sequence():
     assert P > 1
     need = la.chunk_fwd_workspace_bytes(1, 1, 65536, 64, 64, 64)
     assert need >= P * 64 * 64 * 4
+    # the token decays add 4 bytes per head-token of prefix sums
+    assert la.chunk_fwd_workspace_bytes(1, 1, 65536, 64, 64, 64, la.LA_BF16, 3) >= need + 65536 * 4
+    assert _fwd(L=65536, kind=3, decay=P16, ws=P16, ws_bytes=need) == WS
     assert _fwd(L=65536, ws=None, ws_bytes=0) == WS
     assert _fwd(L=65536, ws=P16, ws_bytes=need - 1) == WS
     assert _fwd(L=65536, ws=P8, ws_bytes=need) == ALIGN
