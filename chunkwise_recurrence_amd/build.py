@@ -22,8 +22,10 @@ ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 # Packed fp32 arithmetic stays off: the compiler must not form v_pk_*_f32.
+# MFMA accumulators stay in ordinary VGPRs (no AGPR copies).
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=true",
           "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 

@@ -49,6 +49,8 @@
 // the associative (decay, state) composition (the parallel / associative
 // scan idea of the tutorial's section 3.3 applied to these pairs).
 #pragma once
+#include <type_traits>
+
 #include "la_device.h"
 
 namespace la {
@@ -91,6 +93,11 @@ __device__ __forceinline__ int swz(int row, int col) {
   const int chunk = (col >> 3) ^ ((row / R) & (WC - 1));
   return row * (WC * 16) + (chunk << 4) + ((col & 7) << 1);
 }
+
+// An empty volatile statement: the block that holds it runs only when its
+// condition holds (the compiler may not if-convert it into always-executed
+// arithmetic plus a select).
+__device__ __forceinline__ void no_speculation() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ u32x4 lds_b128(const char* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
@@ -174,10 +181,21 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
   constexpr bool decayed = CAT != kCatNone;
   const bool elu = a.phi == kPhiElu1;
 
-  __shared__ __align__(16) char sK[2][G::K_TILE * 2];
-  __shared__ __align__(16) char sV[2][G::V_TILE * 2];
-  __shared__ __align__(16) char sST[2][STATE_ONLY ? 16 : G::S_TILE * 2];
-  __shared__ __align__(16) float sB[2][CAT == kCatToken ? G::CP : 4];
+  // Separate arrays per pipeline stage (not one [2][...] array): the DMA into
+  // one stage and the reads of the other are then provably disjoint, so the
+  // compiler does not wait for the prefetch before touching LDS.
+  __shared__ __align__(16) char sK0[G::K_TILE * 2], sK1[G::K_TILE * 2];
+  __shared__ __align__(16) char sV0[G::V_TILE * 2], sV1[G::V_TILE * 2];
+  __shared__ __align__(16) char sST0[STATE_ONLY ? 16 : G::S_TILE * 2];
+  __shared__ __align__(16) char sST1[STATE_ONLY ? 16 : G::S_TILE * 2];
+  __shared__ __align__(16) float sB0[CAT == kCatToken ? G::CP : 4];
+  __shared__ __align__(16) float sB1[CAT == kCatToken ? G::CP : 4];
+  auto stage_k = [&](auto BUF) -> char* { if constexpr (decltype(BUF)::value == 0) return sK0; else return sK1; };
+  auto stage_v = [&](auto BUF) -> char* { if constexpr (decltype(BUF)::value == 0) return sV0; else return sV1; };
+  auto stage_s = [&](auto BUF) -> char* { if constexpr (decltype(BUF)::value == 0) return sST0; else return sST1; };
+  auto stage_b = [&](auto BUF) -> float* { if constexpr (decltype(BUF)::value == 0) return sB0; else return sB1; };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   const size_t head_k = (size_t)bh * L * DK;
   const size_t head_v = (size_t)bh * L * DV;
@@ -186,10 +204,47 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
   const uint16_t* vh = static_cast<const uint16_t*>(a.v) + head_v + dv0;
   uint16_t* oh = static_cast<uint16_t*>(a.out) + head_v + dv0;
   const float* bws = CAT == kCatToken ? a.ws_b + (size_t)bh * L : nullptr;
-  const float lg = CAT == kCatHead ? logf(a.decay[h]) : 0.0f;
+  // per-head decay in log2 units: b_i = (i + 1) lg2 inside a chunk
+  const float lg2 = CAT == kCatHead ? log2f(a.decay[h]) : 0.0f;
 
   // state tiles of this wave: one value tile nt, key tiles mt = (wave + 4 t) / NTV
   const int nt_w = wave % G::NTV;
+  // the 8 tokens of this lane group in state-update k-step s2: k0(s2) + (0..7)
+  auto k0_of = [&](int s2) { return (C >= 32) ? 32 * s2 + 8 * g4 : (8 * g4) & 15; };
+
+  // ---- loop-invariant weights (no decay / per-head decay) --------------
+  // dm[j][jj][i]: mask and decay of query row r = 16 st + l16 against key
+  // c = 16 jj + 4 g4 + i, i.e. [c <= r] gamma^(r - c); er[j] = gamma^(r + 1)
+  // (the decay of the carried state seen by row r); vs[s2][e] = gamma^(C-1-t)
+  // for the update's tokens t; eLf = gamma^C.  Exponents are all >= 0, so no
+  // factor exceeds 1.
+  float dm[G::SPW][G::NSTRIP][4];
+  float er[G::SPW];
+  float vs[G::CSTEPS][8];
+  float eLf = 1.0f;
+  if constexpr (CAT != kCatToken) {
+#pragma unroll
+    for (int j = 0; j < G::SPW; ++j) {
+      const int r = 16 * (wave + 4 * j) + l16;
+      er[j] = CAT == kCatHead ? __builtin_amdgcn_exp2f((float)(r + 1) * lg2) : 1.0f;
+#pragma unroll
+      for (int jj = 0; jj < G::NSTRIP; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cc = 16 * jj + 4 * g4 + i;
+          const float w = CAT == kCatHead ? __builtin_amdgcn_exp2f((float)(r - cc) * lg2) : 1.0f;
+          dm[j][jj][i] = cc <= r ? w : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < G::CSTEPS; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vs[s2][e] = CAT == kCatHead
+                        ? __builtin_amdgcn_exp2f((float)max(C - 1 - (k0_of(s2) + e), 0) * lg2)
+                        : 1.0f;
+    if (CAT == kCatHead) eLf = __builtin_amdgcn_exp2f((float)C * lg2);
+  }
 
   // ---- initial state of this unit --------------------------------------
   f32x4 accS[G::TPW];
@@ -208,44 +263,65 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
           float s = a.state ? a.state[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
           for (int p = 0; p < sigma; ++p) {
             const size_t seg = (size_t)bh * a.P + p;
-            s = expf(a.ws_logA[seg]) * s + a.ws_S[(seg * DK + dk) * DV + dv];
+            s = exp2f(a.ws_logA[seg]) * s + a.ws_S[(seg * DK + dk) * DV + dv];
           }
           accS[t][i] = s;
         }
         u32x2 w;
         w[0] = cvt2(accS[t][0], accS[t][1]);
         w[1] = cvt2(accS[t][2], accS[t][3]);
-        *reinterpret_cast<u32x2*>(&sST[0][swz<G::WCK>(16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
+        *reinterpret_cast<u32x2*>(&sST0[swz<G::WCK>(16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
       }
     }
   }
 
   // ---- loads of one chunk: K, V tiles and b into LDS, Q into registers ----
+  constexpr int KBLK = (G::NK_CHUNKS + 255) / 256;  // 64-chunk blocks per wave
+  constexpr int VBLK = (G::NV_CHUNKS + 255) / 256;
+  // per-lane source offsets (elements) of the DMA blocks, relative to the chunk's first row
+  int koff[KBLK], krow[KBLK], voff[VBLK], vrow[VBLK];
+#pragma unroll
+  for (int i = 0; i < KBLK; ++i) {
+    const int q = 64 * (wave + 4 * i) + lane;
+    const int r = q / G::WCK, p = q % G::WCK;
+    const int cc = p ^ ((r / (G::WCK >= 16 ? 1 : 16 / G::WCK)) & (G::WCK - 1));
+    krow[i] = r;
+    koff[i] = r * DK + 8 * cc;
+  }
+#pragma unroll
+  for (int i = 0; i < VBLK; ++i) {
+    const int q = 64 * (wave + 4 * i) + lane;
+    const int r = q / G::WCV, p = q % G::WCV;
+    const int cc = p ^ ((r / (G::WCV >= 16 ? 1 : 16 / G::WCV)) & (G::WCV - 1));
+    vrow[i] = r;
+    voff[i] = r * DV + 8 * cc;
+  }
   u32x4 qnext[G::SPW][G::KSTEPS];
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
-  auto issue_loads = [&](int c, int buf) {
+  auto issue_loads = [&](auto BUF, int c) {
+    constexpr int buf = decltype(BUF)::value;
     const int t0 = c * C;
+    const bool full = t0 + C <= L;
+    const uint16_t* kc = kh + (size_t)t0 * DK;
+    const uint16_t* vc = vh + (size_t)t0 * DV;
 #pragma unroll
-    for (int i = 0; i < (G::NK_CHUNKS + 255) / 256; ++i) {
-      const int idx = wave + 4 * i;              // 64-chunk block of the tile
+    for (int i = 0; i < KBLK; ++i) {
+      const int idx = wave + 4 * i;
       const int q = 64 * idx + lane;
       if (64 * idx < G::NK_CHUNKS && q < G::NK_CHUNKS) {
-        const int r = q / G::WCK, p = q % G::WCK;
-        const int cc = p ^ ((r / (G::WCK >= 16 ? 1 : 16 / G::WCK)) & (G::WCK - 1));
-        const int t = min(t0 + r, L - 1);
-        dma16(kh + (size_t)t * DK + 8 * cc, &sK[buf][1024 * idx]);
+        // rows past the sequence re-read its last row; they are zeroed before use
+        const int off = full ? koff[i] : koff[i] - (max(krow[i] - (L - 1 - t0), 0)) * DK;
+        dma16(kc + off, stage_k(BUF) + 1024 * idx);
       }
     }
 #pragma unroll
-    for (int i = 0; i < (G::NV_CHUNKS + 255) / 256; ++i) {
+    for (int i = 0; i < VBLK; ++i) {
       const int idx = wave + 4 * i;
       const int q = 64 * idx + lane;
       if (64 * idx < G::NV_CHUNKS && q < G::NV_CHUNKS) {
-        const int r = q / G::WCV, p = q % G::WCV;
-        const int cc = p ^ ((r / (G::WCV >= 16 ? 1 : 16 / G::WCV)) & (G::WCV - 1));
-        const int t = min(t0 + r, L - 1);
-        dma16(vh + (size_t)t * DV + 8 * cc, &sV[buf][1024 * idx]);
+        const int off = full ? voff[i] : voff[i] - (max(vrow[i] - (L - 1 - t0), 0)) * DV;
+        dma16(vc + off, stage_v(BUF) + 1024 * idx);
       }
     }
     if constexpr (CAT == kCatToken) {
@@ -253,7 +329,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
       for (int i = 0; i < (C + 63) / 64; ++i) {
         if (wave == i && 64 * i + lane < C) {
           const int t = min(t0 + 64 * i + lane, L - 1);
-          dma4(bws + t, &sB[buf][64 * i]);
+          dma4(bws + t, stage_b(BUF) + 64 * i);
         }
       }
     }
@@ -264,25 +340,25 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
         const int t = t0 + 16 * st + l16;
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
+          // clamped in-bounds address; rows past the sequence and key columns
+          // past DK are zeroed where the registers are used (not here, which
+          // would wait for the load)
           const int col = 32 * s + 8 * g4;
-          qnext[j][s] = (st < G::NSTRIP && t < L && col < DK)
-                            ? *reinterpret_cast<const u32x4*>(qh + (size_t)t * DK + col)
-                            : zero4;
+          qnext[j][s] = *reinterpret_cast<const u32x4*>(qh + (size_t)min(t, L - 1) * DK + min(col, DK - 8));
         }
       }
     }
   };
 
   float logA = 0.0f;
-  issue_loads(c_begin, 0);
 
-  for (int c = c_begin; c < c_end; ++c) {
-    const int buf = (c - c_begin) & 1;
+  auto body = [&](auto BUF, int c) {
+    constexpr int buf = decltype(BUF)::value;
     const int t0 = c * C;
     const int nvalid = min(C, L - t0);
-    char* kb = sK[buf];
-    char* vb = sV[buf];
-    const float* sb = sB[buf];
+    char* kb = stage_k(BUF);
+    char* vb = stage_v(BUF);
+    const float* sb = stage_b(BUF);
 
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c have landed
     __syncthreads();                // ... and everybody's; chunk c-1 is finished
@@ -291,9 +367,26 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
 #pragma unroll
       for (int j = 0; j < G::SPW; ++j)
 #pragma unroll
-        for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = elu ? elu1_x8(qnext[j][s]) : qnext[j][s];
+        for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = qnext[j][s];
+      if (nvalid < C || DK < 32) {
+        no_speculation();
+#pragma unroll
+        for (int j = 0; j < G::SPW; ++j)
+#pragma unroll
+          for (int s = 0; s < G::KSTEPS; ++s) {
+            const bool ok = 16 * (wave + 4 * j) + l16 < nvalid && 32 * s + 8 * g4 < DK;
+            qcur[j][s] = ok ? qcur[j][s] : zero4;
+          }
+      }
+      if (elu) {
+        no_speculation();
+#pragma unroll
+        for (int j = 0; j < G::SPW; ++j)
+#pragma unroll
+          for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = elu1_x8(qcur[j][s]);
+      }
     }
-    if (c + 1 < c_end) issue_loads(c + 1, buf ^ 1);
+    if (c + 1 < c_end) issue_loads(std::integral_constant<int, buf ^ 1>{}, c + 1);
 
     // a short last chunk: zero the rows past the sequence (they hold clamped copies)
     if (nvalid < C) {
@@ -312,19 +405,16 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
       __syncthreads();
     }
 
-    // b_i of this chunk (inclusive prefix of log a; per-head decay in closed form)
-    auto bval = [&](int i) -> float {
-      if constexpr (CAT == kCatHead) return (float)(min(i, nvalid - 1) + 1) * lg;
-      else if constexpr (CAT == kCatToken) return sb[i];
-      else return 0.0f;
-    };
-    const float bL = bval(nvalid - 1);
+    // log2-decay of the chunk's last real token (the state's decay over the chunk)
+    float bL = 0.0f;
+    if constexpr (CAT == kCatHead) bL = (float)nvalid * lg2;
+    if constexpr (CAT == kCatToken) bL = sb[nvalid - 1];
 
     // (a) outputs of this chunk's query strips.  Every strip computes scores
     // against all key blocks; the causal mask zeroes the blocks past the
     // diagonal.  The slowest wave (the last strip) needs all of them anyway.
     if constexpr (!STATE_ONLY) {
-      const char* stc = sST[buf];
+      const char* stc = stage_s(BUF);
 #pragma unroll
       for (int j = 0; j < G::SPW; ++j) {
         const int st = wave + 4 * j;
@@ -374,16 +464,26 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
           }
           // pt[jj][i] = score of query row r against key 16 jj + 4 g4 + i: mask and decay
           const int r = 16 * st + l16;
-          const float br = bval(r);
+          float erow;
+          if constexpr (CAT == kCatToken) {
+            const float br = sb[r];
+            erow = __builtin_amdgcn_exp2f(br);
 #pragma unroll
-          for (int jj = 0; jj < G::NSTRIP; ++jj) {
+            for (int jj = 0; jj < G::NSTRIP; ++jj) {
+              const f32x4 bc = *reinterpret_cast<const f32x4*>(&sb[16 * jj + 4 * g4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int cc = 16 * jj + 4 * g4 + i;
-              float x = pt[jj][i];
-              if constexpr (decayed) x *= __expf(br - bval(cc));
-              pt[jj][i] = cc <= r ? x : 0.0f;
+              for (int i = 0; i < 4; ++i) {
+                const int cc = 16 * jj + 4 * g4 + i;
+                const float x = pt[jj][i] * __builtin_amdgcn_exp2f(br - bc[i]);
+                pt[jj][i] = cc <= r ? x : 0.0f;
+              }
             }
+          } else {
+            erow = er[j];
+#pragma unroll
+            for (int jj = 0; jj < G::NSTRIP; ++jj)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pt[jj][i] *= dm[j][jj][i];
           }
           u32x4 pb[G::CSTEPS];
 #pragma unroll
@@ -402,9 +502,10 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
           for (int s = 0; s < G::KSTEPS; ++s)
 #pragma unroll
             for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = mfma16x16x32(sA[mo][s], qcur[j][s], acc[mo]);
-          const float erow = decayed ? __expf(br) : 1.0f;
+          if constexpr (decayed) {
 #pragma unroll
-          for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = acc[mo] * erow;
+            for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = acc[mo] * erow;
+          }
 #pragma unroll
           for (int s2 = 0; s2 < G::CSTEPS; ++s2)
 #pragma unroll
@@ -427,20 +528,35 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
     // each 16-lane group); for a 16-token chunk the lane groups past the chunk
     // read rows 0..15 again and are zeroed afterwards.
     if (G::TPW > 1 || wave < G::NT_S) {
-      const float eL = decayed ? __expf(bL) : 1.0f;
-      char* stn = sST[buf ^ 1];
+      char* stn = stage_s(std::integral_constant<int, buf ^ 1>{});
       u32x4 vB[G::CSTEPS];
 #pragma unroll
       for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
-        const int k0 = (C >= 32) ? 32 * s2 + 8 * g4 : (8 * g4) & 15;
+        const int k0 = k0_of(s2);
         u32x4 w = lds_tr8<G::WCV>(vb, k0, k0 + 4, 16 * nt_w, l16);
         if constexpr (decayed) {
+          float sc[8];
+          if constexpr (CAT == kCatToken) {
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(&sb[k0]);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(&sb[k0 + 4]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {  // word e holds tokens k0 + 2e, k0 + 2e + 1
-            const int t_lo = k0 + 2 * e;
-            w[e] = cvt2(bf16_to_f32(w[e] & 0xffffu) * __expf(bL - bval(min(t_lo, C - 1))),
-                        bf16_to_f32(w[e] >> 16) * __expf(bL - bval(min(t_lo + 1, C - 1))));
+            for (int e = 0; e < 4; ++e) {
+              sc[e] = __builtin_amdgcn_exp2f(bL - b0[e]);
+              sc[4 + e] = __builtin_amdgcn_exp2f(bL - b1[e]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc[e] = vs[s2][e];
+            if (nvalid < C) {  // the short last chunk decays from its last real token
+              no_speculation();
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                sc[e] = __builtin_amdgcn_exp2f((float)max(nvalid - 1 - (k0 + e), 0) * lg2);
+            }
           }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)  // word e holds tokens k0 + 2e, k0 + 2e + 1
+            w[e] = cvt2(bf16_to_f32(w[e] & 0xffffu) * sc[2 * e], bf16_to_f32(w[e] >> 16) * sc[2 * e + 1]);
         }
         vB[s2] = (C < 32 && g4 >= 2) ? zero4 : w;
       }
@@ -450,13 +566,20 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
         const int mt = min((wave + 4 * t) / G::NTV, G::NMK - 1);
 #pragma unroll
         for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
-          const int k0 = (C >= 32) ? 32 * s2 + 8 * g4 : (8 * g4) & 15;
+          const int k0 = k0_of(s2);
           const u32x4 w = lds_tr8<G::WCK>(kb, k0, k0 + 4, 16 * mt, l16);
           kA2[t][s2] = (C < 32 && g4 >= 2) ? zero4 : w;
         }
       }
+      if constexpr (decayed) {
+        float eL = eLf;
+        if (CAT == kCatToken || nvalid < C) {
+          no_speculation();
+          eL = __builtin_amdgcn_exp2f(bL);
+        }
 #pragma unroll
-      for (int t = 0; t < G::TPW; ++t) accS[t] = accS[t] * eL;
+        for (int t = 0; t < G::TPW; ++t) accS[t] = accS[t] * eL;
+      }
 #pragma unroll
       for (int s2 = 0; s2 < G::CSTEPS; ++s2)
 #pragma unroll
@@ -476,6 +599,12 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
       }
     }
     logA += bL;
+  };
+
+  issue_loads(std::integral_constant<int, 0>{}, c_begin);
+  for (int c = c_begin; c < c_end; c += 2) {
+    body(std::integral_constant<int, 0>{}, c);
+    if (c + 1 < c_end) body(std::integral_constant<int, 1>{}, c + 1);
   }
 
   // ---- epilogue ---------------------------------------------------------

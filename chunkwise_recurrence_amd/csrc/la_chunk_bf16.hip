@@ -4,9 +4,10 @@
 namespace la {
 namespace {
 
-// b_t = sum of log a over the tokens of t's chunk up to and including t, for
-// the token-dependent decays; one wave per chunk, one wave64 inclusive scan
-// (two tokens per lane, chunks of at most 128 tokens).
+// b_t = log2(e) * (sum of log a over the tokens of t's chunk up to and
+// including t), for the token-dependent decays (the kernels work in log2
+// units so that every decay factor is one v_exp_f32); one wave per chunk, one
+// wave64 inclusive scan (two tokens per lane, chunks of at most 128 tokens).
 __global__ __launch_bounds__(256) void decay_prefix_kernel(const ChunkArgs a, int total_chunks) {
   const int lane = threadIdx.x & 63;
   const int gid = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -18,8 +19,9 @@ __global__ __launch_bounds__(256) void decay_prefix_kernel(const ChunkArgs a, in
   const float* in = a.decay + (size_t)bh * a.L;
   float* out = a.ws_b + (size_t)bh * a.L;
   const bool v0 = i0 < a.C && t0 + i0 < a.L, v1 = i1 < a.C && t0 + i1 < a.L;
-  const float x0 = v0 ? token_log_decay(a.decay_kind, in[t0 + i0]) : 0.0f;
-  const float x1 = v1 ? token_log_decay(a.decay_kind, in[t0 + i1]) : 0.0f;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float x0 = v0 ? token_log_decay(a.decay_kind, in[t0 + i0]) * kLog2e : 0.0f;
+  const float x1 = v1 ? token_log_decay(a.decay_kind, in[t0 + i1]) * kLog2e : 0.0f;
   float s = x0 + x1;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
