@@ -82,9 +82,9 @@ def bench_chunk(la, torch, W, steps, warmup):
     torch.cuda.synchronize()
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
     by, flops = chunk_algorithmic(w, with_state=True)
-    tv, P = la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)
-    return dict(w=w, ms_step=ms_step, wall=wall, kern_ms=kern_ms, bytes=by, flops=flops, tv=tv,
-                P=P, need=need)
+    tile, P, groups = la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)
+    return dict(w=w, ms_step=ms_step, wall=wall, kern_ms=kern_ms, bytes=by, flops=flops, tile=tile,
+                P=P, groups=groups, need=need)
 
 
 def bench_decode(la, torch, W, steps):
@@ -196,7 +196,7 @@ def main():
         "config": {"workload": "retnet_bf16", "B": w.B, "H": w.H, "L": w.L, "d_k": w.dk,
                    "d_v": w.dv, "C": w.C, "decay": "per-head gamma = linspace(0.9, 0.999, 32)",
                    "inputs": "q,k,v ~ N(0,1)/sqrt(128) in bf16",
-                   "plan": {"dv_tile": c["tv"], "segments": c["P"]}},
+                   "plan": {"dv_tile": c["tile"], "segments": c["P"], "column_groups": c["groups"]}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel_ms": c["kern_ms"], "algorithmic_bytes": c["bytes"],

@@ -57,9 +57,9 @@ def load():
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i]
     lib.la_chunk_fwd_plan.restype = i
-    lib.la_chunk_fwd_plan.argtypes = [i] * 7 + [ctypes.POINTER(ctypes.c_int)] * 2
+    lib.la_chunk_fwd_plan.argtypes = [i] * 7 + [ctypes.POINTER(ctypes.c_int)] * 3
     lib.la_set_plan.restype = i
-    lib.la_set_plan.argtypes = [i, i]
+    lib.la_set_plan.argtypes = [i, i, i]
     _lib = lib
     return lib
 
@@ -103,16 +103,16 @@ def _check(status: int, where: str):
 
 
 def plan(B: int, H: int, L: int, dk: int, dv: int, C: int, dtype: int = LA_BF16):
-    """(value-tile width, segments per head) that la_chunk_fwd will use."""
-    tv, p = ctypes.c_int(0), ctypes.c_int(0)
-    _check(load().la_chunk_fwd_plan(B, H, L, dk, dv, C, dtype, ctypes.byref(tv), ctypes.byref(p)),
-           "la_chunk_fwd_plan")
-    return tv.value, p.value
+    """(value columns per workgroup, segments per head, column groups) la_chunk_fwd will use."""
+    tv, p, g = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().la_chunk_fwd_plan(B, H, L, dk, dv, C, dtype, ctypes.byref(tv), ctypes.byref(p),
+                                    ctypes.byref(g)), "la_chunk_fwd_plan")
+    return tv.value, p.value, g.value
 
 
-def set_plan(dv_tile: int = 0, segments: int = 0):
+def set_plan(dv_tile: int = 0, segments: int = 0, groups: int = 0):
     """Override the bf16 launch plan process-wide (0 = automatic)."""
-    _check(load().la_set_plan(int(dv_tile), int(segments)), "la_set_plan")
+    _check(load().la_set_plan(int(dv_tile), int(segments), int(groups)), "la_set_plan")
 
 
 def chunk_fwd_workspace_bytes(B: int, H: int, L: int, dk: int, dv: int, C: int,

@@ -13,20 +13,21 @@ namespace {
 
 // Workgroups the bf16 plan aims for: one per compute unit of an MI355X.
 constexpr int kTargetWorkgroups = 256;
-// Widest value tile of one bf16 workgroup.
-constexpr int kMaxTile = 64;
 // A segment of the sequence keeps at least this many chunks.
 constexpr int kMinSegmentChunks = 4;
 
-std::atomic<int> g_plan_tv{0};
+std::atomic<int> g_plan_tile{0};
 std::atomic<int> g_plan_segments{0};
+std::atomic<int> g_plan_groups{0};
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 struct Plan {
-  int tv = 0;        // value-tile width of one workgroup (bf16 path)
+  int tile = 0;      // value columns of one workgroup
+  int ng = 1;        // column groups (of 4 waves) per workgroup (bf16 path)
+  int tv = 0;        // value columns per column group
   int P = 1;         // sequence segments per head
   int seg_chunks = 0;
   size_t ws_bytes = 0;
@@ -35,6 +36,10 @@ struct Plan {
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool t_fits(int d_k, int tile, int ng, int C) {
+  return tile % ng == 0 && la::chunk_bf16_supported(d_k, tile / ng, ng, C);
+}
 
 la_status check_chunk_shape(int dtype, int B, int H, int L, int d_k, int d_v, int C) {
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
@@ -48,25 +53,34 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   const int heads = B * H;
   const int nchunks = L > 0 ? (L + C - 1) / C : 0;
   if (dtype == LA_F32) {
-    p.tv = d_v < 32 ? d_v : 32;
+    p.tile = p.tv = d_v < 32 ? d_v : 32;
+    p.ng = 1;
     p.P = 1;
     p.seg_chunks = nchunks;
     return p;
   }
-  // value tile: the widest (at most 64) that still gives enough workgroups, not below 32
-  int tv = d_v < kMaxTile ? d_v : kMaxTile;
-  while ((long long)heads * (d_v / tv) < kTargetWorkgroups && tv > 32) tv /= 2;
-  const int forced_tv = g_plan_tv.load();
-  if (forced_tv > 0) {
-    tv = forced_tv;
-    while (tv > d_v || tv > kMaxTile) tv /= 2;
+  // One 4-wave workgroup per (head, 64-column value tile, sequence segment);
+  // the sequence is split into segments until the chip has a workgroup per
+  // compute unit.  Wider workgroups (two column groups of 4 waves) can be
+  // asked for with la_set_plan.
+  int tile = d_v < 64 ? d_v : 64;
+  const int forced_tile = g_plan_tile.load(), forced_groups = g_plan_groups.load();
+  if (forced_tile > 0) {
+    tile = forced_tile;
+    while (tile > d_v) tile /= 2;
   }
-  while (tv > 16 && !la::chunk_bf16_supported(d_k, tv, C)) tv /= 2;
-  p.tv = tv;
-  // sequence segments: split further only while workgroups are short and every
-  // segment keeps a few chunks
+  auto groups_for = [&](int t) {
+    int g = forced_groups > 0 ? forced_groups : 1;
+    if (t / g < 16) g = 1;
+    return g;
+  };
+  // the widest layout that has a kernel and fits the LDS
+  while (tile > 16 && !(t_fits(d_k, tile, groups_for(tile), C))) tile /= 2;
+  p.tile = tile;
+  p.ng = groups_for(tile);
+  p.tv = tile / p.ng;
   int P = 1;
-  const long long units = (long long)heads * (d_v / tv);
+  const long long units = (long long)heads * (d_v / tile);
   while (units * P < kTargetWorkgroups && (long long)P * 2 * kMinSegmentChunks <= nchunks) P *= 2;
   const int forced_P = g_plan_segments.load();
   if (forced_P > 0) P = forced_P;
@@ -108,21 +122,24 @@ const char* la_status_string(int s) {
   return "unknown la_status";
 }
 
-la_status la_set_plan(int dv_tile, int segments) {
+la_status la_set_plan(int dv_tile, int segments, int groups) {
   if (dv_tile != 0 && !dim_ok(dv_tile)) return LA_ERR_UNSUPPORTED;
+  if (groups != 0 && groups != 1 && groups != 2) return LA_ERR_UNSUPPORTED;
   if (segments < 0) return LA_ERR_SHAPE;
-  g_plan_tv.store(dv_tile);
+  g_plan_tile.store(dv_tile);
   g_plan_segments.store(segments);
+  g_plan_groups.store(groups);
   return LA_OK;
 }
 
 la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int* dv_tile,
-                            int* segments) {
+                            int* segments, int* groups) {
   const la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
   if (st != LA_OK) return st;
   const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, LA_DECAY_NONE);
-  if (dv_tile) *dv_tile = p.tv;
+  if (dv_tile) *dv_tile = p.tile;
   if (segments) *segments = p.P;
+  if (groups) *groups = p.ng;
   return LA_OK;
 }
 
@@ -178,7 +195,8 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
   a.phi = phi;
   a.decay_kind = decay_kind;
   a.tv = p.tv;
-  a.n_v = d_v / p.tv;
+  a.ng = p.ng;
+  a.n_v = d_v / p.tile;
   a.P = p.P;
   a.seg_chunks = p.seg_chunks;
   const hipStream_t s = as_stream(stream);

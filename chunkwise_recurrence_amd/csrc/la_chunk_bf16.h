@@ -59,26 +59,49 @@ namespace bf16k {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int DK, int TV, int C>
+// Geometry of one kernel instance: key dim DK, value columns per column group
+// TV, chunk C, NG column groups of 4 waves each (the workgroup covers NG*TV
+// value columns with 4*NG waves).
+template <int DK, int TV, int C, int NG>
 struct Geo {
+  static constexpr int NW = 4 * NG;                // waves per workgroup
+  static constexpr int TVW = NG * TV;              // value columns per workgroup
   static constexpr int CP = C < 32 ? 32 : C;       // chunk padded to whole MFMA k-steps
   static constexpr int KSTEPS = DK < 32 ? 1 : DK / 32;  // k-steps over the key dim
   static constexpr int CSTEPS = CP / 32;           // k-steps over the chunk's tokens
   static constexpr int WCK = DK / 8;               // 16-byte chunks per K row
-  static constexpr int WCV = TV / 8;               // 16-byte chunks per V row
+  static constexpr int WCV = TVW / 8;              // 16-byte chunks per V row (all groups)
   static constexpr int NSTRIP = C / 16;            // 16-row query strips per chunk
   static constexpr int SPW = (NSTRIP + 3) / 4;     // strips per wave
-  static constexpr int NTV = TV / 16;              // 16-wide value tiles
+  static constexpr int NTV = TV / 16;              // 16-wide value tiles per group
   static constexpr int NMK = DK / 16;              // 16-wide key tiles
-  static constexpr int NT_S = NMK * NTV;           // 16x16 tiles of the state
+  static constexpr int NT_S = NMK * NTV;           // 16x16 state tiles per group
   static constexpr int TPW = (NT_S + 3) / 4;       // state tiles per wave
   static constexpr int K_TILE = C * DK;            // elements of one K tile
-  static constexpr int V_TILE = C * TV;
-  static constexpr int S_TILE = TV * DK;
+  static constexpr int V_TILE = C * TVW;
+  static constexpr int S_TILE = TVW * DK;          // S^T of all groups
   static constexpr int NK_CHUNKS = C * WCK;        // 16-byte chunks of one K tile
   static constexpr int NV_CHUNKS = C * WCV;
-  static constexpr size_t LDS_MAIN = 2 * (2 * (size_t)K_TILE + 2 * (size_t)V_TILE +
-                                          2 * (size_t)S_TILE) + 2 * 4 * (size_t)CP;
+  // 1 KB DMA blocks (64 lanes x 16 B) per wave; the last block may be partial
+  static constexpr int KBLK = ((NK_CHUNKS + 63) / 64 + NW - 1) / NW;
+  static constexpr int VBLK = ((NV_CHUNKS + 63) / 64 + NW - 1) / NW;
+  // Every wave issues the same number of memory instructions per chunk (all
+  // waves own query strips and equal shares of the K and V tiles): then the
+  // wait at the top of a chunk can count instructions and keep later chunks'
+  // loads in flight.
+  static constexpr bool UNIFORM = NK_CHUNKS % (64 * NW) == 0 && NV_CHUNKS % (64 * NW) == 0 &&
+                                  NSTRIP % 4 == 0 && C % NW == 0;
+  static constexpr size_t stage_bytes(int n) {
+    return (size_t)n * (2 * (size_t)K_TILE + 2 * (size_t)V_TILE + 4 * (size_t)CP) +
+           2 * 2 * (size_t)S_TILE;
+  }
+  // pipeline depth: three stages (loads two chunks ahead) where they fit
+  static constexpr int NSTG = (UNIFORM && stage_bytes(3) <= 160 * 1024) ? 3 : 2;
+  static constexpr size_t LDS_MAIN = stage_bytes(NSTG);
+  // precomputed per-lane mask/decay weights only while they stay small
+  static constexpr bool DM_REGS = NSTRIP <= 4;
+  // operands of a whole strip preloaded (more ILP) only in the narrow layout
+  static constexpr bool PRELOAD = NG == 1 && NSTRIP <= 4;
 };
 
 constexpr size_t kMaxLds = 160 * 1024;
@@ -154,14 +177,25 @@ __device__ __forceinline__ void dma4(const void* src, void* dst) {
 // prefix sums from the prefix pass).
 enum { kCatNone = 0, kCatHead = 1, kCatToken = 2 };
 
-template <int DK, int TV, int C, int CAT, bool STATE_ONLY>
-__global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
-  using G = Geo<DK, TV, C>;
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt left
+// at their maxima): at most n vector memory instructions may be outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int DK, int TV, int C, int NG, int CAT, bool STATE_ONLY>
+__global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a) {
+  using G = Geo<DK, TV, C, NG>;
   static_assert(G::NTV <= 4, "a wave's state tiles must share one value tile");
+  constexpr int NS = G::NSTG;
+  constexpr int NW = G::NW;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __builtin_assume(wave >= 0 && wave < 4);
+  __builtin_assume(wave >= 0 && wave < NW);
+  const int grp = wave >> 2, wl = wave & 3;  // column group, wave within the group
   const int l16 = lane & 15, g4 = lane >> 4;
 
   // workgroup -> (unit, value tile); the tiles of one unit share an XCD
@@ -173,7 +207,8 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
   const int segs = STATE_ONLY ? a.P - 1 : a.P;
   const int bh = u / segs, sigma = u % segs;
   const int h = bh % a.H;
-  const int dv0 = vt * TV;
+  const int dv0 = vt * G::TVW;             // first value column of the workgroup
+  const int dvg = dv0 + grp * TV;          // ... of this wave's column group
   const int L = a.L, DV = a.DV;
   const int nchunks = (L + C - 1) / C;
   const int c_begin = sigma * a.seg_chunks;
@@ -181,34 +216,41 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
   constexpr bool decayed = CAT != kCatNone;
   const bool elu = a.phi == kPhiElu1;
 
-  // Separate arrays per pipeline stage (not one [2][...] array): the DMA into
-  // one stage and the reads of the other are then provably disjoint, so the
+  // One array per pipeline stage (not one [NS][...] array): the DMA into one
+  // stage and the reads of another are then provably disjoint, so the
   // compiler does not wait for the prefetch before touching LDS.
-  __shared__ __align__(16) char sK0[G::K_TILE * 2], sK1[G::K_TILE * 2];
-  __shared__ __align__(16) char sV0[G::V_TILE * 2], sV1[G::V_TILE * 2];
-  __shared__ __align__(16) char sST0[STATE_ONLY ? 16 : G::S_TILE * 2];
-  __shared__ __align__(16) char sST1[STATE_ONLY ? 16 : G::S_TILE * 2];
-  __shared__ __align__(16) float sB0[CAT == kCatToken ? G::CP : 4];
-  __shared__ __align__(16) float sB1[CAT == kCatToken ? G::CP : 4];
-  auto stage_k = [&](auto BUF) -> char* { if constexpr (decltype(BUF)::value == 0) return sK0; else return sK1; };
-  auto stage_v = [&](auto BUF) -> char* { if constexpr (decltype(BUF)::value == 0) return sV0; else return sV1; };
-  auto stage_s = [&](auto BUF) -> char* { if constexpr (decltype(BUF)::value == 0) return sST0; else return sST1; };
-  auto stage_b = [&](auto BUF) -> float* { if constexpr (decltype(BUF)::value == 0) return sB0; else return sB1; };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
+  constexpr int KB = G::K_TILE * 2, VB = G::V_TILE * 2, BB = CAT == kCatToken ? G::CP : 4;
+  __shared__ __align__(16) char sK0[KB], sK1[KB], sK2[NS > 2 ? KB : 16];
+  __shared__ __align__(16) char sV0[VB], sV1[VB], sV2[NS > 2 ? VB : 16];
+  __shared__ __align__(16) float sB0[BB], sB1[BB], sB2[NS > 2 ? BB : 4];
+  __shared__ __align__(16) char sST[2][STATE_ONLY ? 16 : G::S_TILE * 2];
+  auto stage_k = [&](auto BUF) -> char* {
+    constexpr int b = decltype(BUF)::value;
+    if constexpr (b == 0) return sK0; else if constexpr (b == 1) return sK1; else return sK2;
+  };
+  auto stage_v = [&](auto BUF) -> char* {
+    constexpr int b = decltype(BUF)::value;
+    if constexpr (b == 0) return sV0; else if constexpr (b == 1) return sV1; else return sV2;
+  };
+  auto stage_b = [&](auto BUF) -> float* {
+    constexpr int b = decltype(BUF)::value;
+    if constexpr (b == 0) return sB0; else if constexpr (b == 1) return sB1; else return sB2;
+  };
 
   const size_t head_k = (size_t)bh * L * DK;
   const size_t head_v = (size_t)bh * L * DV;
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + head_k;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + head_k;
   const uint16_t* vh = static_cast<const uint16_t*>(a.v) + head_v + dv0;
-  uint16_t* oh = static_cast<uint16_t*>(a.out) + head_v + dv0;
+  uint16_t* og = static_cast<uint16_t*>(a.out) + head_v + dvg;
   const float* bws = CAT == kCatToken ? a.ws_b + (size_t)bh * L : nullptr;
   // per-head decay in log2 units: b_i = (i + 1) lg2 inside a chunk
   const float lg2 = CAT == kCatHead ? log2f(a.decay[h]) : 0.0f;
 
-  // state tiles of this wave: one value tile nt, key tiles mt = (wave + 4 t) / NTV
-  const int nt_w = wave % G::NTV;
+  // state tiles of this wave: one value tile nt, key tiles mt = (wl + 4 t) / NTV
+  const int nt_w = wl % G::NTV;
+  // rows of S^T (one per value column of the workgroup) owned by this group start here
+  const int srow0 = grp * TV;
   // the 8 tokens of this lane group in state-update k-step s2: k0(s2) + (0..7)
   auto k0_of = [&](int s2) { return (C >= 32) ? 32 * s2 + 8 * g4 : (8 * g4) & 15; };
 
@@ -218,23 +260,25 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
   // (the decay of the carried state seen by row r); vs[s2][e] = gamma^(C-1-t)
   // for the update's tokens t; eLf = gamma^C.  Exponents are all >= 0, so no
   // factor exceeds 1.
-  float dm[G::SPW][G::NSTRIP][4];
+  float dm[G::DM_REGS ? G::SPW : 1][G::DM_REGS ? G::NSTRIP : 1][4];
   float er[G::SPW];
   float vs[G::CSTEPS][8];
   float eLf = 1.0f;
   if constexpr (CAT != kCatToken) {
 #pragma unroll
     for (int j = 0; j < G::SPW; ++j) {
-      const int r = 16 * (wave + 4 * j) + l16;
+      const int r = 16 * (wl + 4 * j) + l16;
       er[j] = CAT == kCatHead ? __builtin_amdgcn_exp2f((float)(r + 1) * lg2) : 1.0f;
+      if constexpr (G::DM_REGS) {
 #pragma unroll
-      for (int jj = 0; jj < G::NSTRIP; ++jj)
+        for (int jj = 0; jj < G::NSTRIP; ++jj)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int cc = 16 * jj + 4 * g4 + i;
-          const float w = CAT == kCatHead ? __builtin_amdgcn_exp2f((float)(r - cc) * lg2) : 1.0f;
-          dm[j][jj][i] = cc <= r ? w : 0.0f;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int cc = 16 * jj + 4 * g4 + i;
+            const float w = CAT == kCatHead ? __builtin_amdgcn_exp2f((float)(r - cc) * lg2) : 1.0f;
+            dm[j][jj][i] = cc <= r ? w : 0.0f;
+          }
+      }
     }
 #pragma unroll
     for (int s2 = 0; s2 < G::CSTEPS; ++s2)
@@ -253,10 +297,10 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
   if constexpr (!STATE_ONLY) {
 #pragma unroll
     for (int t = 0; t < G::TPW; ++t) {
-      const int tau = wave + 4 * t;
+      const int tau = wl + 4 * t;
       if (tau < G::NT_S) {
         const int mt = tau / G::NTV;
-        const int dv = dv0 + 16 * nt_w + l16;
+        const int dv = dvg + 16 * nt_w + l16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int dk = 16 * mt + 4 * g4 + i;
@@ -270,19 +314,18 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
         u32x2 w;
         w[0] = cvt2(accS[t][0], accS[t][1]);
         w[1] = cvt2(accS[t][2], accS[t][3]);
-        *reinterpret_cast<u32x2*>(&sST0[swz<G::WCK>(16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
+        *reinterpret_cast<u32x2*>(&sST[0][swz<G::WCK>(srow0 + 16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
       }
     }
   }
 
   // ---- loads of one chunk: K, V tiles and b into LDS, Q into registers ----
-  constexpr int KBLK = (G::NK_CHUNKS + 255) / 256;  // 64-chunk blocks per wave
-  constexpr int VBLK = (G::NV_CHUNKS + 255) / 256;
+  constexpr int KBLK = G::KBLK, VBLK = G::VBLK;
   // per-lane source offsets (elements) of the DMA blocks, relative to the chunk's first row
   int koff[KBLK], krow[KBLK], voff[VBLK], vrow[VBLK];
 #pragma unroll
   for (int i = 0; i < KBLK; ++i) {
-    const int q = 64 * (wave + 4 * i) + lane;
+    const int q = 64 * (wave + NW * i) + lane;
     const int r = q / G::WCK, p = q % G::WCK;
     const int cc = p ^ ((r / (G::WCK >= 16 ? 1 : 16 / G::WCK)) & (G::WCK - 1));
     krow[i] = r;
@@ -290,14 +333,20 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < VBLK; ++i) {
-    const int q = 64 * (wave + 4 * i) + lane;
+    const int q = 64 * (wave + NW * i) + lane;
     const int r = q / G::WCV, p = q % G::WCV;
     const int cc = p ^ ((r / (G::WCV >= 16 ? 1 : 16 / G::WCV)) & (G::WCV - 1));
     vrow[i] = r;
     voff[i] = r * DV + 8 * cc;
   }
-  u32x4 qnext[G::SPW][G::KSTEPS];
+  // Q of each stage, in registers
+  u32x4 qst[NS][G::SPW][G::KSTEPS];
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+
+  // Vector memory instructions one chunk's loads and stores issue per wave
+  // (meaningful when G::UNIFORM).
+  constexpr int LOADS = KBLK + VBLK + (CAT == kCatToken ? 1 : 0) + (STATE_ONLY ? 0 : G::SPW * G::KSTEPS);
+  constexpr int STORES = STATE_ONLY ? 0 : G::SPW * G::NTV;
 
   auto issue_loads = [&](auto BUF, int c) {
     constexpr int buf = decltype(BUF)::value;
@@ -307,7 +356,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
     const uint16_t* vc = vh + (size_t)t0 * DV;
 #pragma unroll
     for (int i = 0; i < KBLK; ++i) {
-      const int idx = wave + 4 * i;
+      const int idx = wave + NW * i;
       const int q = 64 * idx + lane;
       if (64 * idx < G::NK_CHUNKS && q < G::NK_CHUNKS) {
         // rows past the sequence re-read its last row; they are zeroed before use
@@ -317,7 +366,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < VBLK; ++i) {
-      const int idx = wave + 4 * i;
+      const int idx = wave + NW * i;
       const int q = 64 * idx + lane;
       if (64 * idx < G::NV_CHUNKS && q < G::NV_CHUNKS) {
         const int off = full ? voff[i] : voff[i] - (max(vrow[i] - (L - 1 - t0), 0)) * DV;
@@ -325,18 +374,17 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
       }
     }
     if constexpr (CAT == kCatToken) {
-#pragma unroll
-      for (int i = 0; i < (C + 63) / 64; ++i) {
-        if (wave == i && 64 * i + lane < C) {
-          const int t = min(t0 + 64 * i + lane, L - 1);
-          dma4(bws + t, stage_b(BUF) + 64 * i);
-        }
+      // each wave brings its share of the chunk's prefix sums
+      constexpr int PER = (C + NW - 1) / NW;
+      if (lane < PER && wave * PER + lane < C) {
+        const int t = min(t0 + wave * PER + lane, L - 1);
+        dma4(bws + t, stage_b(BUF) + wave * PER);
       }
     }
     if constexpr (!STATE_ONLY) {
 #pragma unroll
       for (int j = 0; j < G::SPW; ++j) {
-        const int st = wave + 4 * j;
+        const int st = wl + 4 * j;
         const int t = t0 + 16 * st + l16;
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
@@ -344,7 +392,8 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
           // past DK are zeroed where the registers are used (not here, which
           // would wait for the load)
           const int col = 32 * s + 8 * g4;
-          qnext[j][s] = *reinterpret_cast<const u32x4*>(qh + (size_t)min(t, L - 1) * DK + min(col, DK - 8));
+          qst[buf][j][s] =
+              *reinterpret_cast<const u32x4*>(qh + (size_t)min(t, L - 1) * DK + min(col, DK - 8));
         }
       }
     }
@@ -359,22 +408,39 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
     char* kb = stage_k(BUF);
     char* vb = stage_v(BUF);
     const float* sb = stage_b(BUF);
+    const int sp = (c - c_begin) & 1;  // S^T double buffer: read sp, write sp ^ 1
 
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk c have landed
-    __syncthreads();                // ... and everybody's; chunk c-1 is finished
+    // Wait until this wave's loads of chunk c have landed, keeping the loads
+    // of later chunks (and the stores issued since) in flight: in issue order,
+    // chunk c's loads are followed by nS chunks' stores and nL chunks' loads.
+    if constexpr (G::UNIFORM && NS == 3) {
+      const int nS = min(NS - 1, c - c_begin), nL = min(NS - 2, c_end - 1 - c);
+      if (nS == 2 && nL == 1) wait_vmcnt<2 * STORES + LOADS>();
+      else if (nS == 2) wait_vmcnt<2 * STORES>();
+      else if (nS == 1 && nL == 1) wait_vmcnt<STORES + LOADS>();
+      else if (nS == 1) wait_vmcnt<STORES>();
+      else if (nL == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    } else if constexpr (G::UNIFORM) {
+      if (c > c_begin) wait_vmcnt<STORES>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();  // everybody's loads of chunk c landed; chunk c-1 is finished
     u32x4 qcur[G::SPW][G::KSTEPS];
     if constexpr (!STATE_ONLY) {
 #pragma unroll
       for (int j = 0; j < G::SPW; ++j)
 #pragma unroll
-        for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = qnext[j][s];
+        for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = qst[buf][j][s];
       if (nvalid < C || DK < 32) {
         no_speculation();
 #pragma unroll
         for (int j = 0; j < G::SPW; ++j)
 #pragma unroll
           for (int s = 0; s < G::KSTEPS; ++s) {
-            const bool ok = 16 * (wave + 4 * j) + l16 < nvalid && 32 * s + 8 * g4 < DK;
+            const bool ok = 16 * (wl + 4 * j) + l16 < nvalid && 32 * s + 8 * g4 < DK;
             qcur[j][s] = ok ? qcur[j][s] : zero4;
           }
       }
@@ -386,19 +452,19 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
           for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = elu1_x8(qcur[j][s]);
       }
     }
-    if (c + 1 < c_end) issue_loads(std::integral_constant<int, buf ^ 1>{}, c + 1);
+    if (c + NS - 1 < c_end) issue_loads(std::integral_constant<int, (buf + NS - 1) % NS>{}, c + NS - 1);
 
     // a short last chunk: zero the rows past the sequence (they hold clamped copies)
     if (nvalid < C) {
-      for (int q = tid; q < (C - nvalid) * G::WCK; q += 256)
+      for (int q = tid; q < (C - nvalid) * G::WCK; q += 64 * NW)
         *reinterpret_cast<u32x4*>(kb + 16 * (nvalid * G::WCK + q)) = zero4;
-      for (int q = tid; q < (C - nvalid) * G::WCV; q += 256)
+      for (int q = tid; q < (C - nvalid) * G::WCV; q += 64 * NW)
         *reinterpret_cast<u32x4*>(vb + 16 * (nvalid * G::WCV + q)) = zero4;
       __syncthreads();
     }
     // feature map on the staged keys, in place
     if (elu) {
-      for (int q = tid; q < G::NK_CHUNKS; q += 256) {
+      for (int q = tid; q < G::NK_CHUNKS; q += 64 * NW) {
         u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
         *p = elu1_x8(*p);
       }
@@ -414,52 +480,41 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
     // against all key blocks; the causal mask zeroes the blocks past the
     // diagonal.  The slowest wave (the last strip) needs all of them anyway.
     if constexpr (!STATE_ONLY) {
-      const char* stc = stage_s(BUF);
+      const char* stc = sST[sp];
 #pragma unroll
       for (int j = 0; j < G::SPW; ++j) {
-        const int st = wave + 4 * j;
+        const int st = wl + 4 * j;
         if (G::NSTRIP >= 4 * (j + 1) || st < G::NSTRIP) {
-          // all K operands of the strip's scores, then the MFMAs interleaved over key blocks
-          u32x4 kA[G::NSTRIP][G::KSTEPS];
-#pragma unroll
-          for (int jj = 0; jj < G::NSTRIP; ++jj)
-#pragma unroll
-            for (int s = 0; s < G::KSTEPS; ++s)
-              kA[jj][s] = (DK >= 32 || g4 < 2)
-                              ? lds_b128(kb, swz<G::WCK>(16 * jj + l16, 32 * s + 8 * g4))
-                              : zero4;
           f32x4 pt[G::NSTRIP];
 #pragma unroll
           for (int jj = 0; jj < G::NSTRIP; ++jj) pt[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < G::KSTEPS; ++s)
+          if constexpr (G::PRELOAD) {
+            // all K operands of the strip's scores, then the MFMAs interleaved over key blocks
+            u32x4 kA[G::NSTRIP][G::KSTEPS];
 #pragma unroll
             for (int jj = 0; jj < G::NSTRIP; ++jj)
-              pt[jj] = mfma16x16x32(kA[jj][s], qcur[j][s], pt[jj]);
-          // operands of the inter- and intra-chunk products
-          u32x4 sA[G::NTV][G::KSTEPS];
-          u32x4 vA[G::NTV][G::CSTEPS];
 #pragma unroll
-          for (int mo = 0; mo < G::NTV; ++mo) {
+              for (int s = 0; s < G::KSTEPS; ++s)
+                kA[jj][s] = (DK >= 32 || g4 < 2)
+                                ? lds_b128(kb, swz<G::WCK>(16 * jj + l16, 32 * s + 8 * g4))
+                                : zero4;
 #pragma unroll
             for (int s = 0; s < G::KSTEPS; ++s)
-              sA[mo][s] = (DK >= 32 || g4 < 2)
-                              ? lds_b128(stc, swz<G::WCK>(16 * mo + l16, 32 * s + 8 * g4))
-                              : zero4;
 #pragma unroll
-            for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
-              if constexpr (C >= 32) {
-                // V^T rows for tokens 32 s2 + 4 g4 + (0..3) and 32 s2 + 16 + 4 g4 + (0..3)
-                vA[mo][s2] = lds_tr8<G::WCV>(vb, 32 * s2 + 4 * g4, 32 * s2 + 16 + 4 * g4,
-                                             16 * mo, l16);
-              } else {
-                // a 16-token chunk: the second run of 4 tokens lies past the chunk
-                const int j2 = l16 >> 2, m2 = l16 & 3;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(vb + swz<G::WCV>(4 * g4 + j2, 16 * mo + 4 * m2)));
-                const u32x2 lw = __builtin_bit_cast(u32x2, lo);
-                vA[mo][s2] = u32x4{lw[0], lw[1], 0u, 0u};
-              }
+              for (int jj = 0; jj < G::NSTRIP; ++jj)
+                pt[jj] = mfma16x16x32(kA[jj][s], qcur[j][s], pt[jj]);
+          } else {
+            // one k-step of K operands at a time
+#pragma unroll
+            for (int s = 0; s < G::KSTEPS; ++s) {
+              u32x4 kA[G::NSTRIP];
+#pragma unroll
+              for (int jj = 0; jj < G::NSTRIP; ++jj)
+                kA[jj] = (DK >= 32 || g4 < 2)
+                             ? lds_b128(kb, swz<G::WCK>(16 * jj + l16, 32 * s + 8 * g4))
+                             : zero4;
+#pragma unroll
+              for (int jj = 0; jj < G::NSTRIP; ++jj) pt[jj] = mfma16x16x32(kA[jj], qcur[j][s], pt[jj]);
             }
           }
           // pt[jj][i] = score of query row r against key 16 jj + 4 g4 + i: mask and decay
@@ -478,12 +533,23 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
                 pt[jj][i] = cc <= r ? x : 0.0f;
               }
             }
-          } else {
+          } else if constexpr (G::DM_REGS) {
             erow = er[j];
 #pragma unroll
             for (int jj = 0; jj < G::NSTRIP; ++jj)
 #pragma unroll
               for (int i = 0; i < 4; ++i) pt[jj][i] *= dm[j][jj][i];
+          } else {
+            erow = er[j];
+#pragma unroll
+            for (int jj = 0; jj < G::NSTRIP; ++jj)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int cc = 16 * jj + 4 * g4 + i;
+                float x = pt[jj][i];
+                if constexpr (CAT == kCatHead) x *= __builtin_amdgcn_exp2f((float)(r - cc) * lg2);
+                pt[jj][i] = cc <= r ? x : 0.0f;
+              }
           }
           u32x4 pb[G::CSTEPS];
 #pragma unroll
@@ -495,28 +561,53 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
             pb[s2][2] = cvt2(hi[0], hi[1]);
             pb[s2][3] = cvt2(hi[2], hi[3]);
           }
+          // inter-chunk term (S^T of this group from LDS), then the intra-chunk term
           f32x4 acc[G::NTV];
 #pragma unroll
           for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < G::KSTEPS; ++s)
+          for (int s = 0; s < G::KSTEPS; ++s) {
+            u32x4 sA[G::NTV];
 #pragma unroll
-            for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = mfma16x16x32(sA[mo][s], qcur[j][s], acc[mo]);
+            for (int mo = 0; mo < G::NTV; ++mo)
+              sA[mo] = (DK >= 32 || g4 < 2)
+                           ? lds_b128(stc, swz<G::WCK>(srow0 + 16 * mo + l16, 32 * s + 8 * g4))
+                           : zero4;
+#pragma unroll
+            for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = mfma16x16x32(sA[mo], qcur[j][s], acc[mo]);
+          }
           if constexpr (decayed) {
 #pragma unroll
             for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = acc[mo] * erow;
           }
 #pragma unroll
-          for (int s2 = 0; s2 < G::CSTEPS; ++s2)
+          for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
+            u32x4 vA[G::NTV];
 #pragma unroll
-            for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = mfma16x16x32(vA[mo][s2], pb[s2], acc[mo]);
+            for (int mo = 0; mo < G::NTV; ++mo) {
+              if constexpr (C >= 32) {
+                // V^T rows for tokens 32 s2 + 4 g4 + (0..3) and 32 s2 + 16 + 4 g4 + (0..3)
+                vA[mo] = lds_tr8<G::WCV>(vb, 32 * s2 + 4 * g4, 32 * s2 + 16 + 4 * g4,
+                                         srow0 + 16 * mo, l16);
+              } else {
+                // a 16-token chunk: the second run of 4 tokens lies past the chunk
+                const int j2 = l16 >> 2, m2 = l16 & 3;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(vb + swz<G::WCV>(4 * g4 + j2, srow0 + 16 * mo + 4 * m2)));
+                const u32x2 lw = __builtin_bit_cast(u32x2, lo);
+                vA[mo] = u32x4{lw[0], lw[1], 0u, 0u};
+              }
+            }
+#pragma unroll
+            for (int mo = 0; mo < G::NTV; ++mo) acc[mo] = mfma16x16x32(vA[mo], pb[s2], acc[mo]);
+          }
           if (r < nvalid) {
 #pragma unroll
             for (int mo = 0; mo < G::NTV; ++mo) {
               u32x2 w;
               w[0] = cvt2(acc[mo][0], acc[mo][1]);
               w[1] = cvt2(acc[mo][2], acc[mo][3]);
-              *reinterpret_cast<u32x2*>(oh + (size_t)(t0 + r) * DV + 16 * mo + 4 * g4) = w;
+              *reinterpret_cast<u32x2*>(og + (size_t)(t0 + r) * DV + 16 * mo + 4 * g4) = w;
             }
           }
         }
@@ -527,13 +618,13 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
     // transpose reads take every lane of the wave (they exchange data within
     // each 16-lane group); for a 16-token chunk the lane groups past the chunk
     // read rows 0..15 again and are zeroed afterwards.
-    if (G::TPW > 1 || wave < G::NT_S) {
-      char* stn = stage_s(std::integral_constant<int, buf ^ 1>{});
+    if (G::TPW > 1 || wl < G::NT_S) {
+      char* stn = sST[sp ^ 1];
       u32x4 vB[G::CSTEPS];
 #pragma unroll
       for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
         const int k0 = k0_of(s2);
-        u32x4 w = lds_tr8<G::WCV>(vb, k0, k0 + 4, 16 * nt_w, l16);
+        u32x4 w = lds_tr8<G::WCV>(vb, k0, k0 + 4, srow0 + 16 * nt_w, l16);
         if constexpr (decayed) {
           float sc[8];
           if constexpr (CAT == kCatToken) {
@@ -560,17 +651,6 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
         }
         vB[s2] = (C < 32 && g4 >= 2) ? zero4 : w;
       }
-      u32x4 kA2[G::TPW][G::CSTEPS];
-#pragma unroll
-      for (int t = 0; t < G::TPW; ++t) {
-        const int mt = min((wave + 4 * t) / G::NTV, G::NMK - 1);
-#pragma unroll
-        for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
-          const int k0 = k0_of(s2);
-          const u32x4 w = lds_tr8<G::WCK>(kb, k0, k0 + 4, 16 * mt, l16);
-          kA2[t][s2] = (C < 32 && g4 >= 2) ? zero4 : w;
-        }
-      }
       if constexpr (decayed) {
         float eL = eLf;
         if (CAT == kCatToken || nvalid < C) {
@@ -580,20 +660,45 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
 #pragma unroll
         for (int t = 0; t < G::TPW; ++t) accS[t] = accS[t] * eL;
       }
+      if constexpr (G::PRELOAD) {
+        u32x4 kA2[G::TPW][G::CSTEPS];
 #pragma unroll
-      for (int s2 = 0; s2 < G::CSTEPS; ++s2)
+        for (int t = 0; t < G::TPW; ++t) {
+          const int mt = min((wl + 4 * t) / G::NTV, G::NMK - 1);
 #pragma unroll
-        for (int t = 0; t < G::TPW; ++t) accS[t] = mfma16x16x32(kA2[t][s2], vB[s2], accS[t]);
+          for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
+            const int k0 = k0_of(s2);
+            const u32x4 w = lds_tr8<G::WCK>(kb, k0, k0 + 4, 16 * mt, l16);
+            kA2[t][s2] = (C < 32 && g4 >= 2) ? zero4 : w;
+          }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < G::CSTEPS; ++s2)
+#pragma unroll
+          for (int t = 0; t < G::TPW; ++t) accS[t] = mfma16x16x32(kA2[t][s2], vB[s2], accS[t]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < G::TPW; ++t) {
+          const int mt = min((wl + 4 * t) / G::NTV, G::NMK - 1);
+#pragma unroll
+          for (int s2 = 0; s2 < G::CSTEPS; ++s2) {
+            const int k0 = k0_of(s2);
+            u32x4 w = lds_tr8<G::WCK>(kb, k0, k0 + 4, 16 * mt, l16);
+            w = (C < 32 && g4 >= 2) ? zero4 : w;
+            accS[t] = mfma16x16x32(w, vB[s2], accS[t]);
+          }
+        }
+      }
       if constexpr (!STATE_ONLY) {
 #pragma unroll
         for (int t = 0; t < G::TPW; ++t) {
-          const int tau = wave + 4 * t;
+          const int tau = wl + 4 * t;
           if (tau < G::NT_S) {
             const int mt = tau / G::NTV;
             u32x2 w;
             w[0] = cvt2(accS[t][0], accS[t][1]);
             w[1] = cvt2(accS[t][2], accS[t][3]);
-            *reinterpret_cast<u32x2*>(&stn[swz<G::WCK>(16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
+            *reinterpret_cast<u32x2*>(&stn[swz<G::WCK>(srow0 + 16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
           }
         }
       }
@@ -601,10 +706,22 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
     logA += bL;
   };
 
-  issue_loads(std::integral_constant<int, 0>{}, c_begin);
-  for (int c = c_begin; c < c_end; c += 2) {
-    body(std::integral_constant<int, 0>{}, c);
-    if (c + 1 < c_end) body(std::integral_constant<int, 1>{}, c + 1);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  issue_loads(S0{}, c_begin);
+  if constexpr (NS == 3) {
+    if (c_begin + 1 < c_end) issue_loads(S1{}, c_begin + 1);
+    for (int c = c_begin; c < c_end; c += 3) {
+      body(S0{}, c);
+      if (c + 1 < c_end) body(S1{}, c + 1);
+      if (c + 2 < c_end) body(S2{}, c + 2);
+    }
+  } else {
+    for (int c = c_begin; c < c_end; c += 2) {
+      body(S0{}, c);
+      if (c + 1 < c_end) body(S1{}, c + 1);
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------
@@ -618,47 +735,57 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(const ChunkArgs a) {
   if (dst != nullptr) {
 #pragma unroll
     for (int t = 0; t < G::TPW; ++t) {
-      const int tau = wave + 4 * t;
+      const int tau = wl + 4 * t;
       if (tau < G::NT_S) {
         const int mt = tau / G::NTV;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          dst[(size_t)(16 * mt + 4 * g4 + i) * DV + dv0 + 16 * nt_w + l16] = accS[t][i];
+          dst[(size_t)(16 * mt + 4 * g4 + i) * DV + dvg + 16 * nt_w + l16] = accS[t][i];
       }
     }
   }
 }
 
-template <int DK, int TV, int C, int CAT>
+// ---- launch and dispatch ----------------------------------------------------
+template <int DK, int TV, int C, int NG, int CAT>
 hipError_t launch_one(const ChunkArgs& a, bool state_only, hipStream_t s) {
   const int groups = (a.n_units + 7) / 8;
-  const dim3 grid(groups * 8 * a.n_v), block(256);
+  const dim3 grid(groups * 8 * a.n_v), block(256 * NG);
   if (state_only)
-    hipLaunchKernelGGL((chunk_bf16_kernel<DK, TV, C, CAT, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((chunk_bf16_kernel<DK, TV, C, NG, CAT, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((chunk_bf16_kernel<DK, TV, C, CAT, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((chunk_bf16_kernel<DK, TV, C, NG, CAT, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-template <int DK, int TV, int CAT>
+template <int DK, int TV, int NG, int CAT>
 hipError_t dispatch_c(const ChunkArgs& a, bool so, hipStream_t s) {
   switch (a.C) {
-    case 16: return launch_one<DK, TV, 16, CAT>(a, so, s);
-    case 32: return launch_one<DK, TV, 32, CAT>(a, so, s);
-    case 64: return launch_one<DK, TV, 64, CAT>(a, so, s);
+    case 16: return launch_one<DK, TV, 16, NG, CAT>(a, so, s);
+    case 32: return launch_one<DK, TV, 32, NG, CAT>(a, so, s);
+    case 64: return launch_one<DK, TV, 64, NG, CAT>(a, so, s);
     case 128:
-      if constexpr (Geo<DK, TV, 128>::LDS_MAIN <= kMaxLds) return launch_one<DK, TV, 128, CAT>(a, so, s);
+      if constexpr (Geo<DK, TV, 128, NG>::LDS_MAIN <= kMaxLds) return launch_one<DK, TV, 128, NG, CAT>(a, so, s);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }
 
+// a.tv is the width of one column group; a.ng the number of groups (1 or 2)
 template <int DK, int CAT>
 hipError_t dispatch_tv(const ChunkArgs& a, bool so, hipStream_t s) {
+  if (a.ng == 2) {
+    switch (a.tv) {
+      case 16: return dispatch_c<DK, 16, 2, CAT>(a, so, s);
+      case 32: return dispatch_c<DK, 32, 2, CAT>(a, so, s);
+      case 64: return dispatch_c<DK, 64, 2, CAT>(a, so, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.tv) {
-    case 16: return dispatch_c<DK, 16, CAT>(a, so, s);
-    case 32: return dispatch_c<DK, 32, CAT>(a, so, s);
-    case 64: return dispatch_c<DK, 64, CAT>(a, so, s);
+    case 16: return dispatch_c<DK, 16, 1, CAT>(a, so, s);
+    case 32: return dispatch_c<DK, 32, 1, CAT>(a, so, s);
+    case 64: return dispatch_c<DK, 64, 1, CAT>(a, so, s);
   }
   return hipErrorInvalidValue;
 }
@@ -672,17 +799,18 @@ hipError_t dispatch_cat(const ChunkArgs& a, bool so, hipStream_t s) {
   }
 }
 
-template <int DK, int TV>
+template <int DK, int TV, int NG>
 constexpr size_t lds_of(int C) {
-  return C == 16    ? Geo<DK, TV, 16>::LDS_MAIN
-         : C == 32  ? Geo<DK, TV, 32>::LDS_MAIN
-         : C == 64  ? Geo<DK, TV, 64>::LDS_MAIN
-                    : Geo<DK, TV, 128>::LDS_MAIN;
+  return C == 16    ? Geo<DK, TV, 16, NG>::LDS_MAIN
+         : C == 32  ? Geo<DK, TV, 32, NG>::LDS_MAIN
+         : C == 64  ? Geo<DK, TV, 64, NG>::LDS_MAIN
+                    : Geo<DK, TV, 128, NG>::LDS_MAIN;
 }
 
 template <int DK>
-constexpr size_t lds_tv(int TV, int C) {
-  return TV == 16 ? lds_of<DK, 16>(C) : TV == 32 ? lds_of<DK, 32>(C) : lds_of<DK, 64>(C);
+constexpr size_t lds_tv(int TV, int NG, int C) {
+  return NG == 2 ? (TV == 16 ? lds_of<DK, 16, 2>(C) : TV == 32 ? lds_of<DK, 32, 2>(C) : lds_of<DK, 64, 2>(C))
+                 : (TV == 16 ? lds_of<DK, 16, 1>(C) : TV == 32 ? lds_of<DK, 32, 1>(C) : lds_of<DK, 64, 1>(C));
 }
 
 }  // namespace bf16k

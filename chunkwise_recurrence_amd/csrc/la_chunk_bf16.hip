@@ -41,15 +41,16 @@ hipError_t launch_decay_prefix(const ChunkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-bool chunk_bf16_supported(int DK, int TV, int C) {
+bool chunk_bf16_supported(int DK, int TV, int NG, int C) {
   if (C != 16 && C != 32 && C != 64 && C != 128) return false;
   if (TV != 16 && TV != 32 && TV != 64) return false;
+  if (NG != 1 && NG != 2) return false;
   size_t lds = 0;
   switch (DK) {
-    case 16: lds = bf16k::lds_tv<16>(TV, C); break;
-    case 32: lds = bf16k::lds_tv<32>(TV, C); break;
-    case 64: lds = bf16k::lds_tv<64>(TV, C); break;
-    case 128: lds = bf16k::lds_tv<128>(TV, C); break;
+    case 16: lds = bf16k::lds_tv<16>(TV, NG, C); break;
+    case 32: lds = bf16k::lds_tv<32>(TV, NG, C); break;
+    case 64: lds = bf16k::lds_tv<64>(TV, NG, C); break;
+    case 128: lds = bf16k::lds_tv<128>(TV, NG, C); break;
     default: return false;
   }
   return lds <= bf16k::kMaxLds;

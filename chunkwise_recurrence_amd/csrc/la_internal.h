@@ -27,8 +27,9 @@ struct ChunkArgs {
   int P;                // sequence segments per head
   int seg_chunks;       // chunks per segment (the last one may hold fewer)
   int n_units;          // work units: B*H*P (main) or B*H*(P-1) (state pass)
-  int n_v;              // d_v tiles per head
-  int tv;               // d_v tile width
+  int n_v;              // value tiles per head (one workgroup each)
+  int tv;               // value columns per column group of a workgroup
+  int ng;               // column groups (of 4 waves) per workgroup
   int phi, decay_kind;
 };
 
@@ -50,7 +51,8 @@ hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 
-// Whether a bf16 (DK, TV, C) combination has a compiled kernel.
-bool chunk_bf16_supported(int DK, int TV, int C);
+// Whether a bf16 kernel exists for key dim DK, NG column groups of TV columns
+// and chunk C (and fits the LDS).
+bool chunk_bf16_supported(int DK, int TV, int NG, int C);
 
 }  // namespace la

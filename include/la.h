@@ -138,24 +138,25 @@ const char* la_status_string(int status);
 
 /*
  * la_chunk_fwd_plan -- the launch plan la_chunk_fwd would use (host only,
- * for tests and benchmarks): the d_v tile width of one workgroup and the
- * number of sequence segments each head is split into.  Returns LA_OK or the
- * error la_chunk_fwd would return for these arguments.
+ * for tests and benchmarks): the value columns one workgroup covers, the
+ * number of sequence segments each head is split into, and the number of
+ * 4-wave column groups per workgroup (bf16).  Any output pointer may be NULL.
+ * Returns LA_OK or the error la_chunk_fwd would return for these arguments.
  */
 la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype,
-                            int* dv_tile, int* segments);
+                            int* dv_tile, int* segments, int* groups);
 
 /*
  * la_set_plan -- override the launch plan la_chunk_fwd chooses for the bf16
- * path: the d_v tile width of one workgroup (16, 32, 64 or 128; must divide
- * d_v) and the number of sequence segments per head (>= 1).  0 restores the
- * automatic choice for that field; values that do not fit a given call are
- * clamped to the nearest valid ones for that call.  Results do not depend on
- * the plan beyond rounding; tests use it to check exactly that.
- * Process-wide; returns LA_ERR_UNSUPPORTED for an invalid tile, LA_ERR_SHAPE
- * for a negative segment count.
+ * path: the value columns one workgroup covers (16, 32, 64 or 128), the
+ * number of sequence segments per head (>= 1), and the number of 4-wave
+ * column groups per workgroup (1 or 2).  0 restores the automatic choice for
+ * that field; values that do not fit a given call are reduced to ones that
+ * do.  Results do not depend on the plan beyond rounding; tests use it to
+ * check exactly that.  Process-wide; returns LA_ERR_UNSUPPORTED for an
+ * invalid tile or group count, LA_ERR_SHAPE for a negative segment count.
  */
-la_status la_set_plan(int dv_tile, int segments);
+la_status la_set_plan(int dv_tile, int segments, int groups);
 
 #ifdef __cplusplus
 }

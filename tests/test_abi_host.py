@@ -66,7 +66,7 @@ def test_zero_length_is_ok_without_touching_memory():
 
 def test_workspace_is_required_when_the_plan_splits_the_sequence():
     # 1 head of 64 x 64 over 64K tokens: the plan splits the sequence
-    tv, P = la.plan(1, 1, 65536, 64, 64, 64)
+    tile, P, groups = la.plan(1, 1, 65536, 64, 64, 64)
     assert P > 1
     need = la.chunk_fwd_workspace_bytes(1, 1, 65536, 64, 64, 64)
     assert need >= P * 64 * 64 * 4
@@ -79,29 +79,43 @@ def test_workspace_is_required_when_the_plan_splits_the_sequence():
 
 
 def test_plans_of_the_workloads():
-    # retnet: 64 heads x 4 value tiles of 32 = 256 workgroups, one segment
-    assert la.plan(2, 32, 16384, 128, 128, 64) == (32, 1)
-    # gated: 16 heads x 4 tiles x 4 segments = 256 workgroups
-    assert la.plan(1, 16, 65536, 128, 128, 64) == (32, 4)
-    # elu: 64 heads x 2 tiles x 2 segments
-    assert la.plan(4, 16, 4096, 64, 64, 64) == (32, 2)
+    # 4-wave workgroups over 64-column value tiles; segments bring the grid
+    # to 256 workgroups.  retnet: 64 heads x 2 tiles x 2 segments
+    assert la.plan(2, 32, 16384, 128, 128, 64) == (64, 2, 1)
+    # gated: 16 heads x 2 tiles x 8 segments
+    assert la.plan(1, 16, 65536, 128, 128, 64) == (64, 8, 1)
+    # elu: 64 heads x 4 segments
+    assert la.plan(4, 16, 4096, 64, 64, 64) == (64, 4, 1)
+    assert la.plan(1, 1, 100, 16, 16, 16) == (16, 1, 1)
+    # two 64-column groups of 128-token chunks exceed the LDS: one group
+    la.set_plan(128, 0, 2)
+    try:
+        assert la.plan(1, 1, 100, 128, 128, 128) == (64, 1, 2)
+    finally:
+        la.set_plan(0, 0, 0)
     # fp32: one segment, 16- or 32-wide tiles
-    assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32) == (16, 1)
+    assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32) == (16, 1, 1)
     assert la.chunk_fwd_workspace_bytes(1, 1, 300, 16, 16, 64, la.LA_F32) == 0
 
 
 def test_plan_override_and_clamping():
     try:
-        la.set_plan(64, 3)
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (64, 3)
-        assert la.plan(1, 1, 64 * 2, 128, 32, 64) == (32, 2)   # tile clamped to d_v, P to chunks
+        la.set_plan(64, 3, 1)
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (64, 3, 1)
+        assert la.plan(1, 1, 64 * 2, 128, 32, 64) == (32, 2, 1)   # tile clamped to d_v, P to chunks
+        la.set_plan(32, 0, 2)
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64)[::2] == (32, 2)
+        la.set_plan(16, 0, 2)   # 8-column groups do not exist
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64)[::2] == (16, 1)
         with pytest.raises(la.LAError):
             la.set_plan(48, 0)
         with pytest.raises(la.LAError):
             la.set_plan(0, -1)
+        with pytest.raises(la.LAError):
+            la.set_plan(0, 0, 3)
     finally:
-        la.set_plan(0, 0)
-    assert la.plan(2, 32, 16384, 128, 128, 64) == (32, 1)
+        la.set_plan(0, 0, 0)
+    assert la.plan(2, 32, 16384, 128, 128, 64) == (64, 2, 1)
 
 
 def _dec(**kw):

@@ -105,20 +105,24 @@ def test_chunk_size_invariance_on_gpu(gpu_lib):
         assert oracle.rel_err(o, outs[0]) < 1e-2
 
 
-@pytest.mark.parametrize("tv,segments", [(16, 1), (32, 1), (64, 1), (128, 1), (32, 2), (32, 3),
-                                         (64, 8), (128, 5)])
-def test_launch_plan_invariance(gpu_lib, tv, segments):
-    """Value-tile width and sequence segments change the work split, not the result."""
+@pytest.mark.parametrize("tile,segments,groups", [
+    (16, 1, 1), (32, 1, 1), (64, 1, 1), (32, 1, 2), (64, 1, 2), (128, 1, 2), (32, 2, 1),
+    (32, 3, 2), (64, 8, 1), (128, 5, 2), (128, 3, 2), (64, 2, 2)])
+def test_launch_plan_invariance(gpu_lib, tile, segments, groups):
+    """Value tile, column groups and sequence segments change the work split, not the result."""
     la = gpu_lib
-    la.set_plan(tv, segments)
+    la.set_plan(tile, segments, groups)
     try:
+        # 21 chunks: segments of ceil(21 / P) chunks, so P = 8 runs as 7 segments of 3
+        got = la.plan(1, 2, 64 * 20 + 17, 128, 128, 64)
+        assert got[::2] == (tile, groups) and got[1] == -(-21 // -(-21 // segments))
         for kind in (W.DECAY_NONE, W.DECAY_GATE, W.DECAY_HEAD):
             c = W.RandomCase(1, 2, 64 * 20 + 17, 128, 128, torch.bfloat16, 0, kind,
-                             seed=tv + segments + kind, scale=1.0 / np.sqrt(128),
+                             seed=tile + segments + kind, scale=1.0 / np.sqrt(128),
                              gate_shift=-5.0, with_state=True)
-            _check_case(la, c, 64, f"plan tv={tv} P={segments}")
+            _check_case(la, c, 64, f"plan tile={tile} P={segments} groups={groups}")
     finally:
-        la.set_plan(0, 0)
+        la.set_plan(0, 0, 0)
 
 
 def test_resume_equals_one_call(gpu_lib):
