@@ -123,9 +123,9 @@ def bench_chunk(la, torch, W, steps, warmup):
     torch.cuda.synchronize()
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
     by, flops = chunk_algorithmic(w, with_state=True)
-    tile, P, groups = la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)
-    return dict(w=w, ms_step=ms_step, wall=wall, kern_ms=kern_ms, bytes=by, flops=flops, tile=tile,
-                P=P, groups=groups, need=need)
+    kernel, tile, P, groups = la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)
+    return dict(w=w, ms_step=ms_step, wall=wall, kern_ms=kern_ms, bytes=by, flops=flops,
+                kernel=kernel, tile=tile, P=P, groups=groups, need=need)
 
 
 def bench_decode(la, torch, W, steps, reps=3):
@@ -260,7 +260,8 @@ def main():
         "config": {"workload": "retnet_bf16", "B": w.B, "H": w.H, "L": w.L, "d_k": w.dk,
                    "d_v": w.dv, "C": w.C, "decay": "per-head gamma = linspace(0.9, 0.999, 32)",
                    "inputs": "q,k,v ~ N(0,1)/sqrt(128) in bf16",
-                   "plan": {"dv_tile": c["tile"], "segments": c["P"], "column_groups": c["groups"]}},
+                   "plan": {"kernel": {1: "strip", 2: "stripe"}.get(c["kernel"], c["kernel"]),
+                            "dv_tile": c["tile"], "segments": c["P"]}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profile_value(TRAFFIC_PROFILE, "hbm_bytes_per_forward"),

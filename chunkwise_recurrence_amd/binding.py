@@ -17,6 +17,13 @@ _LIB_PATH = os.path.join(HERE, "liblinattn.so")
 LA_F32, LA_BF16 = 0, 1
 PHI_IDENTITY, PHI_ELU1 = 0, 1
 DECAY_NONE, DECAY_HEAD, DECAY_LOG, DECAY_GATE = 0, 1, 2, 3
+KERNEL_AUTO, KERNEL_STRIP, KERNEL_STRIPE, KERNEL_F32 = 0, 1, 2, 3
+
+
+class Plan(ctypes.Structure):
+    """la_plan: kernel, value columns per workgroup, segments, column groups."""
+    _fields_ = [("kernel", ctypes.c_int), ("dv_tile", ctypes.c_int),
+                ("segments", ctypes.c_int), ("groups", ctypes.c_int)]
 
 # every symbol include/la.h declares
 EXPORTS = ("la_state_init", "la_chunk_fwd_workspace_bytes", "la_chunk_fwd", "la_decode_step",
@@ -57,9 +64,9 @@ def load():
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i]
     lib.la_chunk_fwd_plan.restype = i
-    lib.la_chunk_fwd_plan.argtypes = [i] * 7 + [ctypes.POINTER(ctypes.c_int)] * 3
+    lib.la_chunk_fwd_plan.argtypes = [i] * 7 + [ctypes.POINTER(Plan)]
     lib.la_set_plan.restype = i
-    lib.la_set_plan.argtypes = [i, i, i]
+    lib.la_set_plan.argtypes = [ctypes.POINTER(Plan)]
     _lib = lib
     return lib
 
@@ -103,16 +110,17 @@ def _check(status: int, where: str):
 
 
 def plan(B: int, H: int, L: int, dk: int, dv: int, C: int, dtype: int = LA_BF16):
-    """(value columns per workgroup, segments per head, column groups) la_chunk_fwd will use."""
-    tv, p, g = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
-    _check(load().la_chunk_fwd_plan(B, H, L, dk, dv, C, dtype, ctypes.byref(tv), ctypes.byref(p),
-                                    ctypes.byref(g)), "la_chunk_fwd_plan")
-    return tv.value, p.value, g.value
+    """(kernel, value columns per workgroup, segments per head, column groups) of la_chunk_fwd."""
+    p = Plan()
+    _check(load().la_chunk_fwd_plan(B, H, L, dk, dv, C, dtype, ctypes.byref(p)),
+           "la_chunk_fwd_plan")
+    return p.kernel, p.dv_tile, p.segments, p.groups
 
 
-def set_plan(dv_tile: int = 0, segments: int = 0, groups: int = 0):
+def set_plan(kernel: int = 0, dv_tile: int = 0, segments: int = 0, groups: int = 0):
     """Override the bf16 launch plan process-wide (0 = automatic)."""
-    _check(load().la_set_plan(int(dv_tile), int(segments), int(groups)), "la_set_plan")
+    p = Plan(int(kernel), int(dv_tile), int(segments), int(groups))
+    _check(load().la_set_plan(ctypes.byref(p)), "la_set_plan")
 
 
 def chunk_fwd_workspace_bytes(B: int, H: int, L: int, dk: int, dv: int, C: int,

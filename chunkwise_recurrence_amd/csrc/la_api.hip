@@ -16,6 +16,7 @@ constexpr int kTargetWorkgroups = 256;
 // A segment of the sequence keeps at least this many chunks.
 constexpr int kMinSegmentChunks = 4;
 
+std::atomic<int> g_plan_kernel{0};
 std::atomic<int> g_plan_tile{0};
 std::atomic<int> g_plan_segments{0};
 std::atomic<int> g_plan_groups{0};
@@ -25,6 +26,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 struct Plan {
+  int kernel = 0;    // LA_KERNEL_F32, LA_KERNEL_STRIP or LA_KERNEL_STRIPE
   int tile = 0;      // value columns of one workgroup
   int ng = 1;        // column groups (of 4 waves) per workgroup (bf16 path)
   int tv = 0;        // value columns per column group
@@ -53,32 +55,50 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   const int heads = B * H;
   const int nchunks = L > 0 ? (L + C - 1) / C : 0;
   if (dtype == LA_F32) {
+    p.kernel = LA_KERNEL_F32;
     p.tile = p.tv = d_v < 32 ? d_v : 32;
     p.ng = 1;
     p.P = 1;
     p.seg_chunks = nchunks;
     return p;
   }
-  // One 4-wave workgroup per (head, 64-column value tile, sequence segment);
-  // the sequence is split into segments until the chip has a workgroup per
-  // compute unit.  Wider workgroups (two column groups of 4 waves) can be
-  // asked for with la_set_plan.
-  int tile = d_v < 64 ? d_v : 64;
-  const int forced_tile = g_plan_tile.load(), forced_groups = g_plan_groups.load();
-  if (forced_tile > 0) {
-    tile = forced_tile;
+  const int forced_kernel = g_plan_kernel.load(), forced_tile = g_plan_tile.load(),
+            forced_groups = g_plan_groups.load();
+  // The stripe kernel (32x32 MFMA, the state in registers, one workgroup per
+  // head and segment) where the shape allows it; the strip kernel (16x16
+  // MFMA, 4-wave groups over 64-column tiles) otherwise.
+  int tile = 0;
+  if (forced_kernel != LA_KERNEL_STRIP) {
+    // two waves per 32-column stripe (each holding half of the keys) where
+    // d_k allows, for two waves per SIMD
+    auto parts_for = [&](int t) {
+      if (forced_groups > 0) return forced_groups;
+      return la::chunk_stripe_supported(d_k, t, 2, C) ? 2 : 1;
+    };
+    tile = forced_tile > 0 ? forced_tile : d_v;
     while (tile > d_v) tile /= 2;
+    while (tile >= 32 && !la::chunk_stripe_supported(d_k, tile, parts_for(tile), C)) tile /= 2;
+    if (tile >= 32) {
+      p.kernel = LA_KERNEL_STRIPE;
+      p.tile = p.tv = tile;
+      p.ng = parts_for(tile);
+    }
   }
-  auto groups_for = [&](int t) {
-    int g = forced_groups > 0 ? forced_groups : 1;
-    if (t / g < 16) g = 1;
-    return g;
-  };
-  // the widest layout that has a kernel and fits the LDS
-  while (tile > 16 && !(t_fits(d_k, tile, groups_for(tile), C))) tile /= 2;
-  p.tile = tile;
-  p.ng = groups_for(tile);
-  p.tv = tile / p.ng;
+  if (p.kernel == 0) {
+    p.kernel = LA_KERNEL_STRIP;
+    tile = forced_tile > 0 ? forced_tile : (d_v < 64 ? d_v : 64);
+    while (tile > d_v) tile /= 2;
+    auto groups_for = [&](int t) {
+      int g = forced_groups > 0 ? forced_groups : 1;
+      if (t / g < 16) g = 1;
+      return g;
+    };
+    // the widest layout that has a kernel and fits the LDS
+    while (tile > 16 && !(t_fits(d_k, tile, groups_for(tile), C))) tile /= 2;
+    p.tile = tile;
+    p.ng = groups_for(tile);
+    p.tv = tile / p.ng;
+  }
   int P = 1;
   const long long units = (long long)heads * (d_v / tile);
   while (units * P < kTargetWorkgroups && (long long)P * 2 * kMinSegmentChunks <= nchunks) P *= 2;
@@ -122,24 +142,31 @@ const char* la_status_string(int s) {
   return "unknown la_status";
 }
 
-la_status la_set_plan(int dv_tile, int segments, int groups) {
-  if (dv_tile != 0 && !dim_ok(dv_tile)) return LA_ERR_UNSUPPORTED;
-  if (groups != 0 && groups != 1 && groups != 2) return LA_ERR_UNSUPPORTED;
-  if (segments < 0) return LA_ERR_SHAPE;
-  g_plan_tile.store(dv_tile);
-  g_plan_segments.store(segments);
-  g_plan_groups.store(groups);
+la_status la_set_plan(const la_plan* plan) {
+  const la_plan zero{};
+  const la_plan& p = plan ? *plan : zero;
+  if (p.kernel != 0 && p.kernel != LA_KERNEL_STRIP && p.kernel != LA_KERNEL_STRIPE)
+    return LA_ERR_UNSUPPORTED;
+  if (p.dv_tile != 0 && !dim_ok(p.dv_tile)) return LA_ERR_UNSUPPORTED;
+  if (p.groups != 0 && p.groups != 1 && p.groups != 2) return LA_ERR_UNSUPPORTED;
+  if (p.segments < 0) return LA_ERR_SHAPE;
+  g_plan_kernel.store(p.kernel);
+  g_plan_tile.store(p.dv_tile);
+  g_plan_segments.store(p.segments);
+  g_plan_groups.store(p.groups);
   return LA_OK;
 }
 
-la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int* dv_tile,
-                            int* segments, int* groups) {
+la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                            la_plan* plan) {
   const la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
   if (st != LA_OK) return st;
+  if (!plan) return LA_ERR_NULL;
   const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, LA_DECAY_NONE);
-  if (dv_tile) *dv_tile = p.tile;
-  if (segments) *segments = p.P;
-  if (groups) *groups = p.ng;
+  plan->kernel = p.kernel;
+  plan->dv_tile = p.tile;
+  plan->segments = p.P;
+  plan->groups = p.ng;
   return LA_OK;
 }
 
@@ -216,11 +243,13 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
       a.ws_S = reinterpret_cast<float*>(ws + p.ws_S_off);
       a.ws_logA = reinterpret_cast<float*>(ws + p.ws_logA_off);
       a.n_units = B * H * (p.P - 1);
-      e = la::launch_chunk_bf16(a, /*state_only=*/true, s);
+      e = p.kernel == LA_KERNEL_STRIPE ? la::launch_chunk_stripe(a, /*state_only=*/true, s)
+                                       : la::launch_chunk_bf16(a, /*state_only=*/true, s);
       if (e != hipSuccess) return LA_ERR_DEVICE;
     }
     a.n_units = B * H * p.P;
-    e = la::launch_chunk_bf16(a, /*state_only=*/false, s);
+    e = p.kernel == LA_KERNEL_STRIPE ? la::launch_chunk_stripe(a, /*state_only=*/false, s)
+                                     : la::launch_chunk_bf16(a, /*state_only=*/false, s);
   }
   return e == hipSuccess ? LA_OK : LA_ERR_DEVICE;
 }

@@ -1,0 +1,729 @@
+// la_chunk_stripe.h -- chunkwise causal linear attention, bf16 in, gfx950
+// v_mfma_f32_32x32x16_bf16; each wave owns a 32-column stripe of the value
+// dimension and keeps its part of the state in registers.
+//
+// The arithmetic is the same as the per-strip kernel's (la_chunk_bf16.h): for
+// every chunk of C tokens, with b the inclusive in-chunk prefix of log a,
+//
+//   O_c     = diag(e^b) Q_c S_c + ((Q_c K_c^T) o D_c) V_c,   D_c[i,j] = e^{b_i - b_j} [j <= i]
+//   S_{c+1} = e^{b_last} S_c + K_c^T diag(e^{b_last - b}) V_c
+//
+// (the chunkwise form of "Linear / Sparse Attention - minimal runnable
+// implementation", linear_attn_chunkwise, with the decay folded into S_c and
+// the in-chunk mask as the linear/sparse attention tutorial's section 6.2
+// says; the per-element decay is the log-space construction of CS336 lecture 4
+// code 1, gated_linear_attention_parallel).  Only the work split differs:
+//
+//   * a workgroup of NWV waves owns one head, NWV*32 value columns and one
+//     segment of the sequence; wave w owns value columns [32w, 32w + 32).
+//   * S[:, stripe] (d_k x 32, fp32) lives in the wave's MFMA accumulators as
+//     d_k/32 tiles of 32x32.  The inter-chunk term is computed transposed,
+//     O^T[stripe, rows] = S^T Q^T, with the accumulators themselves (packed to
+//     bf16) as the A operand: an accumulator lane holds one value column and
+//     the keys {8q + 4h + (0..3)}, so the A operand's k positions run over
+//     keys 16s + 4h + (0..3) and 16s + 8 + 4h + (0..3), and the Q^T operand
+//     reads the same keys (two 8-byte LDS reads).  S never goes through LDS.
+//   * the causal 32x32 score blocks P^T[J, I] = K_J Q_I^T (J <= I) are spread
+//     over the waves, masked and decayed in registers and written to LDS as
+//     bf16 P~ (row-major, swizzled); after one barrier every wave reads the
+//     rows it needs as the B operand of O^T += V^T P~^T.
+//   * V^T operands (lane = value column, 8 consecutive tokens) come from the
+//     row-major V tile through ds_read_b64_tr_b16; the same registers, scaled
+//     by e^{b_last - b_t}, are the B operand of the state update
+//     S += K^T diag(e^{b_last - b}) V, whose K^T operand is read the same way.
+//   * Q, K, V tiles stream from HBM into LDS with global_load_lds_dwordx4,
+//     NSTG chunks deep; workgroup barriers wait for LDS only, so the prefetch
+//     stays in flight across them.
+//   * output rows leave as 8-byte stores of 4 consecutive value columns.
+//
+// STATE_ONLY computes a segment's state increment and total log2 decay from a
+// zero state (the first pass of the segment split); the main pass composes
+// the exclusive prefix of the (decay, state) pairs in its prologue, the
+// parallel / associative scan idea of the tutorial's section 3.3.
+#pragma once
+#include <type_traits>
+
+#include "la_device.h"
+
+namespace la {
+namespace stripe {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+template <int DK, int NWV, int KH, int C>
+struct Geo {
+  static constexpr int NW = NWV * KH;           // waves of the workgroup
+  static constexpr int TVW = 32 * NWV;          // value columns of the workgroup
+  static constexpr int WCK = DK / 8;            // 16-byte chunks per Q/K row
+  static constexpr int WCV = TVW / 8;           // ... per V row
+  static constexpr int WCP = C / 8;             // ... per P~ row
+  static constexpr int NRB = C / 32;            // 32-row blocks of a chunk
+  static constexpr int NKS = DK / 16;           // 16-key MFMA steps
+  static constexpr int NMK = DK / 32;           // 32-key state tiles
+  static constexpr int NKS_OWN = NKS / KH;      // ... of one wave's key part
+  static constexpr int NMK_OWN = NMK / KH;
+  static constexpr int NTS = C / 16;            // 16-token MFMA steps
+  static constexpr int NB = NRB * (NRB + 1) / 2;  // causal 32x32 score blocks
+  static constexpr int BPW = (NB + NW - 1) / NW;  // score blocks per wave (at most)
+  static constexpr int RBW = (NRB + KH - 1) / KH;  // output row blocks per wave (at most)
+  static constexpr int QK_BYTES = C * DK * 2;
+  static constexpr int V_BYTES = C * TVW * 2;
+  static constexpr int QK_BLK = QK_BYTES / 1024;  // 1 KB DMA blocks (64 lanes x 16 B)
+  static constexpr int V_BLK = V_BYTES / 1024;
+  static constexpr int QK_PER = (QK_BLK + NW - 1) / NW;  // per wave
+  static constexpr int V_PER = (V_BLK + NW - 1) / NW;
+  // vector memory instructions of one chunk per wave (at most)
+  static constexpr int LOADS_MAX = 2 * QK_PER + V_PER + 1;
+  static constexpr int STORES = 4 * RBW;
+  // every wave issues the same memory instructions per chunk and their count
+  // fits the 6-bit vmcnt, so the wait at the top of a chunk can count them
+  static constexpr bool UNIFORM = QK_BLK % NW == 0 && V_BLK % NW == 0 && NRB % KH == 0 &&
+                                  STORES + LOADS_MAX < 64;
+  static constexpr size_t XCH_BYTES = KH > 1 ? (size_t)NWV * NRB * 4096 : 16;
+  static constexpr size_t stage_bytes(int n) {
+    return (size_t)n * (2 * (size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
+           2 * (size_t)C * C + 2 * 4 * (size_t)NW * C + XCH_BYTES + 256;
+  }
+  static constexpr int NSTG =
+      (UNIFORM && stage_bytes(3) <= kMaxLds && 2 * STORES + LOADS_MAX < 64) ? 3 : 2;
+  static constexpr size_t LDS = stage_bytes(NSTG);
+  static_assert(QK_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "tiles are whole DMA blocks");
+  static_assert(KH == 1 || NMK % KH == 0, "key parts hold whole 32-key tiles");
+};
+
+// Row-major bf16 tiles with WC 16-byte chunks per row keep their chunks
+// XOR-swizzled by g(m), m = the row's 256-byte bank line.  g is a bijection on
+// m mod WC, so 16 consecutive rows read at one logical chunk hit 16 distinct
+// bank slots; and 4 consecutive rows move an aligned group of 4 chunks to 4
+// distinct groups, so a transpose read (4 rows x 4 chunks per 32 lanes) is
+// conflict-free too.
+template <int WC>
+__device__ __forceinline__ int swz_xor(int row) {
+  constexpr int RPL = WC >= 16 ? 1 : 16 / WC;   // rows per bank line
+  constexpr int A = WC >= 4 ? WC / 4 : 1;       // groups of 4 chunks per row
+  const int m = row / RPL;
+  return (((m & (A - 1)) << 2) | ((m / A) & 3)) & (WC - 1);
+}
+template <int WC>
+__device__ __forceinline__ int swz(int row, int col) {
+  const int chunk = (col >> 3) ^ swz_xor<WC>(row);
+  return row * (WC * 16) + (chunk << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ u32x4 lds_b128(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ u32x2 lds_b64(const char* base, int off) {
+  return *reinterpret_cast<const u32x2*>(base + off);
+}
+
+// Transpose read of 8 tokens of one column: lane i of each 16-lane group gets
+// column col0 + i of rows k0 .. k0+3 (elements 0-3) and k0+4 .. k0+7 (4-7).
+// Every lane of the wave must take part.
+template <int WC>
+__device__ __forceinline__ u32x4 lds_tr8(const char* base, int k0, int col0, int l16) {
+  const int j = l16 >> 2, m = l16 & 3;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + swz<WC>(k0 + j, col0 + 4 * m)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + swz<WC>(k0 + 4 + j, col0 + 4 * m)));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+__device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 elu1_x8(u32x4 w) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = cvt2(feature_elu1(bf16_to_f32(w[e] & 0xffffu)), feature_elu1(bf16_to_f32(w[e] >> 16)));
+  return w;
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
+__device__ __forceinline__ void no_speculation() { asm volatile("" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for data exchanged through LDS: this wave's LDS accesses
+// complete, then s_barrier; no memory fence, so global loads in flight stay
+// in flight.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS writes of this wave complete before its later LDS reads of other lanes'
+// data (LDS requests of one wave are processed in order; this only stops the
+// compiler from reordering).
+__device__ __forceinline__ void lds_wave_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("" ::: "memory");
+}
+
+enum { kCatNone = 0, kCatHead = 1, kCatToken = 2 };
+
+// (I, J) of causal score block b in the order (0,0), (1,0), (1,1), (2,0), ...
+__host__ __device__ constexpr int block_i(int b) {
+  int i = 0;
+  while ((i + 1) * (i + 2) / 2 <= b) ++i;
+  return i;
+}
+__host__ __device__ constexpr int block_j(int b) { return b - block_i(b) * (block_i(b) + 1) / 2; }
+
+template <int DK, int NWV, int KH, int C, int CAT, bool STATE_ONLY>
+__global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const ChunkArgs a) {
+  using G = Geo<DK, NWV, KH, C>;
+  constexpr int NS = G::NSTG;
+  constexpr int NW = G::NW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < NW);
+  const int l32 = lane & 31, h = lane >> 5, l16 = lane & 15, g4 = lane >> 4;
+  // wave = stripe + NWV * key part: the wave owns value columns
+  // [32 stripe, +32) of the tile and keys [part * DK / KH, +DK / KH) of the state
+  const int stripe = wave % NWV, part = wave / NWV;
+
+  // workgroup -> (unit, value tile); the tiles of one unit share an XCD
+  const int f = blockIdx.x;
+  const int slot = f >> 3;
+  const int vt = slot % a.n_v;
+  const int u = (slot / a.n_v) * 8 + (f & 7);
+  if (u >= a.n_units) return;
+  const int segs = STATE_ONLY ? a.P - 1 : a.P;
+  const int bh = u / segs, sigma = u % segs;
+  const int hd = bh % a.H;
+  const int L = a.L, DV = a.DV;
+  const int dv0 = vt * G::TVW;      // first value column of the workgroup
+  const int cw = 32 * stripe;       // first column of this wave's stripe, in the tile
+  const int mk0 = part * G::NMK_OWN;  // first 32-key state tile of this wave
+  const int nchunks = (L + C - 1) / C;
+  const int c_begin = sigma * a.seg_chunks;
+  const int c_end = min(c_begin + a.seg_chunks, nchunks);
+  const bool elu = a.phi == kPhiElu1;
+
+  __shared__ __align__(16) char sQ0[STATE_ONLY ? 16 : G::QK_BYTES], sQ1[STATE_ONLY ? 16 : G::QK_BYTES],
+      sQ2[(NS > 2 && !STATE_ONLY) ? G::QK_BYTES : 16];
+  __shared__ __align__(16) char sK0[G::QK_BYTES], sK1[G::QK_BYTES], sK2[NS > 2 ? G::QK_BYTES : 16];
+  __shared__ __align__(16) char sV0[G::V_BYTES], sV1[G::V_BYTES], sV2[NS > 2 ? G::V_BYTES : 16];
+  __shared__ __align__(16) float sB0[CAT == kCatToken ? C : 4], sB1[CAT == kCatToken ? C : 4],
+      sB2[(NS > 2 && CAT == kCatToken) ? C : 4];
+  __shared__ __align__(16) char sP[STATE_ONLY ? 16 : 2 * C * C];
+  // partial inter-chunk terms handed between the key parts of a stripe:
+  // [stripe][row block][16-byte chunk k][lane]
+  __shared__ __align__(16) char sX[(STATE_ONLY || KH == 1) ? 16 : G::XCH_BYTES];
+  // per-wave weights of the current chunk: [0] e^{b_last - b_t}, [1] e^{b_t}
+  __shared__ __align__(16) float sW[NW][2][C];
+
+  auto stage_q = [&](auto BUF) -> char* {
+    constexpr int b = decltype(BUF)::value;
+    if constexpr (b == 0) return sQ0; else if constexpr (b == 1) return sQ1; else return sQ2;
+  };
+  auto stage_k = [&](auto BUF) -> char* {
+    constexpr int b = decltype(BUF)::value;
+    if constexpr (b == 0) return sK0; else if constexpr (b == 1) return sK1; else return sK2;
+  };
+  auto stage_v = [&](auto BUF) -> char* {
+    constexpr int b = decltype(BUF)::value;
+    if constexpr (b == 0) return sV0; else if constexpr (b == 1) return sV1; else return sV2;
+  };
+  auto stage_b = [&](auto BUF) -> float* {
+    constexpr int b = decltype(BUF)::value;
+    if constexpr (b == 0) return sB0; else if constexpr (b == 1) return sB1; else return sB2;
+  };
+
+  const size_t head_k = (size_t)bh * L * DK;
+  const size_t head_v = (size_t)bh * L * DV;
+  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + head_k;
+  const uint16_t* kh = static_cast<const uint16_t*>(a.k) + head_k;
+  const uint16_t* vh = static_cast<const uint16_t*>(a.v) + head_v + dv0;
+  uint16_t* oh = static_cast<uint16_t*>(a.out) + head_v + dv0 + cw;
+  const float* bws = CAT == kCatToken ? a.ws_b + (size_t)bh * L : nullptr;
+  const float lg2 = CAT == kCatHead ? log2f(a.decay[hd]) : 0.0f;  // b_i = (i + 1) lg2
+  float* wq = sW[wave][0];
+  float* eq = sW[wave][1];
+
+  // ---- loop-invariant mask/decay weights of this wave's score blocks ------
+  // block (I, J), register r: query row i = 32 I + l32, token
+  // j = 32 J + 8 (r / 4) + 4 h + r % 4; weight [j <= i] gamma^(i - j).
+  float dm[CAT == kCatToken ? 1 : G::BPW][16];
+  if constexpr (CAT != kCatToken && !STATE_ONLY) {
+#pragma unroll
+    for (int bb = 0; bb < G::BPW; ++bb) {
+      const int b = wave + NW * bb;
+      const int I = b < G::NB ? block_i(b) : 0, J = b < G::NB ? block_j(b) : 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = 32 * I + l32, j = 32 * J + 8 * (r >> 2) + 4 * h + (r & 3);
+        const float w = CAT == kCatHead ? __builtin_amdgcn_exp2f((float)(i - j) * lg2) : 1.0f;
+        dm[bb][r] = j <= i ? w : 0.0f;
+      }
+    }
+  }
+
+  // ---- initial state of this wave's part ---------------------------------
+  // own tile t (state tile mk0 + t), register r: key 32 (mk0 + t) + 8 (r / 4)
+  // + 4 h + r % 4, value column dv0 + cw + l32
+  f32x16 accS[G::NMK_OWN];
+#pragma unroll
+  for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accS[t][r] = 0.0f;
+  if constexpr (!STATE_ONLY) {
+    const int dv = dv0 + cw + l32;
+#pragma unroll
+    for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dk = 32 * (mk0 + t) + 8 * (r >> 2) + 4 * h + (r & 3);
+        float sv = a.state ? a.state[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
+        for (int p = 0; p < sigma; ++p) {
+          const size_t seg = (size_t)bh * a.P + p;
+          sv = exp2f(a.ws_logA[seg]) * sv + a.ws_S[(seg * DK + dk) * DV + dv];
+        }
+        accS[t][r] = sv;
+      }
+  }
+  // bf16 A operands of the inter-chunk term: own key step s (global step
+  // part * NKS_OWN + s) uses own tile s / 2, registers 8 (s % 2) .. +7
+  u32x4 sbf[G::NKS_OWN];
+  auto pack_state = [&]() {
+#pragma unroll
+    for (int s = 0; s < G::NKS_OWN; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sbf[s][e] = cvt2(accS[s >> 1][8 * (s & 1) + 2 * e], accS[s >> 1][8 * (s & 1) + 2 * e + 1]);
+  };
+
+  // ---- loads of one chunk: Q, K, V tiles and b into LDS --------------------
+  // DMA block i of a tile covers its 16-byte chunks 64 i .. 64 i + 63 (in
+  // swizzled order); lane l moves chunk 64 i + l.  Per-lane source offsets:
+  int koff[G::QK_PER], krow[G::QK_PER], voff[G::V_PER], vrow[G::V_PER];
+#pragma unroll
+  for (int i = 0; i < G::QK_PER; ++i) {
+    const int p = 64 * (wave + NW * i) + lane;
+    const int r = p / G::WCK, pc = p % G::WCK;
+    const int cc = pc ^ swz_xor<G::WCK>(r);
+    krow[i] = r;
+    koff[i] = r * DK + 8 * cc;
+  }
+#pragma unroll
+  for (int i = 0; i < G::V_PER; ++i) {
+    const int p = 64 * (wave + NW * i) + lane;
+    const int r = p / G::WCV, pc = p % G::WCV;
+    const int cc = pc ^ swz_xor<G::WCV>(r);
+    vrow[i] = r;
+    voff[i] = r * DV + 8 * cc;
+  }
+  constexpr int LOADS = (STATE_ONLY ? 1 : 2) * G::QK_PER + G::V_PER + (CAT == kCatToken ? 1 : 0);
+  constexpr int STORES = STATE_ONLY ? 0 : G::STORES;
+
+  auto issue_loads = [&](auto BUF, int c) {
+    const int t0 = c * C;
+    const bool full = t0 + C <= L;
+    const uint16_t* kc = kh + (size_t)t0 * DK;
+    const uint16_t* qc = qh + (size_t)t0 * DK;
+    const uint16_t* vc = vh + (size_t)t0 * DV;
+#pragma unroll
+    for (int i = 0; i < G::QK_PER; ++i) {
+      const int idx = wave + NW * i;
+      if (idx < G::QK_BLK) {
+        // rows past the sequence re-read its last row; they are zeroed before use
+        const int off = full ? koff[i] : koff[i] - max(krow[i] - (L - 1 - t0), 0) * DK;
+        dma16(kc + off, stage_k(BUF) + 1024 * idx);
+        if constexpr (!STATE_ONLY) dma16(qc + off, stage_q(BUF) + 1024 * idx);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G::V_PER; ++i) {
+      const int idx = wave + NW * i;
+      if (idx < G::V_BLK) {
+        const int off = full ? voff[i] : voff[i] - max(vrow[i] - (L - 1 - t0), 0) * DV;
+        dma16(vc + off, stage_v(BUF) + 1024 * idx);
+      }
+    }
+    if constexpr (CAT == kCatToken) {
+      // each wave brings its share of the chunk's prefix sums
+      constexpr int PER = (C + NW - 1) / NW;
+      if (lane < PER && wave * PER + lane < C) {
+        const int t = min(t0 + wave * PER + lane, L - 1);
+        dma4(bws + t, stage_b(BUF) + wave * PER);
+      }
+    }
+  };
+
+  float logA = 0.0f;
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+
+  auto body = [&](auto BUF, int c) {
+    constexpr int buf = decltype(BUF)::value;
+    const int t0 = c * C;
+    const int nvalid = min(C, L - t0);
+    char* qb = stage_q(BUF);
+    char* kb = stage_k(BUF);
+    char* vb = stage_v(BUF);
+    const float* sb = stage_b(BUF);
+
+    // Wait until this wave's loads of chunk c have landed, keeping later
+    // chunks' loads (and the stores issued since) in flight: in issue order,
+    // chunk c's loads are followed by nS chunks' stores and nL chunks' loads.
+    if constexpr (G::UNIFORM && NS == 3) {
+      const int nS = min(NS - 1, c - c_begin), nL = min(NS - 2, c_end - 1 - c);
+      if (nS == 2 && nL == 1) wait_vmcnt<2 * STORES + LOADS>();
+      else if (nS == 2) wait_vmcnt<2 * STORES>();
+      else if (nS == 1 && nL == 1) wait_vmcnt<STORES + LOADS>();
+      else if (nS == 1) wait_vmcnt<STORES>();
+      else if (nL == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    } else if constexpr (G::UNIFORM) {
+      if (c > c_begin) wait_vmcnt<STORES>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // everybody's loads of chunk c landed; chunk c-1 is finished
+    if (c + NS - 1 < c_end) issue_loads(std::integral_constant<int, (buf + NS - 1) % NS>{}, c + NS - 1);
+
+    // a short last chunk: zero the rows past the sequence (clamped copies)
+    if (nvalid < C) {
+      for (int q = tid; q < (C - nvalid) * G::WCK; q += 64 * NW) {
+        *reinterpret_cast<u32x4*>(kb + 16 * (nvalid * G::WCK + q)) = zero4;
+        if constexpr (!STATE_ONLY) *reinterpret_cast<u32x4*>(qb + 16 * (nvalid * G::WCK + q)) = zero4;
+      }
+      for (int q = tid; q < (C - nvalid) * G::WCV; q += 64 * NW)
+        *reinterpret_cast<u32x4*>(vb + 16 * (nvalid * G::WCV + q)) = zero4;
+      lds_barrier();
+    }
+    // feature map on the staged queries and keys, in place
+    if (elu) {
+      for (int q = tid; q < G::QK_BYTES / 16; q += 64 * NW) {
+        u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
+        *p = elu1_x8(*p);
+        if constexpr (!STATE_ONLY) {
+          u32x4* pq = reinterpret_cast<u32x4*>(qb + 16 * q);
+          *pq = elu1_x8(*pq);
+        }
+      }
+      lds_barrier();
+    }
+
+    // log2 decay of the chunk's last real token
+    float bL = 0.0f;
+    if constexpr (CAT == kCatHead) bL = (float)nvalid * lg2;
+    if constexpr (CAT == kCatToken) bL = sb[nvalid - 1];
+
+    // per-token weights of this wave: e^{b_last - b_t} (update; 0 past the
+    // chunk) and e^{b_t} (inter-chunk term), t = lane (+ 64)
+    if constexpr (CAT != kCatNone) {
+#pragma unroll
+      for (int t = lane; t < C; t += 64) {
+        const float bt = CAT == kCatHead ? (float)(t + 1) * lg2 : sb[t];
+        wq[t] = t < nvalid ? __builtin_amdgcn_exp2f(bL - bt) : 0.0f;
+        if constexpr (!STATE_ONLY) eq[t] = __builtin_amdgcn_exp2f(bt);
+      }
+      lds_wave_sync();
+    }
+
+    // V^T operands of this wave's stripe: lane (value cw + l32, h), tokens
+    // 16 ks + 8 h + (0..7)
+    u32x4 vA[G::NTS];
+#pragma unroll
+    for (int ks = 0; ks < G::NTS; ++ks)
+      vA[ks] = lds_tr8<G::WCV>(vb, 16 * ks + 8 * (g4 >> 1), cw + 16 * (g4 & 1), l16);
+
+    if constexpr (!STATE_ONLY) {
+      // (1a) causal score blocks of this wave -> P~ in LDS
+#pragma unroll
+      for (int bb = 0; bb < G::BPW; ++bb) {
+        const int b = wave + NW * bb;
+        if (b < G::NB) {
+          const int I = block_i(b), J = block_j(b);
+          f32x16 pacc;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
+#pragma unroll
+          for (int s = 0; s < G::NKS; ++s) {
+            const u32x4 kA = lds_b128(kb, swz<G::WCK>(32 * J + l32, 16 * s + 8 * h));
+            const u32x4 qB = lds_b128(qb, swz<G::WCK>(32 * I + l32, 16 * s + 8 * h));
+            pacc = mfma32(kA, qB, pacc);
+          }
+          // register r: token j = 32 J + 8 (r / 4) + 4 h + r % 4, row i = 32 I + l32
+          if constexpr (CAT == kCatToken) {
+            const float bi = sb[32 * I + l32];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 bj = *reinterpret_cast<const f32x4*>(&sb[32 * J + 8 * q + 4 * h]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = pacc[4 * q + e] * __builtin_amdgcn_exp2f(bi - bj[e]);
+                pacc[4 * q + e] = (I != J || 8 * q + 4 * h + e <= l32) ? x : 0.0f;
+              }
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pacc[r] *= dm[bb][r];
+          }
+          const int i = 32 * I + l32;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            u32x2 w;
+            w[0] = cvt2(pacc[4 * q + 0], pacc[4 * q + 1]);
+            w[1] = cvt2(pacc[4 * q + 2], pacc[4 * q + 3]);
+            *reinterpret_cast<u32x2*>(sP + swz<G::WCP>(i, 32 * J + 8 * q + 4 * h)) = w;
+          }
+        }
+      }
+
+      // (1b) inter-chunk term over this wave's keys, every row block:
+      //      part[I] = S_part^T Q_part^T (transposed: lane = row, registers = values)
+      pack_state();
+      f32x16 pin[G::NRB];
+#pragma unroll
+      for (int I = 0; I < G::NRB; ++I) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pin[I][r] = 0.0f;
+        const int i = 32 * I + l32;
+#pragma unroll
+        for (int s = 0; s < G::NKS_OWN; ++s) {
+          const int sg = part * G::NKS_OWN + s;
+          const u32x2 lo = lds_b64(qb, swz<G::WCK>(i, 16 * sg + 4 * h));
+          const u32x2 hi = lds_b64(qb, swz<G::WCK>(i, 16 * sg + 8 + 4 * h));
+          pin[I] = mfma32(sbf[s], u32x4{lo[0], lo[1], hi[0], hi[1]}, pin[I]);
+        }
+      }
+      // row block I belongs to key part I % KH; the other parts hand it their partial
+      if constexpr (KH > 1) {
+#pragma unroll
+        for (int I = 0; I < G::NRB; ++I)
+          if (I % KH != part) {
+            char* xb = sX + (size_t)(stripe * G::NRB + I) * 4096 + 16 * lane;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              *reinterpret_cast<f32x4*>(xb + 1024 * k) =
+                  f32x4{pin[I][4 * k], pin[I][4 * k + 1], pin[I][4 * k + 2], pin[I][4 * k + 3]};
+          }
+      }
+      lds_barrier();  // P~ and the partials complete
+
+      // (2) outputs of this wave's row blocks: O^T = diag(e^b) (S^T Q^T) + V^T P~^T
+#pragma unroll
+      for (int I = 0; I < G::NRB; ++I) {
+        if (I % KH != part) continue;
+        f32x16 acc = pin[I];
+        if constexpr (KH > 1) {
+          const char* xb = sX + (size_t)(stripe * G::NRB + I) * 4096 + 16 * lane;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(xb + 1024 * k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * k + e] += x[e];
+          }
+        }
+        const int i = 32 * I + l32;
+        if constexpr (CAT != kCatNone) {
+          const float er = eq[i];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] *= er;
+        }
+#pragma unroll
+        for (int J = 0; J <= I; ++J)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int ks = 2 * J + s2;
+            const u32x4 pB = lds_b128(sP, swz<G::WCP>(i, 16 * ks + 8 * h));
+            acc = mfma32(vA[ks], pB, acc);
+          }
+        // lane: row t0 + i, value columns cw + 8 q + 4 h + (0..3)
+        if (i < nvalid) {
+          uint16_t* orow = oh + (size_t)(t0 + i) * DV + 4 * h;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            u32x2 w;
+            w[0] = cvt2(acc[4 * q + 0], acc[4 * q + 1]);
+            w[1] = cvt2(acc[4 * q + 2], acc[4 * q + 3]);
+            *reinterpret_cast<u32x2*>(orow + 8 * q) = w;
+          }
+        }
+      }
+    }
+
+    // (3) state update of this wave's tiles: S <- e^{b_last} S + K^T diag(e^{b_last - b}) V
+    if constexpr (CAT != kCatNone) {
+      const float eL = __builtin_amdgcn_exp2f(bL);
+#pragma unroll
+      for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accS[t][r] *= eL;
+    }
+#pragma unroll
+    for (int ks = 0; ks < G::NTS; ++ks) {
+      u32x4 vB = vA[ks];
+      if constexpr (CAT != kCatNone) {
+        const int tb = 16 * ks + 8 * h;
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wq[tb]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wq[tb + 4]);
+        const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vB[e] = cvt2(bf16_to_f32(vB[e] & 0xffffu) * w[2 * e], bf16_to_f32(vB[e] >> 16) * w[2 * e + 1]);
+      }
+#pragma unroll
+      for (int t = 0; t < G::NMK_OWN; ++t) {
+        const u32x4 kA =
+            lds_tr8<G::WCK>(kb, 16 * ks + 8 * (g4 >> 1), 32 * (mk0 + t) + 16 * (g4 & 1), l16);
+        accS[t] = mfma32(kA, vB, accS[t]);
+      }
+    }
+    logA += bL;
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  if (c_begin < c_end) issue_loads(S0{}, c_begin);
+  if constexpr (NS == 3) {
+    if (c_begin + 1 < c_end) issue_loads(S1{}, c_begin + 1);
+    for (int c = c_begin; c < c_end; c += 3) {
+      body(S0{}, c);
+      if (c + 1 < c_end) body(S1{}, c + 1);
+      if (c + 2 < c_end) body(S2{}, c + 2);
+    }
+  } else {
+    for (int c = c_begin; c < c_end; c += 2) {
+      body(S0{}, c);
+      if (c + 1 < c_end) body(S1{}, c + 1);
+    }
+  }
+
+  // ---- epilogue ---------------------------------------------------------
+  float* dst = nullptr;
+  if constexpr (STATE_ONLY) {
+    dst = a.ws_S + ((size_t)bh * a.P + sigma) * DK * DV;
+    if (vt == 0 && tid == 0) a.ws_logA[(size_t)bh * a.P + sigma] = logA;
+  } else {
+    if (sigma == a.P - 1 && a.state != nullptr) dst = a.state + (size_t)bh * DK * DV;
+  }
+  if (dst != nullptr) {
+    const int dv = dv0 + cw + l32;
+#pragma unroll
+    for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        dst[(size_t)(32 * (mk0 + t) + 8 * (r >> 2) + 4 * h + (r & 3)) * DV + dv] = accS[t][r];
+  }
+}
+
+// ---- launch and dispatch ----------------------------------------------------
+template <int DK, int NWV, int KH, int C, int CAT>
+hipError_t launch_one(const ChunkArgs& a, bool state_only, hipStream_t s) {
+  const int groups = (a.n_units + 7) / 8;
+  const dim3 grid(groups * 8 * a.n_v), block(64 * NWV * KH);
+  if (state_only)
+    hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DK, int NWV, int KH, int CAT>
+hipError_t dispatch_c(const ChunkArgs& a, bool so, hipStream_t s) {
+  switch (a.C) {
+    case 32:
+      if constexpr (Geo<DK, NWV, KH, 32>::LDS <= kMaxLds) return launch_one<DK, NWV, KH, 32, CAT>(a, so, s);
+      return hipErrorInvalidValue;
+    case 64:
+      if constexpr (Geo<DK, NWV, KH, 64>::LDS <= kMaxLds) return launch_one<DK, NWV, KH, 64, CAT>(a, so, s);
+      return hipErrorInvalidValue;
+    case 128:
+      if constexpr (Geo<DK, NWV, KH, 128>::LDS <= kMaxLds) return launch_one<DK, NWV, KH, 128, CAT>(a, so, s);
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+// a.tv is the workgroup's value width (32, 64 or 128 columns: 1, 2, 4
+// stripes); a.ng the number of key parts per stripe (1 or 2)
+template <int DK, int CAT>
+hipError_t dispatch_w(const ChunkArgs& a, bool so, hipStream_t s) {
+  if (a.ng == 2) {
+    if constexpr (DK >= 64) {
+      switch (a.tv) {
+        case 32: return dispatch_c<DK, 1, 2, CAT>(a, so, s);
+        case 64: return dispatch_c<DK, 2, 2, CAT>(a, so, s);
+        case 128: return dispatch_c<DK, 4, 2, CAT>(a, so, s);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (a.tv) {
+    case 32: return dispatch_c<DK, 1, 1, CAT>(a, so, s);
+    case 64: return dispatch_c<DK, 2, 1, CAT>(a, so, s);
+    case 128: return dispatch_c<DK, 4, 1, CAT>(a, so, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DK>
+hipError_t dispatch_cat(const ChunkArgs& a, bool so, hipStream_t s) {
+  switch (a.decay_kind) {
+    case kDecayNone: return dispatch_w<DK, kCatNone>(a, so, s);
+    case kDecayHead: return dispatch_w<DK, kCatHead>(a, so, s);
+    default: return dispatch_w<DK, kCatToken>(a, so, s);
+  }
+}
+
+template <int DK, int NWV, int KH>
+constexpr size_t lds_c(int C) {
+  return C == 32 ? Geo<DK, NWV, KH, 32>::LDS
+                 : C == 64 ? Geo<DK, NWV, KH, 64>::LDS : Geo<DK, NWV, KH, 128>::LDS;
+}
+template <int DK>
+constexpr size_t lds_of(int TVW, int KH, int C) {
+  if constexpr (DK >= 64) {
+    if (KH == 2)
+      return TVW == 32 ? lds_c<DK, 1, 2>(C) : TVW == 64 ? lds_c<DK, 2, 2>(C) : lds_c<DK, 4, 2>(C);
+  }
+  return TVW == 32 ? lds_c<DK, 1, 1>(C) : TVW == 64 ? lds_c<DK, 2, 1>(C) : lds_c<DK, 4, 1>(C);
+}
+
+}  // namespace stripe
+
+hipError_t launch_chunk_stripe_dk32(const ChunkArgs& a, bool state_only, hipStream_t s);
+hipError_t launch_chunk_stripe_dk64(const ChunkArgs& a, bool state_only, hipStream_t s);
+hipError_t launch_chunk_stripe_dk128(const ChunkArgs& a, bool state_only, hipStream_t s);
+
+}  // namespace la

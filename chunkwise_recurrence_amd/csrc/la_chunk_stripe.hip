@@ -1,0 +1,30 @@
+// Dispatch of the stripe kernel (la_chunk_stripe.h) by key dimension, and the
+// shapes it supports.
+#include "la_chunk_stripe.h"
+
+namespace la {
+
+bool chunk_stripe_supported(int DK, int TVW, int KH, int C) {
+  if (DK != 32 && DK != 64 && DK != 128) return false;
+  if (TVW != 32 && TVW != 64 && TVW != 128) return false;
+  if (C != 32 && C != 64 && C != 128) return false;
+  if (KH != 1 && !(KH == 2 && DK >= 64)) return false;
+  size_t lds = 0;
+  switch (DK) {
+    case 32: lds = stripe::lds_of<32>(TVW, KH, C); break;
+    case 64: lds = stripe::lds_of<64>(TVW, KH, C); break;
+    default: lds = stripe::lds_of<128>(TVW, KH, C); break;
+  }
+  return lds <= stripe::kMaxLds;
+}
+
+hipError_t launch_chunk_stripe(const ChunkArgs& a, bool state_only, hipStream_t s) {
+  switch (a.DK) {
+    case 32: return launch_chunk_stripe_dk32(a, state_only, s);
+    case 64: return launch_chunk_stripe_dk64(a, state_only, s);
+    case 128: return launch_chunk_stripe_dk128(a, state_only, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace la

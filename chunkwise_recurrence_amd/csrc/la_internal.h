@@ -28,8 +28,9 @@ struct ChunkArgs {
   int seg_chunks;       // chunks per segment (the last one may hold fewer)
   int n_units;          // work units: B*H*P (main) or B*H*(P-1) (state pass)
   int n_v;              // value tiles per head (one workgroup each)
-  int tv;               // value columns per column group of a workgroup
-  int ng;               // column groups (of 4 waves) per workgroup
+  int tv;               // strip kernel: value columns per column group; stripe kernel: per workgroup
+  int ng;               // strip kernel: column groups (of 4 waves) per workgroup;
+                        // stripe kernel: key parts per 32-column stripe
   int phi, decay_kind;
 };
 
@@ -46,6 +47,7 @@ struct DecodeArgs {
 
 // Launchers (return the launch error, hipSuccess when enqueued).
 hipError_t launch_chunk_bf16(const ChunkArgs& a, bool state_only, hipStream_t s);
+hipError_t launch_chunk_stripe(const ChunkArgs& a, bool state_only, hipStream_t s);
 hipError_t launch_decay_prefix(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
@@ -54,5 +56,8 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 // Whether a bf16 kernel exists for key dim DK, NG column groups of TV columns
 // and chunk C (and fits the LDS).
 bool chunk_bf16_supported(int DK, int TV, int NG, int C);
+// Whether the stripe kernel exists for key dim DK, TVW value columns per
+// workgroup, KH key parts per stripe and chunk C (and fits the LDS).
+bool chunk_stripe_supported(int DK, int TVW, int KH, int C);
 
 }  // namespace la

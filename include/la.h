@@ -137,26 +137,46 @@ la_status la_decode_step(const void* q, const void* k, const void* v, int dtype,
 const char* la_status_string(int status);
 
 /*
- * la_chunk_fwd_plan -- the launch plan la_chunk_fwd would use (host only,
- * for tests and benchmarks): the value columns one workgroup covers, the
- * number of sequence segments each head is split into, and the number of
- * 4-wave column groups per workgroup (bf16).  Any output pointer may be NULL.
- * Returns LA_OK or the error la_chunk_fwd would return for these arguments.
+ * Launch plan of la_chunk_fwd (host only, for tests and benchmarks).
+ *   kernel    LA_KERNEL_F32 (fp32 inputs: one workgroup per head and 32-column
+ *             tile), LA_KERNEL_STRIP (bf16: 16x16 MFMA, 4-wave column groups,
+ *             any d_k, d_v, C) or LA_KERNEL_STRIPE (bf16: 32x32 MFMA, one
+ *             wave per 32 value columns holding its part of the state in
+ *             registers; d_k, d_v >= 32 and C >= 32).
+ *   dv_tile   value columns one workgroup covers
+ *   segments  sequence segments per head (> 1: a state pass runs first)
+ *   groups    strip kernel: 4-wave column groups per workgroup (1 or 2);
+ *             stripe kernel: waves per 32-column stripe, each holding a
+ *             share of the keys of the state (1 or 2; 2 needs d_k >= 64)
  */
-la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype,
-                            int* dv_tile, int* segments, int* groups);
+typedef struct {
+  int kernel;
+  int dv_tile;
+  int segments;
+  int groups;
+} la_plan;
+
+enum { LA_KERNEL_AUTO = 0, LA_KERNEL_STRIP = 1, LA_KERNEL_STRIPE = 2, LA_KERNEL_F32 = 3 };
 
 /*
- * la_set_plan -- override the launch plan la_chunk_fwd chooses for the bf16
- * path: the value columns one workgroup covers (16, 32, 64 or 128), the
- * number of sequence segments per head (>= 1), and the number of 4-wave
- * column groups per workgroup (1 or 2).  0 restores the automatic choice for
- * that field; values that do not fit a given call are reduced to ones that
- * do.  Results do not depend on the plan beyond rounding; tests use it to
- * check exactly that.  Process-wide; returns LA_ERR_UNSUPPORTED for an
- * invalid tile or group count, LA_ERR_SHAPE for a negative segment count.
+ * la_chunk_fwd_plan -- the plan la_chunk_fwd would use for these arguments
+ * (written to *plan).  Returns LA_OK, LA_ERR_NULL for a NULL plan, or the
+ * error la_chunk_fwd would return for these shapes.
  */
-la_status la_set_plan(int dv_tile, int segments, int groups);
+la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype,
+                            la_plan* plan);
+
+/*
+ * la_set_plan -- override the bf16 plan process-wide.  Fields at 0 (or a
+ * NULL plan) keep the automatic choice: kernel (LA_KERNEL_STRIP or
+ * LA_KERNEL_STRIPE), dv_tile (16, 32, 64 or 128), segments (>= 1), groups
+ * (1 or 2).  Values that do not fit a given call are reduced to ones that do
+ * (a stripe plan the shape does not allow falls back to the strip kernel).
+ * Results do not depend on the plan beyond rounding; tests use it to check
+ * exactly that.  Returns LA_ERR_UNSUPPORTED for an invalid kernel, tile or
+ * group count, LA_ERR_SHAPE for a negative segment count.
+ */
+la_status la_set_plan(const la_plan* plan);
 
 #ifdef __cplusplus
 }

@@ -66,7 +66,7 @@ def test_zero_length_is_ok_without_touching_memory():
 
 def test_workspace_is_required_when_the_plan_splits_the_sequence():
     # 1 head of 64 x 64 over 64K tokens: the plan splits the sequence
-    tile, P, groups = la.plan(1, 1, 65536, 64, 64, 64)
+    kernel, tile, P, groups = la.plan(1, 1, 65536, 64, 64, 64)
     assert P > 1
     need = la.chunk_fwd_workspace_bytes(1, 1, 65536, 64, 64, 64)
     assert need >= P * 64 * 64 * 4
@@ -78,44 +78,62 @@ def test_workspace_is_required_when_the_plan_splits_the_sequence():
     assert _fwd(L=65536, ws=P8, ws_bytes=need) == ALIGN
 
 
+STRIP, STRIPE, F32 = la.KERNEL_STRIP, la.KERNEL_STRIPE, la.KERNEL_F32
+
+
 def test_plans_of_the_workloads():
-    # 4-wave workgroups over 64-column value tiles; segments bring the grid
-    # to 256 workgroups.  retnet: 64 heads x 2 tiles x 2 segments
-    assert la.plan(2, 32, 16384, 128, 128, 64) == (64, 2, 1)
-    # gated: 16 heads x 2 tiles x 8 segments
-    assert la.plan(1, 16, 65536, 128, 128, 64) == (64, 8, 1)
-    # elu: 64 heads x 4 segments
-    assert la.plan(4, 16, 4096, 64, 64, 64) == (64, 4, 1)
-    assert la.plan(1, 1, 100, 16, 16, 16) == (16, 1, 1)
-    # two 64-column groups of 128-token chunks exceed the LDS: one group
-    la.set_plan(128, 0, 2)
-    try:
-        assert la.plan(1, 1, 100, 128, 128, 128) == (64, 1, 2)
-    finally:
-        la.set_plan(0, 0, 0)
-    # fp32: one segment, 16- or 32-wide tiles
-    assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32) == (16, 1, 1)
+    # the stripe kernel: one workgroup per head (2 waves per 32 value columns)
+    # and segment; segments bring the grid to 256 workgroups.  retnet: 64
+    # heads x 4 segments
+    assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
+    # gated: 16 heads x 16 segments
+    assert la.plan(1, 16, 65536, 128, 128, 64) == (STRIPE, 128, 16, 2)
+    # elu: 64 heads x 4 segments, 4-wave workgroups
+    assert la.plan(4, 16, 4096, 64, 64, 64) == (STRIPE, 64, 4, 2)
+    # d_k = 32 keeps one wave per stripe
+    assert la.plan(1, 1, 100, 32, 32, 64) == (STRIPE, 32, 1, 1)
+    # 16-wide heads or 16-token chunks: the strip kernel
+    assert la.plan(1, 1, 100, 16, 16, 16) == (STRIP, 16, 1, 1)
+    assert la.plan(1, 1, 100, 128, 128, 16)[0] == STRIP
+    assert la.plan(1, 1, 100, 16, 128, 64)[0] == STRIP
+    # 128-token chunks at d_k = 128 exceed the stripe kernel's LDS; at d_k = 64 they fit
+    assert la.plan(1, 1, 100, 128, 128, 128) == (STRIP, 16, 1, 1)
+    assert la.plan(1, 1, 100, 64, 64, 128)[0] == STRIPE
+    # fp32: its own kernel, one segment, 16- or 32-wide tiles
+    assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32) == (F32, 16, 1, 1)
     assert la.chunk_fwd_workspace_bytes(1, 1, 300, 16, 16, 64, la.LA_F32) == 0
 
 
 def test_plan_override_and_clamping():
     try:
-        la.set_plan(64, 3, 1)
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (64, 3, 1)
-        assert la.plan(1, 1, 64 * 2, 128, 32, 64) == (32, 2, 1)   # tile clamped to d_v, P to chunks
-        la.set_plan(32, 0, 2)
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64)[::2] == (32, 2)
-        la.set_plan(16, 0, 2)   # 8-column groups do not exist
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64)[::2] == (16, 1)
+        la.set_plan(STRIP, 64, 3, 1)
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (STRIP, 64, 3, 1)
+        assert la.plan(1, 1, 64 * 2, 128, 32, 64) == (STRIP, 32, 2, 1)  # tile clamped to d_v, P to chunks
+        la.set_plan(STRIP, 32, 0, 2)
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64)[1::2] == (32, 2)
+        la.set_plan(STRIP, 16, 0, 2)   # 8-column groups do not exist
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64)[1::2] == (16, 1)
+        la.set_plan(STRIP, 64, 0, 2)
+        assert la.plan(1, 1, 100, 64, 64, 64) == (STRIP, 64, 1, 2)
+        # two 64-column groups of d_k = 128 exceed the LDS: the tile is halved
+        assert la.plan(1, 1, 100, 128, 128, 64)[1::2] == (64, 2)
+        la.set_plan(STRIPE, 64, 2)
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 64, 2, 2)
+        la.set_plan(STRIPE, 128, 2, 1)
+        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 128, 2, 1)
+        # a stripe plan the shape does not allow falls back to the strip kernel
+        assert la.plan(1, 1, 64 * 30, 16, 16, 64)[0] == STRIP
         with pytest.raises(la.LAError):
-            la.set_plan(48, 0)
+            la.set_plan(STRIP, 48, 0)
         with pytest.raises(la.LAError):
-            la.set_plan(0, -1)
+            la.set_plan(STRIP, 0, -1)
         with pytest.raises(la.LAError):
-            la.set_plan(0, 0, 3)
+            la.set_plan(STRIP, 0, 0, 3)
+        with pytest.raises(la.LAError):
+            la.set_plan(7)
     finally:
-        la.set_plan(0, 0, 0)
-    assert la.plan(2, 32, 16384, 128, 128, 64) == (64, 2, 1)
+        la.set_plan()
+    assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
 
 
 def _dec(**kw):

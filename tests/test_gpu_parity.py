@@ -105,24 +105,29 @@ def test_chunk_size_invariance_on_gpu(gpu_lib):
         assert oracle.rel_err(o, outs[0]) < 1e-2
 
 
-@pytest.mark.parametrize("tile,segments,groups", [
-    (16, 1, 1), (32, 1, 1), (64, 1, 1), (32, 1, 2), (64, 1, 2), (128, 1, 2), (32, 2, 1),
-    (32, 3, 2), (64, 8, 1), (128, 5, 2), (128, 3, 2), (64, 2, 2)])
-def test_launch_plan_invariance(gpu_lib, tile, segments, groups):
-    """Value tile, column groups and sequence segments change the work split, not the result."""
+@pytest.mark.parametrize("kernel,tile,segments,groups", [
+    (1, 16, 1, 1), (1, 32, 1, 1), (1, 64, 1, 1), (1, 32, 1, 2), (1, 64, 1, 2), (1, 32, 2, 1),
+    (1, 32, 3, 2), (1, 64, 8, 1), (1, 64, 5, 2), (1, 64, 2, 2), (1, 16, 4, 1),
+    (2, 128, 1, 1), (2, 64, 5, 1), (2, 32, 2, 1), (2, 128, 1, 2), (2, 64, 1, 2), (2, 32, 1, 2),
+    (2, 128, 3, 2), (2, 64, 5, 2), (2, 32, 8, 2), (2, 128, 21, 2)])
+def test_launch_plan_invariance(gpu_lib, kernel, tile, segments, groups):
+    """Kernel, value tile, column groups and sequence segments change the work split,
+    not the result."""
     la = gpu_lib
-    la.set_plan(tile, segments, groups)
+    la.set_plan(kernel, tile, segments, groups)
     try:
         # 21 chunks: segments of ceil(21 / P) chunks, so P = 8 runs as 7 segments of 3
         got = la.plan(1, 2, 64 * 20 + 17, 128, 128, 64)
-        assert got[::2] == (tile, groups) and got[1] == -(-21 // -(-21 // segments))
+        assert got[:2] == (kernel, tile) and got[2] == -(-21 // -(-21 // segments))
+        assert got[3] == groups
         for kind in (W.DECAY_NONE, W.DECAY_GATE, W.DECAY_HEAD):
             c = W.RandomCase(1, 2, 64 * 20 + 17, 128, 128, torch.bfloat16, 0, kind,
                              seed=tile + segments + kind, scale=1.0 / np.sqrt(128),
                              gate_shift=-5.0, with_state=True)
-            _check_case(la, c, 64, f"plan tile={tile} P={segments} groups={groups}")
+            _check_case(la, c, 64, f"plan kernel={kernel} tile={tile} P={segments} "
+                                   f"groups={groups}")
     finally:
-        la.set_plan(0, 0, 0)
+        la.set_plan()
 
 
 def test_resume_equals_one_call(gpu_lib):
