@@ -265,8 +265,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profile_value(TRAFFIC_PROFILE, "hbm_bytes_per_forward"),
-                     "kernel": "chunk_bf16_kernel: segment state pass + output pass of one "
-                               "la_chunk_fwd (HIP events around the call)",
+                     "kernel": "the chunked forward of one la_chunk_fwd: its segment state pass "
+                               "and output pass (HIP events around the call)",
                      "kernel_ms": c["kern_ms"], "algorithmic_bytes": c["bytes"],
                      "mfma_tflops": c["flops"] / (c["kern_ms"] / 1000.0) / 1e12,
                      "mfma_frac": c["flops"] / (c["kern_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS,

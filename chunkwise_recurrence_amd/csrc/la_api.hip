@@ -11,8 +11,10 @@
 
 namespace {
 
-// Workgroups the bf16 plan aims for: one per compute unit of an MI355X.
-constexpr int kTargetWorkgroups = 256;
+// Workgroups the bf16 plan aims for: one 8-wave stripe workgroup per compute
+// unit of an MI355X, or two 4-wave strip workgroups per compute unit.
+constexpr int kTargetStripe = 256;
+constexpr int kTargetStrip = 512;
 // A segment of the sequence keeps at least this many chunks.
 constexpr int kMinSegmentChunks = 4;
 
@@ -64,11 +66,14 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   }
   const int forced_kernel = g_plan_kernel.load(), forced_tile = g_plan_tile.load(),
             forced_groups = g_plan_groups.load();
-  // The stripe kernel (32x32 MFMA, the state in registers, one workgroup per
-  // head and segment) where the shape allows it; the strip kernel (16x16
-  // MFMA, 4-wave groups over 64-column tiles) otherwise.
+  // 128-wide heads: the stripe kernel (32x32 MFMA, the state in registers,
+  // one 8-wave workgroup per head and segment).  Narrower heads, 16-token
+  // chunks and shapes the stripe kernel does not cover: the strip kernel
+  // (16x16 MFMA, 4-wave workgroups over 32-column tiles, siblings sharing q
+  // and k through L2).  Both measured on MI355X; la_set_plan overrides.
   int tile = 0;
-  if (forced_kernel != LA_KERNEL_STRIP) {
+  const bool stripe_auto = d_v == 128 && d_k >= 64;
+  if (forced_kernel == LA_KERNEL_STRIPE || (forced_kernel == 0 && stripe_auto)) {
     // two waves per 32-column stripe (each holding half of the keys) where
     // d_k allows, for two waves per SIMD
     auto parts_for = [&](int t) {
@@ -86,7 +91,7 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   }
   if (p.kernel == 0) {
     p.kernel = LA_KERNEL_STRIP;
-    tile = forced_tile > 0 ? forced_tile : (d_v < 64 ? d_v : 64);
+    tile = forced_tile > 0 ? forced_tile : (d_v < 32 ? d_v : 32);
     while (tile > d_v) tile /= 2;
     auto groups_for = [&](int t) {
       int g = forced_groups > 0 ? forced_groups : 1;
@@ -101,7 +106,8 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   }
   int P = 1;
   const long long units = (long long)heads * (d_v / tile);
-  while (units * P < kTargetWorkgroups && (long long)P * 2 * kMinSegmentChunks <= nchunks) P *= 2;
+  const long long target = p.kernel == LA_KERNEL_STRIPE ? kTargetStripe : kTargetStrip;
+  while (units * P < target && (long long)P * 2 * kMinSegmentChunks <= nchunks) P *= 2;
   const int forced_P = g_plan_segments.load();
   if (forced_P > 0) P = forced_P;
   if (P > nchunks) P = nchunks;

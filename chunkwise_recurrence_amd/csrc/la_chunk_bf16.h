@@ -91,14 +91,11 @@ struct Geo {
   // loads in flight.
   static constexpr bool UNIFORM = NK_CHUNKS % (64 * NW) == 0 && NV_CHUNKS % (64 * NW) == 0 &&
                                   NSTRIP % 4 == 0 && C % NW == 0;
-  // a stage holds the chunk's Q and K tiles (same shape), its V tile and its
-  // decay prefix; S^T is double-buffered
   static constexpr size_t stage_bytes(int n) {
-    return (size_t)n * (4 * (size_t)K_TILE + 2 * (size_t)V_TILE + 4 * (size_t)CP) +
+    return (size_t)n * (2 * (size_t)K_TILE + 2 * (size_t)V_TILE + 4 * (size_t)CP) +
            2 * 2 * (size_t)S_TILE;
   }
-  // pipeline depth: three stages (loads two chunks ahead) where they fit;
-  // 256 bytes cover the placeholder arrays of unused stages
+  // pipeline depth: three stages (loads two chunks ahead) where they fit
   static constexpr int NSTG = (UNIFORM && stage_bytes(3) + 256 <= 160 * 1024) ? 3 : 2;
   static constexpr size_t LDS_MAIN = stage_bytes(NSTG) + 256;
   // precomputed per-lane mask/decay weights only while they stay small
@@ -187,12 +184,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is six bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-
-// Workgroup barrier for data exchanged through LDS only: this wave's LDS
-// accesses complete (lgkmcnt 0), then s_barrier.  No memory fence, so global
-// loads and stores in flight (the prefetch of later chunks) stay in flight;
-// the empty asm statements keep the compiler from moving memory accesses
-// across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
@@ -235,8 +226,6 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
   // stage and the reads of another are then provably disjoint, so the
   // compiler does not wait for the prefetch before touching LDS.
   constexpr int KB = G::K_TILE * 2, VB = G::V_TILE * 2, BB = CAT == kCatToken ? G::CP : 4;
-  constexpr int QB = STATE_ONLY ? 16 : KB;
-  __shared__ __align__(16) char sQ0[QB], sQ1[QB], sQ2[NS > 2 ? QB : 16];
   __shared__ __align__(16) char sK0[KB], sK1[KB], sK2[NS > 2 ? KB : 16];
   __shared__ __align__(16) char sV0[VB], sV1[VB], sV2[NS > 2 ? VB : 16];
   __shared__ __align__(16) float sB0[BB], sB1[BB], sB2[NS > 2 ? BB : 4];
@@ -244,10 +233,6 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
   auto stage_k = [&](auto BUF) -> char* {
     constexpr int b = decltype(BUF)::value;
     if constexpr (b == 0) return sK0; else if constexpr (b == 1) return sK1; else return sK2;
-  };
-  auto stage_q = [&](auto BUF) -> char* {
-    constexpr int b = decltype(BUF)::value;
-    if constexpr (b == 0) return sQ0; else if constexpr (b == 1) return sQ1; else return sQ2;
   };
   auto stage_v = [&](auto BUF) -> char* {
     constexpr int b = decltype(BUF)::value;
@@ -360,12 +345,13 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
     vrow[i] = r;
     voff[i] = r * DV + 8 * cc;
   }
+  // Q of each stage, in registers
+  u32x4 qst[NS][G::SPW][G::KSTEPS];
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
   // Vector memory instructions one chunk's loads and stores issue per wave
-  // (meaningful when G::UNIFORM): K, V and (output pass) Q blocks, the decay
-  // prefix, and the output rows.
-  constexpr int LOADS = KBLK + VBLK + (CAT == kCatToken ? 1 : 0) + (STATE_ONLY ? 0 : KBLK);
+  // (meaningful when G::UNIFORM).
+  constexpr int LOADS = KBLK + VBLK + (CAT == kCatToken ? 1 : 0) + (STATE_ONLY ? 0 : G::SPW * G::KSTEPS);
   constexpr int STORES = STATE_ONLY ? 0 : G::SPW * G::NTV;
 
   auto issue_loads = [&](auto BUF, int c) {
@@ -373,7 +359,6 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
     const int t0 = c * C;
     const bool full = t0 + C <= L;
     const uint16_t* kc = kh + (size_t)t0 * DK;
-    const uint16_t* qc = qh + (size_t)t0 * DK;
     const uint16_t* vc = vh + (size_t)t0 * DV;
 #pragma unroll
     for (int i = 0; i < KBLK; ++i) {
@@ -383,17 +368,6 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
         // rows past the sequence re-read its last row; they are zeroed before use
         const int off = full ? koff[i] : koff[i] - (max(krow[i] - (L - 1 - t0), 0)) * DK;
         dma16(kc + off, stage_k(BUF) + 1024 * idx);
-      }
-    }
-    if constexpr (!STATE_ONLY) {
-#pragma unroll
-      for (int i = 0; i < KBLK; ++i) {
-        const int idx = wave + NW * i;
-        const int q = 64 * idx + lane;
-        if (64 * idx < G::NK_CHUNKS && q < G::NK_CHUNKS) {
-          const int off = full ? koff[i] : koff[i] - (max(krow[i] - (L - 1 - t0), 0)) * DK;
-          dma16(qc + off, stage_q(BUF) + 1024 * idx);
-        }
       }
     }
 #pragma unroll
@@ -413,6 +387,22 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
         dma4(bws + t, stage_b(BUF) + wave * PER);
       }
     }
+    if constexpr (!STATE_ONLY) {
+#pragma unroll
+      for (int j = 0; j < G::SPW; ++j) {
+        const int st = wl + 4 * j;
+        const int t = t0 + 16 * st + l16;
+#pragma unroll
+        for (int s = 0; s < G::KSTEPS; ++s) {
+          // clamped in-bounds address; rows past the sequence and key columns
+          // past DK are zeroed where the registers are used (not here, which
+          // would wait for the load)
+          const int col = 32 * s + 8 * g4;
+          qst[buf][j][s] =
+              *reinterpret_cast<const u32x4*>(qh + (size_t)min(t, L - 1) * DK + min(col, DK - 8));
+        }
+      }
+    }
   };
 
   float logA = 0.0f;
@@ -422,7 +412,6 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
     const int t0 = c * C;
     const int nvalid = min(C, L - t0);
     char* kb = stage_k(BUF);
-    char* qb = stage_q(BUF);
     char* vb = stage_v(BUF);
     const float* sb = stage_b(BUF);
     const int sp = (c - c_begin) & 1;  // S^T double buffer: read sp, write sp ^ 1
@@ -445,40 +434,47 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
       wait_vmcnt<0>();
     }
     lds_barrier();  // everybody's loads of chunk c landed; chunk c-1 is finished
-    if (c + NS - 1 < c_end) issue_loads(std::integral_constant<int, (buf + NS - 1) % NS>{}, c + NS - 1);
-
-    // a short last chunk: zero the rows past the sequence (they hold clamped copies)
-    if (nvalid < C) {
-      for (int q = tid; q < (C - nvalid) * G::WCK; q += 64 * NW) {
-        *reinterpret_cast<u32x4*>(kb + 16 * (nvalid * G::WCK + q)) = zero4;
-        if constexpr (!STATE_ONLY) *reinterpret_cast<u32x4*>(qb + 16 * (nvalid * G::WCK + q)) = zero4;
-      }
-      for (int q = tid; q < (C - nvalid) * G::WCV; q += 64 * NW)
-        *reinterpret_cast<u32x4*>(vb + 16 * (nvalid * G::WCV + q)) = zero4;
-      lds_barrier();
-    }
-    // feature map on the staged queries and keys, in place
-    if (elu) {
-      for (int q = tid; q < G::NK_CHUNKS; q += 64 * NW) {
-        u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
-        *p = elu1_x8(*p);
-        if constexpr (!STATE_ONLY) {
-          u32x4* pq = reinterpret_cast<u32x4*>(qb + 16 * q);
-          *pq = elu1_x8(*pq);
-        }
-      }
-      lds_barrier();
-    }
-    // this wave's query rows: B operands of the score and inter-chunk MFMAs
     u32x4 qcur[G::SPW][G::KSTEPS];
     if constexpr (!STATE_ONLY) {
 #pragma unroll
       for (int j = 0; j < G::SPW; ++j)
 #pragma unroll
-        for (int s = 0; s < G::KSTEPS; ++s)
-          qcur[j][s] = (DK >= 32 || g4 < 2)
-                           ? lds_b128(qb, swz<G::WCK>(min(16 * (wl + 4 * j), C - 16) + l16, 32 * s + 8 * g4))
-                           : zero4;
+        for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = qst[buf][j][s];
+      if (nvalid < C || DK < 32) {
+        no_speculation();
+#pragma unroll
+        for (int j = 0; j < G::SPW; ++j)
+#pragma unroll
+          for (int s = 0; s < G::KSTEPS; ++s) {
+            const bool ok = 16 * (wl + 4 * j) + l16 < nvalid && 32 * s + 8 * g4 < DK;
+            qcur[j][s] = ok ? qcur[j][s] : zero4;
+          }
+      }
+      if (elu) {
+        no_speculation();
+#pragma unroll
+        for (int j = 0; j < G::SPW; ++j)
+#pragma unroll
+          for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = elu1_x8(qcur[j][s]);
+      }
+    }
+    if (c + NS - 1 < c_end) issue_loads(std::integral_constant<int, (buf + NS - 1) % NS>{}, c + NS - 1);
+
+    // a short last chunk: zero the rows past the sequence (they hold clamped copies)
+    if (nvalid < C) {
+      for (int q = tid; q < (C - nvalid) * G::WCK; q += 64 * NW)
+        *reinterpret_cast<u32x4*>(kb + 16 * (nvalid * G::WCK + q)) = zero4;
+      for (int q = tid; q < (C - nvalid) * G::WCV; q += 64 * NW)
+        *reinterpret_cast<u32x4*>(vb + 16 * (nvalid * G::WCV + q)) = zero4;
+      lds_barrier();
+    }
+    // feature map on the staged keys, in place
+    if (elu) {
+      for (int q = tid; q < G::NK_CHUNKS; q += 64 * NW) {
+        u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
+        *p = elu1_x8(*p);
+      }
+      lds_barrier();
     }
 
     // log2-decay of the chunk's last real token (the state's decay over the chunk)

@@ -88,17 +88,16 @@ def test_plans_of_the_workloads():
     assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
     # gated: 16 heads x 16 segments
     assert la.plan(1, 16, 65536, 128, 128, 64) == (STRIPE, 128, 16, 2)
-    # elu: 64 heads x 4 segments, 4-wave workgroups
-    assert la.plan(4, 16, 4096, 64, 64, 64) == (STRIPE, 64, 4, 2)
-    # d_k = 32 keeps one wave per stripe
-    assert la.plan(1, 1, 100, 32, 32, 64) == (STRIPE, 32, 1, 1)
-    # 16-wide heads or 16-token chunks: the strip kernel
+    # narrower heads: the strip kernel over 32-column tiles.  elu: 64 heads x
+    # 2 tiles x 4 segments
+    assert la.plan(4, 16, 4096, 64, 64, 64) == (STRIP, 32, 4, 1)
     assert la.plan(1, 1, 100, 16, 16, 16) == (STRIP, 16, 1, 1)
+    # 16-token chunks, d_k = 16: the strip kernel
     assert la.plan(1, 1, 100, 128, 128, 16)[0] == STRIP
     assert la.plan(1, 1, 100, 16, 128, 64)[0] == STRIP
-    # 128-token chunks at d_k = 128 exceed the stripe kernel's LDS; at d_k = 64 they fit
-    assert la.plan(1, 1, 100, 128, 128, 128) == (STRIP, 16, 1, 1)
-    assert la.plan(1, 1, 100, 64, 64, 128)[0] == STRIPE
+    # 128-token chunks at d_k = 128 exceed the stripe kernel's LDS
+    assert la.plan(1, 1, 100, 128, 128, 128) == (STRIP, 32, 1, 1)
+    assert la.plan(1, 1, 100, 64, 128, 128)[0] == STRIPE
     # fp32: its own kernel, one segment, 16- or 32-wide tiles
     assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32) == (F32, 16, 1, 1)
     assert la.chunk_fwd_workspace_bytes(1, 1, 300, 16, 16, 64, la.LA_F32) == 0
@@ -119,6 +118,10 @@ def test_plan_override_and_clamping():
         assert la.plan(1, 1, 100, 128, 128, 64)[1::2] == (64, 2)
         la.set_plan(STRIPE, 64, 2)
         assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 64, 2, 2)
+        # d_k = 32 keeps one wave per stripe
+        la.set_plan(STRIPE)
+        assert la.plan(1, 1, 100, 32, 32, 64) == (STRIPE, 32, 1, 1)
+        assert la.plan(1, 1, 100, 64, 64, 128)[0] == STRIPE
         la.set_plan(STRIPE, 128, 2, 1)
         assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 128, 2, 1)
         # a stripe plan the shape does not allow falls back to the strip kernel
