@@ -34,7 +34,9 @@
 //   * Q, K, V tiles stream from HBM into LDS with global_load_lds_dwordx4,
 //     NSTG chunks deep; workgroup barriers wait for LDS only, so the prefetch
 //     stays in flight across them.
-//   * output rows leave as 8-byte stores of 4 consecutive value columns.
+//   * an output row block (32 rows x 32 columns) is transposed back through a
+//     2 KB LDS slot of its wave and leaves as 16-byte stores, 64 contiguous
+//     bytes per row.
 //
 // STATE_ONLY computes a segment's state increment and total log2 decay from a
 // zero state (the first pass of the segment split); the main pass composes
@@ -58,7 +60,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-template <int DK, int NWV, int KH, int C>
+// SO: the state-only pass, which stages no Q tile and needs no P~, partial
+// exchange or output staging (so it can prefetch deeper).
+template <int DK, int NWV, int KH, int C, bool SO = false>
 struct Geo {
   static constexpr int NW = NWV * KH;           // waves of the workgroup
   static constexpr int TVW = 32 * NWV;          // value columns of the workgroup
@@ -81,16 +85,18 @@ struct Geo {
   static constexpr int QK_PER = (QK_BLK + NW - 1) / NW;  // per wave
   static constexpr int V_PER = (V_BLK + NW - 1) / NW;
   // vector memory instructions of one chunk per wave (at most)
-  static constexpr int LOADS_MAX = 2 * QK_PER + V_PER + 1;
-  static constexpr int STORES = 4 * RBW;
+  static constexpr int LOADS_MAX = (SO ? 1 : 2) * QK_PER + V_PER + 1;
+  static constexpr int STORES = SO ? 0 : 2 * RBW;
   // every wave issues the same memory instructions per chunk and their count
   // fits the 6-bit vmcnt, so the wait at the top of a chunk can count them
   static constexpr bool UNIFORM = QK_BLK % NW == 0 && V_BLK % NW == 0 && NRB % KH == 0 &&
                                   STORES + LOADS_MAX < 64;
   static constexpr size_t XCH_BYTES = KH > 1 ? (size_t)NWV * NRB * 4096 : 16;
   static constexpr size_t stage_bytes(int n) {
-    return (size_t)n * (2 * (size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
-           2 * (size_t)C * C + 2 * 4 * (size_t)NW * C + XCH_BYTES + 256;
+    return SO ? (size_t)n * ((size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
+                    2 * 4 * (size_t)NW * C + 256
+              : (size_t)n * (2 * (size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
+                    2 * (size_t)C * C + 2 * 4 * (size_t)NW * C + XCH_BYTES + 2048 * (size_t)NW + 256;
   }
   static constexpr int NSTG =
       (UNIFORM && stage_bytes(3) <= kMaxLds && 2 * STORES + LOADS_MAX < 64) ? 3 : 2;
@@ -206,7 +212,7 @@ __host__ __device__ constexpr int block_j(int b) { return b - block_i(b) * (bloc
 
 template <int DK, int NWV, int KH, int C, int CAT, bool STATE_ONLY>
 __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const ChunkArgs a) {
-  using G = Geo<DK, NWV, KH, C>;
+  using G = Geo<DK, NWV, KH, C, STATE_ONLY>;
   constexpr int NS = G::NSTG;
   constexpr int NW = G::NW;
   const int tid = threadIdx.x;
@@ -248,6 +254,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   __shared__ __align__(16) char sX[(STATE_ONLY || KH == 1) ? 16 : G::XCH_BYTES];
   // per-wave weights of the current chunk: [0] e^{b_last - b_t}, [1] e^{b_t}
   __shared__ __align__(16) float sW[NW][2][C];
+  // per-wave staging of one bf16 output row block: 32 rows x 64 bytes
+  __shared__ __align__(16) char sO[STATE_ONLY ? 1 : NW][STATE_ONLY ? 16 : 2048];
 
   auto stage_q = [&](auto BUF) -> char* {
     constexpr int b = decltype(BUF)::value;
@@ -567,17 +575,25 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
             const u32x4 pB = lds_b128(sP, swz<G::WCP>(i, 16 * ks + 8 * h));
             acc = mfma32(vA[ks], pB, acc);
           }
-        // lane: row t0 + i, value columns cw + 8 q + 4 h + (0..3)
-        if (i < nvalid) {
-          uint16_t* orow = oh + (size_t)(t0 + i) * DV + 4 * h;
+        // lane: row i, value columns cw + 8 q + 4 h + (0..3) -> LDS slot,
+        // then 16-byte pieces of whole rows -> HBM
+        char* so = sO[wave];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            u32x2 w;
-            w[0] = cvt2(acc[4 * q + 0], acc[4 * q + 1]);
-            w[1] = cvt2(acc[4 * q + 2], acc[4 * q + 3]);
-            *reinterpret_cast<u32x2*>(orow + 8 * q) = w;
-          }
+        for (int q = 0; q < 4; ++q) {
+          u32x2 w;
+          w[0] = cvt2(acc[4 * q + 0], acc[4 * q + 1]);
+          w[1] = cvt2(acc[4 * q + 2], acc[4 * q + 3]);
+          *reinterpret_cast<u32x2*>(so + swz<4>(l32, 8 * q + 4 * h)) = w;
         }
+        lds_wave_sync();
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int row = (lane >> 2) + 16 * it, cc = lane & 3;
+          const u32x4 w = lds_b128(so, swz<4>(row, 8 * cc));
+          if (32 * I + row < nvalid)
+            *reinterpret_cast<u32x4*>(oh + (size_t)(t0 + 32 * I + row) * DV + 8 * cc) = w;
+        }
+        lds_wave_sync();
       }
     }
 

@@ -12,7 +12,9 @@
 // DK / (256 / (DV/4)) rows, so a row of the state is read by DV/4 consecutive
 // lanes in one coalesced 16-byte-per-lane access.  All of a lane's state loads
 // are issued before any arithmetic, then the partial sums of o over a lane's
-// rows are combined across row groups through LDS.
+// rows are combined across row groups through LDS.  The state is touched once
+// per step and is larger than every cache, so its loads and stores carry the
+// non-temporal hint.
 #include "la_device.h"
 
 namespace la {
@@ -28,12 +30,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const int h = bh % a.H;
   const int rg = tid / TPR, c4 = tid % TPR;
 
-  float4* S = reinterpret_cast<float4*>(a.state + (size_t)bh * DK * DV);
-  float4 sreg[NPASS];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4* S = reinterpret_cast<f32x4*>(a.state + (size_t)bh * DK * DV);
+  f32x4 sreg[NPASS];
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
     const int r = rg + p * RP;
-    if (r < DK) sreg[p] = S[r * TPR + c4];
+    if (r < DK) sreg[p] = __builtin_nontemporal_load(&S[r * TPR + c4]);
   }
 
   __shared__ float sq[DK], sk[DK], sv[DV];
@@ -68,12 +71,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     const int r = rg + p * RP;
     if (r < DK) {
       const float kr = sk[r], qr = sq[r];
-      float4 s = sreg[p];
+      f32x4 s = sreg[p];
       s.x = fmaf(decay, s.x, kr * vv.x);
       s.y = fmaf(decay, s.y, kr * vv.y);
       s.z = fmaf(decay, s.z, kr * vv.z);
       s.w = fmaf(decay, s.w, kr * vv.w);
-      S[r * TPR + c4] = s;
+      __builtin_nontemporal_store(s, &S[r * TPR + c4]);
       o.x = fmaf(qr, s.x, o.x);
       o.y = fmaf(qr, s.y, o.y);
       o.z = fmaf(qr, s.z, o.z);
