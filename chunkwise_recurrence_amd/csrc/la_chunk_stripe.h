@@ -39,7 +39,11 @@
 //     bytes per row.
 //
 // STATE_ONLY computes a segment's state increment and total log2 decay from a
-// zero state (the first pass of the segment split); the main pass composes
+// zero state (the first pass of the segment split).  It walks the segment's
+// chunks last to first, weighting token t by e^{B_end - B_t} directly (the sum
+// does not depend on the order), so the chunks it reads last -- the starts of
+// the segments -- are the ones the output pass reads first, while they may
+// still sit in the memory-side cache.  The main pass composes
 // the exclusive prefix of the (decay, state) pairs in its prologue, the
 // parallel / associative scan idea of the tutorial's section 3.3.
 #pragma once
@@ -360,7 +364,13 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   constexpr int LOADS = (STATE_ONLY ? 1 : 2) * G::QK_PER + G::V_PER + (CAT == kCatToken ? 1 : 0);
   constexpr int STORES = STATE_ONLY ? 0 : G::STORES;
 
-  auto issue_loads = [&](auto BUF, int c) {
+  // iteration it handles chunk chunk_of(it): forward in the output pass,
+  // backward in the state pass
+  const int n_it = c_end - c_begin;
+  auto chunk_of = [&](int it) { return STATE_ONLY ? c_end - 1 - it : c_begin + it; };
+
+  auto issue_loads = [&](auto BUF, int it) {
+    const int c = chunk_of(it);
     const int t0 = c * C;
     const bool full = t0 + C <= L;
     const uint16_t* kc = kh + (size_t)t0 * DK;
@@ -397,8 +407,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   float logA = 0.0f;
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
-  auto body = [&](auto BUF, int c) {
+  auto body = [&](auto BUF, int it) {
     constexpr int buf = decltype(BUF)::value;
+    const int c = chunk_of(it);
     const int t0 = c * C;
     const int nvalid = min(C, L - t0);
     char* qb = stage_q(BUF);
@@ -406,11 +417,12 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     char* vb = stage_v(BUF);
     const float* sb = stage_b(BUF);
 
-    // Wait until this wave's loads of chunk c have landed, keeping later
-    // chunks' loads (and the stores issued since) in flight: in issue order,
-    // chunk c's loads are followed by nS chunks' stores and nL chunks' loads.
+    // Wait until this wave's loads of iteration it have landed, keeping later
+    // iterations' loads (and the stores issued since) in flight: in issue
+    // order, its loads are followed by nS iterations' stores and nL
+    // iterations' loads.
     if constexpr (G::UNIFORM && NS == 3) {
-      const int nS = min(NS - 1, c - c_begin), nL = min(NS - 2, c_end - 1 - c);
+      const int nS = min(NS - 1, it), nL = min(NS - 2, n_it - 1 - it);
       if (nS == 2 && nL == 1) wait_vmcnt<2 * STORES + LOADS>();
       else if (nS == 2) wait_vmcnt<2 * STORES>();
       else if (nS == 1 && nL == 1) wait_vmcnt<STORES + LOADS>();
@@ -418,13 +430,13 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       else if (nL == 1) wait_vmcnt<LOADS>();
       else wait_vmcnt<0>();
     } else if constexpr (G::UNIFORM) {
-      if (c > c_begin) wait_vmcnt<STORES>();
+      if (it > 0) wait_vmcnt<STORES>();
       else wait_vmcnt<0>();
     } else {
       wait_vmcnt<0>();
     }
-    lds_barrier();  // everybody's loads of chunk c landed; chunk c-1 is finished
-    if (c + NS - 1 < c_end) issue_loads(std::integral_constant<int, (buf + NS - 1) % NS>{}, c + NS - 1);
+    lds_barrier();  // everybody's loads of this chunk landed; the previous one is finished
+    if (it + NS - 1 < n_it) issue_loads(std::integral_constant<int, (buf + NS - 1) % NS>{}, it + NS - 1);
 
     // a short last chunk: zero the rows past the sequence (clamped copies)
     if (nvalid < C) {
@@ -455,12 +467,14 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     if constexpr (CAT == kCatToken) bL = sb[nvalid - 1];
 
     // per-token weights of this wave: e^{b_last - b_t} (update; 0 past the
-    // chunk) and e^{b_t} (inter-chunk term), t = lane (+ 64)
+    // chunk) and e^{b_t} (inter-chunk term), t = lane (+ 64).  The state pass
+    // folds in the decay of the chunks after this one (logA so far).
     if constexpr (CAT != kCatNone) {
+      const float wofs = STATE_ONLY ? logA + bL : bL;
 #pragma unroll
       for (int t = lane; t < C; t += 64) {
         const float bt = CAT == kCatHead ? (float)(t + 1) * lg2 : sb[t];
-        wq[t] = t < nvalid ? __builtin_amdgcn_exp2f(bL - bt) : 0.0f;
+        wq[t] = t < nvalid ? __builtin_amdgcn_exp2f(wofs - bt) : 0.0f;
         if constexpr (!STATE_ONLY) eq[t] = __builtin_amdgcn_exp2f(bt);
       }
       lds_wave_sync();
@@ -598,7 +612,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     }
 
     // (3) state update of this wave's tiles: S <- e^{b_last} S + K^T diag(e^{b_last - b}) V
-    if constexpr (CAT != kCatNone) {
+    // (state pass: S <- S + K^T diag(e^{B_end - B}) V)
+    if constexpr (CAT != kCatNone && !STATE_ONLY) {
       const float eL = __builtin_amdgcn_exp2f(bL);
 #pragma unroll
       for (int t = 0; t < G::NMK_OWN; ++t)
@@ -630,18 +645,18 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  if (c_begin < c_end) issue_loads(S0{}, c_begin);
+  if (n_it > 0) issue_loads(S0{}, 0);
   if constexpr (NS == 3) {
-    if (c_begin + 1 < c_end) issue_loads(S1{}, c_begin + 1);
-    for (int c = c_begin; c < c_end; c += 3) {
-      body(S0{}, c);
-      if (c + 1 < c_end) body(S1{}, c + 1);
-      if (c + 2 < c_end) body(S2{}, c + 2);
+    if (n_it > 1) issue_loads(S1{}, 1);
+    for (int it = 0; it < n_it; it += 3) {
+      body(S0{}, it);
+      if (it + 1 < n_it) body(S1{}, it + 1);
+      if (it + 2 < n_it) body(S2{}, it + 2);
     }
   } else {
-    for (int c = c_begin; c < c_end; c += 2) {
-      body(S0{}, c);
-      if (c + 1 < c_end) body(S1{}, c + 1);
+    for (int it = 0; it < n_it; it += 2) {
+      body(S0{}, it);
+      if (it + 1 < n_it) body(S1{}, it + 1);
     }
   }
 
