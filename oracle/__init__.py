@@ -58,6 +58,9 @@ def _load(path: str | None = None):
         lib.oracle_recurrent.restype = ctypes.c_int
         lib.oracle_recurrent.argtypes = [ctypes.c_int] * 5 + [d, d, d, ctypes.c_int, ctypes.c_int,
                                                              d, d, d, ctypes.c_int]
+        lib.oracle_recurrent_norm.restype = ctypes.c_int
+        lib.oracle_recurrent_norm.argtypes = [ctypes.c_int] * 5 + [
+            d, d, d, ctypes.c_int, ctypes.c_int, d, d, d, d, ctypes.c_int]
         _libs[path] = lib
     return _libs[path]
 
@@ -82,14 +85,18 @@ def host_threads() -> int:
 # the oracle proper
 # --------------------------------------------------------------------------
 def recurrent(q, k, v, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, decay=None,
-              state=None, nthreads: int | None = None, lib_path: str | None = None):
+              state=None, nthreads: int | None = None, lib_path: str | None = None,
+              normalize: bool = False, norm_state=None):
     """Token-by-token fp64 recurrence (`la_oracle.c`).
 
     q, k: [B,H,L,dk]; v: [B,H,L,dv]; decay: None | gamma[H] | log_a or g [B,H,L];
     state: [B,H,dk,dv] initial state (zeros if None).
     lib_path: another build of `la_oracle.c` to run instead of the default one
     (the tests use it to check that deliberately broken copies get caught).
-    Returns (out [B,H,L,dv], final state [B,H,dk,dv]) as float64 arrays.
+    normalize: the normalised form o_t = phi(q_t)^T S_t / phi(q_t)^T z_t with
+    z_t = a_t z_{t-1} + phi(k_t); norm_state: [B,H,dk] z_0 (zeros if None).
+    Returns (out [B,H,L,dv], final state [B,H,dk,dv]) as float64 arrays, and
+    the final z [B,H,dk] as a third element when normalize.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, L, dk = q.shape
@@ -98,6 +105,10 @@ def recurrent(q, k, v, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, de
     S = np.zeros((B, H, dk, dv)) if state is None else _f64(state).copy()
     assert S.shape == (B, H, dk, dv)
     out = np.zeros((B, H, L, dv))
+    Z = None
+    if normalize:
+        Z = np.zeros((B, H, dk)) if norm_state is None else _f64(norm_state).copy()
+        assert Z.shape == (B, H, dk)
     if decay_kind == DECAY_NONE:
         dec = np.zeros(1)
     elif decay_kind == DECAY_HEAD:
@@ -105,28 +116,35 @@ def recurrent(q, k, v, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, de
     else:
         dec = _f64(decay).reshape(B, H, L)
     if B * H == 0 or L == 0:
-        return out, S
+        return (out, S, Z) if normalize else (out, S)
     n = host_threads() if nthreads is None else nthreads
+    if normalize:
+        _load(lib_path).oracle_recurrent_norm(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), phi,
+                                              decay_kind, _ptr(dec), _ptr(S), _ptr(Z),
+                                              _ptr(out), n)
+        return out, S, Z
     _load(lib_path).oracle_recurrent(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), phi,
                                      decay_kind, _ptr(dec), _ptr(S), _ptr(out), n)
     return out, S
 
 
 def decode_step(q, k, v, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, decay=None,
-                state=None, lib_path: str | None = None):
+                state=None, lib_path: str | None = None, normalize: bool = False,
+                norm_state=None):
     """One recurrent step for N sequences x H heads: the same definition with L = 1.
 
-    q, k: [N,H,dk]; v: [N,H,dv]; decay: None | gamma[H] | [N,H]; state [N,H,dk,dv].
-    Returns (o [N,H,dv], new state).
+    q, k: [N,H,dk]; v: [N,H,dv]; decay: None | gamma[H] | [N,H]; state [N,H,dk,dv];
+    norm_state [N,H,dk] (normalised form).
+    Returns (o [N,H,dv], new state) (+ new z when normalize).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     N, H, _ = q.shape
     dec = decay
     if decay_kind in (DECAY_LOG, DECAY_GATE):
         dec = _f64(decay).reshape(N, H, 1)
-    o, S = recurrent(q[:, :, None, :], k[:, :, None, :], v[:, :, None, :], phi, decay_kind,
-                     dec, state, lib_path=lib_path)
-    return o[:, :, 0, :], S
+    r = recurrent(q[:, :, None, :], k[:, :, None, :], v[:, :, None, :], phi, decay_kind,
+                  dec, state, lib_path=lib_path, normalize=normalize, norm_state=norm_state)
+    return (r[0][:, :, 0, :],) + tuple(r[1:])
 
 
 # --------------------------------------------------------------------------
@@ -154,12 +172,15 @@ def decay_multipliers(B: int, H: int, L: int, decay_kind: int, decay) -> np.ndar
     return np.exp(-(np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))))
 
 
-def parallel(q, k, v, a, phi: int = PHI_IDENTITY, state=None):
+def parallel(q, k, v, a, phi: int = PHI_IDENTITY, state=None, normalize: bool = False,
+             norm_state=None):
     """Fully parallel masked form, one [L,L] product per head (O(L^2)).
 
     o_t = sum_{s<=t} D[t,s] (phi(q_t).phi(k_s)) v_s + (prod_{r<=t} a_r) phi(q_t)^T S_0,
     D[t,s] = prod_{r=s+1..t} a_r (an explicit running product, no logs).
     Returns (out, final state) with S_L = sum_s D[L-1,s] phi(k_s) v_s^T + prod(a) S_0.
+    normalize: every row is divided by the same masked sum with v replaced by
+    ones, sum_{s<=t} D[t,s] (phi(q_t).phi(k_s)) + (prod_{r<=t} a_r) phi(q_t).z_0.
     """
     fq, fk, v, a = feature_map(q, phi), feature_map(k, phi), _f64(v), _f64(a)
     B, H, L, dk = fq.shape
@@ -179,6 +200,10 @@ def parallel(q, k, v, a, phi: int = PHI_IDENTITY, state=None):
             head = np.cumprod(a[b, h])  # prod_{r<=t} a_r: decay of S_0 seen at token t
             scores = fq[b, h] @ fk[b, h].T
             out[b, h] = (scores * D) @ v[b, h] + head[:, None] * (fq[b, h] @ S0[b, h])
+            if normalize:
+                z0 = np.zeros(dk) if norm_state is None else _f64(norm_state)[b, h]
+                den = (scores * D).sum(axis=1) + head * (fq[b, h] @ z0)
+                out[b, h] = out[b, h] / den[:, None]
             if L:
                 SL[b, h] = (fk[b, h] * D[L - 1][:, None]).T @ v[b, h] + head[-1] * S0[b, h]
             else:
@@ -186,7 +211,8 @@ def parallel(q, k, v, a, phi: int = PHI_IDENTITY, state=None):
     return out, SL
 
 
-def chunkwise(q, k, v, a, C: int, phi: int = PHI_IDENTITY, state=None, dtype=np.float64):
+def chunkwise(q, k, v, a, C: int, phi: int = PHI_IDENTITY, state=None, dtype=np.float64,
+              normalize: bool = False, norm_state=None):
     """Chunkwise form with decay folded in (log-space, every factor exp(<= 0)).
 
     Per chunk of c <= C tokens with b = inclusive cumsum of log a inside the chunk:
@@ -195,6 +221,9 @@ def chunkwise(q, k, v, a, C: int, phi: int = PHI_IDENTITY, state=None, dtype=np.
     A ragged last chunk simply has c < C rows.
     `dtype` is the working precision (float64 by default; float32 reproduces
     the magnitude of rounding error the pages print for their fp32 run).
+    normalize: z is carried as one more value column of ones (the tutorial's
+    section 6.2 suggestion): the same two formulas with V_c -> 1, and every
+    output row divided by its entry.
     """
     fq, fk = feature_map(q, phi).astype(dtype), feature_map(k, phi).astype(dtype)
     v, a = _f64(v).astype(dtype), _f64(a)
@@ -202,11 +231,15 @@ def chunkwise(q, k, v, a, C: int, phi: int = PHI_IDENTITY, state=None, dtype=np.
     dv = v.shape[-1]
     S = np.zeros((B, H, dk, dv), dtype) if state is None else _f64(state).astype(dtype)
     out = np.zeros((B, H, L, dv), dtype)
+    Z = None
+    if normalize:
+        Z = np.zeros((B, H, dk), dtype) if norm_state is None else _f64(norm_state).astype(dtype)
     with np.errstate(divide="ignore"):
         la = np.log(a)
     for b in range(B):
         for h in range(H):
             Sh = S[b, h]
+            zh = Z[b, h] if normalize else None
             for s in range(0, L, C):
                 e = min(s + C, L)
                 Qc, Kc, Vc = fq[b, h, s:e], fk[b, h, s:e], v[b, h, s:e]
@@ -215,9 +248,15 @@ def chunkwise(q, k, v, a, C: int, phi: int = PHI_IDENTITY, state=None, dtype=np.
                 mask = np.tril(np.ones((e - s, e - s), dtype=bool))
                 Dc = np.where(mask, np.exp(np.where(mask, diff, 0.0)), 0.0).astype(dtype)
                 out[b, h, s:e] = np.exp(bc)[:, None] * (Qc @ Sh) + ((Qc @ Kc.T) * Dc) @ Vc
+                if normalize:
+                    den = np.exp(bc) * (Qc @ zh) + ((Qc @ Kc.T) * Dc).sum(axis=1)
+                    out[b, h, s:e] /= den[:, None]
+                    zh = np.exp(bc[-1]) * zh + (Kc * np.exp(bc[-1] - bc)[:, None]).sum(axis=0)
                 Sh = np.exp(bc[-1]) * Sh + (Kc * np.exp(bc[-1] - bc)[:, None]).T @ Vc
             S[b, h] = Sh
-    return out, S
+            if normalize:
+                Z[b, h] = zh
+    return (out, S, Z) if normalize else (out, S)
 
 
 def rel_err(x, ref) -> float:

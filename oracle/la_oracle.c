@@ -25,6 +25,12 @@
  *    a_t = exp(Delta_t * A) with Delta_t = softplus(g_t), here A = -1, so
  *    a_t = exp(-softplus(g_t)).
  *
+ * The normalised variant (the linear/sparse attention tutorial, section 2.2,
+ * boxed recurrence) also carries z_t = a_t z_{t-1} + phi(k_t) (the decay acts
+ * on z as on S: z is S's extra value column of ones, tutorial section 6.2)
+ * and returns o_t = phi(q_t)^T S_t / phi(q_t)^T z_t, with no term added to the
+ * denominator (the pages give none).
+ *
  * Decay kinds (same numbering as the library's public enum, redeclared here
  * on purpose so that the two sides share no header):
  *   0 none        a_t = 1
@@ -72,10 +78,11 @@ static double oracle_decay(int kind, const double* dh, int t) {
  * One head, L tokens, token by token.
  *   q, k : [L, dk]   v : [L, dv]   out : [L, dv]   S : [dk, dv] (in: S_0, out: S_L)
  *   dh   : decay data of this head (see oracle_decay), may be NULL for kind 0
+ *   z    : NULL (un-normalised) or the normaliser [dk] (in: z_0, out: z_L)
  */
 void oracle_recurrent_head(int L, int dk, int dv, const double* q, const double* k,
                            const double* v, int phi, int decay_kind, const double* dh,
-                           double* S, double* out) {
+                           double* S, double* z, double* out) {
   double* fq = (double*)malloc(sizeof(double) * (size_t)dk);
   double* fk = (double*)malloc(sizeof(double) * (size_t)dk);
   for (int t = 0; t < L; ++t) {
@@ -91,12 +98,21 @@ void oracle_recurrent_head(int L, int dk, int dv, const double* q, const double*
     for (int i = 0; i < dk; ++i)
       for (int j = 0; j < dv; ++j)
         S[(size_t)i * dv + j] = a * S[(size_t)i * dv + j] + fk[i] * vt[j];
+    /* normaliser: z = a z + phi(k_t), den = phi(q_t)^T z */
+    double den = 1.0;
+    if (z) {
+      den = 0.0;
+      for (int i = 0; i < dk; ++i) {
+        z[i] = a * z[i] + fk[i];
+        den += fq[i] * z[i];
+      }
+    }
     /* read: o_t = phi(q_t)^T S (the state that already holds token t) */
     double* ot = out + (size_t)t * dv;
     for (int j = 0; j < dv; ++j) {
       double acc = 0.0;
       for (int i = 0; i < dk; ++i) acc += fq[i] * S[(size_t)i * dv + j];
-      ot[j] = acc;
+      ot[j] = z ? acc / den : acc;
     }
   }
   free(fq);
@@ -106,7 +122,7 @@ void oracle_recurrent_head(int L, int dk, int dv, const double* q, const double*
 typedef struct {
   int B, H, L, dk, dv, phi, kind;
   const double *q, *k, *v, *decay;
-  double *S, *out;
+  double *S, *Z, *out;
   int first, last; /* head range [first, last) of this thread */
 } oracle_job;
 
@@ -121,6 +137,7 @@ static void* oracle_worker(void* p) {
     oracle_recurrent_head(j->L, j->dk, j->dv, j->q + (size_t)bh * j->L * j->dk,
                           j->k + (size_t)bh * j->L * j->dk, j->v + (size_t)bh * j->L * j->dv,
                           j->phi, j->kind, dh, j->S + (size_t)bh * j->dk * j->dv,
+                          j->Z ? j->Z + (size_t)bh * j->dk : NULL,
                           j->out + (size_t)bh * j->L * j->dv);
   }
   return NULL;
@@ -130,11 +147,12 @@ static void* oracle_worker(void* p) {
  * All heads of a [B, H, L, d] problem, heads spread over `nthreads` threads.
  *   q, k : [B,H,L,dk]  v : [B,H,L,dv]  out : [B,H,L,dv]  S : [B,H,dk,dv] in/out
  *   decay: NULL | gamma[H] | log_a or g [B,H,L]
+ *   Z    : NULL (un-normalised) or the normaliser state [B,H,dk] in/out
  * Returns the number of threads actually used.
  */
-int oracle_recurrent(int B, int H, int L, int dk, int dv, const double* q, const double* k,
-                     const double* v, int phi, int decay_kind, const double* decay, double* S,
-                     double* out, int nthreads) {
+int oracle_recurrent_norm(int B, int H, int L, int dk, int dv, const double* q, const double* k,
+                          const double* v, int phi, int decay_kind, const double* decay,
+                          double* S, double* Z, double* out, int nthreads) {
   const int heads = B * H;
   if (heads <= 0) return 0;
   if (nthreads < 1) nthreads = 1;
@@ -144,7 +162,7 @@ int oracle_recurrent(int B, int H, int L, int dk, int dv, const double* q, const
   for (int i = 0; i < nthreads; ++i) {
     oracle_job* j = &jobs[i];
     j->B = B; j->H = H; j->L = L; j->dk = dk; j->dv = dv; j->phi = phi; j->kind = decay_kind;
-    j->q = q; j->k = k; j->v = v; j->decay = decay; j->S = S; j->out = out;
+    j->q = q; j->k = k; j->v = v; j->decay = decay; j->S = S; j->Z = Z; j->out = out;
     j->first = (int)((long long)heads * i / nthreads);
     j->last = (int)((long long)heads * (i + 1) / nthreads);
   }
@@ -154,4 +172,12 @@ int oracle_recurrent(int B, int H, int L, int dk, int dv, const double* q, const
   free(jobs);
   free(th);
   return nthreads;
+}
+
+/* The un-normalised recurrence (no z). */
+int oracle_recurrent(int B, int H, int L, int dk, int dv, const double* q, const double* k,
+                     const double* v, int phi, int decay_kind, const double* decay, double* S,
+                     double* out, int nthreads) {
+  return oracle_recurrent_norm(B, H, L, dk, dv, q, k, v, phi, decay_kind, decay, S, NULL, out,
+                               nthreads);
 }

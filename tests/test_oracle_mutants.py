@@ -37,6 +37,9 @@ MUTANTS = {
     "token_decay_off_by_one": ("case ORACLE_DECAY_LOG: return exp(dh[t]);",
                                "case ORACLE_DECAY_LOG: return exp(dh[t > 0 ? t - 1 : 0]);"),
     "feature_map_on_values": ("+ fk[i] * vt[j];", "+ fk[i] * oracle_phi(phi, vt[j]);"),
+    "normaliser_not_decayed": ("z[i] = a * z[i] + fk[i];", "z[i] = z[i] + fk[i];"),
+    "normaliser_of_queries": ("z[i] = a * z[i] + fk[i];", "z[i] = a * z[i] + fq[i];"),
+    "denominator_with_keys": ("den += fq[i] * z[i];", "den += fk[i] * z[i];"),
 }
 
 
@@ -73,6 +76,14 @@ def _battery(lib):
             op, Sp = oracle.parallel(q, k, v, a, phi, S0)
             if oracle.rel_err(o, op) > 1e-12 or oracle.rel_err(S, Sp) > 1e-12:
                 failed.append(f"parallel phi={phi} kind={kind}")
+    # the normalised form: recurrent == parallel (explicit products, masked row sums)
+    for kind, dec in decays.items():
+        o, S, Z = oracle.recurrent(q, k, v, oracle.PHI_ELU1, kind, dec, normalize=True,
+                                   lib_path=lib)
+        a = oracle.decay_multipliers(B, H, L, kind, dec)
+        op, _ = oracle.parallel(q, k, v, a, oracle.PHI_ELU1, normalize=True)
+        if oracle.rel_err(o, op) > 1e-12:
+            failed.append(f"normalised parallel kind={kind}")
     # phi read out against torch's elu + 1
     x = np.linspace(-4.0, 3.0, 6)
     o, _ = oracle.recurrent(x[None, None, None], np.zeros((1, 1, 1, 6)), np.zeros((1, 1, 1, 6)),

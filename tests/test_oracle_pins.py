@@ -375,3 +375,79 @@ def test_gated_workload_decay_statistics():
     sums = -np.log(a).reshape(-1, w.C).sum(axis=1)
     assert 30 < sums.min() and sums.max() < 80 and abs(sums.mean() - 51.6) < 1.0
     assert math.exp(-sums.max()) > np.finfo(np.float32).tiny
+
+
+# ---------------------------------------------------------------------------
+# the normalised form (tutorial section 2.2, boxed recurrence; z as the extra
+# value column of ones, section 6.2)
+# ---------------------------------------------------------------------------
+def _norm_case(seed, kind, L=23, with_state=True):
+    q, k, v, dec, S0 = _case(seed, 1, 2, L, 5, 3, kind, with_state=False)
+    rng = np.random.default_rng(seed + 100)
+    fk0 = oracle.feature_map(rng.standard_normal((1, 2, 4, 5)), oracle.PHI_ELU1)
+    # a consistent initial pair: S_0 = sum of phi(k) v^T, z_0 = sum of phi(k)
+    # over 4 earlier tokens, so every denominator stays positive
+    v0 = rng.standard_normal((1, 2, 4, 3))
+    S0 = np.einsum("bhtk,bhtv->bhkv", fk0, v0) if with_state else None
+    z0 = fk0.sum(axis=2) if with_state else None
+    return q, k, v, dec, S0, z0
+
+
+@pytest.mark.parametrize("kind", [oracle.DECAY_NONE, oracle.DECAY_HEAD, oracle.DECAY_LOG,
+                                  oracle.DECAY_GATE])
+def test_normalised_recurrent_equals_parallel_and_chunkwise(kind):
+    q, k, v, dec, S0, z0 = _norm_case(11 + kind, kind)
+    a = oracle.decay_multipliers(1, 2, 23, kind, dec)
+    o, S, Z = oracle.recurrent(q, k, v, oracle.PHI_ELU1, kind, dec, S0, normalize=True,
+                               norm_state=z0)
+    op, Sp = oracle.parallel(q, k, v, a, oracle.PHI_ELU1, S0, normalize=True, norm_state=z0)
+    assert np.abs(o - op).max() < 1e-12 * max(1.0, np.abs(op).max())
+    for C in (1, 4, 7, 23):
+        oc, Sc, Zc = oracle.chunkwise(q, k, v, a, C, oracle.PHI_ELU1, S0, normalize=True,
+                                      norm_state=z0)
+        assert np.abs(o - oc).max() < 1e-12 * max(1.0, np.abs(o).max())
+        assert np.abs(Z - Zc).max() < 1e-12 * max(1.0, np.abs(Z).max())
+    # the normaliser is the un-normalised output for v = 1 (z is S's column of ones)
+    ones = np.ones((1, 2, 23, 1))
+    den, zS = oracle.recurrent(q, k, ones, oracle.PHI_ELU1, kind, dec, z0[..., None])
+    num, _ = oracle.recurrent(q, k, v, oracle.PHI_ELU1, kind, dec, S0)
+    assert np.abs(o - num / den).max() < 1e-12 * max(1.0, np.abs(o).max())
+    assert np.abs(Z - zS[..., 0]).max() < 1e-12 * np.abs(Z).max()
+
+
+def test_normalised_first_token_returns_its_value():
+    # z_0 = 0, S_0 = 0: o_0 = (phi(q).phi(k) v_0) / (phi(q).phi(k)) = v_0
+    q, k, v, dec, _, _ = _norm_case(5, oracle.DECAY_GATE, with_state=False)
+    o, _, _ = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_GATE, dec, normalize=True)
+    assert np.allclose(o[:, :, 0], v[:, :, 0], rtol=1e-14, atol=1e-14)
+
+
+def test_normalised_output_is_a_convex_combination_of_values():
+    # phi = elu + 1 > 0 and no decay: o_t = sum_s w_ts v_s with w_ts > 0, sum_s w_ts = 1
+    q, k, v, _, _, _ = _norm_case(6, oracle.DECAY_NONE, L=40, with_state=False)
+    o, _, _ = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_NONE, normalize=True)
+    lo = np.minimum.accumulate(v, axis=2)
+    hi = np.maximum.accumulate(v, axis=2)
+    assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12)
+
+
+@pytest.mark.parametrize("kind", [oracle.DECAY_HEAD, oracle.DECAY_GATE])
+def test_normalised_constant_values_pass_through(kind):
+    # v_t = c for every t (and S_0 = z_0 c^T): every output is exactly c
+    q, k, _, dec, _, z0 = _norm_case(7, kind)
+    c = np.array([0.5, -2.0, 3.0])
+    v = np.broadcast_to(c, (1, 2, 23, 3)).copy()
+    S0 = z0[..., None] * c
+    o, _, _ = oracle.recurrent(q, k, v, oracle.PHI_ELU1, kind, dec, S0, normalize=True,
+                               norm_state=z0)
+    assert np.allclose(o, c, rtol=1e-12, atol=1e-12)
+
+
+def test_normalised_decode_step_is_one_token():
+    q, k, v, dec, S0, z0 = _norm_case(8, oracle.DECAY_LOG, L=1)
+    o, S, Z = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_LOG, dec, S0,
+                               normalize=True, norm_state=z0)
+    od, Sd, Zd = oracle.decode_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], oracle.PHI_ELU1,
+                                    oracle.DECAY_LOG, dec[:, :, 0], S0, normalize=True,
+                                    norm_state=z0)
+    assert np.array_equal(o[:, :, 0], od) and np.array_equal(S, Sd) and np.array_equal(Z, Zd)
