@@ -27,7 +27,8 @@ class Plan(ctypes.Structure):
 
 # every symbol include/la.h declares
 EXPORTS = ("la_state_init", "la_chunk_fwd_workspace_bytes", "la_chunk_fwd", "la_decode_step",
-           "la_status_string", "la_chunk_fwd_plan", "la_set_plan")
+           "la_status_string", "la_chunk_fwd_plan", "la_set_plan", "la_chunk_fwd_norm",
+           "la_decode_step_norm")
 
 _lib = None
 
@@ -61,6 +62,11 @@ def load():
                                  ctypes.c_size_t, vp]
     lib.la_decode_step.restype = i
     lib.la_decode_step.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp]
+    lib.la_chunk_fwd_norm.restype = i
+    lib.la_chunk_fwd_norm.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
+    lib.la_decode_step_norm.restype = i
+    lib.la_decode_step_norm.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, vp]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i]
     lib.la_chunk_fwd_plan.restype = i
@@ -140,13 +146,16 @@ def state_init(state: torch.Tensor, stream=None) -> torch.Tensor:
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, C: int = 64,
               phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, decay=None, state=None,
-              out=None, workspace=None, stream=None) -> torch.Tensor:
+              out=None, workspace=None, stream=None, normalize: bool = False,
+              norm_state=None) -> torch.Tensor:
     """Chunkwise causal linear attention over [B,H,L,d] inputs; returns out [B,H,L,dv].
 
     `state` (fp32 [B,H,dk,dv]) is read as S_0 and overwritten with S_L when given.
+    normalize: the normalised form (la_chunk_fwd_norm); `norm_state` (fp32
+    [B,H,dk]) is read as z_0 and overwritten with z_L when given.
     """
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (decay, "decay"), (state, "state"),
-                 (out, "out"), (workspace, "workspace")):
+                 (out, "out"), (workspace, "workspace"), (norm_state, "norm_state")):
         _dev(t, n)
     B, H, L, dk = q.shape
     dv = v.shape[-1]
@@ -161,10 +170,19 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, C: int = 64,
         raise ValueError("decay data must be float32")
     if state is not None and (state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv)):
         raise ValueError("state must be float32 [B,H,dk,dv]")
+    if norm_state is not None and (norm_state.dtype != torch.float32
+                                   or tuple(norm_state.shape) != (B, H, dk)):
+        raise ValueError("norm_state must be float32 [B,H,dk]")
     need = chunk_fwd_workspace_bytes(B, H, L, dk, dv, C, dt, decay_kind)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if normalize:
+        _check(load().la_chunk_fwd_norm(_ptr(q), _ptr(k), _ptr(v), dt, B, H, L, dk, dv, C, phi,
+                                        decay_kind, _ptr(decay), _ptr(state), _ptr(norm_state),
+                                        _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
+               "la_chunk_fwd_norm")
+        return out
     _check(load().la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, H, L, dk, dv, C, phi,
                                decay_kind, _ptr(decay), _ptr(state), _ptr(out), _ptr(workspace),
                                ws_bytes, _stream(stream)), "la_chunk_fwd")
@@ -173,15 +191,25 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, C: int = 64,
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor,
                 phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, decay=None, out=None,
-                stream=None) -> torch.Tensor:
-    """One recurrent token for [N,H,d] inputs, updating `state` in place; returns o [N,H,dv]."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (state, "state"), (decay, "decay"), (out, "out")):
+                stream=None, norm_state=None) -> torch.Tensor:
+    """One recurrent token for [N,H,d] inputs, updating `state` in place; returns o [N,H,dv].
+
+    With `norm_state` (fp32 [N,H,dk], updated in place) the step is the
+    normalised form (la_decode_step_norm).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (state, "state"), (decay, "decay"), (out, "out"),
+                 (norm_state, "norm_state")):
         _dev(t, n)
     N, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    if norm_state is not None:
+        _check(load().la_decode_step_norm(_ptr(q), _ptr(k), _ptr(v), dt, N, H, dk, dv, phi,
+                                          decay_kind, _ptr(decay), _ptr(state), _ptr(norm_state),
+                                          _ptr(out), _stream(stream)), "la_decode_step_norm")
+        return out
     _check(load().la_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, N, H, dk, dv, phi, decay_kind,
                                  _ptr(decay), _ptr(state), _ptr(out), _stream(stream)),
            "la_decode_step")

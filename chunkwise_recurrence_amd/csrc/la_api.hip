@@ -35,7 +35,7 @@ struct Plan {
   int P = 1;         // sequence segments per head
   int seg_chunks = 0;
   size_t ws_bytes = 0;
-  size_t ws_S_off = 0, ws_logA_off = 0, ws_b_off = 0;
+  size_t ws_S_off = 0, ws_logA_off = 0, ws_b_off = 0, ws_z_off = 0;
   bool prefix = false;  // token decays: in-chunk prefix sums of log a in the workspace
 };
 
@@ -52,7 +52,8 @@ la_status check_chunk_shape(int dtype, int B, int H, int L, int d_k, int d_v, in
   return LA_OK;
 }
 
-Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int decay_kind) {
+Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int decay_kind,
+               bool norm = false) {
   Plan p;
   const int heads = B * H;
   const int nchunks = L > 0 ? (L + C - 1) / C : 0;
@@ -72,8 +73,9 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   // (16x16 MFMA, 4-wave workgroups over 32-column tiles, siblings sharing q
   // and k through L2).  Both measured on MI355X; la_set_plan overrides.
   int tile = 0;
-  const bool stripe_auto = d_v == 128 && d_k >= 64;
-  if (forced_kernel == LA_KERNEL_STRIPE || (forced_kernel == 0 && stripe_auto)) {
+  // the normalised form runs in the stripe kernel only
+  const bool stripe_auto = norm || (d_v == 128 && d_k >= 64);
+  if (norm || forced_kernel == LA_KERNEL_STRIPE || (forced_kernel == 0 && stripe_auto)) {
     // two waves per 32-column stripe (each holding half of the keys) where
     // d_k allows, for two waves per SIMD
     auto parts_for = [&](int t) {
@@ -120,6 +122,8 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
     off += round256((size_t)heads * p.P * d_k * d_v * sizeof(float));
     p.ws_logA_off = off;
     off += round256((size_t)heads * p.P * sizeof(float));
+    p.ws_z_off = off;  // the normalised form's per-segment z increments
+    off += round256((size_t)heads * p.P * d_k * sizeof(float));
   }
   if (decay_kind == LA_DECAY_TOKEN_LOG || decay_kind == LA_DECAY_TOKEN_GATE) {
     p.prefix = true;
@@ -180,7 +184,10 @@ size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C
                                     int decay_kind) {
   if (check_chunk_shape(dtype, B, H, L, d_k, d_v, C) != LA_OK || L == 0) return 0;
   if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return 0;
-  return make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind).ws_bytes;
+  // one size serves both forms: the larger of the two plans' workspaces
+  const size_t plain = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind).ws_bytes;
+  const size_t normed = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, true).ws_bytes;
+  return plain > normed ? plain : normed;
 }
 
 la_status la_state_init(float* state, int B, int H, int d_k, int d_v, void* stream) {
@@ -192,21 +199,28 @@ la_status la_state_init(float* state, int B, int H, int d_k, int d_v, void* stre
   return la::launch_fill_zero(state, n, as_stream(stream)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
 }
 
-la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H,
-                       int L, int d_k, int d_v, int C, int phi, int decay_kind,
-                       const float* decay_data, float* state, void* out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                         int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                         const float* decay_data, float* state, float* norm_state, bool norm,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
   la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
   if (st != LA_OK) return st;
   if (phi != LA_PHI_IDENTITY && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
   if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return LA_ERR_UNSUPPORTED;
+  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, norm);
+  // bf16 inputs reach the normalised form through the stripe kernel only
+  if (norm && dtype == LA_BF16 && p.kernel != LA_KERNEL_STRIPE) return LA_ERR_UNSUPPORTED;
   if (L == 0) return LA_OK;
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (decay_kind != LA_DECAY_NONE && !decay_data) return LA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      (state && !aligned(state, 16)) || (decay_data && !aligned(decay_data, 4)))
+      (state && !aligned(state, 16)) || (norm_state && !aligned(norm_state, 16)) ||
+      (decay_data && !aligned(decay_data, 4)))
     return LA_ERR_ALIGN;
-  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind);
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return LA_ERR_ALIGN;
@@ -232,6 +246,8 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
   a.n_v = d_v / p.tile;
   a.P = p.P;
   a.seg_chunks = p.seg_chunks;
+  a.norm = norm ? 1 : 0;
+  a.zstate = norm ? norm_state : nullptr;
   const hipStream_t s = as_stream(stream);
 
   hipError_t e;
@@ -248,6 +264,7 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
     if (p.P > 1) {
       a.ws_S = reinterpret_cast<float*>(ws + p.ws_S_off);
       a.ws_logA = reinterpret_cast<float*>(ws + p.ws_logA_off);
+      a.ws_z = reinterpret_cast<float*>(ws + p.ws_z_off);
       a.n_units = B * H * (p.P - 1);
       e = p.kernel == LA_KERNEL_STRIPE ? la::launch_chunk_stripe(a, /*state_only=*/true, s)
                                        : la::launch_chunk_bf16(a, /*state_only=*/true, s);
@@ -260,18 +277,19 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
   return e == hipSuccess ? LA_OK : LA_ERR_DEVICE;
 }
 
-la_status la_decode_step(const void* q, const void* k, const void* v, int dtype, int N, int H,
-                         int d_k, int d_v, int phi, int decay_kind, const float* decay_data,
-                         float* state, void* out, void* stream) {
+la_status decode_impl(const void* q, const void* k, const void* v, int dtype, int N, int H,
+                      int d_k, int d_v, int phi, int decay_kind, const float* decay_data,
+                      float* state, float* norm_state, bool norm, void* out, void* stream) {
   if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
   if (N < 1 || H < 1) return LA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return LA_ERR_UNSUPPORTED;
   if (phi != LA_PHI_IDENTITY && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
   if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return LA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !state || !out) return LA_ERR_NULL;
+  if (!q || !k || !v || !state || !out || (norm && !norm_state)) return LA_ERR_NULL;
   if (decay_kind != LA_DECAY_NONE && !decay_data) return LA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      !aligned(state, 16) || (decay_data && !aligned(decay_data, 4)))
+      !aligned(state, 16) || (norm && !aligned(norm_state, 16)) ||
+      (decay_data && !aligned(decay_data, 4)))
     return LA_ERR_ALIGN;
   la::DecodeArgs a{};
   a.q = q;
@@ -279,6 +297,7 @@ la_status la_decode_step(const void* q, const void* k, const void* v, int dtype,
   a.v = v;
   a.out = out;
   a.state = state;
+  a.zstate = norm ? norm_state : nullptr;
   a.decay = decay_kind == LA_DECAY_NONE ? nullptr : decay_data;
   a.N = N;
   a.H = H;
@@ -287,6 +306,41 @@ la_status la_decode_step(const void* q, const void* k, const void* v, int dtype,
   a.phi = phi;
   a.decay_kind = decay_kind;
   return la::launch_decode(a, dtype, as_stream(stream)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                       int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                       const float* decay_data, float* state, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl(q, k, v, dtype, B, H, L, d_k, d_v, C, phi, decay_kind, decay_data, state,
+                        nullptr, false, out, workspace, workspace_bytes, stream);
+}
+
+la_status la_chunk_fwd_norm(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                            int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                            const float* decay_data, float* state, float* norm_state, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl(q, k, v, dtype, B, H, L, d_k, d_v, C, phi, decay_kind, decay_data, state,
+                        norm_state, true, out, workspace, workspace_bytes, stream);
+}
+
+la_status la_decode_step(const void* q, const void* k, const void* v, int dtype, int N, int H,
+                         int d_k, int d_v, int phi, int decay_kind, const float* decay_data,
+                         float* state, void* out, void* stream) {
+  return decode_impl(q, k, v, dtype, N, H, d_k, d_v, phi, decay_kind, decay_data, state, nullptr,
+                     false, out, stream);
+}
+
+la_status la_decode_step_norm(const void* q, const void* k, const void* v, int dtype, int N,
+                              int H, int d_k, int d_v, int phi, int decay_kind,
+                              const float* decay_data, float* state, float* norm_state, void* out,
+                              void* stream) {
+  return decode_impl(q, k, v, dtype, N, H, d_k, d_v, phi, decay_kind, decay_data, state,
+                     norm_state, true, out, stream);
 }
 
 }  // extern "C"

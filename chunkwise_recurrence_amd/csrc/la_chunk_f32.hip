@@ -7,7 +7,9 @@
 // exactness rather than speed: plain fp32 FMA, the decayed score block and the
 // state tile in LDS, q and k read through the caches with phi applied on the
 // fly.  One workgroup per (head, 32-column value tile), chunks in sequence.
-// It serves small fp32 problems such as the 300 x 16 demo.
+// It serves small fp32 problems such as the 300 x 16 demo.  The normalised
+// form also carries z (z <- e^{b_last} z + sum_j e^{b_last - b_j} phi(k_j)) and
+// divides each output row by e^{b_i} phi(q_i).z + sum_{j<=i} P[i][j].
 #include "la_device.h"
 
 namespace la {
@@ -33,6 +35,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
   __shared__ float sP[kMaxC * kMaxC];
   __shared__ float sS[128 * kTileF32];
   __shared__ float sB[kMaxC];
+  __shared__ float sZ[128], sDen[kMaxC];
+  const bool norm = a.norm != 0;
 
   const float* qh = static_cast<const float*>(a.q) + (size_t)bh * L * DK;
   const float* kh = static_cast<const float*>(a.k) + (size_t)bh * L * DK;
@@ -45,6 +49,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
     const int d = i / tv, v = i % tv;
     sS[i] = a.state ? a.state[((size_t)bh * DK + d) * DV + dv0 + v] : 0.0f;
   }
+  if (norm)
+    for (int d = tid; d < DK; d += 256) sZ[d] = a.zstate ? a.zstate[(size_t)bh * DK + d] : 0.0f;
 
   for (int t0 = 0; t0 < L; t0 += C) {
     const int n = min(C, L - t0);
@@ -72,6 +78,17 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
       sP[i * kMaxC + j] = p;
     }
     __syncthreads();
+    // normalised form: den_i = e^{b_i} phi(q_i).z + sum_{j<=i} P[i][j]
+    if (norm) {
+      for (int i = tid; i < n; i += 256) {
+        const float* qi = qh + (size_t)(t0 + i) * DK;
+        float dz = 0.0f, ds = 0.0f;
+        for (int d = 0; d < DK; ++d) dz = fmaf(phi_f32(elu, qi[d]), sZ[d], dz);
+        for (int j = 0; j <= i; ++j) ds += sP[i * kMaxC + j];
+        sDen[i] = expf(sB[i]) * dz + ds;
+      }
+      __syncthreads();
+    }
     // o_i = e^{b_i} phi(q_i)^T S + sum_{j<=i} P[i][j] v_j
     for (int idx = tid; idx < n * tv; idx += 256) {
       const int i = idx / tv, v = idx % tv;
@@ -80,7 +97,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
       for (int d = 0; d < DK; ++d) inter = fmaf(phi_f32(elu, qi[d]), sS[d * tv + v], inter);
       float intra = 0.0f;
       for (int j = 0; j <= i; ++j) intra = fmaf(sP[i * kMaxC + j], vh[(size_t)(t0 + j) * DV + v], intra);
-      oh[(size_t)(t0 + i) * DV + v] = expf(sB[i]) * inter + intra;
+      const float o = expf(sB[i]) * inter + intra;
+      oh[(size_t)(t0 + i) * DV + v] = norm ? o / sDen[i] : o;
     }
     __syncthreads();
     // S <- e^{b_last} S + sum_j e^{b_last - b_j} phi(k_j) v_j^T
@@ -92,6 +110,14 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
                    vh[(size_t)(t0 + j) * DV + v], acc);
       sS[idx] = expf(bL) * sS[idx] + acc;
     }
+    if (norm) {
+      for (int d = tid; d < DK; d += 256) {
+        float acc = 0.0f;
+        for (int j = 0; j < n; ++j)
+          acc = fmaf(expf(bL - sB[j]), phi_f32(elu, kh[(size_t)(t0 + j) * DK + d]), acc);
+        sZ[d] = expf(bL) * sZ[d] + acc;
+      }
+    }
   }
   __syncthreads();
   if (a.state) {
@@ -100,6 +126,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
       a.state[((size_t)bh * DK + d) * DV + dv0 + v] = sS[i];
     }
   }
+  if (norm && a.zstate && vt == 0)
+    for (int d = tid; d < DK; d += 256) a.zstate[(size_t)bh * DK + d] = sZ[d];
 }
 
 }  // namespace

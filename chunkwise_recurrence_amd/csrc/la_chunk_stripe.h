@@ -38,6 +38,15 @@
 //     2 KB LDS slot of its wave and leaves as 16-byte stores, 64 contiguous
 //     bytes per row.
 //
+// NORM adds the normalised form (the tutorial's section 2.2, boxed
+// recurrence): z_t = a_t z_{t-1} + phi(k_t) is carried like one more value
+// column of ones and o_t = phi(q_t)^T S_t / phi(q_t)^T z_t.  Per chunk the
+// denominator is e^{b_i} phi(q_i).z_c (one more MFMA per key step with z in
+// the first row of the A operand, computed by the waves of stripe 0) plus the
+// row sums of the masked, decayed scores (taken where the score blocks are
+// made); z itself is updated by the waves of stripe 0 from the K^T operands
+// and token weights of the state update.
+//
 // STATE_ONLY computes a segment's state increment and total log2 decay from a
 // zero state (the first pass of the segment split).  It walks the segment's
 // chunks last to first, weighting token t by e^{B_end - B_t} directly (the sum
@@ -96,11 +105,14 @@ struct Geo {
   static constexpr bool UNIFORM = QK_BLK % NW == 0 && V_BLK % NW == 0 && NRB % KH == 0 &&
                                   STORES + LOADS_MAX < 64;
   static constexpr size_t XCH_BYTES = KH > 1 ? (size_t)NWV * NRB * 4096 : 16;
+  // the normalised form's z, denominator partials and row sums (counted for
+  // every instance, so both forms run the same pipeline depth)
+  static constexpr size_t NORM_BYTES = 2 * 4 * (size_t)DK + 4 * (size_t)C * (KH + NRB);
   static constexpr size_t stage_bytes(int n) {
     return SO ? (size_t)n * ((size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
-                    2 * 4 * (size_t)NW * C + 256
+                    2 * 4 * (size_t)NW * C + NORM_BYTES + 256
               : (size_t)n * (2 * (size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
-                    2 * (size_t)C * C + 2 * 4 * (size_t)NW * C + XCH_BYTES + 2048 * (size_t)NW + 256;
+                    2 * (size_t)C * C + 2 * 4 * (size_t)NW * C + XCH_BYTES + 2048 * (size_t)NW  + NORM_BYTES + 256;
   }
   static constexpr int NSTG =
       (UNIFORM && stage_bytes(3) <= kMaxLds && 2 * STORES + LOADS_MAX < 64) ? 3 : 2;
@@ -214,7 +226,7 @@ __host__ __device__ constexpr int block_i(int b) {
 }
 __host__ __device__ constexpr int block_j(int b) { return b - block_i(b) * (block_i(b) + 1) / 2; }
 
-template <int DK, int NWV, int KH, int C, int CAT, bool STATE_ONLY>
+template <int DK, int NWV, int KH, int C, int CAT, bool STATE_ONLY, bool NORM>
 __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const ChunkArgs a) {
   using G = Geo<DK, NWV, KH, C, STATE_ONLY>;
   constexpr int NS = G::NSTG;
@@ -258,6 +270,11 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   __shared__ __align__(16) char sX[(STATE_ONLY || KH == 1) ? 16 : G::XCH_BYTES];
   // per-wave weights of the current chunk: [0] e^{b_last - b_t}, [1] e^{b_t}
   __shared__ __align__(16) float sW[NW][2][C];
+  // normalised form: z (double-buffered by chunk parity), the denominators'
+  // inter-chunk partials per key part and the score row sums per key block
+  __shared__ __align__(16) float sZ[NORM ? 2 : 1][NORM ? DK : 4];
+  __shared__ __align__(16) float sDen[(NORM && !STATE_ONLY) ? KH : 1][(NORM && !STATE_ONLY) ? C : 4];
+  __shared__ __align__(16) float sRS[(NORM && !STATE_ONLY) ? G::NRB : 1][(NORM && !STATE_ONLY) ? C : 4];
   // per-wave staging of one bf16 output row block: 32 rows x 64 bytes
   __shared__ __align__(16) char sO[STATE_ONLY ? 1 : NW][STATE_ONLY ? 16 : 2048];
 
@@ -330,6 +347,26 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         accS[t][r] = sv;
       }
   }
+  // normalised form: the waves of stripe 0 hold z for their keys, lane l32
+  // of own tile t holding key 32 (mk0 + t) + l32
+  float zr[NORM ? G::NMK_OWN : 1];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int t = 0; t < G::NMK_OWN; ++t) {
+      const int dk = 32 * (mk0 + t) + l32;
+      float zv = 0.0f;
+      if constexpr (!STATE_ONLY) {
+        zv = a.zstate ? a.zstate[(size_t)bh * DK + dk] : 0.0f;
+        for (int p = 0; p < sigma; ++p) {
+          const size_t seg = (size_t)bh * a.P + p;
+          zv = exp2f(a.ws_logA[seg]) * zv + a.ws_z[seg * DK + dk];
+        }
+      }
+      zr[t] = zv;
+      if (stripe == 0 && h == 0) sZ[0][dk] = zv;
+    }
+  }
+
   // bf16 A operands of the inter-chunk term: own key step s (global step
   // part * NKS_OWN + s) uses own tile s / 2, registers 8 (s % 2) .. +7
   u32x4 sbf[G::NKS_OWN];
@@ -520,6 +557,14 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
             for (int r = 0; r < 16; ++r) pacc[r] *= dm[bb][r];
           }
           const int i = 32 * I + l32;
+          if constexpr (NORM) {
+            // row i's sum over the block's 32 tokens (16 per lane half)
+            float rs = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rs += pacc[r];
+            rs += __shfl_xor(rs, 32);
+            if (h == 0) sRS[J][i] = rs;
+          }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             u32x2 w;
@@ -533,19 +578,45 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       // (1b) inter-chunk term over this wave's keys, every row block:
       //      part[I] = S_part^T Q_part^T (transposed: lane = row, registers = values)
       pack_state();
+      // normalised form, stripe 0: z of this wave's keys as the first row of
+      // an A operand (every other row zero), in the key order of sbf
+      u32x4 zA[NORM ? G::NKS_OWN : 1];
+      if constexpr (NORM) {
+        const float* zc = sZ[it & 1];
+#pragma unroll
+        for (int s = 0; s < G::NKS_OWN; ++s) {
+          const int sg = part * G::NKS_OWN + s;
+          const f32x4 z0 = *reinterpret_cast<const f32x4*>(&zc[16 * sg + 4 * h]);
+          const f32x4 z1 = *reinterpret_cast<const f32x4*>(&zc[16 * sg + 8 + 4 * h]);
+          const u32x4 w = u32x4{cvt2(z0[0], z0[1]), cvt2(z0[2], z0[3]), cvt2(z1[0], z1[1]),
+                                cvt2(z1[2], z1[3])};
+          zA[s] = l32 == 0 ? w : zero4;
+        }
+      }
       f32x16 pin[G::NRB];
 #pragma unroll
       for (int I = 0; I < G::NRB; ++I) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) pin[I][r] = 0.0f;
+        f32x16 dacc;
+        if constexpr (NORM) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dacc[r] = 0.0f;
+        }
         const int i = 32 * I + l32;
 #pragma unroll
         for (int s = 0; s < G::NKS_OWN; ++s) {
           const int sg = part * G::NKS_OWN + s;
           const u32x2 lo = lds_b64(qb, swz<G::WCK>(i, 16 * sg + 4 * h));
           const u32x2 hi = lds_b64(qb, swz<G::WCK>(i, 16 * sg + 8 + 4 * h));
-          pin[I] = mfma32(sbf[s], u32x4{lo[0], lo[1], hi[0], hi[1]}, pin[I]);
+          const u32x4 qop = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          pin[I] = mfma32(sbf[s], qop, pin[I]);
+          if constexpr (NORM)
+            if (stripe == 0) dacc = mfma32(zA[s], qop, dacc);
         }
+        // row i's partial phi(q_i).z over this wave's keys sits in register 0 of lane (i, h = 0)
+        if constexpr (NORM)
+          if (stripe == 0 && h == 0) sDen[part][i] = dacc[0];
       }
       // row block I belongs to key part I % KH; the other parts hand it their partial
       if constexpr (KH > 1) {
@@ -576,8 +647,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
           }
         }
         const int i = 32 * I + l32;
+        float er = 1.0f;
         if constexpr (CAT != kCatNone) {
-          const float er = eq[i];
+          er = eq[i];
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] *= er;
         }
@@ -589,6 +661,17 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
             const u32x4 pB = lds_b128(sP, swz<G::WCP>(i, 16 * ks + 8 * h));
             acc = mfma32(vA[ks], pB, acc);
           }
+        if constexpr (NORM) {
+          // denominator of row i: e^{b_i} phi(q_i).z_c + its masked score row sum
+          float dz = 0.0f, ds = 0.0f;
+#pragma unroll
+          for (int p = 0; p < KH; ++p) dz += sDen[p][i];
+#pragma unroll
+          for (int J = 0; J <= I; ++J) ds += sRS[J][i];
+          const float inv = 1.0f / (er * dz + ds);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] *= inv;
+        }
         // lane: row i, value columns cw + 8 q + 4 h + (0..3) -> LDS slot,
         // then 16-byte pieces of whole rows -> HBM
         char* so = sO[wave];
@@ -620,14 +703,29 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
         for (int r = 0; r < 16; ++r) accS[t][r] *= eL;
     }
+    float zacc[NORM ? G::NMK_OWN : 1];
+    if constexpr (NORM) {
+#pragma unroll
+      for (int t = 0; t < G::NMK_OWN; ++t) zacc[t] = 0.0f;
+    }
 #pragma unroll
     for (int ks = 0; ks < G::NTS; ++ks) {
       u32x4 vB = vA[ks];
+      float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+      if constexpr (CAT == kCatNone && NORM) {
+        // rows past a short last chunk hold phi(0), not 0: keep them out of z
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = 16 * ks + 8 * h + e < nvalid ? 1.0f : 0.0f;
+      }
       if constexpr (CAT != kCatNone) {
         const int tb = 16 * ks + 8 * h;
         const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wq[tb]);
         const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wq[tb + 4]);
-        const float w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[e] = w0[e];
+          w[4 + e] = w1[e];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           vB[e] = cvt2(bf16_to_f32(vB[e] & 0xffffu) * w[2 * e], bf16_to_f32(vB[e] >> 16) * w[2 * e + 1]);
@@ -637,6 +735,25 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         const u32x4 kA =
             lds_tr8<G::WCK>(kb, 16 * ks + 8 * (g4 >> 1), 32 * (mk0 + t) + 16 * (g4 & 1), l16);
         accS[t] = mfma32(kA, vB, accS[t]);
+        if constexpr (NORM) {
+          // z += sum_t w_t phi(k_t) over this lane's 8 tokens of key 32 (mk0 + t) + l32
+          if (stripe == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              zacc[t] += w[2 * e] * bf16_to_f32(kA[e] & 0xffffu) + w[2 * e + 1] * bf16_to_f32(kA[e] >> 16);
+          }
+        }
+      }
+    }
+    if constexpr (NORM) {
+      if (stripe == 0) {
+        const float eLz = (CAT != kCatNone && !STATE_ONLY) ? __builtin_amdgcn_exp2f(bL) : 1.0f;
+#pragma unroll
+        for (int t = 0; t < G::NMK_OWN; ++t) {
+          const float zsum = zacc[t] + __shfl_xor(zacc[t], 32);
+          zr[t] = eLz * zr[t] + zsum;
+          if (h == 0) sZ[(it + 1) & 1][32 * (mk0 + t) + l32] = zr[t];
+        }
       }
     }
     logA += bL;
@@ -676,6 +793,15 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       for (int r = 0; r < 16; ++r)
         dst[(size_t)(32 * (mk0 + t) + 8 * (r >> 2) + 4 * h + (r & 3)) * DV + dv] = accS[t][r];
   }
+  if constexpr (NORM) {
+    float* zdst = nullptr;
+    if constexpr (STATE_ONLY) zdst = a.ws_z + ((size_t)bh * a.P + sigma) * DK;
+    else if (sigma == a.P - 1 && a.zstate != nullptr) zdst = a.zstate + (size_t)bh * DK;
+    if (zdst != nullptr && stripe == 0 && h == 0 && vt == 0) {
+#pragma unroll
+      for (int t = 0; t < G::NMK_OWN; ++t) zdst[32 * (mk0 + t) + l32] = zr[t];
+    }
+  }
 }
 
 // ---- launch and dispatch ----------------------------------------------------
@@ -683,10 +809,17 @@ template <int DK, int NWV, int KH, int C, int CAT>
 hipError_t launch_one(const ChunkArgs& a, bool state_only, hipStream_t s) {
   const int groups = (a.n_units + 7) / 8;
   const dim3 grid(groups * 8 * a.n_v), block(64 * NWV * KH);
-  if (state_only)
-    hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, false>), grid, block, 0, s, a);
+  if (a.norm) {
+    if (state_only)
+      hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, true, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, false, true>), grid, block, 0, s, a);
+  } else {
+    if (state_only)
+      hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, true, false>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -728,15 +861,6 @@ hipError_t dispatch_w(const ChunkArgs& a, bool so, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int DK>
-hipError_t dispatch_cat(const ChunkArgs& a, bool so, hipStream_t s) {
-  switch (a.decay_kind) {
-    case kDecayNone: return dispatch_w<DK, kCatNone>(a, so, s);
-    case kDecayHead: return dispatch_w<DK, kCatHead>(a, so, s);
-    default: return dispatch_w<DK, kCatToken>(a, so, s);
-  }
-}
-
 template <int DK, int NWV, int KH>
 constexpr size_t lds_c(int C) {
   return C == 32 ? Geo<DK, NWV, KH, 32>::LDS
@@ -753,8 +877,12 @@ constexpr size_t lds_of(int TVW, int KH, int C) {
 
 }  // namespace stripe
 
-hipError_t launch_chunk_stripe_dk32(const ChunkArgs& a, bool state_only, hipStream_t s);
-hipError_t launch_chunk_stripe_dk64(const ChunkArgs& a, bool state_only, hipStream_t s);
-hipError_t launch_chunk_stripe_dk128(const ChunkArgs& a, bool state_only, hipStream_t s);
+// One per (key dimension, decay category), each in its own translation unit.
+#define LA_STRIPE_DECL(DK, CAT) \
+  hipError_t launch_chunk_stripe_dk##DK##_c##CAT(const ChunkArgs& a, bool state_only, hipStream_t s);
+LA_STRIPE_DECL(32, 0) LA_STRIPE_DECL(32, 1) LA_STRIPE_DECL(32, 2)
+LA_STRIPE_DECL(64, 0) LA_STRIPE_DECL(64, 1) LA_STRIPE_DECL(64, 2)
+LA_STRIPE_DECL(128, 0) LA_STRIPE_DECL(128, 1) LA_STRIPE_DECL(128, 2)
+#undef LA_STRIPE_DECL
 
 }  // namespace la

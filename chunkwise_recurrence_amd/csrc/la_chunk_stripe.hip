@@ -19,11 +19,19 @@ bool chunk_stripe_supported(int DK, int TVW, int KH, int C) {
 }
 
 hipError_t launch_chunk_stripe(const ChunkArgs& a, bool state_only, hipStream_t s) {
+  const int cat = a.decay_kind == kDecayNone ? stripe::kCatNone
+                  : a.decay_kind == kDecayHead ? stripe::kCatHead : stripe::kCatToken;
+#define LA_CASE(DK)                                                       \
+  case DK:                                                                \
+    return cat == 0 ? launch_chunk_stripe_dk##DK##_c0(a, state_only, s)   \
+           : cat == 1 ? launch_chunk_stripe_dk##DK##_c1(a, state_only, s) \
+                      : launch_chunk_stripe_dk##DK##_c2(a, state_only, s);
   switch (a.DK) {
-    case 32: return launch_chunk_stripe_dk32(a, state_only, s);
-    case 64: return launch_chunk_stripe_dk64(a, state_only, s);
-    case 128: return launch_chunk_stripe_dk128(a, state_only, s);
+    LA_CASE(32)
+    LA_CASE(64)
+    LA_CASE(128)
   }
+#undef LA_CASE
   return hipErrorInvalidValue;
 }
 

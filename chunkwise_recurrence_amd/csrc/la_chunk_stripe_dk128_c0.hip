@@ -1,0 +1,9 @@
+// Instantiations of the stripe kernel for d_k = 128, decay category 0
+// (0 none, 1 per head, 2 per token); one file each so they compile in parallel.
+#include "la_chunk_stripe.h"
+
+namespace la {
+hipError_t launch_chunk_stripe_dk128_c0(const ChunkArgs& a, bool state_only, hipStream_t s) {
+  return stripe::dispatch_w<128, 0>(a, state_only, s);
+}
+}  // namespace la

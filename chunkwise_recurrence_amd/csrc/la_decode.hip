@@ -6,6 +6,9 @@
 //
 //   S' = a S + phi(k) v^T,   o = phi(q)^T S'
 //
+// The normalised form also updates z' = a z + phi(k) and divides o by
+// phi(q)^T z' (the tutorial's section 2.2, boxed recurrence).
+//
 // The step is a pure stream over the fp32 state: every element is read once,
 // updated and written once, and o is reduced on the way.  One workgroup of 256
 // lanes per head; each lane owns 4 adjacent columns (one 16-byte vector) of
@@ -62,6 +65,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   if (a.decay_kind == kDecayHead) decay = a.decay[h];
   else if (a.decay_kind == kDecayLog || a.decay_kind == kDecayGate)
     decay = expf(token_log_decay(a.decay_kind, a.decay[bh]));
+  __shared__ float sden[DK];
+  if (a.zstate != nullptr) {
+    __syncthreads();
+    if (tid < DK) {
+      float* zp = a.zstate + (size_t)bh * DK + tid;
+      const float z = fmaf(decay, *zp, sk[tid]);
+      *zp = z;
+      sden[tid] = sq[tid] * z;
+    }
+  }
   __syncthreads();
 
   const float4 vv = make_float4(sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]);
@@ -95,6 +108,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     constexpr int used = DK < RP ? DK : RP;
 #pragma unroll
     for (int g = 0; g < used; ++g) acc += red[g][tid];
+    if (a.zstate != nullptr) {
+      float den = 0.0f;
+      for (int d = 0; d < DK; ++d) den += sden[d];
+      acc /= den;
+    }
     if constexpr (BF16)
       static_cast<uint16_t*>(a.out)[(size_t)bh * DV + tid] = (uint16_t)f32_to_bf16(acc);
     else

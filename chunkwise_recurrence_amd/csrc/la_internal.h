@@ -23,6 +23,9 @@ struct ChunkArgs {
   float* ws_S;          // [B*H, P, DK, DV] per-segment state increments
   float* ws_logA;       // [B*H, P] per-segment total log decay
   float* ws_b;          // [B*H, L] in-chunk inclusive prefix of log a (token decays)
+  float* zstate;        // normalised form: [B,H,DK] z in/out, or nullptr
+  float* ws_z;          // normalised form: [B*H, P, DK] per-segment z increments
+  int norm;             // 1: the normalised form
   int B, H, L, DK, DV, C;
   int P;                // sequence segments per head
   int seg_chunks;       // chunks per segment (the last one may hold fewer)
@@ -40,6 +43,7 @@ struct DecodeArgs {
   const void* v;        // [N,H,DV]
   void* out;            // [N,H,DV]
   float* state;         // [N,H,DK,DV]
+  float* zstate;        // normalised form: [N,H,DK], or nullptr
   const float* decay;   // nullptr | gamma[H] | [N,H]
   int N, H, DK, DV;
   int phi, decay_kind;

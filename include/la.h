@@ -81,11 +81,12 @@ typedef enum {
 la_status la_state_init(float* state, int B, int H, int d_k, int d_v, void* stream);
 
 /*
- * la_chunk_fwd_workspace_bytes -- bytes of device workspace la_chunk_fwd needs
- * for this problem (0 when none is needed): per-segment state increments when
- * the sequence is split into segments, and the in-chunk prefix sums of log a
- * (4 bytes per head-token) for the token-dependent decays.  Pure host
- * function; returns 0 for arguments la_chunk_fwd would reject.
+ * la_chunk_fwd_workspace_bytes -- bytes of device workspace la_chunk_fwd and
+ * la_chunk_fwd_norm need for this problem (0 when none is needed): per-segment
+ * state (and normaliser) increments when the sequence is split into segments,
+ * and the in-chunk prefix sums of log a (4 bytes per head-token) for the
+ * token-dependent decays.  Pure host function; returns 0 for arguments
+ * la_chunk_fwd would reject.
  */
 size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                                     int decay_kind);
@@ -132,6 +133,40 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
 la_status la_decode_step(const void* q, const void* k, const void* v, int dtype, int N, int H,
                          int d_k, int d_v, int phi, int decay_kind, const float* decay_data,
                          float* state, void* out, void* stream);
+
+/*
+ * la_chunk_fwd_norm -- the normalised form (the linear/sparse attention
+ * tutorial, section 2.2, boxed recurrence):
+ *
+ *   S_t = a_t S_{t-1} + phi(k_t) v_t^T,   z_t = a_t z_{t-1} + phi(k_t),
+ *   o_t = phi(q_t)^T S_t / phi(q_t)^T z_t
+ *
+ * z is carried chunkwise as one more value column of ones (tutorial section
+ * 6.2).  Nothing is added to the denominator (the pages give no term); it
+ * stays positive for phi = elu + 1 and positive initial z, and is otherwise
+ * the caller's responsibility (a zero gives Inf/NaN).
+ *   norm_state : [B,H,d_k] fp32 z; in: z_0, out: z_L.  NULL: z_0 = 0 and
+ *                z_L is not written.  16-byte aligned.
+ * Every other argument, the workspace size (la_chunk_fwd_workspace_bytes)
+ * and the errors are those of la_chunk_fwd.  bf16 inputs need d_k, d_v >= 32
+ * and C in {32, 64, 128} within the LDS (else LA_ERR_UNSUPPORTED); fp32
+ * inputs take every supported shape.
+ */
+la_status la_chunk_fwd_norm(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                            int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                            const float* decay_data, float* state, float* norm_state, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * la_decode_step_norm -- one token of the normalised form for N x H heads:
+ * S' = a S + phi(k) v^T, z' = a z + phi(k), o = phi(q)^T S' / phi(q)^T z'.
+ *   norm_state : [N,H,d_k] fp32 z, updated in place (required).
+ * Every other argument and the errors are those of la_decode_step.
+ */
+la_status la_decode_step_norm(const void* q, const void* k, const void* v, int dtype, int N,
+                              int H, int d_k, int d_v, int phi, int decay_kind,
+                              const float* decay_data, float* state, float* norm_state, void* out,
+                              void* stream);
 
 /* la_status_string -- a static, human-readable name for a status code. */
 const char* la_status_string(int status);

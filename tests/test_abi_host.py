@@ -166,6 +166,38 @@ def test_state_init_rejects(args, code):
     assert la.load().la_state_init(*args, None) == code
 
 
+def _fwd_norm(**kw):
+    a = dict(q=P16, k=P16, v=P16, dtype=1, B=1, H=1, L=64, dk=64, dv=64, C=64, phi=1, kind=0,
+             decay=None, state=None, z=None, out=P16, ws=None, ws_bytes=0)
+    a.update(kw)
+    return la.load().la_chunk_fwd_norm(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["H"], a["L"],
+                                       a["dk"], a["dv"], a["C"], a["phi"], a["kind"], a["decay"],
+                                       a["state"], a["z"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(B=0), SHAPE), (dict(dk=48), UNSUP),
+    # bf16 normalised form: the stripe kernel's shapes only
+    (dict(dk=16, dv=16), UNSUP), (dict(dv=16), UNSUP), (dict(C=16), UNSUP),
+    (dict(z=P8), ALIGN), (dict(state=P8), ALIGN),
+])
+def test_chunk_fwd_norm_rejects(kw, code):
+    assert _fwd_norm(**kw) == code
+
+
+def test_chunk_fwd_norm_fp32_takes_every_shape():
+    # the fp32 kernel has no shape limits beyond the common ones; L = 0 returns before any launch
+    assert _fwd_norm(dtype=0, dk=16, dv=16, C=16, L=0) == OK
+
+
+def test_decode_norm_requires_its_state():
+    lib = la.load()
+    assert lib.la_decode_step_norm(P16, P16, P16, 1, 2, 2, 64, 64, 1, 0, None, P16, None, P16,
+                                   None) == NULL
+    assert lib.la_decode_step_norm(P16, P16, P16, 1, 2, 2, 64, 64, 1, 0, None, P16, P8, P16,
+                                   None) == ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 16)
