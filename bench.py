@@ -128,6 +128,40 @@ def bench_chunk(la, torch, W, steps, warmup):
                 kernel=kernel, tile=tile, P=P, groups=groups, need=need)
 
 
+def bench_chunk_norm(la, torch, W, steps, warmup):
+    """The normalised form (la_chunk_fwd_norm) on the timed workload's shapes,
+    with phi = elu + 1 so that every denominator is positive."""
+    w = W.WORKLOADS["retnet_bf16"]
+    dev = torch.device("cuda:0")
+    q, k, v, gamma = W.chunk_inputs(w)
+    q, k, v, gamma = q.to(dev), k.to(dev), v.to(dev), gamma.to(dev)
+    S = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
+    z = torch.zeros(w.B, w.H, w.dk, device=dev)
+    out = torch.empty_like(v)
+    need = la.chunk_fwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, w.C, la.LA_BF16, w.decay_kind)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        la.chunk_fwd(q, k, v, C=w.C, phi=la.PHI_ELU1, decay_kind=w.decay_kind, decay=gamma,
+                     state=S, out=out, workspace=ws if need else None, stream=stream,
+                     normalize=True, norm_state=z)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    by, _ = chunk_algorithmic(w, with_state=True)
+    by += 2 * w.B * w.H * w.dk * 4                 # read z_0, write z_L
+    return dict(w=w, ms=ms, bytes=by)
+
+
 def bench_decode(la, torch, W, steps, reps=3):
     w = W.DECODE
     dev = torch.device("cuda:0")
@@ -238,6 +272,7 @@ def main():
         profile_pass(la, torch, W)
         return
     c = bench_chunk(la, torch, W, args.steps, args.warmup)
+    n = bench_chunk_norm(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
     d = bench_decode(la, torch, W, args.decode_steps)
     w = c["w"]
     tokens = w.B * w.L
@@ -271,6 +306,11 @@ def main():
                      "mfma_tflops": c["flops"] / (c["kern_ms"] / 1000.0) / 1e12,
                      "mfma_frac": c["flops"] / (c["kern_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS,
                      "rocprof_mfma_busy_pct": profile_value(MFMA_PROFILE, "mfma_busy_pct")},
+        "normalized": {"workload": "retnet_bf16 shapes, normalised form, phi = elu+1",
+                       "ms_per_call": n["ms"], "tokens_per_s": tokens / (n["ms"] / 1000.0),
+                       "algorithmic_bytes": n["bytes"],
+                       "achieved_GBs": n["bytes"] / (n["ms"] / 1000.0) / 1e9,
+                       "hbm_frac": n["bytes"] / (n["ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS},
         "decode": {"workload": "decode_bf16", "N": d["w"].N, "H": d["w"].H, "d": d["w"].dk,
                    "steps": d["steps"], "steps_per_s": 1e6 / d["step_us"],
                    "us_per_step": d["step_us"], "bytes_per_step": d["bytes"],
