@@ -43,6 +43,7 @@ DECAY_NONE = 0
 DECAY_HEAD = 1
 DECAY_LOG = 2
 DECAY_GATE = 3
+DECAY_CHANNEL = 4
 
 _libs: dict = {}
 
@@ -113,6 +114,8 @@ def recurrent(q, k, v, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, de
         dec = np.zeros(1)
     elif decay_kind == DECAY_HEAD:
         dec = _f64(decay).reshape(H)
+    elif decay_kind == DECAY_CHANNEL:
+        dec = _f64(decay).reshape(B, H, L, dk)
     else:
         dec = _f64(decay).reshape(B, H, L)
     if B * H == 0 or L == 0:
@@ -142,6 +145,8 @@ def decode_step(q, k, v, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE, 
     dec = decay
     if decay_kind in (DECAY_LOG, DECAY_GATE):
         dec = _f64(decay).reshape(N, H, 1)
+    elif decay_kind == DECAY_CHANNEL:
+        dec = _f64(decay).reshape(N, H, 1, -1)
     r = recurrent(q[:, :, None, :], k[:, :, None, :], v[:, :, None, :], phi, decay_kind,
                   dec, state, lib_path=lib_path, normalize=normalize, norm_state=norm_state)
     return (r[0][:, :, 0, :],) + tuple(r[1:])
@@ -159,7 +164,10 @@ def feature_map(x, phi: int) -> np.ndarray:
 
 
 def decay_multipliers(B: int, H: int, L: int, decay_kind: int, decay) -> np.ndarray:
-    """a_t for every (b, h, t) as fp64 [B,H,L] (1 for no decay)."""
+    """a_t for every (b, h, t) as fp64 [B,H,L] (1 for no decay); [B,H,L,dk] for
+    the per-channel kind."""
+    if decay_kind == DECAY_CHANNEL:
+        return np.exp(_f64(decay))
     if decay_kind == DECAY_NONE:
         return np.ones((B, H, L))
     if decay_kind == DECAY_HEAD:
@@ -265,3 +273,68 @@ def rel_err(x, ref) -> float:
     den = np.max(np.abs(ref)) if ref.size else 0.0
     num = np.max(np.abs(x - ref)) if ref.size else 0.0
     return float(num / den) if den > 0 else float(num)
+
+
+# --------------------------------------------------------------------------
+# the per-channel (GLA) gate: S_t = diag(alpha_t) S_{t-1} + k_t v_t^T
+# (linear/sparse attention tutorial, section 2.4)
+# --------------------------------------------------------------------------
+def parallel_channel(q, k, v, a, phi: int = PHI_IDENTITY, state=None):
+    """Fully parallel form of the per-channel gate with explicit products.
+
+    a: [B,H,L,dk] multipliers.  o_t = sum_{s<=t} sum_d phi(q)_td phi(k)_sd
+    D[t,s,d] v_s + sum_d phi(q)_td (prod_{r<=t} a_rd) S_0[d,:],
+    D[t,s,d] = prod_{r=s+1..t} a_rd; S_L[d,:] = sum_s D[L-1,s,d] phi(k)_sd v_s
+    + prod_r a_rd S_0[d,:].
+    """
+    fq, fk, v, a = feature_map(q, phi), feature_map(k, phi), _f64(v), _f64(a)
+    B, H, L, dk = fq.shape
+    dv = v.shape[-1]
+    S0 = np.zeros((B, H, dk, dv)) if state is None else _f64(state)
+    out = np.zeros((B, H, L, dv))
+    SL = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            D = np.zeros((L, L, dk))
+            for s in range(L):
+                p = np.ones(dk)
+                D[s, s] = 1.0
+                for t in range(s + 1, L):
+                    p = p * a[b, h, t]
+                    D[t, s] = p
+            head = np.cumprod(a[b, h], axis=0)  # [L, dk]
+            scores = np.einsum("td,sd,tsd->ts", fq[b, h], fk[b, h], D)
+            out[b, h] = scores @ v[b, h] + (fq[b, h] * head) @ S0[b, h]
+            if L:
+                SL[b, h] = (fk[b, h] * D[L - 1]).T @ v[b, h] + head[-1][:, None] * S0[b, h]
+            else:
+                SL[b, h] = S0[b, h]
+    return out, SL
+
+
+def chunkwise_channel(q, k, v, log_a, C: int, phi: int = PHI_IDENTITY, state=None):
+    """Chunkwise form of the per-channel gate, per chunk with B = inclusive
+    cumsum of log a inside the chunk (per channel, every factor exp(<= 0)):
+      O_c     = (Q_c o e^{B}) S_c + P V_c,  P[i,j] = [j<=i] sum_d q_id k_jd e^{B_id - B_jd}
+      S_{c+1} = diag(e^{B_last}) S_c + (K_c o e^{B_last - B})^T V_c
+    """
+    fq, fk, v, la = feature_map(q, phi), feature_map(k, phi), _f64(v), _f64(log_a)
+    B_, H, L, dk = fq.shape
+    dv = v.shape[-1]
+    S = np.zeros((B_, H, dk, dv)) if state is None else _f64(state).copy()
+    out = np.zeros((B_, H, L, dv))
+    for b in range(B_):
+        for h in range(H):
+            Sh = S[b, h]
+            for s in range(0, L, C):
+                e = min(s + C, L)
+                Qc, Kc, Vc = fq[b, h, s:e], fk[b, h, s:e], v[b, h, s:e]
+                Bc = np.cumsum(la[b, h, s:e], axis=0)  # [c, dk]
+                diff = Bc[:, None, :] - Bc[None, :, :]  # [c, c, dk]
+                mask = np.tril(np.ones((e - s, e - s), dtype=bool))
+                P = np.einsum("id,jd,ijd->ij", Qc, Kc, np.exp(np.where(mask[..., None], diff, 0.0)))
+                P = np.where(mask, P, 0.0)
+                out[b, h, s:e] = (Qc * np.exp(Bc)) @ Sh + P @ Vc
+                Sh = np.exp(Bc[-1])[:, None] * Sh + (Kc * np.exp(Bc[-1] - Bc)).T @ Vc
+            S[b, h] = Sh
+    return out, S

@@ -37,6 +37,10 @@
  *   1 per head    a_t = gamma[h]                   (data: gamma[H])
  *   2 log decay   a_t = exp(log_a[b,h,t])          (data: log_a[B,H,L])
  *   3 gate        a_t = exp(-softplus(g[b,h,t]))   (data: g[B,H,L])
+ *   4 per channel a_t = diag(exp(log_a[b,h,t,:]))  (data: log_a[B,H,L,dk])
+ *     GLA's data-dependent diagonal gate (the tutorial, section 2.4):
+ *     S_t = diag(alpha_t) S_{t-1} + k_t v_t^T, one factor per key channel
+ *     (row of S), so it scales the previous state row by row.
  */
 #include <math.h>
 #include <pthread.h>
@@ -51,6 +55,7 @@
 #define ORACLE_DECAY_HEAD 1
 #define ORACLE_DECAY_LOG 2
 #define ORACLE_DECAY_GATE 3
+#define ORACLE_DECAY_CHANNEL 4
 
 /* phi(x) = elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) for x <= 0. */
 static double oracle_phi(int phi, double x) {
@@ -77,7 +82,8 @@ static double oracle_decay(int kind, const double* dh, int t) {
 /*
  * One head, L tokens, token by token.
  *   q, k : [L, dk]   v : [L, dv]   out : [L, dv]   S : [dk, dv] (in: S_0, out: S_L)
- *   dh   : decay data of this head (see oracle_decay), may be NULL for kind 0
+ *   dh   : decay data of this head (see oracle_decay), may be NULL for kind 0;
+ *          for kind 4 the head's [L, dk] log_a rows
  *   z    : NULL (un-normalised) or the normaliser [dk] (in: z_0, out: z_L)
  */
 void oracle_recurrent_head(int L, int dk, int dv, const double* q, const double* k,
@@ -94,16 +100,19 @@ void oracle_recurrent_head(int L, int dk, int dv, const double* q, const double*
       fk[i] = oracle_phi(phi, kt[i]);
     }
     const double a = oracle_decay(decay_kind, dh, t);
-    /* write: S = a S + phi(k_t) v_t^T */
-    for (int i = 0; i < dk; ++i)
+    /* write: S = a S + phi(k_t) v_t^T (kind 4: row i decays by exp(log_a[t][i])) */
+    for (int i = 0; i < dk; ++i) {
+      const double ai = decay_kind == ORACLE_DECAY_CHANNEL ? exp(dh[(size_t)t * dk + i]) : a;
       for (int j = 0; j < dv; ++j)
-        S[(size_t)i * dv + j] = a * S[(size_t)i * dv + j] + fk[i] * vt[j];
+        S[(size_t)i * dv + j] = ai * S[(size_t)i * dv + j] + fk[i] * vt[j];
+    }
     /* normaliser: z = a z + phi(k_t), den = phi(q_t)^T z */
     double den = 1.0;
     if (z) {
       den = 0.0;
       for (int i = 0; i < dk; ++i) {
-        z[i] = a * z[i] + fk[i];
+        const double ai = decay_kind == ORACLE_DECAY_CHANNEL ? exp(dh[(size_t)t * dk + i]) : a;
+        z[i] = ai * z[i] + fk[i];
         den += fq[i] * z[i];
       }
     }
@@ -134,6 +143,8 @@ static void* oracle_worker(void* p) {
     if (j->kind == ORACLE_DECAY_HEAD) dh = j->decay + h;
     else if (j->kind == ORACLE_DECAY_LOG || j->kind == ORACLE_DECAY_GATE)
       dh = j->decay + (size_t)bh * j->L;
+    else if (j->kind == ORACLE_DECAY_CHANNEL)
+      dh = j->decay + (size_t)bh * j->L * j->dk;
     oracle_recurrent_head(j->L, j->dk, j->dv, j->q + (size_t)bh * j->L * j->dk,
                           j->k + (size_t)bh * j->L * j->dk, j->v + (size_t)bh * j->L * j->dv,
                           j->phi, j->kind, dh, j->S + (size_t)bh * j->dk * j->dv,
@@ -146,7 +157,7 @@ static void* oracle_worker(void* p) {
 /*
  * All heads of a [B, H, L, d] problem, heads spread over `nthreads` threads.
  *   q, k : [B,H,L,dk]  v : [B,H,L,dv]  out : [B,H,L,dv]  S : [B,H,dk,dv] in/out
- *   decay: NULL | gamma[H] | log_a or g [B,H,L]
+ *   decay: NULL | gamma[H] | log_a or g [B,H,L] | log_a [B,H,L,dk]
  *   Z    : NULL (un-normalised) or the normaliser state [B,H,dk] in/out
  * Returns the number of threads actually used.
  */

@@ -40,6 +40,10 @@ MUTANTS = {
     "normaliser_not_decayed": ("z[i] = a * z[i] + fk[i];", "z[i] = z[i] + fk[i];"),
     "normaliser_of_queries": ("z[i] = a * z[i] + fk[i];", "z[i] = a * z[i] + fq[i];"),
     "denominator_with_keys": ("den += fq[i] * z[i];", "den += fk[i] * z[i];"),
+    "channel_gate_reversed": ("? exp(dh[(size_t)t * dk + i]) : a;",
+                              "? exp(dh[(size_t)t * dk + (dk - 1 - i)]) : a;"),
+    "channel_gate_of_previous_token": ("? exp(dh[(size_t)t * dk + i]) : a;",
+                                       "? exp(dh[(size_t)(t > 0 ? t - 1 : 0) * dk + i]) : a;"),
 }
 
 
@@ -84,6 +88,13 @@ def _battery(lib):
         op, _ = oracle.parallel(q, k, v, a, oracle.PHI_ELU1, normalize=True)
         if oracle.rel_err(o, op) > 1e-12:
             failed.append(f"normalised parallel kind={kind}")
+    # the per-channel gate: recurrent == parallel with explicit per-channel products
+    la = -np.abs(rng.standard_normal((B, H, L, dk))) * 0.5
+    for phi in (oracle.PHI_IDENTITY, oracle.PHI_ELU1):
+        o, S = oracle.recurrent(q, k, v, phi, oracle.DECAY_CHANNEL, la, S0, lib_path=lib)
+        op, Sp = oracle.parallel_channel(q, k, v, np.exp(la), phi, S0)
+        if oracle.rel_err(o, op) > 1e-12 or oracle.rel_err(S, Sp) > 1e-12:
+            failed.append(f"channel gate phi={phi}")
     # phi read out against torch's elu + 1
     x = np.linspace(-4.0, 3.0, 6)
     o, _ = oracle.recurrent(x[None, None, None], np.zeros((1, 1, 1, 6)), np.zeros((1, 1, 1, 6)),

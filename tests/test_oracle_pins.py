@@ -451,3 +451,81 @@ def test_normalised_decode_step_is_one_token():
                                     oracle.DECAY_LOG, dec[:, :, 0], S0, normalize=True,
                                     norm_state=z0)
     assert np.array_equal(o[:, :, 0], od) and np.array_equal(S, Sd) and np.array_equal(Z, Zd)
+
+
+# ---------------------------------------------------------------------------
+# the per-channel (GLA) gate, tutorial section 2.4: S_t = diag(alpha_t) S_{t-1} + k v^T
+# ---------------------------------------------------------------------------
+def _channel_case(seed, L=19, dk=5, dv=3, strength=0.5):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, 2, L, dk))
+    k = rng.standard_normal((1, 2, L, dk))
+    v = rng.standard_normal((1, 2, L, dv))
+    la = -np.abs(rng.standard_normal((1, 2, L, dk))) * strength
+    S0 = rng.standard_normal((1, 2, dk, dv))
+    return q, k, v, la, S0
+
+
+@pytest.mark.parametrize("phi", [oracle.PHI_IDENTITY, oracle.PHI_ELU1])
+def test_channel_gate_recurrent_equals_parallel_and_chunkwise(phi):
+    q, k, v, la, S0 = _channel_case(40 + phi)
+    o, S = oracle.recurrent(q, k, v, phi, oracle.DECAY_CHANNEL, la, S0)
+    op, Sp = oracle.parallel_channel(q, k, v, np.exp(la), phi, S0)
+    assert oracle.rel_err(o, op) < 1e-13 and oracle.rel_err(S, Sp) < 1e-13
+    for C in (1, 4, 7, 19):
+        oc, Sc = oracle.chunkwise_channel(q, k, v, la, C, phi, S0)
+        assert oracle.rel_err(o, oc) < 1e-13 and oracle.rel_err(S, Sc) < 1e-13
+
+
+def test_channel_gate_with_equal_channels_is_the_scalar_gate():
+    # alpha_t the same in every channel: the scalar log-decay recurrence
+    q, k, v, la, S0 = _channel_case(43)
+    la_tok = la[..., 0]
+    la_all = np.repeat(la_tok[..., None], q.shape[-1], axis=-1)
+    o, S = oracle.recurrent(q, k, v, oracle.PHI_IDENTITY, oracle.DECAY_CHANNEL, la_all, S0)
+    os_, Ss = oracle.recurrent(q, k, v, oracle.PHI_IDENTITY, oracle.DECAY_LOG, la_tok, S0)
+    assert oracle.rel_err(o, os_) < 1e-14 and oracle.rel_err(S, Ss) < 1e-14
+
+
+def test_channel_gate_exact_rational_sum():
+    # integer q, k, v and dyadic per-channel gates: the definition in rationals
+    rng = np.random.default_rng(44)
+    L, dk, dv = 6, 3, 2
+    q = rng.integers(-3, 4, (L, dk))
+    k = rng.integers(-3, 4, (L, dk))
+    v = rng.integers(-3, 4, (L, dv))
+    a = rng.choice([Fraction(1, 2), Fraction(3, 4), Fraction(1)], size=(L, dk))
+    S0 = rng.integers(-2, 3, (dk, dv))
+    S = [[Fraction(int(S0[i][j])) for j in range(dv)] for i in range(dk)]
+    ref = []
+    for t in range(L):
+        for i in range(dk):
+            for j in range(dv):
+                S[i][j] = a[t][i] * S[i][j] + int(k[t][i]) * int(v[t][j])
+        ref.append([sum(int(q[t][i]) * S[i][j] for i in range(dk)) for j in range(dv)])
+    la = np.log(np.array([[float(x) for x in row] for row in a]))
+    o, Sg = oracle.recurrent(q[None, None], k[None, None], v[None, None], oracle.PHI_IDENTITY,
+                             oracle.DECAY_CHANNEL, la[None, None], S0[None, None].astype(float))
+    assert np.max(np.abs(o[0, 0] - np.array(ref, dtype=float))) < 1e-12
+    assert np.max(np.abs(Sg[0, 0] - np.array([[float(x) for x in r] for r in S]))) < 1e-12
+
+
+def test_channel_gate_decays_rows_of_the_state():
+    # one channel fully forgotten each step (log a = -inf): that row of S keeps
+    # only the newest write, the other rows accumulate
+    q, k, v, la, S0 = _channel_case(45, L=5, dk=3, dv=2)
+    la[:] = 0.0
+    la[..., 1] = -np.inf
+    _, S = oracle.recurrent(q, k, v, oracle.PHI_IDENTITY, oracle.DECAY_CHANNEL, la, S0)
+    newest = k[:, :, -1, 1, None] * v[:, :, -1, :]
+    assert np.allclose(S[:, :, 1, :], newest, rtol=1e-14, atol=1e-14)
+    acc = S0[:, :, 0, :] + np.einsum("bht,bhtv->bhv", k[..., 0], v)
+    assert np.allclose(S[:, :, 0, :], acc, rtol=1e-13, atol=1e-13)
+
+
+def test_channel_gate_decode_step_is_one_token():
+    q, k, v, la, S0 = _channel_case(46, L=1)
+    o, S = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_CHANNEL, la, S0)
+    od, Sd = oracle.decode_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], oracle.PHI_ELU1,
+                                oracle.DECAY_CHANNEL, la[:, :, 0], S0)
+    assert np.array_equal(o[:, :, 0], od) and np.array_equal(S, Sd)
