@@ -21,8 +21,8 @@ import oracle
 SRC = os.path.join(os.path.dirname(oracle.__file__), "la_oracle.c")
 
 MUTANTS = {
-    "decay_hits_current_write": ("a * S[(size_t)i * dv + j] + fk[i] * vt[j]",
-                                 "a * (S[(size_t)i * dv + j] + fk[i] * vt[j])"),
+    "decay_hits_current_write": ("ai * S[(size_t)i * dv + j] + fk[i] * vt[j]",
+                                 "ai * (S[(size_t)i * dv + j] + fk[i] * vt[j])"),
     "query_written_instead_of_key": ("+ fk[i] * vt[j]", "+ fq[i] * vt[j]"),
     "elu_plus_one_garbled": ("return x > 0.0 ? x + 1.0 : exp(x);",
                              "return x > 0.0 ? x + 1.0 : exp(x) + 1.0;"),
