@@ -37,8 +37,8 @@ MUTANTS = {
     "token_decay_off_by_one": ("case ORACLE_DECAY_LOG: return exp(dh[t]);",
                                "case ORACLE_DECAY_LOG: return exp(dh[t > 0 ? t - 1 : 0]);"),
     "feature_map_on_values": ("+ fk[i] * vt[j];", "+ fk[i] * oracle_phi(phi, vt[j]);"),
-    "normaliser_not_decayed": ("z[i] = a * z[i] + fk[i];", "z[i] = z[i] + fk[i];"),
-    "normaliser_of_queries": ("z[i] = a * z[i] + fk[i];", "z[i] = a * z[i] + fq[i];"),
+    "normaliser_not_decayed": ("z[i] = ai * z[i] + fk[i];", "z[i] = z[i] + fk[i];"),
+    "normaliser_of_queries": ("z[i] = ai * z[i] + fk[i];", "z[i] = ai * z[i] + fq[i];"),
     "denominator_with_keys": ("den += fq[i] * z[i];", "den += fk[i] * z[i];"),
     "channel_gate_reversed": ("? exp(dh[(size_t)t * dk + i]) : a;",
                               "? exp(dh[(size_t)t * dk + (dk - 1 - i)]) : a;"),
