@@ -16,7 +16,7 @@ _LIB_PATH = os.path.join(HERE, "liblinattn.so")
 
 LA_F32, LA_BF16 = 0, 1
 PHI_IDENTITY, PHI_ELU1 = 0, 1
-DECAY_NONE, DECAY_HEAD, DECAY_LOG, DECAY_GATE = 0, 1, 2, 3
+DECAY_NONE, DECAY_HEAD, DECAY_LOG, DECAY_GATE, DECAY_CHANNEL = 0, 1, 2, 3, 4
 KERNEL_AUTO, KERNEL_STRIP, KERNEL_STRIPE, KERNEL_F32 = 0, 1, 2, 3
 
 

@@ -73,18 +73,20 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   // (16x16 MFMA, 4-wave workgroups over 32-column tiles, siblings sharing q
   // and k through L2).  Both measured on MI355X; la_set_plan overrides.
   int tile = 0;
-  // the normalised form runs in the stripe kernel only
-  const bool stripe_auto = norm || (d_v == 128 && d_k >= 64);
-  if (norm || forced_kernel == LA_KERNEL_STRIPE || (forced_kernel == 0 && stripe_auto)) {
+  // the normalised form and the per-channel decay run in the stripe kernel only
+  const bool chan = decay_kind == LA_DECAY_CHANNEL_LOG;
+  const bool stripe_only = norm || chan;
+  const bool stripe_auto = stripe_only || (d_v == 128 && d_k >= 64);
+  if (stripe_only || forced_kernel == LA_KERNEL_STRIPE || (forced_kernel == 0 && stripe_auto)) {
     // two waves per 32-column stripe (each holding half of the keys) where
     // d_k allows, for two waves per SIMD
     auto parts_for = [&](int t) {
       if (forced_groups > 0) return forced_groups;
-      return la::chunk_stripe_supported(d_k, t, 2, C) ? 2 : 1;
+      return la::chunk_stripe_supported(d_k, t, 2, C, chan) ? 2 : 1;
     };
     tile = forced_tile > 0 ? forced_tile : d_v;
     while (tile > d_v) tile /= 2;
-    while (tile >= 32 && !la::chunk_stripe_supported(d_k, tile, parts_for(tile), C)) tile /= 2;
+    while (tile >= 32 && !la::chunk_stripe_supported(d_k, tile, parts_for(tile), C, chan)) tile /= 2;
     if (tile >= 32) {
       p.kernel = LA_KERNEL_STRIPE;
       p.tile = p.tv = tile;
@@ -120,8 +122,8 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   if (p.P > 1) {
     p.ws_S_off = off;
     off += round256((size_t)heads * p.P * d_k * d_v * sizeof(float));
-    p.ws_logA_off = off;
-    off += round256((size_t)heads * p.P * sizeof(float));
+    p.ws_logA_off = off;  // one total per segment, or per segment and key channel
+    off += round256((size_t)heads * p.P * (chan ? d_k : 1) * sizeof(float));
     p.ws_z_off = off;  // the normalised form's per-segment z increments
     off += round256((size_t)heads * p.P * d_k * sizeof(float));
   }
@@ -183,7 +185,7 @@ la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dt
 size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                                     int decay_kind) {
   if (check_chunk_shape(dtype, B, H, L, d_k, d_v, C) != LA_OK || L == 0) return 0;
-  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return 0;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_CHANNEL_LOG) return 0;
   // one size serves both forms: the larger of the two plans' workspaces
   const size_t plain = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind).ws_bytes;
   const size_t normed = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, true).ws_bytes;
@@ -210,10 +212,13 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
   la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
   if (st != LA_OK) return st;
   if (phi != LA_PHI_IDENTITY && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
-  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return LA_ERR_UNSUPPORTED;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_CHANNEL_LOG) return LA_ERR_UNSUPPORTED;
   const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, norm);
-  // bf16 inputs reach the normalised form through the stripe kernel only
-  if (norm && dtype == LA_BF16 && p.kernel != LA_KERNEL_STRIPE) return LA_ERR_UNSUPPORTED;
+  // bf16 inputs reach the normalised form and the per-channel decay through
+  // the stripe kernel only, and not both at once
+  const bool chan = decay_kind == LA_DECAY_CHANNEL_LOG;
+  if ((norm || chan) && dtype == LA_BF16 && p.kernel != LA_KERNEL_STRIPE) return LA_ERR_UNSUPPORTED;
+  if (norm && chan && dtype == LA_BF16) return LA_ERR_UNSUPPORTED;
   if (L == 0) return LA_OK;
   if (!q || !k || !v || !out) return LA_ERR_NULL;
   if (decay_kind != LA_DECAY_NONE && !decay_data) return LA_ERR_NULL;
@@ -284,7 +289,7 @@ la_status decode_impl(const void* q, const void* k, const void* v, int dtype, in
   if (N < 1 || H < 1) return LA_ERR_SHAPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return LA_ERR_UNSUPPORTED;
   if (phi != LA_PHI_IDENTITY && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
-  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return LA_ERR_UNSUPPORTED;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_CHANNEL_LOG) return LA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !state || !out || (norm && !norm_state)) return LA_ERR_NULL;
   if (decay_kind != LA_DECAY_NONE && !decay_data) return LA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||

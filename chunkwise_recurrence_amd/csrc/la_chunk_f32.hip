@@ -10,6 +10,12 @@
 // It serves small fp32 problems such as the 300 x 16 demo.  The normalised
 // form also carries z (z <- e^{b_last} z + sum_j e^{b_last - b_j} phi(k_j)) and
 // divides each output row by e^{b_i} phi(q_i).z + sum_{j<=i} P[i][j].
+//
+// The per-channel gate (the tutorial's section 2.4) makes b a matrix b[t][d]
+// of in-chunk prefix sums per key channel; every e^{b...} factor above then
+// moves inside the sum over d: P[i][j] = sum_d q_id k_jd e^{b_id - b_jd},
+// the inter term is sum_d q_id e^{b_id} S[d][:], and row d of S (entry d of z)
+// decays by e^{b_{last,d}}.
 #include "la_device.h"
 
 namespace la {
@@ -36,7 +42,9 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
   __shared__ float sS[128 * kTileF32];
   __shared__ float sB[kMaxC];
   __shared__ float sZ[128], sDen[kMaxC];
+  __shared__ float sBc[kMaxC * 128];  // per-channel prefixes b[t][d]
   const bool norm = a.norm != 0;
+  const bool chan = kind == kDecayChannel;
 
   const float* qh = static_cast<const float*>(a.q) + (size_t)bh * L * DK;
   const float* kh = static_cast<const float*>(a.k) + (size_t)bh * L * DK;
@@ -44,6 +52,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
   float* oh = static_cast<float*>(a.out) + (size_t)bh * L * DV + dv0;
   const float* dtok = (kind == kDecayLog || kind == kDecayGate) ? a.decay + (size_t)bh * L : nullptr;
   const float lg = (kind == kDecayHead) ? logf(a.decay[h]) : 0.0f;
+  const float* dch = chan ? a.decay + (size_t)bh * L * DK : nullptr;
 
   for (int i = tid; i < DK * tv; i += 256) {
     const int d = i / tv, v = i % tv;
@@ -63,6 +72,13 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
         sB[i] = b;
       }
     }
+    if (chan && tid < DK) {
+      float b = 0.0f;
+      for (int i = 0; i < n; ++i) {
+        b += dch[(size_t)(t0 + i) * DK + tid];
+        sBc[i * DK + tid] = b;
+      }
+    }
     __syncthreads();
     const float bL = sB[n - 1];
     // decayed scores P[i][j] = (phi(q_i).phi(k_j)) e^{b_i - b_j}, j <= i
@@ -72,8 +88,14 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
       if (j <= i) {
         const float* qi = qh + (size_t)(t0 + i) * DK;
         const float* kj = kh + (size_t)(t0 + j) * DK;
-        for (int d = 0; d < DK; ++d) p = fmaf(phi_f32(elu, qi[d]), phi_f32(elu, kj[d]), p);
-        p *= expf(sB[i] - sB[j]);
+        if (chan) {
+          for (int d = 0; d < DK; ++d)
+            p = fmaf(phi_f32(elu, qi[d]) * expf(sBc[i * DK + d] - sBc[j * DK + d]),
+                     phi_f32(elu, kj[d]), p);
+        } else {
+          for (int d = 0; d < DK; ++d) p = fmaf(phi_f32(elu, qi[d]), phi_f32(elu, kj[d]), p);
+          p *= expf(sB[i] - sB[j]);
+        }
       }
       sP[i * kMaxC + j] = p;
     }
@@ -83,9 +105,15 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
       for (int i = tid; i < n; i += 256) {
         const float* qi = qh + (size_t)(t0 + i) * DK;
         float dz = 0.0f, ds = 0.0f;
-        for (int d = 0; d < DK; ++d) dz = fmaf(phi_f32(elu, qi[d]), sZ[d], dz);
+        if (chan) {
+          for (int d = 0; d < DK; ++d)
+            dz = fmaf(phi_f32(elu, qi[d]) * expf(sBc[i * DK + d]), sZ[d], dz);
+        } else {
+          for (int d = 0; d < DK; ++d) dz = fmaf(phi_f32(elu, qi[d]), sZ[d], dz);
+          dz *= expf(sB[i]);
+        }
         for (int j = 0; j <= i; ++j) ds += sP[i * kMaxC + j];
-        sDen[i] = expf(sB[i]) * dz + ds;
+        sDen[i] = dz + ds;
       }
       __syncthreads();
     }
@@ -94,28 +122,40 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
       const int i = idx / tv, v = idx % tv;
       const float* qi = qh + (size_t)(t0 + i) * DK;
       float inter = 0.0f;
-      for (int d = 0; d < DK; ++d) inter = fmaf(phi_f32(elu, qi[d]), sS[d * tv + v], inter);
+      if (chan) {
+        for (int d = 0; d < DK; ++d)
+          inter = fmaf(phi_f32(elu, qi[d]) * expf(sBc[i * DK + d]), sS[d * tv + v], inter);
+      } else {
+        for (int d = 0; d < DK; ++d) inter = fmaf(phi_f32(elu, qi[d]), sS[d * tv + v], inter);
+        inter *= expf(sB[i]);
+      }
       float intra = 0.0f;
       for (int j = 0; j <= i; ++j) intra = fmaf(sP[i * kMaxC + j], vh[(size_t)(t0 + j) * DV + v], intra);
-      const float o = expf(sB[i]) * inter + intra;
+      const float o = inter + intra;
       oh[(size_t)(t0 + i) * DV + v] = norm ? o / sDen[i] : o;
     }
     __syncthreads();
     // S <- e^{b_last} S + sum_j e^{b_last - b_j} phi(k_j) v_j^T
     for (int idx = tid; idx < DK * tv; idx += 256) {
       const int d = idx / tv, v = idx % tv;
+      const float bLd = chan ? sBc[(n - 1) * DK + d] : bL;
       float acc = 0.0f;
-      for (int j = 0; j < n; ++j)
-        acc = fmaf(expf(bL - sB[j]) * phi_f32(elu, kh[(size_t)(t0 + j) * DK + d]),
+      for (int j = 0; j < n; ++j) {
+        const float bj = chan ? sBc[j * DK + d] : sB[j];
+        acc = fmaf(expf(bLd - bj) * phi_f32(elu, kh[(size_t)(t0 + j) * DK + d]),
                    vh[(size_t)(t0 + j) * DV + v], acc);
-      sS[idx] = expf(bL) * sS[idx] + acc;
+      }
+      sS[idx] = expf(bLd) * sS[idx] + acc;
     }
     if (norm) {
       for (int d = tid; d < DK; d += 256) {
+        const float bLd = chan ? sBc[(n - 1) * DK + d] : bL;
         float acc = 0.0f;
-        for (int j = 0; j < n; ++j)
-          acc = fmaf(expf(bL - sB[j]), phi_f32(elu, kh[(size_t)(t0 + j) * DK + d]), acc);
-        sZ[d] = expf(bL) * sZ[d] + acc;
+        for (int j = 0; j < n; ++j) {
+          const float bj = chan ? sBc[j * DK + d] : sB[j];
+          acc = fmaf(expf(bLd - bj), phi_f32(elu, kh[(size_t)(t0 + j) * DK + d]), acc);
+        }
+        sZ[d] = expf(bLd) * sZ[d] + acc;
       }
     }
   }

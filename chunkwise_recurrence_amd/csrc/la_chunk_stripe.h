@@ -47,12 +47,30 @@
 // made); z itself is updated by the waves of stripe 0 from the K^T operands
 // and token weights of the state update.
 //
+// The per-channel decay (CAT kCatChannel; GLA's diagonal gate, the tutorial's
+// section 2.4: S_t = diag(a_t) S_{t-1} + k_t v_t^T with a_t a vector over the
+// key channels) no longer factors out of the contraction over keys:
+// P[i][j] = sum_d q_id k_jd e^{b_id - b_jd}, with b[t][d] the in-chunk prefix
+// of log a per channel.  The factor is split around r_d = b_{last,d} / 2,
+//
+//   q~_id = q_id e^{b_id - r_d},   k~_jd = k_jd e^{r_d - b_jd}
+//
+// (each exponent within half the chunk's total decay, so both stay in fp32
+// range), which turns the scores into q~ k~^T, the inter-chunk term into
+// q~ (diag(e^r) S) and the update into
+// S' = diag(e^{b_last - r}) (diag(e^r) S + k~^T V).  The prefix runs over
+// log a loaded straight into registers (each thread scans a run of tokens for
+// two channels, the runs combine through LDS), and q~, k~ replace q, k in
+// their LDS tiles, so everything after is the kernel's usual MFMA work.
+//
 // STATE_ONLY computes a segment's state increment and total log2 decay from a
 // zero state (the first pass of the segment split).  It walks the segment's
 // chunks last to first, weighting token t by e^{B_end - B_t} directly (the sum
 // does not depend on the order), so the chunks it reads last -- the starts of
 // the segments -- are the ones the output pass reads first, while they may
-// still sit in the memory-side cache.  The main pass composes
+// still sit in the memory-side cache.  (With the per-channel decay it walks
+// forward and applies the main pass's update, whose factors stay bounded.)
+// The main pass composes
 // the exclusive prefix of the (decay, state) pairs in its prologue, the
 // parallel / associative scan idea of the tutorial's section 3.3.
 #pragma once
@@ -74,8 +92,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr size_t kMaxLds = 160 * 1024;
 
 // SO: the state-only pass, which stages no Q tile and needs no P~, partial
-// exchange or output staging (so it can prefetch deeper).
-template <int DK, int NWV, int KH, int C, bool SO = false>
+// exchange or output staging (so it can prefetch deeper).  CH: the
+// per-channel decay, whose log a tile goes to registers (TPR tokens of two
+// channels per thread) instead of per-wave token weights to LDS.
+template <int DK, int NWV, int KH, int C, bool SO = false, bool CH = false>
 struct Geo {
   static constexpr int NW = NWV * KH;           // waves of the workgroup
   static constexpr int TVW = 32 * NWV;          // value columns of the workgroup
@@ -97,8 +117,12 @@ struct Geo {
   static constexpr int V_BLK = V_BYTES / 1024;
   static constexpr int QK_PER = (QK_BLK + NW - 1) / NW;  // per wave
   static constexpr int V_PER = (V_BLK + NW - 1) / NW;
+  // per-channel decay: the workgroup's threads split into RUNS runs of TPR
+  // consecutive tokens, each thread taking two key channels of its run
+  static constexpr int RUNS = 128 * NW / DK;
+  static constexpr int TPR = RUNS > 0 && C % RUNS == 0 ? C / RUNS : 0;
   // vector memory instructions of one chunk per wave (at most)
-  static constexpr int LOADS_MAX = (SO ? 1 : 2) * QK_PER + V_PER + 1;
+  static constexpr int LOADS_MAX = (SO ? 1 : 2) * QK_PER + V_PER + (CH ? TPR : 1);
   static constexpr int STORES = SO ? 0 : 2 * RBW;
   // every wave issues the same memory instructions per chunk and their count
   // fits the 6-bit vmcnt, so the wait at the top of a chunk can count them
@@ -108,12 +132,18 @@ struct Geo {
   // the normalised form's z, denominator partials and row sums (counted for
   // every instance, so both forms run the same pipeline depth)
   static constexpr size_t NORM_BYTES = 2 * 4 * (size_t)DK + 4 * (size_t)C * (KH + NRB);
+  // per-wave token weights, or (per-channel decay) the run totals and the
+  // per-channel factors e^r, e^{b_last - r}
+  static constexpr size_t W_BYTES = CH ? 4 * (size_t)RUNS * DK + 2 * 4 * (size_t)DK
+                                       : 2 * 4 * (size_t)NW * C;
   static constexpr size_t stage_bytes(int n) {
     return SO ? (size_t)n * ((size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
-                    2 * 4 * (size_t)NW * C + NORM_BYTES + 256
+                    W_BYTES + NORM_BYTES + 256
               : (size_t)n * (2 * (size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
-                    2 * (size_t)C * C + 2 * 4 * (size_t)NW * C + XCH_BYTES + 2048 * (size_t)NW  + NORM_BYTES + 256;
+                    2 * (size_t)C * C + W_BYTES + XCH_BYTES + 2048 * (size_t)NW  + NORM_BYTES + 256;
   }
+  // the per-channel decay's prefetch registers stay bounded (TPR <= 16)
+  static constexpr bool CH_OK = !CH || (TPR >= 1 && TPR <= 16 && DK >= 32);
   static constexpr int NSTG =
       (UNIFORM && stage_bytes(3) <= kMaxLds && 2 * STORES + LOADS_MAX < 64) ? 3 : 2;
   static constexpr size_t LDS = stage_bytes(NSTG);
@@ -216,7 +246,7 @@ __device__ __forceinline__ void lds_wave_sync() {
   asm volatile("" ::: "memory");
 }
 
-enum { kCatNone = 0, kCatHead = 1, kCatToken = 2 };
+enum { kCatNone = 0, kCatHead = 1, kCatToken = 2, kCatChannel = 3 };
 
 // (I, J) of causal score block b in the order (0,0), (1,0), (1,1), (2,0), ...
 __host__ __device__ constexpr int block_i(int b) {
@@ -228,7 +258,10 @@ __host__ __device__ constexpr int block_j(int b) { return b - block_i(b) * (bloc
 
 template <int DK, int NWV, int KH, int C, int CAT, bool STATE_ONLY, bool NORM>
 __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const ChunkArgs a) {
-  using G = Geo<DK, NWV, KH, C, STATE_ONLY>;
+  constexpr bool CHN = CAT == kCatChannel;
+  static_assert(!(CHN && NORM), "the normalised form takes no per-channel decay");
+  using G = Geo<DK, NWV, KH, C, STATE_ONLY, CHN>;
+  static_assert(G::CH_OK, "per-channel decay layout");
   constexpr int NS = G::NSTG;
   constexpr int NW = G::NW;
   const int tid = threadIdx.x;
@@ -269,7 +302,11 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   // [stripe][row block][16-byte chunk k][lane]
   __shared__ __align__(16) char sX[(STATE_ONLY || KH == 1) ? 16 : G::XCH_BYTES];
   // per-wave weights of the current chunk: [0] e^{b_last - b_t}, [1] e^{b_t}
-  __shared__ __align__(16) float sW[NW][2][C];
+  __shared__ __align__(16) float sW[CHN ? 1 : NW][2][CHN ? 4 : C];
+  // per-channel decay: log2-decay totals of each run, then e^r and
+  // e^{b_last - r} per key channel
+  __shared__ __align__(16) float sTot[CHN ? G::RUNS : 1][CHN ? DK : 4];
+  __shared__ __align__(16) float sER[CHN ? DK : 4], sEL[CHN ? DK : 4];
   // normalised form: z (double-buffered by chunk parity), the denominators'
   // inter-chunk partials per key part and the score row sums per key block
   __shared__ __align__(16) float sZ[NORM ? 2 : 1][NORM ? DK : 4];
@@ -303,14 +340,17 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   uint16_t* oh = static_cast<uint16_t*>(a.out) + head_v + dv0 + cw;
   const float* bws = CAT == kCatToken ? a.ws_b + (size_t)bh * L : nullptr;
   const float lg2 = CAT == kCatHead ? log2f(a.decay[hd]) : 0.0f;  // b_i = (i + 1) lg2
-  float* wq = sW[wave][0];
-  float* eq = sW[wave][1];
+  float* wq = sW[CHN ? 0 : wave][0];
+  float* eq = sW[CHN ? 0 : wave][1];
+  // per-channel decay: this thread's run of tokens and pair of key channels
+  const float* dch = CHN ? a.decay + (size_t)bh * L * DK : nullptr;
+  const int pr = tid % (DK / 2), run = tid / (DK / 2);
 
   // ---- loop-invariant mask/decay weights of this wave's score blocks ------
   // block (I, J), register r: query row i = 32 I + l32, token
   // j = 32 J + 8 (r / 4) + 4 h + r % 4; weight [j <= i] gamma^(i - j).
-  float dm[CAT == kCatToken ? 1 : G::BPW][16];
-  if constexpr (CAT != kCatToken && !STATE_ONLY) {
+  float dm[(CAT == kCatToken || CHN) ? 1 : G::BPW][16];
+  if constexpr (CAT != kCatToken && !CHN && !STATE_ONLY) {
 #pragma unroll
     for (int bb = 0; bb < G::BPW; ++bb) {
       const int b = wave + NW * bb;
@@ -342,7 +382,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         float sv = a.state ? a.state[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
         for (int p = 0; p < sigma; ++p) {
           const size_t seg = (size_t)bh * a.P + p;
-          sv = exp2f(a.ws_logA[seg]) * sv + a.ws_S[(seg * DK + dk) * DV + dv];
+          const float la2 = CHN ? a.ws_logA[seg * DK + dk] : a.ws_logA[seg];
+          sv = exp2f(la2) * sv + a.ws_S[(seg * DK + dk) * DV + dv];
         }
         accS[t][r] = sv;
       }
@@ -398,13 +439,18 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     vrow[i] = r;
     voff[i] = r * DV + 8 * cc;
   }
-  constexpr int LOADS = (STATE_ONLY ? 1 : 2) * G::QK_PER + G::V_PER + (CAT == kCatToken ? 1 : 0);
+  constexpr int LOADS = (STATE_ONLY ? 1 : 2) * G::QK_PER + G::V_PER + (CAT == kCatToken ? 1 : 0) +
+                        (CHN ? G::TPR : 0);
   constexpr int STORES = STATE_ONLY ? 0 : G::STORES;
 
   // iteration it handles chunk chunk_of(it): forward in the output pass,
-  // backward in the state pass
+  // backward in the state pass (forward with the per-channel decay)
   const int n_it = c_end - c_begin;
-  auto chunk_of = [&](int it) { return STATE_ONLY ? c_end - 1 - it : c_begin + it; };
+  auto chunk_of = [&](int it) { return (STATE_ONLY && !CHN) ? c_end - 1 - it : c_begin + it; };
+
+  // per-channel decay: log a of this thread's tokens and channels, per stage
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 lreg[CHN ? NS : 1][CHN ? G::TPR : 1];
 
   auto issue_loads = [&](auto BUF, int it) {
     const int c = chunk_of(it);
@@ -439,9 +485,19 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         dma4(bws + t, stage_b(BUF) + wave * PER);
       }
     }
+    if constexpr (CHN) {
+      // rows past the sequence re-read its last row; they are zeroed before use
+      constexpr int buf = decltype(BUF)::value;
+#pragma unroll
+      for (int i = 0; i < G::TPR; ++i) {
+        const int t = min(t0 + run * G::TPR + i, L - 1);
+        lreg[buf][i] = *reinterpret_cast<const f32x2*>(dch + (size_t)t * DK + 2 * pr);
+      }
+    }
   };
 
   float logA = 0.0f;
+  f32x2 logA2 = f32x2{0.0f, 0.0f};  // per-channel decay: totals of channels 2 pr, 2 pr + 1
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
   auto body = [&](auto BUF, int it) {
@@ -485,8 +541,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         *reinterpret_cast<u32x4*>(vb + 16 * (nvalid * G::WCV + q)) = zero4;
       lds_barrier();
     }
-    // feature map on the staged queries and keys, in place
-    if (elu) {
+    // feature map on the staged queries and keys, in place (the per-channel
+    // decay applies it in its rescaling pass below)
+    if (elu && !CHN) {
       for (int q = tid; q < G::QK_BYTES / 16; q += 64 * NW) {
         u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
         *p = elu1_x8(*p);
@@ -498,6 +555,74 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       lds_barrier();
     }
 
+    if constexpr (CHN) {
+      // in-chunk prefix of log2 a over this thread's run (tokens past the
+      // sequence contribute nothing), then the runs' totals through LDS
+      constexpr float kLog2e = 1.4426950408889634f;
+      f32x2 bl[G::TPR];
+      f32x2 accb = f32x2{0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < G::TPR; ++i) {
+        const f32x2 x = lreg[buf][i] * kLog2e;
+        accb += run * G::TPR + i < nvalid ? x : f32x2{0.0f, 0.0f};
+        bl[i] = accb;
+      }
+      *reinterpret_cast<f32x2*>(&sTot[run][2 * pr]) = accb;
+      lds_barrier();
+      f32x2 off = f32x2{0.0f, 0.0f}, tot = f32x2{0.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < G::RUNS; ++r) {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(&sTot[r][2 * pr]);
+        off += r < run ? x : f32x2{0.0f, 0.0f};
+        tot += x;
+      }
+      const f32x2 rr = tot * 0.5f;  // r = b_last / 2
+      // q~ = phi(q) e^{b - r}, k~ = phi(k) e^{r - b}, in place
+#pragma unroll
+      for (int i = 0; i < G::TPR; ++i) {
+        const f32x2 b = off + bl[i];
+        const int o = swz<G::WCK>(run * G::TPR + i, 2 * pr);
+        uint32_t* kp = reinterpret_cast<uint32_t*>(kb + o);
+        const uint32_t kw = *kp;
+        float k0 = bf16_to_f32(kw & 0xffffu), k1 = bf16_to_f32(kw >> 16);
+        if (elu) {
+          k0 = feature_elu1(k0);
+          k1 = feature_elu1(k1);
+        }
+        *kp = cvt2(k0 * __builtin_amdgcn_exp2f(rr[0] - b[0]), k1 * __builtin_amdgcn_exp2f(rr[1] - b[1]));
+        if constexpr (!STATE_ONLY) {
+          uint32_t* qp = reinterpret_cast<uint32_t*>(qb + o);
+          const uint32_t qw = *qp;
+          float q0 = bf16_to_f32(qw & 0xffffu), q1 = bf16_to_f32(qw >> 16);
+          if (elu) {
+            q0 = feature_elu1(q0);
+            q1 = feature_elu1(q1);
+          }
+          *qp = cvt2(q0 * __builtin_amdgcn_exp2f(b[0] - rr[0]), q1 * __builtin_amdgcn_exp2f(b[1] - rr[1]));
+        }
+      }
+      if (run == 0) {
+        *reinterpret_cast<f32x2*>(&sER[2 * pr]) =
+            f32x2{__builtin_amdgcn_exp2f(rr[0]), __builtin_amdgcn_exp2f(rr[1])};
+        *reinterpret_cast<f32x2*>(&sEL[2 * pr]) =
+            f32x2{__builtin_amdgcn_exp2f(tot[0] - rr[0]), __builtin_amdgcn_exp2f(tot[1] - rr[1])};
+      }
+      logA2 += tot;
+      lds_barrier();
+    }
+    // rows of this wave's state tiles scaled by a per-channel factor from LDS
+    // (register r of own tile t holds key 32 (mk0 + t) + 8 (r / 4) + 4 h + r % 4)
+    auto scale_rows = [&](const float* f) {
+#pragma unroll
+      for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&f[32 * (mk0 + t) + 8 * q + 4 * h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) accS[t][4 * q + e] *= x[e];
+        }
+    };
+
     // log2 decay of the chunk's last real token
     float bL = 0.0f;
     if constexpr (CAT == kCatHead) bL = (float)nvalid * lg2;
@@ -506,7 +631,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     // per-token weights of this wave: e^{b_last - b_t} (update; 0 past the
     // chunk) and e^{b_t} (inter-chunk term), t = lane (+ 64).  The state pass
     // folds in the decay of the chunks after this one (logA so far).
-    if constexpr (CAT != kCatNone) {
+    if constexpr (CAT != kCatNone && !CHN) {
       const float wofs = STATE_ONLY ? logA + bL : bL;
 #pragma unroll
       for (int t = lane; t < C; t += 64) {
@@ -541,7 +666,12 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
             pacc = mfma32(kA, qB, pacc);
           }
           // register r: token j = 32 J + 8 (r / 4) + 4 h + r % 4, row i = 32 I + l32
-          if constexpr (CAT == kCatToken) {
+          if constexpr (CHN) {
+            // the decay is inside q~ and k~: causal mask only
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              pacc[r] = (I != J || 8 * (r >> 2) + 4 * h + (r & 3) <= l32) ? pacc[r] : 0.0f;
+          } else if constexpr (CAT == kCatToken) {
             const float bi = sb[32 * I + l32];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -577,6 +707,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 
       // (1b) inter-chunk term over this wave's keys, every row block:
       //      part[I] = S_part^T Q_part^T (transposed: lane = row, registers = values)
+      // (per-channel decay: of diag(e^r) S against q~; the scaled state then
+      // carries on into the update)
+      if constexpr (CHN) scale_rows(sER);
       pack_state();
       // normalised form, stripe 0: z of this wave's keys as the first row of
       // an A operand (every other row zero), in the key order of sbf
@@ -648,7 +781,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         }
         const int i = 32 * I + l32;
         float er = 1.0f;
-        if constexpr (CAT != kCatNone) {
+        if constexpr (CAT != kCatNone && !CHN) {
           er = eq[i];
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] *= er;
@@ -696,7 +829,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 
     // (3) state update of this wave's tiles: S <- e^{b_last} S + K^T diag(e^{b_last - b}) V
     // (state pass: S <- S + K^T diag(e^{B_end - B}) V)
-    if constexpr (CAT != kCatNone && !STATE_ONLY) {
+    // (per-channel decay: S <- diag(e^{b_last - r}) (diag(e^r) S + k~^T V))
+    if constexpr (CHN && STATE_ONLY) scale_rows(sER);
+    if constexpr (CAT != kCatNone && !CHN && !STATE_ONLY) {
       const float eL = __builtin_amdgcn_exp2f(bL);
 #pragma unroll
       for (int t = 0; t < G::NMK_OWN; ++t)
@@ -717,7 +852,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
         for (int e = 0; e < 8; ++e) w[e] = 16 * ks + 8 * h + e < nvalid ? 1.0f : 0.0f;
       }
-      if constexpr (CAT != kCatNone) {
+      if constexpr (CAT != kCatNone && !CHN) {
         const int tb = 16 * ks + 8 * h;
         const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wq[tb]);
         const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wq[tb + 4]);
@@ -745,6 +880,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         }
       }
     }
+    if constexpr (CHN) scale_rows(sEL);
     if constexpr (NORM) {
       if (stripe == 0) {
         const float eLz = (CAT != kCatNone && !STATE_ONLY) ? __builtin_amdgcn_exp2f(bL) : 1.0f;
@@ -781,7 +917,12 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   float* dst = nullptr;
   if constexpr (STATE_ONLY) {
     dst = a.ws_S + ((size_t)bh * a.P + sigma) * DK * DV;
-    if (vt == 0 && tid == 0) a.ws_logA[(size_t)bh * a.P + sigma] = logA;
+    if constexpr (CHN) {
+      if (vt == 0 && run == 0)
+        *reinterpret_cast<f32x2*>(&a.ws_logA[((size_t)bh * a.P + sigma) * DK + 2 * pr]) = logA2;
+    } else {
+      if (vt == 0 && tid == 0) a.ws_logA[(size_t)bh * a.P + sigma] = logA;
+    }
   } else {
     if (sigma == a.P - 1 && a.state != nullptr) dst = a.state + (size_t)bh * DK * DV;
   }
@@ -809,7 +950,13 @@ template <int DK, int NWV, int KH, int C, int CAT>
 hipError_t launch_one(const ChunkArgs& a, bool state_only, hipStream_t s) {
   const int groups = (a.n_units + 7) / 8;
   const dim3 grid(groups * 8 * a.n_v), block(64 * NWV * KH);
-  if (a.norm) {
+  if constexpr (CAT == kCatChannel) {
+    if (a.norm) return hipErrorInvalidValue;
+    if (state_only)
+      hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, true, false>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, false, false>), grid, block, 0, s, a);
+  } else if (a.norm) {
     if (state_only)
       hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, true, true>), grid, block, 0, s, a);
     else
@@ -823,17 +970,23 @@ hipError_t launch_one(const ChunkArgs& a, bool state_only, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DK, int NWV, int KH, int C, int CAT>
+constexpr bool fits() {
+  using G = Geo<DK, NWV, KH, C, false, CAT == kCatChannel>;
+  return G::LDS <= kMaxLds && G::CH_OK;
+}
+
 template <int DK, int NWV, int KH, int CAT>
 hipError_t dispatch_c(const ChunkArgs& a, bool so, hipStream_t s) {
   switch (a.C) {
     case 32:
-      if constexpr (Geo<DK, NWV, KH, 32>::LDS <= kMaxLds) return launch_one<DK, NWV, KH, 32, CAT>(a, so, s);
+      if constexpr (fits<DK, NWV, KH, 32, CAT>()) return launch_one<DK, NWV, KH, 32, CAT>(a, so, s);
       return hipErrorInvalidValue;
     case 64:
-      if constexpr (Geo<DK, NWV, KH, 64>::LDS <= kMaxLds) return launch_one<DK, NWV, KH, 64, CAT>(a, so, s);
+      if constexpr (fits<DK, NWV, KH, 64, CAT>()) return launch_one<DK, NWV, KH, 64, CAT>(a, so, s);
       return hipErrorInvalidValue;
     case 128:
-      if constexpr (Geo<DK, NWV, KH, 128>::LDS <= kMaxLds) return launch_one<DK, NWV, KH, 128, CAT>(a, so, s);
+      if constexpr (fits<DK, NWV, KH, 128, CAT>()) return launch_one<DK, NWV, KH, 128, CAT>(a, so, s);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
@@ -862,17 +1015,23 @@ hipError_t dispatch_w(const ChunkArgs& a, bool so, hipStream_t s) {
 }
 
 template <int DK, int NWV, int KH>
-constexpr size_t lds_c(int C) {
-  return C == 32 ? Geo<DK, NWV, KH, 32>::LDS
-                 : C == 64 ? Geo<DK, NWV, KH, 64>::LDS : Geo<DK, NWV, KH, 128>::LDS;
+constexpr bool fits_c(int C, bool ch) {
+  if (ch)
+    return C == 32 ? fits<DK, NWV, KH, 32, kCatChannel>()
+                   : C == 64 ? fits<DK, NWV, KH, 64, kCatChannel>() : fits<DK, NWV, KH, 128, kCatChannel>();
+  return C == 32 ? fits<DK, NWV, KH, 32, kCatToken>()
+                 : C == 64 ? fits<DK, NWV, KH, 64, kCatToken>() : fits<DK, NWV, KH, 128, kCatToken>();
 }
+// Whether the layout (TVW value columns, KH key parts, chunk C) fits: the
+// per-token category stands for the three factorised ones (they share one
+// LDS plan), the per-channel one has its own.
 template <int DK>
-constexpr size_t lds_of(int TVW, int KH, int C) {
+constexpr bool fits_of(int TVW, int KH, int C, bool ch) {
   if constexpr (DK >= 64) {
     if (KH == 2)
-      return TVW == 32 ? lds_c<DK, 1, 2>(C) : TVW == 64 ? lds_c<DK, 2, 2>(C) : lds_c<DK, 4, 2>(C);
+      return TVW == 32 ? fits_c<DK, 1, 2>(C, ch) : TVW == 64 ? fits_c<DK, 2, 2>(C, ch) : fits_c<DK, 4, 2>(C, ch);
   }
-  return TVW == 32 ? lds_c<DK, 1, 1>(C) : TVW == 64 ? lds_c<DK, 2, 1>(C) : lds_c<DK, 4, 1>(C);
+  return TVW == 32 ? fits_c<DK, 1, 1>(C, ch) : TVW == 64 ? fits_c<DK, 2, 1>(C, ch) : fits_c<DK, 4, 1>(C, ch);
 }
 
 }  // namespace stripe
@@ -880,9 +1039,9 @@ constexpr size_t lds_of(int TVW, int KH, int C) {
 // One per (key dimension, decay category), each in its own translation unit.
 #define LA_STRIPE_DECL(DK, CAT) \
   hipError_t launch_chunk_stripe_dk##DK##_c##CAT(const ChunkArgs& a, bool state_only, hipStream_t s);
-LA_STRIPE_DECL(32, 0) LA_STRIPE_DECL(32, 1) LA_STRIPE_DECL(32, 2)
-LA_STRIPE_DECL(64, 0) LA_STRIPE_DECL(64, 1) LA_STRIPE_DECL(64, 2)
-LA_STRIPE_DECL(128, 0) LA_STRIPE_DECL(128, 1) LA_STRIPE_DECL(128, 2)
+LA_STRIPE_DECL(32, 0) LA_STRIPE_DECL(32, 1) LA_STRIPE_DECL(32, 2) LA_STRIPE_DECL(32, 3)
+LA_STRIPE_DECL(64, 0) LA_STRIPE_DECL(64, 1) LA_STRIPE_DECL(64, 2) LA_STRIPE_DECL(64, 3)
+LA_STRIPE_DECL(128, 0) LA_STRIPE_DECL(128, 1) LA_STRIPE_DECL(128, 2) LA_STRIPE_DECL(128, 3)
 #undef LA_STRIPE_DECL
 
 }  // namespace la

@@ -7,7 +7,9 @@
 //   S' = a S + phi(k) v^T,   o = phi(q)^T S'
 //
 // The normalised form also updates z' = a z + phi(k) and divides o by
-// phi(q)^T z' (the tutorial's section 2.2, boxed recurrence).
+// phi(q)^T z' (the tutorial's section 2.2, boxed recurrence).  With the
+// per-channel gate (the tutorial's section 2.4) a is a vector over the key
+// channels: row i of S and entry i of z decay by a_i.
 //
 // The step is a pure stream over the fp32 state: every element is read once,
 // updated and written once, and o is reduced on the way.  One workgroup of 256
@@ -65,12 +67,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   if (a.decay_kind == kDecayHead) decay = a.decay[h];
   else if (a.decay_kind == kDecayLog || a.decay_kind == kDecayGate)
     decay = expf(token_log_decay(a.decay_kind, a.decay[bh]));
+  const bool chan = a.decay_kind == kDecayChannel;
+  __shared__ float sdec[DK];
+  if (tid < DK) sdec[tid] = chan ? expf(a.decay[(size_t)bh * DK + tid]) : decay;
   __shared__ float sden[DK];
   if (a.zstate != nullptr) {
     __syncthreads();
     if (tid < DK) {
       float* zp = a.zstate + (size_t)bh * DK + tid;
-      const float z = fmaf(decay, *zp, sk[tid]);
+      const float z = fmaf(sdec[tid], *zp, sk[tid]);
       *zp = z;
       sden[tid] = sq[tid] * z;
     }
@@ -84,11 +89,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     const int r = rg + p * RP;
     if (r < DK) {
       const float kr = sk[r], qr = sq[r];
+      const float dr = chan ? sdec[r] : decay;
       f32x4 s = sreg[p];
-      s.x = fmaf(decay, s.x, kr * vv.x);
-      s.y = fmaf(decay, s.y, kr * vv.y);
-      s.z = fmaf(decay, s.z, kr * vv.z);
-      s.w = fmaf(decay, s.w, kr * vv.w);
+      s.x = fmaf(dr, s.x, kr * vv.x);
+      s.y = fmaf(dr, s.y, kr * vv.y);
+      s.z = fmaf(dr, s.z, kr * vv.z);
+      s.w = fmaf(dr, s.w, kr * vv.w);
       __builtin_nontemporal_store(s, &S[r * TPR + c4]);
       o.x = fmaf(qr, s.x, o.x);
       o.y = fmaf(qr, s.y, o.y);

@@ -10,7 +10,7 @@ namespace la {
 // Public enum values, mirrored for device code.
 enum { kF32 = 0, kBF16 = 1 };
 enum { kPhiIdentity = 0, kPhiElu1 = 1 };
-enum { kDecayNone = 0, kDecayHead = 1, kDecayLog = 2, kDecayGate = 3 };
+enum { kDecayNone = 0, kDecayHead = 1, kDecayLog = 2, kDecayGate = 3, kDecayChannel = 4 };
 
 // One la_chunk_fwd launch (main pass or segment-state pass).
 struct ChunkArgs {
@@ -19,9 +19,9 @@ struct ChunkArgs {
   const void* v;        // [B,H,L,DV]
   void* out;            // [B,H,L,DV]
   float* state;         // [B,H,DK,DV] or nullptr
-  const float* decay;   // nullptr | gamma[H] | [B,H,L]
+  const float* decay;   // nullptr | gamma[H] | [B,H,L] | [B,H,L,DK] (per channel)
   float* ws_S;          // [B*H, P, DK, DV] per-segment state increments
-  float* ws_logA;       // [B*H, P] per-segment total log decay
+  float* ws_logA;       // [B*H, P] per-segment total log2 decay ([B*H, P, DK] per channel)
   float* ws_b;          // [B*H, L] in-chunk inclusive prefix of log a (token decays)
   float* zstate;        // normalised form: [B,H,DK] z in/out, or nullptr
   float* ws_z;          // normalised form: [B*H, P, DK] per-segment z increments
@@ -44,7 +44,7 @@ struct DecodeArgs {
   void* out;            // [N,H,DV]
   float* state;         // [N,H,DK,DV]
   float* zstate;        // normalised form: [N,H,DK], or nullptr
-  const float* decay;   // nullptr | gamma[H] | [N,H]
+  const float* decay;   // nullptr | gamma[H] | [N,H] | [N,H,DK] (per channel)
   int N, H, DK, DV;
   int phi, decay_kind;
 };
@@ -62,6 +62,7 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 bool chunk_bf16_supported(int DK, int TV, int NG, int C);
 // Whether the stripe kernel exists for key dim DK, TVW value columns per
 // workgroup, KH key parts per stripe and chunk C (and fits the LDS).
-bool chunk_stripe_supported(int DK, int TVW, int KH, int C);
+// With `channel`, for the per-channel decay.
+bool chunk_stripe_supported(int DK, int TVW, int KH, int C, bool channel = false);
 
 }  // namespace la

@@ -17,6 +17,11 @@ seeding 0 and splits the sequence into chunks of 64):
                per token per head, a_t = exp(-softplus(g_t)), C=64
   decode_bf16  N=256 H=32 d=128, fp32 state ~ 0.01 N(0,1), bf16 q,k,v /
                sqrt(128) per step, 1000 steps
+  gla_bf16     the retnet_bf16 shapes with a per-channel gate (GLA's
+               diagonal decay): log a[b,h,t,d] = -Exp(mean 0.8), i.i.d. per
+               token, head and key channel (the pages print no workload for
+               this variant; 0.8 is close to the mean of softplus(N(0,1)),
+               the gated workload's per-token decay)
 """
 from __future__ import annotations
 
@@ -31,6 +36,7 @@ DECAY_NONE = 0
 DECAY_HEAD = 1
 DECAY_LOG = 2
 DECAY_GATE = 3
+DECAY_CHANNEL = 4
 
 
 @dataclass
@@ -48,6 +54,7 @@ class ChunkWorkload:
     seed: int
     scale: float = 1.0
     gate_shift: float = 0.0
+    channel_mean: float = 0.8
     note: str = ""
 
 
@@ -78,6 +85,9 @@ WORKLOADS = {
                                  PHI_IDENTITY, DECAY_HEAD, seed=3, scale=1.0 / math.sqrt(128.0)),
     "gated_bf16": ChunkWorkload("gated_bf16", 1, 16, 65536, 128, 128, 64, torch.bfloat16,
                                 PHI_IDENTITY, DECAY_GATE, seed=4, scale=1.0 / math.sqrt(128.0)),
+    "gla_bf16": ChunkWorkload("gla_bf16", 2, 32, 16384, 128, 128, 64, torch.bfloat16,
+                              PHI_IDENTITY, DECAY_CHANNEL, seed=6, scale=1.0 / math.sqrt(128.0),
+                              channel_mean=0.8),
 }
 
 DECODE = DecodeWorkload("decode_bf16", 256, 32, 128, 128, 1000, torch.bfloat16, seed=5)
@@ -93,7 +103,8 @@ def chunk_inputs(w: ChunkWorkload, heads: slice | None = None):
 
     Draw order: q, k, v, then the gate g (gated workload only), each as one
     fp32 `randn` over the full [B,H,L,d] shape, multiplied by `scale` in fp32
-    and rounded to the workload dtype (round-to-nearest-even).
+    and rounded to the workload dtype (round-to-nearest-even); the
+    per-channel log decay is one fp32 `exponential_` draw over [B,H,L,dk].
     `heads` (a slice over the flattened B*H axis) trims what is returned but
     not what is drawn, so a subset is bit-identical to the full tensors.
     """
@@ -116,13 +127,16 @@ def chunk_inputs(w: ChunkWorkload, heads: slice | None = None):
         decay = torch.randn((w.B, w.H, w.L), generator=g, dtype=torch.float32)
         if w.gate_shift:
             decay = decay + torch.tensor(w.gate_shift, dtype=torch.float32)
+    elif w.decay_kind == DECAY_CHANNEL:
+        decay = -torch.empty(shp_k, dtype=torch.float32).exponential_(1.0 / w.channel_mean,
+                                                                      generator=g)
     else:
         decay = None
     if heads is not None:
         def sel(x):
             return x.reshape(w.B * w.H, *x.shape[2:])[heads].contiguous()
         q, k, v = sel(q), sel(k), sel(v)
-        if decay is not None and decay.dim() == 3:
+        if decay is not None and decay.dim() >= 3:
             decay = sel(decay)
     return q, k, v, decay
 
@@ -171,6 +185,7 @@ class RandomCase:
     seed: int = 0
     scale: float = 1.0
     gate_shift: float = 0.0
+    channel_mean: float = 0.5
     with_state: bool = False
     extra: dict = field(default_factory=dict)
 
@@ -179,7 +194,8 @@ def random_inputs(c: RandomCase):
     """Seeded q, k, v, decay data and (optionally) an initial state for a test case.
 
     Decay data: gamma[H] in [0.8, 1.0] for per-head decay, g ~ N(0,1) + shift
-    for the gate, log a = -|N(0, 0.1)| for the log-decay kind.
+    for the gate, log a = -|N(0, 0.1)| for the log-decay kind, log a[b,h,t,d]
+    = -Exp(mean channel_mean) for the per-channel kind.
     """
     g = torch.Generator().manual_seed(c.seed)
     sc = torch.tensor(c.scale, dtype=torch.float32)
@@ -192,6 +208,8 @@ def random_inputs(c: RandomCase):
         decay = torch.randn((c.B, c.H, c.L), generator=g) + c.gate_shift
     elif c.decay_kind == DECAY_LOG:
         decay = -(0.1 * torch.randn((c.B, c.H, c.L), generator=g)).abs()
+    elif c.decay_kind == DECAY_CHANNEL:
+        decay = -torch.empty((c.B, c.H, c.L, c.dk)).exponential_(1.0 / c.channel_mean, generator=g)
     else:
         decay = None
     state = None

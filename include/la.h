@@ -68,7 +68,10 @@ typedef enum {
   LA_DECAY_NONE = 0,       /* a_t = 1; decay_data ignored (may be NULL)          */
   LA_DECAY_HEAD = 1,       /* a_t = gamma[h]; decay_data = float gamma[H], 0<gamma<=1 */
   LA_DECAY_TOKEN_LOG = 2,  /* a_t = exp(log_a[b,h,t]); decay_data = float [B,H,L], <= 0 */
-  LA_DECAY_TOKEN_GATE = 3  /* a_t = exp(-softplus(g[b,h,t])); decay_data = float [B,H,L] */
+  LA_DECAY_TOKEN_GATE = 3, /* a_t = exp(-softplus(g[b,h,t])); decay_data = float [B,H,L] */
+  LA_DECAY_CHANNEL_LOG = 4 /* per key channel (GLA's diagonal gate, the tutorial's
+                              section 2.4): S_t = diag(exp(log_a[b,h,t,:])) S_{t-1} + k v^T;
+                              decay_data = float [B,H,L,d_k], <= 0 */
 } la_decay_kind;
 
 /*
@@ -103,7 +106,12 @@ size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C
  *                the result does not depend on C beyond rounding.  C >= L means
  *                one chunk.  The requested C is honoured, never replaced.
  *   phi        : la_phi
- *   decay_kind : la_decay_kind; decay_data as described there (device, read)
+ *   decay_kind : la_decay_kind; decay_data as described there (device, read).
+ *                LA_DECAY_CHANNEL_LOG on bf16 inputs needs the log decay of
+ *                every chunk, summed per channel, to be >= -150: the kernel
+ *                splits each factor e^{b_i - b_j} around half the chunk's
+ *                total, and both halves must stay in fp32 range (beyond that
+ *                the results are inf or NaN; this is not checked).
  *   state      : float [B, H, d_k, d_v] (device) or NULL.  In: S_0; out: S_L.
  *                NULL means S_0 = 0 and the final state is dropped.
  *   out        : [B, H, L, d_v], same dtype as q (device, written)
@@ -126,6 +134,7 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
  *
  *   q, k       : [N, H, d_k], dtype     v : [N, H, d_v], dtype   (device, read)
  *   decay_data : NULL | float gamma[H] | float [N, H] (this step's log a or g)
+ *                | float [N, H, d_k] (LA_DECAY_CHANNEL_LOG: this step's log a)
  *   state      : float [N, H, d_k, d_v] (device, read and written; required)
  *   out        : [N, H, d_v], same dtype as q (device, written)
  * Errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_UNSUPPORTED, LA_ERR_ALIGN, LA_ERR_DEVICE.
@@ -149,8 +158,8 @@ la_status la_decode_step(const void* q, const void* k, const void* v, int dtype,
  *                z_L is not written.  16-byte aligned.
  * Every other argument, the workspace size (la_chunk_fwd_workspace_bytes)
  * and the errors are those of la_chunk_fwd.  bf16 inputs need d_k, d_v >= 32
- * and C in {32, 64, 128} within the LDS (else LA_ERR_UNSUPPORTED); fp32
- * inputs take every supported shape.
+ * and C in {32, 64, 128} within the LDS and not LA_DECAY_CHANNEL_LOG (else
+ * LA_ERR_UNSUPPORTED); fp32 inputs take every supported shape and decay.
  */
 la_status la_chunk_fwd_norm(const void* q, const void* k, const void* v, int dtype, int B, int H,
                             int L, int d_k, int d_v, int C, int phi, int decay_kind,

@@ -51,8 +51,8 @@ def _fwd(**kw):
     (dict(kind=1, decay=None), NULL), (dict(kind=3, decay=None), NULL),
     (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(L=-5), SHAPE), (dict(C=0), SHAPE),
     (dict(dk=48), UNSUP), (dict(dv=256), UNSUP), (dict(dk=8), UNSUP), (dict(C=256), UNSUP),
-    (dict(C=48), UNSUP), (dict(dtype=2), UNSUP), (dict(phi=2), UNSUP), (dict(kind=4), UNSUP),
-    (dict(kind=-1), UNSUP),
+    (dict(C=48), UNSUP), (dict(dtype=2), UNSUP), (dict(phi=2), UNSUP), (dict(kind=5), UNSUP),
+    (dict(kind=-1), UNSUP), (dict(kind=4, decay=None), NULL),
     (dict(q=P8), ALIGN), (dict(out=P8), ALIGN), (dict(state=P8), ALIGN),
     (dict(kind=1, decay=ctypes.c_void_p((1 << 20) + 2)), ALIGN),
 ])
@@ -196,6 +196,39 @@ def test_decode_norm_requires_its_state():
                                    None) == NULL
     assert lib.la_decode_step_norm(P16, P16, P16, 1, 2, 2, 64, 64, 1, 0, None, P16, P8, P16,
                                    None) == ALIGN
+
+
+# bf16 per-channel decay: the stripe kernel's layouts whose log-decay
+# prefetch stays within 16 tokens per thread and whose tiles fit the LDS
+@pytest.mark.parametrize("dk,dv,C", [(128, 128, 128), (64, 64, 128), (128, 32, 64), (32, 32, 128),
+                                     (16, 16, 32), (64, 16, 64), (32, 32, 16)])
+def test_channel_decay_bf16_unsupported_shapes(dk, dv, C):
+    assert _fwd(kind=4, decay=P16, dk=dk, dv=dv, C=C) == UNSUP
+    # fp32 inputs take them (the call then fails only on the NULL q)
+    assert _fwd(kind=4, decay=P16, dk=dk, dv=dv, C=C, dtype=0, q=None) == NULL
+
+
+@pytest.mark.parametrize("dk,dv,C", [(128, 128, 64), (128, 128, 32), (64, 64, 64), (32, 128, 128),
+                                     (128, 32, 32), (64, 32, 64)])
+def test_channel_decay_bf16_supported_shapes(dk, dv, C):
+    assert _fwd(kind=4, decay=P16, dk=dk, dv=dv, C=C, q=None) == NULL
+
+
+def test_channel_decay_bf16_has_no_normalised_form():
+    assert _fwd_norm(kind=4, decay=P16, dk=128, dv=128) == UNSUP
+    assert _fwd_norm(kind=4, decay=P16, dtype=0, q=None) == NULL
+
+
+def test_channel_decay_workspace_holds_per_channel_totals():
+    # a split sequence keeps one log-decay total per segment, or d_k of them
+    # for the per-channel decay (both plans: stripe kernel, same segments)
+    B, H, L, d = 1, 1, 65536, 128
+    kernel, tile, P, groups = la.plan(B, H, L, d, d, 64)
+    assert kernel == la.KERNEL_STRIPE and P > 1
+    head = la.chunk_fwd_workspace_bytes(B, H, L, d, d, 64, la.LA_BF16, la.DECAY_HEAD)
+    ch = la.chunk_fwd_workspace_bytes(B, H, L, d, d, 64, la.LA_BF16, la.DECAY_CHANNEL)
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert ch - head == r256(P * d * 4) - r256(P * 4)
 
 
 def test_binding_refuses_cpu_tensors():

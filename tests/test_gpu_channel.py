@@ -1,0 +1,188 @@
+"""GPU parity of the per-channel gate (LA_DECAY_CHANNEL_LOG, GLA's diagonal
+decay, the linear/sparse attention tutorial's section 2.4):
+S_t = diag(a_t) S_{t-1} + phi(k_t) v_t^T with log a_t in [B,H,L,d_k], against
+the fp64 token-by-token oracle.  Bars as for the other decays: 1e-4 (fp32),
+1e-2 (bf16 inputs), as max|err| / max|ref|."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunkwise_recurrence_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+DEV = torch.device("cuda:0")
+
+
+def _np(t):
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def _run(la, c: W.RandomCase, C: int, label: str):
+    q, k, v, decay, S0 = W.random_inputs(c)
+    S0 = S0 if S0 is not None else torch.zeros(c.B, c.H, c.dk, c.dv)
+    print(f"[channel case] {label} B={c.B} H={c.H} L={c.L} dk={c.dk} dv={c.dv} C={C} "
+          f"dtype={c.dtype} phi={c.phi} mean={c.channel_mean}", flush=True)
+    S = S0.to(DEV).contiguous()
+    out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=C, phi=c.phi,
+                       decay_kind=W.DECAY_CHANNEL, decay=decay.to(DEV).contiguous(), state=S)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), c.phi, W.DECAY_CHANNEL, _np(decay),
+                                  _np(S0))
+    tol = TOL[c.dtype]
+    e = (oracle.rel_err(_np(out), ref), oracle.rel_err(_np(S), ref_s))
+    assert e[0] <= tol and e[1] <= tol, f"{label}: out/state rel err {e}"
+    return e
+
+
+@pytest.mark.parametrize("mean", [0.05, 1.0])
+@pytest.mark.parametrize("phi", [W.PHI_IDENTITY, W.PHI_ELU1])
+@pytest.mark.parametrize("d", [64, 128])
+def test_channel_variants_bf16(gpu_lib, d, phi, mean):
+    """Ragged length (5 chunks of 64 and 23 tokens), an initial state, weak and strong decay."""
+    c = W.RandomCase(2, 2, 64 * 5 + 23, d, d, torch.bfloat16, phi, W.DECAY_CHANNEL,
+                     seed=400 + d + 10 * phi + int(100 * mean), scale=1.0 / np.sqrt(d),
+                     channel_mean=mean, with_state=True)
+    _run(gpu_lib, c, 64, "variants")
+
+
+@pytest.mark.parametrize("phi", [W.PHI_IDENTITY, W.PHI_ELU1])
+def test_channel_fp32(gpu_lib, phi):
+    c = W.RandomCase(1, 2, 300, 16, 16, torch.float32, phi, W.DECAY_CHANNEL, seed=430 + phi,
+                     channel_mean=0.3, with_state=True)
+    _run(gpu_lib, c, 64, "fp32 16")
+    c = W.RandomCase(1, 2, 77, 32, 64, torch.float32, phi, W.DECAY_CHANNEL, seed=440 + phi,
+                     channel_mean=0.3, with_state=True)
+    _run(gpu_lib, c, 32, "fp32 32x64")
+
+
+@pytest.mark.parametrize("dk,dv,C", [(32, 32, 32), (64, 128, 64), (128, 64, 32), (32, 128, 128),
+                                     (32, 64, 128), (64, 32, 64), (128, 32, 32), (128, 128, 32)])
+def test_channel_head_dims(gpu_lib, dk, dv, C):
+    # the mean keeps a chunk's summed log decay far inside the documented bound
+    c = W.RandomCase(1, 3, 200, dk, dv, torch.bfloat16, W.PHI_IDENTITY, W.DECAY_CHANNEL,
+                     seed=dk + dv + C + 7, scale=1.0 / np.sqrt(dk), channel_mean=0.4,
+                     with_state=True)
+    _run(gpu_lib, c, C, "head dims")
+
+
+@pytest.mark.parametrize("tile,segments,parts", [(128, 1, 2), (128, 3, 2), (128, 7, 1), (64, 5, 2),
+                                                 (64, 2, 2), (128, 21, 2)])
+def test_channel_plan_invariance(gpu_lib, tile, segments, parts):
+    """Value tiles, key parts and sequence segments (the segment scan composes
+    per-channel decays) all give the oracle's result."""
+    la = gpu_lib
+    la.set_plan(la.KERNEL_STRIPE, tile, segments, parts)
+    try:
+        c = W.RandomCase(1, 2, 64 * 21 + 5, 128, 128, torch.bfloat16, W.PHI_IDENTITY,
+                         W.DECAY_CHANNEL, seed=460 + tile + segments + parts,
+                         scale=1.0 / np.sqrt(128), channel_mean=0.02, with_state=True)
+        _run(la, c, 64, f"plan tile={tile} P={segments} parts={parts}")
+    finally:
+        la.set_plan(0, 0, 0, 0)
+
+
+def test_channel_broadcast_equals_token_decay(gpu_lib):
+    """log a[t, d] = log a[t] for every channel is the per-token decay: both
+    kinds agree with each other and with the oracle."""
+    la = gpu_lib
+    c = W.RandomCase(1, 2, 64 * 4 + 9, 128, 128, torch.bfloat16, W.PHI_IDENTITY, W.DECAY_LOG,
+                     seed=470, scale=1.0 / np.sqrt(128), with_state=True)
+    q, k, v, log_a, S0 = W.random_inputs(c)
+    chan = log_a[..., None].expand(c.B, c.H, c.L, c.dk).contiguous()
+    S1, S2 = S0.to(DEV).contiguous(), S0.to(DEV).contiguous()
+    o1 = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=64, decay_kind=W.DECAY_LOG,
+                      decay=log_a.to(DEV), state=S1)
+    o2 = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=64, decay_kind=W.DECAY_CHANNEL,
+                      decay=chan.to(DEV), state=S2)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), 0, W.DECAY_LOG, _np(log_a), _np(S0))
+    assert oracle.rel_err(_np(o2), ref) <= 1e-2 and oracle.rel_err(_np(S2), ref_s) <= 1e-2
+    assert oracle.rel_err(_np(o2), _np(o1)) <= 1e-2
+    assert oracle.rel_err(_np(S2), _np(S1)) <= 1e-2
+
+
+def test_channel_zero_decay_is_ungated(gpu_lib):
+    """log a = 0 (a = 1) reduces to the ungated form."""
+    la = gpu_lib
+    c = W.RandomCase(2, 2, 150, 64, 64, torch.bfloat16, W.PHI_ELU1, W.DECAY_NONE, seed=480,
+                     scale=1.0 / np.sqrt(64), with_state=True)
+    q, k, v, _, S0 = W.random_inputs(c)
+    S = S0.to(DEV).contiguous()
+    out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=64, phi=W.PHI_ELU1,
+                       decay_kind=W.DECAY_CHANNEL, decay=torch.zeros(2, 2, 150, 64, device=DEV),
+                       state=S)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), W.PHI_ELU1, W.DECAY_NONE, None, _np(S0))
+    assert oracle.rel_err(_np(out), ref) <= 1e-2 and oracle.rel_err(_np(S), ref_s) <= 1e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_channel_prefill_then_decode(gpu_lib, dtype):
+    """chunk_fwd over L tokens, then n decode steps from its state == the recurrence over L + n."""
+    la = gpu_lib
+    L, n = 130, 6
+    c = W.RandomCase(2, 3, L + n, 64, 64, dtype, W.PHI_IDENTITY, W.DECAY_CHANNEL, seed=490,
+                     scale=1.0 / np.sqrt(64), channel_mean=0.2, with_state=True)
+    q, k, v, d, S0 = W.random_inputs(c)
+    S = S0.to(DEV).contiguous()
+    dd = d.to(DEV)
+    pre = la.chunk_fwd(q[:, :, :L].contiguous().to(DEV), k[:, :, :L].contiguous().to(DEV),
+                       v[:, :, :L].contiguous().to(DEV), C=32, decay_kind=W.DECAY_CHANNEL,
+                       decay=dd[:, :, :L].contiguous(), state=S)
+    steps = []
+    for t in range(L, L + n):
+        steps.append(la.decode_step(q[:, :, t].contiguous().to(DEV), k[:, :, t].contiguous().to(DEV),
+                                    v[:, :, t].contiguous().to(DEV), S, decay_kind=W.DECAY_CHANNEL,
+                                    decay=dd[:, :, t].contiguous()))
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), 0, W.DECAY_CHANNEL, _np(d), _np(S0))
+    tol = TOL[dtype]
+    assert oracle.rel_err(_np(pre), ref[:, :, :L]) <= tol
+    got = np.stack([_np(o) for o in steps], axis=2)
+    assert oracle.rel_err(got, ref[:, :, L:]) <= tol
+    assert oracle.rel_err(_np(S), ref_s) <= tol
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 128), (128, 32), (128, 128)])
+def test_channel_decode_head_dims(gpu_lib, dk, dv):
+    la = gpu_lib
+    N, H, T = 5, 3, 4
+    g = torch.Generator().manual_seed(dk * 1000 + dv + 1)
+    S0 = torch.randn(N, H, dk, dv, generator=g) * 0.1
+    S = S0.to(DEV)
+    ref_S = _np(S0)
+    for _ in range(T):
+        q, k, v = (torch.randn(N, H, d, generator=g).to(torch.bfloat16) for d in (dk, dk, dv))
+        log_a = -torch.rand(N, H, dk, generator=g)
+        o = la.decode_step(q.to(DEV), k.to(DEV), v.to(DEV), S, decay_kind=W.DECAY_CHANNEL,
+                           decay=log_a.to(DEV))
+        torch.cuda.synchronize()
+        ro, ref_S = oracle.decode_step(_np(q), _np(k), _np(v), 0, W.DECAY_CHANNEL, _np(log_a),
+                                       ref_S)
+        assert oracle.rel_err(_np(o), ro) < 1e-2
+    assert oracle.rel_err(_np(S), ref_S) < 1e-5  # the state itself stays fp32
+
+
+def test_gla_workload_sampled_heads(gpu_lib):
+    """The full gla_bf16 workload (B=2, H=32, L=16384, d=128, C=64) in the
+    bench's launch configuration; the oracle recomputes three sampled heads."""
+    la = gpu_lib
+    w = W.WORKLOADS["gla_bf16"]
+    print(f"[workload] gla_bf16 plan={la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)}", flush=True)
+    q, k, v, decay = W.chunk_inputs(w)
+    S = torch.zeros(w.B, w.H, w.dk, w.dv, device=DEV)
+    out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=w.C, decay_kind=W.DECAY_CHANNEL,
+                       decay=decay.to(DEV), state=S)
+    torch.cuda.synchronize()
+    heads = [0, 33, 63]
+    flat = lambda x: x.reshape(w.B * w.H, *x.shape[2:])  # noqa: E731
+    qs, ks, vs, ds = (flat(x)[heads][None] for x in (q, k, v, decay))
+    ref, ref_s = oracle.recurrent(_np(qs), _np(ks), _np(vs), 0, W.DECAY_CHANNEL, _np(ds))
+    got = _np(flat(out.cpu())[heads][None])
+    got_s = _np(flat(S.cpu())[heads][None])
+    e_out, e_s = oracle.rel_err(got, ref), oracle.rel_err(got_s, ref_s)
+    print(f"gla_bf16: sampled heads {heads}: output rel err {e_out:.3e}, state rel err {e_s:.3e}")
+    assert e_out <= 1e-2 and e_s <= 1e-2
