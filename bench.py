@@ -73,6 +73,8 @@ def chunk_algorithmic(w, with_state: bool):
     by = ht * (2 * w.dk + 2 * w.dv) * esz          # read q, k, v; write o
     if w.decay_kind in (2, 3):
         by += ht * 4                               # per-token decay data
+    elif w.decay_kind == 4:
+        by += ht * w.dk * 4                        # per-channel log decay
     elif w.decay_kind == 1:
         by += w.H * 4
     if with_state:
@@ -162,6 +164,37 @@ def bench_chunk_norm(la, torch, W, steps, warmup):
     return dict(w=w, ms=ms, bytes=by)
 
 
+def bench_chunk_gla(la, torch, W, steps, warmup):
+    """The per-channel (GLA) gate on its workload: la_chunk_fwd with log a
+    given per token, head and key channel."""
+    w = W.WORKLOADS["gla_bf16"]
+    dev = torch.device("cuda:0")
+    q, k, v, log_a = W.chunk_inputs(w)
+    q, k, v, log_a = q.to(dev), k.to(dev), v.to(dev), log_a.to(dev)
+    S = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
+    out = torch.empty_like(v)
+    need = la.chunk_fwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, w.C, la.LA_BF16, w.decay_kind)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        la.chunk_fwd(q, k, v, C=w.C, phi=w.phi, decay_kind=w.decay_kind, decay=log_a, state=S,
+                     out=out, workspace=ws if need else None, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    by, flops = chunk_algorithmic(w, with_state=True)
+    return dict(w=w, ms=ms, bytes=by, flops=flops)
+
+
 def bench_decode(la, torch, W, steps, reps=3):
     w = W.DECODE
     dev = torch.device("cuda:0")
@@ -231,7 +264,8 @@ def cpu_baseline(W):
 def profile_pass(la, torch, W):
     """A short fixed sequence of launches for counter passes: one plain copy of
     COPY_BYTES (the calibration), then the forward of the timed workload
-    (state init + la_chunk_fwd) three times, then 20 decode steps."""
+    (state init + la_chunk_fwd) three times, 20 decode steps, then two
+    forwards of the per-channel gate workload."""
     dev = torch.device("cuda:0")
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -241,6 +275,7 @@ def profile_pass(la, torch, W):
     del src, dst
     bench_chunk(la, torch, W, steps=1, warmup=1)
     bench_decode(la, torch, W, steps=20, reps=1)
+    bench_chunk_gla(la, torch, W, steps=1, warmup=1)
     torch.cuda.synchronize()
     print(json.dumps({"profile_pass": True, "copy_bytes": COPY_BYTES,
                       "source_sha256": kernel_source_digest()}), flush=True)
@@ -273,6 +308,7 @@ def main():
         return
     c = bench_chunk(la, torch, W, args.steps, args.warmup)
     n = bench_chunk_norm(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
+    g = bench_chunk_gla(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
     d = bench_decode(la, torch, W, args.decode_steps)
     w = c["w"]
     tokens = w.B * w.L
@@ -311,6 +347,12 @@ def main():
                        "algorithmic_bytes": n["bytes"],
                        "achieved_GBs": n["bytes"] / (n["ms"] / 1000.0) / 1e9,
                        "hbm_frac": n["bytes"] / (n["ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS},
+        "gla": {"workload": "gla_bf16: retnet_bf16 shapes, per-channel gate, "
+                            "log a ~ -Exp(mean 0.8) per token, head and key channel",
+                "ms_per_call": g["ms"], "tokens_per_s": tokens / (g["ms"] / 1000.0),
+                "algorithmic_bytes": g["bytes"],
+                "achieved_GBs": g["bytes"] / (g["ms"] / 1000.0) / 1e9,
+                "hbm_frac": g["bytes"] / (g["ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS},
         "decode": {"workload": "decode_bf16", "N": d["w"].N, "H": d["w"].H, "d": d["w"].dk,
                    "steps": d["steps"], "steps_per_s": 1e6 / d["step_us"],
                    "us_per_step": d["step_us"], "bytes_per_step": d["bytes"],
