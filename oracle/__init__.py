@@ -62,6 +62,9 @@ def _load(path: str | None = None):
         lib.oracle_recurrent_norm.restype = ctypes.c_int
         lib.oracle_recurrent_norm.argtypes = [ctypes.c_int] * 5 + [
             d, d, d, ctypes.c_int, ctypes.c_int, d, d, d, d, ctypes.c_int]
+        lib.oracle_delta.restype = ctypes.c_int
+        lib.oracle_delta.argtypes = [ctypes.c_int] * 5 + [d, d, d, d, ctypes.c_int, d, d, d,
+                                                         ctypes.c_int]
         _libs[path] = lib
     return _libs[path]
 
@@ -336,5 +339,122 @@ def chunkwise_channel(q, k, v, log_a, C: int, phi: int = PHI_IDENTITY, state=Non
                 P = np.where(mask, P, 0.0)
                 out[b, h, s:e] = (Qc * np.exp(Bc)) @ Sh + P @ Vc
                 Sh = np.exp(Bc[-1])[:, None] * Sh + (Kc * np.exp(Bc[-1] - Bc)).T @ Vc
+            S[b, h] = Sh
+    return out, S
+
+
+# --------------------------------------------------------------------------
+# the delta rule (DeltaNet; Gated DeltaNet with a scalar decay a_t)
+# ("Linear / Sparse Attention", delta_rule_recurrent; the tutorial, section
+# 5.1-5.3, Q15, Q17, Q23)
+# --------------------------------------------------------------------------
+def delta_recurrent(q, k, v, beta, decay_kind: int = DECAY_NONE, decay=None, state=None,
+                    nthreads: int | None = None, lib_path: str | None = None):
+    """Token-by-token fp64 delta rule (`la_oracle.c`, oracle_delta): THE oracle
+    the GPU's delta path is compared with.
+
+    S_t = a_t (S_{t-1} - beta_t k_t (k_t^T S_{t-1})) + beta_t k_t v_t^T,
+    o_t = q_t^T S_t; S is [dk, dv] (the transpose of the pages' value-by-key
+    state).  q, k: [B,H,L,dk]; v: [B,H,L,dv]; beta: [B,H,L];
+    decay: None | gamma[H] | log_a or g [B,H,L].  Returns (out, final state).
+    """
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, H, L, dk) and v.shape == (B, H, L, dv) and beta.shape == (B, H, L)
+    S = np.zeros((B, H, dk, dv)) if state is None else _f64(state).copy()
+    assert S.shape == (B, H, dk, dv)
+    out = np.zeros((B, H, L, dv))
+    assert decay_kind in (DECAY_NONE, DECAY_HEAD, DECAY_LOG, DECAY_GATE)
+    if decay_kind == DECAY_NONE:
+        dec = np.zeros(1)
+    elif decay_kind == DECAY_HEAD:
+        dec = _f64(decay).reshape(H)
+    else:
+        dec = _f64(decay).reshape(B, H, L)
+    if B * H == 0 or L == 0:
+        return out, S
+    n = host_threads() if nthreads is None else nthreads
+    _load(lib_path).oracle_delta(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                 decay_kind, _ptr(dec), _ptr(S), _ptr(out), n)
+    return out, S
+
+
+def delta_decode_step(q, k, v, beta, decay_kind: int = DECAY_NONE, decay=None, state=None,
+                      lib_path: str | None = None):
+    """One delta-rule step for N sequences x H heads (L = 1 of the recurrence).
+    q, k: [N,H,dk]; v: [N,H,dv]; beta: [N,H]; decay: None | gamma[H] | [N,H]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, H, _ = q.shape
+    dec = decay
+    if decay_kind in (DECAY_LOG, DECAY_GATE):
+        dec = _f64(decay).reshape(N, H, 1)
+    out, S = delta_recurrent(q[:, :, None, :], k[:, :, None, :], v[:, :, None, :],
+                             _f64(beta).reshape(N, H, 1), decay_kind, dec, state,
+                             lib_path=lib_path)
+    return out[:, :, 0, :], S
+
+
+def delta_explicit(q, k, v, beta, a, state=None):
+    """The delta rule as the pages write it, with explicit matrices: a value-by-key
+    state S'_t = a_t S'_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T and
+    o_t = S'_t q_t, then transposed back to the [dk, dv] orientation.
+    a: [B,H,L] multipliers (decay_multipliers).  A separate computation path
+    (full d_k x d_k products, the other orientation) that pins `delta_recurrent`.
+    """
+    q, k, v, beta, a = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(a)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    S0 = np.zeros((B, H, dk, dv)) if state is None else _f64(state)
+    out = np.zeros((B, H, L, dv))
+    SL = np.zeros((B, H, dk, dv))
+    eye = np.eye(dk)
+    for b in range(B):
+        for h in range(H):
+            Sp = S0[b, h].T.copy()  # [dv, dk]
+            for t in range(L):
+                kt = k[b, h, t]
+                Sp = a[b, h, t] * Sp @ (eye - beta[b, h, t] * np.outer(kt, kt)) \
+                    + beta[b, h, t] * np.outer(v[b, h, t], kt)
+                out[b, h, t] = Sp @ q[b, h, t]
+            SL[b, h] = Sp.T
+    return out, SL
+
+
+def delta_chunkwise(q, k, v, beta, log_a, C: int, state=None):
+    """Chunkwise (WY / UT) form of the delta rule, derived by unrolling the
+    recurrence over one chunk (the tutorial's section 5.3 and Q23 give the
+    idea -- the chunk's product of (I - beta k k^T) factors in a compact WY
+    form -- but no steps).  Writing S_t = a_t S_{t-1} + k_t u_t^T with
+    u_t = beta_t (v_t - a_t S_{t-1}^T k_t), and b the in-chunk inclusive
+    cumsum of log a, the chunk's u's solve the unit lower-triangular system
+
+      (I + diag(beta) (tril(K K^T, -1) o G)) U = diag(beta) (V - diag(e^b) K S_c),
+      G[i,j] = e^{b_i - b_j},
+
+    and then O_c = diag(e^b) Q S_c + ((Q K^T) o D) U with D = tril(G) (diagonal
+    included) and S_{c+1} = e^{b_last} S_c + (diag(e^{b_last - b}) K)^T U.
+    log_a: [B,H,L] (zeros for no decay).  fp64; np.linalg.solve for the system.
+    """
+    q, k, v, beta, la = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(log_a)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if state is None else _f64(state).copy()
+    out = np.zeros((B, H, L, dv))
+    for b in range(B):
+        for h in range(H):
+            Sh = S[b, h]
+            for s in range(0, L, C):
+                e = min(s + C, L)
+                n = e - s
+                Qc, Kc, Vc, bc = q[b, h, s:e], k[b, h, s:e], v[b, h, s:e], beta[b, h, s:e]
+                bb = np.cumsum(la[b, h, s:e])
+                G = np.exp(np.where(np.tril(np.ones((n, n), dtype=bool)),
+                                    bb[:, None] - bb[None, :], -np.inf))
+                A = np.eye(n) + bc[:, None] * (np.tril(Kc @ Kc.T, -1) * G)
+                R = bc[:, None] * (Vc - np.exp(bb)[:, None] * (Kc @ Sh))
+                U = np.linalg.solve(A, R)
+                out[b, h, s:e] = np.exp(bb)[:, None] * (Qc @ Sh) + ((Qc @ Kc.T) * G) @ U
+                Sh = np.exp(bb[-1]) * Sh + (np.exp(bb[-1] - bb)[:, None] * Kc).T @ U
             S[b, h] = Sh
     return out, S

@@ -31,6 +31,20 @@
  * and returns o_t = phi(q_t)^T S_t / phi(q_t)^T z_t, with no term added to the
  * denominator (the pages give none).
  *
+ * The delta rule (DeltaNet; with a_t, Gated DeltaNet) is the second
+ * recurrence here ("Linear / Sparse Attention - minimal runnable
+ * implementation", delta_rule_recurrent; the tutorial, section 5.1-5.2, Q15
+ * and Q17).  The pages write it with a d_v x d_k state S' that maps keys to
+ * values, S'_t = a_t S'_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T; the
+ * state here is its transpose S = S'^T (d_k x d_v, the orientation of the
+ * linear-attention state), so the same step reads
+ *
+ *   S   <- a_t (S - beta_t k_t (k_t^T S)) + beta_t k_t v_t^T
+ *   o_t <- q_t^T S                            read AFTER the write
+ *
+ * (the erase acts on the decayed previous state, the write is undecayed;
+ * the keys are taken as given: the pages normalise them before the call).
+ *
  * Decay kinds (same numbering as the library's public enum, redeclared here
  * on purpose so that the two sides share no header):
  *   0 none        a_t = 1
@@ -191,4 +205,94 @@ int oracle_recurrent(int B, int H, int L, int dk, int dv, const double* q, const
                      double* out, int nthreads) {
   return oracle_recurrent_norm(B, H, L, dk, dv, q, k, v, phi, decay_kind, decay, S, NULL, out,
                                nthreads);
+}
+
+/*
+ * The delta rule, one head, L tokens, token by token.
+ *   q, k : [L, dk]   v : [L, dv]   beta : [L]   out : [L, dv]
+ *   S    : [dk, dv] (in: S_0, out: S_L)
+ *   dh   : decay data of this head (kinds 0-3 as above), may be NULL for kind 0
+ */
+void oracle_delta_head(int L, int dk, int dv, const double* q, const double* k, const double* v,
+                       const double* beta, int decay_kind, const double* dh, double* S,
+                       double* out) {
+  double* r = (double*)malloc(sizeof(double) * (size_t)dv);
+  for (int t = 0; t < L; ++t) {
+    const double* qt = q + (size_t)t * dk;
+    const double* kt = k + (size_t)t * dk;
+    const double* vt = v + (size_t)t * dv;
+    const double a = oracle_decay(decay_kind, dh, t);
+    const double bt = beta[t];
+    /* what the previous state returns for k_t: r = k_t^T S_{t-1} */
+    for (int j = 0; j < dv; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < dk; ++i) acc += kt[i] * S[(size_t)i * dv + j];
+      r[j] = acc;
+    }
+    /* erase along k_t, decay, then write: S = a (S - beta k r^T) + beta k v^T */
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j)
+        S[(size_t)i * dv + j] = a * (S[(size_t)i * dv + j] - bt * kt[i] * r[j]) + bt * kt[i] * vt[j];
+    /* read: o_t = q_t^T S */
+    double* ot = out + (size_t)t * dv;
+    for (int j = 0; j < dv; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < dk; ++i) acc += qt[i] * S[(size_t)i * dv + j];
+      ot[j] = acc;
+    }
+  }
+  free(r);
+}
+
+typedef struct {
+  int H, L, dk, dv, kind;
+  const double *q, *k, *v, *beta, *decay;
+  double *S, *out;
+  int first, last;
+} oracle_delta_job;
+
+static void* oracle_delta_worker(void* p) {
+  oracle_delta_job* j = (oracle_delta_job*)p;
+  for (int bh = j->first; bh < j->last; ++bh) {
+    const int h = bh % j->H;
+    const double* dh = NULL;
+    if (j->kind == ORACLE_DECAY_HEAD) dh = j->decay + h;
+    else if (j->kind == ORACLE_DECAY_LOG || j->kind == ORACLE_DECAY_GATE)
+      dh = j->decay + (size_t)bh * j->L;
+    oracle_delta_head(j->L, j->dk, j->dv, j->q + (size_t)bh * j->L * j->dk,
+                      j->k + (size_t)bh * j->L * j->dk, j->v + (size_t)bh * j->L * j->dv,
+                      j->beta + (size_t)bh * j->L, j->kind, dh,
+                      j->S + (size_t)bh * j->dk * j->dv, j->out + (size_t)bh * j->L * j->dv);
+  }
+  return NULL;
+}
+
+/*
+ * The delta rule over all heads of a [B, H, L, d] problem.
+ *   q, k : [B,H,L,dk]  v : [B,H,L,dv]  beta : [B,H,L]  out : [B,H,L,dv]
+ *   S    : [B,H,dk,dv] in/out   decay: NULL | gamma[H] | log_a or g [B,H,L]
+ * Returns the number of threads actually used.
+ */
+int oracle_delta(int B, int H, int L, int dk, int dv, const double* q, const double* k,
+                 const double* v, const double* beta, int decay_kind, const double* decay,
+                 double* S, double* out, int nthreads) {
+  const int heads = B * H;
+  if (heads <= 0) return 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > heads) nthreads = heads;
+  oracle_delta_job* jobs = (oracle_delta_job*)calloc((size_t)nthreads, sizeof(oracle_delta_job));
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  for (int i = 0; i < nthreads; ++i) {
+    oracle_delta_job* j = &jobs[i];
+    j->H = H; j->L = L; j->dk = dk; j->dv = dv; j->kind = decay_kind;
+    j->q = q; j->k = k; j->v = v; j->beta = beta; j->decay = decay; j->S = S; j->out = out;
+    j->first = (int)((long long)heads * i / nthreads);
+    j->last = (int)((long long)heads * (i + 1) / nthreads);
+  }
+  for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, oracle_delta_worker, &jobs[i]);
+  oracle_delta_worker(&jobs[0]);
+  for (int i = 1; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(jobs);
+  free(th);
+  return nthreads;
 }

@@ -44,6 +44,14 @@ MUTANTS = {
                               "? exp(dh[(size_t)t * dk + (dk - 1 - i)]) : a;"),
     "channel_gate_of_previous_token": ("? exp(dh[(size_t)t * dk + i]) : a;",
                                        "? exp(dh[(size_t)(t > 0 ? t - 1 : 0) * dk + i]) : a;"),
+    # the delta rule
+    "delta_erase_along_query": ("acc += kt[i] * S[(size_t)i * dv + j];",
+                                "acc += qt[i] * S[(size_t)i * dv + j];"),
+    "delta_beta_missing_on_erase": ("a * (S[(size_t)i * dv + j] - bt * kt[i] * r[j])",
+                                    "a * (S[(size_t)i * dv + j] - kt[i] * r[j])"),
+    "delta_write_decayed": ("+ bt * kt[i] * vt[j];", "+ a * bt * kt[i] * vt[j];"),
+    "delta_erase_not_decayed": ("a * (S[(size_t)i * dv + j] - bt * kt[i] * r[j])",
+                                "a * S[(size_t)i * dv + j] - bt * kt[i] * r[j]"),
 }
 
 
@@ -95,6 +103,15 @@ def _battery(lib):
         op, Sp = oracle.parallel_channel(q, k, v, np.exp(la), phi, S0)
         if oracle.rel_err(o, op) > 1e-12 or oracle.rel_err(S, Sp) > 1e-12:
             failed.append(f"channel gate phi={phi}")
+    # the delta rule: the C recurrence == the pages' explicit (I - beta k k^T) form
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    beta = rng.uniform(0.1, 1.0, (B, H, L))
+    for kind, dec in decays.items():
+        o, S = oracle.delta_recurrent(q, kn, v, beta, kind, dec, S0, lib_path=lib)
+        a = oracle.decay_multipliers(B, H, L, kind, dec)
+        oe, Se = oracle.delta_explicit(q, kn, v, beta, a, S0)
+        if oracle.rel_err(o, oe) > 1e-12 or oracle.rel_err(S, Se) > 1e-12:
+            failed.append(f"delta explicit kind={kind}")
     # phi read out against torch's elu + 1
     x = np.linspace(-4.0, 3.0, 6)
     o, _ = oracle.recurrent(x[None, None, None], np.zeros((1, 1, 1, 6)), np.zeros((1, 1, 1, 6)),
