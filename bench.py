@@ -195,6 +195,37 @@ def bench_chunk_gla(la, torch, W, steps, warmup):
     return dict(w=w, ms=ms, bytes=by, flops=flops)
 
 
+def bench_delta(la, torch, W, steps, warmup):
+    """The delta rule (Gated DeltaNet) on delta_bf16: la_delta_fwd, both passes."""
+    w = W.DELTA
+    dev = torch.device("cuda:0")
+    q, k, v, beta, g = W.delta_inputs(w)
+    q, k, v, beta, g = q.to(dev), k.to(dev), v.to(dev), beta.to(dev), g.to(dev)
+    S = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
+    out = torch.empty_like(v)
+    ws = torch.empty(la.delta_fwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, w.C, la.LA_BF16),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        la.delta_fwd(q, k, v, beta, C=w.C, decay_kind=w.decay_kind, decay=g, state=S, out=out,
+                     workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    by, _ = chunk_algorithmic(w, with_state=True)
+    by += w.B * w.H * w.L * 4                      # beta
+    return dict(w=w, ms=ms, bytes=by)
+
+
 def bench_decode(la, torch, W, steps, reps=3):
     w = W.DECODE
     dev = torch.device("cuda:0")
@@ -309,6 +340,7 @@ def main():
     c = bench_chunk(la, torch, W, args.steps, args.warmup)
     n = bench_chunk_norm(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
     g = bench_chunk_gla(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
+    dl = bench_delta(la, torch, W, max(args.steps // 10, 1), max(args.warmup // 5, 1))
     d = bench_decode(la, torch, W, args.decode_steps)
     w = c["w"]
     tokens = w.B * w.L
@@ -353,6 +385,12 @@ def main():
                 "algorithmic_bytes": g["bytes"],
                 "achieved_GBs": g["bytes"] / (g["ms"] / 1000.0) / 1e9,
                 "hbm_frac": g["bytes"] / (g["ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS},
+        "delta": {"workload": "delta_bf16: Gated DeltaNet on the retnet_bf16 shapes, unit keys, "
+                              "beta ~ U(0,1), gate g ~ N(0,1), C = 64",
+                  "ms_per_call": dl["ms"], "tokens_per_s": tokens / (dl["ms"] / 1000.0),
+                  "algorithmic_bytes": dl["bytes"],
+                  "achieved_GBs": dl["bytes"] / (dl["ms"] / 1000.0) / 1e9,
+                  "hbm_frac": dl["bytes"] / (dl["ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS},
         "decode": {"workload": "decode_bf16", "N": d["w"].N, "H": d["w"].H, "d": d["w"].dk,
                    "steps": d["steps"], "steps_per_s": 1e6 / d["step_us"],
                    "us_per_step": d["step_us"], "bytes_per_step": d["bytes"],

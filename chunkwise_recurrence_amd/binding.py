@@ -28,7 +28,8 @@ class Plan(ctypes.Structure):
 # every symbol include/la.h declares
 EXPORTS = ("la_state_init", "la_chunk_fwd_workspace_bytes", "la_chunk_fwd", "la_decode_step",
            "la_status_string", "la_chunk_fwd_plan", "la_set_plan", "la_chunk_fwd_norm",
-           "la_decode_step_norm")
+           "la_decode_step_norm", "la_delta_fwd_workspace_bytes", "la_delta_fwd",
+           "la_delta_decode_step")
 
 _lib = None
 
@@ -67,6 +68,13 @@ def load():
                                       ctypes.c_size_t, vp]
     lib.la_decode_step_norm.restype = i
     lib.la_decode_step_norm.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, vp, vp]
+    lib.la_delta_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.la_delta_fwd_workspace_bytes.argtypes = [i] * 7
+    lib.la_delta_fwd.restype = i
+    lib.la_delta_fwd.argtypes = [vp, vp, vp, f, i, i, i, i, i, i, i, i, f, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
+    lib.la_delta_decode_step.restype = i
+    lib.la_delta_decode_step.argtypes = [vp, vp, vp, f, i, i, i, i, i, i, f, vp, vp, vp]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i]
     lib.la_chunk_fwd_plan.restype = i
@@ -214,3 +222,64 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.
                                  _ptr(decay), _ptr(state), _ptr(out), _stream(stream)),
            "la_decode_step")
     return out
+
+
+def delta_fwd_workspace_bytes(B: int, H: int, L: int, dk: int, dv: int, C: int,
+                              dtype: int = LA_BF16) -> int:
+    return int(load().la_delta_fwd_workspace_bytes(B, H, L, dk, dv, C, dtype))
+
+
+def delta_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor, C: int = 64,
+              decay_kind: int = DECAY_NONE, decay=None, state=None, out=None, workspace=None,
+              stream=None) -> torch.Tensor:
+    """The chunkwise delta rule (la_delta_fwd) over [B,H,L,d] inputs; beta fp32 [B,H,L].
+
+    `state` (fp32 [B,H,dk,dv]) is read as S_0 and overwritten with S_L when given.
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (decay, "decay"),
+                 (state, "state"), (out, "out"), (workspace, "workspace")):
+        _dev(t, n)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,L,dk] and v [B,H,L,dv]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (B, H, L):
+        raise ValueError("beta must be float32 [B,H,L]")
+    if decay is not None and decay.dtype != torch.float32:
+        raise ValueError("decay data must be float32")
+    if state is not None and (state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv)):
+        raise ValueError("state must be float32 [B,H,dk,dv]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    need = delta_fwd_workspace_bytes(B, H, L, dk, dv, C, dt)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().la_delta_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), dt, B, H, L, dk, dv, C,
+                               decay_kind, _ptr(decay), _ptr(state), _ptr(out), _ptr(workspace),
+                               ws_bytes, _stream(stream)), "la_delta_fwd")
+    return out
+
+
+def delta_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                      state: torch.Tensor, decay_kind: int = DECAY_NONE, decay=None, out=None,
+                      stream=None) -> torch.Tensor:
+    """One delta-rule token for [N,H,d] inputs (beta fp32 [N,H]), updating `state` in place."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (state, "state"),
+                 (decay, "decay"), (out, "out")):
+        _dev(t, n)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if beta.dtype != torch.float32 or tuple(beta.shape) != (N, H):
+        raise ValueError("beta must be float32 [N,H]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _check(load().la_delta_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), dt, N, H, dk, dv,
+                                       decay_kind, _ptr(decay), _ptr(state), _ptr(out),
+                                       _stream(stream)), "la_delta_decode_step")
+    return out
+

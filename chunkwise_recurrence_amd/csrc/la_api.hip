@@ -349,3 +349,96 @@ la_status la_decode_step_norm(const void* q, const void* k, const void* v, int d
 }
 
 }  // extern "C"
+
+namespace {
+
+size_t delta_ws_bytes(int B, int H, int L, int d_k, int d_v) {
+  const size_t ht = (size_t)B * H * L;
+  return round256(ht * d_k * sizeof(float)) + round256(ht * d_v * sizeof(float));
+}
+
+la_status check_delta_shape(int dtype, int B, int H, int L, int d_k, int d_v, int C) {
+  const la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
+  if (st != LA_OK) return st;
+  if (C > la::kDeltaMaxC) return LA_ERR_UNSUPPORTED;
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la_delta_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
+  if (check_delta_shape(dtype, B, H, L, d_k, d_v, C) != LA_OK || L == 0) return 0;
+  return delta_ws_bytes(B, H, L, d_k, d_v);
+}
+
+la_status la_delta_fwd(const void* q, const void* k, const void* v, const float* beta, int dtype,
+                       int B, int H, int L, int d_k, int d_v, int C, int decay_kind,
+                       const float* decay_data, float* state, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  la_status st = check_delta_shape(dtype, B, H, L, d_k, d_v, C);
+  if (st != LA_OK) return st;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return LA_ERR_UNSUPPORTED;
+  if (L == 0) return LA_OK;
+  if (!q || !k || !v || !beta || !out) return LA_ERR_NULL;
+  if (decay_kind != LA_DECAY_NONE && !decay_data) return LA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      (state && !aligned(state, 16)) || !aligned(beta, 4) ||
+      (decay_data && !aligned(decay_data, 4)))
+    return LA_ERR_ALIGN;
+  const size_t need = delta_ws_bytes(B, H, L, d_k, d_v);
+  if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return LA_ERR_ALIGN;
+  la::DeltaArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.out = out;
+  a.state = state;
+  a.decay = decay_kind == LA_DECAY_NONE ? nullptr : decay_data;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_W = reinterpret_cast<float*>(ws);
+  a.ws_U = reinterpret_cast<float*>(ws + round256((size_t)B * H * L * d_k * sizeof(float)));
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.DK = d_k;
+  a.DV = d_v;
+  a.C = C;
+  a.decay_kind = decay_kind;
+  a.dtype = dtype;
+  return la::launch_delta(a, as_stream(stream)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+}
+
+la_status la_delta_decode_step(const void* q, const void* k, const void* v, const float* beta,
+                               int dtype, int N, int H, int d_k, int d_v, int decay_kind,
+                               const float* decay_data, float* state, void* out, void* stream) {
+  if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+  if (N < 1 || H < 1) return LA_ERR_SHAPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return LA_ERR_UNSUPPORTED;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_TOKEN_GATE) return LA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !beta || !state || !out) return LA_ERR_NULL;
+  if (decay_kind != LA_DECAY_NONE && !decay_data) return LA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      !aligned(state, 16) || !aligned(beta, 4) || (decay_data && !aligned(decay_data, 4)))
+    return LA_ERR_ALIGN;
+  la::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.state = state;
+  a.beta = beta;
+  a.decay = decay_kind == LA_DECAY_NONE ? nullptr : decay_data;
+  a.N = N;
+  a.H = H;
+  a.DK = d_k;
+  a.DV = d_v;
+  a.phi = LA_PHI_IDENTITY;
+  a.decay_kind = decay_kind;
+  return la::launch_decode(a, dtype, as_stream(stream)) == hipSuccess ? LA_OK : LA_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -11,6 +11,11 @@
 // per-channel gate (the tutorial's section 2.4) a is a vector over the key
 // channels: row i of S and entry i of z decay by a_i.
 //
+// The delta rule (DeltaNet, gated by a scalar a; "Linear / Sparse Attention",
+// delta_rule_recurrent, stored transposed) first reads what the old state
+// returns for k, r = k^T S, then writes S' = a (S - beta k r^T) + beta k v^T:
+// one more reduction over the rows the lanes already hold.
+//
 // The step is a pure stream over the fp32 state: every element is read once,
 // updated and written once, and o is reduced on the way.  One workgroup of 256
 // lanes per head; each lane owns 4 adjacent columns (one 16-byte vector) of
@@ -70,6 +75,39 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const bool chan = a.decay_kind == kDecayChannel;
   __shared__ float sdec[DK];
   if (tid < DK) sdec[tid] = chan ? expf(a.decay[(size_t)bh * DK + tid]) : decay;
+  // delta rule: r = k^T S of the previous state, reduced over the row groups
+  __shared__ float sr[DV];
+  float bta = 0.0f;
+  if (a.beta != nullptr) {
+    bta = a.beta[bh];
+    __syncthreads();
+    float4 rp = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int r = rg + p * RP;
+      if (r < DK) {
+        const float kr = sk[r];
+        rp.x = fmaf(kr, sreg[p].x, rp.x);
+        rp.y = fmaf(kr, sreg[p].y, rp.y);
+        rp.z = fmaf(kr, sreg[p].z, rp.z);
+        rp.w = fmaf(kr, sreg[p].w, rp.w);
+      }
+    }
+    if (rg < RP) {
+      red[rg][4 * c4] = rp.x;
+      red[rg][4 * c4 + 1] = rp.y;
+      red[rg][4 * c4 + 2] = rp.z;
+      red[rg][4 * c4 + 3] = rp.w;
+    }
+    __syncthreads();
+    if (tid < DV) {
+      float acc = 0.0f;
+      constexpr int used = DK < RP ? DK : RP;
+#pragma unroll
+      for (int g = 0; g < used; ++g) acc += red[g][tid];
+      sr[tid] = acc;
+    }
+  }
   __shared__ float sden[DK];
   if (a.zstate != nullptr) {
     __syncthreads();
@@ -83,6 +121,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   __syncthreads();
 
   const float4 vv = make_float4(sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]);
+  float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (a.beta != nullptr) rv = make_float4(sr[4 * c4], sr[4 * c4 + 1], sr[4 * c4 + 2], sr[4 * c4 + 3]);
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
@@ -91,10 +131,19 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       const float kr = sk[r], qr = sq[r];
       const float dr = chan ? sdec[r] : decay;
       f32x4 s = sreg[p];
-      s.x = fmaf(dr, s.x, kr * vv.x);
-      s.y = fmaf(dr, s.y, kr * vv.y);
-      s.z = fmaf(dr, s.z, kr * vv.z);
-      s.w = fmaf(dr, s.w, kr * vv.w);
+      if (a.beta != nullptr) {
+        // S' = a (S - beta k r^T) + beta k v^T
+        const float bk = bta * kr;
+        s.x = fmaf(dr, fmaf(-bk, rv.x, s.x), bk * vv.x);
+        s.y = fmaf(dr, fmaf(-bk, rv.y, s.y), bk * vv.y);
+        s.z = fmaf(dr, fmaf(-bk, rv.z, s.z), bk * vv.z);
+        s.w = fmaf(dr, fmaf(-bk, rv.w, s.w), bk * vv.w);
+      } else {
+        s.x = fmaf(dr, s.x, kr * vv.x);
+        s.y = fmaf(dr, s.y, kr * vv.y);
+        s.z = fmaf(dr, s.z, kr * vv.z);
+        s.w = fmaf(dr, s.w, kr * vv.w);
+      }
       __builtin_nontemporal_store(s, &S[r * TPR + c4]);
       o.x = fmaf(qr, s.x, o.x);
       o.y = fmaf(qr, s.y, o.y);

@@ -37,6 +37,25 @@ struct ChunkArgs {
   int phi, decay_kind;
 };
 
+// Largest chunk the delta-rule kernels take.
+constexpr int kDeltaMaxC = 64;
+
+// One la_delta_fwd: the chunk-parallel solve pass and the sequential pass.
+struct DeltaArgs {
+  const void* q;        // [B,H,L,DK]
+  const void* k;        // [B,H,L,DK]
+  const void* v;        // [B,H,L,DV]
+  const float* beta;    // [B,H,L]
+  void* out;            // [B,H,L,DV]
+  float* state;         // [B,H,DK,DV] or nullptr
+  const float* decay;   // nullptr | gamma[H] | [B,H,L]
+  float* ws_W;          // [B*H, L, DK] W = T diag(beta e^b) K per chunk
+  float* ws_U;          // [B*H, L, DV] U0 = T diag(beta) V per chunk
+  int B, H, L, DK, DV, C;
+  int decay_kind, dtype;
+  int n_v;              // value tiles per head
+};
+
 struct DecodeArgs {
   const void* q;        // [N,H,DK]
   const void* k;        // [N,H,DK]
@@ -44,6 +63,7 @@ struct DecodeArgs {
   void* out;            // [N,H,DV]
   float* state;         // [N,H,DK,DV]
   float* zstate;        // normalised form: [N,H,DK], or nullptr
+  const float* beta;    // delta rule: [N,H] write strengths, or nullptr
   const float* decay;   // nullptr | gamma[H] | [N,H] | [N,H,DK] (per channel)
   int N, H, DK, DV;
   int phi, decay_kind;
@@ -55,6 +75,7 @@ hipError_t launch_chunk_stripe(const ChunkArgs& a, bool state_only, hipStream_t 
 hipError_t launch_decay_prefix(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_delta(const DeltaArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 
 // Whether a bf16 kernel exists for key dim DK, NG column groups of TV columns

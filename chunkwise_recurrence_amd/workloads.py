@@ -17,6 +17,12 @@ seeding 0 and splits the sequence into chunks of 64):
                per token per head, a_t = exp(-softplus(g_t)), C=64
   decode_bf16  N=256 H=32 d=128, fp32 state ~ 0.01 N(0,1), bf16 q,k,v /
                sqrt(128) per step, 1000 steps
+  delta_bf16   the delta rule (Gated DeltaNet) on the retnet_bf16 shapes:
+               q, v / sqrt(128); keys uniform on the unit sphere (a Gaussian
+               row divided by its length -- the pages normalise keys before the
+               delta rule); beta ~ U(0, 1) per token and head; the gated
+               workload's gate g ~ N(0,1); C = 64 (the pages print no workload
+               for it)
   gla_bf16     the retnet_bf16 shapes with a per-channel gate (GLA's
                diagonal decay): log a[b,h,t,d] = -Exp(mean 0.8), i.i.d. per
                token, head and key channel (the pages print no workload for
@@ -90,6 +96,9 @@ WORKLOADS = {
                               channel_mean=0.8),
 }
 
+DELTA = ChunkWorkload("delta_bf16", 2, 32, 16384, 128, 128, 64, torch.bfloat16, PHI_IDENTITY,
+                      DECAY_GATE, seed=7, scale=1.0 / math.sqrt(128.0))
+
 DECODE = DecodeWorkload("decode_bf16", 256, 32, 128, 128, 1000, torch.bfloat16, seed=5)
 
 
@@ -139,6 +148,50 @@ def chunk_inputs(w: ChunkWorkload, heads: slice | None = None):
         if decay is not None and decay.dim() >= 3:
             decay = sel(decay)
     return q, k, v, decay
+
+
+def unit_rows(x: torch.Tensor) -> torch.Tensor:
+    """Rows of a Gaussian draw scaled to length 1 (uniform on the unit sphere)."""
+    return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+
+
+def delta_inputs(w: ChunkWorkload = DELTA, heads: slice | None = None):
+    """Draw (q, k, v, beta, decay) for a delta-rule workload on the CPU.
+
+    Draw order: q, k, v as one fp32 `randn` each over [B,H,L,d] (q and v
+    times `scale`; k rows scaled to unit length in fp32), then beta as one
+    fp32 `rand` over [B,H,L], then the gate g (gate kinds) as one `randn`;
+    q, k, v are rounded to the workload dtype.
+    """
+    g = torch.Generator().manual_seed(w.seed)
+    shp_k = (w.B, w.H, w.L, w.dk)
+    sc = torch.tensor(w.scale, dtype=torch.float32)
+    q = (torch.randn(shp_k, generator=g) * sc).to(w.dtype)
+    k = unit_rows(torch.randn(shp_k, generator=g)).to(w.dtype)
+    v = (torch.randn((w.B, w.H, w.L, w.dv), generator=g) * sc).to(w.dtype)
+    beta = torch.rand((w.B, w.H, w.L), generator=g)
+    if w.decay_kind in (DECAY_GATE, DECAY_LOG):
+        decay = torch.randn((w.B, w.H, w.L), generator=g)
+    elif w.decay_kind == DECAY_HEAD:
+        decay = retnet_gammas(w.H)
+    else:
+        decay = None
+    if heads is not None:
+        def sel(x):
+            return x.reshape(w.B * w.H, *x.shape[2:])[heads].contiguous()
+        q, k, v, beta = sel(q), sel(k), sel(v), sel(beta)
+        if decay is not None and decay.dim() >= 3:
+            decay = sel(decay)
+    return q, k, v, beta, decay
+
+
+def random_delta_inputs(c: "RandomCase"):
+    """random_inputs with unit-length keys and beta ~ U(0.05, 1) drawn after them."""
+    q, k, v, decay, state = random_inputs(c)
+    g = torch.Generator().manual_seed(c.seed + 1)
+    k = unit_rows(k.float()).to(c.dtype)
+    beta = 0.05 + 0.95 * torch.rand((c.B, c.H, c.L), generator=g)
+    return q, k, v, beta, decay, state
 
 
 def small_fp32_inputs():

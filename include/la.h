@@ -181,6 +181,58 @@ la_status la_decode_step_norm(const void* q, const void* k, const void* v, int d
 const char* la_status_string(int status);
 
 /*
+ * The delta rule (DeltaNet; with a scalar decay, Gated DeltaNet): "Linear /
+ * Sparse Attention - minimal runnable implementation", delta_rule_recurrent,
+ * and the linear/sparse attention tutorial, sections 5.1-5.3, Q15, Q17, Q23.
+ * The pages' value-by-key state S' is stored transposed (S = S'^T, d_k x d_v,
+ * row = key dim, like the linear-attention state), so per head and token
+ *
+ *   S_t = a_t (S_{t-1} - beta_t k_t (k_t^T S_{t-1})) + beta_t k_t v_t^T
+ *   o_t = q_t^T S_t                                   (read after the write)
+ *
+ * Keys are used as given (the pages normalise them before the call; the
+ * update is a contraction for unit keys and 0 <= beta <= 2).  No feature map.
+ *
+ * la_delta_fwd -- the chunkwise form over a [B,H,L] batch.  The chunk's erase
+ * products are folded into a unit lower-triangular solve per chunk (the WY
+ * idea of tutorial section 5.3): a chunk-parallel pass solves every chunk and
+ * writes W = T diag(beta e^b) K and U0 = T diag(beta) V into the workspace,
+ * then a sequential pass per head computes U = U0 - W S_c and the decayed
+ * linear-attention chunk with V replaced by U.  All arithmetic is fp32.
+ *   q, k       : [B,H,L,d_k] (device, read), dtype LA_F32 or LA_BF16
+ *   v          : [B,H,L,d_v] (device, read)
+ *   beta       : [B,H,L] fp32 write strengths (device, read), 4-byte aligned
+ *   C          : chunk length, 16, 32 or 64
+ *   decay_kind : LA_DECAY_NONE, _HEAD, _TOKEN_LOG or _TOKEN_GATE with
+ *                decay_data as for la_chunk_fwd (the per-channel kind is
+ *                LA_ERR_UNSUPPORTED here)
+ *   state      : [B,H,d_k,d_v] fp32 or NULL; in: S_0, out: S_L (NULL: S_0 = 0)
+ *   out        : [B,H,L,d_v] of dtype (device, written)
+ *   workspace  : device scratch of at least la_delta_fwd_workspace_bytes(),
+ *                16-byte aligned, owned by the caller; contents undefined after
+ * Shapes, alignment and errors as for la_chunk_fwd (LA_ERR_NULL for a NULL
+ * beta, LA_ERR_WORKSPACE for a missing or small workspace).  Asynchronous on
+ * `stream`.
+ */
+size_t la_delta_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype);
+la_status la_delta_fwd(const void* q, const void* k, const void* v, const float* beta, int dtype,
+                       int B, int H, int L, int d_k, int d_v, int C, int decay_kind,
+                       const float* decay_data, float* state, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * la_delta_decode_step -- one token of the delta rule for N sequences x H
+ * heads: r = k^T S, S' = a (S - beta k r^T) + beta k v^T, o = q^T S'.
+ *   beta       : [N,H] fp32 (device, read)
+ *   decay_data : NULL | gamma[H] | [N,H] (this step's log a or g)
+ * Every other argument and the errors are those of la_decode_step (phi is
+ * the identity; the per-channel kind is LA_ERR_UNSUPPORTED).
+ */
+la_status la_delta_decode_step(const void* q, const void* k, const void* v, const float* beta,
+                               int dtype, int N, int H, int d_k, int d_v, int decay_kind,
+                               const float* decay_data, float* state, void* out, void* stream);
+
+/*
  * Launch plan of la_chunk_fwd (host only, for tests and benchmarks).
  *   kernel    LA_KERNEL_F32 (fp32 inputs: one workgroup per head and 32-column
  *             tile), LA_KERNEL_STRIP (bf16: 16x16 MFMA, 4-wave column groups,

@@ -231,6 +231,46 @@ def test_channel_decay_workspace_holds_per_channel_totals():
     assert ch - head == r256(P * d * 4) - r256(P * 4)
 
 
+def _delta(**kw):
+    a = dict(q=P16, k=P16, v=P16, beta=P16, dtype=1, B=1, H=1, L=64, dk=64, dv=64, C=64, kind=0,
+             decay=None, state=None, out=P16, ws=P16, ws_bytes=1 << 30)
+    a.update(kw)
+    return la.load().la_delta_fwd(a["q"], a["k"], a["v"], a["beta"], a["dtype"], a["B"], a["H"],
+                                  a["L"], a["dk"], a["dv"], a["C"], a["kind"], a["decay"],
+                                  a["state"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(beta=None), NULL), (dict(out=None), NULL),
+    (dict(kind=3, decay=None), NULL), (dict(B=0), SHAPE), (dict(L=-1), SHAPE),
+    (dict(C=128), UNSUP), (dict(C=48), UNSUP), (dict(dk=48), UNSUP), (dict(kind=4, decay=P16), UNSUP),
+    (dict(dtype=2), UNSUP), (dict(q=P8), ALIGN), (dict(beta=ctypes.c_void_p((1 << 20) + 2)), ALIGN),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS), (dict(ws=P8), ALIGN),
+])
+def test_delta_fwd_rejects(kw, code):
+    assert _delta(**kw) == code
+
+
+def test_delta_zero_length_and_workspace_size():
+    assert _delta(L=0, q=None, k=None, v=None, beta=None, out=None, ws=None) == OK
+    B, H, L, dk, dv = 2, 3, 100, 32, 64
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert la.delta_fwd_workspace_bytes(B, H, L, dk, dv, 64, la.LA_BF16) == \
+        r256(B * H * L * dk * 4) + r256(B * H * L * dv * 4)
+    assert la.delta_fwd_workspace_bytes(B, H, L, dk, dv, 128, la.LA_BF16) == 0
+
+
+def test_delta_decode_rejects():
+    lib = la.load()
+    call = lambda **kw: lib.la_delta_decode_step(  # noqa: E731
+        kw.get("q", P16), P16, P16, kw.get("beta", P16), 1, 2, 2, 64, 64, kw.get("kind", 0),
+        kw.get("decay", None), kw.get("state", P16), P16, None)
+    assert call(beta=None) == NULL
+    assert call(state=None) == NULL
+    assert call(kind=4, decay=P16) == UNSUP
+    assert call(q=P8) == ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 16)

@@ -1,0 +1,162 @@
+"""GPU parity of the delta rule (la_delta_fwd, la_delta_decode_step) against
+the fp64 oracle (`oracle.delta_recurrent`): DeltaNet and Gated DeltaNet,
+S_t = a_t (S_{t-1} - beta_t k_t (k_t^T S_{t-1})) + beta_t k_t v_t^T, o_t = q_t^T S_t
+("Linear / Sparse Attention", delta_rule_recurrent; the tutorial's sections
+5.1-5.3).  Keys have unit length, as the pages normalise them.  Bars as for
+the other paths: 1e-4 (fp32), 1e-2 (bf16 inputs), max|err| / max|ref|."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunkwise_recurrence_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+DEV = torch.device("cuda:0")
+
+
+def _np(t):
+    return None if t is None else t.detach().to("cpu", torch.float64).numpy()
+
+
+def _run(la, c: W.RandomCase, C: int, label: str):
+    q, k, v, beta, decay, S0 = W.random_delta_inputs(c)
+    S0 = S0 if S0 is not None else torch.zeros(c.B, c.H, c.dk, c.dv)
+    print(f"[delta case] {label} B={c.B} H={c.H} L={c.L} dk={c.dk} dv={c.dv} C={C} "
+          f"dtype={c.dtype} decay={c.decay_kind}", flush=True)
+    S = S0.to(DEV).contiguous()
+    out = la.delta_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), C=C,
+                       decay_kind=c.decay_kind,
+                       decay=None if decay is None else decay.to(DEV).contiguous(), state=S)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.delta_recurrent(_np(q), _np(k), _np(v), _np(beta), c.decay_kind,
+                                        _np(decay), _np(S0))
+    tol = TOL[c.dtype]
+    e = (oracle.rel_err(_np(out), ref), oracle.rel_err(_np(S), ref_s))
+    assert e[0] <= tol and e[1] <= tol, f"{label}: out/state rel err {e}"
+    return e
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_delta_variants(gpu_lib, dtype, kind):
+    """Ragged length (3 chunks of 64 and 23 tokens), an initial state, every decay."""
+    c = W.RandomCase(2, 2, 64 * 3 + 23, 64, 64, dtype, W.PHI_IDENTITY, kind, seed=600 + kind,
+                     scale=1.0 / np.sqrt(64), with_state=True)
+    _run(gpu_lib, c, 64, "variants")
+
+
+@pytest.mark.parametrize("dk,dv,C", [(16, 16, 16), (32, 128, 32), (128, 32, 64), (128, 128, 64),
+                                     (64, 32, 16)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_delta_head_dims_and_chunks(gpu_lib, dk, dv, C, dtype):
+    c = W.RandomCase(1, 3, 150, dk, dv, dtype, W.PHI_IDENTITY, W.DECAY_GATE,
+                     seed=dk + dv + C + 61, scale=1.0 / np.sqrt(dk), with_state=True)
+    _run(gpu_lib, c, C, "head dims")
+
+
+def test_delta_chunk_size_invariance(gpu_lib):
+    la = gpu_lib
+    c = W.RandomCase(1, 2, 200, 64, 64, torch.float32, W.PHI_IDENTITY, W.DECAY_LOG, seed=640,
+                     scale=1.0 / np.sqrt(64), with_state=True)
+    q, k, v, beta, decay, S0 = W.random_delta_inputs(c)
+    outs = []
+    for C in (16, 32, 64):
+        S = S0.to(DEV).contiguous()
+        outs.append(_np(la.delta_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), C=C,
+                                     decay_kind=W.DECAY_LOG, decay=decay.to(DEV), state=S)))
+    for o in outs[1:]:
+        assert oracle.rel_err(o, outs[0]) <= 1e-5
+
+
+def test_delta_unit_beta_orthonormal_keys_is_additive(gpu_lib):
+    """Check [e] of the pages on the GPU: orthonormal keys and beta = 1 make the
+    delta rule the additive one (la_chunk_fwd on the same inputs)."""
+    la = gpu_lib
+    d = 64
+    g = torch.Generator().manual_seed(650)
+    Qm, _ = torch.linalg.qr(torch.randn(d, d, generator=g, dtype=torch.float64))
+    k = Qm.T.to(torch.float32).reshape(1, 1, d, d).contiguous()
+    q = torch.randn(1, 1, d, d, generator=g)
+    v = torch.randn(1, 1, d, d, generator=g)
+    od = la.delta_fwd(q.to(DEV), k.to(DEV), v.to(DEV), torch.ones(1, 1, d, device=DEV), C=32)
+    oa = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=32)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(_np(od), _np(oa)) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("kind", [0, 3])
+def test_delta_prefill_then_decode(gpu_lib, dtype, kind):
+    """la_delta_fwd over L tokens, then n decode steps from its state == the recurrence over L + n."""
+    la = gpu_lib
+    L, n = 100, 5
+    c = W.RandomCase(2, 3, L + n, 32, 64, dtype, W.PHI_IDENTITY, kind, seed=660 + kind,
+                     scale=1.0 / np.sqrt(32), with_state=True)
+    q, k, v, beta, d, S0 = W.random_delta_inputs(c)
+    S = S0.to(DEV).contiguous()
+    dd = None if d is None else d.to(DEV)
+    pre = la.delta_fwd(q[:, :, :L].contiguous().to(DEV), k[:, :, :L].contiguous().to(DEV),
+                       v[:, :, :L].contiguous().to(DEV), beta[:, :, :L].contiguous().to(DEV),
+                       C=32, decay_kind=kind,
+                       decay=None if dd is None else dd[:, :, :L].contiguous(), state=S)
+    steps = []
+    for t in range(L, L + n):
+        steps.append(la.delta_decode_step(
+            q[:, :, t].contiguous().to(DEV), k[:, :, t].contiguous().to(DEV),
+            v[:, :, t].contiguous().to(DEV), beta[:, :, t].contiguous().to(DEV), S,
+            decay_kind=kind, decay=None if dd is None else dd[:, :, t].contiguous()))
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.delta_recurrent(_np(q), _np(k), _np(v), _np(beta), kind, _np(d), _np(S0))
+    tol = TOL[dtype]
+    assert oracle.rel_err(_np(pre), ref[:, :, :L]) <= tol
+    got = np.stack([_np(o) for o in steps], axis=2)
+    assert oracle.rel_err(got, ref[:, :, L:]) <= tol
+    assert oracle.rel_err(_np(S), ref_s) <= tol
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 128), (128, 32), (128, 128)])
+def test_delta_decode_head_dims(gpu_lib, dk, dv):
+    la = gpu_lib
+    N, H, T = 5, 3, 4
+    g = torch.Generator().manual_seed(dk * 1000 + dv + 2)
+    S0 = torch.randn(N, H, dk, dv, generator=g) * 0.1
+    S = S0.to(DEV)
+    ref_S = _np(S0)
+    for _ in range(T):
+        q = torch.randn(N, H, dk, generator=g).to(torch.bfloat16)
+        k = W.unit_rows(torch.randn(N, H, dk, generator=g)).to(torch.bfloat16)
+        v = torch.randn(N, H, dv, generator=g).to(torch.bfloat16)
+        beta = torch.rand(N, H, generator=g)
+        gate = torch.randn(N, H, generator=g)
+        o = la.delta_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), S,
+                                 decay_kind=W.DECAY_GATE, decay=gate.to(DEV))
+        torch.cuda.synchronize()
+        ro, ref_S = oracle.delta_decode_step(_np(q), _np(k), _np(v), _np(beta), W.DECAY_GATE,
+                                             _np(gate), ref_S)
+        assert oracle.rel_err(_np(o), ro) < 1e-2
+    assert oracle.rel_err(_np(S), ref_S) < 1e-5  # the state itself stays fp32
+
+
+def test_delta_workload_sampled_heads(gpu_lib):
+    """The full delta_bf16 workload (B=2, H=32, L=16384, d=128, C=64, gated) as the
+    bench launches it; the oracle recomputes three sampled heads."""
+    la = gpu_lib
+    w = W.DELTA
+    print(f"[workload] delta_bf16 B={w.B} H={w.H} L={w.L} d={w.dk} C={w.C}", flush=True)
+    q, k, v, beta, decay = W.delta_inputs(w)
+    S = torch.zeros(w.B, w.H, w.dk, w.dv, device=DEV)
+    out = la.delta_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), C=w.C,
+                       decay_kind=w.decay_kind, decay=decay.to(DEV), state=S)
+    torch.cuda.synchronize()
+    heads = [0, 33, 63]
+    flat = lambda x: x.reshape(w.B * w.H, *x.shape[2:])  # noqa: E731
+    qs, ks, vs, bs, ds = (flat(x)[heads][None] for x in (q, k, v, beta, decay))
+    ref, ref_s = oracle.delta_recurrent(_np(qs), _np(ks), _np(vs), _np(bs), w.decay_kind, _np(ds))
+    got = _np(flat(out.cpu())[heads][None])
+    got_s = _np(flat(S.cpu())[heads][None])
+    e_out, e_s = oracle.rel_err(got, ref), oracle.rel_err(got_s, ref_s)
+    print(f"delta_bf16: sampled heads {heads}: output rel err {e_out:.3e}, state rel err {e_s:.3e}")
+    assert e_out <= 1e-2 and e_s <= 1e-2
