@@ -19,12 +19,13 @@
 //   O_c = diag(e^b) Q S_c + ((Q K^T) o tril(G)) U
 //   S_{c+1} = e^{b_last} S_c + (diag(e^{b_last - b}) K)^T U
 //
-// Two kernels: delta_prep_kernel (one workgroup per head and chunk) solves
-// each chunk's system by forward substitution and writes W and U0 to the
-// workspace in fp32; delta_chunk_kernel (one workgroup per head and 32 value
-// columns -- the columns of S are independent under this update) walks the
-// chunks in order with its part of S in LDS.  Both keep their tiles in LDS
-// as fp32 and use plain FMA.
+// Two passes: delta_prep_kernel (one workgroup per head and chunk) solves
+// each chunk's system and writes W and U0 to the workspace; then one
+// workgroup per head and 32 value columns (the columns of S are independent
+// under this update) walks the chunks in order: delta_chunk_mfma_kernel for
+// bf16 inputs with C = 64 (bf16 MFMA operands, fp32 accumulation, the state
+// in accumulators), delta_chunk_kernel otherwise (fp32 tiles in LDS, plain
+// FMA, no bf16 rounding anywhere).
 #include "la_device.h"
 
 namespace la {
@@ -57,7 +58,56 @@ __device__ void chunk_log_prefix(const DeltaArgs& a, int bh, int h, int t0, int 
   }
 }
 
-template <bool BF16, int DK>
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transpose read of a row-major bf16 LDS tile with a row stride of `stride`
+// elements: lane i of each 16-lane group receives column col0 + i of rows
+// k0 .. k0 + 7 (two ds_read_b64_tr_b16, each source lane addressing 4 columns
+// of one row).  The 8 values are the k-run of an MFMA operand lane.  Every
+// lane of the wave must take part.
+__device__ __forceinline__ u32x4 lds_tr8(const uint16_t* base, int stride, int k0, int col0,
+                                         int l16) {
+  const int j = l16 >> 2, m = l16 & 3;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + (k0 + j) * stride + col0 + 4 * m));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + (k0 + 4 + j) * stride + col0 + 4 * m));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// log a_t of token t (0 past the sequence)
+__device__ __forceinline__ float token_log(const DeltaArgs& a, float lg, const float* dt, int t) {
+  if (a.decay_kind == kDecayHead) return lg;
+  if (dt) return token_log_decay(a.decay_kind, dt[t]);
+  return 0.0f;
+}
+
+// Inclusive prefix of log a over the chunk's tokens by wave 0 (C <= 64):
+// lane t holds token t0 + t; tokens past the sequence add nothing, so
+// sb[t] for t >= n repeats b_last.
+__device__ __forceinline__ void chunk_log_prefix_wave(const DeltaArgs& a, int bh, int h, int t0,
+                                                      int n, float* sb) {
+  const int lane = threadIdx.x & 63;
+  const float lg = a.decay_kind == kDecayHead ? logf(a.decay[h]) : 0.0f;
+  const float* dt = (a.decay_kind == kDecayLog || a.decay_kind == kDecayGate)
+                        ? a.decay + (size_t)bh * a.L + t0 : nullptr;
+  float x = lane < n ? token_log(a, lg, dt, lane) : 0.0f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane < a.C) sb[lane] = x;
+}
+
+// One workgroup per (head, chunk): T = (I + N)^-1 with
+// N = diag(beta) (tril(K K^T, -1) o G) by 16 x 16 blocks (diagonal blocks by
+// forward substitution, all at once; then block rows I = 1.. with
+// T_IJ = -T_II sum_{J <= M < I} N_IM T_MJ), then W = T diag(beta e^b) K and
+// U0 = T diag(beta) V.  W goes out as fp32 or (for the MFMA chunk pass) bf16.
+template <bool BF16, int DK, bool WBF16>
 __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a) {
   constexpr int KP = DK + 1;  // padded row stride (fp32 words)
   const int tid = threadIdx.x;
@@ -66,11 +116,13 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a) {
   const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
   const int h = bh % a.H;
   const int t0 = c * C, n = min(C, L - t0);
+  const int NB = C / 16;  // 16 x 16 blocks per side
 
   __shared__ float sK[kDeltaMaxC * KP];
   __shared__ float sV[kDeltaMaxC * (128 + 1)];
   __shared__ float sN[kDeltaMaxC][kDeltaMaxC + 1];
   __shared__ float sT[kDeltaMaxC][kDeltaMaxC + 1];
+  __shared__ float sX[3 * 16][17];
   __shared__ float sb[kDeltaMaxC], sbeta[kDeltaMaxC];
   const int VP = DV + 1;
 
@@ -79,15 +131,16 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a) {
     sK[(idx / DK) * KP + idx % DK] = ld<BF16>(a.k, rowk * DK + idx);
   for (int idx = tid; idx < n * DV; idx += 256)
     sV[(idx / DV) * VP + idx % DV] = ld<BF16>(a.v, rowk * DV + idx);
-  if (tid < n) sbeta[tid] = a.beta[rowk + tid];
-  if (tid == 0) chunk_log_prefix(a, bh, h, t0, n, sb);
+  if (tid < C) sbeta[tid] = tid < n ? a.beta[rowk + tid] : 0.0f;
+  if (tid < 64) chunk_log_prefix_wave(a, bh, h, t0, n, sb);
+  for (int idx = tid; idx < C * C; idx += 256) sT[idx / C][idx % C] = 0.0f;
   __syncthreads();
 
-  // N[i][j] = beta_i (k_i . k_j) e^{b_i - b_j} below the diagonal
-  for (int idx = tid; idx < n * n; idx += 256) {
-    const int i = idx / n, j = idx % n;
+  // N[i][j] = beta_i (k_i . k_j) e^{b_i - b_j} below the diagonal (0 past the sequence)
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int i = idx / C, j = idx % C;
     float x = 0.0f;
-    if (j < i) {
+    if (j < i && i < n) {
       float dot = 0.0f;
       for (int d = 0; d < DK; ++d) dot = fmaf(sK[i * KP + d], sK[j * KP + d], dot);
       x = sbeta[i] * dot * expf(sb[i] - sb[j]);
@@ -95,34 +148,79 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a) {
     sN[i][j] = x;
   }
   __syncthreads();
-  // T = (I + N)^-1 by rows: T[i][j] = [i == j] - sum_{j <= m < i} N[i][m] T[m][j]
-  for (int i = 0; i < n; ++i) {
-    if (tid < n) {
-      const int j = tid;
-      float x = j == i ? 1.0f : 0.0f;
+  // diagonal blocks: T[i][j] = [i == j] - sum_{j <= m < i} N[i][m] T[m][j] inside each block
+  for (int i = 0; i < 16; ++i) {
+    if (tid < 16 * NB) {
+      const int q0 = 16 * (tid >> 4), j = tid & 15;
+      float x = i == j ? 1.0f : 0.0f;
       if (j < i) {
-        float s = 0.0f;
-        for (int m = j; m < i; ++m) s = fmaf(sN[i][m], sT[m][j], s);
-        x = -s;
+        float s2 = 0.0f;
+        for (int m = j; m < i; ++m) s2 = fmaf(sN[q0 + i][q0 + m], sT[q0 + m][q0 + j], s2);
+        x = -s2;
       }
-      sT[i][j] = x;
+      sT[q0 + i][q0 + j] = x;
     }
     __syncthreads();
   }
-  // W = T diag(beta e^b) K, U0 = T diag(beta) V  (T is lower triangular)
-  float* wW = a.ws_W + rowk * DK;
-  float* wU = a.ws_U + rowk * DV;
+  // block rows below: X_J = sum_{J <= M < I} N_IM T_MJ, then T_IJ = -T_II X_J
+  for (int I = 1; I < NB; ++I) {
+    for (int idx = tid; idx < I * 256; idx += 256) {
+      const int J = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+      float x = 0.0f;
+      for (int m = 16 * J; m < 16 * I; ++m) x = fmaf(sN[16 * I + r][m], sT[m][16 * J + cc], x);
+      sX[16 * J + r][cc] = x;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < I * 256; idx += 256) {
+      const int J = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+      float x = 0.0f;
+      for (int m = 0; m < 16; ++m) x = fmaf(sT[16 * I + r][16 * I + m], sX[16 * J + m][cc], x);
+      sT[16 * I + r][16 * J + cc] = -x;
+    }
+    __syncthreads();
+  }
+  // scale the rows once: K row m by beta_m e^{b_m}, V row m by beta_m
   for (int idx = tid; idx < n * DK; idx += 256) {
-    const int i = idx / DK, d = idx % DK;
-    float s = 0.0f;
-    for (int m = 0; m <= i; ++m) s = fmaf(sT[i][m] * sbeta[m] * expf(sb[m]), sK[m * KP + d], s);
-    wW[idx] = s;
+    const int m = idx / DK;
+    sK[m * KP + idx % DK] *= sbeta[m] * expf(sb[m]);
   }
   for (int idx = tid; idx < n * DV; idx += 256) {
-    const int i = idx / DV, cc = idx % DV;
-    float s = 0.0f;
-    for (int m = 0; m <= i; ++m) s = fmaf(sT[i][m] * sbeta[m], sV[m * VP + cc], s);
-    wU[idx] = s;
+    const int m = idx / DV;
+    sV[m * VP + idx % DV] *= sbeta[m];
+  }
+  __syncthreads();
+  // W = T K~, U0 = T V~, four adjacent columns per thread
+  for (int idx = tid; idx < n * (DK / 4); idx += 256) {
+    const int i = idx / (DK / 4), d0 = 4 * (idx % (DK / 4));
+    float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+    for (int m = 0; m <= i; ++m) {
+      const float t = sT[i][m];
+      const float* kr = &sK[m * KP + d0];
+      x0 = fmaf(t, kr[0], x0);
+      x1 = fmaf(t, kr[1], x1);
+      x2 = fmaf(t, kr[2], x2);
+      x3 = fmaf(t, kr[3], x3);
+    }
+    const size_t o = (rowk + i) * DK + d0;
+    if constexpr (WBF16) {
+      uint16_t* w = reinterpret_cast<uint16_t*>(a.ws_W);
+      *reinterpret_cast<uint2*>(w + o) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+    } else {
+      *reinterpret_cast<float4*>(a.ws_W + o) = make_float4(x0, x1, x2, x3);
+    }
+  }
+  for (int idx = tid; idx < n * (DV / 4); idx += 256) {
+    const int i = idx / (DV / 4), c0 = 4 * (idx % (DV / 4));
+    float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+    for (int m = 0; m <= i; ++m) {
+      const float t = sT[i][m];
+      const float* vr = &sV[m * VP + c0];
+      x0 = fmaf(t, vr[0], x0);
+      x1 = fmaf(t, vr[1], x1);
+      x2 = fmaf(t, vr[2], x2);
+      x3 = fmaf(t, vr[3], x3);
+    }
+    *reinterpret_cast<float4*>(a.ws_U + (rowk + i) * DV + c0) = make_float4(x0, x1, x2, x3);
   }
 }
 
@@ -141,7 +239,7 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
   __shared__ float sU[kDeltaMaxC][TV + 1];
   __shared__ float sS[DK][TV + 1];
   __shared__ float sP[kDeltaMaxC][kDeltaMaxC + 1];
-  __shared__ float sb[kDeltaMaxC];
+  __shared__ float sb[kDeltaMaxC], swt[kDeltaMaxC];
 
   for (int idx = tid; idx < DK * tv; idx += 256) {
     const int d = idx / tv, cc = idx % tv;
@@ -163,7 +261,9 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
     }
     if (tid == 0) chunk_log_prefix(a, bh, h, t0, n, sb);
     __syncthreads();
-    // U = U0 - W S (each thread its own elements), scores P = (Q K^T) o tril(G)
+    // U = U0 - W S (each thread its own elements), scores P = (Q K^T) o tril(G),
+    // update weights e^{b_last - b_j}
+    if (tid < n) swt[tid] = expf(sb[n - 1] - sb[tid]);
     for (int idx = tid; idx < n * tv; idx += 256) {
       const int i = idx / tv, cc = idx % tv;
       float s = sU[i][cc];
@@ -195,7 +295,7 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
     for (int idx = tid; idx < DK * tv; idx += 256) {
       const int d = idx / tv, cc = idx % tv;
       float s = 0.0f;
-      for (int j = 0; j < n; ++j) s = fmaf(expf(bL - sb[j]) * sK[j * KP + d], sU[j][cc], s);
+      for (int j = 0; j < n; ++j) s = fmaf(swt[j] * sK[j * KP + d], sU[j][cc], s);
       sS[d][cc] = fmaf(expf(bL), sS[d][cc], s);
     }
   }
@@ -208,14 +308,437 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
   }
 }
 
+// The solve pass for bf16 inputs with C = 64 (the MFMA path): one workgroup
+// of 4 waves per (head, chunk).
+//   * G = K K^T on v_mfma_f32_16x16x32_bf16 (exact products of the bf16
+//     inputs, fp32 sums), N = diag(beta) (tril(G, -1) o e^{b_i - b_j}) in LDS.
+//   * T = (I + N)^-1: wave w inverts diagonal block w by forward substitution
+//     with its 16 columns in registers (lane j holds column j, no barriers);
+//     the blocks below the diagonal follow block row by block row,
+//     T_IJ = -T_II sum_{J <= M < I} N_IM T_MJ.
+//   * W = (T diag(beta e^b)) K and U0 = (T diag(beta)) V on MFMA, with the
+//     fp32 left factor split into a bf16 high part and a bf16 remainder (two
+//     MFMAs, ~16 significant bits); W leaves as bf16, U0 as fp32.
+template <int DK>
+__global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a) {
+  constexpr int C = 64, QS = DK + 8, CS = C + 8, KST = DK / 32, NCH = DK / 8;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int L = a.L, DV = a.DV;
+  const int nch = (L + C - 1) / C;
+  const int bh = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int h = bh % a.H;
+  const int t0 = c * C, n = min(C, L - t0);
+
+  constexpr int VS = 128 + 8;  // row stride of the V tile (d_v <= 128)
+  __shared__ __align__(16) uint16_t sK[C * QS];
+  __shared__ __align__(16) uint16_t sV[C * VS];
+  __shared__ __align__(16) uint16_t sTh[C * CS], sTl[C * CS];
+  __shared__ float sN[C][C + 1], sT[C][C + 1];
+  __shared__ float sX[3 * 16][17];
+  __shared__ float sb[C], sbeta[C];
+
+  const size_t rowk = (size_t)bh * L + t0;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k) + rowk * DK;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v) + rowk * DV;
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  for (int idx = tid; idx < C * NCH; idx += 256) {
+    const int row = idx / NCH, ch = idx % NCH;
+    const u32x4 x = row < n ? *reinterpret_cast<const u32x4*>(kc + (size_t)row * DK + 8 * ch) : zero4;
+    *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = x;
+  }
+  const int VCH = DV / 8;
+  for (int idx = tid; idx < C * VCH; idx += 256) {
+    const int row = idx / VCH, ch = idx % VCH;
+    const u32x4 x = row < n ? *reinterpret_cast<const u32x4*>(vc + (size_t)row * DV + 8 * ch) : zero4;
+    *reinterpret_cast<u32x4*>(&sV[row * VS + 8 * ch]) = x;
+  }
+  if (tid < C) sbeta[tid] = tid < n ? a.beta[rowk + tid] : 0.0f;
+  if (w == 0) chunk_log_prefix_wave(a, bh, h, t0, n, sb);
+  for (int idx = tid; idx < C * C; idx += 256) sT[idx / C][idx % C] = 0.0f;
+  __syncthreads();
+
+  // N: wave w, query rows 16w .. 16w + 15, key tiles jt <= w
+  for (int jt = 0; jt <= w; ++jt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KST; ++s) {
+      const u32x4 ai = *reinterpret_cast<const u32x4*>(&sK[(16 * w + l16) * QS + 32 * s + 8 * g4]);
+      const u32x4 bj = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
+      acc = mfma16x16x32(ai, bj, acc);
+    }
+    const int j = 16 * jt + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * g4 + r;
+      sN[i][j] = (j < i && i < n) ? sbeta[i] * acc[r] * expf(sb[i] - sb[j]) : 0.0f;
+    }
+  }
+  __syncthreads();
+  // diagonal block w: lane j < 16 carries column j of the block
+  if (lane < 16) {
+    const int q0 = 16 * w, j = lane;
+    float tc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float sacc = 0.0f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) sacc = fmaf(sN[q0 + i][q0 + m], tc[m], sacc);
+      tc[i] = i == j ? 1.0f : (j < i ? -sacc : 0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[q0 + i][q0 + j] = tc[i];
+  }
+  __syncthreads();
+  for (int I = 1; I < C / 16; ++I) {
+    // 16-term groups unrolled so that their LDS reads are in flight together
+    for (int idx = tid; idx < I * 256; idx += 256) {
+      const int J = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+      float x = 0.0f;
+      for (int mb = 16 * J; mb < 16 * I; mb += 16) {
+#pragma unroll
+        for (int mm = 0; mm < 16; ++mm) x = fmaf(sN[16 * I + r][mb + mm], sT[mb + mm][16 * J + cc], x);
+      }
+      sX[16 * J + r][cc] = x;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < I * 256; idx += 256) {
+      const int J = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+      float x = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) x = fmaf(sT[16 * I + r][16 * I + m], sX[16 * J + m][cc], x);
+      sT[16 * I + r][16 * J + cc] = -x;
+    }
+    __syncthreads();
+  }
+  // left factor (T diag(f)) as bf16 high + remainder, row-major [C][CS]
+  auto split = [&](bool with_decay) {
+    for (int idx = tid; idx < C * C / 2; idx += 256) {
+      const int i = idx / (C / 2), m = 2 * (idx % (C / 2));
+      float x0 = sT[i][m] * sbeta[m], x1 = sT[i][m + 1] * sbeta[m + 1];
+      if (with_decay) {
+        x0 *= expf(sb[m]);
+        x1 *= expf(sb[m + 1]);
+      }
+      const uint32_t hi = pack_bf16x2(x0, x1);
+      const float r0 = x0 - bf16_to_f32(hi & 0xffffu), r1 = x1 - bf16_to_f32(hi >> 16);
+      *reinterpret_cast<uint32_t*>(&sTh[i * CS + m]) = hi;
+      *reinterpret_cast<uint32_t*>(&sTl[i * CS + m]) = pack_bf16x2(r0, r1);
+    }
+  };
+  split(true);
+  __syncthreads();
+  // W = (T diag(beta e^b)) K: wave w, rows 16w .., every 16-column tile of the keys
+  uint16_t* wo = reinterpret_cast<uint16_t*>(a.ws_W) + rowk * DK;
+  for (int nt = 0; nt < DK / 16; ++nt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C / 32; ++s) {
+      const int ao = (16 * w + l16) * CS + 32 * s + 8 * g4;
+      const u32x4 bk = lds_tr8(sK, QS, 32 * s + 8 * g4, 16 * nt, l16);
+      acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(&sTh[ao]), bk, acc);
+      acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(&sTl[ao]), bk, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * g4 + r;
+      if (i < n) wo[(size_t)i * DK + 16 * nt + l16] = (uint16_t)f32_to_bf16(acc[r]);
+    }
+  }
+  __syncthreads();
+  split(false);
+  __syncthreads();
+  // U0 = (T diag(beta)) V
+  float* uo = a.ws_U + rowk * DV;
+  for (int nt = 0; nt < DV / 16; ++nt) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C / 32; ++s) {
+      const int ao = (16 * w + l16) * CS + 32 * s + 8 * g4;
+      const u32x4 bv = lds_tr8(sV, VS, 32 * s + 8 * g4, 16 * nt, l16);
+      acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(&sTh[ao]), bv, acc);
+      acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(&sTl[ao]), bv, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * w + 4 * g4 + r;
+      if (i < n) uo[(size_t)i * DV + 16 * nt + l16] = acc[r];
+    }
+  }
+}
+
+// The sequential pass for bf16 inputs on v_mfma_f32_16x16x32_bf16: one
+// workgroup of 4 waves per (head, 32 value columns), C = 64.  Wave w owns the
+// chunk's query rows 16w .. 16w + 15 and the state rows (keys) of 16-row
+// tiles w, w + 4, ...; the state tile lives in its fp32 accumulators, with a
+// bf16 copy S^T in LDS (double-buffered by chunk parity) as the B operand of
+// W S and Q S.  Per chunk:
+//   (1) U = U0 - W S for the wave's rows -> U^T and (e^{b_last - b} U)^T in
+//       LDS (bf16); the scores P^T = K Q^T of the wave's query columns,
+//       masked and decayed -> P in LDS (bf16);
+//   (2) O = diag(e^b) Q S + P U for the wave's rows -> HBM; the state update
+//       S = e^{b_last} S + K^T (e^{b_last - b} U), the K^T operand read from
+//       the row-major K tile with transpose reads; the new S^T to the other
+//       LDS buffer.
+// The next chunk's q, k, W and U0 are loaded into registers while the
+// current one computes.
+template <int DK>
+__global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a) {
+  constexpr int C = 64, TV = 32;
+  constexpr int QS = DK + 8;        // bf16 row stride of the Q, K, W tiles and of S^T
+  constexpr int CS = C + 8;         // bf16 row stride of K^T, P, U^T
+  constexpr int KST = DK / 32;      // 32-wide k-steps over the keys
+  constexpr int NMT = DK / 16;      // 16-row tiles of the state
+  constexpr int MTW = (NMT + 3) / 4;
+  constexpr int NCH = DK / 8;       // 16-byte pieces of one Q/K/W row
+  constexpr int PER = C * NCH / 256;
+  static_assert(PER >= 1 && C * NCH % 256 == 0, "tile pieces per thread");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int bh = blockIdx.x / a.n_v, vt = blockIdx.x % a.n_v;
+  const int h = bh % a.H;
+  const int L = a.L, DV = a.DV;
+  const int dv0 = vt * TV;
+  const int nch = (L + C - 1) / C;
+
+  __shared__ __align__(16) uint16_t sQ[C * QS], sK[C * QS], sW[C * QS];
+  __shared__ __align__(16) uint16_t sST[2][TV * QS];
+  __shared__ __align__(16) uint16_t sUT[TV * CS], sUwT[TV * CS], sP[C * CS];
+  __shared__ float sb[C];
+
+  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * L * DK;
+  const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
+  const uint16_t* wh = reinterpret_cast<const uint16_t*>(a.ws_W) + (size_t)bh * L * DK;
+  const float* uh = a.ws_U + (size_t)bh * L * DV + dv0;
+  uint16_t* oh = static_cast<uint16_t*>(a.out) + (size_t)bh * L * DV + dv0;
+
+  // ---- register prefetch of one chunk: q, k, W rows and this lane's U0 ----
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  u32x4 rq[PER], rk[PER], rw[PER];
+  float ru[2][4];
+  auto fetch = [&](int c) {
+    const int t0 = c * C, n = min(C, L - t0);
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
+      if (row < n) {
+        const size_t off = (size_t)(t0 + row) * DK + 8 * ch;
+        rq[p] = *reinterpret_cast<const u32x4*>(qh + off);
+        rk[p] = *reinterpret_cast<const u32x4*>(kh + off);
+        rw[p] = *reinterpret_cast<const u32x4*>(wh + off);
+      } else {
+        rq[p] = zero4;
+        rk[p] = zero4;
+        rw[p] = zero4;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * g4 + r;
+        ru[nt][r] = i < n ? uh[(size_t)(t0 + i) * DV + 16 * nt + l16] : 0.0f;
+      }
+  };
+
+  // ---- the state: own tiles (mt = w + 4 m, nt), lane rows 16 mt + 4 g4 + r, column 16 nt + l16
+  f32x4 accS[MTW][2];
+  auto put_state = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      const int mt = w + 4 * m;
+      if (mt < NMT) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          *reinterpret_cast<uint2*>(&sST[buf][(16 * nt + l16) * QS + 16 * mt + 4 * g4]) =
+              make_uint2(pack_bf16x2(accS[m][nt][0], accS[m][nt][1]),
+                         pack_bf16x2(accS[m][nt][2], accS[m][nt][3]));
+      }
+    }
+  };
+#pragma unroll
+  for (int m = 0; m < MTW; ++m)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mt = w + 4 * m, d = 16 * mt + 4 * g4 + r;
+        accS[m][nt][r] = (a.state && mt < NMT)
+                             ? a.state[((size_t)bh * DK + d) * DV + dv0 + 16 * nt + l16]
+                             : 0.0f;
+      }
+  put_state(0);
+  if (nch > 0) fetch(0);
+
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * C, n = min(C, L - t0);
+    const int sp = c & 1;
+    __syncthreads();  // the previous chunk is done with every tile; S^T[sp] is complete
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
+      *reinterpret_cast<u32x4*>(&sQ[row * QS + 8 * ch]) = rq[p];
+      *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = rk[p];
+      *reinterpret_cast<u32x4*>(&sW[row * QS + 8 * ch]) = rw[p];
+    }
+    if (w == 0) chunk_log_prefix_wave(a, bh, h, t0, n, sb);
+    float u0[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u0[nt][r] = ru[nt][r];
+    if (c + 1 < nch) fetch(c + 1);
+    __syncthreads();  // the chunk's tiles and prefixes are in LDS
+    const float bL = sb[n - 1];
+    const uint16_t* st = sST[sp];
+
+    // (1a) U = U0 - W S for rows 16w .. 16w + 15
+    {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < KST; ++s) {
+        const u32x4 aw = *reinterpret_cast<const u32x4*>(&sW[(16 * w + l16) * QS + 32 * s + 8 * g4]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
+          acc[nt] = mfma16x16x32(aw, bs, acc[nt]);
+        }
+      }
+      const int i0 = 16 * w + 4 * g4;
+      float wt[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wt[r] = i0 + r < n ? expf(bL - sb[i0 + r]) : 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = u0[nt][r] - acc[nt][r];
+        const int o = (16 * nt + l16) * CS + i0;
+        *reinterpret_cast<uint2*>(&sUT[o]) = make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
+        *reinterpret_cast<uint2*>(&sUwT[o]) = make_uint2(pack_bf16x2(u[0] * wt[0], u[1] * wt[1]),
+                                                         pack_bf16x2(u[2] * wt[2], u[3] * wt[3]));
+      }
+    }
+    // (1b) P^T tiles of query columns 16w .. 16w + 15: token rows 16 jt + 4 g4 + r
+    {
+      const int i = 16 * w + l16;
+      const float bi = sb[i];
+#pragma unroll
+      for (int jt = 0; jt < C / 16; ++jt) {
+        float pv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (jt <= w) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KST; ++s) {
+            const u32x4 ak = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
+            const u32x4 bq = *reinterpret_cast<const u32x4*>(&sQ[i * QS + 32 * s + 8 * g4]);
+            acc = mfma16x16x32(ak, bq, acc);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jt + 4 * g4 + r;
+            pv[r] = j <= i ? acc[r] * expf(bi - sb[j]) : 0.0f;
+          }
+        }
+        *reinterpret_cast<uint2*>(&sP[i * CS + 16 * jt + 4 * g4]) =
+            make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+      }
+    }
+    __syncthreads();  // U^T, (wU)^T and P complete
+
+    // (2a) O = diag(e^b) Q S + P U for rows 16w .. 16w + 15
+    {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < KST; ++s) {
+        const u32x4 aq = *reinterpret_cast<const u32x4*>(&sQ[(16 * w + l16) * QS + 32 * s + 8 * g4]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
+          acc[nt] = mfma16x16x32(aq, bs, acc[nt]);
+        }
+      }
+      const int i0 = 16 * w + 4 * g4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = expf(sb[i0 + r]);
+        acc[0][r] *= e;
+        acc[1][r] *= e;
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < C / 32; ++s2) {
+        const u32x4 ap = *reinterpret_cast<const u32x4*>(&sP[(16 * w + l16) * CS + 32 * s2 + 8 * g4]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
+          acc[nt] = mfma16x16x32(ap, bu, acc[nt]);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (i0 + r < n)
+            oh[(size_t)(t0 + i0 + r) * DV + 16 * nt + l16] = (uint16_t)f32_to_bf16(acc[nt][r]);
+    }
+    // (2b) S = e^{b_last} S + K^T (e^{b_last - b} U) for the wave's state tiles
+    {
+      const float eL = expf(bL);
+#pragma unroll
+      for (int m = 0; m < MTW; ++m) {
+        const int mt = w + 4 * m;
+        if (mt < NMT) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            f32x4 acc = accS[m][nt] * eL;
+#pragma unroll
+            for (int s2 = 0; s2 < C / 32; ++s2) {
+              const u32x4 ak = lds_tr8(sK, QS, 32 * s2 + 8 * g4, 16 * mt, l16);
+              const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUwT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
+              acc = mfma16x16x32(ak, bu, acc);
+            }
+            accS[m][nt] = acc;
+          }
+        }
+      }
+      put_state(sp ^ 1);
+    }
+  }
+  if (a.state) {
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      const int mt = w + 4 * m;
+      if (mt < NMT) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            a.state[((size_t)bh * DK + 16 * mt + 4 * g4 + r) * DV + dv0 + 16 * nt + l16] = accS[m][nt][r];
+      }
+    }
+  }
+}
+
 template <bool BF16>
 hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
   const int nch = (a.L + a.C - 1) / a.C;
   const dim3 gp(a.B * a.H * nch), gc(a.B * a.H * a.n_v), blk(256);
+  // bf16 inputs, C = 64, d_k >= 32 and whole 32-column value tiles: the MFMA pass
+  const bool mfma = BF16 && a.C == 64 && a.DK >= 32 && a.DV % 32 == 0;
   switch (a.DK) {
 #define LA_DK(D)                                                                  \
   case D:                                                                         \
-    hipLaunchKernelGGL((delta_prep_kernel<BF16, D>), gp, blk, 0, s, a);           \
+    if constexpr (BF16 && D >= 32) {                                              \
+      if (mfma) {                                                                 \
+        hipLaunchKernelGGL((delta_prep_mfma_kernel<D>), gp, blk, 0, s, a);        \
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;        \
+        hipLaunchKernelGGL((delta_chunk_mfma_kernel<D>), gc, blk, 0, s, a);       \
+        return hipGetLastError();                                                 \
+      }                                                                           \
+    }                                                                             \
+    hipLaunchKernelGGL((delta_prep_kernel<BF16, D, false>), gp, blk, 0, s, a);    \
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;            \
     hipLaunchKernelGGL((delta_chunk_kernel<BF16, D>), gc, blk, 0, s, a);          \
     return hipGetLastError();
