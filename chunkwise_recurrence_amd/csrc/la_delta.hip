@@ -58,6 +58,27 @@ __device__ void chunk_log_prefix(const DeltaArgs& a, int bh, int h, int t0, int 
   }
 }
 
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS
+// accesses complete (lgkmcnt(0)), then s_barrier.  No memory fence, so global
+// loads and stores in flight stay in flight (__syncthreads would wait for
+// them).  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Two fp32 values to packed bf16 (round to nearest even) with the hardware
+// conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -94,6 +115,26 @@ __device__ __forceinline__ void chunk_log_prefix_wave(const DeltaArgs& a, int bh
   const float* dt = (a.decay_kind == kDecayLog || a.decay_kind == kDecayGate)
                         ? a.decay + (size_t)bh * a.L + t0 : nullptr;
   float x = lane < n ? token_log(a, lg, dt, lane) : 0.0f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane < a.C) sb[lane] = x;
+}
+
+// The same prefix from decay data already in a register: lane t of wave 0
+// holds the raw value of token t0 + t (gamma's log for the per-head kind).
+// In log2 units (b log2(e)), so that every factor is one v_exp_f32.
+__device__ __forceinline__ void chunk_log_prefix_reg(const DeltaArgs& a, float raw, int n, float* sb) {
+  const int lane = threadIdx.x & 63;
+  constexpr float kLog2e = 1.4426950408889634f;
+  float x = 0.0f;
+  if (lane < n) {
+    if (a.decay_kind == kDecayHead) x = raw * kLog2e;
+    else if (a.decay_kind == kDecayLog || a.decay_kind == kDecayGate)
+      x = token_log_decay(a.decay_kind, raw) * kLog2e;
+  }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const float y = __shfl_up(x, off, 64);
@@ -334,8 +375,13 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   constexpr int VS = 128 + 8;  // row stride of the V tile (d_v <= 128)
   __shared__ __align__(16) uint16_t sK[C * QS];
   __shared__ __align__(16) uint16_t sV[C * VS];
-  __shared__ __align__(16) uint16_t sTh[C * CS], sTl[C * CS];
-  __shared__ float sN[C][C + 1], sT[C][C + 1];
+  // N (fp32) is dead once T is known; its space then holds the split factor
+  constexpr int NS = CS;  // row stride of N in fp32 words (C + 8)
+  __shared__ __align__(16) float sNT[C * NS];
+  float (*sN)[NS] = reinterpret_cast<float (*)[NS]>(sNT);
+  uint16_t* sTh = reinterpret_cast<uint16_t*>(sNT);
+  uint16_t* sTl = sTh + C * CS;
+  __shared__ float sT[C][C + 1];
   __shared__ float sX[3 * 16][17];
   __shared__ float sb[C], sbeta[C];
 
@@ -357,7 +403,7 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   if (tid < C) sbeta[tid] = tid < n ? a.beta[rowk + tid] : 0.0f;
   if (w == 0) chunk_log_prefix_wave(a, bh, h, t0, n, sb);
   for (int idx = tid; idx < C * C; idx += 256) sT[idx / C][idx % C] = 0.0f;
-  __syncthreads();
+  lds_barrier();
 
   // N: wave w, query rows 16w .. 16w + 15, key tiles jt <= w
   for (int jt = 0; jt <= w; ++jt) {
@@ -375,7 +421,7 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
       sN[i][j] = (j < i && i < n) ? sbeta[i] * acc[r] * expf(sb[i] - sb[j]) : 0.0f;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // diagonal block w: lane j < 16 carries column j of the block
   if (lane < 16) {
     const int q0 = 16 * w, j = lane;
@@ -390,7 +436,7 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 #pragma unroll
     for (int i = 0; i < 16; ++i) sT[q0 + i][q0 + j] = tc[i];
   }
-  __syncthreads();
+  lds_barrier();
   for (int I = 1; I < C / 16; ++I) {
     // 16-term groups unrolled so that their LDS reads are in flight together
     for (int idx = tid; idx < I * 256; idx += 256) {
@@ -402,7 +448,7 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
       }
       sX[16 * J + r][cc] = x;
     }
-    __syncthreads();
+    lds_barrier();
     for (int idx = tid; idx < I * 256; idx += 256) {
       const int J = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
       float x = 0.0f;
@@ -410,7 +456,7 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
       for (int m = 0; m < 16; ++m) x = fmaf(sT[16 * I + r][16 * I + m], sX[16 * J + m][cc], x);
       sT[16 * I + r][16 * J + cc] = -x;
     }
-    __syncthreads();
+    lds_barrier();
   }
   // left factor (T diag(f)) as bf16 high + remainder, row-major [C][CS]
   auto split = [&](bool with_decay) {
@@ -421,14 +467,14 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
         x0 *= expf(sb[m]);
         x1 *= expf(sb[m + 1]);
       }
-      const uint32_t hi = pack_bf16x2(x0, x1);
+      const uint32_t hi = cvt2(x0, x1);
       const float r0 = x0 - bf16_to_f32(hi & 0xffffu), r1 = x1 - bf16_to_f32(hi >> 16);
       *reinterpret_cast<uint32_t*>(&sTh[i * CS + m]) = hi;
-      *reinterpret_cast<uint32_t*>(&sTl[i * CS + m]) = pack_bf16x2(r0, r1);
+      *reinterpret_cast<uint32_t*>(&sTl[i * CS + m]) = cvt2(r0, r1);
     }
   };
   split(true);
-  __syncthreads();
+  lds_barrier();
   // W = (T diag(beta e^b)) K: wave w, rows 16w .., every 16-column tile of the keys
   uint16_t* wo = reinterpret_cast<uint16_t*>(a.ws_W) + rowk * DK;
   for (int nt = 0; nt < DK / 16; ++nt) {
@@ -443,12 +489,12 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * w + 4 * g4 + r;
-      if (i < n) wo[(size_t)i * DK + 16 * nt + l16] = (uint16_t)f32_to_bf16(acc[r]);
+      if (i < n) wo[(size_t)i * DK + 16 * nt + l16] = (uint16_t)(cvt2(acc[r], 0.0f) & 0xffffu);
     }
   }
-  __syncthreads();
+  lds_barrier();
   split(false);
-  __syncthreads();
+  lds_barrier();
   // U0 = (T diag(beta)) V
   float* uo = a.ws_U + rowk * DV;
   for (int nt = 0; nt < DV / 16; ++nt) {
@@ -469,7 +515,7 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 }
 
 // The sequential pass for bf16 inputs on v_mfma_f32_16x16x32_bf16: one
-// workgroup of 4 waves per (head, 32 value columns), C = 64.  Wave w owns the
+// workgroup of 4 waves per (head, TV = 16 or 32 value columns), C = 64.  Wave w owns the
 // chunk's query rows 16w .. 16w + 15 and the state rows (keys) of 16-row
 // tiles w, w + 4, ...; the state tile lives in its fp32 accumulators, with a
 // bf16 copy S^T in LDS (double-buffered by chunk parity) as the B operand of
@@ -483,9 +529,10 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 //       LDS buffer.
 // The next chunk's q, k, W and U0 are loaded into registers while the
 // current one computes.
-template <int DK>
+template <int DK, int TV>
 __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a) {
-  constexpr int C = 64, TV = 32;
+  constexpr int C = 64;
+  constexpr int NT = TV / 16;       // 16-column tiles of the workgroup's value columns
   constexpr int QS = DK + 8;        // bf16 row stride of the Q, K, W tiles and of S^T
   constexpr int CS = C + 8;         // bf16 row stride of K^T, P, U^T
   constexpr int KST = DK / 32;      // 32-wide k-steps over the keys
@@ -507,6 +554,9 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   __shared__ __align__(16) uint16_t sST[2][TV * QS];
   __shared__ __align__(16) uint16_t sUT[TV * CS], sUwT[TV * CS], sP[C * CS];
   __shared__ float sb[C];
+  // U0 of the chunk, each lane's own elements (staged through LDS so that no
+  // prefetched register has to be copied across the loop's back edge)
+  __shared__ float sU0[C * TV];
 
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * L * DK;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
@@ -517,9 +567,30 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   // ---- register prefetch of one chunk: q, k, W rows and this lane's U0 ----
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
   u32x4 rq[PER], rk[PER], rw[PER];
-  float ru[2][4];
+  float ru[NT][4];
+  float rdec = 0.0f;  // wave 0: the decay data of token t0 + lane
+  const bool tok = a.decay_kind == kDecayLog || a.decay_kind == kDecayGate;
+  const float lgh = a.decay_kind == kDecayHead ? logf(a.decay[h]) : 0.0f;
   auto fetch = [&](int c) {
     const int t0 = c * C, n = min(C, L - t0);
+    if (w == 0) rdec = tok ? (lane < n ? a.decay[(size_t)bh * L + t0 + lane] : 0.0f) : lgh;
+    if (n == C) {
+      // a whole chunk: no row checks
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
+        const size_t off = (size_t)(t0 + row) * DK + 8 * ch;
+        rq[p] = *reinterpret_cast<const u32x4*>(qh + off);
+        rk[p] = *reinterpret_cast<const u32x4*>(kh + off);
+        rw[p] = *reinterpret_cast<const u32x4*>(wh + off);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ru[nt][r] = uh[(size_t)(t0 + 16 * w + 4 * g4 + r) * DV + 16 * nt + l16];
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
@@ -535,7 +606,7 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
       }
     }
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * w + 4 * g4 + r;
@@ -544,24 +615,23 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   };
 
   // ---- the state: own tiles (mt = w + 4 m, nt), lane rows 16 mt + 4 g4 + r, column 16 nt + l16
-  f32x4 accS[MTW][2];
+  f32x4 accS[MTW][NT];
   auto put_state = [&](int buf) {
 #pragma unroll
     for (int m = 0; m < MTW; ++m) {
       const int mt = w + 4 * m;
       if (mt < NMT) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
           *reinterpret_cast<uint2*>(&sST[buf][(16 * nt + l16) * QS + 16 * mt + 4 * g4]) =
-              make_uint2(pack_bf16x2(accS[m][nt][0], accS[m][nt][1]),
-                         pack_bf16x2(accS[m][nt][2], accS[m][nt][3]));
+              make_uint2(cvt2(accS[m][nt][0], accS[m][nt][1]), cvt2(accS[m][nt][2], accS[m][nt][3]));
       }
     }
   };
 #pragma unroll
   for (int m = 0; m < MTW; ++m)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int mt = w + 4 * m, d = 16 * mt + 4 * g4 + r;
@@ -575,7 +645,7 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * C, n = min(C, L - t0);
     const int sp = c & 1;
-    __syncthreads();  // the previous chunk is done with every tile; S^T[sp] is complete
+    lds_barrier();  // the previous chunk is done with every tile; S^T[sp] is complete
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
@@ -583,25 +653,26 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
       *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = rk[p];
       *reinterpret_cast<u32x4*>(&sW[row * QS + 8 * ch]) = rw[p];
     }
-    if (w == 0) chunk_log_prefix_wave(a, bh, h, t0, n, sb);
-    float u0[2][4];
+    if (w == 0) chunk_log_prefix_reg(a, rdec, n, sb);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) u0[nt][r] = ru[nt][r];
+      for (int r = 0; r < 4; ++r) sU0[(16 * w + 4 * g4 + r) * TV + 16 * nt + l16] = ru[nt][r];
     if (c + 1 < nch) fetch(c + 1);
-    __syncthreads();  // the chunk's tiles and prefixes are in LDS
+    lds_barrier();  // the chunk's tiles and prefixes are in LDS
     const float bL = sb[n - 1];
     const uint16_t* st = sST[sp];
 
     // (1a) U = U0 - W S for rows 16w .. 16w + 15
     {
-      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KST; ++s) {
         const u32x4 aw = *reinterpret_cast<const u32x4*>(&sW[(16 * w + l16) * QS + 32 * s + 8 * g4]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
           acc[nt] = mfma16x16x32(aw, bs, acc[nt]);
         }
@@ -609,53 +680,64 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
       const int i0 = 16 * w + 4 * g4;
       float wt[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wt[r] = i0 + r < n ? expf(bL - sb[i0 + r]) : 0.0f;
+      for (int r = 0; r < 4; ++r) wt[r] = i0 + r < n ? ex2(bL - sb[i0 + r]) : 0.0f;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         float u[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = u0[nt][r] - acc[nt][r];
+        for (int r = 0; r < 4; ++r) u[r] = sU0[(i0 + r) * TV + 16 * nt + l16] - acc[nt][r];
         const int o = (16 * nt + l16) * CS + i0;
-        *reinterpret_cast<uint2*>(&sUT[o]) = make_uint2(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]));
-        *reinterpret_cast<uint2*>(&sUwT[o]) = make_uint2(pack_bf16x2(u[0] * wt[0], u[1] * wt[1]),
-                                                         pack_bf16x2(u[2] * wt[2], u[3] * wt[3]));
+        *reinterpret_cast<uint2*>(&sUT[o]) = make_uint2(cvt2(u[0], u[1]), cvt2(u[2], u[3]));
+        *reinterpret_cast<uint2*>(&sUwT[o]) = make_uint2(cvt2(u[0] * wt[0], u[1] * wt[1]),
+                                                         cvt2(u[2] * wt[2], u[3] * wt[3]));
       }
     }
-    // (1b) P^T tiles of query columns 16w .. 16w + 15: token rows 16 jt + 4 g4 + r
-    {
-      const int i = 16 * w + l16;
-      const float bi = sb[i];
+    // (1b) the causal P^T tiles (query tile qt, token tile jt <= qt), 10 of
+    //      them spread over the waves: P^T = K Q^T, lane = query 16 qt + l16,
+    //      registers = tokens 16 jt + 4 g4 + r; masked, decayed -> P (row-major).
+    //      The two tiles above the diagonal that the P U k-steps still cover
+    //      ((0, 1) and (2, 3)) are written as zeros.
+    for (int tix = w; tix < 12; tix += 4) {
+      int qt, jt;
+      if (tix < 10) {
+        qt = tix < 1 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
+        jt = tix - qt * (qt + 1) / 2;
+      } else {
+        qt = tix == 10 ? 0 : 2;
+        jt = qt + 1;
+      }
+      const int i = 16 * qt + l16;
+      float pv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (jt <= qt) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jt = 0; jt < C / 16; ++jt) {
-        float pv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (jt <= w) {
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KST; ++s) {
-            const u32x4 ak = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
-            const u32x4 bq = *reinterpret_cast<const u32x4*>(&sQ[i * QS + 32 * s + 8 * g4]);
-            acc = mfma16x16x32(ak, bq, acc);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * jt + 4 * g4 + r;
-            pv[r] = j <= i ? acc[r] * expf(bi - sb[j]) : 0.0f;
-          }
+        for (int s = 0; s < KST; ++s) {
+          const u32x4 ak = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
+          const u32x4 bq = *reinterpret_cast<const u32x4*>(&sQ[i * QS + 32 * s + 8 * g4]);
+          acc = mfma16x16x32(ak, bq, acc);
         }
-        *reinterpret_cast<uint2*>(&sP[i * CS + 16 * jt + 4 * g4]) =
-            make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+        const float bi = sb[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jt + 4 * g4 + r;
+          pv[r] = j <= i ? acc[r] * ex2(bi - sb[j]) : 0.0f;
+        }
       }
+      *reinterpret_cast<uint2*>(&sP[i * CS + 16 * jt + 4 * g4]) =
+          make_uint2(cvt2(pv[0], pv[1]), cvt2(pv[2], pv[3]));
     }
-    __syncthreads();  // U^T, (wU)^T and P complete
+    lds_barrier();  // U^T, (wU)^T and P complete
 
     // (2a) O = diag(e^b) Q S + P U for rows 16w .. 16w + 15
     {
-      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KST; ++s) {
         const u32x4 aq = *reinterpret_cast<const u32x4*>(&sQ[(16 * w + l16) * QS + 32 * s + 8 * g4]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
           acc[nt] = mfma16x16x32(aq, bs, acc[nt]);
         }
@@ -663,35 +745,35 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
       const int i0 = 16 * w + 4 * g4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = expf(sb[i0 + r]);
-        acc[0][r] *= e;
-        acc[1][r] *= e;
-      }
+        const float e = ex2(sb[i0 + r]);
 #pragma unroll
-      for (int s2 = 0; s2 < C / 32; ++s2) {
+        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
+      }
+      // token k-steps up to the diagonal: rows 16w .. need tokens < 16w + 16
+      for (int s2 = 0; s2 <= w / 2; ++s2) {
         const u32x4 ap = *reinterpret_cast<const u32x4*>(&sP[(16 * w + l16) * CS + 32 * s2 + 8 * g4]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
           acc[nt] = mfma16x16x32(ap, bu, acc[nt]);
         }
       }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (i0 + r < n)
-            oh[(size_t)(t0 + i0 + r) * DV + 16 * nt + l16] = (uint16_t)f32_to_bf16(acc[nt][r]);
+            oh[(size_t)(t0 + i0 + r) * DV + 16 * nt + l16] = (uint16_t)(cvt2(acc[nt][r], 0.0f) & 0xffffu);
     }
     // (2b) S = e^{b_last} S + K^T (e^{b_last - b} U) for the wave's state tiles
     {
-      const float eL = expf(bL);
+      const float eL = ex2(bL);
 #pragma unroll
       for (int m = 0; m < MTW; ++m) {
         const int mt = w + 4 * m;
         if (mt < NMT) {
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
             f32x4 acc = accS[m][nt] * eL;
 #pragma unroll
             for (int s2 = 0; s2 < C / 32; ++s2) {
@@ -712,7 +794,7 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
       const int mt = w + 4 * m;
       if (mt < NMT) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             a.state[((size_t)bh * DK + 16 * mt + 4 * g4 + r) * DV + dv0 + 16 * nt + l16] = accS[m][nt][r];
@@ -734,7 +816,10 @@ hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
       if (mfma) {                                                                 \
         hipLaunchKernelGGL((delta_prep_mfma_kernel<D>), gp, blk, 0, s, a);        \
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;        \
-        hipLaunchKernelGGL((delta_chunk_mfma_kernel<D>), gc, blk, 0, s, a);       \
+        if (a.n_v == a.DV / 16)                                                   \
+          hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16>), gc, blk, 0, s, a); \
+        else                                                                      \
+          hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 32>), gc, blk, 0, s, a); \
         return hipGetLastError();                                                 \
       }                                                                           \
     }                                                                             \
@@ -755,7 +840,12 @@ hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
 
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t s) {
   DeltaArgs b = a;
-  const int tv = a.DV < kDeltaTile ? a.DV : kDeltaTile;
+  int tv = a.DV < kDeltaTile ? a.DV : kDeltaTile;
+  // the MFMA pass: 16-column workgroups when 32-column ones would leave
+  // fewer than two per compute unit of an MI355X (256 of them)
+  if (a.dtype == kBF16 && a.C == 64 && a.DK >= 32 && a.DV % 32 == 0 &&
+      (long long)a.B * a.H * (a.DV / 32) < 512)
+    tv = 16;
   b.n_v = a.DV / tv;
   return a.dtype == kBF16 ? launch_dk<true>(b, s) : launch_dk<false>(b, s);
 }

@@ -160,3 +160,11 @@ def test_delta_workload_sampled_heads(gpu_lib):
     e_out, e_s = oracle.rel_err(got, ref), oracle.rel_err(got_s, ref_s)
     print(f"delta_bf16: sampled heads {heads}: output rel err {e_out:.3e}, state rel err {e_s:.3e}")
     assert e_out <= 1e-2 and e_s <= 1e-2
+
+
+def test_delta_many_heads_takes_the_32_column_pass(gpu_lib):
+    """B*H*(d_v/32) >= 512 keeps 32-column workgroups in the MFMA pass; the
+    smaller cases above run the 16-column ones."""
+    c = W.RandomCase(4, 32, 64 * 2 + 5, 128, 128, torch.bfloat16, W.PHI_IDENTITY, W.DECAY_GATE,
+                     seed=670, scale=1.0 / np.sqrt(128), with_state=True)
+    _run(gpu_lib, c, 64, "32-column pass")
