@@ -295,8 +295,8 @@ def cpu_baseline(W):
 def profile_pass(la, torch, W):
     """A short fixed sequence of launches for counter passes: one plain copy of
     COPY_BYTES (the calibration), then the forward of the timed workload
-    (state init + la_chunk_fwd) three times, 20 decode steps, then two
-    forwards of the per-channel gate workload."""
+    (state init + la_chunk_fwd) three times, 20 decode steps, two forwards
+    of the per-channel gate workload, then two delta-rule forwards."""
     dev = torch.device("cuda:0")
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -307,6 +307,7 @@ def profile_pass(la, torch, W):
     bench_chunk(la, torch, W, steps=1, warmup=1)
     bench_decode(la, torch, W, steps=20, reps=1)
     bench_chunk_gla(la, torch, W, steps=1, warmup=1)
+    bench_delta(la, torch, W, steps=1, warmup=1)
     torch.cuda.synchronize()
     print(json.dumps({"profile_pass": True, "copy_bytes": COPY_BYTES,
                       "source_sha256": kernel_source_digest()}), flush=True)

@@ -544,7 +544,14 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int bh = blockIdx.x / a.n_v, vt = blockIdx.x % a.n_v;
+  // workgroup -> (head, value tile): the tiles of one head get workgroup ids
+  // that are equal mod 8, so they run on one XCD and share q, k and W
+  // through its L2
+  const int f = blockIdx.x;
+  const int slot = f >> 3;
+  const int vt = slot % a.n_v;
+  const int bh = (slot / a.n_v) * 8 + (f & 7);
+  if (bh >= a.B * a.H) return;
   const int h = bh % a.H;
   const int L = a.L, DV = a.DV;
   const int dv0 = vt * TV;
@@ -807,6 +814,8 @@ template <bool BF16>
 hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
   const int nch = (a.L + a.C - 1) / a.C;
   const dim3 gp(a.B * a.H * nch), gc(a.B * a.H * a.n_v), blk(256);
+  // the MFMA pass numbers its workgroups by groups of 8 heads (see there)
+  const dim3 gm(((a.B * a.H + 7) / 8) * 8 * a.n_v);
   // bf16 inputs, C = 64, d_k >= 32 and whole 32-column value tiles: the MFMA pass
   const bool mfma = BF16 && a.C == 64 && a.DK >= 32 && a.DV % 32 == 0;
   switch (a.DK) {
@@ -817,9 +826,9 @@ hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((delta_prep_mfma_kernel<D>), gp, blk, 0, s, a);        \
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;        \
         if (a.n_v == a.DV / 16)                                                   \
-          hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16>), gc, blk, 0, s, a); \
+          hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16>), gm, blk, 0, s, a); \
         else                                                                      \
-          hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 32>), gc, blk, 0, s, a); \
+          hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 32>), gm, blk, 0, s, a); \
         return hipGetLastError();                                                 \
       }                                                                           \
     }                                                                             \
