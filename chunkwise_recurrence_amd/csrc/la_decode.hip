@@ -30,8 +30,10 @@
 namespace la {
 namespace {
 
-template <int DK, int DV, bool BF16>
+// VAR: 0 a scalar decay (or none), 1 the per-channel decay, 2 the delta rule
+template <int DK, int DV, bool BF16, int VAR>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
+  constexpr bool DELTA = VAR == 2, CHAN = VAR == 1;
   constexpr int TPR = DV / 4;                      // lanes per state row
   constexpr int RP = 256 / TPR;                    // rows per pass
   constexpr int NPASS = (DK + RP - 1) / RP;
@@ -72,13 +74,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   if (a.decay_kind == kDecayHead) decay = a.decay[h];
   else if (a.decay_kind == kDecayLog || a.decay_kind == kDecayGate)
     decay = expf(token_log_decay(a.decay_kind, a.decay[bh]));
-  const bool chan = a.decay_kind == kDecayChannel;
   __shared__ float sdec[DK];
-  if (tid < DK) sdec[tid] = chan ? expf(a.decay[(size_t)bh * DK + tid]) : decay;
+  if (tid < DK) sdec[tid] = CHAN ? expf(a.decay[(size_t)bh * DK + tid]) : decay;
   // delta rule: r = k^T S of the previous state, reduced over the row groups
-  __shared__ float sr[DV];
+  __shared__ float sr[DELTA ? DV : 1];
   float bta = 0.0f;
-  if (a.beta != nullptr) {
+  if constexpr (DELTA) {
     bta = a.beta[bh];
     __syncthreads();
     float4 rp = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -122,16 +123,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 
   const float4 vv = make_float4(sv[4 * c4], sv[4 * c4 + 1], sv[4 * c4 + 2], sv[4 * c4 + 3]);
   float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (a.beta != nullptr) rv = make_float4(sr[4 * c4], sr[4 * c4 + 1], sr[4 * c4 + 2], sr[4 * c4 + 3]);
+  if constexpr (DELTA) rv = make_float4(sr[4 * c4], sr[4 * c4 + 1], sr[4 * c4 + 2], sr[4 * c4 + 3]);
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int p = 0; p < NPASS; ++p) {
     const int r = rg + p * RP;
     if (r < DK) {
       const float kr = sk[r], qr = sq[r];
-      const float dr = chan ? sdec[r] : decay;
+      const float dr = CHAN ? sdec[r] : decay;
       f32x4 s = sreg[p];
-      if (a.beta != nullptr) {
+      if constexpr (DELTA) {
         // S' = a (S - beta k r^T) + beta k v^T
         const float bk = bta * kr;
         s.x = fmaf(dr, fmaf(-bk, rv.x, s.x), bk * vv.x);
@@ -178,9 +179,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 template <int DK, int DV>
 hipError_t launch_dk_dv(const DecodeArgs& a, int dtype, hipStream_t s) {
   const dim3 grid(a.N * a.H), block(256);
-  if (dtype == kBF16) hipLaunchKernelGGL((decode_kernel<DK, DV, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((decode_kernel<DK, DV, false>), grid, block, 0, s, a);
-  return hipGetLastError();
+  const int var = a.beta != nullptr ? 2 : a.decay_kind == kDecayChannel ? 1 : 0;
+#define LA_VAR(V)                                                                           \
+  if (var == V) {                                                                           \
+    if (dtype == kBF16) hipLaunchKernelGGL((decode_kernel<DK, DV, true, V>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((decode_kernel<DK, DV, false, V>), grid, block, 0, s, a);      \
+    return hipGetLastError();                                                               \
+  }
+  LA_VAR(0)
+  LA_VAR(1)
+  LA_VAR(2)
+#undef LA_VAR
+  return hipErrorInvalidValue;
 }
 
 template <int DK>
