@@ -147,8 +147,8 @@ __device__ __forceinline__ void chunk_log_prefix_reg(const DeltaArgs& a, float r
 // N = diag(beta) (tril(K K^T, -1) o G) by 16 x 16 blocks (diagonal blocks by
 // forward substitution, all at once; then block rows I = 1.. with
 // T_IJ = -T_II sum_{J <= M < I} N_IM T_MJ), then W = T diag(beta e^b) K and
-// U0 = T diag(beta) V.  W goes out as fp32 or (for the MFMA chunk pass) bf16.
-template <bool BF16, int DK, bool WBF16>
+// U0 = T diag(beta) V, both in fp32 (the fp32-arithmetic path).
+template <bool BF16, int DK>
 __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a) {
   constexpr int KP = DK + 1;  // padded row stride (fp32 words)
   const int tid = threadIdx.x;
@@ -242,13 +242,7 @@ __global__ __launch_bounds__(256) void delta_prep_kernel(const DeltaArgs a) {
       x2 = fmaf(t, kr[2], x2);
       x3 = fmaf(t, kr[3], x3);
     }
-    const size_t o = (rowk + i) * DK + d0;
-    if constexpr (WBF16) {
-      uint16_t* w = reinterpret_cast<uint16_t*>(a.ws_W);
-      *reinterpret_cast<uint2*>(w + o) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
-    } else {
-      *reinterpret_cast<float4*>(a.ws_W + o) = make_float4(x0, x1, x2, x3);
-    }
+    *reinterpret_cast<float4*>(a.ws_W + (rowk + i) * DK + d0) = make_float4(x0, x1, x2, x3);
   }
   for (int idx = tid; idx < n * (DV / 4); idx += 256) {
     const int i = idx / (DV / 4), c0 = 4 * (idx % (DV / 4));
@@ -832,7 +826,7 @@ hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
         return hipGetLastError();                                                 \
       }                                                                           \
     }                                                                             \
-    hipLaunchKernelGGL((delta_prep_kernel<BF16, D, false>), gp, blk, 0, s, a);    \
+    hipLaunchKernelGGL((delta_prep_kernel<BF16, D>), gp, blk, 0, s, a);           \
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;            \
     hipLaunchKernelGGL((delta_chunk_kernel<BF16, D>), gc, blk, 0, s, a);          \
     return hipGetLastError();

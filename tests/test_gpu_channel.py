@@ -186,3 +186,35 @@ def test_gla_workload_sampled_heads(gpu_lib):
     e_out, e_s = oracle.rel_err(got, ref), oracle.rel_err(got_s, ref_s)
     print(f"gla_bf16: sampled heads {heads}: output rel err {e_out:.3e}, state rel err {e_s:.3e}")
     assert e_out <= 1e-2 and e_s <= 1e-2
+
+
+@pytest.mark.parametrize("phi", [W.PHI_IDENTITY, W.PHI_ELU1])
+def test_channel_normalised_fp32(gpu_lib, phi):
+    """fp32 inputs take the normalised form with the per-channel gate:
+    z_t = diag(a_t) z_{t-1} + phi(k_t), o_t = phi(q_t)^T S_t / phi(q_t)^T z_t."""
+    la = gpu_lib
+    c = W.RandomCase(1, 2, 150, 32, 64, torch.float32, phi, W.DECAY_CHANNEL, seed=500 + phi,
+                     channel_mean=0.2, with_state=True)
+    q, k, v, decay, S0 = W.random_inputs(c)
+    if phi == W.PHI_IDENTITY:  # keep every denominator away from zero
+        q, k = q.abs() + 0.1, k.abs() + 0.1
+    g = torch.Generator().manual_seed(501)
+    z0 = torch.rand((1, 2, 32), generator=g) * 4.0 + 0.5
+    S, z = S0.to(DEV).contiguous(), z0.to(DEV).contiguous()
+    out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=32, phi=phi, decay_kind=W.DECAY_CHANNEL,
+                       decay=decay.to(DEV), state=S, normalize=True, norm_state=z)
+    torch.cuda.synchronize()
+    ref, ref_s, ref_z = oracle.recurrent(_np(q), _np(k), _np(v), phi, W.DECAY_CHANNEL, _np(decay),
+                                         _np(S0), normalize=True, norm_state=_np(z0))
+    assert oracle.rel_err(_np(out), ref) <= 1e-4
+    assert oracle.rel_err(_np(S), ref_s) <= 1e-4 and oracle.rel_err(_np(z), ref_z) <= 1e-4
+    # and the decode step continues it
+    Sd, zd = S.clone(), z.clone()
+    qd, kd, vd = (x[:, :, 0].contiguous() for x in (q, k, v))
+    ld = decay[:, :, 0].contiguous()
+    od = la.decode_step(qd.to(DEV), kd.to(DEV), vd.to(DEV), Sd, phi=phi,
+                        decay_kind=W.DECAY_CHANNEL, decay=ld.to(DEV), norm_state=zd)
+    torch.cuda.synchronize()
+    ro, rs, rz = oracle.decode_step(_np(qd), _np(kd), _np(vd), phi, W.DECAY_CHANNEL, _np(ld),
+                                    ref_s, normalize=True, norm_state=ref_z)
+    assert oracle.rel_err(_np(od), ro) <= 1e-4 and oracle.rel_err(_np(zd), rz) <= 1e-4
