@@ -218,3 +218,22 @@ def test_channel_normalised_fp32(gpu_lib, phi):
     ro, rs, rz = oracle.decode_step(_np(qd), _np(kd), _np(vd), phi, W.DECAY_CHANNEL, _np(ld),
                                     ref_s, normalize=True, norm_state=ref_z)
     assert oracle.rel_err(_np(od), ro) <= 1e-4 and oracle.rel_err(_np(zd), rz) <= 1e-4
+
+
+def test_channel_strong_decay_near_the_documented_range(gpu_lib):
+    """log a = -2.2 for every token and channel: a 64-token chunk sums to
+    -140.8, inside the bf16 kernel's documented bound (>= -150 per chunk and
+    channel); the split factors reach e^{70} and must still give the oracle's
+    result.  Past the bound fp32 would overflow (documented, not tested)."""
+    la = gpu_lib
+    c = W.RandomCase(1, 2, 64 * 3 + 10, 128, 128, torch.bfloat16, W.PHI_IDENTITY,
+                     W.DECAY_CHANNEL, seed=520, scale=1.0 / np.sqrt(128), with_state=True)
+    q, k, v, _, S0 = W.random_inputs(c)
+    decay = torch.full((1, 2, c.L, 128), -2.2)
+    S = S0.to(DEV).contiguous()
+    out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=64, decay_kind=W.DECAY_CHANNEL,
+                       decay=decay.to(DEV), state=S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), 0, W.DECAY_CHANNEL, _np(decay), _np(S0))
+    assert oracle.rel_err(_np(out), ref) <= 1e-2 and oracle.rel_err(_np(S), ref_s) <= 1e-2
