@@ -160,17 +160,6 @@ __device__ __forceinline__ u32x4 elu1_x8(u32x4 w) {
   return w;
 }
 
-// Global -> LDS copy of one 16-byte chunk per lane; `dst` is wave-uniform and
-// lane l's chunk lands at dst + 16 l.
-__device__ __forceinline__ void dma16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
-}
-
 // Decay category of a launch (a template parameter, so the kernel has no
 // per-element branches on it): none, one constant per head, or per token
 // (log a given, or the gate a = exp(-softplus(g)); both arrive as in-chunk

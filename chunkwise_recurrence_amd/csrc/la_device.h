@@ -51,4 +51,32 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Global -> LDS copies: lane l of the wave writes bytes [16 l, 16 l + 16) (or
+// [4 l, 4 l + 4)) past dst, which is wave-uniform and goes to M0.  They are
+// issued from inline asm on purpose: the compiler tracks copies made with the
+// builtin and, unable to tell that the buffers they fill are not the ones read
+// or written meanwhile, puts a full vmcnt(0) wait before later LDS accesses,
+// which drains the next chunk's prefetch (and the output stores) in the middle
+// of every chunk.  Hidden from the compiler, the copies are ordered only by
+// the kernels' own counted waits (s_waitcnt vmcnt) and barriers.  They write
+// no register, and M0 is restored after each one.
+// (The low 32 bits of a generic pointer into LDS are its LDS address.)
+__device__ __forceinline__ uint32_t lds_u32(void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)p);
+}
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep) : "v"(src), "s"(lds_u32(dst)) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep) : "v"(src), "s"(lds_u32(dst)) : "memory");
+}
+
 }  // namespace la
