@@ -36,6 +36,10 @@ struct Plan {
   int seg_chunks = 0;
   size_t ws_bytes = 0;
   size_t ws_S_off = 0, ws_logA_off = 0, ws_b_off = 0, ws_z_off = 0;
+  // copies of S_0 (segment split) and z_0 (normalised form, a head spread over
+  // several workgroups); 0 = none
+  size_t ws_S0_off = 0, ws_z0_off = 0;
+  bool copy_S0 = false, copy_z0 = false;
   bool prefix = false;  // token decays: in-chunk prefix sums of log a in the workspace
 };
 
@@ -63,6 +67,11 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
     p.ng = 1;
     p.P = 1;
     p.seg_chunks = nchunks;
+    if (norm && d_v / p.tile > 1) {
+      p.copy_z0 = true;
+      p.ws_z0_off = 0;
+      p.ws_bytes = round256((size_t)heads * d_k * sizeof(float));
+    }
     return p;
   }
   const int forced_kernel = g_plan_kernel.load(), forced_tile = g_plan_tile.load(),
@@ -126,6 +135,14 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
     off += round256((size_t)heads * p.P * (chan ? d_k : 1) * sizeof(float));
     p.ws_z_off = off;  // the normalised form's per-segment z increments
     off += round256((size_t)heads * p.P * d_k * sizeof(float));
+    p.copy_S0 = true;
+    p.ws_S0_off = off;
+    off += round256((size_t)heads * d_k * d_v * sizeof(float));
+  }
+  if (norm && (p.P > 1 || d_v / p.tile > 1)) {
+    p.copy_z0 = true;
+    p.ws_z0_off = off;
+    off += round256((size_t)heads * d_k * sizeof(float));
   }
   if (decay_kind == LA_DECAY_TOKEN_LOG || decay_kind == LA_DECAY_TOKEN_GATE) {
     p.prefix = true;
@@ -253,14 +270,24 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
   a.seg_chunks = p.seg_chunks;
   a.norm = norm ? 1 : 0;
   a.zstate = norm ? norm_state : nullptr;
+  a.s0 = state;
+  a.z0 = a.zstate;
   const hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  // z_0 is read by every workgroup of a head and z_L written by one of them:
+  // the workgroups read a copy
+  if (p.copy_z0 && norm_state) {
+    float* z0 = reinterpret_cast<float*>(ws + p.ws_z0_off);
+    if (la::launch_copy_f32(z0, norm_state, (size_t)B * H * d_k, s) != hipSuccess)
+      return LA_ERR_DEVICE;
+    a.z0 = z0;
+  }
 
   hipError_t e;
   if (dtype == LA_F32) {
     a.n_units = B * H;
     e = la::launch_chunk_f32(a, s);
   } else {
-    char* ws = static_cast<char*>(workspace);
     if (p.prefix) {
       a.ws_b = reinterpret_cast<float*>(ws + p.ws_b_off);
       e = la::launch_decay_prefix(a, s);
@@ -270,10 +297,15 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
       a.ws_S = reinterpret_cast<float*>(ws + p.ws_S_off);
       a.ws_logA = reinterpret_cast<float*>(ws + p.ws_logA_off);
       a.ws_z = reinterpret_cast<float*>(ws + p.ws_z_off);
+      // the state pass copies S_0 for the output pass, whose last segment
+      // overwrites state with S_L
+      a.ws_S0 = state ? reinterpret_cast<float*>(ws + p.ws_S0_off) : nullptr;
       a.n_units = B * H * (p.P - 1);
       e = p.kernel == LA_KERNEL_STRIPE ? la::launch_chunk_stripe(a, /*state_only=*/true, s)
                                        : la::launch_chunk_bf16(a, /*state_only=*/true, s);
       if (e != hipSuccess) return LA_ERR_DEVICE;
+      a.s0 = a.ws_S0;
+      a.ws_S0 = nullptr;
     }
     a.n_units = B * H * p.P;
     e = p.kernel == LA_KERNEL_STRIPE ? la::launch_chunk_stripe(a, /*state_only=*/false, s)

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int dk = 16 * mt + 4 * g4 + i;
-          float s = a.state ? a.state[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
+          float s = a.s0 ? a.s0[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
           for (int p = 0; p < sigma; ++p) {
             const size_t seg = (size_t)bh * a.P + p;
             s = exp2f(a.ws_logA[seg]) * s + a.ws_S[(seg * DK + dk) * DV + dv];
@@ -310,6 +310,22 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
         w[0] = cvt2(accS[t][0], accS[t][1]);
         w[1] = cvt2(accS[t][2], accS[t][3]);
         *reinterpret_cast<u32x2*>(&sST[0][swz<G::WCK>(srow0 + 16 * nt_w + l16, 16 * mt + 4 * g4)]) = w;
+      }
+    }
+  } else if (sigma == 0 && a.ws_S0 != nullptr) {
+    // the first segment's workgroups copy S_0 for the output pass (its last
+    // segment overwrites the caller's state with S_L)
+#pragma unroll
+    for (int t = 0; t < G::TPW; ++t) {
+      const int tau = wl + 4 * t;
+      if (tau < G::NT_S) {
+        const int mt = tau / G::NTV;
+        const int dv = dvg + 16 * nt_w + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const size_t o = ((size_t)bh * DK + 16 * mt + 4 * g4 + i) * DV + dv;
+          a.ws_S0[o] = a.state[o];
+        }
       }
     }
   }

@@ -56,10 +56,10 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
 
   for (int i = tid; i < DK * tv; i += 256) {
     const int d = i / tv, v = i % tv;
-    sS[i] = a.state ? a.state[((size_t)bh * DK + d) * DV + dv0 + v] : 0.0f;
+    sS[i] = a.s0 ? a.s0[((size_t)bh * DK + d) * DV + dv0 + v] : 0.0f;
   }
   if (norm)
-    for (int d = tid; d < DK; d += 256) sZ[d] = a.zstate ? a.zstate[(size_t)bh * DK + d] : 0.0f;
+    for (int d = tid; d < DK; d += 256) sZ[d] = a.z0 ? a.z0[(size_t)bh * DK + d] : 0.0f;
 
   for (int t0 = 0; t0 < L; t0 += C) {
     const int n = min(C, L - t0);

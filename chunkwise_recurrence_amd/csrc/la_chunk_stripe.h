@@ -370,7 +370,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int dk = 32 * (mk0 + t) + 8 * (r >> 2) + 4 * h + (r & 3);
-        float sv = a.state ? a.state[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
+        float sv = a.s0 ? a.s0[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
         for (int p = 0; p < sigma; ++p) {
           const size_t seg = (size_t)bh * a.P + p;
           const float la2 = CHN ? a.ws_logA[seg * DK + dk] : a.ws_logA[seg];
@@ -378,6 +378,23 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         }
         accS[t][r] = sv;
       }
+  }
+  // State pass: the first segment's workgroups copy S_0 for the output pass,
+  // whose last segment overwrites the caller's state with S_L.  The values are
+  // loaded here, ahead of the first tile loads, and stored after the last
+  // chunk, so the copy adds no latency of its own.
+  const bool copy_s0 = STATE_ONLY && sigma == 0 && a.ws_S0 != nullptr;
+  auto s0_index = [&](int t, int r) -> size_t {
+    return ((size_t)bh * DK + 32 * (mk0 + t) + 8 * (r >> 2) + 4 * h + (r & 3)) * DV + dv0 + cw + l32;
+  };
+  float s0v[STATE_ONLY ? G::NMK_OWN : 1][16];
+  if constexpr (STATE_ONLY) {
+    if (copy_s0) {
+#pragma unroll
+      for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s0v[t][r] = a.state[s0_index(t, r)];
+    }
   }
   // normalised form: the waves of stripe 0 hold z for their keys, lane l32
   // of own tile t holding key 32 (mk0 + t) + l32
@@ -388,7 +405,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       const int dk = 32 * (mk0 + t) + l32;
       float zv = 0.0f;
       if constexpr (!STATE_ONLY) {
-        zv = a.zstate ? a.zstate[(size_t)bh * DK + dk] : 0.0f;
+        zv = a.z0 ? a.z0[(size_t)bh * DK + dk] : 0.0f;
         for (int p = 0; p < sigma; ++p) {
           const size_t seg = (size_t)bh * a.P + p;
           zv = exp2f(a.ws_logA[seg]) * zv + a.ws_z[seg * DK + dk];
@@ -640,6 +657,76 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     for (int ks = 0; ks < G::NTS; ++ks)
       vA[ks] = lds_tr8<G::WCV>(vb, 16 * ks + 8 * (g4 >> 1), cw + 16 * (g4 & 1), l16);
 
+    // (3) state update of this wave's tiles (after the outputs; it reads only
+    // K, V and the weights, and S_c is already packed for the inter term)
+    auto state_update = [&]() {
+      // S <- e^{b_last} S + K^T diag(e^{b_last - b}) V
+      // (state pass: S <- S + K^T diag(e^{B_end - B}) V)
+      // (per-channel decay: S <- diag(e^{b_last - r}) (diag(e^r) S + k~^T V))
+      if constexpr (CHN && STATE_ONLY) scale_rows(sER);
+      if constexpr (CAT != kCatNone && !CHN && !STATE_ONLY) {
+        const float eL = __builtin_amdgcn_exp2f(bL);
+#pragma unroll
+        for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) accS[t][r] *= eL;
+      }
+      float zacc[NORM ? G::NMK_OWN : 1];
+      if constexpr (NORM) {
+#pragma unroll
+        for (int t = 0; t < G::NMK_OWN; ++t) zacc[t] = 0.0f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < G::NTS; ++ks) {
+        u32x4 vB = vA[ks];
+        float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+        if constexpr (CAT == kCatNone && NORM) {
+          // rows past a short last chunk hold phi(0), not 0: keep them out of z
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = 16 * ks + 8 * h + e < nvalid ? 1.0f : 0.0f;
+        }
+        if constexpr (CAT != kCatNone && !CHN) {
+          const int tb = 16 * ks + 8 * h;
+          const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wq[tb]);
+          const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wq[tb + 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[e] = w0[e];
+            w[4 + e] = w1[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            vB[e] = cvt2(bf16_to_f32(vB[e] & 0xffffu) * w[2 * e], bf16_to_f32(vB[e] >> 16) * w[2 * e + 1]);
+        }
+#pragma unroll
+        for (int t = 0; t < G::NMK_OWN; ++t) {
+          const u32x4 kA =
+              lds_tr8<G::WCK>(kb, 16 * ks + 8 * (g4 >> 1), 32 * (mk0 + t) + 16 * (g4 & 1), l16);
+          accS[t] = mfma32(kA, vB, accS[t]);
+          if constexpr (NORM) {
+            // z += sum_t w_t phi(k_t) over this lane's 8 tokens of key 32 (mk0 + t) + l32
+            if (stripe == 0) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                zacc[t] += w[2 * e] * bf16_to_f32(kA[e] & 0xffffu) + w[2 * e + 1] * bf16_to_f32(kA[e] >> 16);
+            }
+          }
+        }
+      }
+      if constexpr (CHN) scale_rows(sEL);
+      if constexpr (NORM) {
+        if (stripe == 0) {
+          const float eLz = (CAT != kCatNone && !STATE_ONLY) ? __builtin_amdgcn_exp2f(bL) : 1.0f;
+#pragma unroll
+          for (int t = 0; t < G::NMK_OWN; ++t) {
+            const float zsum = zacc[t] + __shfl_xor(zacc[t], 32);
+            zr[t] = eLz * zr[t] + zsum;
+            if (h == 0) sZ[(it + 1) & 1][32 * (mk0 + t) + l32] = zr[t];
+          }
+        }
+      }
+    };
+
     if constexpr (!STATE_ONLY) {
       // (1a) causal score blocks of this wave -> P~ in LDS
 #pragma unroll
@@ -818,71 +905,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       }
     }
 
-    // (3) state update of this wave's tiles: S <- e^{b_last} S + K^T diag(e^{b_last - b}) V
-    // (state pass: S <- S + K^T diag(e^{B_end - B}) V)
-    // (per-channel decay: S <- diag(e^{b_last - r}) (diag(e^r) S + k~^T V))
-    if constexpr (CHN && STATE_ONLY) scale_rows(sER);
-    if constexpr (CAT != kCatNone && !CHN && !STATE_ONLY) {
-      const float eL = __builtin_amdgcn_exp2f(bL);
-#pragma unroll
-      for (int t = 0; t < G::NMK_OWN; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) accS[t][r] *= eL;
-    }
-    float zacc[NORM ? G::NMK_OWN : 1];
-    if constexpr (NORM) {
-#pragma unroll
-      for (int t = 0; t < G::NMK_OWN; ++t) zacc[t] = 0.0f;
-    }
-#pragma unroll
-    for (int ks = 0; ks < G::NTS; ++ks) {
-      u32x4 vB = vA[ks];
-      float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-      if constexpr (CAT == kCatNone && NORM) {
-        // rows past a short last chunk hold phi(0), not 0: keep them out of z
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = 16 * ks + 8 * h + e < nvalid ? 1.0f : 0.0f;
-      }
-      if constexpr (CAT != kCatNone && !CHN) {
-        const int tb = 16 * ks + 8 * h;
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&wq[tb]);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&wq[tb + 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[e] = w0[e];
-          w[4 + e] = w1[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vB[e] = cvt2(bf16_to_f32(vB[e] & 0xffffu) * w[2 * e], bf16_to_f32(vB[e] >> 16) * w[2 * e + 1]);
-      }
-#pragma unroll
-      for (int t = 0; t < G::NMK_OWN; ++t) {
-        const u32x4 kA =
-            lds_tr8<G::WCK>(kb, 16 * ks + 8 * (g4 >> 1), 32 * (mk0 + t) + 16 * (g4 & 1), l16);
-        accS[t] = mfma32(kA, vB, accS[t]);
-        if constexpr (NORM) {
-          // z += sum_t w_t phi(k_t) over this lane's 8 tokens of key 32 (mk0 + t) + l32
-          if (stripe == 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              zacc[t] += w[2 * e] * bf16_to_f32(kA[e] & 0xffffu) + w[2 * e + 1] * bf16_to_f32(kA[e] >> 16);
-          }
-        }
-      }
-    }
-    if constexpr (CHN) scale_rows(sEL);
-    if constexpr (NORM) {
-      if (stripe == 0) {
-        const float eLz = (CAT != kCatNone && !STATE_ONLY) ? __builtin_amdgcn_exp2f(bL) : 1.0f;
-#pragma unroll
-        for (int t = 0; t < G::NMK_OWN; ++t) {
-          const float zsum = zacc[t] + __shfl_xor(zacc[t], 32);
-          zr[t] = eLz * zr[t] + zsum;
-          if (h == 0) sZ[(it + 1) & 1][32 * (mk0 + t) + l32] = zr[t];
-        }
-      }
-    }
+    state_update();
     logA += bL;
   };
 
@@ -905,6 +928,14 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   }
 
   // ---- epilogue ---------------------------------------------------------
+  if constexpr (STATE_ONLY) {
+    if (copy_s0) {
+#pragma unroll
+      for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a.ws_S0[s0_index(t, r)] = s0v[t][r];
+    }
+  }
   float* dst = nullptr;
   if constexpr (STATE_ONLY) {
     dst = a.ws_S + ((size_t)bh * a.P + sigma) * DK * DV;

@@ -210,6 +210,14 @@ __global__ void fill_zero_kernel(float4* p, size_t n4) {
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// dst[i] = src[i] for n floats in 16-byte pieces (n a multiple of 4, both
+// 16-byte aligned).
+__global__ void copy_f32_kernel(float4* dst, const float4* src, size_t n4) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
@@ -230,6 +238,16 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<float4*>(p), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t s) {
+  const size_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  size_t blocks = (n4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     reinterpret_cast<float4*>(dst), reinterpret_cast<const float4*>(src), n4);
   return hipGetLastError();
 }
 

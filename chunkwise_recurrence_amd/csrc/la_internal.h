@@ -18,7 +18,15 @@ struct ChunkArgs {
   const void* k;        // [B,H,L,DK]
   const void* v;        // [B,H,L,DV]
   void* out;            // [B,H,L,DV]
-  float* state;         // [B,H,DK,DV] or nullptr
+  float* state;         // [B,H,DK,DV] or nullptr; S_0 in, S_L out
+  // Where the output pass reads S_0 and z_0.  A head whose work spans several
+  // workgroups must not read them from state / zstate, which the workgroup of
+  // its last segment (or first value tile) overwrites with S_L / z_L: then
+  // they are copies in the workspace (S_0 copied by the state pass, z_0 by a
+  // copy launched before the passes).
+  const float* s0;      // [B,H,DK,DV] or nullptr (S_0 = 0)
+  const float* z0;      // normalised form: [B,H,DK] or nullptr (z_0 = 0)
+  float* ws_S0;         // state pass: where it copies S_0 (nullptr: no copy)
   const float* decay;   // nullptr | gamma[H] | [B,H,L] | [B,H,L,DK] (per channel)
   float* ws_S;          // [B*H, P, DK, DV] per-segment state increments
   float* ws_logA;       // [B*H, P] per-segment total log2 decay ([B*H, P, DK] per channel)
@@ -77,6 +85,7 @@ hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
+hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t s);
 
 // Whether a bf16 kernel exists for key dim DK, NG column groups of TV columns
 // and chunk C (and fits the LDS).

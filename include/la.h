@@ -86,10 +86,12 @@ la_status la_state_init(float* state, int B, int H, int d_k, int d_v, void* stre
 /*
  * la_chunk_fwd_workspace_bytes -- bytes of device workspace la_chunk_fwd and
  * la_chunk_fwd_norm need for this problem (0 when none is needed): per-segment
- * state (and normaliser) increments when the sequence is split into segments,
- * and the in-chunk prefix sums of log a (4 bytes per head-token) for the
- * token-dependent decays.  Pure host function; returns 0 for arguments
- * la_chunk_fwd would reject.
+ * state (and normaliser) increments and a copy of S_0 when the sequence is
+ * split into segments, a copy of z_0 when the normalised form spreads a head
+ * over several workgroups (the workgroup that writes S_L or z_L back may
+ * finish before the others have read S_0 or z_0), and the in-chunk prefix
+ * sums of log a (4 bytes per head-token) for the token-dependent decays.
+ * Pure host function; returns 0 for arguments la_chunk_fwd would reject.
  */
 size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype,
                                     int decay_kind);

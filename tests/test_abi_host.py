@@ -74,7 +74,20 @@ def test_workspace_is_required_when_the_plan_splits_the_sequence():
     assert la.chunk_fwd_workspace_bytes(1, 1, 65536, 64, 64, 64, la.LA_BF16, 3) >= need + 65536 * 4
     assert _fwd(L=65536, kind=3, decay=P16, ws=P16, ws_bytes=need) == WS
     assert _fwd(L=65536, ws=None, ws_bytes=0) == WS
-    assert _fwd(L=65536, ws=P16, ws_bytes=need - 1) == WS
+    # the smallest size the host check accepts (past it the call goes on to the
+    # launch, which fails without a GPU): within the query, and one byte less is refused
+    lo, hi = 0, need
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if _fwd(L=65536, ws=P16, ws_bytes=mid) == WS:
+            lo = mid
+        else:
+            hi = mid
+    assert _fwd(L=65536, ws=P16, ws_bytes=hi) != WS
+    assert _fwd(L=65536, ws=P16, ws_bytes=hi - 1) == WS
+    # per-segment increments plus the copy of S_0 the output pass reads (the
+    # last segment's workgroup overwrites the caller's state with S_L)
+    assert P * 64 * 64 * 4 + 64 * 64 * 4 <= hi <= need
     assert _fwd(L=65536, ws=P8, ws_bytes=need) == ALIGN
 
 

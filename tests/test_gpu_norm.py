@@ -74,7 +74,7 @@ def test_norm_head_dims(gpu_lib, dk, dv, C):
 
 
 @pytest.mark.parametrize("tile,segments,parts", [(128, 1, 2), (128, 3, 2), (128, 7, 1), (64, 5, 2),
-                                                 (32, 4, 2), (128, 21, 2)])
+                                                 (32, 4, 2), (128, 21, 2), (64, 1, 2), (32, 1, 1)])
 def test_norm_plan_invariance(gpu_lib, tile, segments, parts):
     la = gpu_lib
     la.set_plan(la.KERNEL_STRIPE, tile, segments, parts)
