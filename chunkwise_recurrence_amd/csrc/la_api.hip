@@ -384,9 +384,13 @@ la_status la_decode_step_norm(const void* q, const void* k, const void* v, int d
 
 namespace {
 
-size_t delta_ws_bytes(int B, int H, int L, int d_k, int d_v) {
+// W (fp32-sized; the matrix-core path keeps it in bf16), U0 in fp32, and on
+// the matrix-core path the chunks' bf16 score rows.
+size_t delta_ws_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
   const size_t ht = (size_t)B * H * L;
-  return round256(ht * d_k * sizeof(float)) + round256(ht * d_v * sizeof(float));
+  size_t by = round256(ht * d_k * sizeof(float)) + round256(ht * d_v * sizeof(float));
+  if (la::delta_uses_mfma(dtype, C, d_k, d_v)) by += round256(ht * la::kDeltaMaxC * 2);
+  return by;
 }
 
 la_status check_delta_shape(int dtype, int B, int H, int L, int d_k, int d_v, int C) {
@@ -402,7 +406,7 @@ extern "C" {
 
 size_t la_delta_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
   if (check_delta_shape(dtype, B, H, L, d_k, d_v, C) != LA_OK || L == 0) return 0;
-  return delta_ws_bytes(B, H, L, d_k, d_v);
+  return delta_ws_bytes(B, H, L, d_k, d_v, C, dtype);
 }
 
 la_status la_delta_fwd(const void* q, const void* k, const void* v, const float* beta, int dtype,
@@ -419,7 +423,7 @@ la_status la_delta_fwd(const void* q, const void* k, const void* v, const float*
       (state && !aligned(state, 16)) || !aligned(beta, 4) ||
       (decay_data && !aligned(decay_data, 4)))
     return LA_ERR_ALIGN;
-  const size_t need = delta_ws_bytes(B, H, L, d_k, d_v);
+  const size_t need = delta_ws_bytes(B, H, L, d_k, d_v, C, dtype);
   if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return LA_ERR_ALIGN;
   la::DeltaArgs a{};
@@ -433,6 +437,10 @@ la_status la_delta_fwd(const void* q, const void* k, const void* v, const float*
   char* ws = static_cast<char*>(workspace);
   a.ws_W = reinterpret_cast<float*>(ws);
   a.ws_U = reinterpret_cast<float*>(ws + round256((size_t)B * H * L * d_k * sizeof(float)));
+  a.ws_P = la::delta_uses_mfma(dtype, C, d_k, d_v)
+               ? ws + round256((size_t)B * H * L * d_k * sizeof(float)) +
+                     round256((size_t)B * H * L * d_v * sizeof(float))
+               : nullptr;
   a.B = B;
   a.H = H;
   a.L = L;

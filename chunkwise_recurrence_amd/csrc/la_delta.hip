@@ -20,7 +20,8 @@
 //   S_{c+1} = e^{b_last} S_c + (diag(e^{b_last - b}) K)^T U
 //
 // Two passes: delta_prep_kernel (one workgroup per head and chunk) solves
-// each chunk's system and writes W and U0 to the workspace; then one
+// each chunk's system and writes W and U0 (and, on the matrix-core path, the
+// chunk's causal scores) to the workspace; then one
 // workgroup per head and 32 value columns (the columns of S are independent
 // under this update) walks the chunks in order: delta_chunk_mfma_kernel for
 // bf16 inputs with C = 64 (bf16 MFMA operands, fp32 accumulation, the state
@@ -354,6 +355,9 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
 //   * W = (T diag(beta e^b)) K and U0 = (T diag(beta)) V on MFMA, with the
 //     fp32 left factor split into a bf16 high part and a bf16 remainder (two
 //     MFMAs, ~16 significant bits); W leaves as bf16, U0 as fp32.
+//   * the chunk's causal scores (q_i . k_j) e^{b_i - b_j} [j <= i] as bf16
+//     rows, computed here once per head and chunk instead of once per value
+//     tile in the sequential pass.
 template <int DK>
 __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a) {
   constexpr int C = 64, QS = DK + 8, CS = C + 8, KST = DK / 32, NCH = DK / 8;
@@ -383,19 +387,62 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   const uint16_t* kc = static_cast<const uint16_t*>(a.k) + rowk * DK;
   const uint16_t* vc = static_cast<const uint16_t*>(a.v) + rowk * DV;
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  for (int idx = tid; idx < C * NCH; idx += 256) {
-    const int row = idx / NCH, ch = idx % NCH;
-    const u32x4 x = row < n ? *reinterpret_cast<const u32x4*>(kc + (size_t)row * DK + 8 * ch) : zero4;
-    *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = x;
+  // query row 16w + l16 as the B operand of the score tiles below, loaded
+  // first so that its latency hides behind the tile loads and G = K K^T
+  // (rows past the sequence re-read its last row, unconditionally, and are
+  // zeroed where the value is used: a load under a condition makes the
+  // compiler wait for it on the spot)
+  const int iq = 16 * w + l16;
+  u32x4 bq[KST];
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (rowk + min(iq, n - 1)) * DK;
+#pragma unroll
+    for (int s = 0; s < KST; ++s) bq[s] = *reinterpret_cast<const u32x4*>(qr + 32 * s + 8 * g4);
   }
+  // beta of token t0 + tid and (wave 0) the decay data of token t0 + lane
+  const float rbeta = a.beta[rowk + min(tid, n - 1)];
+  const bool tok = a.decay_kind == kDecayLog || a.decay_kind == kDecayGate;
+  float rdec = 0.0f;
+  if (w == 0) {
+    if (tok) rdec = a.decay[rowk + min(lane, n - 1)];
+    else if (a.decay_kind == kDecayHead) rdec = logf(a.decay[h]);
+  }
+  // the K and V tiles: every load issued before the first LDS store, so the
+  // workgroup (which handles one chunk) waits for memory once.  A whole chunk
+  // takes no row checks; the short last chunk of a sequence re-reads its last
+  // row and zeroes the rows past it.
+  constexpr int PK = C * NCH / 256;   // 16-byte pieces of K per thread
+  constexpr int PV = C * 16 / 256;    // ... of V at most (d_v <= 128)
+  static_assert(PK >= 1 && C * NCH % 256 == 0, "K tile pieces per thread");
   const int VCH = DV / 8;
-  for (int idx = tid; idx < C * VCH; idx += 256) {
-    const int row = idx / VCH, ch = idx % VCH;
-    const u32x4 x = row < n ? *reinterpret_cast<const u32x4*>(vc + (size_t)row * DV + 8 * ch) : zero4;
-    *reinterpret_cast<u32x4*>(&sV[row * VS + 8 * ch]) = x;
-  }
-  if (tid < C) sbeta[tid] = tid < n ? a.beta[rowk + tid] : 0.0f;
-  if (w == 0) chunk_log_prefix_wave(a, bh, h, t0, n, sb);
+  auto stage = [&](bool whole) {
+    u32x4 xk[PK], xv[PV];
+#pragma unroll
+    for (int p = 0; p < PK; ++p) {
+      const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
+      xk[p] = *reinterpret_cast<const u32x4*>(kc + (size_t)(whole ? row : min(row, n - 1)) * DK + 8 * ch);
+    }
+    // (pieces past a narrower V tile repeat its last piece, load and store)
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+      const int idx = min(tid + 256 * p, C * VCH - 1), row = idx / VCH, ch = idx % VCH;
+      xv[p] = *reinterpret_cast<const u32x4*>(vc + (size_t)(whole ? row : min(row, n - 1)) * DV + 8 * ch);
+    }
+#pragma unroll
+    for (int p = 0; p < PK; ++p) {
+      const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
+      *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = (whole || row < n) ? xk[p] : zero4;
+    }
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+      const int idx = min(tid + 256 * p, C * VCH - 1), row = idx / VCH, ch = idx % VCH;
+      *reinterpret_cast<u32x4*>(&sV[row * VS + 8 * ch]) = (whole || row < n) ? xv[p] : zero4;
+    }
+  };
+  if (n == C) stage(true);
+  else stage(false);
+  if (tid < C) sbeta[tid] = tid < n ? rbeta : 0.0f;
+  if (w == 0) chunk_log_prefix_reg(a, rdec, n, sb);  // log2 units
   for (int idx = tid; idx < C * C; idx += 256) sT[idx / C][idx % C] = 0.0f;
   lds_barrier();
 
@@ -412,7 +459,34 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * w + 4 * g4 + r;
-      sN[i][j] = (j < i && i < n) ? sbeta[i] * acc[r] * expf(sb[i] - sb[j]) : 0.0f;
+      sN[i][j] = (j < i && i < n) ? sbeta[i] * acc[r] * ex2(sb[i] - sb[j]) : 0.0f;
+    }
+  }
+  // The chunk's causal scores P[i][j] = (q_i . k_j) e^{b_i - b_j} [j <= i] for
+  // the sequential pass, which then needs no score products of its own: wave
+  // w, query rows i = 16w .. 16w + 15 (q straight from memory as the B
+  // operand), every token column (zeros above the diagonal), bf16 rows.
+  {
+    const int i = iq;
+    uint16_t* po = static_cast<uint16_t*>(a.ws_P) + (rowk + i) * C;
+#pragma unroll
+    for (int jt = 0; jt < C / 16; ++jt) {
+      float pv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (jt <= w) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KST; ++s) {
+          const u32x4 ak = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
+          acc = mfma16x16x32(ak, i < n ? bq[s] : zero4, acc);
+        }
+        // register r: token j = 16 jt + 4 g4 + r of query row i
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jt + 4 * g4 + r;
+          pv[r] = j <= i ? acc[r] * ex2(sb[i] - sb[j]) : 0.0f;
+        }
+      }
+      if (i < n) *reinterpret_cast<uint2*>(po + 16 * jt + 4 * g4) = make_uint2(cvt2(pv[0], pv[1]), cvt2(pv[2], pv[3]));
     }
   }
   lds_barrier();
@@ -458,8 +532,8 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
       const int i = idx / (C / 2), m = 2 * (idx % (C / 2));
       float x0 = sT[i][m] * sbeta[m], x1 = sT[i][m + 1] * sbeta[m + 1];
       if (with_decay) {
-        x0 *= expf(sb[m]);
-        x1 *= expf(sb[m + 1]);
+        x0 *= ex2(sb[m]);
+        x1 *= ex2(sb[m + 1]);
       }
       const uint32_t hi = cvt2(x0, x1);
       const float r0 = x0 - bf16_to_f32(hi & 0xffffu), r1 = x1 - bf16_to_f32(hi >> 16);
@@ -515,13 +589,14 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 // bf16 copy S^T in LDS (double-buffered by chunk parity) as the B operand of
 // W S and Q S.  Per chunk:
 //   (1) U = U0 - W S for the wave's rows -> U^T and (e^{b_last - b} U)^T in
-//       LDS (bf16); the scores P^T = K Q^T of the wave's query columns,
-//       masked and decayed -> P in LDS (bf16);
+//       LDS (bf16); the chunk's masked, decayed scores P come ready from the
+//       solve pass (bf16 rows in the workspace), so no score products sit on
+//       this pass's chunk-to-chunk critical path;
 //   (2) O = diag(e^b) Q S + P U for the wave's rows -> HBM; the state update
 //       S = e^{b_last} S + K^T (e^{b_last - b} U), the K^T operand read from
 //       the row-major K tile with transpose reads; the new S^T to the other
 //       LDS buffer.
-// The next chunk's q, k, W and U0 are loaded into registers while the
+// The next chunk's q, k, W, P and U0 are loaded into registers while the
 // current one computes.
 template <int DK, int TV>
 __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a) {
@@ -535,6 +610,7 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   constexpr int NCH = DK / 8;       // 16-byte pieces of one Q/K/W row
   constexpr int PER = C * NCH / 256;
   static_assert(PER >= 1 && C * NCH % 256 == 0, "tile pieces per thread");
+  constexpr int PPER = C * (C / 8) / 256;  // 16-byte pieces of the score tile per thread
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -562,12 +638,13 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * L * DK;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
   const uint16_t* wh = reinterpret_cast<const uint16_t*>(a.ws_W) + (size_t)bh * L * DK;
+  const uint16_t* ph = static_cast<const uint16_t*>(a.ws_P) + (size_t)bh * L * C;
   const float* uh = a.ws_U + (size_t)bh * L * DV + dv0;
   uint16_t* oh = static_cast<uint16_t*>(a.out) + (size_t)bh * L * DV + dv0;
 
   // ---- register prefetch of one chunk: q, k, W rows and this lane's U0 ----
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  u32x4 rq[PER], rk[PER], rw[PER];
+  u32x4 rq[PER], rk[PER], rw[PER], rp[PPER];
   float ru[NT][4];
   float rdec = 0.0f;  // wave 0: the decay data of token t0 + lane
   const bool tok = a.decay_kind == kDecayLog || a.decay_kind == kDecayGate;
@@ -584,6 +661,11 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
         rq[p] = *reinterpret_cast<const u32x4*>(qh + off);
         rk[p] = *reinterpret_cast<const u32x4*>(kh + off);
         rw[p] = *reinterpret_cast<const u32x4*>(wh + off);
+      }
+#pragma unroll
+      for (int p = 0; p < PPER; ++p) {
+        const int idx = tid + 256 * p, row = idx / (C / 8), ch = idx % (C / 8);
+        rp[p] = *reinterpret_cast<const u32x4*>(ph + (size_t)(t0 + row) * C + 8 * ch);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -605,6 +687,11 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
         rk[p] = zero4;
         rw[p] = zero4;
       }
+    }
+#pragma unroll
+    for (int p = 0; p < PPER; ++p) {
+      const int idx = tid + 256 * p, row = idx / (C / 8), ch = idx % (C / 8);
+      rp[p] = row < n ? *reinterpret_cast<const u32x4*>(ph + (size_t)(t0 + row) * C + 8 * ch) : zero4;
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -654,6 +741,11 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
       *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = rk[p];
       *reinterpret_cast<u32x4*>(&sW[row * QS + 8 * ch]) = rw[p];
     }
+#pragma unroll
+    for (int p = 0; p < PPER; ++p) {
+      const int idx = tid + 256 * p, row = idx / (C / 8), ch = idx % (C / 8);
+      *reinterpret_cast<u32x4*>(&sP[row * CS + 8 * ch]) = rp[p];
+    }
     if (w == 0) chunk_log_prefix_reg(a, rdec, n, sb);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -693,41 +785,7 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
                                                          cvt2(u[2] * wt[2], u[3] * wt[3]));
       }
     }
-    // (1b) the causal P^T tiles (query tile qt, token tile jt <= qt), 10 of
-    //      them spread over the waves: P^T = K Q^T, lane = query 16 qt + l16,
-    //      registers = tokens 16 jt + 4 g4 + r; masked, decayed -> P (row-major).
-    //      The two tiles above the diagonal that the P U k-steps still cover
-    //      ((0, 1) and (2, 3)) are written as zeros.
-    for (int tix = w; tix < 12; tix += 4) {
-      int qt, jt;
-      if (tix < 10) {
-        qt = tix < 1 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
-        jt = tix - qt * (qt + 1) / 2;
-      } else {
-        qt = tix == 10 ? 0 : 2;
-        jt = qt + 1;
-      }
-      const int i = 16 * qt + l16;
-      float pv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (jt <= qt) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KST; ++s) {
-          const u32x4 ak = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
-          const u32x4 bq = *reinterpret_cast<const u32x4*>(&sQ[i * QS + 32 * s + 8 * g4]);
-          acc = mfma16x16x32(ak, bq, acc);
-        }
-        const float bi = sb[i];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jt + 4 * g4 + r;
-          pv[r] = j <= i ? acc[r] * ex2(bi - sb[j]) : 0.0f;
-        }
-      }
-      *reinterpret_cast<uint2*>(&sP[i * CS + 16 * jt + 4 * g4]) =
-          make_uint2(cvt2(pv[0], pv[1]), cvt2(pv[2], pv[3]));
-    }
-    lds_barrier();  // U^T, (wU)^T and P complete
+    lds_barrier();  // U^T and (wU)^T complete
 
     // (2a) O = diag(e^b) Q S + P U for rows 16w .. 16w + 15
     {
@@ -811,7 +869,7 @@ hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
   // the MFMA pass numbers its workgroups by groups of 8 heads (see there)
   const dim3 gm(((a.B * a.H + 7) / 8) * 8 * a.n_v);
   // bf16 inputs, C = 64, d_k >= 32 and whole 32-column value tiles: the MFMA pass
-  const bool mfma = BF16 && a.C == 64 && a.DK >= 32 && a.DV % 32 == 0;
+  const bool mfma = BF16 && delta_uses_mfma(a.dtype, a.C, a.DK, a.DV);
   switch (a.DK) {
 #define LA_DK(D)                                                                  \
   case D:                                                                         \
@@ -846,8 +904,7 @@ hipError_t launch_delta(const DeltaArgs& a, hipStream_t s) {
   int tv = a.DV < kDeltaTile ? a.DV : kDeltaTile;
   // the MFMA pass: 16-column workgroups when 32-column ones would leave
   // fewer than two per compute unit of an MI355X (256 of them)
-  if (a.dtype == kBF16 && a.C == 64 && a.DK >= 32 && a.DV % 32 == 0 &&
-      (long long)a.B * a.H * (a.DV / 32) < 512)
+  if (delta_uses_mfma(a.dtype, a.C, a.DK, a.DV) && (long long)a.B * a.H * (a.DV / 32) < 512)
     tv = 16;
   b.n_v = a.DV / tv;
   return a.dtype == kBF16 ? launch_dk<true>(b, s) : launch_dk<false>(b, s);

@@ -59,10 +59,19 @@ struct DeltaArgs {
   const float* decay;   // nullptr | gamma[H] | [B,H,L]
   float* ws_W;          // [B*H, L, DK] W = T diag(beta e^b) K per chunk
   float* ws_U;          // [B*H, L, DV] U0 = T diag(beta) V per chunk
+  void* ws_P;           // matrix-core path: [B*H, L, kDeltaMaxC] bf16 rows of each chunk's
+                        // causal scores (q_i . k_j) e^{b_i - b_j} [j <= i]
   int B, H, L, DK, DV, C;
   int decay_kind, dtype;
   int n_v;              // value tiles per head
 };
+
+// The delta rule's matrix-core path (bf16 inputs, 64-token chunks, d_k >= 32,
+// whole 32-column value tiles); other problems take the fp32-arithmetic
+// kernels.
+inline bool delta_uses_mfma(int dtype, int C, int DK, int DV) {
+  return dtype == kBF16 && C == 64 && DK >= 32 && DV % 32 == 0;
+}
 
 struct DecodeArgs {
   const void* q;        // [N,H,DK]
