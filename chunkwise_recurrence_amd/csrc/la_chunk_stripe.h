@@ -364,20 +364,46 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
     for (int r = 0; r < 16; ++r) accS[t][r] = 0.0f;
   if constexpr (!STATE_ONLY) {
+    // S_in = S_0 composed with the (decay, increment) pairs of the earlier
+    // segments, GS segments at a time with every load of a batch issued
+    // before the first use: one wait for memory per batch, not one per
+    // segment and state element.  Segments past sigma in the last batch
+    // re-read segment sigma - 1 and are weighted out (factor 1, increment 0).
     const int dv = dv0 + cw + l32;
+    auto dk_of = [&](int t, int r) { return 32 * (mk0 + t) + 8 * (r >> 2) + 4 * h + (r & 3); };
+    if (a.s0 != nullptr) {
 #pragma unroll
-    for (int t = 0; t < G::NMK_OWN; ++t)
+      for (int t = 0; t < G::NMK_OWN; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dk = 32 * (mk0 + t) + 8 * (r >> 2) + 4 * h + (r & 3);
-        float sv = a.s0 ? a.s0[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
-        for (int p = 0; p < sigma; ++p) {
-          const size_t seg = (size_t)bh * a.P + p;
-          const float la2 = CHN ? a.ws_logA[seg * DK + dk] : a.ws_logA[seg];
-          sv = exp2f(la2) * sv + a.ws_S[(seg * DK + dk) * DV + dv];
-        }
-        accS[t][r] = sv;
+        for (int r = 0; r < 16; ++r) accS[t][r] = a.s0[((size_t)bh * DK + dk_of(t, r)) * DV + dv];
+    }
+    constexpr int GS = CHN ? 2 : 4;
+    for (int p0 = 0; p0 < sigma; p0 += GS) {
+      float inc[GS][G::NMK_OWN][16], lg[GS][CHN ? G::NMK_OWN : 1][CHN ? 16 : 1];
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const size_t seg = (size_t)bh * a.P + min(p0 + g, sigma - 1);
+#pragma unroll
+        for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            inc[g][t][r] = a.ws_S[(seg * DK + dk_of(t, r)) * DV + dv];
+            if constexpr (CHN) lg[g][t][r] = a.ws_logA[seg * DK + dk_of(t, r)];
+          }
+        if constexpr (!CHN) lg[g][0][0] = a.ws_logA[seg];
       }
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const float m = p0 + g < sigma ? 1.0f : 0.0f;
+#pragma unroll
+        for (int t = 0; t < G::NMK_OWN; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float la2 = CHN ? lg[g][CHN ? t : 0][CHN ? r : 0] : lg[g][0][0];
+            accS[t][r] = exp2f(la2 * m) * accS[t][r] + m * inc[g][t][r];
+          }
+      }
+    }
   }
   // State pass: the first segment's workgroups copy S_0 for the output pass,
   // whose last segment overwrites the caller's state with S_L.  The values are
