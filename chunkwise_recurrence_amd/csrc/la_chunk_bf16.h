@@ -290,22 +290,49 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
 #pragma unroll
   for (int t = 0; t < G::TPW; ++t) accS[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (!STATE_ONLY) {
+    // S_in = S_0 composed with the (decay, increment) pairs of the earlier
+    // segments, four segments at a time with every load of a batch issued
+    // before the first use (one wait for memory per batch).  Segments past
+    // sigma in the last batch re-read segment sigma - 1 and are weighted out;
+    // tiles past a wave's share read tile NT_S - 1 and are never stored.
+    const int dv = dvg + 16 * nt_w + l16;
+    auto idx_of = [&](int t, int i) {
+      const int mt = min(wl + 4 * t, G::NT_S - 1) / G::NTV;
+      return (size_t)(16 * mt + 4 * g4 + i) * DV + dv;
+    };
+    if (a.s0 != nullptr) {
+#pragma unroll
+      for (int t = 0; t < G::TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accS[t][i] = a.s0[(size_t)bh * DK * DV + idx_of(t, i)];
+    }
+    constexpr int GS = 4;
+    for (int p0 = 0; p0 < sigma; p0 += GS) {
+      float inc[GS][G::TPW][4], lg[GS];
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const size_t seg = (size_t)bh * a.P + min(p0 + g, sigma - 1);
+        lg[g] = a.ws_logA[seg];
+#pragma unroll
+        for (int t = 0; t < G::TPW; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) inc[g][t][i] = a.ws_S[seg * DK * DV + idx_of(t, i)];
+      }
+#pragma unroll
+      for (int g = 0; g < GS; ++g) {
+        const float m = p0 + g < sigma ? 1.0f : 0.0f;
+        const float e = exp2f(lg[g] * m);
+#pragma unroll
+        for (int t = 0; t < G::TPW; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) accS[t][i] = e * accS[t][i] + m * inc[g][t][i];
+      }
+    }
 #pragma unroll
     for (int t = 0; t < G::TPW; ++t) {
       const int tau = wl + 4 * t;
       if (tau < G::NT_S) {
         const int mt = tau / G::NTV;
-        const int dv = dvg + 16 * nt_w + l16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int dk = 16 * mt + 4 * g4 + i;
-          float s = a.s0 ? a.s0[((size_t)bh * DK + dk) * DV + dv] : 0.0f;
-          for (int p = 0; p < sigma; ++p) {
-            const size_t seg = (size_t)bh * a.P + p;
-            s = exp2f(a.ws_logA[seg]) * s + a.ws_S[(seg * DK + dk) * DV + dv];
-          }
-          accS[t][i] = s;
-        }
         u32x2 w;
         w[0] = cvt2(accS[t][0], accS[t][1]);
         w[1] = cvt2(accS[t][2], accS[t][3]);
