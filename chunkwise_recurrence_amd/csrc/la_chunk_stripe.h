@@ -431,10 +431,21 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       const int dk = 32 * (mk0 + t) + l32;
       float zv = 0.0f;
       if constexpr (!STATE_ONLY) {
+        // composed like S_in: four segments' loads per wait
         zv = a.z0 ? a.z0[(size_t)bh * DK + dk] : 0.0f;
-        for (int p = 0; p < sigma; ++p) {
-          const size_t seg = (size_t)bh * a.P + p;
-          zv = exp2f(a.ws_logA[seg]) * zv + a.ws_z[seg * DK + dk];
+        for (int p0 = 0; p0 < sigma; p0 += 4) {
+          float zi[4], lz[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const size_t seg = (size_t)bh * a.P + min(p0 + g, sigma - 1);
+            lz[g] = a.ws_logA[seg];
+            zi[g] = a.ws_z[seg * DK + dk];
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float m = p0 + g < sigma ? 1.0f : 0.0f;
+            zv = exp2f(lz[g] * m) * zv + m * zi[g];
+          }
         }
       }
       zr[t] = zv;
