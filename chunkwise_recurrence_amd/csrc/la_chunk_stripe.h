@@ -936,7 +936,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
           const int row = (lane >> 2) + 16 * it, cc = lane & 3;
           const u32x4 w = lds_b128(so, swz<4>(row, 8 * cc));
           if (32 * I + row < nvalid)
-            *reinterpret_cast<u32x4*>(oh + (size_t)(t0 + 32 * I + row) * DV + 8 * cc) = w;
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(oh + (size_t)(t0 + 32 * I + row) * DV + 8 * cc));
         }
         lds_wave_sync();
       }
