@@ -510,8 +510,13 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       if (idx < G::QK_BLK) {
         // rows past the sequence re-read its last row; they are zeroed before use
         const int off = full ? koff[i] : koff[i] - max(krow[i] - (L - 1 - t0), 0) * DK;
-        dma16(kc + off, stage_k(BUF) + 1024 * idx);
-        if constexpr (!STATE_ONLY) dma16(qc + off, stage_q(BUF) + 1024 * idx);
+        // (the output pass reads q, k and v for the last time)
+        if constexpr (STATE_ONLY) {
+          dma16(kc + off, stage_k(BUF) + 1024 * idx);
+        } else {
+          dma16_nt(kc + off, stage_k(BUF) + 1024 * idx);
+          dma16_nt(qc + off, stage_q(BUF) + 1024 * idx);
+        }
       }
     }
 #pragma unroll
@@ -519,7 +524,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       const int idx = wave + NW * i;
       if (idx < G::V_BLK) {
         const int off = full ? voff[i] : voff[i] - max(vrow[i] - (L - 1 - t0), 0) * DV;
-        dma16(vc + off, stage_v(BUF) + 1024 * idx);
+        if constexpr (STATE_ONLY) dma16(vc + off, stage_v(BUF) + 1024 * idx);
+        else dma16_nt(vc + off, stage_v(BUF) + 1024 * idx);
       }
     }
     if constexpr (CAT == kCatToken) {

@@ -71,6 +71,14 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
       "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
       : "=&s"(keep) : "v"(src), "s"(lds_u32(dst)) : "memory");
 }
+// The same with the non-temporal hint, for data read for the last time.
+__device__ __forceinline__ void dma16_nt(const void* src, void* dst) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep) : "v"(src), "s"(lds_u32(dst)) : "memory");
+}
 __device__ __forceinline__ void dma4(const void* src, void* dst) {
   uint32_t keep;
   asm volatile(
