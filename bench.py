@@ -84,6 +84,21 @@ def chunk_algorithmic(w, with_state: bool):
     return by, flops
 
 
+SETTLE_S = 0.1  # seconds of untimed steps before each forward leg's warm-up
+
+
+def settle(torch, fn):
+    """Run fn untimed for SETTLE_S seconds of wall time.  The inputs of each leg
+    are drawn on the CPU, during which the GPU idles and lowers its clocks; it
+    takes some milliseconds of work to bring them back, longer than a few
+    warm-up steps last, so without this the first timed steps run slow."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
 def bench_chunk(la, torch, W, steps, warmup):
     w = W.WORKLOADS["retnet_bf16"]
     dev = torch.device("cuda:0")
@@ -100,6 +115,7 @@ def bench_chunk(la, torch, W, steps, warmup):
         la.chunk_fwd(q, k, v, C=w.C, phi=w.phi, decay_kind=w.decay_kind, decay=gamma, state=S,
                      out=out, workspace=ws if need else None, stream=stream)
 
+    settle(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -149,6 +165,7 @@ def bench_chunk_norm(la, torch, W, steps, warmup):
                      state=S, out=out, workspace=ws if need else None, stream=stream,
                      normalize=True, norm_state=z)
 
+    settle(torch, call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -181,6 +198,7 @@ def bench_chunk_gla(la, torch, W, steps, warmup):
         la.chunk_fwd(q, k, v, C=w.C, phi=w.phi, decay_kind=w.decay_kind, decay=log_a, state=S,
                      out=out, workspace=ws if need else None, stream=stream)
 
+    settle(torch, call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -211,6 +229,7 @@ def bench_delta(la, torch, W, steps, warmup):
         la.delta_fwd(q, k, v, beta, C=w.C, decay_kind=w.decay_kind, decay=g, state=S, out=out,
                      workspace=ws, stream=stream)
 
+    settle(torch, call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -336,6 +355,9 @@ def main():
     from chunkwise_recurrence_amd import workloads as W
     la.load()
     if args.profile:
+        # counter passes want a short, fixed launch sequence: no settle phase
+        global SETTLE_S
+        SETTLE_S = 0.0
         profile_pass(la, torch, W)
         return
     c = bench_chunk(la, torch, W, args.steps, args.warmup)
