@@ -299,7 +299,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
       a.ws_z = reinterpret_cast<float*>(ws + p.ws_z_off);
       // the state pass copies S_0 for the output pass, whose last segment
       // overwrites state with S_L
-      a.ws_S0 = state ? reinterpret_cast<float*>(ws + p.ws_S0_off) : nullptr;
+      a.ws_S0 = (p.copy_S0 && state) ? reinterpret_cast<float*>(ws + p.ws_S0_off) : nullptr;
       a.n_units = B * H * (p.P - 1);
       e = p.kernel == LA_KERNEL_STRIPE ? la::launch_chunk_stripe(a, /*state_only=*/true, s)
                                        : la::launch_chunk_bf16(a, /*state_only=*/true, s);
