@@ -114,6 +114,10 @@ def test_plans_of_the_workloads():
     # fp32: its own kernel, one segment, 16- or 32-wide tiles
     assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32) == (F32, 16, 1, 1)
     assert la.chunk_fwd_workspace_bytes(1, 1, 300, 16, 16, 64, la.LA_F32) == 0
+    # fp32 with two 32-column value tiles: the normalised form reads z_0 from
+    # a copy (the first tile's workgroup writes z_L back), 256 bytes rounded
+    assert la.chunk_fwd_workspace_bytes(1, 1, 300, 16, 64, 64, la.LA_F32) == 256
+    assert la.chunk_fwd_workspace_bytes(2, 3, 300, 32, 64, 64, la.LA_F32) == 2 * 3 * 32 * 4
 
 
 def test_plan_override_and_clamping():
