@@ -233,3 +233,56 @@ def test_head_permutation_equivariance(gpu_lib):
     op, _ = _gpu_fwd(la, q[:, perm].contiguous(), k[:, perm].contiguous(), v[:, perm].contiguous(),
                      64, 1, 0, None, None)
     assert torch.equal(o[:, perm], op)
+
+
+# --------------------------------------------------------------------------
+# degenerate decays: a = 1, a -> 0, gates saturated both ways
+# --------------------------------------------------------------------------
+def _degenerate_inputs(dk, dv, H, L, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(1, H, L, dk, generator=g) / np.sqrt(dk)).to(dtype)
+    k = (torch.randn(1, H, L, dk, generator=g) / np.sqrt(dk)).to(dtype)
+    v = torch.randn(1, H, L, dv, generator=g).to(dtype)
+    s0 = torch.randn(1, H, dk, dv, generator=g) * 0.1
+    # per token, saturated gates: g = +30 (a = e^-30, nearly a reset) or g = -30
+    # (a = 1 to fp32 precision), and ordinary ones, mixed at random
+    pick = torch.randint(0, 3, (1, H, L), generator=g)
+    gate = torch.where(pick == 0, torch.full((1, H, L), 30.0),
+                       torch.where(pick == 1, torch.full((1, H, L), -30.0),
+                                   torch.randn(1, H, L, generator=g)))
+    return q, k, v, s0, gate
+
+
+@pytest.mark.parametrize("dtype,dk,dv,plan", [
+    (torch.bfloat16, 128, 128, (0, 0, 0, 0)), (torch.bfloat16, 128, 128, (2, 128, 3, 2)),
+    (torch.bfloat16, 64, 64, (0, 0, 0, 0)), (torch.bfloat16, 64, 64, (1, 32, 4, 1)),
+    (torch.float32, 32, 64, (0, 0, 0, 0))])
+def test_degenerate_decays(gpu_lib, dtype, dk, dv, plan):
+    """gamma = 1 exactly, gamma = 1e-20 (the a -> 0 limit: every step forgets the
+    past), 1 - 2^-20 and 0.5 across heads; saturated gates both ways per token.
+    Exponents reach -4e3 in log2 units: no inf - inf, no NaN, and a carried
+    state of fp32 zeros where the decay wipes it."""
+    la = gpu_lib
+    la.set_plan(*plan)
+    try:
+        H, L = 4, 64 * 6 + 29
+        q, k, v, s0, gate = _degenerate_inputs(dk, dv, H, L, dtype, seed=dk + dv + plan[2])
+        gamma = torch.tensor([1.0, 1e-20, 1.0 - 2.0 ** -20, 0.5], dtype=torch.float32)
+        tol = TOL[dtype]
+        for kind, d in ((W.DECAY_HEAD, gamma), (W.DECAY_GATE, gate)):
+            out, s_out = _gpu_fwd(la, q, k, v, 64, 0, kind, d, s0)
+            ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), 0, kind, _np(d), _np(s0))
+            assert torch.isfinite(out.float()).all() and torch.isfinite(s_out).all()
+            e_out, e_s = oracle.rel_err(_np(out), ref), oracle.rel_err(_np(s_out), ref_s)
+            print(f"[degenerate] plan={plan} dtype={dtype} kind={kind}: out {e_out:.2e} "
+                  f"state {e_s:.2e}", flush=True)
+            assert e_out <= tol and e_s <= tol
+            if kind == W.DECAY_HEAD:
+                # head 1 (gamma = 1e-20) keeps only the current token:
+                # o_t = (q_t . k_t) v_t, a closed form independent of the oracle
+                qd, kd, vd = (_np(x[0, 1]) for x in (q, k, v))
+                closed = (qd * kd).sum(-1, keepdims=True) * vd
+                got = _np(out[0, 1])
+                assert np.abs(got - closed).max() <= tol * np.abs(closed).max()
+    finally:
+        la.set_plan()
