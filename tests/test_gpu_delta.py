@@ -168,3 +168,37 @@ def test_delta_many_heads_takes_the_32_column_pass(gpu_lib):
     c = W.RandomCase(4, 32, 64 * 2 + 5, 128, 128, torch.bfloat16, W.PHI_IDENTITY, W.DECAY_GATE,
                      seed=670, scale=1.0 / np.sqrt(128), with_state=True)
     _run(gpu_lib, c, 64, "32-column pass")
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 64),
+                                         (torch.float32, 32, 64)])
+def test_delta_degenerate_gates_and_strengths(gpu_lib, dtype, dk, dv):
+    """Saturated gates (g = +30: a = e^-30, g = -30: a = 1 to fp32 precision)
+    mixed with ordinary ones per token, and write strengths at the ends of
+    their range (beta = 0: no write; beta = 1 with a unit key: the key's
+    direction is replaced), against the oracle."""
+    la = gpu_lib
+    B, H, L = 1, 3, 64 * 4 + 21
+    g = torch.Generator().manual_seed(700 + dk + dv)
+    q = (torch.randn(B, H, L, dk, generator=g) / np.sqrt(dk)).to(dtype)
+    kr = torch.randn(B, H, L, dk, generator=g)
+    k = (kr / kr.norm(dim=-1, keepdim=True)).to(dtype)
+    v = torch.randn(B, H, L, dv, generator=g).to(dtype)
+    pick = torch.randint(0, 3, (B, H, L), generator=g)
+    beta = torch.where(pick == 0, torch.zeros(B, H, L),
+                       torch.where(pick == 1, torch.ones(B, H, L), torch.rand(B, H, L, generator=g)))
+    pick = torch.randint(0, 3, (B, H, L), generator=g)
+    gate = torch.where(pick == 0, torch.full((B, H, L), 30.0),
+                       torch.where(pick == 1, torch.full((B, H, L), -30.0),
+                                   torch.randn(B, H, L, generator=g)))
+    S0 = torch.randn(B, H, dk, dv, generator=g) * 0.1
+    S = S0.to(DEV).contiguous()
+    out = la.delta_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), C=64,
+                       decay_kind=W.DECAY_GATE, decay=gate.to(DEV), state=S)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.delta_recurrent(_np(q), _np(k), _np(v), _np(beta), W.DECAY_GATE,
+                                        _np(gate), _np(S0))
+    assert torch.isfinite(out.float()).all() and torch.isfinite(S).all()
+    tol = TOL[dtype]
+    e = (oracle.rel_err(_np(out), ref), oracle.rel_err(_np(S), ref_s))
+    assert e[0] <= tol and e[1] <= tol, f"out/state rel err {e}"

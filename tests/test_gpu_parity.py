@@ -286,3 +286,37 @@ def test_degenerate_decays(gpu_lib, dtype, dk, dv, plan):
                 assert np.abs(got - closed).max() <= tol * np.abs(closed).max()
     finally:
         la.set_plan()
+
+
+def test_decode_degenerate_decays(gpu_lib):
+    """Decode steps with gamma = 1, 1e-20 (S' = k v^T: the step forgets the
+    state), 1 - 2^-20 and 0.5 across heads, then with saturated gates."""
+    la = gpu_lib
+    dev = torch.device("cuda:0")
+    N, H, d = 4, 4, 128
+    g = torch.Generator().manual_seed(990)
+    S0 = torch.randn(N, H, d, d, generator=g) * 0.1
+    gamma = torch.tensor([1.0, 1e-20, 1.0 - 2.0 ** -20, 0.5], dtype=torch.float32)
+    for kind in (W.DECAY_HEAD, W.DECAY_GATE):
+        S = S0.to(dev).contiguous()
+        ref_S = _np(S0)
+        for t in range(3):
+            q, k, v = ((torch.randn(N, H, d, generator=g) / np.sqrt(d)).to(torch.bfloat16)
+                       for _ in range(3))
+            if kind == W.DECAY_HEAD:
+                dd = gamma
+            else:
+                dd = torch.where(torch.rand(N, H, generator=g) < 0.5, torch.full((N, H), 30.0),
+                                 torch.full((N, H), -30.0))
+            o = la.decode_step(q.to(dev), k.to(dev), v.to(dev), S, decay_kind=kind,
+                               decay=dd.to(dev))
+            torch.cuda.synchronize()
+            ro, ref_S = oracle.decode_step(_np(q), _np(k), _np(v), 0, kind, _np(dd), ref_S)
+            assert torch.isfinite(o.float()).all()
+            assert oracle.rel_err(_np(o), ro) < 1e-2
+        assert oracle.rel_err(_np(S), ref_S) < 1e-5
+        if kind == W.DECAY_HEAD:
+            # head 1 keeps only the last token's k v^T
+            kd, vd = _np(k[:, 1]), _np(v[:, 1])
+            outer = kd[:, :, None] * vd[:, None, :]
+            assert np.abs(_np(S[:, 1]) - outer).max() <= 1e-5 * np.abs(outer).max()
