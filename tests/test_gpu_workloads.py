@@ -110,3 +110,28 @@ def test_decode_workload_sampled_heads(gpu_lib):
     e_s = oracle.rel_err(got_S, ref_S)
     print(f"decode: worst sampled output rel err {worst:.3e}, state rel err {e_s:.3e}")
     assert worst <= 1e-2 and e_s <= 1e-4
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_single_long_head_many_segments(gpu_lib, d):
+    """One head over 65536 tokens: the plan splits it into 256 segments of four
+    chunks, so the last segment composes 255 earlier (decay, increment) pairs;
+    a mild gate (a ~ 0.993) keeps the state alive across all of them."""
+    la = gpu_lib
+    L = 65536
+    plan = la.plan(1, 1, L, d, d, 64)
+    assert plan[2] == 256, plan
+    w = W.ChunkWorkload(f"long_head_{d}", 1, 1, L, d, d, 64, torch.bfloat16, 0, W.DECAY_GATE,
+                        seed=45 + d, scale=1.0 / np.sqrt(d), gate_shift=-5.0)
+    q, k, v, decay = W.chunk_inputs(w)
+    g = torch.Generator().manual_seed(46 + d)
+    S0 = torch.randn(1, 1, d, d, generator=g) * 0.1
+    dev = torch.device("cuda:0")
+    S = S0.to(dev).contiguous()
+    out = la.chunk_fwd(q.to(dev), k.to(dev), v.to(dev), C=64, decay_kind=W.DECAY_GATE,
+                       decay=decay.to(dev), state=S)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), 0, W.DECAY_GATE, _np(decay), _np(S0))
+    e_out, e_s = oracle.rel_err(_np(out.cpu()), ref), oracle.rel_err(_np(S.cpu()), ref_s)
+    print(f"long head d={d} plan={plan}: out {e_out:.3e} state {e_s:.3e}")
+    assert e_out <= 1e-2 and e_s <= 1e-2
