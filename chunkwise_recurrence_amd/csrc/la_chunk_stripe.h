@@ -580,6 +580,25 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       wait_vmcnt<0>();
     }
     lds_barrier();  // everybody's loads of this chunk landed; the previous one is finished
+    // per-channel decay: this thread's in-run prefix of log2 a (tokens past the
+    // sequence contribute nothing), taken from its registers before the next
+    // chunk's loads are issued -- the compiler waits for those registers by
+    // count and does not see the tile copies, so a later wait would also
+    // hold back the next chunk's copies
+    constexpr float kLog2e = 1.4426950408889634f;
+    f32x2 bl[CHN ? G::TPR : 1];
+    f32x2 accb = f32x2{0.0f, 0.0f};
+    if constexpr (CHN) {
+#pragma unroll
+      for (int i = 0; i < G::TPR; ++i) {
+        const f32x2 x = lreg[buf][i] * kLog2e;
+        accb += run * G::TPR + i < nvalid ? x : f32x2{0.0f, 0.0f};
+        bl[i] = accb;
+      }
+      // the run total depends on every register: using it here keeps the
+      // compiler's wait for them ahead of the copies below
+      asm volatile("" ::"v"(accb[0]), "v"(accb[1]));
+    }
     if (it + NS - 1 < n_it) issue_loads(std::integral_constant<int, (buf + NS - 1) % NS>{}, it + NS - 1);
 
     // a short last chunk: zero the rows past the sequence (clamped copies)
@@ -607,17 +626,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     }
 
     if constexpr (CHN) {
-      // in-chunk prefix of log2 a over this thread's run (tokens past the
-      // sequence contribute nothing), then the runs' totals through LDS
-      constexpr float kLog2e = 1.4426950408889634f;
-      f32x2 bl[G::TPR];
-      f32x2 accb = f32x2{0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < G::TPR; ++i) {
-        const f32x2 x = lreg[buf][i] * kLog2e;
-        accb += run * G::TPR + i < nvalid ? x : f32x2{0.0f, 0.0f};
-        bl[i] = accb;
-      }
+      // the runs' totals of the in-run prefixes through LDS
       *reinterpret_cast<f32x2*>(&sTot[run][2 * pr]) = accb;
       lds_barrier();
       f32x2 off = f32x2{0.0f, 0.0f}, tot = f32x2{0.0f, 0.0f};
