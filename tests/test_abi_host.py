@@ -101,9 +101,13 @@ def test_plans_of_the_workloads():
     assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
     # gated: 16 heads x 16 segments
     assert la.plan(1, 16, 65536, 128, 128, 64) == (STRIPE, 128, 16, 2)
-    # narrower heads: the strip kernel over 32-column tiles.  elu: 64 heads x
-    # 2 tiles x 4 segments
-    assert la.plan(4, 16, 4096, 64, 64, 64) == (STRIP, 32, 4, 1)
+    # narrower heads: the strip kernel.  64-wide value heads with d_k >= 64
+    # take one 64-column tile in two groups; elu: 64 heads x 2 groups x 4
+    # segments, the 512 4-wave units of 32-column tiles
+    assert la.plan(4, 16, 4096, 64, 64, 64) == (STRIP, 64, 4, 2)
+    assert la.plan(2, 32, 8192, 128, 64, 64) == (STRIP, 64, 4, 2)
+    # d_k = 32 keeps 32-column tiles in one group
+    assert la.plan(2, 32, 8192, 32, 64, 64) == (STRIP, 32, 4, 1)
     assert la.plan(1, 1, 100, 16, 16, 16) == (STRIP, 16, 1, 1)
     # 16-token chunks, d_k = 16: the strip kernel
     assert la.plan(1, 1, 100, 128, 128, 16)[0] == STRIP
