@@ -465,6 +465,21 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
     } else {
       wait_vmcnt<0>();
     }
+    // feature map on this wave's own copies of the chunk's key blocks, in
+    // place: they have landed (the wait above; a copy's lane l fills bytes
+    // 16l..16l+15 of its block) and no other wave reads them before the
+    // barrier below, which then also publishes the result
+    if (elu) {
+#pragma unroll
+      for (int i = 0; i < KBLK; ++i) {
+        const int idx = wave + NW * i;
+        const int q = 64 * idx + lane;
+        if (64 * idx < G::NK_CHUNKS && q < G::NK_CHUNKS) {
+          u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
+          *p = elu1_x8(*p);
+        }
+      }
+    }
     lds_barrier();  // everybody's loads of chunk c landed; chunk c-1 is finished
     u32x4 qcur[G::SPW][G::KSTEPS];
     if constexpr (!STATE_ONLY) {
@@ -498,14 +513,6 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
         *reinterpret_cast<u32x4*>(kb + 16 * (nvalid * G::WCK + q)) = zero4;
       for (int q = tid; q < (C - nvalid) * G::WCV; q += 64 * NW)
         *reinterpret_cast<u32x4*>(vb + 16 * (nvalid * G::WCV + q)) = zero4;
-      lds_barrier();
-    }
-    // feature map on the staged keys, in place
-    if (elu) {
-      for (int q = tid; q < G::NK_CHUNKS; q += 64 * NW) {
-        u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
-        *p = elu1_x8(*p);
-      }
       lds_barrier();
     }
 

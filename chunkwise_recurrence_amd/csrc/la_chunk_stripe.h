@@ -579,6 +579,25 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     } else {
       wait_vmcnt<0>();
     }
+    // feature map on this wave's own copies of the chunk's key (and query)
+    // blocks, in place: they have landed (the wait above; a copy's lane l
+    // fills bytes 16l..16l+15 of its block) and no other wave reads them
+    // before the barrier below, which then also publishes the result (the
+    // per-channel decay applies the map in its rescaling pass instead)
+    if (elu && !CHN) {
+#pragma unroll
+      for (int i = 0; i < G::QK_PER; ++i) {
+        const int idx = wave + NW * i;
+        if (idx < G::QK_BLK) {
+          u32x4* p = reinterpret_cast<u32x4*>(kb + 1024 * idx + 16 * lane);
+          *p = elu1_x8(*p);
+          if constexpr (!STATE_ONLY) {
+            u32x4* pq = reinterpret_cast<u32x4*>(qb + 1024 * idx + 16 * lane);
+            *pq = elu1_x8(*pq);
+          }
+        }
+      }
+    }
     lds_barrier();  // everybody's loads of this chunk landed; the previous one is finished
     // per-channel decay: this thread's in-run prefix of log2 a (tokens past the
     // sequence contribute nothing), taken from its registers before the next
@@ -609,19 +628,6 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       }
       for (int q = tid; q < (C - nvalid) * G::WCV; q += 64 * NW)
         *reinterpret_cast<u32x4*>(vb + 16 * (nvalid * G::WCV + q)) = zero4;
-      lds_barrier();
-    }
-    // feature map on the staged queries and keys, in place (the per-channel
-    // decay applies it in its rescaling pass below)
-    if (elu && !CHN) {
-      for (int q = tid; q < G::QK_BYTES / 16; q += 64 * NW) {
-        u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
-        *p = elu1_x8(*p);
-        if constexpr (!STATE_ONLY) {
-          u32x4* pq = reinterpret_cast<u32x4*>(qb + 16 * q);
-          *pq = elu1_x8(*pq);
-        }
-      }
       lds_barrier();
     }
 
@@ -733,7 +739,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         u32x4 vB = vA[ks];
         float w[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
         if constexpr (CAT == kCatNone && NORM) {
-          // rows past a short last chunk hold phi(0), not 0: keep them out of z
+          // rows past a short last chunk are zeroed after the feature map;
+          // the mask keeps them out of z whatever they hold
 #pragma unroll
           for (int e = 0; e < 8; ++e) w[e] = 16 * ks + 8 * h + e < nvalid ? 1.0f : 0.0f;
         }
