@@ -197,6 +197,13 @@ __device__ __forceinline__ uint32_t cvt2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// c + a.lo * b.lo + a.hi * b.hi over two packed bf16 values (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -757,17 +764,24 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
           for (int e = 0; e < 4; ++e)
             vB[e] = cvt2(bf16_to_f32(vB[e] & 0xffffu) * w[2 * e], bf16_to_f32(vB[e] >> 16) * w[2 * e + 1]);
         }
+        // the token weights as packed bf16 pairs for z (the value operand
+        // carries them in bf16 too)
+        uint32_t wp[NORM ? 4 : 1];
+        if constexpr (NORM) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wp[e] = cvt2(w[2 * e], w[2 * e + 1]);
+        }
 #pragma unroll
         for (int t = 0; t < G::NMK_OWN; ++t) {
           const u32x4 kA =
               lds_tr8<G::WCK>(kb, 16 * ks + 8 * (g4 >> 1), 32 * (mk0 + t) + 16 * (g4 & 1), l16);
           accS[t] = mfma32(kA, vB, accS[t]);
           if constexpr (NORM) {
-            // z += sum_t w_t phi(k_t) over this lane's 8 tokens of key 32 (mk0 + t) + l32
+            // z += sum_t w_t phi(k_t) over this lane's 8 tokens of key 32 (mk0 + t) + l32,
+            // two tokens per dot product
             if (stripe == 0) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                zacc[t] += w[2 * e] * bf16_to_f32(kA[e] & 0xffffu) + w[2 * e + 1] * bf16_to_f32(kA[e] >> 16);
+              for (int e = 0; e < 4; ++e) zacc[t] = dot2_bf16(kA[e], wp[e], zacc[t]);
             }
           }
         }
