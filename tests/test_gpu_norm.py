@@ -141,3 +141,33 @@ def test_norm_unsupported_shape_is_refused(gpu_lib):
     x = torch.zeros(1, 1, 64, 16, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(la.LAError):
         la.chunk_fwd(x, x, x, C=64, normalize=True)
+
+
+def test_norm_on_the_full_retnet_shapes_sampled_heads(gpu_lib):
+    """The normalised form at the size the benchmark times it: the retnet_bf16
+    inputs ([2,32,16384,128], per-head gamma) with phi = elu+1, S_0 = 0 and
+    z_0 = 0, in the automatic launch plan; four heads against the oracle, each
+    with its own gamma."""
+    la = gpu_lib
+    w = W.WORKLOADS["retnet_bf16"]
+    print(f"[norm case] full retnet shapes plan={la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)}",
+          flush=True)
+    q, k, v, gamma = W.chunk_inputs(w)
+    S = torch.zeros(w.B, w.H, w.dk, w.dv, device=DEV)
+    z = torch.zeros(w.B, w.H, w.dk, device=DEV)
+    out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=w.C, phi=W.PHI_ELU1,
+                       decay_kind=w.decay_kind, decay=gamma.to(DEV), state=S, normalize=True,
+                       norm_state=z)
+    torch.cuda.synchronize()
+    flat = lambda x: x.reshape(w.B * w.H, *x.shape[2:])  # noqa: E731
+    got_o, got_s, got_z = flat(out.cpu()), flat(S.cpu()), flat(z.cpu())
+    for bh in (0, 31, 32, 63):
+        h = bh % w.H
+        one = lambda x: _np(flat(x)[bh][None, None])  # noqa: E731
+        ref_o, ref_s, ref_z = oracle.recurrent(one(q), one(k), one(v), W.PHI_ELU1, W.DECAY_HEAD,
+                                               np.array([float(gamma[h])]), normalize=True)
+        e = (oracle.rel_err(_np(got_o[bh])[None, None], ref_o),
+             oracle.rel_err(_np(got_s[bh])[None, None], ref_s),
+             oracle.rel_err(_np(got_z[bh])[None, None], ref_z))
+        print(f"head {bh}: out/state/z rel err {e}", flush=True)
+        assert max(e) <= 1e-2, f"head {bh}: out/state/z rel err {e}"
