@@ -222,6 +222,29 @@ def parallel(q, k, v, a, phi: int = PHI_IDENTITY, state=None, normalize: bool = 
     return out, SL
 
 
+def chunk_spans(L: int, C: int):
+    """(first, stop) token indices of the chunks of C tokens covering 0..L-1; the
+    last span is shorter when C does not divide L."""
+    firsts = np.arange(0, L, C, dtype=np.int64)
+    stops = np.minimum(firsts + C, L)
+    return list(zip(firsts.tolist(), stops.tolist()))
+
+
+def _decayed_chunk(carry, Qc, Kc, Vc, log_ac, dtype):
+    """One chunk of the decayed chunkwise form.  carry: the [dk, dv'] state on
+    entry (dv' = dv, or dv + 1 with z as the last column).  Returns the chunk's
+    rows of the numerator and the carry on exit."""
+    cum = np.cumsum(log_ac).astype(dtype)           # b_i, inclusive, local to the chunk
+    n = cum.shape[0]
+    causal = np.tri(n, dtype=bool)                  # j <= i, diagonal included
+    gaps = np.where(causal, cum[:, None] - cum[None, :], 0.0)
+    weights = np.where(causal, np.exp(gaps), 0.0).astype(dtype)
+    rows = np.exp(cum)[:, None] * (Qc @ carry) + ((Qc @ Kc.T) * weights) @ Vc
+    tail = np.exp(cum[-1] - cum)                    # e^{b_last - b_j}
+    carry = np.exp(cum[-1]) * carry + (Kc * tail[:, None]).T @ Vc
+    return rows, carry
+
+
 def chunkwise(q, k, v, a, C: int, phi: int = PHI_IDENTITY, state=None, dtype=np.float64,
               normalize: bool = False, norm_state=None):
     """Chunkwise form with decay folded in (log-space, every factor exp(<= 0)).
@@ -229,45 +252,43 @@ def chunkwise(q, k, v, a, C: int, phi: int = PHI_IDENTITY, state=None, dtype=np.
     Per chunk of c <= C tokens with b = inclusive cumsum of log a inside the chunk:
       O_c     = diag(e^b) Q_c S_c + ((Q_c K_c^T) o D_c) V_c,  D_c[i,j] = e^{b_i - b_j} [j <= i]
       S_{c+1} = e^{b_last} S_c + (diag(e^{b_last - b}) K_c)^T V_c
-    A ragged last chunk simply has c < C rows.
+    ("Linear / Sparse Attention" `linear_attn_chunkwise` gives the undecayed
+    form; the tutorial's section 6.2 says the decay folds into S_c and the
+    in-chunk mask; the formulas come from expanding the recurrence over one
+    chunk.)  A ragged last chunk simply has c < C rows.
     `dtype` is the working precision (float64 by default; float32 reproduces
     the magnitude of rounding error the pages print for their fp32 run).
     normalize: z is carried as one more value column of ones (the tutorial's
-    section 6.2 suggestion): the same two formulas with V_c -> 1, and every
-    output row divided by its entry.
+    section 6.2 suggestion), and every output row is divided by its entry.
     """
     fq, fk = feature_map(q, phi).astype(dtype), feature_map(k, phi).astype(dtype)
     v, a = _f64(v).astype(dtype), _f64(a)
     B, H, L, dk = fq.shape
     dv = v.shape[-1]
-    S = np.zeros((B, H, dk, dv), dtype) if state is None else _f64(state).astype(dtype)
+    S0 = np.zeros((B, H, dk, dv)) if state is None else _f64(state)
+    z0 = np.zeros((B, H, dk)) if norm_state is None else _f64(norm_state)
+    width = dv + 1 if normalize else dv
     out = np.zeros((B, H, L, dv), dtype)
-    Z = None
-    if normalize:
-        Z = np.zeros((B, H, dk), dtype) if norm_state is None else _f64(norm_state).astype(dtype)
+    S_fin = np.zeros((B, H, dk, dv), dtype)
+    Z_fin = np.zeros((B, H, dk), dtype) if normalize else None
     with np.errstate(divide="ignore"):
-        la = np.log(a)
-    for b in range(B):
-        for h in range(H):
-            Sh = S[b, h]
-            zh = Z[b, h] if normalize else None
-            for s in range(0, L, C):
-                e = min(s + C, L)
-                Qc, Kc, Vc = fq[b, h, s:e], fk[b, h, s:e], v[b, h, s:e]
-                bc = np.cumsum(la[b, h, s:e]).astype(dtype)
-                diff = bc[:, None] - bc[None, :]
-                mask = np.tril(np.ones((e - s, e - s), dtype=bool))
-                Dc = np.where(mask, np.exp(np.where(mask, diff, 0.0)), 0.0).astype(dtype)
-                out[b, h, s:e] = np.exp(bc)[:, None] * (Qc @ Sh) + ((Qc @ Kc.T) * Dc) @ Vc
-                if normalize:
-                    den = np.exp(bc) * (Qc @ zh) + ((Qc @ Kc.T) * Dc).sum(axis=1)
-                    out[b, h, s:e] /= den[:, None]
-                    zh = np.exp(bc[-1]) * zh + (Kc * np.exp(bc[-1] - bc)[:, None]).sum(axis=0)
-                Sh = np.exp(bc[-1]) * Sh + (Kc * np.exp(bc[-1] - bc)[:, None]).T @ Vc
-            S[b, h] = Sh
-            if normalize:
-                Z[b, h] = zh
-    return (out, S, Z) if normalize else (out, S)
+        log_a = np.log(a)
+    spans = chunk_spans(L, C)
+    for bh in np.ndindex(B, H):
+        # the value columns, with a column of ones appended for z
+        vals = np.concatenate([v[bh], np.ones((L, 1), dtype)], axis=1) if normalize else v[bh]
+        carry = np.zeros((dk, width), dtype)
+        carry[:, :dv] = S0[bh]
+        if normalize:
+            carry[:, dv] = z0[bh]
+        for first, stop in spans:
+            rows, carry = _decayed_chunk(carry, fq[bh][first:stop], fk[bh][first:stop],
+                                         vals[first:stop], log_a[bh][first:stop], dtype)
+            out[bh][first:stop] = rows[:, :dv] / rows[:, dv:] if normalize else rows
+        S_fin[bh] = carry[:, :dv]
+        if normalize:
+            Z_fin[bh] = carry[:, dv]
+    return (out, S_fin, Z_fin) if normalize else (out, S_fin)
 
 
 def rel_err(x, ref) -> float:
@@ -282,13 +303,18 @@ def rel_err(x, ref) -> float:
 # the per-channel (GLA) gate: S_t = diag(alpha_t) S_{t-1} + k_t v_t^T
 # (linear/sparse attention tutorial, section 2.4)
 # --------------------------------------------------------------------------
-def parallel_channel(q, k, v, a, phi: int = PHI_IDENTITY, state=None):
+def parallel_channel(q, k, v, a, phi: int = PHI_IDENTITY, state=None, normalize: bool = False,
+                     norm_state=None):
     """Fully parallel form of the per-channel gate with explicit products.
 
     a: [B,H,L,dk] multipliers.  o_t = sum_{s<=t} sum_d phi(q)_td phi(k)_sd
     D[t,s,d] v_s + sum_d phi(q)_td (prod_{r<=t} a_rd) S_0[d,:],
     D[t,s,d] = prod_{r=s+1..t} a_rd; S_L[d,:] = sum_s D[L-1,s,d] phi(k)_sd v_s
     + prod_r a_rd S_0[d,:].
+    normalize: each row is divided by the same masked sum with v replaced by
+    ones, sum_{s<=t} sum_d phi(q)_td phi(k)_sd D[t,s,d] + sum_d phi(q)_td
+    (prod_{r<=t} a_rd) z_0[d] (the tutorial's section 2.2 boxed recurrence,
+    with the diagonal gate of section 2.4 acting on z as on each row of S).
     """
     fq, fk, v, a = feature_map(q, phi), feature_map(k, phi), _f64(v), _f64(a)
     B, H, L, dk = fq.shape
@@ -308,6 +334,10 @@ def parallel_channel(q, k, v, a, phi: int = PHI_IDENTITY, state=None):
             head = np.cumprod(a[b, h], axis=0)  # [L, dk]
             scores = np.einsum("td,sd,tsd->ts", fq[b, h], fk[b, h], D)
             out[b, h] = scores @ v[b, h] + (fq[b, h] * head) @ S0[b, h]
+            if normalize:
+                z0 = np.zeros(dk) if norm_state is None else _f64(norm_state)[b, h]
+                den = scores.sum(axis=1) + (fq[b, h] * head) @ z0
+                out[b, h] = out[b, h] / den[:, None]
             if L:
                 SL[b, h] = (fk[b, h] * D[L - 1]).T @ v[b, h] + head[-1][:, None] * S0[b, h]
             else:
@@ -315,32 +345,47 @@ def parallel_channel(q, k, v, a, phi: int = PHI_IDENTITY, state=None):
     return out, SL
 
 
-def chunkwise_channel(q, k, v, log_a, C: int, phi: int = PHI_IDENTITY, state=None):
-    """Chunkwise form of the per-channel gate, per chunk with B = inclusive
-    cumsum of log a inside the chunk (per channel, every factor exp(<= 0)):
-      O_c     = (Q_c o e^{B}) S_c + P V_c,  P[i,j] = [j<=i] sum_d q_id k_jd e^{B_id - B_jd}
-      S_{c+1} = diag(e^{B_last}) S_c + (K_c o e^{B_last - B})^T V_c
-    """
+def _channel_chunk(carry, Qc, Kc, Vc, log_ac):
+    """One chunk of the per-channel gate.  carry: [dk, dv'] on entry.  With
+    cum[i, d] the in-chunk inclusive cumsum of log a per channel:
+      rows  = (Q_c o e^{cum}) carry + P V_c,  P[i,j] = [j<=i] sum_d q_id k_jd e^{cum_id - cum_jd}
+      carry = diag(e^{cum_last}) carry + (K_c o e^{cum_last - cum})^T V_c
+    (every exponent <= 0)."""
+    cum = np.cumsum(log_ac, axis=0)                   # [c, dk]
+    n = cum.shape[0]
+    causal = np.tri(n, dtype=bool)
+    gaps = np.where(causal[..., None], cum[:, None, :] - cum[None, :, :], 0.0)
+    P = np.where(causal, np.einsum("id,jd,ijd->ij", Qc, Kc, np.exp(gaps)), 0.0)
+    rows = (Qc * np.exp(cum)) @ carry + P @ Vc
+    carry = np.exp(cum[-1])[:, None] * carry + (Kc * np.exp(cum[-1] - cum)).T @ Vc
+    return rows, carry
+
+
+def chunkwise_channel(q, k, v, log_a, C: int, phi: int = PHI_IDENTITY, state=None,
+                      normalize: bool = False, norm_state=None):
+    """Chunkwise form of the per-channel gate (see `_channel_chunk`), chunk
+    after chunk.  normalize: z rides along as one more value column of ones
+    (tutorial section 6.2), decayed per channel like every row of S."""
     fq, fk, v, la = feature_map(q, phi), feature_map(k, phi), _f64(v), _f64(log_a)
     B_, H, L, dk = fq.shape
     dv = v.shape[-1]
-    S = np.zeros((B_, H, dk, dv)) if state is None else _f64(state).copy()
+    S0 = np.zeros((B_, H, dk, dv)) if state is None else _f64(state)
+    z0 = np.zeros((B_, H, dk)) if norm_state is None else _f64(norm_state)
     out = np.zeros((B_, H, L, dv))
-    for b in range(B_):
-        for h in range(H):
-            Sh = S[b, h]
-            for s in range(0, L, C):
-                e = min(s + C, L)
-                Qc, Kc, Vc = fq[b, h, s:e], fk[b, h, s:e], v[b, h, s:e]
-                Bc = np.cumsum(la[b, h, s:e], axis=0)  # [c, dk]
-                diff = Bc[:, None, :] - Bc[None, :, :]  # [c, c, dk]
-                mask = np.tril(np.ones((e - s, e - s), dtype=bool))
-                P = np.einsum("id,jd,ijd->ij", Qc, Kc, np.exp(np.where(mask[..., None], diff, 0.0)))
-                P = np.where(mask, P, 0.0)
-                out[b, h, s:e] = (Qc * np.exp(Bc)) @ Sh + P @ Vc
-                Sh = np.exp(Bc[-1])[:, None] * Sh + (Kc * np.exp(Bc[-1] - Bc)).T @ Vc
-            S[b, h] = Sh
-    return out, S
+    S_fin = np.zeros((B_, H, dk, dv))
+    Z_fin = np.zeros((B_, H, dk)) if normalize else None
+    spans = chunk_spans(L, C)
+    for bh in np.ndindex(B_, H):
+        vals = np.concatenate([v[bh], np.ones((L, 1))], axis=1) if normalize else v[bh]
+        carry = np.concatenate([S0[bh], z0[bh][:, None]], axis=1) if normalize else S0[bh].copy()
+        for first, stop in spans:
+            rows, carry = _channel_chunk(carry, fq[bh][first:stop], fk[bh][first:stop],
+                                         vals[first:stop], la[bh][first:stop])
+            out[bh][first:stop] = rows[:, :dv] / rows[:, dv:] if normalize else rows
+        S_fin[bh] = carry[:, :dv]
+        if normalize:
+            Z_fin[bh] = carry[:, dv]
+    return (out, S_fin, Z_fin) if normalize else (out, S_fin)
 
 
 # --------------------------------------------------------------------------
@@ -421,6 +466,20 @@ def delta_explicit(q, k, v, beta, a, state=None):
     return out, SL
 
 
+def _delta_chunk(carry, Qc, Kc, Vc, beta_c, log_ac):
+    """One chunk of the delta rule's chunkwise form (see `delta_chunkwise`)."""
+    cum = np.cumsum(log_ac)
+    n = cum.shape[0]
+    below = np.tri(n, dtype=bool)
+    G = np.exp(np.where(below, cum[:, None] - cum[None, :], -np.inf))   # 0 above the diagonal
+    system = np.eye(n) + beta_c[:, None] * (np.tril(Kc @ Kc.T, -1) * G)
+    rhs = beta_c[:, None] * (Vc - np.exp(cum)[:, None] * (Kc @ carry))
+    U = np.linalg.solve(system, rhs)
+    rows = np.exp(cum)[:, None] * (Qc @ carry) + ((Qc @ Kc.T) * G) @ U
+    carry = np.exp(cum[-1]) * carry + (np.exp(cum[-1] - cum)[:, None] * Kc).T @ U
+    return rows, carry
+
+
 def delta_chunkwise(q, k, v, beta, log_a, C: int, state=None):
     """Chunkwise (WY / UT) form of the delta rule, derived by unrolling the
     recurrence over one chunk (the tutorial's section 5.3 and Q23 give the
@@ -439,22 +498,15 @@ def delta_chunkwise(q, k, v, beta, log_a, C: int, state=None):
     q, k, v, beta, la = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(log_a)
     B, H, L, dk = q.shape
     dv = v.shape[-1]
-    S = np.zeros((B, H, dk, dv)) if state is None else _f64(state).copy()
+    S0 = np.zeros((B, H, dk, dv)) if state is None else _f64(state)
     out = np.zeros((B, H, L, dv))
-    for b in range(B):
-        for h in range(H):
-            Sh = S[b, h]
-            for s in range(0, L, C):
-                e = min(s + C, L)
-                n = e - s
-                Qc, Kc, Vc, bc = q[b, h, s:e], k[b, h, s:e], v[b, h, s:e], beta[b, h, s:e]
-                bb = np.cumsum(la[b, h, s:e])
-                G = np.exp(np.where(np.tril(np.ones((n, n), dtype=bool)),
-                                    bb[:, None] - bb[None, :], -np.inf))
-                A = np.eye(n) + bc[:, None] * (np.tril(Kc @ Kc.T, -1) * G)
-                R = bc[:, None] * (Vc - np.exp(bb)[:, None] * (Kc @ Sh))
-                U = np.linalg.solve(A, R)
-                out[b, h, s:e] = np.exp(bb)[:, None] * (Qc @ Sh) + ((Qc @ Kc.T) * G) @ U
-                Sh = np.exp(bb[-1]) * Sh + (np.exp(bb[-1] - bb)[:, None] * Kc).T @ U
-            S[b, h] = Sh
-    return out, S
+    S_fin = np.zeros((B, H, dk, dv))
+    spans = chunk_spans(L, C)
+    for bh in np.ndindex(B, H):
+        carry = S0[bh].copy()
+        for first, stop in spans:
+            out[bh][first:stop], carry = _delta_chunk(
+                carry, q[bh][first:stop], k[bh][first:stop], v[bh][first:stop],
+                beta[bh][first:stop], la[bh][first:stop])
+        S_fin[bh] = carry
+    return out, S_fin

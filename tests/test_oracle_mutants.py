@@ -42,6 +42,9 @@ MUTANTS = {
     "denominator_with_keys": ("den += fq[i] * z[i];", "den += fk[i] * z[i];"),
     "channel_gate_reversed": ("? exp(dh[(size_t)t * dk + i]) : a;",
                               "? exp(dh[(size_t)t * dk + (dk - 1 - i)]) : a;"),
+    "normaliser_channel_gate_scalar": (
+        "? exp(dh[(size_t)t * dk + i]) : a;\n        z[i] = ai * z[i] + fk[i];",
+        "? a : a;\n        z[i] = ai * z[i] + fk[i];"),
     "channel_gate_of_previous_token": ("? exp(dh[(size_t)t * dk + i]) : a;",
                                        "? exp(dh[(size_t)(t > 0 ? t - 1 : 0) * dk + i]) : a;"),
     # the delta rule
@@ -103,6 +106,14 @@ def _battery(lib):
         op, Sp = oracle.parallel_channel(q, k, v, np.exp(la), phi, S0)
         if oracle.rel_err(o, op) > 1e-12 or oracle.rel_err(S, Sp) > 1e-12:
             failed.append(f"channel gate phi={phi}")
+    # the normalised form under the per-channel gate: recurrent == parallel (explicit products)
+    z0 = np.abs(rng.standard_normal((B, H, dk))) + 0.5
+    o, S, Z = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_CHANNEL, la, None,
+                               normalize=True, norm_state=z0, lib_path=lib)
+    op, _ = oracle.parallel_channel(q, k, v, np.exp(la), oracle.PHI_ELU1, normalize=True,
+                                    norm_state=z0)
+    if oracle.rel_err(o, op) > 1e-12:
+        failed.append("normalised channel gate")
     # the delta rule: the C recurrence == the pages' explicit (I - beta k k^T) form
     kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
     beta = rng.uniform(0.1, 1.0, (B, H, L))

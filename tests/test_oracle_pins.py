@@ -529,3 +529,70 @@ def test_channel_gate_decode_step_is_one_token():
     od, Sd = oracle.decode_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], oracle.PHI_ELU1,
                                 oracle.DECAY_CHANNEL, la[:, :, 0], S0)
     assert np.array_equal(o[:, :, 0], od) and np.array_equal(S, Sd)
+
+
+# ---------------------------------------------------------------------------
+# the normalised form under the per-channel gate (tutorial section 2.2 boxed
+# recurrence with section 2.4's diagonal gate: z decays per channel like each
+# row of S, since z is S's extra value column of ones, section 6.2)
+# ---------------------------------------------------------------------------
+def _channel_norm_case(seed, L=19, dk=5, dv=3):
+    q, k, v, la, _ = _channel_case(seed, L, dk, dv)
+    rng = np.random.default_rng(seed + 500)
+    # a consistent positive initial pair, as after 4 earlier tokens
+    fk0 = oracle.feature_map(rng.standard_normal((1, 2, 4, dk)), oracle.PHI_ELU1)
+    v0 = rng.standard_normal((1, 2, 4, dv))
+    return q, k, v, la, np.einsum("bhtk,bhtv->bhkv", fk0, v0), fk0.sum(axis=2)
+
+
+def test_channel_gate_normalised_recurrent_equals_parallel_and_chunkwise():
+    q, k, v, la, S0, z0 = _channel_norm_case(60)
+    o, S, Z = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_CHANNEL, la, S0,
+                               normalize=True, norm_state=z0)
+    op, Sp = oracle.parallel_channel(q, k, v, np.exp(la), oracle.PHI_ELU1, S0, normalize=True,
+                                     norm_state=z0)
+    assert oracle.rel_err(o, op) < 1e-13 and oracle.rel_err(S, Sp) < 1e-13
+    for C in (1, 4, 7, 19):
+        oc, Sc, Zc = oracle.chunkwise_channel(q, k, v, la, C, oracle.PHI_ELU1, S0,
+                                              normalize=True, norm_state=z0)
+        assert oracle.rel_err(o, oc) < 1e-13 and oracle.rel_err(S, Sc) < 1e-13
+        assert oracle.rel_err(Z, Zc) < 1e-13
+
+
+def test_channel_gate_normalised_with_equal_channels_is_the_scalar_gate():
+    # alpha_t equal in every channel: the normalised scalar log-decay recurrence
+    q, k, v, la, S0, z0 = _channel_norm_case(61)
+    la_tok = la[..., 0]
+    la_all = np.repeat(la_tok[..., None], q.shape[-1], axis=-1)
+    o, S, Z = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_CHANNEL, la_all, S0,
+                               normalize=True, norm_state=z0)
+    os_, Ss, Zs = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_LOG, la_tok, S0,
+                                   normalize=True, norm_state=z0)
+    assert oracle.rel_err(o, os_) < 1e-14 and oracle.rel_err(Z, Zs) < 1e-14
+
+
+def test_channel_gate_normalised_z_is_the_state_for_unit_values():
+    # z_t is exactly the un-normalised state's column for v = 1, decayed per channel,
+    # and the output is the un-normalised output divided by that column's read-out
+    q, k, v, la, S0, z0 = _channel_norm_case(62)
+    o, _, Z = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_CHANNEL, la, S0,
+                               normalize=True, norm_state=z0)
+    ones = np.ones(v.shape[:-1] + (1,))
+    den, zS = oracle.recurrent(q, k, ones, oracle.PHI_ELU1, oracle.DECAY_CHANNEL, la,
+                               z0[..., None])
+    num, _ = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_CHANNEL, la, S0)
+    assert oracle.rel_err(Z, zS[..., 0]) < 1e-14
+    assert oracle.rel_err(o, num / den) < 1e-13
+
+
+def test_channel_gate_normalised_forgotten_channel():
+    # a channel with log a = -inf forgets z's entry every step: z_d = phi(k_t)_d of the newest
+    # token; a channel with log a = 0 accumulates: z_d = z0_d + sum_t phi(k_t)_d
+    q, k, v, la, S0, z0 = _channel_norm_case(63, L=6, dk=3, dv=2)
+    la[:] = 0.0
+    la[..., 2] = -np.inf
+    _, _, Z = oracle.recurrent(q, k, v, oracle.PHI_ELU1, oracle.DECAY_CHANNEL, la, S0,
+                               normalize=True, norm_state=z0)
+    fk = oracle.feature_map(k, oracle.PHI_ELU1)
+    assert np.allclose(Z[..., 2], fk[:, :, -1, 2], rtol=1e-14, atol=0)
+    assert np.allclose(Z[..., 0], z0[..., 0] + fk[..., 0].sum(axis=2), rtol=1e-13, atol=0)
