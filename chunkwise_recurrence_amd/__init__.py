@@ -10,5 +10,6 @@ from .binding import (  # noqa: F401
     DECAY_CHANNEL, DECAY_GATE, DECAY_HEAD, DECAY_LOG, DECAY_NONE, PHI_ELU1, PHI_IDENTITY, LAError,
     EXPORTS, KERNEL_AUTO, KERNEL_F32, KERNEL_STRIP, KERNEL_STRIPE, LA_BF16, LA_F32, Plan,
     chunk_fwd, chunk_fwd_workspace_bytes, decode_step, delta_decode_step, delta_fwd,
-    delta_fwd_workspace_bytes, lib_path, load, plan, set_plan, state_init, status_string,
+    delta_fwd_workspace_bytes, lib_path, load, plan, plan_workspace_bytes, state_init, status_string,
+    using_plan,
 )

@@ -1,8 +1,9 @@
 // la_api.hip -- the C ABI of liblinattn.so (declared in include/la.h):
 // argument validation on the host, the launch plan, and the launches.
 //
-// Validation happens before any HIP call, so every error path can be
-// exercised on a machine without a GPU.
+// Validation happens before any launch, so every error path can be exercised
+// on a machine without a GPU (the plan asks the runtime for the current
+// device's compute units, and assumes an MI355X's 256 when none is visible).
 #include <atomic>
 #include <stdint.h>
 
@@ -11,17 +12,34 @@
 
 namespace {
 
-// Workgroups the bf16 plan aims for: one 8-wave stripe workgroup per compute
-// unit of an MI355X, or two 4-wave strip workgroups per compute unit.
-constexpr int kTargetStripe = 256;
-constexpr int kTargetStrip = 512;
 // A segment of the sequence keeps at least this many chunks.
 constexpr int kMinSegmentChunks = 4;
+// Compute units assumed when no device is visible (plan queries on a host
+// without a GPU): an MI355X.
+constexpr int kDefaultComputeUnits = 256;
+constexpr int kMaxDevices = 64;
 
-std::atomic<int> g_plan_kernel{0};
-std::atomic<int> g_plan_tile{0};
-std::atomic<int> g_plan_segments{0};
-std::atomic<int> g_plan_groups{0};
+// The library's only global state: compute units per device, queried once
+// per device and cached (0 = not yet known).  Concurrent first calls may both
+// query; they store the same value.
+std::atomic<int> g_device_cus[kMaxDevices];
+
+int device_compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultComputeUnits;
+  }
+  int n = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    return kDefaultComputeUnits;
+  }
+  g_device_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -56,8 +74,19 @@ la_status check_chunk_shape(int dtype, int B, int H, int L, int d_k, int d_v, in
   return LA_OK;
 }
 
+// A caller's plan request: every field 0 = automatic.
+la_status check_request(const la_plan* r) {
+  if (!r) return LA_OK;
+  if (r->kernel != 0 && r->kernel != LA_KERNEL_STRIP && r->kernel != LA_KERNEL_STRIPE)
+    return LA_ERR_UNSUPPORTED;
+  if (r->dv_tile != 0 && !dim_ok(r->dv_tile)) return LA_ERR_UNSUPPORTED;
+  if (r->groups != 0 && r->groups != 1 && r->groups != 2) return LA_ERR_UNSUPPORTED;
+  if (r->segments < 0) return LA_ERR_SHAPE;
+  return LA_OK;
+}
+
 Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int decay_kind,
-               bool norm = false) {
+               bool norm, const la_plan* request) {
   Plan p;
   const int heads = B * H;
   const int nchunks = L > 0 ? (L + C - 1) / C : 0;
@@ -74,13 +103,15 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
     }
     return p;
   }
-  const int forced_kernel = g_plan_kernel.load(), forced_tile = g_plan_tile.load(),
-            forced_groups = g_plan_groups.load();
+  const la_plan none{};
+  const la_plan& req = request ? *request : none;
+  const int forced_kernel = req.kernel, forced_tile = req.dv_tile, forced_groups = req.groups;
   // 128-wide heads: the stripe kernel (32x32 MFMA, the state in registers,
   // one 8-wave workgroup per head and segment).  Narrower heads, 16-token
   // chunks and shapes the stripe kernel does not cover: the strip kernel
   // (16x16 MFMA, 4-wave workgroups over 32-column tiles, siblings sharing q
-  // and k through L2).  Both measured on MI355X; la_set_plan overrides.
+  // and k through L2).  Both measured on MI355X; a caller's plan request
+  // (la_chunk_fwd_planned) overrides.
   int tile = 0;
   // the normalised form and the per-channel decay run in the stripe kernel only
   const bool chan = decay_kind == LA_DECAY_CHANNEL_LOG;
@@ -127,9 +158,12 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   // gets the segment count of two one-group tiles
   const long long units =
       (long long)heads * (d_v / tile) * (p.kernel == LA_KERNEL_STRIP ? p.ng : 1);
-  const long long target = p.kernel == LA_KERNEL_STRIPE ? kTargetStripe : kTargetStrip;
+  // one 8-wave stripe workgroup per compute unit, or two 4-wave strip
+  // workgroups per compute unit
+  const int cus = device_compute_units();
+  const long long target = p.kernel == LA_KERNEL_STRIPE ? cus : 2LL * cus;
   while (units * P < target && (long long)P * 2 * kMinSegmentChunks <= nchunks) P *= 2;
-  const int forced_P = g_plan_segments.load();
+  const int forced_P = req.segments;
   if (forced_P > 0) P = forced_P;
   if (P > nchunks) P = nchunks;
   if (P < 1) P = 1;
@@ -179,31 +213,22 @@ const char* la_status_string(int s) {
   return "unknown la_status";
 }
 
-la_status la_set_plan(const la_plan* plan) {
-  const la_plan zero{};
-  const la_plan& p = plan ? *plan : zero;
-  if (p.kernel != 0 && p.kernel != LA_KERNEL_STRIP && p.kernel != LA_KERNEL_STRIPE)
-    return LA_ERR_UNSUPPORTED;
-  if (p.dv_tile != 0 && !dim_ok(p.dv_tile)) return LA_ERR_UNSUPPORTED;
-  if (p.groups != 0 && p.groups != 1 && p.groups != 2) return LA_ERR_UNSUPPORTED;
-  if (p.segments < 0) return LA_ERR_SHAPE;
-  g_plan_kernel.store(p.kernel);
-  g_plan_tile.store(p.dv_tile);
-  g_plan_segments.store(p.segments);
-  g_plan_groups.store(p.groups);
-  return LA_OK;
-}
-
 la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype,
-                            la_plan* plan) {
+                            int decay_kind, int normalize, la_plan* plan,
+                            size_t* workspace_bytes) {
   const la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
   if (st != LA_OK) return st;
+  if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_CHANNEL_LOG) return LA_ERR_UNSUPPORTED;
   if (!plan) return LA_ERR_NULL;
-  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, LA_DECAY_NONE);
+  const la_status rs = check_request(plan);
+  if (rs != LA_OK) return rs;
+  const la_plan request = *plan;
+  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, normalize != 0, &request);
   plan->kernel = p.kernel;
   plan->dv_tile = p.tile;
   plan->segments = p.P;
   plan->groups = p.ng;
+  if (workspace_bytes) *workspace_bytes = L > 0 ? p.ws_bytes : 0;
   return LA_OK;
 }
 
@@ -212,8 +237,8 @@ size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C
   if (check_chunk_shape(dtype, B, H, L, d_k, d_v, C) != LA_OK || L == 0) return 0;
   if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_CHANNEL_LOG) return 0;
   // one size serves both forms: the larger of the two plans' workspaces
-  const size_t plain = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind).ws_bytes;
-  const size_t normed = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, true).ws_bytes;
+  const size_t plain = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, false, nullptr).ws_bytes;
+  const size_t normed = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, true, nullptr).ws_bytes;
   return plain > normed ? plain : normed;
 }
 
@@ -233,12 +258,15 @@ namespace {
 la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype, int B, int H,
                          int L, int d_k, int d_v, int C, int phi, int decay_kind,
                          const float* decay_data, float* state, float* norm_state, bool norm,
-                         void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                         const la_plan* request, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
   if (st != LA_OK) return st;
   if (phi != LA_PHI_IDENTITY && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
   if (decay_kind < LA_DECAY_NONE || decay_kind > LA_DECAY_CHANNEL_LOG) return LA_ERR_UNSUPPORTED;
-  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, norm);
+  st = check_request(request);
+  if (st != LA_OK) return st;
+  const Plan p = make_plan(B, H, L, d_k, d_v, C, dtype, decay_kind, norm, request);
   // bf16 inputs reach the normalised form and the per-channel decay through
   // the stripe kernel only, and not both at once
   const bool chan = decay_kind == LA_DECAY_CHANNEL_LOG;
@@ -362,7 +390,7 @@ la_status la_chunk_fwd(const void* q, const void* k, const void* v, int dtype, i
                        const float* decay_data, float* state, void* out, void* workspace,
                        size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl(q, k, v, dtype, B, H, L, d_k, d_v, C, phi, decay_kind, decay_data, state,
-                        nullptr, false, out, workspace, workspace_bytes, stream);
+                        nullptr, false, nullptr, out, workspace, workspace_bytes, stream);
 }
 
 la_status la_chunk_fwd_norm(const void* q, const void* k, const void* v, int dtype, int B, int H,
@@ -370,7 +398,17 @@ la_status la_chunk_fwd_norm(const void* q, const void* k, const void* v, int dty
                             const float* decay_data, float* state, float* norm_state, void* out,
                             void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl(q, k, v, dtype, B, H, L, d_k, d_v, C, phi, decay_kind, decay_data, state,
-                        norm_state, true, out, workspace, workspace_bytes, stream);
+                        norm_state, true, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+la_status la_chunk_fwd_planned(const void* q, const void* k, const void* v, int dtype, int B,
+                               int H, int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                               const float* decay_data, float* state, float* norm_state,
+                               int normalize, const la_plan* plan, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return chunk_fwd_impl(q, k, v, dtype, B, H, L, d_k, d_v, C, phi, decay_kind, decay_data, state,
+                        normalize ? norm_state : nullptr, normalize != 0, plan, out, workspace,
+                        workspace_bytes, stream);
 }
 
 la_status la_decode_step(const void* q, const void* k, const void* v, int dtype, int N, int H,

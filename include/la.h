@@ -39,7 +39,8 @@
  *   checked: NaN and Inf propagate.
  * - Outputs must not alias inputs or the state (not checked).
  * - Calls are thread-safe; calls that share output buffers must be ordered
- *   by the caller.
+ *   by the caller.  The library's only global state is a cache of each
+ *   device's compute-unit count, filled on first use.
  */
 #ifndef LA_H_
 #define LA_H_
@@ -237,17 +238,25 @@ la_status la_delta_decode_step(const void* q, const void* k, const void* v, cons
                                const float* decay_data, float* state, void* out, void* stream);
 
 /*
- * Launch plan of la_chunk_fwd (host only, for tests and benchmarks).
+ * Launch plan of la_chunk_fwd (for tests and benchmarks).  The library keeps
+ * no plan state: a plan is requested per call.
  *   kernel    LA_KERNEL_F32 (fp32 inputs: one workgroup per head and 32-column
  *             tile), LA_KERNEL_STRIP (bf16: 16x16 MFMA, 4-wave column groups,
  *             any d_k, d_v, C) or LA_KERNEL_STRIPE (bf16: 32x32 MFMA, one
  *             wave per 32 value columns holding its part of the state in
  *             registers; d_k, d_v >= 32 and C >= 32).
- *   dv_tile   value columns one workgroup covers
+ *   dv_tile   value columns one workgroup covers (16, 32, 64 or 128)
  *   segments  sequence segments per head (> 1: a state pass runs first)
  *   groups    strip kernel: 4-wave column groups per workgroup (1 or 2);
  *             stripe kernel: waves per 32-column stripe, each holding a
  *             share of the keys of the state (1 or 2; 2 needs d_k >= 64)
+ * In a request, a field at 0 keeps the automatic choice.  The automatic plan
+ * splits sequences into segments until the grid covers the current device's
+ * compute units (queried once per device and cached; 256 when no device is
+ * visible).  Requested values that do not fit a call are reduced to ones that
+ * do (a stripe request the shape does not allow falls back to the strip
+ * kernel).  fp32 inputs have one plan and ignore requests.  Results do not
+ * depend on the plan beyond rounding; tests use requests to check that.
  */
 typedef struct {
   int kernel;
@@ -259,24 +268,32 @@ typedef struct {
 enum { LA_KERNEL_AUTO = 0, LA_KERNEL_STRIP = 1, LA_KERNEL_STRIPE = 2, LA_KERNEL_F32 = 3 };
 
 /*
- * la_chunk_fwd_plan -- the plan la_chunk_fwd would use for these arguments
- * (written to *plan).  Returns LA_OK, LA_ERR_NULL for a NULL plan, or the
- * error la_chunk_fwd would return for these shapes.
+ * la_chunk_fwd_plan -- resolve a plan (host only, launches nothing).
+ *   plan            in: the request (all zero: automatic); out: the plan
+ *                   la_chunk_fwd_planned takes with that request for these
+ *                   arguments (la_chunk_fwd / la_chunk_fwd_norm: all zero)
+ *   normalize       0: la_chunk_fwd; 1: la_chunk_fwd_norm
+ *   workspace_bytes NULL, or out: the workspace bytes that plan needs
+ * Returns LA_OK, LA_ERR_NULL for a NULL plan, LA_ERR_UNSUPPORTED for an
+ * invalid kernel, tile or group count, LA_ERR_SHAPE for a negative segment
+ * count, or the error la_chunk_fwd would return for these shapes.
  */
 la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype,
-                            la_plan* plan);
+                            int decay_kind, int normalize, la_plan* plan,
+                            size_t* workspace_bytes);
 
 /*
- * la_set_plan -- override the bf16 plan process-wide.  Fields at 0 (or a
- * NULL plan) keep the automatic choice: kernel (LA_KERNEL_STRIP or
- * LA_KERNEL_STRIPE), dv_tile (16, 32, 64 or 128), segments (>= 1), groups
- * (1 or 2).  Values that do not fit a given call are reduced to ones that do
- * (a stripe plan the shape does not allow falls back to the strip kernel).
- * Results do not depend on the plan beyond rounding; tests use it to check
- * exactly that.  Returns LA_ERR_UNSUPPORTED for an invalid kernel, tile or
- * group count, LA_ERR_SHAPE for a negative segment count.
+ * la_chunk_fwd_planned -- la_chunk_fwd (normalize = 0; norm_state ignored) or
+ * la_chunk_fwd_norm (normalize = 1) with a requested plan (NULL or all zero:
+ * automatic).  The workspace must hold what la_chunk_fwd_plan reports for the
+ * same request.  Errors: those of la_chunk_fwd, plus those of
+ * la_chunk_fwd_plan for an invalid request.
  */
-la_status la_set_plan(const la_plan* plan);
+la_status la_chunk_fwd_planned(const void* q, const void* k, const void* v, int dtype, int B,
+                               int H, int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                               const float* decay_data, float* state, float* norm_state,
+                               int normalize, const la_plan* plan, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

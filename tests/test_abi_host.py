@@ -124,40 +124,73 @@ def test_plans_of_the_workloads():
     assert la.chunk_fwd_workspace_bytes(2, 3, 300, 32, 64, 64, la.LA_F32) == 2 * 3 * 32 * 4
 
 
-def test_plan_override_and_clamping():
-    try:
-        la.set_plan(STRIP, 64, 3, 1)
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (STRIP, 64, 3, 1)
-        assert la.plan(1, 1, 64 * 2, 128, 32, 64) == (STRIP, 32, 2, 1)  # tile clamped to d_v, P to chunks
-        la.set_plan(STRIP, 32, 0, 2)
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64)[1::2] == (32, 2)
-        la.set_plan(STRIP, 16, 0, 2)   # 8-column groups do not exist
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64)[1::2] == (16, 1)
-        la.set_plan(STRIP, 64, 0, 2)
-        assert la.plan(1, 1, 100, 64, 64, 64) == (STRIP, 64, 1, 2)
-        # two 64-column groups of d_k = 128 exceed the LDS: the tile is halved
-        assert la.plan(1, 1, 100, 128, 128, 64)[1::2] == (64, 2)
-        la.set_plan(STRIPE, 64, 2)
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 64, 2, 2)
-        # d_k = 32 keeps one wave per stripe
-        la.set_plan(STRIPE)
-        assert la.plan(1, 1, 100, 32, 32, 64) == (STRIPE, 32, 1, 1)
-        assert la.plan(1, 1, 100, 64, 64, 128)[0] == STRIPE
-        la.set_plan(STRIPE, 128, 2, 1)
-        assert la.plan(1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 128, 2, 1)
-        # a stripe plan the shape does not allow falls back to the strip kernel
-        assert la.plan(1, 1, 64 * 30, 16, 16, 64)[0] == STRIP
-        with pytest.raises(la.LAError):
-            la.set_plan(STRIP, 48, 0)
-        with pytest.raises(la.LAError):
-            la.set_plan(STRIP, 0, -1)
-        with pytest.raises(la.LAError):
-            la.set_plan(STRIP, 0, 0, 3)
-        with pytest.raises(la.LAError):
-            la.set_plan(7)
-    finally:
-        la.set_plan()
+def test_plan_requests_and_clamping():
+    def got(req, *shape):
+        return la.plan(*shape, request=req)
+    assert got((STRIP, 64, 3, 1), 1, 1, 64 * 30, 128, 128, 64) == (STRIP, 64, 3, 1)
+    # tile clamped to d_v, P to chunks
+    assert got((STRIP, 64, 3, 1), 1, 1, 64 * 2, 128, 32, 64) == (STRIP, 32, 2, 1)
+    assert got((STRIP, 32, 0, 2), 1, 1, 64 * 30, 128, 128, 64)[1::2] == (32, 2)
+    # 8-column groups do not exist
+    assert got((STRIP, 16, 0, 2), 1, 1, 64 * 30, 128, 128, 64)[1::2] == (16, 1)
+    assert got((STRIP, 64, 0, 2), 1, 1, 100, 64, 64, 64) == (STRIP, 64, 1, 2)
+    # two 64-column groups of d_k = 128 exceed the LDS: the tile is halved
+    assert got((STRIP, 64, 0, 2), 1, 1, 100, 128, 128, 64)[1::2] == (64, 2)
+    assert got((STRIPE, 64, 2), 1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 64, 2, 2)
+    # d_k = 32 keeps one wave per stripe
+    assert got((STRIPE,), 1, 1, 100, 32, 32, 64) == (STRIPE, 32, 1, 1)
+    assert got((STRIPE,), 1, 1, 100, 64, 64, 128)[0] == STRIPE
+    assert got((STRIPE, 128, 2, 1), 1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 128, 2, 1)
+    # a stripe request the shape does not allow falls back to the strip kernel
+    assert got((STRIPE, 128, 2, 1), 1, 1, 64 * 30, 16, 16, 64)[0] == STRIP
+    for bad, code in (((STRIP, 48, 0), UNSUP), ((STRIP, 0, -1), SHAPE), ((STRIP, 0, 0, 3), UNSUP),
+                      ((7,), UNSUP)):
+        with pytest.raises(la.LAError) as e:
+            got(bad, 1, 1, 100, 64, 64, 64)
+        assert e.value.status == code
+    # the request is per call: the automatic plan is untouched
     assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
+    # within a using_plan block the binding passes the block's request
+    with la.using_plan(STRIP, 32, 2, 1):
+        assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIP, 32, 2, 1)
+        # the workspace query follows the request: two segments' states + the S_0 copy
+        ws = la.plan_workspace_bytes(2, 32, 16384, 128, 128, 64)
+        assert ws >= 64 * 2 * 128 * 128 * 4 + 64 * 128 * 128 * 4
+    assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
+
+
+def test_plan_query_rejects():
+    lib = la.load()
+    p = la.Plan()
+    assert lib.la_chunk_fwd_plan(1, 1, 64, 64, 64, 64, 1, 0, 0, None, None) == NULL
+    assert lib.la_chunk_fwd_plan(0, 1, 64, 64, 64, 64, 1, 0, 0, ctypes.byref(p), None) == SHAPE
+    assert lib.la_chunk_fwd_plan(1, 1, 64, 48, 64, 64, 1, 0, 0, ctypes.byref(p), None) == UNSUP
+    assert lib.la_chunk_fwd_plan(1, 1, 64, 64, 64, 64, 1, 9, 0, ctypes.byref(p), None) == UNSUP
+    ws = ctypes.c_size_t(7)
+    assert lib.la_chunk_fwd_plan(1, 1, 64, 64, 64, 64, 1, 0, 0, ctypes.byref(p),
+                                 ctypes.byref(ws)) == OK
+    assert ws.value == 0 and p.segments == 1
+
+
+def _planned(req, **kw):
+    a = dict(q=P16, k=P16, v=P16, dtype=1, B=1, H=1, L=64 * 30, dk=128, dv=128, C=64, phi=0,
+             kind=0, decay=None, state=None, z=None, norm=0, out=P16, ws=None, ws_bytes=0)
+    a.update(kw)
+    return la.load().la_chunk_fwd_planned(
+        a["q"], a["k"], a["v"], a["dtype"], a["B"], a["H"], a["L"], a["dk"], a["dv"], a["C"],
+        a["phi"], a["kind"], a["decay"], a["state"], a["z"], a["norm"],
+        None if req is None else ctypes.byref(req), a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_planned_forward_rejects():
+    assert _planned(la.Plan(7, 0, 0, 0)) == UNSUP
+    assert _planned(la.Plan(STRIP, 24, 0, 0)) == UNSUP
+    assert _planned(la.Plan(STRIP, 0, -2, 0)) == SHAPE
+    assert _planned(la.Plan(STRIP, 0, 0, 5)) == UNSUP
+    # a request that splits the sequence needs its workspace
+    assert _planned(la.Plan(STRIPE, 128, 3, 2)) == WS
+    assert _planned(la.Plan(STRIPE, 128, 3, 2), q=None) == NULL
+    assert _planned(None, L=0, q=None, k=None, v=None, out=None) == OK
 
 
 def _dec(**kw):
@@ -301,5 +334,120 @@ def test_delta_decode_rejects():
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 16)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="GPU tensor"):
         la.chunk_fwd(x, x, x)
+
+
+# The C ABI sees pointers only, so the binding checks every tensor's shape and
+# dtype before the call.  These run on CPU tensors: the shape checks come
+# before the device check, so each case raises for the reason it names.
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _f(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+@pytest.mark.parametrize("kw,match", [
+    (dict(k=("b", 2, 3, 64, 16)), "share a shape"),
+    (dict(v=("b", 2, 3, 32, 32)), "last dim"),
+    (dict(k=("f", 2, 3, 64, 32)), "share a dtype"),
+    (dict(state=("f", 2, 3, 32, 16)), "state"),
+    (dict(state=("b", 2, 3, 32, 32)), "state"),
+    (dict(out=("b", 2, 3, 64, 16)), "out"),
+    (dict(out=("f", 2, 3, 64, 32)), "out"),
+    (dict(decay_kind=1, decay=("f", 2)), "decay"),
+    (dict(decay_kind=1), "decay"),
+    (dict(decay_kind=3, decay=("f", 2, 3, 63)), "decay"),
+    (dict(decay_kind=2, decay=("f", 2, 3, 64, 32)), "decay"),
+    (dict(decay_kind=4, decay=("f", 2, 3, 64)), "decay"),
+    (dict(decay_kind=4, decay=("b", 2, 3, 64, 32)), "decay"),
+    (dict(decay_kind=6, decay=("f", 3)), "decay kind"),
+    (dict(normalize=True, norm_state=("f", 2, 3, 16)), "norm_state"),
+    (dict(norm_state=("f", 2, 3, 32)), "normalize"),
+    (dict(workspace=("u", 3)), "workspace"),
+])
+def test_binding_chunk_fwd_checks_shapes(kw, match):
+    import torch
+    args = dict(q=("b", 2, 3, 64, 32), k=("b", 2, 3, 64, 32), v=("b", 2, 3, 64, 32))
+    args.update(kw)
+    mk = {"b": lambda *s: _t(*s), "f": _f, "u": lambda *s: _t(*s, dtype=torch.uint8)}
+    call = {n: (mk[x[0]](*x[1:]) if isinstance(x, tuple) else x) for n, x in args.items()}
+    if kw.get("workspace"):
+        # a workspace that is too small for a split sequence
+        call.update(q=_t(1, 1, 65536, 64), k=_t(1, 1, 65536, 64), v=_t(1, 1, 65536, 64))
+    with pytest.raises(ValueError, match=match):
+        la.chunk_fwd(**call)
+
+
+@pytest.mark.parametrize("kw,match", [
+    (dict(k=("b", 4, 2, 32)), "share a shape"),
+    (dict(v=("f", 4, 2, 16)), "share a dtype"),
+    (dict(state=("f", 4, 2, 16, 32)), "state"),
+    (dict(state=("b", 4, 2, 16, 16)), "state"),
+    (dict(state=None), "state"),
+    (dict(out=("b", 4, 2, 32)), "out"),
+    (dict(decay_kind=1, decay=("f", 4)), "decay"),
+    (dict(decay_kind=3, decay=("f", 4)), "decay"),
+    (dict(decay_kind=3), "decay"),
+    (dict(decay_kind=4, decay=("f", 4, 2)), "decay"),
+    (dict(norm_state=("f", 4, 2, 32)), "norm_state"),
+])
+def test_binding_decode_step_checks_shapes(kw, match):
+    args = dict(q=("b", 4, 2, 16), k=("b", 4, 2, 16), v=("b", 4, 2, 16),
+                state=("f", 4, 2, 16, 16))
+    args.update(kw)
+    mk = {"b": lambda *s: _t(*s), "f": _f}
+    call = {n: (mk[x[0]](*x[1:]) if isinstance(x, tuple) else x) for n, x in args.items()}
+    with pytest.raises(ValueError, match=match):
+        la.decode_step(**call)
+
+
+@pytest.mark.parametrize("kw,match", [
+    (dict(beta=("f", 2, 3, 63)), "beta"),
+    (dict(beta=("b", 2, 3, 64)), "beta"),
+    (dict(state=("f", 2, 3, 16, 32)), "state"),
+    (dict(out=("f", 2, 3, 64, 16)), "out"),
+    (dict(decay_kind=4, decay=("f", 2, 3, 64, 16)), "decay kind"),
+    (dict(decay_kind=3, decay=("f", 2, 3)), "decay"),
+])
+def test_binding_delta_fwd_checks_shapes(kw, match):
+    args = dict(q=("b", 2, 3, 64, 16), k=("b", 2, 3, 64, 16), v=("b", 2, 3, 64, 16),
+                beta=("f", 2, 3, 64))
+    args.update(kw)
+    mk = {"b": lambda *s: _t(*s), "f": _f}
+    call = {n: (mk[x[0]](*x[1:]) if isinstance(x, tuple) else x) for n, x in args.items()}
+    with pytest.raises(ValueError, match=match):
+        la.delta_fwd(**call)
+
+
+@pytest.mark.parametrize("kw,match", [
+    (dict(beta=("f", 4)), "beta"),
+    (dict(state=("f", 4, 2, 16, 32)), "state"),
+    (dict(state=("b", 4, 2, 16, 16)), "state"),
+    (dict(out=("b", 4, 2, 8)), "out"),
+    (dict(decay_kind=2, decay=("f", 2)), "decay"),
+    (dict(decay_kind=4, decay=("f", 4, 2, 16)), "decay kind"),
+])
+def test_binding_delta_decode_checks_shapes(kw, match):
+    args = dict(q=("b", 4, 2, 16), k=("b", 4, 2, 16), v=("b", 4, 2, 16), beta=("f", 4, 2),
+                state=("f", 4, 2, 16, 16))
+    args.update(kw)
+    mk = {"b": lambda *s: _t(*s), "f": _f}
+    call = {n: (mk[x[0]](*x[1:]) if isinstance(x, tuple) else x) for n, x in args.items()}
+    with pytest.raises(ValueError, match=match):
+        la.delta_decode_step(**call)
+
+
+def test_binding_well_formed_cpu_call_reaches_the_device_check():
+    # every shape right: the only complaint left is that the tensors are not on a GPU
+    with pytest.raises(ValueError, match="GPU tensor"):
+        la.decode_step(_t(4, 2, 16), _t(4, 2, 16), _t(4, 2, 16), _f(4, 2, 16, 16),
+                       decay_kind=la.DECAY_CHANNEL, decay=_f(4, 2, 16), out=_t(4, 2, 16))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        la.chunk_fwd(_t(2, 3, 64, 32), _t(2, 3, 64, 32), _t(2, 3, 64, 32),
+                     decay_kind=la.DECAY_CHANNEL, decay=_f(2, 3, 64, 32),
+                     state=_f(2, 3, 32, 32), out=_t(2, 3, 64, 32))

@@ -74,14 +74,11 @@ def test_channel_plan_invariance(gpu_lib, tile, segments, parts):
     """Value tiles, key parts and sequence segments (the segment scan composes
     per-channel decays) all give the oracle's result."""
     la = gpu_lib
-    la.set_plan(la.KERNEL_STRIPE, tile, segments, parts)
-    try:
+    with la.using_plan(la.KERNEL_STRIPE, tile, segments, parts):
         c = W.RandomCase(1, 2, 64 * 21 + 5, 128, 128, torch.bfloat16, W.PHI_IDENTITY,
                          W.DECAY_CHANNEL, seed=460 + tile + segments + parts,
                          scale=1.0 / np.sqrt(128), channel_mean=0.02, with_state=True)
         _run(la, c, 64, f"plan tile={tile} P={segments} parts={parts}")
-    finally:
-        la.set_plan(0, 0, 0, 0)
 
 
 def test_channel_broadcast_equals_token_decay(gpu_lib):

@@ -77,15 +77,12 @@ def test_norm_head_dims(gpu_lib, dk, dv, C):
                                                  (32, 4, 2), (128, 21, 2), (64, 1, 2), (32, 1, 1)])
 def test_norm_plan_invariance(gpu_lib, tile, segments, parts):
     la = gpu_lib
-    la.set_plan(la.KERNEL_STRIPE, tile, segments, parts)
-    try:
+    with la.using_plan(la.KERNEL_STRIPE, tile, segments, parts):
         for kind in (W.DECAY_HEAD, W.DECAY_GATE, W.DECAY_NONE):
             c = W.RandomCase(1, 2, 64 * 20 + 17, 128, 128, torch.bfloat16, W.PHI_ELU1, kind,
                              seed=tile + segments + kind, scale=1.0 / np.sqrt(128),
                              gate_shift=-4.0, with_state=True)
             _run(la, c, 64, f"plan tile={tile} P={segments} parts={parts}")
-    finally:
-        la.set_plan()
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])

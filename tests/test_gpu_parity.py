@@ -114,8 +114,7 @@ def test_launch_plan_invariance(gpu_lib, kernel, tile, segments, groups):
     """Kernel, value tile, column groups and sequence segments change the work split,
     not the result."""
     la = gpu_lib
-    la.set_plan(kernel, tile, segments, groups)
-    try:
+    with la.using_plan(kernel, tile, segments, groups):
         # 21 chunks: segments of ceil(21 / P) chunks, so P = 8 runs as 7 segments of 3
         got = la.plan(1, 2, 64 * 20 + 17, 128, 128, 64)
         assert got[:2] == (kernel, tile) and got[2] == -(-21 // -(-21 // segments))
@@ -126,8 +125,6 @@ def test_launch_plan_invariance(gpu_lib, kernel, tile, segments, groups):
                              gate_shift=-5.0, with_state=True)
             _check_case(la, c, 64, f"plan kernel={kernel} tile={tile} P={segments} "
                                    f"groups={groups}")
-    finally:
-        la.set_plan()
 
 
 def test_resume_equals_one_call(gpu_lib):
@@ -263,8 +260,7 @@ def test_degenerate_decays(gpu_lib, dtype, dk, dv, plan):
     Exponents reach -4e3 in log2 units: no inf - inf, no NaN, and a carried
     state of fp32 zeros where the decay wipes it."""
     la = gpu_lib
-    la.set_plan(*plan)
-    try:
+    with la.using_plan(*plan):
         H, L = 4, 64 * 6 + 29
         q, k, v, s0, gate = _degenerate_inputs(dk, dv, H, L, dtype, seed=dk + dv + plan[2])
         gamma = torch.tensor([1.0, 1e-20, 1.0 - 2.0 ** -20, 0.5], dtype=torch.float32)
@@ -284,8 +280,6 @@ def test_degenerate_decays(gpu_lib, dtype, dk, dv, plan):
                 closed = (qd * kd).sum(-1, keepdims=True) * vd
                 got = _np(out[0, 1])
                 assert np.abs(got - closed).max() <= tol * np.abs(closed).max()
-    finally:
-        la.set_plan()
 
 
 def test_decode_degenerate_decays(gpu_lib):
