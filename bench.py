@@ -27,8 +27,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA
 # `python bench.py --profile`: HBM traffic (FETCH_SIZE / WRITE_SIZE scaled by a
 # copy kernel of known size) and MFMA busy time.  Each file records the sha256
 # of the library sources it was measured on and is used only while they match.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "chunk_stripe_retnet_hbm_traffic.md")
-MFMA_PROFILE = os.path.join(ROOT, "profiles", "chunk_stripe_retnet_mfma.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "forward_legs_hbm_traffic.md")
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "forward_legs_mfma.md")
 COPY_BYTES = 1 << 29           # the calibration copy: 512 MiB read, 512 MiB written
 
 
@@ -144,6 +144,70 @@ def bench_chunk(la, torch, W, steps, warmup):
     kernel, tile, P, groups = la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)
     return dict(w=w, ms_step=ms_step, wall=wall, kern_ms=kern_ms, bytes=by, flops=flops,
                 kernel=kernel, tile=tile, P=P, groups=groups, need=need)
+
+
+SCRUB_BYTES = 1 << 29  # a cold call is preceded by a 512 MiB write (the MALL holds 256 MB)
+
+
+def bench_forward_leg(la, torch, W, name, steps, warmup, cold=False):
+    """la_chunk_fwd on workload `name` (state init outside the timing), each call
+    bracketed by HIP events on the launch stream.  cold: before every call a
+    512 MiB buffer is written, so the inputs are not served from the memory-side
+    cache (elu_bf16's 100 MB of inputs fit in it)."""
+    w = W.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v, decay = W.chunk_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    decay = None if decay is None else decay.to(dev)
+    S = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
+    out = torch.empty_like(v)
+    need = la.chunk_fwd_workspace_bytes(w.B, w.H, w.L, w.dk, w.dv, w.C, la.LA_BF16, w.decay_kind)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device=dev) if cold else None
+
+    def call():
+        la.chunk_fwd(q, k, v, C=w.C, phi=w.phi, decay_kind=w.decay_kind, decay=decay, state=S,
+                     out=out, workspace=ws if need else None, stream=stream)
+
+    settle(torch, call)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        la.state_init(S, stream=stream)
+        if cold:
+            scrub.fill_(i & 0xFF)
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    by, flops = chunk_algorithmic(w, with_state=True)
+    return dict(w=w, ms=ms, bytes=by, flops=flops, plan=la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C))
+
+
+def leg_report(r, tokens, profile_key=None, plan=None):
+    """The per-leg JSON object: time, tokens/s and the roofline block (algorithmic
+    bytes / HIP-event time against 8 TB/s; counter traffic and MFMA busy from
+    profiles/ while their sources match)."""
+    ach = r["bytes"] / (r["ms"] / 1000.0) / 1e9
+    rep = {"ms_per_call": r["ms"], "tokens_per_s": tokens / (r["ms"] / 1000.0),
+           "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": r["bytes"],
+                        "traffic": None if profile_key is None else
+                        profile_value(TRAFFIC_PROFILE, f"hbm_bytes_{profile_key}"),
+                        "rocprof_mfma_busy_pct": None if profile_key is None else
+                        profile_value(MFMA_PROFILE, f"mfma_busy_pct_{profile_key}")}}
+    if "flops" in r:
+        tf = r["flops"] / (r["ms"] / 1000.0) / 1e12
+        rep["roofline"]["mfma_tflops"] = tf
+        rep["roofline"]["mfma_frac"] = tf / BF16_PEAK_TFLOPS
+    if plan is not None:
+        rep["plan"] = plan
+    return rep
 
 
 def bench_chunk_norm(la, torch, W, steps, warmup):
@@ -277,45 +341,93 @@ def bench_decode(la, torch, W, steps, reps=3):
     return dict(w=w, steps=steps, ms=ms, step_us=1000.0 * ms / steps, bytes=per_step_bytes)
 
 
-def cpu_baseline(W):
-    """The fp64 oracle on the same workload, on all host cores.
+CPU_BUDGET_S = 6.0  # seconds of oracle work per config in the CPU baseline
 
-    The whole batch is used when one pass takes under ~30 s on this host
-    (calibrated on one head); otherwise the first heads that fit."""
+
+def _oracle_chunk_rate(W, name, cores):
+    """Oracle tokens/s on workload `name`: the whole batch when it fits the budget
+    (calibrated on one head), else the first heads that do, scaled to the batch."""
     import oracle
-    w = W.WORKLOADS["retnet_bf16"]
-    cores = oracle.host_threads()
+    w = W.WORKLOADS[name]
     heads_all = w.B * w.H
-    f64 = lambda t: t.double().numpy()  # noqa: E731
-    q, k, v, gamma = W.chunk_inputs(w, heads=slice(0, 1))
+    f64 = lambda t: None if t is None else t.double().numpy()  # noqa: E731
+
+    def args_for(n):
+        q, k, v, d = W.chunk_inputs(w, heads=slice(0, n))
+        if w.decay_kind == 1:
+            # gamma[h] of the first n flattened heads, one per head of a [1, n] batch
+            dec = f64(d)[[bh % w.H for bh in range(n)]]
+        else:
+            dec = f64(d)
+            if dec is not None:
+                dec = dec[None]
+        return (f64(q)[None], f64(k)[None], f64(v)[None], w.phi, w.decay_kind, dec)
+
+    a1 = args_for(1)
     t0 = time.perf_counter()
-    oracle.recurrent(f64(q)[None], f64(k)[None], f64(v)[None], 0, 1, f64(gamma[:1]), nthreads=1)
+    oracle.recurrent(*a1, nthreads=1)
     one = time.perf_counter() - t0
-    fit = int(30.0 / max(one, 1e-3)) * cores
-    if fit >= heads_all:
-        q, k, v, gamma = W.chunk_inputs(w)
-        n, args = heads_all, (f64(q), f64(k), f64(v), 0, 1, f64(gamma))
-    else:
-        n = max(1, min(w.H, fit))
-        q, k, v, gamma = W.chunk_inputs(w, heads=slice(0, n))
-        args = (f64(q)[None], f64(k)[None], f64(v)[None], 0, 1, f64(gamma[:n]))
+    n = max(1, min(heads_all, int(CPU_BUDGET_S / max(one, 1e-4)) * cores))
+    a = args_for(n)
     t0 = time.perf_counter()
-    oracle.recurrent(*args, nthreads=cores)
+    oracle.recurrent(*a, nthreads=cores)
     el = time.perf_counter() - t0
     used = min(cores, n)
     # a token (b, t) carries H head-tokens; the sample held n * L head-tokens
-    tokens_per_s = n * w.L / el / w.H
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"{n} of {heads_all} heads x L={w.L} of the retnet_bf16 workload, fp64 "
-                      f"token by token in {el:.1f} s on {used} threads; scaled to tokens/s of "
-                      f"the whole batch"}
+    rate = n * w.L / el / w.H
+    return rate, used, (f"{n} of {heads_all} heads x L={w.L} of the {name} workload, fp64 token "
+                        f"by token in {el:.2f} s on {used} threads; scaled to tokens/s of the "
+                        f"whole batch")
+
+
+def _oracle_decode_rate(W, cores, sequences=32):
+    """Oracle decode steps/s: `sequences` of the 256 sequences (x 32 heads), drawn
+    with the decode workload's recipe, through all its steps -- the oracle's
+    decode step is one token of the recurrence, so the steps of a head run as
+    one recurrence -- scaled to steps/s of all 256 x 32 heads."""
+    import oracle
+    w = W.DECODE
+    st = W.DecodeStream(w, N=sequences)
+    S0 = st.initial_state().double().numpy()
+    qkv = [st.step() for _ in range(w.steps)]
+    q, k, v = (torch_stack_steps([x[i] for x in qkv]) for i in range(3))
+    t0 = time.perf_counter()
+    oracle.recurrent(q, k, v, state=S0, nthreads=cores)
+    el = time.perf_counter() - t0
+    frac = sequences / w.N
+    return w.steps * frac / el, min(cores, sequences * w.H), (
+        f"{sequences} of {w.N} sequences x {w.H} heads x {w.steps} steps of decode_bf16, fp64 in "
+        f"{el:.2f} s; scaled to steps/s of all {w.N * w.H} heads")
+
+
+def torch_stack_steps(xs):
+    """[T] list of [N, H, d] step tensors -> fp64 [N, H, T, d]."""
+    import torch
+    return torch.stack(xs, dim=2).double().numpy()
+
+
+def cpu_baseline(W):
+    """The fp64 oracle on every timed workload, on all host cores: the headline
+    (retnet_bf16) as the baseline proper, the others under `configs`."""
+    import oracle
+    cores = oracle.host_threads()
+    rate, used, sample = _oracle_chunk_rate(W, "retnet_bf16", cores)
+    res = {"value": rate, "unit": "tokens/s", "cores": used, "kind": "oracle", "sample": sample,
+           "configs": {}}
+    for name in ("elu_bf16", "gated_bf16"):
+        r, u, smp = _oracle_chunk_rate(W, name, cores)
+        res["configs"][name] = {"value": r, "unit": "tokens/s", "cores": u, "sample": smp}
+    r, u, smp = _oracle_decode_rate(W, cores)
+    res["configs"]["decode_bf16"] = {"value": r, "unit": "steps/s", "cores": u, "sample": smp}
+    return res
 
 
 def profile_pass(la, torch, W):
     """A short fixed sequence of launches for counter passes: one plain copy of
     COPY_BYTES (the calibration), then the forward of the timed workload
-    (state init + la_chunk_fwd) three times, 20 decode steps, two forwards
-    of the per-channel gate workload, then two delta-rule forwards."""
+    (state init + la_chunk_fwd) three times, 20 decode steps, three forwards
+    each of elu_bf16 and gated_bf16, two of the normalised form, two of the
+    per-channel gate workload, then two delta-rule forwards."""
     dev = torch.device("cuda:0")
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -325,6 +437,9 @@ def profile_pass(la, torch, W):
     del src, dst
     bench_chunk(la, torch, W, steps=1, warmup=1)
     bench_decode(la, torch, W, steps=20, reps=1)
+    bench_forward_leg(la, torch, W, "elu_bf16", steps=2, warmup=1)
+    bench_forward_leg(la, torch, W, "gated_bf16", steps=2, warmup=1)
+    bench_chunk_norm(la, torch, W, steps=1, warmup=1)
     bench_chunk_gla(la, torch, W, steps=1, warmup=1)
     bench_delta(la, torch, W, steps=1, warmup=1)
     torch.cuda.synchronize()
@@ -361,6 +476,10 @@ def main():
         profile_pass(la, torch, W)
         return
     c = bench_chunk(la, torch, W, args.steps, args.warmup)
+    e_warm = bench_forward_leg(la, torch, W, "elu_bf16", args.steps, args.warmup)
+    e_cold = bench_forward_leg(la, torch, W, "elu_bf16", max(args.steps // 2, 1),
+                               max(args.warmup // 2, 1), cold=True)
+    gt = bench_forward_leg(la, torch, W, "gated_bf16", args.steps, args.warmup)
     n = bench_chunk_norm(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
     g = bench_chunk_gla(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
     dl = bench_delta(la, torch, W, max(args.steps // 10, 1), max(args.warmup // 5, 1))
@@ -390,13 +509,21 @@ def main():
                             "dv_tile": c["tile"], "segments": c["P"]}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": profile_value(TRAFFIC_PROFILE, "hbm_bytes_per_forward"),
+                     "traffic": profile_value(TRAFFIC_PROFILE, "hbm_bytes_retnet_bf16"),
                      "kernel": "the chunked forward of one la_chunk_fwd: its segment state pass "
                                "and output pass (HIP events around the call)",
                      "kernel_ms": c["kern_ms"], "algorithmic_bytes": c["bytes"],
                      "mfma_tflops": c["flops"] / (c["kern_ms"] / 1000.0) / 1e12,
                      "mfma_frac": c["flops"] / (c["kern_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS,
-                     "rocprof_mfma_busy_pct": profile_value(MFMA_PROFILE, "mfma_busy_pct")},
+                     "rocprof_mfma_busy_pct": profile_value(MFMA_PROFILE,
+                                                            "mfma_busy_pct_retnet_bf16")},
+        "elu": dict(workload="elu_bf16: B=4, H=16, L=4096, d=64, phi = elu+1, no decay, C=64",
+                    warm=leg_report(e_warm, e_warm["w"].B * e_warm["w"].L, "elu_bf16",
+                                    e_warm["plan"]),
+                    cold=leg_report(e_cold, e_cold["w"].B * e_cold["w"].L)),
+        "gated": dict(workload="gated_bf16: B=1, H=16, L=65536, d=128, a_t = exp(-softplus(g_t)), "
+                               "C=64",
+                      **leg_report(gt, gt["w"].B * gt["w"].L, "gated_bf16", gt["plan"])),
         "normalized": {"workload": "retnet_bf16 shapes, normalised form, phi = elu+1",
                        "ms_per_call": n["ms"], "tokens_per_s": tokens / (n["ms"] / 1000.0),
                        "algorithmic_bytes": n["bytes"],

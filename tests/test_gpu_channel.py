@@ -163,25 +163,24 @@ def test_channel_decode_head_dims(gpu_lib, dk, dv):
     assert oracle.rel_err(_np(S), ref_S) < 1e-5  # the state itself stays fp32
 
 
-def test_gla_workload_sampled_heads(gpu_lib):
+def test_gla_workload_whole_output(gpu_lib):
     """The full gla_bf16 workload (B=2, H=32, L=16384, d=128, C=64) in the
-    bench's launch configuration; the oracle recomputes three sampled heads."""
+    bench's launch configuration; the oracle recomputes every head, and the
+    whole output and final state are compared."""
     la = gpu_lib
     w = W.WORKLOADS["gla_bf16"]
-    print(f"[workload] gla_bf16 plan={la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)}", flush=True)
+    print(f"[workload] gla_bf16 plan={la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C, decay_kind=4)}",
+          flush=True)
     q, k, v, decay = W.chunk_inputs(w)
     S = torch.zeros(w.B, w.H, w.dk, w.dv, device=DEV)
     out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=w.C, decay_kind=W.DECAY_CHANNEL,
                        decay=decay.to(DEV), state=S)
     torch.cuda.synchronize()
-    heads = [0, 33, 63]
-    flat = lambda x: x.reshape(w.B * w.H, *x.shape[2:])  # noqa: E731
-    qs, ks, vs, ds = (flat(x)[heads][None] for x in (q, k, v, decay))
-    ref, ref_s = oracle.recurrent(_np(qs), _np(ks), _np(vs), 0, W.DECAY_CHANNEL, _np(ds))
-    got = _np(flat(out.cpu())[heads][None])
-    got_s = _np(flat(S.cpu())[heads][None])
+    got, got_s = _np(out), _np(S)
+    del out, S
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), 0, W.DECAY_CHANNEL, _np(decay))
     e_out, e_s = oracle.rel_err(got, ref), oracle.rel_err(got_s, ref_s)
-    print(f"gla_bf16: sampled heads {heads}: output rel err {e_out:.3e}, state rel err {e_s:.3e}")
+    print(f"gla_bf16: all heads: output rel err {e_out:.3e}, state rel err {e_s:.3e}", flush=True)
     assert e_out <= 1e-2 and e_s <= 1e-2
 
 

@@ -140,9 +140,10 @@ def test_delta_decode_head_dims(gpu_lib, dk, dv):
     assert oracle.rel_err(_np(S), ref_S) < 1e-5  # the state itself stays fp32
 
 
-def test_delta_workload_sampled_heads(gpu_lib):
+def test_delta_workload_whole_output(gpu_lib):
     """The full delta_bf16 workload (B=2, H=32, L=16384, d=128, C=64, gated) as the
-    bench launches it; the oracle recomputes three sampled heads."""
+    bench launches it; the oracle recomputes every head, and the whole output
+    and final state are compared."""
     la = gpu_lib
     w = W.DELTA
     print(f"[workload] delta_bf16 B={w.B} H={w.H} L={w.L} d={w.dk} C={w.C}", flush=True)
@@ -151,14 +152,13 @@ def test_delta_workload_sampled_heads(gpu_lib):
     out = la.delta_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), C=w.C,
                        decay_kind=w.decay_kind, decay=decay.to(DEV), state=S)
     torch.cuda.synchronize()
-    heads = [0, 33, 63]
-    flat = lambda x: x.reshape(w.B * w.H, *x.shape[2:])  # noqa: E731
-    qs, ks, vs, bs, ds = (flat(x)[heads][None] for x in (q, k, v, beta, decay))
-    ref, ref_s = oracle.delta_recurrent(_np(qs), _np(ks), _np(vs), _np(bs), w.decay_kind, _np(ds))
-    got = _np(flat(out.cpu())[heads][None])
-    got_s = _np(flat(S.cpu())[heads][None])
+    got, got_s = _np(out), _np(S)
+    del out, S
+    ref, ref_s = oracle.delta_recurrent(_np(q), _np(k), _np(v), _np(beta), w.decay_kind,
+                                        _np(decay))
     e_out, e_s = oracle.rel_err(got, ref), oracle.rel_err(got_s, ref_s)
-    print(f"delta_bf16: sampled heads {heads}: output rel err {e_out:.3e}, state rel err {e_s:.3e}")
+    print(f"delta_bf16: all heads: output rel err {e_out:.3e}, state rel err {e_s:.3e}",
+          flush=True)
     assert e_out <= 1e-2 and e_s <= 1e-2
 
 
