@@ -31,7 +31,9 @@ class Plan(ctypes.Structure):
 EXPORTS = ("la_state_init", "la_chunk_fwd_workspace_bytes", "la_chunk_fwd", "la_decode_step",
            "la_status_string", "la_chunk_fwd_plan", "la_chunk_fwd_planned", "la_chunk_fwd_norm",
            "la_decode_step_norm", "la_delta_fwd_workspace_bytes", "la_delta_fwd",
-           "la_delta_decode_step")
+           "la_delta_decode_step", "la_chunk_fwd_noalloc")
+# size of the fixed scratch array la_chunk_fwd_noalloc uses (LA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 # the plan request chunk_fwd passes when given none (tests use `using_plan`);
@@ -80,6 +82,8 @@ def load():
                                  ctypes.c_size_t, vp]
     lib.la_delta_decode_step.restype = i
     lib.la_delta_decode_step.argtypes = [vp, vp, vp, f, i, i, i, i, i, i, f, vp, vp, vp]
+    lib.la_chunk_fwd_noalloc.restype = i
+    lib.la_chunk_fwd_noalloc.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp, vp, vp]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i]
     lib.la_chunk_fwd_plan.restype = i
@@ -292,6 +296,28 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, C: int = 64,
     _check(lib.la_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, H, L, dk, dv, C, phi,
                             decay_kind, _ptr(decay), _ptr(state), _ptr(out), _ptr(workspace),
                             ws_bytes, _stream(stream)), "la_chunk_fwd")
+    return out
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                      C: int = 64, phi: int = PHI_IDENTITY, decay_kind: int = DECAY_NONE,
+                      decay=None, state=None, stream=None) -> torch.Tensor:
+    """la_chunk_fwd_noalloc: the forward without a workspace, for callers that cannot
+    allocate.  `out` ([B,H,L,dv], q's dtype) is required, since this call allocates
+    nothing; the library's fixed per-device scratch stands in for the workspace."""
+    dt = _qkv(q, k, v, 3)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    decay = _check_decay(decay, decay_kind, B, H, L, dk)
+    _shape(state, "state", (B, H, dk, dv), torch.float32)
+    if out is None:
+        raise ValueError("chunk_fwd_noalloc needs out: it allocates nothing")
+    _shape(out, "out", (B, H, L, dv), q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (decay, "decay"), (state, "state"), (out, "out")):
+        _dev(t, n)
+    _check(load().la_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), dt, B, H, L, dk, dv, C, phi,
+                                       decay_kind, _ptr(decay), _ptr(state), _ptr(out),
+                                       _stream(stream)), "la_chunk_fwd_noalloc")
     return out
 
 

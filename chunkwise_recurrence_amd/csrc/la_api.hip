@@ -5,6 +5,7 @@
 // on a machine without a GPU (the plan asks the runtime for the current
 // device's compute units, and assumes an MI355X's 256 when none is visible).
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "la.h"
@@ -39,6 +40,35 @@ int device_compute_units() {
   }
   g_device_cus[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// Scratch for la_chunk_fwd_noalloc: a fixed device array instead of a caller
+// workspace.  Each device the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: host code uses only the address hipGetSymbolAddress returns
+// for the current device (g_scratch_ptr).
+constexpr size_t kScratchBytes = LA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's scratch address, looked up once per device with that
+// device current.  nullptr if the lookup failed.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    if (g_scratch_err[dev] != hipSuccess) (void)hipGetLastError();
+  });
+  return g_scratch_ptr[dev];
 }
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -259,7 +289,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
                          int L, int d_k, int d_v, int C, int phi, int decay_kind,
                          const float* decay_data, float* state, float* norm_state, bool norm,
                          const la_plan* request, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, bool use_scratch = false) {
   la_status st = check_chunk_shape(dtype, B, H, L, d_k, d_v, C);
   if (st != LA_OK) return st;
   if (phi != LA_PHI_IDENTITY && phi != LA_PHI_ELU1) return LA_ERR_UNSUPPORTED;
@@ -280,6 +310,13 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
       (decay_data && !aligned(decay_data, 4)))
     return LA_ERR_ALIGN;
   if (p.ws_bytes > 0) {
+    if (use_scratch) {
+      // la_chunk_fwd_noalloc: the device's fixed scratch array, if the plan fits it
+      if (p.ws_bytes > kScratchBytes) return LA_ERR_WORKSPACE;
+      workspace = device_scratch();
+      workspace_bytes = kScratchBytes;
+      if (!workspace) return LA_ERR_DEVICE;
+    }
     if (!workspace || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return LA_ERR_ALIGN;
   }
@@ -399,6 +436,13 @@ la_status la_chunk_fwd_norm(const void* q, const void* k, const void* v, int dty
                             void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_fwd_impl(q, k, v, dtype, B, H, L, d_k, d_v, C, phi, decay_kind, decay_data, state,
                         norm_state, true, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+la_status la_chunk_fwd_noalloc(const void* q, const void* k, const void* v, int dtype, int B,
+                               int H, int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                               const float* decay_data, float* state, void* out, void* stream) {
+  return chunk_fwd_impl(q, k, v, dtype, B, H, L, d_k, d_v, C, phi, decay_kind, decay_data, state,
+                        nullptr, false, nullptr, out, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 la_status la_chunk_fwd_planned(const void* q, const void* k, const void* v, int dtype, int B,

@@ -238,6 +238,27 @@ la_status la_delta_decode_step(const void* q, const void* k, const void* v, cons
                                const float* decay_data, float* state, void* out, void* stream);
 
 /*
+ * la_chunk_fwd_noalloc -- la_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): no workspace argument, and the call allocates and
+ * frees nothing.  The workspace la_chunk_fwd would take lives instead in a
+ * fixed scratch array of LA_NOALLOC_SCRATCH_BYTES bytes in the library's
+ * device memory, one per device, held from the library's load until the
+ * process ends.  Every other argument, the result and the errors are those
+ * of la_chunk_fwd; a problem whose workspace
+ * (la_chunk_fwd_workspace_bytes) exceeds the scratch returns
+ * LA_ERR_WORKSPACE before anything is launched, and LA_ERR_DEVICE means the
+ * scratch's device address could not be looked up.  The scratch needs no
+ * initialisation and keeps the last call's contents.  All calls on one
+ * device share it: calls that may overlap on one device (other streams,
+ * other threads) race and must be ordered by the caller.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+la_status la_chunk_fwd_noalloc(const void* q, const void* k, const void* v, int dtype, int B,
+                               int H, int L, int d_k, int d_v, int C, int phi, int decay_kind,
+                               const float* decay_data, float* state, void* out, void* stream);
+
+/*
  * Launch plan of la_chunk_fwd (for tests and benchmarks).  The library keeps
  * no plan state: a plan is requested per call.
  *   kernel    LA_KERNEL_F32 (fp32 inputs: one workgroup per head and 32-column

@@ -451,3 +451,21 @@ def test_binding_well_formed_cpu_call_reaches_the_device_check():
         la.chunk_fwd(_t(2, 3, 64, 32), _t(2, 3, 64, 32), _t(2, 3, 64, 32),
                      decay_kind=la.DECAY_CHANNEL, decay=_f(2, 3, 64, 32),
                      state=_f(2, 3, 32, 32), out=_t(2, 3, 64, 32))
+
+
+def test_noalloc_host_checks():
+    # la_chunk_fwd_noalloc validates like la_chunk_fwd, and refuses a workspace beyond its
+    # fixed scratch before touching the device
+    lib = la.load()
+    call = lambda **kw: lib.la_chunk_fwd_noalloc(  # noqa: E731
+        kw.get("q", P16), P16, P16, 1, 1, 1, kw.get("L", 64), 64, 64, 64, 0, kw.get("kind", 0),
+        kw.get("decay", None), None, kw.get("out", P16), None)
+    assert call(L=0, q=None, out=None) == OK
+    assert call(q=None) == NULL
+    assert call(out=P8) == ALIGN
+    assert call(kind=3) == NULL
+    assert call(kind=7, decay=P16) == UNSUP
+    # a 16M-token gated head: segment states plus 64 MiB of prefix sums
+    assert la.chunk_fwd_workspace_bytes(1, 1, 1 << 24, 64, 64, 64, la.LA_BF16, 3) > \
+        la.NOALLOC_SCRATCH_BYTES
+    assert call(L=1 << 24, kind=3, decay=P16) == WS
