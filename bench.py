@@ -27,8 +27,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X published dense bf16 MFMA
 # `python bench.py --profile`: HBM traffic (FETCH_SIZE / WRITE_SIZE scaled by a
 # copy kernel of known size) and MFMA busy time.  Each file records the sha256
 # of the library sources it was measured on and is used only while they match.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "forward_legs_hbm_traffic.md")
-MFMA_PROFILE = os.path.join(ROOT, "profiles", "forward_legs_mfma.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "bench_legs_hbm_traffic.md")
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "bench_legs_mfma.md")
 COPY_BYTES = 1 << 29           # the calibration copy: 512 MiB read, 512 MiB written
 
 
