@@ -88,6 +88,11 @@ struct Plan {
   // several workgroups); 0 = none
   size_t ws_S0_off = 0, ws_z0_off = 0;
   bool copy_S0 = false, copy_z0 = false;
+  // per-channel decay (stripe kernel): one flag per output-pass workgroup for
+  // the exact re-run, and (one segment) a copy of S_0 that re-run reads, since
+  // the first pass has overwritten the caller's state with S_L by then
+  size_t ws_flag_off = 0;
+  bool flags = false, copy_S0_host = false;
   bool prefix = false;  // token decays: in-chunk prefix sums of log a in the workspace
 };
 
@@ -210,6 +215,17 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
     p.copy_S0 = true;
     p.ws_S0_off = off;
     off += round256((size_t)heads * d_k * d_v * sizeof(float));
+  }
+  if (chan && p.kernel == LA_KERNEL_STRIPE) {
+    const long long groups = ((long long)heads * p.P + 7) / 8;
+    p.flags = true;
+    p.ws_flag_off = off;
+    off += round256((size_t)groups * 8 * (d_v / p.tile) * sizeof(int));
+    if (p.P == 1) {
+      p.copy_S0_host = true;
+      p.ws_S0_off = off;
+      off += round256((size_t)heads * d_k * d_v * sizeof(float));
+    }
   }
   if (norm && (p.P > 1 || d_v / p.tile > 1)) {
     p.copy_z0 = true;
@@ -354,6 +370,14 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
     if (la::launch_copy_f32(z0, norm_state, (size_t)B * H * d_k, s) != hipSuccess)
       return LA_ERR_DEVICE;
     a.z0 = z0;
+  }
+
+  if (p.flags) a.ws_flag = reinterpret_cast<int*>(ws + p.ws_flag_off);
+  if (p.copy_S0_host && state) {
+    float* s0 = reinterpret_cast<float*>(ws + p.ws_S0_off);
+    if (la::launch_copy_f32(s0, state, (size_t)B * H * d_k * d_v, s) != hipSuccess)
+      return LA_ERR_DEVICE;
+    a.s0 = s0;
   }
 
   hipError_t e;

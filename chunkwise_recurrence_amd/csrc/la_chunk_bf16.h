@@ -320,12 +320,14 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
       }
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
-        const float m = p0 + g < sigma ? 1.0f : 0.0f;
-        const float e = exp2f(lg[g] * m);
+        // segments past sigma are left out by selection (a total decay of
+        // -inf times a 0 weight would give NaN)
+        const bool m = p0 + g < sigma;
+        const float e = exp2f(lg[g]);
 #pragma unroll
         for (int t = 0; t < G::TPW; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) accS[t][i] = e * accS[t][i] + m * inc[g][t][i];
+          for (int i = 0; i < 4; ++i) accS[t][i] = m ? e * accS[t][i] + inc[g][t][i] : accS[t][i];
       }
     }
 #pragma unroll

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(const ChunkArgs a) {
     if (chan && tid < DK) {
       float b = 0.0f;
       for (int i = 0; i < n; ++i) {
-        b += dch[(size_t)(t0 + i) * DK + tid];
+        b += clamp_log_decay(dch[(size_t)(t0 + i) * DK + tid]);
         sBc[i * DK + tid] = b;
       }
     }

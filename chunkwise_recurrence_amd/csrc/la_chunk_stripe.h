@@ -55,13 +55,21 @@
 //
 //   q~_id = q_id e^{b_id - r_d},   k~_jd = k_jd e^{r_d - b_jd}
 //
-// (each exponent within half the chunk's total decay, so both stay in fp32
-// range), which turns the scores into q~ k~^T, the inter-chunk term into
-// q~ (diag(e^r) S) and the update into
+// (each exponent within half the chunk's total decay), which turns the scores
+// into q~ k~^T, the inter-chunk term into q~ (diag(e^r) S) and the update into
 // S' = diag(e^{b_last - r}) (diag(e^r) S + k~^T V).  The prefix runs over
 // log a loaded straight into registers (each thread scans a run of tokens for
 // two channels, the runs combine through LDS), and q~, k~ replace q, k in
 // their LDS tiles, so everything after is the kernel's usual MFMA work.
+// The split stays in range while every channel's log2 decay over a chunk sums
+// to at least -kSplitMax (factors up to 2^96).  A workgroup that meets a chunk
+// beyond that flags itself, and a second launch (EXACT) recomputes exactly the
+// flagged workgroups' segments -- the secondary-chunking idea for GLA's gate,
+// taken to single tokens: scores per element in fp32 with each exponent a
+// direct sum of log2 a over (j, i] (never a difference of prefix sums), the
+// inter term against q^ = q e^{b} and the update S' = diag(e^{b_last}) S +
+// (k e^{b_last - b})^T V, every exponent <= 0.  The state pass always uses
+// that exact update, so its segment increments are right whatever the decay.
 //
 // STATE_ONLY computes a segment's state increment and total log2 decay from a
 // zero state (the first pass of the segment split).  It walks the segment's
@@ -69,7 +77,7 @@
 // does not depend on the order), so the chunks it reads last -- the starts of
 // the segments -- are the ones the output pass reads first, while they may
 // still sit in the memory-side cache.  (With the per-channel decay it walks
-// forward and applies the main pass's update, whose factors stay bounded.)
+// forward and applies the exact update above.)
 // The main pass composes
 // the exclusive prefix of the (decay, state) pairs in its prologue, the
 // parallel / associative scan idea of the tutorial's section 3.3.
@@ -129,6 +137,10 @@ struct Geo {
   static constexpr bool UNIFORM = QK_BLK % NW == 0 && V_BLK % NW == 0 && NRB % KH == 0 &&
                                   STORES + LOADS_MAX < 64;
   static constexpr size_t XCH_BYTES = KH > 1 ? (size_t)NWV * NRB * 4096 : 16;
+  // the key parts' exchange, or (per-channel decay, output pass) the exact
+  // path's log2 a tile [C][DK] fp32, which it holds before the exchange is used
+  static constexpr size_t LA_BYTES = (CH && !SO) ? 4 * (size_t)C * DK : 16;
+  static constexpr size_t XU_BYTES = XCH_BYTES > LA_BYTES ? XCH_BYTES : LA_BYTES;
   // the normalised form's z, denominator partials and row sums (counted for
   // every instance, so both forms run the same pipeline depth)
   static constexpr size_t NORM_BYTES = 2 * 4 * (size_t)DK + 4 * (size_t)C * (KH + NRB);
@@ -140,7 +152,7 @@ struct Geo {
     return SO ? (size_t)n * ((size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
                     W_BYTES + NORM_BYTES + 256
               : (size_t)n * (2 * (size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
-                    2 * (size_t)C * C + W_BYTES + XCH_BYTES + 2048 * (size_t)NW  + NORM_BYTES + 256;
+                    2 * (size_t)C * C + W_BYTES + XU_BYTES + 2048 * (size_t)NW  + NORM_BYTES + 256;
   }
   // the per-channel decay's prefetch registers stay bounded (TPR <= 16)
   static constexpr bool CH_OK = !CH || (TPR >= 1 && TPR <= 16 && DK >= 32);
@@ -246,6 +258,11 @@ __device__ __forceinline__ void lds_wave_sync() {
 
 enum { kCatNone = 0, kCatHead = 1, kCatToken = 2, kCatChannel = 3 };
 
+// Per-channel decay: the largest |log2 decay| of a chunk (per channel) the
+// split q e^{b - r}, k e^{r - b} takes (factors up to 2^96); beyond it the
+// chunk takes the exact path.
+constexpr float kSplitMax = 192.0f;
+
 // (I, J) of causal score block b in the order (0,0), (1,0), (1,1), (2,0), ...
 __host__ __device__ constexpr int block_i(int b) {
   int i = 0;
@@ -254,9 +271,72 @@ __host__ __device__ constexpr int block_i(int b) {
 }
 __host__ __device__ constexpr int block_j(int b) { return b - block_i(b) * (block_i(b) + 1) / 2; }
 
-template <int DK, int NWV, int KH, int C, int CAT, bool STATE_ONLY, bool NORM>
+// Per-channel decay, exact path: P~[i][j] = sum_d phi(q)_id phi(k)_jd 2^{D_ijd}
+// for j <= i < nvalid (zero elsewhere), with D_ijd the sum of log2 a over
+// tokens j+1 .. i of channel d, accumulated directly as j steps down: no
+// difference of prefix sums (no cancellation, no inf - inf) and every
+// exponent <= 0.  GR lanes share a query row, CPG channels each; the q and k
+// tiles (row-major bf16, swizzled) hold phi already, lat is the chunk's log2 a
+// [C][DK] fp32 and sP the bf16 P~ tile.
+template <int DK, int C, int NW>
+__device__ __forceinline__ void exact_scores(const char* qb, const char* kb,
+                                                        const float* lat, char* sP, int nvalid,
+                                                        int tid) {
+  constexpr int WCK = DK / 8, WCP = C / 8;
+  constexpr int T = 64 * NW;
+  constexpr int GR0 = T >= 8 * C ? 8 : T >= 4 * C ? 4 : T >= 2 * C ? 2 : 1;
+  constexpr int GR = GR0 < DK / 8 ? GR0 : DK / 8;
+  constexpr int CPG = DK / GR;
+  for (int task = tid; task < C * GR; task += T) {
+    const int i = task / GR, g = task % GR, c0 = CPG * g;
+    float qv[CPG], D[CPG];
+#pragma unroll
+    for (int m = 0; m < CPG / 8; ++m) {
+      const u32x4 w = lds_b128(qb, swz<WCK>(i, c0 + 8 * m));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[8 * m + 2 * e] = bf16_to_f32(w[e] & 0xffffu);
+        qv[8 * m + 2 * e + 1] = bf16_to_f32(w[e] >> 16);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPG; ++c) D[c] = 0.0f;
+    const int jtop = i < nvalid ? i : -1;
+    for (int j = jtop; j >= 0; --j) {
+      float p = 0.0f;
+#pragma unroll
+      for (int m = 0; m < CPG / 8; ++m) {
+        const u32x4 w = lds_b128(kb, swz<WCK>(j, c0 + 8 * m));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p += qv[8 * m + 2 * e] * bf16_to_f32(w[e] & 0xffffu) *
+               __builtin_amdgcn_exp2f(D[8 * m + 2 * e]);
+          p += qv[8 * m + 2 * e + 1] * bf16_to_f32(w[e] >> 16) *
+               __builtin_amdgcn_exp2f(D[8 * m + 2 * e + 1]);
+        }
+      }
+#pragma unroll
+      for (int sh = 1; sh < GR; sh <<= 1) p += __shfl_xor(p, sh);
+      if (j % GR == g) *reinterpret_cast<uint16_t*>(sP + swz<WCP>(i, j)) = (uint16_t)cvt2(p, 0.0f);
+#pragma unroll
+      for (int m = 0; m < CPG / 4; ++m) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(&lat[j * DK + c0 + 4 * m]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) D[4 * m + e] += x[e];
+      }
+    }
+    for (int j = jtop + 1; j < C; ++j)
+      if (j % GR == g) *reinterpret_cast<uint16_t*>(sP + swz<WCP>(i, j)) = 0;
+  }
+}
+
+template <int DK, int NWV, int KH, int C, int CAT, bool STATE_ONLY, bool NORM, bool EXACT = false>
 __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const ChunkArgs a) {
   constexpr bool CHN = CAT == kCatChannel;
+  static_assert(!EXACT || (CHN && !STATE_ONLY), "the exact pass is the per-channel output pass");
+  // per-channel decay: whether every chunk takes the exact form (the state
+  // pass, and the exact re-run of flagged output-pass workgroups)
+  constexpr bool XF = CHN && (STATE_ONLY || EXACT);
   static_assert(!(CHN && NORM), "the normalised form takes no per-channel decay");
   using G = Geo<DK, NWV, KH, C, STATE_ONLY, CHN>;
   static_assert(G::CH_OK, "per-channel decay layout");
@@ -277,6 +357,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   const int vt = slot % a.n_v;
   const int u = (slot / a.n_v) * 8 + (f & 7);
   if (u >= a.n_units) return;
+  // the exact re-run recomputes only the workgroups the fast pass flagged
+  if constexpr (EXACT)
+    if (a.ws_flag[f] == 0) return;
   const int segs = STATE_ONLY ? a.P - 1 : a.P;
   const int bh = u / segs, sigma = u % segs;
   const int hd = bh % a.H;
@@ -298,7 +381,12 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   __shared__ __align__(16) char sP[STATE_ONLY ? 16 : 2 * C * C];
   // partial inter-chunk terms handed between the key parts of a stripe:
   // [stripe][row block][16-byte chunk k][lane]
-  __shared__ __align__(16) char sX[(STATE_ONLY || KH == 1) ? 16 : G::XCH_BYTES];
+  // (per-channel decay: the exact path's log2 a tile [C][DK] shares it; it is
+  // written and read before the exchange)
+  __shared__ __align__(16) char sX[STATE_ONLY ? 16 : G::XU_BYTES];
+  // per-channel decay, fast output pass: set when a chunk's decay is too strong
+  // for the split (the workgroup's results are then recomputed exactly)
+  __shared__ int sBad;
   // per-wave weights of the current chunk: [0] e^{b_last - b_t}, [1] e^{b_t}
   __shared__ __align__(16) float sW[CHN ? 1 : NW][2][CHN ? 4 : C];
   // per-channel decay: log2-decay totals of each run, then e^r and
@@ -401,13 +489,15 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       }
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
-        const float m = p0 + g < sigma ? 1.0f : 0.0f;
+        // segments past sigma are left out by selection (a total decay of
+        // -inf times a 0 weight would give NaN)
+        const bool m = p0 + g < sigma;
 #pragma unroll
         for (int t = 0; t < G::NMK_OWN; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float la2 = CHN ? lg[g][CHN ? t : 0][CHN ? r : 0] : lg[g][0][0];
-            accS[t][r] = exp2f(la2 * m) * accS[t][r] + m * inc[g][t][r];
+            accS[t][r] = m ? exp2f(la2) * accS[t][r] + inc[g][t][r] : accS[t][r];
           }
       }
     }
@@ -449,10 +539,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
             zi[g] = a.ws_z[seg * DK + dk];
           }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float m = p0 + g < sigma ? 1.0f : 0.0f;
-            zv = exp2f(lz[g] * m) * zv + m * zi[g];
-          }
+          for (int g = 0; g < 4; ++g) zv = p0 + g < sigma ? exp2f(lz[g]) * zv + zi[g] : zv;
         }
       }
       zr[t] = zv;
@@ -554,6 +641,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     }
   };
 
+  if (CHN && tid == 0) sBad = 0;
+
   float logA = 0.0f;
   f32x2 logA2 = f32x2{0.0f, 0.0f};  // per-channel decay: totals of channels 2 pr, 2 pr + 1
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
@@ -642,28 +731,33 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       // the runs' totals of the in-run prefixes through LDS
       *reinterpret_cast<f32x2*>(&sTot[run][2 * pr]) = accb;
       lds_barrier();
-      f32x2 off = f32x2{0.0f, 0.0f}, tot = f32x2{0.0f, 0.0f};
+      f32x2 off = f32x2{0.0f, 0.0f}, tot = f32x2{0.0f, 0.0f}, later = f32x2{0.0f, 0.0f};
 #pragma unroll
       for (int r = 0; r < G::RUNS; ++r) {
         const f32x2 x = *reinterpret_cast<const f32x2*>(&sTot[r][2 * pr]);
         off += r < run ? x : f32x2{0.0f, 0.0f};
+        later += r > run ? x : f32x2{0.0f, 0.0f};
         tot += x;
       }
-      const f32x2 rr = tot * 0.5f;  // r = b_last / 2
-      // q~ = phi(q) e^{b - r}, k~ = phi(k) e^{r - b}, in place
+      if constexpr (!XF) {
+        // the split below puts factors up to 2^{-tot/2} into q and k: a chunk
+        // whose log2 decay sums below -kSplitMax in any channel (or is not a
+        // number) flags the workgroup for the exact re-run
+        if (!(tot[0] >= -kSplitMax && tot[1] >= -kSplitMax)) sBad = 1;
+        const f32x2 rr = tot * 0.5f;  // r = b_last / 2
+        // q~ = phi(q) e^{b - r}, k~ = phi(k) e^{r - b}, in place
 #pragma unroll
-      for (int i = 0; i < G::TPR; ++i) {
-        const f32x2 b = off + bl[i];
-        const int o = swz<G::WCK>(run * G::TPR + i, 2 * pr);
-        uint32_t* kp = reinterpret_cast<uint32_t*>(kb + o);
-        const uint32_t kw = *kp;
-        float k0 = bf16_to_f32(kw & 0xffffu), k1 = bf16_to_f32(kw >> 16);
-        if (elu) {
-          k0 = feature_elu1(k0);
-          k1 = feature_elu1(k1);
-        }
-        *kp = cvt2(k0 * __builtin_amdgcn_exp2f(rr[0] - b[0]), k1 * __builtin_amdgcn_exp2f(rr[1] - b[1]));
-        if constexpr (!STATE_ONLY) {
+        for (int i = 0; i < G::TPR; ++i) {
+          const f32x2 b = off + bl[i];
+          const int o = swz<G::WCK>(run * G::TPR + i, 2 * pr);
+          uint32_t* kp = reinterpret_cast<uint32_t*>(kb + o);
+          const uint32_t kw = *kp;
+          float k0 = bf16_to_f32(kw & 0xffffu), k1 = bf16_to_f32(kw >> 16);
+          if (elu) {
+            k0 = feature_elu1(k0);
+            k1 = feature_elu1(k1);
+          }
+          *kp = cvt2(k0 * __builtin_amdgcn_exp2f(rr[0] - b[0]), k1 * __builtin_amdgcn_exp2f(rr[1] - b[1]));
           uint32_t* qp = reinterpret_cast<uint32_t*>(qb + o);
           const uint32_t qw = *qp;
           float q0 = bf16_to_f32(qw & 0xffffu), q1 = bf16_to_f32(qw >> 16);
@@ -673,12 +767,69 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
           }
           *qp = cvt2(q0 * __builtin_amdgcn_exp2f(b[0] - rr[0]), q1 * __builtin_amdgcn_exp2f(b[1] - rr[1]));
         }
-      }
-      if (run == 0) {
-        *reinterpret_cast<f32x2*>(&sER[2 * pr]) =
-            f32x2{__builtin_amdgcn_exp2f(rr[0]), __builtin_amdgcn_exp2f(rr[1])};
-        *reinterpret_cast<f32x2*>(&sEL[2 * pr]) =
-            f32x2{__builtin_amdgcn_exp2f(tot[0] - rr[0]), __builtin_amdgcn_exp2f(tot[1] - rr[1])};
+        if (run == 0) {
+          *reinterpret_cast<f32x2*>(&sER[2 * pr]) =
+              f32x2{__builtin_amdgcn_exp2f(rr[0]), __builtin_amdgcn_exp2f(rr[1])};
+          *reinterpret_cast<f32x2*>(&sEL[2 * pr]) =
+              f32x2{__builtin_amdgcn_exp2f(tot[0] - rr[0]), __builtin_amdgcn_exp2f(tot[1] - rr[1])};
+        }
+      } else {
+        // exact form: every factor is 2^(a direct sum of log2 a <= 0).  sf[i]:
+        // the sum over the run's tokens after token i (exclusive suffix)
+        f32x2 sf[G::TPR];
+        f32x2 acs = f32x2{0.0f, 0.0f};
+#pragma unroll
+        for (int i = G::TPR - 1; i >= 0; --i) {
+          sf[i] = acs;
+          acs += run * G::TPR + i < nvalid ? lreg[buf][i] * kLog2e : f32x2{0.0f, 0.0f};
+        }
+        if constexpr (!STATE_ONLY) {
+          // phi on this thread's q and k elements in place, its log2 a into the tile
+          float* lat = reinterpret_cast<float*>(sX);
+#pragma unroll
+          for (int i = 0; i < G::TPR; ++i) {
+            const int t = run * G::TPR + i;
+            const int o = swz<G::WCK>(t, 2 * pr);
+            if (elu) {
+              uint32_t* kp = reinterpret_cast<uint32_t*>(kb + o);
+              uint32_t* qp = reinterpret_cast<uint32_t*>(qb + o);
+              const uint32_t kw = *kp, qw = *qp;
+              *kp = cvt2(feature_elu1(bf16_to_f32(kw & 0xffffu)), feature_elu1(bf16_to_f32(kw >> 16)));
+              *qp = cvt2(feature_elu1(bf16_to_f32(qw & 0xffffu)), feature_elu1(bf16_to_f32(qw >> 16)));
+            }
+            *reinterpret_cast<f32x2*>(&lat[t * DK + 2 * pr]) =
+                t < nvalid ? lreg[buf][i] * kLog2e : f32x2{0.0f, 0.0f};
+          }
+          lds_barrier();
+          exact_scores<DK, C, NW>(qb, kb, reinterpret_cast<const float*>(sX), sP, nvalid, tid);
+          lds_barrier();  // the scores have read the tiles the rescaling below overwrites
+        }
+        // q^ = phi(q) e^{b}, k^ = phi(k) e^{b_last - b}, in place
+#pragma unroll
+        for (int i = 0; i < G::TPR; ++i) {
+          const int o = swz<G::WCK>(run * G::TPR + i, 2 * pr);
+          const f32x2 ek = sf[i] + later;
+          uint32_t* kp = reinterpret_cast<uint32_t*>(kb + o);
+          const uint32_t kw = *kp;
+          float k0 = bf16_to_f32(kw & 0xffffu), k1 = bf16_to_f32(kw >> 16);
+          if (STATE_ONLY && elu) {
+            k0 = feature_elu1(k0);
+            k1 = feature_elu1(k1);
+          }
+          *kp = cvt2(k0 * __builtin_amdgcn_exp2f(ek[0]), k1 * __builtin_amdgcn_exp2f(ek[1]));
+          if constexpr (!STATE_ONLY) {
+            const f32x2 eb = off + bl[i];
+            uint32_t* qp = reinterpret_cast<uint32_t*>(qb + o);
+            const uint32_t qw = *qp;
+            *qp = cvt2(bf16_to_f32(qw & 0xffffu) * __builtin_amdgcn_exp2f(eb[0]),
+                       bf16_to_f32(qw >> 16) * __builtin_amdgcn_exp2f(eb[1]));
+          }
+        }
+        if (run == 0) {
+          *reinterpret_cast<f32x2*>(&sER[2 * pr]) = f32x2{1.0f, 1.0f};
+          *reinterpret_cast<f32x2*>(&sEL[2 * pr]) =
+              f32x2{__builtin_amdgcn_exp2f(tot[0]), __builtin_amdgcn_exp2f(tot[1])};
+        }
       }
       logA2 += tot;
       lds_barrier();
@@ -728,7 +879,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       // S <- e^{b_last} S + K^T diag(e^{b_last - b}) V
       // (state pass: S <- S + K^T diag(e^{B_end - B}) V)
       // (per-channel decay: S <- diag(e^{b_last - r}) (diag(e^r) S + k~^T V))
-      if constexpr (CHN && STATE_ONLY) scale_rows(sER);
+      // (per-channel decay, exact form -- the state pass, and the output
+      // pass's exact path: S <- diag(e^{b_last}) S + k^^T V)
+      if constexpr (XF) scale_rows(sEL);
       if constexpr (CAT != kCatNone && !CHN && !STATE_ONLY) {
         const float eL = __builtin_amdgcn_exp2f(bL);
 #pragma unroll
@@ -786,7 +939,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
           }
         }
       }
-      if constexpr (CHN) scale_rows(sEL);
+      if constexpr (CHN && !XF) scale_rows(sEL);
       if constexpr (NORM) {
         if (stripe == 0) {
           const float eLz = (CAT != kCatNone && !STATE_ONLY) ? __builtin_amdgcn_exp2f(bL) : 1.0f;
@@ -805,7 +958,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
       for (int bb = 0; bb < G::BPW; ++bb) {
         const int b = wave + NW * bb;
-        if (b < G::NB) {
+        // (the per-channel decay's exact path has written P~ already)
+        if (b < G::NB && !XF) {
           const int I = block_i(b), J = block_j(b);
           f32x16 pacc;
 #pragma unroll
@@ -860,7 +1014,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       //      part[I] = S_part^T Q_part^T (transposed: lane = row, registers = values)
       // (per-channel decay: of diag(e^r) S against q~; the scaled state then
       // carries on into the update)
-      if constexpr (CHN) scale_rows(sER);
+      // (exact path: the unscaled state against q^ = phi(q) e^{b})
+      if constexpr (CHN && !XF) scale_rows(sER);
       pack_state();
       // normalised form, stripe 0: z of this wave's keys as the first row of
       // an A operand (every other row zero), in the key order of sbf
@@ -1001,6 +1156,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   }
 
   // ---- epilogue ---------------------------------------------------------
+  // (every thread's flag write came before a barrier of the last chunk)
+  if constexpr (CHN && !STATE_ONLY && !EXACT)
+    if (tid == 0) a.ws_flag[f] = sBad;
   if constexpr (STATE_ONLY) {
     if (copy_s0) {
 #pragma unroll
@@ -1046,11 +1204,15 @@ hipError_t launch_one(const ChunkArgs& a, bool state_only, hipStream_t s) {
   const int groups = (a.n_units + 7) / 8;
   const dim3 grid(groups * 8 * a.n_v), block(64 * NWV * KH);
   if constexpr (CAT == kCatChannel) {
-    if (a.norm) return hipErrorInvalidValue;
-    if (state_only)
+    if (a.norm || (!state_only && a.ws_flag == nullptr)) return hipErrorInvalidValue;
+    if (state_only) {
       hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, true, false>), grid, block, 0, s, a);
-    else
+    } else {
+      // the split pass flags the workgroups that met a chunk too strongly
+      // decayed for it; the exact pass recomputes those and exits elsewhere
       hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, false, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, false, false, true>), grid, block, 0, s, a);
+    }
   } else if (a.norm) {
     if (state_only)
       hipLaunchKernelGGL((chunk_stripe_kernel<DK, NWV, KH, C, CAT, true, true>), grid, block, 0, s, a);

@@ -38,11 +38,22 @@ __device__ __forceinline__ float feature_elu1_accurate(float x) {
   return x > 0.0f ? x + 1.0f : expf(x);
 }
 
+// Smallest per-token log decay the kernels work with: ln of the smallest
+// normal fp32 (2^-126).  A decay below it, -inf included, is taken as 2^-126:
+// every factor that contains it is then below the fp32 normal range, as the
+// true one is, and the in-chunk prefix sums stay finite (no inf - inf) and
+// small enough (|b| <= 126 C in log2 units) for their differences to keep
+// their precision.  NaN is kept.
+constexpr float kMinLogDecay = -87.33654475f;
+__device__ __forceinline__ float clamp_log_decay(float x) {
+  return x < kMinLogDecay ? kMinLogDecay : x;
+}
+
 // log a_t for the token-dependent decay kinds (0 for none).
 //   log:  the value itself;  gate: -softplus(g) = -(max(g,0) + log1p(e^-|g|)).
 __device__ __forceinline__ float token_log_decay(int kind, float x) {
-  if (kind == kDecayLog) return x;
-  if (kind == kDecayGate) return -(fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x))));
+  if (kind == kDecayLog) return clamp_log_decay(x);
+  if (kind == kDecayGate) return clamp_log_decay(-(fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)))));
   return 0.0f;
 }
 

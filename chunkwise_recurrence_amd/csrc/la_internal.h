@@ -33,6 +33,8 @@ struct ChunkArgs {
   float* ws_b;          // [B*H, L] in-chunk inclusive prefix of log a (token decays)
   float* zstate;        // normalised form: [B,H,DK] z in/out, or nullptr
   float* ws_z;          // normalised form: [B*H, P, DK] per-segment z increments
+  int* ws_flag;         // per-channel decay (stripe kernel): one flag per output-pass
+                        // workgroup, set when its segment needs the exact re-run
   int norm;             // 1: the normalised form
   int B, H, L, DK, DV, C;
   int P;                // sequence segments per head

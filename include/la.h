@@ -110,11 +110,14 @@ size_t la_chunk_fwd_workspace_bytes(int B, int H, int L, int d_k, int d_v, int C
  *                one chunk.  The requested C is honoured, never replaced.
  *   phi        : la_phi
  *   decay_kind : la_decay_kind; decay_data as described there (device, read).
- *                LA_DECAY_CHANNEL_LOG on bf16 inputs needs the log decay of
- *                every chunk, summed per channel, to be >= -150: the kernel
- *                splits each factor e^{b_i - b_j} around half the chunk's
- *                total, and both halves must stay in fp32 range (beyond that
- *                the results are inf or NaN; this is not checked).
+ *                Any log decay <= 0 is taken, -inf included (a = 0: the step
+ *                forgets).  LA_DECAY_CHANNEL_LOG on bf16 inputs: a chunk whose
+ *                decay sums below 2^-192 in some channel makes its workgroup's
+ *                segment be recomputed by an exact (slower) pass; the result
+ *                is the same either way.  The token kinds take a per-token
+ *                decay below 2^-126 (the smallest normal fp32) as 2^-126: any
+ *                factor containing it is below the fp32 normal range either
+ *                way.
  *   state      : float [B, H, d_k, d_v] (device) or NULL.  In: S_0; out: S_L.
  *                NULL means S_0 = 0 and the final state is dropped.
  *   out        : [B, H, L, d_v], same dtype as q (device, written)

@@ -61,7 +61,7 @@ def test_channel_fp32(gpu_lib, phi):
 @pytest.mark.parametrize("dk,dv,C", [(32, 32, 32), (64, 128, 64), (128, 64, 32), (32, 128, 128),
                                      (32, 64, 128), (64, 32, 64), (128, 32, 32), (128, 128, 32)])
 def test_channel_head_dims(gpu_lib, dk, dv, C):
-    # the mean keeps a chunk's summed log decay far inside the documented bound
+    # the mean keeps every chunk's summed log decay within the split's range
     c = W.RandomCase(1, 3, 200, dk, dv, torch.bfloat16, W.PHI_IDENTITY, W.DECAY_CHANNEL,
                      seed=dk + dv + C + 7, scale=1.0 / np.sqrt(dk), channel_mean=0.4,
                      with_state=True)
@@ -216,20 +216,121 @@ def test_channel_normalised_fp32(gpu_lib, phi):
     assert oracle.rel_err(_np(od), ro) <= 1e-4 and oracle.rel_err(_np(zd), rz) <= 1e-4
 
 
-def test_channel_strong_decay_near_the_documented_range(gpu_lib):
-    """log a = -2.2 for every token and channel: a 64-token chunk sums to
-    -140.8, inside the bf16 kernel's documented bound (>= -150 per chunk and
-    channel); the split factors reach e^{70} and must still give the oracle's
-    result.  Past the bound fp32 would overflow (documented, not tested)."""
+def _strong_log_decay(pattern, B, H, L, dk, seed):
+    """Per-channel log decays far past the split's range (a chunk's log2 decay
+    summing below -192 in some channel), for the exact re-run."""
+    g = torch.Generator().manual_seed(seed)
+    mild = -torch.empty((B, H, L, dk)).exponential_(1.0 / 0.05, generator=g)
+    if pattern == "uniform_2.2":       # every chunk: 64 x -2.2 = -140.8 (-203 in log2)
+        return torch.full((B, H, L, dk), -2.2)
+    if pattern == "uniform_16":        # every chunk sums to about -1e3
+        return torch.full((B, H, L, dk), -16.0)
+    if pattern == "forget_all":        # a = 0 everywhere: S_t = k_t v_t^T
+        return torch.full((B, H, L, dk), -float("inf"))
+    if pattern == "mixed":
+        # mild decays, with some channels of some chunks forgetting (-inf) or
+        # decaying by e^-1000 at single tokens, and whole strong chunks in one head
+        x = mild.clone()
+        sel = torch.rand((B, H, L, dk), generator=g)
+        x[sel < 0.004] = -float("inf")
+        x[(sel >= 0.004) & (sel < 0.008)] = -1000.0
+        x[:, -1, 64:128] = -3.0
+        return x
+    if pattern == "alternating":       # strong and mild chunks in turn
+        x = mild.clone()
+        for c0 in range(0, L, 128):
+            x[..., c0:c0 + 64, :] = -4.0
+        return x
+    raise ValueError(pattern)
+
+
+@pytest.mark.parametrize("pattern", ["uniform_2.2", "uniform_16", "forget_all", "mixed",
+                                     "alternating"])
+@pytest.mark.parametrize("plan", [(0, 0, 0, 0), (2, 128, 1, 2), (2, 128, 3, 2), (2, 64, 2, 2)])
+def test_channel_strong_decay_exact(gpu_lib, pattern, plan):
+    """bf16 per-channel gate at decays of any strength: chunks whose log2 decay
+    sums below -192 in some channel are recomputed by the exact pass (scores
+    per element with direct-sum exponents), the others keep the split; every
+    plan (one segment: the re-run reads a copy of S_0; several: the state
+    pass's exact update and the selected composition) gives the oracle's
+    result, and no inf or NaN appears."""
     la = gpu_lib
-    c = W.RandomCase(1, 2, 64 * 3 + 10, 128, 128, torch.bfloat16, W.PHI_IDENTITY,
-                     W.DECAY_CHANNEL, seed=520, scale=1.0 / np.sqrt(128), with_state=True)
+    B, H, L, d = 1, 3, 64 * 7 + 21, 128
+    c = W.RandomCase(B, H, L, d, d, torch.bfloat16, W.PHI_ELU1 if pattern == "mixed" else 0,
+                     W.DECAY_CHANNEL, seed=530 + len(pattern) + plan[2],
+                     scale=1.0 / np.sqrt(d), with_state=True)
     q, k, v, _, S0 = W.random_inputs(c)
-    decay = torch.full((1, 2, c.L, 128), -2.2)
+    decay = _strong_log_decay(pattern, B, H, L, d, seed=531)
+    print(f"[channel strong] pattern={pattern} plan={plan}", flush=True)
+    with la.using_plan(*plan):
+        S = S0.to(DEV).contiguous()
+        out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=64, phi=c.phi,
+                           decay_kind=W.DECAY_CHANNEL, decay=decay.to(DEV), state=S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(S).all()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), c.phi, W.DECAY_CHANNEL, _np(decay),
+                                  _np(S0))
+    e = (oracle.rel_err(_np(out), ref), oracle.rel_err(_np(S), ref_s))
+    print(f"[channel strong] pattern={pattern} plan={plan}: out/state rel err {e}", flush=True)
+    assert e[0] <= 1e-2 and e[1] <= 1e-2
+    if pattern == "forget_all":
+        # a closed form that needs no oracle: o_t = (phi(q_t) . phi(k_t)) v_t, S_L = k_L v_L^T
+        qd, kd, vd = _np(q), _np(k), _np(v)
+        closed = (qd * kd).sum(-1, keepdims=True) * vd
+        assert np.abs(_np(out) - closed).max() <= 1e-2 * np.abs(closed).max()
+        last = kd[:, :, -1, :, None] * vd[:, :, -1, None, :]
+        assert np.abs(_np(S) - last).max() <= 1e-2 * np.abs(last).max()
+
+
+@pytest.mark.parametrize("dk,dv,C", [(64, 64, 64), (128, 32, 32), (32, 128, 128), (64, 32, 64)])
+def test_channel_strong_decay_exact_head_dims(gpu_lib, dk, dv, C):
+    """The exact pass on the other layouts the per-channel gate takes."""
+    la = gpu_lib
+    B, H, L = 1, 2, 3 * C + 9
+    c = W.RandomCase(B, H, L, dk, dv, torch.bfloat16, W.PHI_IDENTITY, W.DECAY_CHANNEL,
+                     seed=560 + dk + dv + C, scale=1.0 / np.sqrt(dk), with_state=True)
+    q, k, v, _, S0 = W.random_inputs(c)
+    decay = _strong_log_decay("mixed", B, H, L, dk, seed=561)
+    decay[:, 0, C:2 * C] = -9.0
+    S = S0.to(DEV).contiguous()
+    out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=C, decay_kind=W.DECAY_CHANNEL,
+                       decay=decay.to(DEV), state=S)
+    torch.cuda.synchronize()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), 0, W.DECAY_CHANNEL, _np(decay), _np(S0))
+    e = (oracle.rel_err(_np(out), ref), oracle.rel_err(_np(S), ref_s))
+    print(f"[channel strong] dk={dk} dv={dv} C={C}: out/state rel err {e}", flush=True)
+    assert e[0] <= 1e-2 and e[1] <= 1e-2
+
+
+def test_channel_strong_decay_fp32_and_decode(gpu_lib):
+    """fp32 inputs and the decode step with forgetting channels (log a = -inf) and
+    e^-1000 steps: no NaN, the oracle's result (fp32 bar)."""
+    la = gpu_lib
+    B, H, L, d = 1, 2, 150, 32
+    c = W.RandomCase(B, H, L, d, d, torch.float32, W.PHI_IDENTITY, W.DECAY_CHANNEL, seed=570,
+                     with_state=True)
+    q, k, v, _, S0 = W.random_inputs(c)
+    decay = _strong_log_decay("mixed", B, H, L, d, seed=571)
     S = S0.to(DEV).contiguous()
     out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=64, decay_kind=W.DECAY_CHANNEL,
                        decay=decay.to(DEV), state=S)
     torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
     ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), 0, W.DECAY_CHANNEL, _np(decay), _np(S0))
-    assert oracle.rel_err(_np(out), ref) <= 1e-2 and oracle.rel_err(_np(S), ref_s) <= 1e-2
+    e = (oracle.rel_err(_np(out), ref), oracle.rel_err(_np(S), ref_s))
+    print(f"[channel strong] fp32: out/state rel err {e}", flush=True)
+    assert e[0] <= 1e-4 and e[1] <= 1e-4
+    # decode: three steps, the first forgetting every channel of head 0
+    Sd = S0.to(DEV).contiguous()
+    ref_S = _np(S0)
+    for t in range(3):
+        ld = decay[:, :, t].clone()
+        if t == 0:
+            ld[:, 0] = -float("inf")
+        o = la.decode_step(q[:, :, t].contiguous().to(DEV), k[:, :, t].contiguous().to(DEV),
+                           v[:, :, t].contiguous().to(DEV), Sd, decay_kind=W.DECAY_CHANNEL,
+                           decay=ld.to(DEV))
+        torch.cuda.synchronize()
+        ro, ref_S = oracle.decode_step(_np(q[:, :, t]), _np(k[:, :, t]), _np(v[:, :, t]), 0,
+                                       W.DECAY_CHANNEL, _np(ld), ref_S)
+        assert oracle.rel_err(_np(o), ro) <= 1e-4
+    assert oracle.rel_err(_np(Sd), ref_S) <= 1e-5
