@@ -583,11 +583,15 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 }
 
 // The sequential pass for bf16 inputs on v_mfma_f32_16x16x32_bf16: one
-// workgroup of 4 waves per (head, TV = 16 or 32 value columns), C = 64.  Wave w owns the
-// chunk's query rows 16w .. 16w + 15 and the state rows (keys) of 16-row
-// tiles w, w + 4, ...; the state tile lives in its fp32 accumulators, with a
-// bf16 copy S^T in LDS (double-buffered by chunk parity) as the B operand of
-// W S and Q S.  Per chunk:
+// workgroup of NG groups of 4 waves per (head, NG x TV value columns), C = 64;
+// group g takes value columns [TV g, TV g + TV) of the workgroup, and the
+// groups share the chunk's q, k, W and P tiles in LDS (one copy per compute
+// unit instead of one per group: those tiles are the same for every value
+// column of a head, and filling LDS with them is what a chunk waits for).
+// Wave w of a group owns the chunk's query rows 16w .. 16w + 15 and the state
+// rows (keys) of 16-row tiles w, w + 4, ...; the state tile lives in its fp32
+// accumulators, with a bf16 copy S^T in LDS (double-buffered by chunk parity)
+// as the B operand of W S and Q S.  Per chunk:
 //   (1) U = U0 - W S for the wave's rows -> U^T and (e^{b_last - b} U)^T in
 //       LDS (bf16); the chunk's masked, decayed scores P come ready from the
 //       solve pass (bf16 rows in the workspace), so no score products sit on
@@ -598,8 +602,8 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 //       LDS buffer.
 // The next chunk's q, k, W, P and U0 are loaded into registers while the
 // current one computes.
-template <int DK, int TV>
-__global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a) {
+template <int DK, int TV, int NG>
+__global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaArgs a) {
   constexpr int C = 64;
   constexpr int NT = TV / 16;       // 16-column tiles of the workgroup's value columns
   constexpr int QS = DK + 8;        // bf16 row stride of the Q, K, W tiles and of S^T
@@ -608,11 +612,15 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   constexpr int NMT = DK / 16;      // 16-row tiles of the state
   constexpr int MTW = (NMT + 3) / 4;
   constexpr int NCH = DK / 8;       // 16-byte pieces of one Q/K/W row
-  constexpr int PER = C * NCH / 256;
-  static_assert(PER >= 1 && C * NCH % 256 == 0, "tile pieces per thread");
-  constexpr int PPER = C * (C / 8) / 256;  // 16-byte pieces of the score tile per thread
+  constexpr int NT_ = 256 * NG;     // threads of the workgroup
+  constexpr int PER = C * NCH / NT_;
+  static_assert(PER >= 1 && C * NCH % NT_ == 0, "tile pieces per thread");
+  constexpr int PPER = C * (C / 8) / NT_;  // 16-byte pieces of the score tile per thread
+  static_assert(PPER >= 1 && C * (C / 8) % NT_ == 0, "score pieces per thread");
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave of the workgroup
+  const int grp = wg / 4;   // column group
+  const int w = wg % 4;     // wave of the group
   const int l16 = lane & 15, g4 = lane >> 4;
   // workgroup -> (head, value tile): the tiles of one head get workgroup ids
   // that are equal mod 8, so they run on one XCD and share q, k and W
@@ -624,16 +632,20 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   if (bh >= a.B * a.H) return;
   const int h = bh % a.H;
   const int L = a.L, DV = a.DV;
-  const int dv0 = vt * TV;
+  const int dv0 = (vt * NG + grp) * TV;
   const int nch = (L + C - 1) / C;
 
   __shared__ __align__(16) uint16_t sQ[C * QS], sK[C * QS], sW[C * QS];
-  __shared__ __align__(16) uint16_t sST[2][TV * QS];
-  __shared__ __align__(16) uint16_t sUT[TV * CS], sUwT[TV * CS], sP[C * CS];
+  __shared__ __align__(16) uint16_t sSTg[NG][2][TV * QS];
+  __shared__ __align__(16) uint16_t sUTg[NG][TV * CS], sUwTg[NG][TV * CS], sP[C * CS];
   __shared__ float sb[C];
   // U0 of the chunk, each lane's own elements (staged through LDS so that no
   // prefetched register has to be copied across the loop's back edge)
-  __shared__ float sU0[C * TV];
+  __shared__ float sU0g[NG][C * TV];
+  auto& sST = sSTg[grp];
+  uint16_t* sUT = sUTg[grp];
+  uint16_t* sUwT = sUwTg[grp];
+  float* sU0 = sU0g[grp];
 
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * L * DK;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
@@ -651,12 +663,12 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   const float lgh = a.decay_kind == kDecayHead ? logf(a.decay[h]) : 0.0f;
   auto fetch = [&](int c) {
     const int t0 = c * C, n = min(C, L - t0);
-    if (w == 0) rdec = tok ? (lane < n ? a.decay[(size_t)bh * L + t0 + lane] : 0.0f) : lgh;
+    if (wg == 0) rdec = tok ? (lane < n ? a.decay[(size_t)bh * L + t0 + lane] : 0.0f) : lgh;
     if (n == C) {
       // a whole chunk: no row checks
 #pragma unroll
       for (int p = 0; p < PER; ++p) {
-        const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
+        const int idx = tid + NT_ * p, row = idx / NCH, ch = idx % NCH;
         const size_t off = (size_t)(t0 + row) * DK + 8 * ch;
         rq[p] = *reinterpret_cast<const u32x4*>(qh + off);
         rk[p] = *reinterpret_cast<const u32x4*>(kh + off);
@@ -664,7 +676,7 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
       }
 #pragma unroll
       for (int p = 0; p < PPER; ++p) {
-        const int idx = tid + 256 * p, row = idx / (C / 8), ch = idx % (C / 8);
+        const int idx = tid + NT_ * p, row = idx / (C / 8), ch = idx % (C / 8);
         rp[p] = *reinterpret_cast<const u32x4*>(ph + (size_t)(t0 + row) * C + 8 * ch);
       }
 #pragma unroll
@@ -676,7 +688,7 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
     }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
+      const int idx = tid + NT_ * p, row = idx / NCH, ch = idx % NCH;
       if (row < n) {
         const size_t off = (size_t)(t0 + row) * DK + 8 * ch;
         rq[p] = *reinterpret_cast<const u32x4*>(qh + off);
@@ -690,7 +702,7 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
     }
 #pragma unroll
     for (int p = 0; p < PPER; ++p) {
-      const int idx = tid + 256 * p, row = idx / (C / 8), ch = idx % (C / 8);
+      const int idx = tid + NT_ * p, row = idx / (C / 8), ch = idx % (C / 8);
       rp[p] = row < n ? *reinterpret_cast<const u32x4*>(ph + (size_t)(t0 + row) * C + 8 * ch) : zero4;
     }
 #pragma unroll
@@ -736,17 +748,17 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
     lds_barrier();  // the previous chunk is done with every tile; S^T[sp] is complete
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
+      const int idx = tid + NT_ * p, row = idx / NCH, ch = idx % NCH;
       *reinterpret_cast<u32x4*>(&sQ[row * QS + 8 * ch]) = rq[p];
       *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = rk[p];
       *reinterpret_cast<u32x4*>(&sW[row * QS + 8 * ch]) = rw[p];
     }
 #pragma unroll
     for (int p = 0; p < PPER; ++p) {
-      const int idx = tid + 256 * p, row = idx / (C / 8), ch = idx % (C / 8);
+      const int idx = tid + NT_ * p, row = idx / (C / 8), ch = idx % (C / 8);
       *reinterpret_cast<u32x4*>(&sP[row * CS + 8 * ch]) = rp[p];
     }
-    if (w == 0) chunk_log_prefix_reg(a, rdec, n, sb);
+    if (wg == 0) chunk_log_prefix_reg(a, rdec, n, sb);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -862,6 +874,24 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   }
 }
 
+// The sequential MFMA pass: 32 value columns per workgroup; where 4-wave
+// 32-column workgroups would leave fewer than two per compute unit of an
+// MI355X (256 of them), 8-wave workgroups of two 16-column groups instead
+// (d_k >= 64: the tiles then still split evenly over the 512 threads).
+template <int D>
+void launch_chunk_mfma(const DeltaArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (D >= 64) {
+    if ((long long)a.B * a.H * a.n_v < 512) {
+      hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16, 2>), grid, dim3(512), 0, s, a);
+      return;
+    }
+  }
+  if (a.n_v == a.DV / 16)
+    hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16, 1>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 32, 1>), grid, dim3(256), 0, s, a);
+}
+
 template <bool BF16>
 hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
   const int nch = (a.L + a.C - 1) / a.C;
@@ -877,10 +907,7 @@ hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
       if (mfma) {                                                                 \
         hipLaunchKernelGGL((delta_prep_mfma_kernel<D>), gp, blk, 0, s, a);        \
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;        \
-        if (a.n_v == a.DV / 16)                                                   \
-          hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16>), gm, blk, 0, s, a); \
-        else                                                                      \
-          hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 32>), gm, blk, 0, s, a); \
+        launch_chunk_mfma<D>(a, gm, s);                                           \
         return hipGetLastError();                                                 \
       }                                                                           \
     }                                                                             \
@@ -902,9 +929,10 @@ hipError_t launch_dk(const DeltaArgs& a, hipStream_t s) {
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t s) {
   DeltaArgs b = a;
   int tv = a.DV < kDeltaTile ? a.DV : kDeltaTile;
-  // the MFMA pass: 16-column workgroups when 32-column ones would leave
-  // fewer than two per compute unit of an MI355X (256 of them)
-  if (delta_uses_mfma(a.dtype, a.C, a.DK, a.DV) && (long long)a.B * a.H * (a.DV / 32) < 512)
+  // the MFMA pass: 16-column 4-wave workgroups where d_k < 64 would leave
+  // fewer than two 32-column workgroups per compute unit (see launch_chunk_mfma)
+  if (delta_uses_mfma(a.dtype, a.C, a.DK, a.DV) && a.DK < 64 &&
+      (long long)a.B * a.H * (a.DV / 32) < 512)
     tv = 16;
   b.n_v = a.DV / tv;
   return a.dtype == kBF16 ? launch_dk<true>(b, s) : launch_dk<false>(b, s);
