@@ -141,9 +141,9 @@ def bench_chunk(la, torch, W, steps, warmup):
     torch.cuda.synchronize()
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
     by, flops = chunk_algorithmic(w, with_state=True)
-    kernel, tile, P, groups = la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)
+    kernel, tile, P, groups, split = la.plan(w.B, w.H, w.L, w.dk, w.dv, w.C)
     return dict(w=w, ms_step=ms_step, wall=wall, kern_ms=kern_ms, bytes=by, flops=flops,
-                kernel=kernel, tile=tile, P=P, groups=groups, need=need)
+                kernel=kernel, tile=tile, P=P, groups=groups, split=split, need=need)
 
 
 SCRUB_BYTES = 1 << 29  # a cold call is preceded by a 512 MiB write (the MALL holds 256 MB)

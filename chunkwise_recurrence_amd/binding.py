@@ -23,9 +23,14 @@ KERNEL_AUTO, KERNEL_STRIP, KERNEL_STRIPE, KERNEL_F32 = 0, 1, 2, 3
 
 
 class Plan(ctypes.Structure):
-    """la_plan: kernel, value columns per workgroup, segments, column groups."""
+    """la_plan: kernel, value columns per workgroup, segments, column groups, state-pass
+    workgroups per segment."""
     _fields_ = [("kernel", ctypes.c_int), ("dv_tile", ctypes.c_int),
-                ("segments", ctypes.c_int), ("groups", ctypes.c_int)]
+                ("segments", ctypes.c_int), ("groups", ctypes.c_int),
+                ("state_split", ctypes.c_int)]
+
+    def as_tuple(self):
+        return (self.kernel, self.dv_tile, self.segments, self.groups, self.state_split)
 
 # every symbol include/la.h declares
 EXPORTS = ("la_state_init", "la_chunk_fwd_workspace_bytes", "la_chunk_fwd", "la_decode_step",
@@ -180,16 +185,20 @@ def _request(plan_request):
     if r is None:
         return None
     if isinstance(r, Plan):
-        return Plan(r.kernel, r.dv_tile, r.segments, r.groups)
-    r = tuple(int(x) for x in r) + (0,) * (4 - len(r))
-    return Plan(*r[:4])
+        return Plan(*r.as_tuple())
+    r = tuple(int(x) for x in r)
+    if len(r) > 5:
+        raise ValueError("a plan request has at most 5 fields")
+    return Plan(*(r + (0,) * (5 - len(r))))
 
 
 @contextlib.contextmanager
-def using_plan(kernel: int = 0, dv_tile: int = 0, segments: int = 0, groups: int = 0):
+def using_plan(kernel: int = 0, dv_tile: int = 0, segments: int = 0, groups: int = 0,
+               state_split: int = 0):
     """Within the block, chunk_fwd and plan() request this launch plan (0 = automatic) unless
     given one explicitly.  Per thread / task: the library itself keeps no plan state."""
-    token = _PLAN_REQUEST.set((int(kernel), int(dv_tile), int(segments), int(groups)))
+    token = _PLAN_REQUEST.set((int(kernel), int(dv_tile), int(segments), int(groups),
+                               int(state_split)))
     try:
         yield
     finally:
@@ -206,9 +215,10 @@ def _resolve(B, H, L, dk, dv, C, dtype, decay_kind, normalize, plan_request):
 
 def plan(B: int, H: int, L: int, dk: int, dv: int, C: int, dtype: int = LA_BF16,
          decay_kind: int = DECAY_NONE, normalize: bool = False, request=None):
-    """(kernel, value columns per workgroup, segments per head, column groups) of the forward."""
+    """(kernel, value columns per workgroup, segments per head, column groups, state-pass
+    workgroups per segment) of the forward."""
     p, _ = _resolve(B, H, L, dk, dv, C, dtype, decay_kind, normalize, request)
-    return p.kernel, p.dv_tile, p.segments, p.groups
+    return p.as_tuple()
 
 
 def plan_workspace_bytes(B: int, H: int, L: int, dk: int, dv: int, C: int, dtype: int = LA_BF16,
@@ -253,7 +263,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, C: int = 64,
     `state` (fp32 [B,H,dk,dv]) is read as S_0 and overwritten with S_L when given.
     normalize: the normalised form (la_chunk_fwd_norm); `norm_state` (fp32
     [B,H,dk]) is read as z_0 and overwritten with z_L when given.
-    plan: a launch-plan request (kernel, dv_tile, segments, groups), 0 = automatic;
+    plan: a launch-plan request (kernel, dv_tile, segments, groups, state_split), 0 =
+    automatic (a shorter tuple leaves the remaining fields automatic);
     None takes the request of an enclosing `using_plan` block, if any.
     """
     dt = _qkv(q, k, v, 3)

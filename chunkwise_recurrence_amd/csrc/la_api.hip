@@ -82,6 +82,7 @@ struct Plan {
   int tv = 0;        // value columns per column group
   int P = 1;         // sequence segments per head
   int seg_chunks = 0;
+  int sub = 1;       // state-pass units per segment (a divisor of seg_chunks)
   size_t ws_bytes = 0;
   size_t ws_S_off = 0, ws_logA_off = 0, ws_b_off = 0, ws_z_off = 0;
   // copies of S_0 (segment split) and z_0 (normalised form, a head spread over
@@ -116,7 +117,7 @@ la_status check_request(const la_plan* r) {
     return LA_ERR_UNSUPPORTED;
   if (r->dv_tile != 0 && !dim_ok(r->dv_tile)) return LA_ERR_UNSUPPORTED;
   if (r->groups != 0 && r->groups != 1 && r->groups != 2) return LA_ERR_UNSUPPORTED;
-  if (r->segments < 0) return LA_ERR_SHAPE;
+  if (r->segments < 0 || r->state_split < 0) return LA_ERR_SHAPE;
   return LA_OK;
 }
 
@@ -204,14 +205,33 @@ Plan make_plan(int B, int H, int L, int d_k, int d_v, int C, int dtype, int deca
   if (P < 1) P = 1;
   p.seg_chunks = nchunks > 0 ? (nchunks + P - 1) / P : 0;
   p.P = p.seg_chunks > 0 ? (nchunks + p.seg_chunks - 1) / p.seg_chunks : 1;
+  if (p.P > 1) {
+    // The strip kernel's state pass (light workgroups, three per compute unit
+    // fit) is split until its grid covers the compute units, at most in four:
+    // elu_bf16's 192 state workgroups become 384, 17.0 -> 13.6 us on MI355X,
+    // the output pass unchanged (it composes twice as many increments; four
+    // splits cost it 2 us).  The stripe kernel's state pass measured no
+    // faster split (retnet_bf16 reads at the HBM rate already).
+    int sub = 1;
+    if (p.kernel == LA_KERNEL_STRIP) {
+      const long long state_wgs = (long long)heads * (d_v / p.tile) * (p.P - 1);
+      while (sub < 4 && state_wgs * sub < cus && p.seg_chunks % (2 * sub) == 0) sub *= 2;
+    }
+    if (req.state_split > 0) sub = req.state_split;
+    if (sub > p.seg_chunks) sub = p.seg_chunks;
+    while (p.seg_chunks % sub != 0) --sub;
+    p.sub = sub;
+  }
   size_t off = 0;
   if (p.P > 1) {
+    // one slot per state-pass unit: P * sub per head (the last segment's unused)
+    const size_t units = (size_t)heads * p.P * p.sub;
     p.ws_S_off = off;
-    off += round256((size_t)heads * p.P * d_k * d_v * sizeof(float));
-    p.ws_logA_off = off;  // one total per segment, or per segment and key channel
-    off += round256((size_t)heads * p.P * (chan ? d_k : 1) * sizeof(float));
-    p.ws_z_off = off;  // the normalised form's per-segment z increments
-    off += round256((size_t)heads * p.P * d_k * sizeof(float));
+    off += round256(units * d_k * d_v * sizeof(float));
+    p.ws_logA_off = off;  // one total per unit, or per unit and key channel
+    off += round256(units * (chan ? d_k : 1) * sizeof(float));
+    p.ws_z_off = off;  // the normalised form's z increments
+    off += round256(units * d_k * sizeof(float));
     p.copy_S0 = true;
     p.ws_S0_off = off;
     off += round256((size_t)heads * d_k * d_v * sizeof(float));
@@ -274,6 +294,7 @@ la_status la_chunk_fwd_plan(int B, int H, int L, int d_k, int d_v, int C, int dt
   plan->dv_tile = p.tile;
   plan->segments = p.P;
   plan->groups = p.ng;
+  plan->state_split = p.sub;
   if (workspace_bytes) *workspace_bytes = L > 0 ? p.ws_bytes : 0;
   return LA_OK;
 }
@@ -357,6 +378,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
   a.n_v = d_v / p.tile;
   a.P = p.P;
   a.seg_chunks = p.seg_chunks;
+  a.sub = p.sub;
   a.norm = norm ? 1 : 0;
   a.zstate = norm ? norm_state : nullptr;
   a.s0 = state;
@@ -397,7 +419,7 @@ la_status chunk_fwd_impl(const void* q, const void* k, const void* v, int dtype,
       // the state pass copies S_0 for the output pass, whose last segment
       // overwrites state with S_L
       a.ws_S0 = (p.copy_S0 && state) ? reinterpret_cast<float*>(ws + p.ws_S0_off) : nullptr;
-      a.n_units = B * H * (p.P - 1);
+      a.n_units = B * H * (p.P - 1) * p.sub;
       e = p.kernel == LA_KERNEL_STRIPE ? la::launch_chunk_stripe(a, /*state_only=*/true, s)
                                        : la::launch_chunk_bf16(a, /*state_only=*/true, s);
       if (e != hipSuccess) return LA_ERR_DEVICE;

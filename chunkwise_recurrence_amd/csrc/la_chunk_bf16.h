@@ -36,7 +36,12 @@
 //   * the state tile S[:, dv0:dv0+TV] lives in fp32 MFMA accumulators, split
 //     over the 4 waves by 16x16 tile; after each update a bf16 copy S^T is
 //     written to LDS (double-buffered) for the next chunk's inter-chunk term.
-//   * Q goes straight from HBM into the B-operand registers of its wave.
+//   * Q tiles take the same DMA route into LDS as K (one pipeline stage each)
+//     where the LDS holds them at the same pipeline depth: then the loop
+//     holds no register loads, whose completion the compiler would wait for
+//     by draining every outstanding memory operation (the previous chunk's
+//     output stores included) where they cross the loop's back edge.
+//     Geometries without room load Q from HBM into B-operand registers.
 //   * one workgroup barrier per chunk.
 //   * the workgroups of one (head, segment) that differ only in the value
 //     tile are numbered so that they land on one XCD and share Q and K
@@ -91,13 +96,16 @@ struct Geo {
   // loads in flight.
   static constexpr bool UNIFORM = NK_CHUNKS % (64 * NW) == 0 && NV_CHUNKS % (64 * NW) == 0 &&
                                   NSTRIP % 4 == 0 && C % NW == 0;
-  static constexpr size_t stage_bytes(int n) {
-    return (size_t)n * (2 * (size_t)K_TILE + 2 * (size_t)V_TILE + 4 * (size_t)CP) +
+  static constexpr size_t stage_bytes(int n, bool q) {
+    return (size_t)n * (2 * (size_t)K_TILE * (q ? 2 : 1) + 2 * (size_t)V_TILE + 4 * (size_t)CP) +
            2 * 2 * (size_t)S_TILE;
   }
   // pipeline depth: three stages (loads two chunks ahead) where they fit
-  static constexpr int NSTG = (UNIFORM && stage_bytes(3) + 256 <= 160 * 1024) ? 3 : 2;
-  static constexpr size_t LDS_MAIN = stage_bytes(NSTG) + 256;
+  static constexpr int NSTG = (UNIFORM && stage_bytes(3, false) + 256 <= 160 * 1024) ? 3 : 2;
+  // Q tiles copied into LDS with the K and V tiles where that keeps the
+  // pipeline depth; otherwise Q goes from HBM into registers.
+  static constexpr bool QL = NG == 2 && stage_bytes(NSTG, true) + 256 <= 160 * 1024;
+  static constexpr size_t LDS_MAIN = stage_bytes(NSTG, QL) + 256;
   // precomputed per-lane mask/decay weights only while they stay small
   static constexpr bool DM_REGS = NSTRIP <= 4;
   // operands of a whole strip preloaded (more ILP) only in the narrow layout
@@ -199,15 +207,21 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
   const int vt = slot % a.n_v;
   const int u = (slot / a.n_v) * 8 + (f & 7);
   if (u >= a.n_units) return;
-  const int segs = STATE_ONLY ? a.P - 1 : a.P;
+  // state pass: each of the first P - 1 segments in a.sub units of
+  // seg_chunks / a.sub chunks; output pass: one unit per segment, composing
+  // the sigma * a.sub state units before it
+  const int segs = STATE_ONLY ? (a.P - 1) * a.sub : a.P;
   const int bh = u / segs, sigma = u % segs;
+  const int span = STATE_ONLY ? a.seg_chunks / a.sub : a.seg_chunks;
+  const int nprev = STATE_ONLY ? 0 : sigma * a.sub;
+  const size_t unit0 = (size_t)bh * a.P * a.sub;  // this head's first state unit
   const int h = bh % a.H;
   const int dv0 = vt * G::TVW;             // first value column of the workgroup
   const int dvg = dv0 + grp * TV;          // ... of this wave's column group
   const int L = a.L, DV = a.DV;
   const int nchunks = (L + C - 1) / C;
-  const int c_begin = sigma * a.seg_chunks;
-  const int c_end = min(c_begin + a.seg_chunks, nchunks);
+  const int c_begin = sigma * span;
+  const int c_end = min(c_begin + span, nchunks);
   constexpr bool decayed = CAT != kCatNone;
   const bool elu = a.phi == kPhiElu1;
 
@@ -218,6 +232,9 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
   __shared__ __align__(16) char sK0[KB], sK1[KB], sK2[NS > 2 ? KB : 16];
   __shared__ __align__(16) char sV0[VB], sV1[VB], sV2[NS > 2 ? VB : 16];
   __shared__ __align__(16) float sB0[BB], sB1[BB], sB2[NS > 2 ? BB : 4];
+  constexpr bool QL = G::QL && !STATE_ONLY;
+  constexpr int QB = QL ? KB : 16;
+  __shared__ __align__(16) char sQ0[QB], sQ1[QB], sQ2[NS > 2 ? QB : 16];
   __shared__ __align__(16) char sST[2][STATE_ONLY ? 16 : G::S_TILE * 2];
   auto stage_k = [&](auto BUF) -> char* {
     constexpr int b = decltype(BUF)::value;
@@ -226,6 +243,10 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
   auto stage_v = [&](auto BUF) -> char* {
     constexpr int b = decltype(BUF)::value;
     if constexpr (b == 0) return sV0; else if constexpr (b == 1) return sV1; else return sV2;
+  };
+  auto stage_q = [&](auto BUF) -> char* {
+    constexpr int b = decltype(BUF)::value;
+    if constexpr (b == 0) return sQ0; else if constexpr (b == 1) return sQ1; else return sQ2;
   };
   auto stage_b = [&](auto BUF) -> float* {
     constexpr int b = decltype(BUF)::value;
@@ -290,11 +311,12 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
 #pragma unroll
   for (int t = 0; t < G::TPW; ++t) accS[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (!STATE_ONLY) {
-    // S_in = S_0 composed with the (decay, increment) pairs of the earlier
-    // segments, four segments at a time with every load of a batch issued
-    // before the first use (one wait for memory per batch).  Segments past
-    // sigma in the last batch re-read segment sigma - 1 and are weighted out;
-    // tiles past a wave's share read tile NT_S - 1 and are never stored.
+    // S_in = S_0 composed with the (decay, increment) pairs of the state
+    // units before this segment, four at a time with every load of a batch
+    // issued before the first use (one wait for memory per batch).  Units
+    // past the last one in the last batch re-read the last one and are
+    // weighted out; tiles past a wave's share read tile NT_S - 1 and are
+    // never stored.
     const int dv = dvg + 16 * nt_w + l16;
     auto idx_of = [&](int t, int i) {
       const int mt = min(wl + 4 * t, G::NT_S - 1) / G::NTV;
@@ -307,11 +329,11 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
         for (int i = 0; i < 4; ++i) accS[t][i] = a.s0[(size_t)bh * DK * DV + idx_of(t, i)];
     }
     constexpr int GS = 4;
-    for (int p0 = 0; p0 < sigma; p0 += GS) {
+    for (int p0 = 0; p0 < nprev; p0 += GS) {
       float inc[GS][G::TPW][4], lg[GS];
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
-        const size_t seg = (size_t)bh * a.P + min(p0 + g, sigma - 1);
+        const size_t seg = unit0 + min(p0 + g, nprev - 1);
         lg[g] = a.ws_logA[seg];
 #pragma unroll
         for (int t = 0; t < G::TPW; ++t)
@@ -320,9 +342,9 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
       }
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
-        // segments past sigma are left out by selection (a total decay of
-        // -inf times a 0 weight would give NaN)
-        const bool m = p0 + g < sigma;
+        // units past the last one are left out by selection (a total decay
+        // of -inf times a 0 weight would give NaN)
+        const bool m = p0 + g < nprev;
         const float e = exp2f(lg[g]);
 #pragma unroll
         for (int t = 0; t < G::TPW; ++t)
@@ -379,13 +401,14 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
     vrow[i] = r;
     voff[i] = r * DV + 8 * cc;
   }
-  // Q of each stage, in registers
-  u32x4 qst[NS][G::SPW][G::KSTEPS];
+  // Q of each stage, in registers (geometries without Q tiles in LDS)
+  u32x4 qst[QL ? 1 : NS][G::SPW][G::KSTEPS];
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
   // Vector memory instructions one chunk's loads and stores issue per wave
   // (meaningful when G::UNIFORM).
-  constexpr int LOADS = KBLK + VBLK + (CAT == kCatToken ? 1 : 0) + (STATE_ONLY ? 0 : G::SPW * G::KSTEPS);
+  constexpr int LOADS = KBLK + VBLK + (CAT == kCatToken ? 1 : 0) +
+                        (STATE_ONLY ? 0 : QL ? KBLK : G::SPW * G::KSTEPS);
   constexpr int STORES = STATE_ONLY ? 0 : G::SPW * G::NTV;
 
   auto issue_loads = [&](auto BUF, int c) {
@@ -393,15 +416,18 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
     const int t0 = c * C;
     const bool full = t0 + C <= L;
     const uint16_t* kc = kh + (size_t)t0 * DK;
+    const uint16_t* qc = qh + (size_t)t0 * DK;
     const uint16_t* vc = vh + (size_t)t0 * DV;
 #pragma unroll
     for (int i = 0; i < KBLK; ++i) {
       const int idx = wave + NW * i;
       const int q = 64 * idx + lane;
       if (64 * idx < G::NK_CHUNKS && q < G::NK_CHUNKS) {
-        // rows past the sequence re-read its last row; they are zeroed before use
+        // rows past the sequence re-read its last row; K rows are zeroed
+        // before use, Q rows only give outputs that are not stored
         const int off = full ? koff[i] : koff[i] - (max(krow[i] - (L - 1 - t0), 0)) * DK;
         dma16(kc + off, stage_k(BUF) + 1024 * idx);
+        if constexpr (QL) dma16(qc + off, stage_q(BUF) + 1024 * idx);
       }
     }
 #pragma unroll
@@ -421,7 +447,7 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
         dma4(bws + t, stage_b(BUF) + wave * PER);
       }
     }
-    if constexpr (!STATE_ONLY) {
+    if constexpr (!STATE_ONLY && !QL) {
 #pragma unroll
       for (int j = 0; j < G::SPW; ++j) {
         const int st = wl + 4 * j;
@@ -467,10 +493,10 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
     } else {
       wait_vmcnt<0>();
     }
-    // feature map on this wave's own copies of the chunk's key blocks, in
-    // place: they have landed (the wait above; a copy's lane l fills bytes
-    // 16l..16l+15 of its block) and no other wave reads them before the
-    // barrier below, which then also publishes the result
+    // feature map on this wave's own copies of the chunk's key (and query)
+    // blocks, in place: they have landed (the wait above; a copy's lane l
+    // fills bytes 16l..16l+15 of its block) and no other wave reads them
+    // before the barrier below, which then also publishes the result
     if (elu) {
 #pragma unroll
       for (int i = 0; i < KBLK; ++i) {
@@ -479,16 +505,34 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
         if (64 * idx < G::NK_CHUNKS && q < G::NK_CHUNKS) {
           u32x4* p = reinterpret_cast<u32x4*>(kb + 16 * q);
           *p = elu1_x8(*p);
+          if constexpr (QL) {
+            u32x4* pq = reinterpret_cast<u32x4*>(stage_q(BUF) + 16 * q);
+            *pq = elu1_x8(*pq);
+          }
         }
       }
     }
     lds_barrier();  // everybody's loads of chunk c landed; chunk c-1 is finished
     u32x4 qcur[G::SPW][G::KSTEPS];
     if constexpr (!STATE_ONLY) {
+      if constexpr (QL) {
+        // B operand of the scores: lane (l16, g4) holds query row 16 st + l16,
+        // key columns 32 s + 8 g4 .. +7
+        const char* qb = stage_q(BUF);
 #pragma unroll
-      for (int j = 0; j < G::SPW; ++j)
+        for (int j = 0; j < G::SPW; ++j) {
+          const int st = min(wl + 4 * j, G::NSTRIP - 1);
 #pragma unroll
-        for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = qst[buf][j][s];
+          for (int s = 0; s < G::KSTEPS; ++s)
+            qcur[j][s] = (DK >= 32 || g4 < 2) ? lds_b128(qb, swz<G::WCK>(16 * st + l16, 32 * s + 8 * g4))
+                                              : zero4;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < G::SPW; ++j)
+#pragma unroll
+          for (int s = 0; s < G::KSTEPS; ++s) qcur[j][s] = qst[buf][j][s];
+      }
       if (nvalid < C || DK < 32) {
         no_speculation();
 #pragma unroll
@@ -499,7 +543,7 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
             qcur[j][s] = ok ? qcur[j][s] : zero4;
           }
       }
-      if (elu) {
+      if (!QL && elu) {
         no_speculation();
 #pragma unroll
         for (int j = 0; j < G::SPW; ++j)
@@ -774,8 +818,8 @@ __global__ __launch_bounds__(256 * NG) void chunk_bf16_kernel(const ChunkArgs a)
   // ---- epilogue ---------------------------------------------------------
   float* dst = nullptr;
   if constexpr (STATE_ONLY) {
-    dst = a.ws_S + ((size_t)bh * a.P + sigma) * DK * DV;
-    if (vt == 0 && tid == 0) a.ws_logA[(size_t)bh * a.P + sigma] = logA;
+    dst = a.ws_S + (unit0 + sigma) * DK * DV;
+    if (vt == 0 && tid == 0) a.ws_logA[unit0 + sigma] = logA;
   } else {
     if (sigma == a.P - 1 && a.state != nullptr) dst = a.state + (size_t)bh * DK * DV;
   }

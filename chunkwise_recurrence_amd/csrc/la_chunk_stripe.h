@@ -360,16 +360,22 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   // the exact re-run recomputes only the workgroups the fast pass flagged
   if constexpr (EXACT)
     if (a.ws_flag[f] == 0) return;
-  const int segs = STATE_ONLY ? a.P - 1 : a.P;
+  // state pass: each of the first P - 1 segments in a.sub units of
+  // seg_chunks / a.sub chunks; output pass: one unit per segment, composing
+  // the sigma * a.sub state units before it
+  const int segs = STATE_ONLY ? (a.P - 1) * a.sub : a.P;
   const int bh = u / segs, sigma = u % segs;
+  const int span = STATE_ONLY ? a.seg_chunks / a.sub : a.seg_chunks;
+  const int nprev = STATE_ONLY ? 0 : sigma * a.sub;
+  const size_t unit0 = (size_t)bh * a.P * a.sub;  // this head's first state unit
   const int hd = bh % a.H;
   const int L = a.L, DV = a.DV;
   const int dv0 = vt * G::TVW;      // first value column of the workgroup
   const int cw = 32 * stripe;       // first column of this wave's stripe, in the tile
   const int mk0 = part * G::NMK_OWN;  // first 32-key state tile of this wave
   const int nchunks = (L + C - 1) / C;
-  const int c_begin = sigma * a.seg_chunks;
-  const int c_end = min(c_begin + a.seg_chunks, nchunks);
+  const int c_begin = sigma * span;
+  const int c_end = min(c_begin + span, nchunks);
   const bool elu = a.phi == kPhiElu1;
 
   __shared__ __align__(16) char sQ0[STATE_ONLY ? 16 : G::QK_BYTES], sQ1[STATE_ONLY ? 16 : G::QK_BYTES],
@@ -459,11 +465,11 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
     for (int r = 0; r < 16; ++r) accS[t][r] = 0.0f;
   if constexpr (!STATE_ONLY) {
-    // S_in = S_0 composed with the (decay, increment) pairs of the earlier
-    // segments, GS segments at a time with every load of a batch issued
-    // before the first use: one wait for memory per batch, not one per
-    // segment and state element.  Segments past sigma in the last batch
-    // re-read segment sigma - 1 and are weighted out (factor 1, increment 0).
+    // S_in = S_0 composed with the (decay, increment) pairs of the state
+    // units before this segment, GS at a time with every load of a batch
+    // issued before the first use: one wait for memory per batch, not one per
+    // unit and state element.  Units past the last one in the last batch
+    // re-read the last one and are weighted out (factor 1, increment 0).
     const int dv = dv0 + cw + l32;
     auto dk_of = [&](int t, int r) { return 32 * (mk0 + t) + 8 * (r >> 2) + 4 * h + (r & 3); };
     if (a.s0 != nullptr) {
@@ -473,11 +479,11 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         for (int r = 0; r < 16; ++r) accS[t][r] = a.s0[((size_t)bh * DK + dk_of(t, r)) * DV + dv];
     }
     constexpr int GS = CHN ? 2 : 4;
-    for (int p0 = 0; p0 < sigma; p0 += GS) {
+    for (int p0 = 0; p0 < nprev; p0 += GS) {
       float inc[GS][G::NMK_OWN][16], lg[GS][CHN ? G::NMK_OWN : 1][CHN ? 16 : 1];
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
-        const size_t seg = (size_t)bh * a.P + min(p0 + g, sigma - 1);
+        const size_t seg = unit0 + min(p0 + g, nprev - 1);
 #pragma unroll
         for (int t = 0; t < G::NMK_OWN; ++t)
 #pragma unroll
@@ -489,9 +495,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       }
 #pragma unroll
       for (int g = 0; g < GS; ++g) {
-        // segments past sigma are left out by selection (a total decay of
-        // -inf times a 0 weight would give NaN)
-        const bool m = p0 + g < sigma;
+        // units past the last one are left out by selection (a total decay
+        // of -inf times a 0 weight would give NaN)
+        const bool m = p0 + g < nprev;
 #pragma unroll
         for (int t = 0; t < G::NMK_OWN; ++t)
 #pragma unroll
@@ -530,16 +536,16 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       if constexpr (!STATE_ONLY) {
         // composed like S_in: four segments' loads per wait
         zv = a.z0 ? a.z0[(size_t)bh * DK + dk] : 0.0f;
-        for (int p0 = 0; p0 < sigma; p0 += 4) {
+        for (int p0 = 0; p0 < nprev; p0 += 4) {
           float zi[4], lz[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const size_t seg = (size_t)bh * a.P + min(p0 + g, sigma - 1);
+            const size_t seg = unit0 + min(p0 + g, nprev - 1);
             lz[g] = a.ws_logA[seg];
             zi[g] = a.ws_z[seg * DK + dk];
           }
 #pragma unroll
-          for (int g = 0; g < 4; ++g) zv = p0 + g < sigma ? exp2f(lz[g]) * zv + zi[g] : zv;
+          for (int g = 0; g < 4; ++g) zv = p0 + g < nprev ? exp2f(lz[g]) * zv + zi[g] : zv;
         }
       }
       zr[t] = zv;
@@ -1169,12 +1175,12 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   }
   float* dst = nullptr;
   if constexpr (STATE_ONLY) {
-    dst = a.ws_S + ((size_t)bh * a.P + sigma) * DK * DV;
+    dst = a.ws_S + (unit0 + sigma) * DK * DV;
     if constexpr (CHN) {
       if (vt == 0 && run == 0)
-        *reinterpret_cast<f32x2*>(&a.ws_logA[((size_t)bh * a.P + sigma) * DK + 2 * pr]) = logA2;
+        *reinterpret_cast<f32x2*>(&a.ws_logA[(unit0 + sigma) * DK + 2 * pr]) = logA2;
     } else {
-      if (vt == 0 && tid == 0) a.ws_logA[(size_t)bh * a.P + sigma] = logA;
+      if (vt == 0 && tid == 0) a.ws_logA[unit0 + sigma] = logA;
     }
   } else {
     if (sigma == a.P - 1 && a.state != nullptr) dst = a.state + (size_t)bh * DK * DV;
@@ -1189,7 +1195,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   }
   if constexpr (NORM) {
     float* zdst = nullptr;
-    if constexpr (STATE_ONLY) zdst = a.ws_z + ((size_t)bh * a.P + sigma) * DK;
+    if constexpr (STATE_ONLY) zdst = a.ws_z + (unit0 + sigma) * DK;
     else if (sigma == a.P - 1 && a.zstate != nullptr) zdst = a.zstate + (size_t)bh * DK;
     if (zdst != nullptr && stripe == 0 && h == 0 && vt == 0) {
 #pragma unroll

@@ -28,18 +28,20 @@ struct ChunkArgs {
   const float* z0;      // normalised form: [B,H,DK] or nullptr (z_0 = 0)
   float* ws_S0;         // state pass: where it copies S_0 (nullptr: no copy)
   const float* decay;   // nullptr | gamma[H] | [B,H,L] | [B,H,L,DK] (per channel)
-  float* ws_S;          // [B*H, P, DK, DV] per-segment state increments
-  float* ws_logA;       // [B*H, P] per-segment total log2 decay ([B*H, P, DK] per channel)
+  float* ws_S;          // [B*H, P*sub, DK, DV] state increments of the state-pass units
+  float* ws_logA;       // [B*H, P*sub] their total log2 decays ([B*H, P*sub, DK] per channel)
   float* ws_b;          // [B*H, L] in-chunk inclusive prefix of log a (token decays)
   float* zstate;        // normalised form: [B,H,DK] z in/out, or nullptr
-  float* ws_z;          // normalised form: [B*H, P, DK] per-segment z increments
+  float* ws_z;          // normalised form: [B*H, P*sub, DK] z increments of the state-pass units
   int* ws_flag;         // per-channel decay (stripe kernel): one flag per output-pass
                         // workgroup, set when its segment needs the exact re-run
   int norm;             // 1: the normalised form
   int B, H, L, DK, DV, C;
   int P;                // sequence segments per head
   int seg_chunks;       // chunks per segment (the last one may hold fewer)
-  int n_units;          // work units: B*H*P (main) or B*H*(P-1) (state pass)
+  int sub;              // state-pass units per segment (a divisor of seg_chunks; each
+                        // covers seg_chunks / sub chunks), composed like segments
+  int n_units;          // work units: B*H*P (main) or B*H*(P-1)*sub (state pass)
   int n_v;              // value tiles per head (one workgroup each)
   int tv;               // strip kernel: value columns per column group; stripe kernel: per workgroup
   int ng;               // strip kernel: column groups (of 4 waves) per workgroup;

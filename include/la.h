@@ -274,6 +274,11 @@ la_status la_chunk_fwd_noalloc(const void* q, const void* k, const void* v, int 
  *   groups    strip kernel: 4-wave column groups per workgroup (1 or 2);
  *             stripe kernel: waves per 32-column stripe, each holding a
  *             share of the keys of the state (1 or 2; 2 needs d_k >= 64)
+ *   state_split  state-pass workgroups per segment (segments > 1): each
+ *             takes an equal share of the segment's chunks, and the output
+ *             pass composes their (decay, increment) pairs like segments; a
+ *             divisor of the segment's chunk count (a request is reduced to
+ *             one), 1 with one segment
  * In a request, a field at 0 keeps the automatic choice.  The automatic plan
  * splits sequences into segments until the grid covers the current device's
  * compute units (queried once per device and cached; 256 when no device is
@@ -287,6 +292,7 @@ typedef struct {
   int dv_tile;
   int segments;
   int groups;
+  int state_split;
 } la_plan;
 
 enum { LA_KERNEL_AUTO = 0, LA_KERNEL_STRIP = 1, LA_KERNEL_STRIPE = 2, LA_KERNEL_F32 = 3 };

@@ -66,7 +66,7 @@ def test_zero_length_is_ok_without_touching_memory():
 
 def test_workspace_is_required_when_the_plan_splits_the_sequence():
     # 1 head of 64 x 64 over 64K tokens: the plan splits the sequence
-    kernel, tile, P, groups = la.plan(1, 1, 65536, 64, 64, 64)
+    kernel, tile, P, groups, _ = la.plan(1, 1, 65536, 64, 64, 64)
     assert P > 1
     need = la.chunk_fwd_workspace_bytes(1, 1, 65536, 64, 64, 64)
     assert need >= P * 64 * 64 * 4
@@ -98,25 +98,29 @@ def test_plans_of_the_workloads():
     # the stripe kernel: one workgroup per head (2 waves per 32 value columns)
     # and segment; segments bring the grid to 256 workgroups.  retnet: 64
     # heads x 4 segments
-    assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
+    assert la.plan(2, 32, 16384, 128, 128, 64)[:4] == (STRIPE, 128, 4, 2)
     # gated: 16 heads x 16 segments
-    assert la.plan(1, 16, 65536, 128, 128, 64) == (STRIPE, 128, 16, 2)
+    assert la.plan(1, 16, 65536, 128, 128, 64)[:4] == (STRIPE, 128, 16, 2)
     # narrower heads: the strip kernel.  64-wide value heads with d_k >= 64
     # take one 64-column tile in two groups; elu: 64 heads x 2 groups x 4
     # segments, the 512 4-wave units of 32-column tiles
-    assert la.plan(4, 16, 4096, 64, 64, 64) == (STRIP, 64, 4, 2)
-    assert la.plan(2, 32, 8192, 128, 64, 64) == (STRIP, 64, 4, 2)
+    assert la.plan(4, 16, 4096, 64, 64, 64)[:4] == (STRIP, 64, 4, 2)
+    # ... whose 192 state-pass workgroups (64 heads x 3 segments) are split in
+    # two to cover the 256 compute units; the stripe kernel's are not split
+    assert la.plan(4, 16, 4096, 64, 64, 64)[4] == 2
+    assert la.plan(2, 32, 16384, 128, 128, 64)[4] == 1
+    assert la.plan(2, 32, 8192, 128, 64, 64)[:4] == (STRIP, 64, 4, 2)
     # d_k = 32 keeps 32-column tiles in one group
-    assert la.plan(2, 32, 8192, 32, 64, 64) == (STRIP, 32, 4, 1)
-    assert la.plan(1, 1, 100, 16, 16, 16) == (STRIP, 16, 1, 1)
+    assert la.plan(2, 32, 8192, 32, 64, 64)[:4] == (STRIP, 32, 4, 1)
+    assert la.plan(1, 1, 100, 16, 16, 16)[:4] == (STRIP, 16, 1, 1)
     # 16-token chunks, d_k = 16: the strip kernel
     assert la.plan(1, 1, 100, 128, 128, 16)[0] == STRIP
     assert la.plan(1, 1, 100, 16, 128, 64)[0] == STRIP
     # 128-token chunks at d_k = 128 exceed the stripe kernel's LDS
-    assert la.plan(1, 1, 100, 128, 128, 128) == (STRIP, 32, 1, 1)
+    assert la.plan(1, 1, 100, 128, 128, 128)[:4] == (STRIP, 32, 1, 1)
     assert la.plan(1, 1, 100, 64, 128, 128)[0] == STRIPE
     # fp32: its own kernel, one segment, 16- or 32-wide tiles
-    assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32) == (F32, 16, 1, 1)
+    assert la.plan(1, 1, 300, 16, 16, 64, la.LA_F32)[:4] == (F32, 16, 1, 1)
     assert la.chunk_fwd_workspace_bytes(1, 1, 300, 16, 16, 64, la.LA_F32) == 0
     # fp32 with two 32-column value tiles: the normalised form reads z_0 from
     # a copy (the first tile's workgroup writes z_L back), 256 bytes rounded
@@ -127,20 +131,20 @@ def test_plans_of_the_workloads():
 def test_plan_requests_and_clamping():
     def got(req, *shape):
         return la.plan(*shape, request=req)
-    assert got((STRIP, 64, 3, 1), 1, 1, 64 * 30, 128, 128, 64) == (STRIP, 64, 3, 1)
+    assert got((STRIP, 64, 3, 1), 1, 1, 64 * 30, 128, 128, 64)[:4] == (STRIP, 64, 3, 1)
     # tile clamped to d_v, P to chunks
-    assert got((STRIP, 64, 3, 1), 1, 1, 64 * 2, 128, 32, 64) == (STRIP, 32, 2, 1)
+    assert got((STRIP, 64, 3, 1), 1, 1, 64 * 2, 128, 32, 64)[:4] == (STRIP, 32, 2, 1)
     assert got((STRIP, 32, 0, 2), 1, 1, 64 * 30, 128, 128, 64)[1::2] == (32, 2)
     # 8-column groups do not exist
     assert got((STRIP, 16, 0, 2), 1, 1, 64 * 30, 128, 128, 64)[1::2] == (16, 1)
-    assert got((STRIP, 64, 0, 2), 1, 1, 100, 64, 64, 64) == (STRIP, 64, 1, 2)
+    assert got((STRIP, 64, 0, 2), 1, 1, 100, 64, 64, 64)[:4] == (STRIP, 64, 1, 2)
     # two 64-column groups of d_k = 128 exceed the LDS: the tile is halved
     assert got((STRIP, 64, 0, 2), 1, 1, 100, 128, 128, 64)[1::2] == (64, 2)
-    assert got((STRIPE, 64, 2), 1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 64, 2, 2)
+    assert got((STRIPE, 64, 2), 1, 1, 64 * 30, 128, 128, 64)[:4] == (STRIPE, 64, 2, 2)
     # d_k = 32 keeps one wave per stripe
-    assert got((STRIPE,), 1, 1, 100, 32, 32, 64) == (STRIPE, 32, 1, 1)
+    assert got((STRIPE,), 1, 1, 100, 32, 32, 64)[:4] == (STRIPE, 32, 1, 1)
     assert got((STRIPE,), 1, 1, 100, 64, 64, 128)[0] == STRIPE
-    assert got((STRIPE, 128, 2, 1), 1, 1, 64 * 30, 128, 128, 64) == (STRIPE, 128, 2, 1)
+    assert got((STRIPE, 128, 2, 1), 1, 1, 64 * 30, 128, 128, 64)[:4] == (STRIPE, 128, 2, 1)
     # a stripe request the shape does not allow falls back to the strip kernel
     assert got((STRIPE, 128, 2, 1), 1, 1, 64 * 30, 16, 16, 64)[0] == STRIP
     for bad, code in (((STRIP, 48, 0), UNSUP), ((STRIP, 0, -1), SHAPE), ((STRIP, 0, 0, 3), UNSUP),
@@ -148,15 +152,30 @@ def test_plan_requests_and_clamping():
         with pytest.raises(la.LAError) as e:
             got(bad, 1, 1, 100, 64, 64, 64)
         assert e.value.status == code
+    # state-pass splits: reduced to a divisor of the segment's chunk count (24
+    # chunks in 3 segments of 8: 3 -> 2), and 1 without a state pass
+    L24 = 64 * 23 + 17
+    assert got((STRIP, 64, 3, 1, 3), 1, 1, L24, 128, 128, 64) == (STRIP, 64, 3, 1, 2)
+    assert got((STRIP, 64, 3, 1, 100), 1, 1, L24, 128, 128, 64)[4] == 8
+    assert got((STRIPE, 128, 1, 2, 4), 1, 1, L24, 128, 128, 64)[4] == 1
+    # one increment (and one decay total) per state-pass unit in the workspace
+    ws = {s: la.plan_workspace_bytes(1, 1, L24, 128, 128, 64, request=(STRIP, 64, 3, 1, s))
+          for s in (1, 2, 4)}
+    assert ws[2] - ws[1] >= 3 * 128 * 128 * 4 and ws[4] - ws[2] >= 6 * 128 * 128 * 4
+    with pytest.raises(la.LAError) as e:
+        got((STRIP, 0, 0, 0, -1), 1, 1, 100, 64, 64, 64)
+    assert e.value.status == SHAPE
+    with pytest.raises(ValueError):
+        got((STRIP, 0, 0, 0, 0, 0), 1, 1, 100, 64, 64, 64)
     # the request is per call: the automatic plan is untouched
-    assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
+    assert la.plan(2, 32, 16384, 128, 128, 64)[:4] == (STRIPE, 128, 4, 2)
     # within a using_plan block the binding passes the block's request
     with la.using_plan(STRIP, 32, 2, 1):
-        assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIP, 32, 2, 1)
+        assert la.plan(2, 32, 16384, 128, 128, 64)[:4] == (STRIP, 32, 2, 1)
         # the workspace query follows the request: two segments' states + the S_0 copy
         ws = la.plan_workspace_bytes(2, 32, 16384, 128, 128, 64)
         assert ws >= 64 * 2 * 128 * 128 * 4 + 64 * 128 * 128 * 4
-    assert la.plan(2, 32, 16384, 128, 128, 64) == (STRIPE, 128, 4, 2)
+    assert la.plan(2, 32, 16384, 128, 128, 64)[:4] == (STRIPE, 128, 4, 2)
 
 
 def test_plan_query_rejects():
@@ -277,7 +296,7 @@ def test_channel_decay_workspace_holds_per_channel_totals():
     # a split sequence keeps one log-decay total per segment, or d_k of them
     # for the per-channel decay (both plans: stripe kernel, same segments)
     B, H, L, d = 1, 1, 65536, 128
-    kernel, tile, P, groups = la.plan(B, H, L, d, d, 64)
+    kernel, tile, P, groups, _ = la.plan(B, H, L, d, d, 64)
     assert kernel == la.KERNEL_STRIPE and P > 1
     head = la.chunk_fwd_workspace_bytes(B, H, L, d, d, 64, la.LA_BF16, la.DECAY_HEAD)
     ch = la.chunk_fwd_workspace_bytes(B, H, L, d, d, 64, la.LA_BF16, la.DECAY_CHANNEL)

@@ -68,17 +68,20 @@ def test_channel_head_dims(gpu_lib, dk, dv, C):
     _run(gpu_lib, c, C, "head dims")
 
 
-@pytest.mark.parametrize("tile,segments,parts", [(128, 1, 2), (128, 3, 2), (128, 7, 1), (64, 5, 2),
-                                                 (64, 2, 2), (128, 21, 2)])
-def test_channel_plan_invariance(gpu_lib, tile, segments, parts):
-    """Value tiles, key parts and sequence segments (the segment scan composes
-    per-channel decays) all give the oracle's result."""
+@pytest.mark.parametrize("tile,segments,parts,split", [
+    (128, 1, 2, 0), (128, 3, 2, 0), (128, 7, 1, 0), (64, 5, 2, 0), (64, 2, 2, 0), (128, 21, 2, 0),
+    (128, 3, 2, 4), (64, 7, 2, 2), (128, 3, 1, 8)])
+def test_channel_plan_invariance(gpu_lib, tile, segments, parts, split):
+    """Value tiles, key parts, sequence segments and state-pass splits (the scans
+    compose per-channel decays) all give the oracle's result."""
     la = gpu_lib
-    with la.using_plan(la.KERNEL_STRIPE, tile, segments, parts):
+    with la.using_plan(la.KERNEL_STRIPE, tile, segments, parts, split):
+        if split:
+            assert la.plan(1, 2, 64 * 21 + 5, 128, 128, 64, decay_kind=4)[4] == split
         c = W.RandomCase(1, 2, 64 * 21 + 5, 128, 128, torch.bfloat16, W.PHI_IDENTITY,
-                         W.DECAY_CHANNEL, seed=460 + tile + segments + parts,
+                         W.DECAY_CHANNEL, seed=460 + tile + segments + parts + split,
                          scale=1.0 / np.sqrt(128), channel_mean=0.02, with_state=True)
-        _run(la, c, 64, f"plan tile={tile} P={segments} parts={parts}")
+        _run(la, c, 64, f"plan tile={tile} P={segments} parts={parts} split={split}")
 
 
 def test_channel_broadcast_equals_token_decay(gpu_lib):

@@ -73,16 +73,19 @@ def test_norm_head_dims(gpu_lib, dk, dv, C):
     _run(gpu_lib, c, C, "head dims")
 
 
-@pytest.mark.parametrize("tile,segments,parts", [(128, 1, 2), (128, 3, 2), (128, 7, 1), (64, 5, 2),
-                                                 (32, 4, 2), (128, 21, 2), (64, 1, 2), (32, 1, 1)])
-def test_norm_plan_invariance(gpu_lib, tile, segments, parts):
+@pytest.mark.parametrize("tile,segments,parts,split", [
+    (128, 1, 2, 0), (128, 3, 2, 0), (128, 7, 1, 0), (64, 5, 2, 0), (32, 4, 2, 0), (128, 21, 2, 0),
+    (64, 1, 2, 0), (32, 1, 1, 0), (128, 3, 2, 7), (64, 4, 2, 6), (128, 4, 1, 2)])
+def test_norm_plan_invariance(gpu_lib, tile, segments, parts, split):
     la = gpu_lib
-    with la.using_plan(la.KERNEL_STRIPE, tile, segments, parts):
+    with la.using_plan(la.KERNEL_STRIPE, tile, segments, parts, split):
+        if split:
+            assert la.plan(1, 2, 64 * 20 + 17, 128, 128, 64, normalize=True)[4] == split
         for kind in (W.DECAY_HEAD, W.DECAY_GATE, W.DECAY_NONE):
             c = W.RandomCase(1, 2, 64 * 20 + 17, 128, 128, torch.bfloat16, W.PHI_ELU1, kind,
-                             seed=tile + segments + kind, scale=1.0 / np.sqrt(128),
+                             seed=tile + segments + kind + split, scale=1.0 / np.sqrt(128),
                              gate_shift=-4.0, with_state=True)
-            _run(la, c, 64, f"plan tile={tile} P={segments} parts={parts}")
+            _run(la, c, 64, f"plan tile={tile} P={segments} parts={parts} split={split}")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])

@@ -127,6 +127,29 @@ def test_launch_plan_invariance(gpu_lib, kernel, tile, segments, groups):
                                    f"groups={groups}")
 
 
+@pytest.mark.parametrize("kernel,tile,segments,groups,split", [
+    (1, 32, 2, 1, 4), (1, 64, 3, 2, 8), (1, 64, 4, 2, 3), (1, 16, 3, 1, 2), (2, 128, 3, 2, 4),
+    (2, 64, 2, 1, 12), (2, 128, 5, 2, 5), (2, 128, 3, 2, 3)])
+def test_state_split_invariance(gpu_lib, kernel, tile, segments, groups, split):
+    """Splitting each segment's state pass over several workgroups (composed like
+    segments) changes the work split, not the result."""
+    la = gpu_lib
+    L = 64 * 23 + 17  # 24 chunks, the last one ragged
+    with la.using_plan(kernel, tile, segments, groups, split):
+        got = la.plan(1, 2, L, 128, 128, 64)
+        seg = -(-24 // segments)
+        assert got[:4] == (kernel, tile, -(-24 // seg), groups)
+        # a request is reduced to a divisor of the segment's chunk count
+        want = max(s for s in range(1, split + 1) if seg % s == 0)
+        assert got[4] == want and want > 1
+        for kind in (W.DECAY_NONE, W.DECAY_GATE, W.DECAY_HEAD):
+            c = W.RandomCase(1, 2, L, 128, 128, torch.bfloat16, 0, kind,
+                             seed=600 + tile + segments + split + kind,
+                             scale=1.0 / np.sqrt(128), gate_shift=-5.0, with_state=True)
+            _check_case(la, c, 64, f"plan kernel={kernel} tile={tile} P={segments} "
+                                   f"groups={groups} split={split}")
+
+
 def test_resume_equals_one_call(gpu_lib):
     """chunk_fwd(L1) then chunk_fwd(L2) from its state == chunk_fwd(L1 + L2)."""
     la = gpu_lib
