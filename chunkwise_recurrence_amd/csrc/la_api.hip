@@ -525,7 +525,8 @@ namespace {
 size_t delta_ws_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
   const size_t ht = (size_t)B * H * L;
   size_t by = round256(ht * d_k * sizeof(float)) + round256(ht * d_v * sizeof(float));
-  if (la::delta_uses_mfma(dtype, C, d_k, d_v)) by += round256(ht * la::kDeltaMaxC * 2);
+  if (la::delta_uses_mfma(dtype, C, d_k, d_v))
+    by += round256(ht * la::kDeltaMaxC * 2) + round256(ht * sizeof(float));
   return by;
 }
 
@@ -573,10 +574,12 @@ la_status la_delta_fwd(const void* q, const void* k, const void* v, const float*
   char* ws = static_cast<char*>(workspace);
   a.ws_W = reinterpret_cast<float*>(ws);
   a.ws_U = reinterpret_cast<float*>(ws + round256((size_t)B * H * L * d_k * sizeof(float)));
-  a.ws_P = la::delta_uses_mfma(dtype, C, d_k, d_v)
-               ? ws + round256((size_t)B * H * L * d_k * sizeof(float)) +
-                     round256((size_t)B * H * L * d_v * sizeof(float))
-               : nullptr;
+  if (la::delta_uses_mfma(dtype, C, d_k, d_v)) {
+    const size_t ht = (size_t)B * H * L;
+    char* p = ws + round256(ht * d_k * sizeof(float)) + round256(ht * d_v * sizeof(float));
+    a.ws_P = p;
+    a.ws_b = reinterpret_cast<float*>(p + round256(ht * la::kDeltaMaxC * 2));
+  }
   a.B = B;
   a.H = H;
   a.L = L;

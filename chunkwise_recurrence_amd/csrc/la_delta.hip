@@ -357,7 +357,9 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
 //     MFMAs, ~16 significant bits); W leaves as bf16, U0 as fp32.
 //   * the chunk's causal scores (q_i . k_j) e^{b_i - b_j} [j <= i] as bf16
 //     rows, computed here once per head and chunk instead of once per value
-//     tile in the sequential pass.
+//     tile in the sequential pass, and the in-chunk prefix b itself (fp32,
+//     log2 units): formed in the sequential pass, its gate logarithms and
+//     six-step scan sat on one wave before every chunk's second barrier.
 template <int DK>
 __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a) {
   constexpr int C = 64, QS = DK + 8, CS = C + 8, KST = DK / 32, NCH = DK / 8;
@@ -442,7 +444,12 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   if (n == C) stage(true);
   else stage(false);
   if (tid < C) sbeta[tid] = tid < n ? rbeta : 0.0f;
-  if (w == 0) chunk_log_prefix_reg(a, rdec, n, sb);  // log2 units
+  if (w == 0) {
+    chunk_log_prefix_reg(a, rdec, n, sb);  // log2 units
+    // for the sequential pass, which then has no prefix to form on its
+    // chunk-to-chunk critical path
+    if (lane < n) a.ws_b[rowk + lane] = sb[lane];
+  }
   for (int idx = tid; idx < C * C; idx += 256) sT[idx / C][idx % C] = 0.0f;
   lds_barrier();
 
@@ -600,7 +607,7 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 //       S = e^{b_last} S + K^T (e^{b_last - b} U), the K^T operand read from
 //       the row-major K tile with transpose reads; the new S^T to the other
 //       LDS buffer.
-// The next chunk's q, k, W, P and U0 are loaded into registers while the
+// The next chunk's q, k, W, P, U0 and b are loaded into registers while the
 // current one computes.
 template <int DK, int TV, int NG>
 __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaArgs a) {
@@ -658,12 +665,12 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
   u32x4 rq[PER], rk[PER], rw[PER], rp[PPER];
   float ru[NT][4];
-  float rdec = 0.0f;  // wave 0: the decay data of token t0 + lane
-  const bool tok = a.decay_kind == kDecayLog || a.decay_kind == kDecayGate;
-  const float lgh = a.decay_kind == kDecayHead ? logf(a.decay[h]) : 0.0f;
+  // wave 0: the prefix b of token t0 + lane from the solve pass (tokens past
+  // the sequence repeat the last one's)
+  float rb = 0.0f;
   auto fetch = [&](int c) {
     const int t0 = c * C, n = min(C, L - t0);
-    if (wg == 0) rdec = tok ? (lane < n ? a.decay[(size_t)bh * L + t0 + lane] : 0.0f) : lgh;
+    if (wg == 0) rb = a.ws_b[(size_t)bh * L + t0 + min(lane, n - 1)];
     if (n == C) {
       // a whole chunk: no row checks
 #pragma unroll
@@ -758,7 +765,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
       const int idx = tid + NT_ * p, row = idx / (C / 8), ch = idx % (C / 8);
       *reinterpret_cast<u32x4*>(&sP[row * CS + 8 * ch]) = rp[p];
     }
-    if (wg == 0) chunk_log_prefix_reg(a, rdec, n, sb);
+    if (wg == 0) sb[lane] = rb;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll

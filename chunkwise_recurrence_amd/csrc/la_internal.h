@@ -65,6 +65,8 @@ struct DeltaArgs {
   float* ws_U;          // [B*H, L, DV] U0 = T diag(beta) V per chunk
   void* ws_P;           // matrix-core path: [B*H, L, kDeltaMaxC] bf16 rows of each chunk's
                         // causal scores (q_i . k_j) e^{b_i - b_j} [j <= i]
+  float* ws_b;          // matrix-core path: [B*H, L] in-chunk inclusive prefix of log2 a,
+                        // written by the solve pass for the sequential pass
   int B, H, L, DK, DV, C;
   int decay_kind, dtype;
   int n_v;              // value tiles per head

@@ -331,9 +331,10 @@ def test_delta_zero_length_and_workspace_size():
     B, H, L, dk, dv = 2, 3, 100, 32, 64
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     # W, U0, and on the matrix-core path (bf16, 64-token chunks) the chunks'
-    # bf16 score rows
+    # bf16 score rows and the fp32 in-chunk decay prefix
     assert la.delta_fwd_workspace_bytes(B, H, L, dk, dv, 64, la.LA_BF16) == \
-        r256(B * H * L * dk * 4) + r256(B * H * L * dv * 4) + r256(B * H * L * 64 * 2)
+        r256(B * H * L * dk * 4) + r256(B * H * L * dv * 4) + r256(B * H * L * 64 * 2) + \
+        r256(B * H * L * 4)
     assert la.delta_fwd_workspace_bytes(B, H, L, dk, dv, 32, la.LA_BF16) == \
         r256(B * H * L * dk * 4) + r256(B * H * L * dv * 4)
     assert la.delta_fwd_workspace_bytes(B, H, L, dk, dv, 64, la.LA_F32) == \
