@@ -589,6 +589,47 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   }
 }
 
+// 16-byte-chunk XOR swizzle of a row-major bf16 tile with WC chunks per row
+// (no padding, so that one 64-lane tile copy fills 1 KB of consecutive LDS):
+// chunk p of row r holds the row's chunk p ^ ((r / R) mod WC), R the rows per
+// 256-byte bank line, so 16 consecutive rows read at one logical column land
+// in 16 distinct bank groups.  Byte offset of element (row, col).
+template <int WC>
+__device__ __forceinline__ int dswz(int row, int col) {
+  constexpr int R = WC >= 16 ? 1 : 16 / WC;
+  const int chunk = (col >> 3) ^ ((row / R) & (WC - 1));
+  return row * (WC * 16) + (chunk << 4) + ((col & 7) << 1);
+}
+// The 16-byte chunk of a tile copy's lane: slot q (row q / WC, LDS chunk
+// q mod WC) holds the row's chunk p ^ ((row / R) mod WC).
+template <int WC>
+__device__ __forceinline__ int dswz_src_chunk(int q) {
+  constexpr int R = WC >= 16 ? 1 : 16 / WC;
+  const int r = q / WC, p = q % WC;
+  return p ^ ((r / R) & (WC - 1));
+}
+// lds_tr8 on a swizzled tile of WC chunks per row
+template <int WC>
+__device__ __forceinline__ u32x4 lds_tr8s(const char* base, int k0, int col0, int l16) {
+  const int j = l16 >> 2, m = l16 & 3;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + dswz<WC>(k0 + j, col0 + 4 * m)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + dswz<WC>(k0 + 4 + j, col0 + 4 * m)));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+__device__ __forceinline__ u32x4 lds_b128(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+// s_waitcnt with only the vector-memory count set: at most N vector memory
+// instructions of this wave may be outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // The sequential pass for bf16 inputs on v_mfma_f32_16x16x32_bf16: one
 // workgroup of NG groups of 4 waves per (head, NG x TV value columns), C = 64;
 // group g takes value columns [TV g, TV g + TV) of the workgroup, and the
@@ -607,23 +648,39 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 //       S = e^{b_last} S + K^T (e^{b_last - b} U), the K^T operand read from
 //       the row-major K tile with transpose reads; the new S^T to the other
 //       LDS buffer.
-// The next chunk's q, k, W, P, U0 and b are loaded into registers while the
-// current one computes.
+// The chunk's q, k, W, P and U0 tiles and its decay prefix b (from the solve
+// pass) go from memory straight into LDS with global_load_lds (two stages:
+// the next chunk's copies fly while the current one computes).  The loop
+// then holds no register loads, whose completion the compiler would wait for
+// by draining every outstanding memory operation, the previous chunk's
+// output stores included; its one wait for memory counts instructions.  Rows
+// past a short last chunk are copies of its last row: they meet zero weights
+// in the state update and give outputs that are not stored.
 template <int DK, int TV, int NG>
 __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaArgs a) {
   constexpr int C = 64;
-  constexpr int NT = TV / 16;       // 16-column tiles of the workgroup's value columns
-  constexpr int QS = DK + 8;        // bf16 row stride of the Q, K, W tiles and of S^T
-  constexpr int CS = C + 8;         // bf16 row stride of K^T, P, U^T
+  constexpr int NT = TV / 16;       // 16-column tiles of a group's value columns
+  constexpr int QS = DK + 8;        // bf16 row stride of S^T
+  constexpr int CS = C + 8;         // bf16 row stride of U^T
   constexpr int KST = DK / 32;      // 32-wide k-steps over the keys
   constexpr int NMT = DK / 16;      // 16-row tiles of the state
   constexpr int MTW = (NMT + 3) / 4;
-  constexpr int NCH = DK / 8;       // 16-byte pieces of one Q/K/W row
-  constexpr int NT_ = 256 * NG;     // threads of the workgroup
-  constexpr int PER = C * NCH / NT_;
-  static_assert(PER >= 1 && C * NCH % NT_ == 0, "tile pieces per thread");
-  constexpr int PPER = C * (C / 8) / NT_;  // 16-byte pieces of the score tile per thread
-  static_assert(PPER >= 1 && C * (C / 8) % NT_ == 0, "score pieces per thread");
+  constexpr int NWV = 4 * NG;       // waves of the workgroup
+  constexpr int WCQ = DK / 8;       // 16-byte chunks of a q / k / W row
+  constexpr int WCP = C / 8;        // ... of a score row
+  constexpr int WCU = TV / 4;       // ... of a group's U0 row (fp32)
+  constexpr int QB = C * DK * 2, PB = C * C * 2, UB = C * TV * 4;  // tile bytes
+  // 1 KB tile copies (64 lanes x 16 bytes) per wave and chunk: equal for every
+  // wave, so the wait below can count them
+  constexpr int QPER = C * WCQ / 64 / NWV;
+  constexpr int PPER = C * WCP / 64 / NWV;
+  constexpr int UPER = C * WCU / 64 / 4;
+  constexpr int BPER = C / NWV;     // decay prefixes each wave copies
+  static_assert(QPER >= 1 && C * WCQ % (64 * NWV) == 0, "q/k/W copies per wave");
+  static_assert(PPER >= 1 && C * WCP % (64 * NWV) == 0, "score copies per wave");
+  static_assert(UPER >= 1 && C * WCU % 256 == 0, "U0 copies per wave");
+  // vector memory instructions of one chunk per wave: copies, then stores
+  constexpr int STORES = 4 * NT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave of the workgroup
   const int grp = wg / 4;   // column group
@@ -637,88 +694,72 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   const int vt = slot % a.n_v;
   const int bh = (slot / a.n_v) * 8 + (f & 7);
   if (bh >= a.B * a.H) return;
-  const int h = bh % a.H;
   const int L = a.L, DV = a.DV;
   const int dv0 = (vt * NG + grp) * TV;
   const int nch = (L + C - 1) / C;
 
-  __shared__ __align__(16) uint16_t sQ[C * QS], sK[C * QS], sW[C * QS];
+  __shared__ __align__(16) char sQ[2][QB], sK[2][QB], sW[2][QB], sP[2][PB];
+  __shared__ __align__(16) char sU0g[2][NG][UB];
+  __shared__ __align__(16) float sb[2][C];
   __shared__ __align__(16) uint16_t sSTg[NG][2][TV * QS];
-  __shared__ __align__(16) uint16_t sUTg[NG][TV * CS], sUwTg[NG][TV * CS], sP[C * CS];
-  __shared__ float sb[C];
-  // U0 of the chunk, each lane's own elements (staged through LDS so that no
-  // prefetched register has to be copied across the loop's back edge)
-  __shared__ float sU0g[NG][C * TV];
+  __shared__ __align__(16) uint16_t sUTg[NG][TV * CS], sUwTg[NG][TV * CS];
   auto& sST = sSTg[grp];
   uint16_t* sUT = sUTg[grp];
   uint16_t* sUwT = sUwTg[grp];
-  float* sU0 = sU0g[grp];
 
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * L * DK;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
   const uint16_t* wh = reinterpret_cast<const uint16_t*>(a.ws_W) + (size_t)bh * L * DK;
   const uint16_t* ph = static_cast<const uint16_t*>(a.ws_P) + (size_t)bh * L * C;
   const float* uh = a.ws_U + (size_t)bh * L * DV + dv0;
+  const float* bhp = a.ws_b + (size_t)bh * L;
   uint16_t* oh = static_cast<uint16_t*>(a.out) + (size_t)bh * L * DV + dv0;
 
-  // ---- register prefetch of one chunk: q, k, W rows and this lane's U0 ----
-  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  u32x4 rq[PER], rk[PER], rw[PER], rp[PPER];
-  float ru[NT][4];
-  // wave 0: the prefix b of token t0 + lane from the solve pass (tokens past
-  // the sequence repeat the last one's)
-  float rb = 0.0f;
-  auto fetch = [&](int c) {
-    const int t0 = c * C, n = min(C, L - t0);
-    if (wg == 0) rb = a.ws_b[(size_t)bh * L + t0 + min(lane, n - 1)];
-    if (n == C) {
-      // a whole chunk: no row checks
+  // per-lane sources of the tile copies, relative to the chunk's first row
+  int qrow[QPER], qoff[QPER], prow[PPER], poff[PPER], urow[UPER], uoff[UPER];
 #pragma unroll
-      for (int p = 0; p < PER; ++p) {
-        const int idx = tid + NT_ * p, row = idx / NCH, ch = idx % NCH;
-        const size_t off = (size_t)(t0 + row) * DK + 8 * ch;
-        rq[p] = *reinterpret_cast<const u32x4*>(qh + off);
-        rk[p] = *reinterpret_cast<const u32x4*>(kh + off);
-        rw[p] = *reinterpret_cast<const u32x4*>(wh + off);
-      }
+  for (int i = 0; i < QPER; ++i) {
+    const int q = 64 * (wg + NWV * i) + lane;
+    qrow[i] = q / WCQ;
+    qoff[i] = qrow[i] * DK + 8 * dswz_src_chunk<WCQ>(q);
+  }
 #pragma unroll
-      for (int p = 0; p < PPER; ++p) {
-        const int idx = tid + NT_ * p, row = idx / (C / 8), ch = idx % (C / 8);
-        rp[p] = *reinterpret_cast<const u32x4*>(ph + (size_t)(t0 + row) * C + 8 * ch);
-      }
+  for (int i = 0; i < PPER; ++i) {
+    const int q = 64 * (wg + NWV * i) + lane;
+    prow[i] = q / WCP;
+    poff[i] = prow[i] * C + 8 * dswz_src_chunk<WCP>(q);
+  }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+  for (int i = 0; i < UPER; ++i) {
+    const int q = 64 * (w + 4 * i) + lane;
+    urow[i] = q / WCU;
+    uoff[i] = urow[i] * DV + 4 * (q % WCU);
+  }
+  // copies of chunk c into stage st (rows past the sequence re-read its last row)
+  auto issue = [&](int c, int st) {
+    const int t0 = c * C, last = min(C, L - t0) - 1;
+    const bool whole = last == C - 1;
+    const size_t rq = (size_t)t0 * DK;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          ru[nt][r] = uh[(size_t)(t0 + 16 * w + 4 * g4 + r) * DV + 16 * nt + l16];
-      return;
+    for (int i = 0; i < QPER; ++i) {
+      const int off = whole ? qoff[i] : qoff[i] - max(qrow[i] - last, 0) * DK;
+      const int dst = 1024 * (wg + NWV * i);
+      dma16(qh + rq + off, sQ[st] + dst);
+      dma16(kh + rq + off, sK[st] + dst);
+      dma16(wh + rq + off, sW[st] + dst);
     }
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int idx = tid + NT_ * p, row = idx / NCH, ch = idx % NCH;
-      if (row < n) {
-        const size_t off = (size_t)(t0 + row) * DK + 8 * ch;
-        rq[p] = *reinterpret_cast<const u32x4*>(qh + off);
-        rk[p] = *reinterpret_cast<const u32x4*>(kh + off);
-        rw[p] = *reinterpret_cast<const u32x4*>(wh + off);
-      } else {
-        rq[p] = zero4;
-        rk[p] = zero4;
-        rw[p] = zero4;
-      }
+    for (int i = 0; i < PPER; ++i) {
+      const int off = whole ? poff[i] : poff[i] - max(prow[i] - last, 0) * C;
+      dma16(ph + (size_t)t0 * C + off, sP[st] + 1024 * (wg + NWV * i));
     }
 #pragma unroll
-    for (int p = 0; p < PPER; ++p) {
-      const int idx = tid + NT_ * p, row = idx / (C / 8), ch = idx % (C / 8);
-      rp[p] = row < n ? *reinterpret_cast<const u32x4*>(ph + (size_t)(t0 + row) * C + 8 * ch) : zero4;
+    for (int i = 0; i < UPER; ++i) {
+      const int off = whole ? uoff[i] : uoff[i] - max(urow[i] - last, 0) * DV;
+      dma16(uh + (size_t)t0 * DV + off, sU0g[st][grp] + 1024 * (w + 4 * i));
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * g4 + r;
-        ru[nt][r] = i < n ? uh[(size_t)(t0 + i) * DV + 16 * nt + l16] : 0.0f;
-      }
+    // lane l of wave wg: prefix wg * BPER + l (one instruction per wave)
+    if (lane < BPER) dma4(bhp + t0 + min(wg * BPER + lane, last), &sb[st][wg * BPER]);
   };
 
   // ---- the state: own tiles (mt = w + 4 m, nt), lane rows 16 mt + 4 g4 + r, column 16 nt + l16
@@ -747,32 +788,24 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
                              : 0.0f;
       }
   put_state(0);
-  if (nch > 0) fetch(0);
+  if (nch > 0) issue(0, 0);
 
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * C, n = min(C, L - t0);
-    const int sp = c & 1;
-    lds_barrier();  // the previous chunk is done with every tile; S^T[sp] is complete
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int idx = tid + NT_ * p, row = idx / NCH, ch = idx % NCH;
-      *reinterpret_cast<u32x4*>(&sQ[row * QS + 8 * ch]) = rq[p];
-      *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = rk[p];
-      *reinterpret_cast<u32x4*>(&sW[row * QS + 8 * ch]) = rw[p];
-    }
-#pragma unroll
-    for (int p = 0; p < PPER; ++p) {
-      const int idx = tid + NT_ * p, row = idx / (C / 8), ch = idx % (C / 8);
-      *reinterpret_cast<u32x4*>(&sP[row * CS + 8 * ch]) = rp[p];
-    }
-    if (wg == 0) sb[lane] = rb;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sU0[(16 * w + 4 * g4 + r) * TV + 16 * nt + l16] = ru[nt][r];
-    if (c + 1 < nch) fetch(c + 1);
-    lds_barrier();  // the chunk's tiles and prefixes are in LDS
-    const float bL = sb[n - 1];
+    const int sp = c & 1;  // tile stage and S^T buffer of this chunk
+    // this wave's copies of chunk c have landed: in issue order they are
+    // followed only by the previous chunk's output stores (a whole chunk)
+    if (c == 0) wait_vm<0>();
+    else wait_vm<STORES>();
+    lds_barrier();  // every wave's copies landed; the previous chunk is done; S^T[sp] complete
+    if (c + 1 < nch) issue(c + 1, sp ^ 1);
+    const char* cQ = sQ[sp];
+    const char* cK = sK[sp];
+    const char* cW = sW[sp];
+    const char* cP = sP[sp];
+    const float* sU0 = reinterpret_cast<const float*>(sU0g[sp][grp]);
+    const float* cb = sb[sp];
+    const float bL = cb[n - 1];
     const uint16_t* st = sST[sp];
 
     // (1a) U = U0 - W S for rows 16w .. 16w + 15
@@ -782,7 +815,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
       for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KST; ++s) {
-        const u32x4 aw = *reinterpret_cast<const u32x4*>(&sW[(16 * w + l16) * QS + 32 * s + 8 * g4]);
+        const u32x4 aw = lds_b128(cW, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
@@ -792,7 +825,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
       const int i0 = 16 * w + 4 * g4;
       float wt[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wt[r] = i0 + r < n ? ex2(bL - sb[i0 + r]) : 0.0f;
+      for (int r = 0; r < 4; ++r) wt[r] = i0 + r < n ? ex2(bL - cb[i0 + r]) : 0.0f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float u[4];
@@ -813,7 +846,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
       for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KST; ++s) {
-        const u32x4 aq = *reinterpret_cast<const u32x4*>(&sQ[(16 * w + l16) * QS + 32 * s + 8 * g4]);
+        const u32x4 aq = lds_b128(cQ, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
@@ -823,13 +856,13 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
       const int i0 = 16 * w + 4 * g4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = ex2(sb[i0 + r]);
+        const float e = ex2(cb[i0 + r]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
       }
       // token k-steps up to the diagonal: rows 16w .. need tokens < 16w + 16
       for (int s2 = 0; s2 <= w / 2; ++s2) {
-        const u32x4 ap = *reinterpret_cast<const u32x4*>(&sP[(16 * w + l16) * CS + 32 * s2 + 8 * g4]);
+        const u32x4 ap = lds_b128(cP, dswz<WCP>(16 * w + l16, 32 * s2 + 8 * g4));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
@@ -855,7 +888,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
             f32x4 acc = accS[m][nt] * eL;
 #pragma unroll
             for (int s2 = 0; s2 < C / 32; ++s2) {
-              const u32x4 ak = lds_tr8(sK, QS, 32 * s2 + 8 * g4, 16 * mt, l16);
+              const u32x4 ak = lds_tr8s<WCQ>(cK, 32 * s2 + 8 * g4, 16 * mt, l16);
               const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUwT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
               acc = mfma16x16x32(ak, bu, acc);
             }
