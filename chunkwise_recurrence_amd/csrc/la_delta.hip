@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
 //     T_IJ = -T_II sum_{J <= M < I} N_IM T_MJ.
 //   * W = (T diag(beta e^b)) K and U0 = (T diag(beta)) V on MFMA, with the
 //     fp32 left factor split into a bf16 high part and a bf16 remainder (two
-//     MFMAs, ~16 significant bits); W leaves as bf16, U0 as fp32.
+//     MFMAs, ~16 significant bits); W and U0 leave as bf16.
 //   * the chunk's causal scores (q_i . k_j) e^{b_i - b_j} [j <= i] as bf16
 //     rows, computed here once per head and chunk instead of once per value
 //     tile in the sequential pass, and the in-chunk prefix b itself (fp32,
@@ -444,53 +444,82 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   if (n == C) stage(true);
   else stage(false);
   if (tid < C) sbeta[tid] = tid < n ? rbeta : 0.0f;
+  for (int idx = tid; idx < C * C; idx += 256) sT[idx / C][idx % C] = 0.0f;
+  lds_barrier();  // the K tile is in LDS
+
+  // The chunk's 20 score tiles: N = K K^T below and on the diagonal (10
+  // tiles, operands from the K tile) and the causal scores P = K q (wave w:
+  // query rows 16w .. 16w + 15, key tiles 0..w, q in registers).  Their
+  // products need no decay factors, so they run before the barrier that
+  // publishes the prefix b, which wave 0 forms meanwhile: wave 0 takes only
+  // its one P tile, and the N tiles are dealt to waves 1-3 (4, 3, 3; with
+  // their 2, 3, 4 P tiles, 6, 6 and 7 tiles each).
+  // N tile t (row block, key block): nibble t of these, tiles in row-major
+  // order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ..
+  constexpr unsigned long long kNR = 0x3333222110ull, kNJ = 0x3210210100ull;
+  const int n_first = w == 0 ? 0 : w == 1 ? 0 : w == 2 ? 4 : 7;
+  const int n_count = w == 0 ? 0 : w == 1 ? 4 : 3;
+  f32x4 accN[4], accP[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    accN[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (u < n_count) {
+      const int R = (int)((kNR >> (4 * (n_first + u))) & 15), J = (int)((kNJ >> (4 * (n_first + u))) & 15);
+#pragma unroll
+      for (int s = 0; s < KST; ++s) {
+        const u32x4 ai = *reinterpret_cast<const u32x4*>(&sK[(16 * R + l16) * QS + 32 * s + 8 * g4]);
+        const u32x4 bj = *reinterpret_cast<const u32x4*>(&sK[(16 * J + l16) * QS + 32 * s + 8 * g4]);
+        accN[u] = mfma16x16x32(ai, bj, accN[u]);
+      }
+    }
+  }
+  const int i_q = iq;
+#pragma unroll
+  for (int jt = 0; jt < C / 16; ++jt) {
+    accP[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (jt <= w) {
+#pragma unroll
+      for (int s = 0; s < KST; ++s) {
+        const u32x4 ak = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
+        accP[jt] = mfma16x16x32(ak, i_q < n ? bq[s] : zero4, accP[jt]);
+      }
+    }
+  }
   if (w == 0) {
     chunk_log_prefix_reg(a, rdec, n, sb);  // log2 units
     // for the sequential pass, which then has no prefix to form on its
     // chunk-to-chunk critical path
     if (lane < n) a.ws_b[rowk + lane] = sb[lane];
   }
-  for (int idx = tid; idx < C * C; idx += 256) sT[idx / C][idx % C] = 0.0f;
-  lds_barrier();
+  lds_barrier();  // the prefix b is in LDS
 
-  // N: wave w, query rows 16w .. 16w + 15, key tiles jt <= w
-  for (int jt = 0; jt <= w; ++jt) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // N[i][j] = beta_i (k_i . k_j) e^{b_i - b_j} for j < i
 #pragma unroll
-    for (int s = 0; s < KST; ++s) {
-      const u32x4 ai = *reinterpret_cast<const u32x4*>(&sK[(16 * w + l16) * QS + 32 * s + 8 * g4]);
-      const u32x4 bj = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
-      acc = mfma16x16x32(ai, bj, acc);
-    }
-    const int j = 16 * jt + l16;
+  for (int u = 0; u < 4; ++u) {
+    if (u < n_count) {
+      const int R = (int)((kNR >> (4 * (n_first + u))) & 15), J = (int)((kNJ >> (4 * (n_first + u))) & 15);
+      const int j = 16 * J + l16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * w + 4 * g4 + r;
-      sN[i][j] = (j < i && i < n) ? sbeta[i] * acc[r] * ex2(sb[i] - sb[j]) : 0.0f;
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * R + 4 * g4 + r;
+        sN[i][j] = (j < i && i < n) ? sbeta[i] * accN[u][r] * ex2(sb[i] - sb[j]) : 0.0f;
+      }
     }
   }
-  // The chunk's causal scores P[i][j] = (q_i . k_j) e^{b_i - b_j} [j <= i] for
-  // the sequential pass, which then needs no score products of its own: wave
-  // w, query rows i = 16w .. 16w + 15 (q straight from memory as the B
-  // operand), every token column (zeros above the diagonal), bf16 rows.
+  // P rows for the sequential pass, which then needs no score products of its
+  // own: every token column (zeros above the diagonal), bf16
   {
-    const int i = iq;
+    const int i = i_q;
     uint16_t* po = static_cast<uint16_t*>(a.ws_P) + (rowk + i) * C;
 #pragma unroll
     for (int jt = 0; jt < C / 16; ++jt) {
+      // register r: token j = 16 jt + 4 g4 + r of query row i
       float pv[4] = {0.f, 0.f, 0.f, 0.f};
       if (jt <= w) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KST; ++s) {
-          const u32x4 ak = *reinterpret_cast<const u32x4*>(&sK[(16 * jt + l16) * QS + 32 * s + 8 * g4]);
-          acc = mfma16x16x32(ak, i < n ? bq[s] : zero4, acc);
-        }
-        // register r: token j = 16 jt + 4 g4 + r of query row i
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * jt + 4 * g4 + r;
-          pv[r] = j <= i ? acc[r] * ex2(sb[i] - sb[j]) : 0.0f;
+          pv[r] = j <= i ? accP[jt][r] * ex2(sb[i] - sb[j]) : 0.0f;
         }
       }
       if (i < n) *reinterpret_cast<uint2*>(po + 16 * jt + 4 * g4) = make_uint2(cvt2(pv[0], pv[1]), cvt2(pv[2], pv[3]));
@@ -570,8 +599,8 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   lds_barrier();
   split(false);
   lds_barrier();
-  // U0 = (T diag(beta)) V
-  float* uo = a.ws_U + rowk * DV;
+  // U0 = (T diag(beta)) V, bf16 like W
+  uint16_t* uo = reinterpret_cast<uint16_t*>(a.ws_U) + rowk * DV;
   for (int nt = 0; nt < DV / 16; ++nt) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -584,7 +613,7 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * w + 4 * g4 + r;
-      if (i < n) uo[(size_t)i * DV + 16 * nt + l16] = acc[r];
+      if (i < n) uo[(size_t)i * DV + 16 * nt + l16] = (uint16_t)(cvt2(acc[r], 0.0f) & 0xffffu);
     }
   }
 }
@@ -668,17 +697,19 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   constexpr int NWV = 4 * NG;       // waves of the workgroup
   constexpr int WCQ = DK / 8;       // 16-byte chunks of a q / k / W row
   constexpr int WCP = C / 8;        // ... of a score row
-  constexpr int WCU = TV / 4;       // ... of a group's U0 row (fp32)
-  constexpr int QB = C * DK * 2, PB = C * C * 2, UB = C * TV * 4;  // tile bytes
+  constexpr int WCU = TV / 8;       // ... of a group's U0 row
+  constexpr int QB = C * DK * 2, PB = C * C * 2, UB = C * TV * 2;  // tile bytes
   // 1 KB tile copies (64 lanes x 16 bytes) per wave and chunk: equal for every
   // wave, so the wait below can count them
   constexpr int QPER = C * WCQ / 64 / NWV;
   constexpr int PPER = C * WCP / 64 / NWV;
-  constexpr int UPER = C * WCU / 64 / 4;
+  // (a group's U0 tile is 2 or 4 KB: its first UBLK waves copy one block each;
+  // the wait counts only what a wave issues after its copies)
+  constexpr int UBLK = C * WCU / 64;
   constexpr int BPER = C / NWV;     // decay prefixes each wave copies
   static_assert(QPER >= 1 && C * WCQ % (64 * NWV) == 0, "q/k/W copies per wave");
   static_assert(PPER >= 1 && C * WCP % (64 * NWV) == 0, "score copies per wave");
-  static_assert(UPER >= 1 && C * WCU % 256 == 0, "U0 copies per wave");
+  static_assert(UBLK >= 1 && UBLK <= 4 && C * WCU % 64 == 0, "U0 copies of a group");
   // vector memory instructions of one chunk per wave: copies, then stores
   constexpr int STORES = 4 * NT;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -711,12 +742,12 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
   const uint16_t* wh = reinterpret_cast<const uint16_t*>(a.ws_W) + (size_t)bh * L * DK;
   const uint16_t* ph = static_cast<const uint16_t*>(a.ws_P) + (size_t)bh * L * C;
-  const float* uh = a.ws_U + (size_t)bh * L * DV + dv0;
+  const uint16_t* uh = reinterpret_cast<const uint16_t*>(a.ws_U) + (size_t)bh * L * DV + dv0;
   const float* bhp = a.ws_b + (size_t)bh * L;
   uint16_t* oh = static_cast<uint16_t*>(a.out) + (size_t)bh * L * DV + dv0;
 
   // per-lane sources of the tile copies, relative to the chunk's first row
-  int qrow[QPER], qoff[QPER], prow[PPER], poff[PPER], urow[UPER], uoff[UPER];
+  int qrow[QPER], qoff[QPER], prow[PPER], poff[PPER];
 #pragma unroll
   for (int i = 0; i < QPER; ++i) {
     const int q = 64 * (wg + NWV * i) + lane;
@@ -729,12 +760,8 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
     prow[i] = q / WCP;
     poff[i] = prow[i] * C + 8 * dswz_src_chunk<WCP>(q);
   }
-#pragma unroll
-  for (int i = 0; i < UPER; ++i) {
-    const int q = 64 * (w + 4 * i) + lane;
-    urow[i] = q / WCU;
-    uoff[i] = urow[i] * DV + 4 * (q % WCU);
-  }
+  const int urow = (64 * w + lane) / WCU;
+  const int uoff = urow * DV + 8 * ((64 * w + lane) % WCU);
   // copies of chunk c into stage st (rows past the sequence re-read its last row)
   auto issue = [&](int c, int st) {
     const int t0 = c * C, last = min(C, L - t0) - 1;
@@ -753,10 +780,9 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
       const int off = whole ? poff[i] : poff[i] - max(prow[i] - last, 0) * C;
       dma16(ph + (size_t)t0 * C + off, sP[st] + 1024 * (wg + NWV * i));
     }
-#pragma unroll
-    for (int i = 0; i < UPER; ++i) {
-      const int off = whole ? uoff[i] : uoff[i] - max(urow[i] - last, 0) * DV;
-      dma16(uh + (size_t)t0 * DV + off, sU0g[st][grp] + 1024 * (w + 4 * i));
+    if (w < UBLK) {
+      const int off = whole ? uoff : uoff - max(urow - last, 0) * DV;
+      dma16(uh + (size_t)t0 * DV + off, sU0g[st][grp] + 1024 * w);
     }
     // lane l of wave wg: prefix wg * BPER + l (one instruction per wave)
     if (lane < BPER) dma4(bhp + t0 + min(wg * BPER + lane, last), &sb[st][wg * BPER]);
@@ -803,7 +829,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
     const char* cK = sK[sp];
     const char* cW = sW[sp];
     const char* cP = sP[sp];
-    const float* sU0 = reinterpret_cast<const float*>(sU0g[sp][grp]);
+    const uint16_t* sU0 = reinterpret_cast<const uint16_t*>(sU0g[sp][grp]);
     const float* cb = sb[sp];
     const float bL = cb[n - 1];
     const uint16_t* st = sST[sp];
@@ -830,7 +856,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
       for (int nt = 0; nt < NT; ++nt) {
         float u[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = sU0[(i0 + r) * TV + 16 * nt + l16] - acc[nt][r];
+        for (int r = 0; r < 4; ++r) u[r] = bf16_to_f32(sU0[(i0 + r) * TV + 16 * nt + l16]) - acc[nt][r];
         const int o = (16 * nt + l16) * CS + i0;
         *reinterpret_cast<uint2*>(&sUT[o]) = make_uint2(cvt2(u[0], u[1]), cvt2(u[2], u[3]));
         *reinterpret_cast<uint2*>(&sUwT[o]) = make_uint2(cvt2(u[0] * wt[0], u[1] * wt[1]),

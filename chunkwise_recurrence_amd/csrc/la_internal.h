@@ -62,7 +62,8 @@ struct DeltaArgs {
   float* state;         // [B,H,DK,DV] or nullptr
   const float* decay;   // nullptr | gamma[H] | [B,H,L]
   float* ws_W;          // [B*H, L, DK] W = T diag(beta e^b) K per chunk
-  float* ws_U;          // [B*H, L, DV] U0 = T diag(beta) V per chunk
+  float* ws_U;          // [B*H, L, DV] U0 = T diag(beta) V per chunk (bf16 on the
+                        // matrix-core path, in the first half of the region)
   void* ws_P;           // matrix-core path: [B*H, L, kDeltaMaxC] bf16 rows of each chunk's
                         // causal scores (q_i . k_j) e^{b_i - b_j} [j <= i]
   float* ws_b;          // matrix-core path: [B*H, L] in-chunk inclusive prefix of log2 a,
