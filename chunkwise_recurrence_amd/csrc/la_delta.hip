@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
 //   * T = (I + N)^-1: wave w inverts diagonal block w by forward substitution
 //     with its 16 columns in registers (lane j holds column j, no barriers);
 //     the blocks below the diagonal follow block row by block row,
-//     T_IJ = -T_II sum_{J <= M < I} N_IM T_MJ.
+//     T_IJ = -T_II sum_{J <= M < I} N_IM T_MJ, on fp32 MFMA.
 //   * W = (T diag(beta e^b)) K and U0 = (T diag(beta)) V on MFMA, with the
 //     fp32 left factor split into a bf16 high part and a bf16 remainder (two
 //     MFMAs, ~16 significant bits); W and U0 leave as bf16.
@@ -541,24 +541,31 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
     for (int i = 0; i < 16; ++i) sT[q0 + i][q0 + j] = tc[i];
   }
   lds_barrier();
+  // The blocks below the diagonal, block row by block row, on
+  // v_mfma_f32_16x16x4_f32 (fp32 operands and sums, like the substitution):
+  // wave J of block row I forms X = sum_{J <= M < I} N_IM T_MJ, passes it
+  // through LDS (its rows become the k-runs of the next B operand) and writes
+  // T_IJ = -T_II X.  Operand lanes: A[l16][g4], B[g4][l16]; result rows
+  // 4 g4 .. 4 g4 + 3 of column l16.
   for (int I = 1; I < C / 16; ++I) {
-    // 16-term groups unrolled so that their LDS reads are in flight together
-    for (int idx = tid; idx < I * 256; idx += 256) {
-      const int J = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
-      float x = 0.0f;
-      for (int mb = 16 * J; mb < 16 * I; mb += 16) {
+    if (w < I) {
+      const int J = w;
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int M = J; M < I; ++M) {
 #pragma unroll
-        for (int mm = 0; mm < 16; ++mm) x = fmaf(sN[16 * I + r][mb + mm], sT[mb + mm][16 * J + cc], x);
+        for (int kk = 0; kk < 4; ++kk)
+          x = __builtin_amdgcn_mfma_f32_16x16x4f32(sN[16 * I + l16][16 * M + 4 * kk + g4],
+                                                    sT[16 * M + 4 * kk + g4][16 * J + l16], x, 0, 0, 0);
       }
-      sX[16 * J + r][cc] = x;
-    }
-    lds_barrier();
-    for (int idx = tid; idx < I * 256; idx += 256) {
-      const int J = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
-      float x = 0.0f;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) x = fmaf(sT[16 * I + r][16 * I + m], sX[16 * J + m][cc], x);
-      sT[16 * I + r][16 * J + cc] = -x;
+      for (int r = 0; r < 4; ++r) sX[16 * J + 4 * g4 + r][l16] = x[r];
+      f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[16 * I + l16][16 * I + 4 * kk + g4],
+                                                  sX[16 * J + 4 * kk + g4][l16], y, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sT[16 * I + 4 * g4 + r][16 * J + l16] = -y[r];
     }
     lds_barrier();
   }
