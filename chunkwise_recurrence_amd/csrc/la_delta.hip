@@ -586,42 +586,41 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   };
   split(true);
   lds_barrier();
-  // W = (T diag(beta e^b)) K: wave w, rows 16w .., every 16-column tile of the keys
+  // W = (T diag(beta e^b)) K: wave w, rows 16w .., every 16-column tile of the
+  // keys.  Formed transposed (K^T as the A operand): lane (l16, g4) then holds
+  // columns 4 g4 .. 4 g4 + 3 of row 16w + l16, one 8-byte store.
   uint16_t* wo = reinterpret_cast<uint16_t*>(a.ws_W) + rowk * DK;
+  const int io = 16 * w + l16;  // the row this lane stores
   for (int nt = 0; nt < DK / 16; ++nt) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < C / 32; ++s) {
-      const int ao = (16 * w + l16) * CS + 32 * s + 8 * g4;
-      const u32x4 bk = lds_tr8(sK, QS, 32 * s + 8 * g4, 16 * nt, l16);
-      acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(&sTh[ao]), bk, acc);
-      acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(&sTl[ao]), bk, acc);
+      const int ao = io * CS + 32 * s + 8 * g4;
+      const u32x4 ak = lds_tr8(sK, QS, 32 * s + 8 * g4, 16 * nt, l16);
+      acc = mfma16x16x32(ak, *reinterpret_cast<const u32x4*>(&sTh[ao]), acc);
+      acc = mfma16x16x32(ak, *reinterpret_cast<const u32x4*>(&sTl[ao]), acc);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * w + 4 * g4 + r;
-      if (i < n) wo[(size_t)i * DK + 16 * nt + l16] = (uint16_t)(cvt2(acc[r], 0.0f) & 0xffffu);
-    }
+    if (io < n)
+      *reinterpret_cast<uint2*>(wo + (size_t)io * DK + 16 * nt + 4 * g4) =
+          make_uint2(cvt2(acc[0], acc[1]), cvt2(acc[2], acc[3]));
   }
   lds_barrier();
   split(false);
   lds_barrier();
-  // U0 = (T diag(beta)) V, bf16 like W
+  // U0 = (T diag(beta)) V, bf16 like W and formed transposed the same way
   uint16_t* uo = reinterpret_cast<uint16_t*>(a.ws_U) + rowk * DV;
   for (int nt = 0; nt < DV / 16; ++nt) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < C / 32; ++s) {
-      const int ao = (16 * w + l16) * CS + 32 * s + 8 * g4;
-      const u32x4 bv = lds_tr8(sV, VS, 32 * s + 8 * g4, 16 * nt, l16);
-      acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(&sTh[ao]), bv, acc);
-      acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(&sTl[ao]), bv, acc);
+      const int ao = io * CS + 32 * s + 8 * g4;
+      const u32x4 av = lds_tr8(sV, VS, 32 * s + 8 * g4, 16 * nt, l16);
+      acc = mfma16x16x32(av, *reinterpret_cast<const u32x4*>(&sTh[ao]), acc);
+      acc = mfma16x16x32(av, *reinterpret_cast<const u32x4*>(&sTl[ao]), acc);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * w + 4 * g4 + r;
-      if (i < n) uo[(size_t)i * DV + 16 * nt + l16] = (uint16_t)(cvt2(acc[r], 0.0f) & 0xffffu);
-    }
+    if (io < n)
+      *reinterpret_cast<uint2*>(uo + (size_t)io * DV + 16 * nt + 4 * g4) =
+          make_uint2(cvt2(acc[0], acc[1]), cvt2(acc[2], acc[3]));
   }
 }
 
