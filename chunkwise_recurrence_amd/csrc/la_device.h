@@ -30,8 +30,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // phi(x) = elu(x) + 1 (alpha = 1): x + 1 for x > 0, e^x otherwise.
+// phi = elu + 1 as max(x + 1, e^{-|x|}): since e^x >= 1 + x, the maximum is
+// x + 1 for x > 0 (where e^{-x} < 1 < x + 1) and e^x for x <= 0.  Four VALU
+// instructions per value (the -|.| is a source modifier of v_exp_f32), no
+// compare and select; the same bf16 result as the branch form for every
+// bf16 input.
 __device__ __forceinline__ float feature_elu1(float x) {
-  return x > 0.0f ? x + 1.0f : __expf(x);
+  return fmaxf(x + 1.0f, __builtin_amdgcn_exp2f(-fabsf(x * 1.4426950408889634f)));
 }
 
 __device__ __forceinline__ float feature_elu1_accurate(float x) {
