@@ -556,6 +556,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   // bf16 A operands of the inter-chunk term: own key step s (global step
   // part * NKS_OWN + s) uses own tile s / 2, registers 8 (s % 2) .. +7
   u32x4 sbf[G::NKS_OWN];
+  // normalised form: the stripe that forms row block I's phi(q).z partials
+  // (never stripe 0 when there are others)
+  auto dz_stripe = [](int I) { return NWV == 1 ? 0 : 1 + I % (NWV - 1); };
   auto pack_state = [&]() {
 #pragma unroll
     for (int s = 0; s < G::NKS_OWN; ++s)
@@ -1023,31 +1026,19 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
       // (exact path: the unscaled state against q^ = phi(q) e^{b})
       if constexpr (CHN && !XF) scale_rows(sER);
       pack_state();
-      // normalised form, stripe 0: z of this wave's keys as the first row of
-      // an A operand (every other row zero), in the key order of sbf
-      u32x4 zA[NORM ? G::NKS_OWN : 1];
-      if constexpr (NORM) {
-        const float* zc = sZ[it & 1];
-#pragma unroll
-        for (int s = 0; s < G::NKS_OWN; ++s) {
-          const int sg = part * G::NKS_OWN + s;
-          const f32x4 z0 = *reinterpret_cast<const f32x4*>(&zc[16 * sg + 4 * h]);
-          const f32x4 z1 = *reinterpret_cast<const f32x4*>(&zc[16 * sg + 8 + 4 * h]);
-          const u32x4 w = u32x4{cvt2(z0[0], z0[1]), cvt2(z0[2], z0[3]), cvt2(z1[0], z1[1]),
-                                cvt2(z1[2], z1[3])};
-          zA[s] = l32 == 0 ? w : zero4;
-        }
-      }
+      // normalised form: row i's phi(q_i).z over this wave's keys, from the
+      // same q pairs as the inter term's operand (lane (i, h) holds 8 of each
+      // 16-key step's keys) against z rounded to bf16 pairs, two keys per
+      // v_dot2_f32_bf16, the two lane halves then summed.  Row block I's goes
+      // to stripe dz_stripe(I), so that stripe 0, which carries the z sums of
+      // the state update, takes none of it.
+      const float* zc = sZ[it & 1];
       f32x16 pin[G::NRB];
 #pragma unroll
       for (int I = 0; I < G::NRB; ++I) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) pin[I][r] = 0.0f;
-        f32x16 dacc;
-        if constexpr (NORM) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dacc[r] = 0.0f;
-        }
+        float dz = 0.0f;
         const int i = 32 * I + l32;
 #pragma unroll
         for (int s = 0; s < G::NKS_OWN; ++s) {
@@ -1056,12 +1047,23 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
           const u32x2 hi = lds_b64(qb, swz<G::WCK>(i, 16 * sg + 8 + 4 * h));
           const u32x4 qop = u32x4{lo[0], lo[1], hi[0], hi[1]};
           pin[I] = mfma32(sbf[s], qop, pin[I]);
-          if constexpr (NORM)
-            if (stripe == 0) dacc = mfma32(zA[s], qop, dacc);
+          if constexpr (NORM) {
+            if (stripe == dz_stripe(I)) {
+              const f32x4 z0 = *reinterpret_cast<const f32x4*>(&zc[16 * sg + 4 * h]);
+              const f32x4 z1 = *reinterpret_cast<const f32x4*>(&zc[16 * sg + 8 + 4 * h]);
+              dz = dot2_bf16(qop[0], cvt2(z0[0], z0[1]), dz);
+              dz = dot2_bf16(qop[1], cvt2(z0[2], z0[3]), dz);
+              dz = dot2_bf16(qop[2], cvt2(z1[0], z1[1]), dz);
+              dz = dot2_bf16(qop[3], cvt2(z1[2], z1[3]), dz);
+            }
+          }
         }
-        // row i's partial phi(q_i).z over this wave's keys sits in register 0 of lane (i, h = 0)
-        if constexpr (NORM)
-          if (stripe == 0 && h == 0) sDen[part][i] = dacc[0];
+        if constexpr (NORM) {
+          if (stripe == dz_stripe(I)) {
+            dz += __shfl_xor(dz, 32);
+            if (h == 0) sDen[part][i] = dz;
+          }
+        }
       }
       // row block I belongs to key part I % KH; the other parts hand it their partial
       if constexpr (KH > 1) {
