@@ -840,18 +840,26 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
     const float bL = cb[n - 1];
     const uint16_t* st = sST[sp];
 
-    // (1a) U = U0 - W S for rows 16w .. 16w + 15
+    // (1a) U = U0 - W S for rows 16w .. 16w + 15, and with it (sharing the S
+    // operand reads, ahead of the barrier the rest of O waits behind) the
+    // part of O that does not wait for U, Q S for the same rows
+    f32x4 accO[NT];
     {
       f32x4 acc[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accO[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int s = 0; s < KST; ++s) {
         const u32x4 aw = lds_b128(cW, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
+        const u32x4 aq = lds_b128(cQ, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
           acc[nt] = mfma16x16x32(aw, bs, acc[nt]);
+          accO[nt] = mfma16x16x32(aq, bs, accO[nt]);
         }
       }
       const int i0 = 16 * w + 4 * g4;
@@ -875,16 +883,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
     {
       f32x4 acc[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KST; ++s) {
-        const u32x4 aq = lds_b128(cQ, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
-          acc[nt] = mfma16x16x32(aq, bs, acc[nt]);
-        }
-      }
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = accO[nt];
       const int i0 = 16 * w + 4 * g4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
