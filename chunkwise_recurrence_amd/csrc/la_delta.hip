@@ -717,7 +717,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   static_assert(PPER >= 1 && C * WCP % (64 * NWV) == 0, "score copies per wave");
   static_assert(UBLK >= 1 && UBLK <= 4 && C * WCU % 64 == 0, "U0 copies of a group");
   // vector memory instructions of one chunk per wave: copies, then stores
-  constexpr int STORES = 4 * NT;
+  constexpr int STORES = NT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave of the workgroup
   const int grp = wg / 4;   // column group
@@ -842,7 +842,9 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
 
     // (1a) U = U0 - W S for rows 16w .. 16w + 15, and with it (sharing the S
     // operand reads, ahead of the barrier the rest of O waits behind) the
-    // part of O that does not wait for U, Q S for the same rows
+    // part of O that does not wait for U, Q S for the same rows.  O is formed
+    // transposed (S^T, U^T rows as the A operand): lane (l16, g4) then holds
+    // value columns 4 g4 .. 4 g4 + 3 of token 16w + l16, one 8-byte store.
     f32x4 accO[NT];
     {
       f32x4 acc[NT];
@@ -859,7 +861,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
         for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
           acc[nt] = mfma16x16x32(aw, bs, acc[nt]);
-          accO[nt] = mfma16x16x32(aq, bs, accO[nt]);
+          accO[nt] = mfma16x16x32(bs, aq, accO[nt]);
         }
       }
       const int i0 = 16 * w + 4 * g4;
@@ -881,31 +883,26 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
 
     // (2a) O = diag(e^b) Q S + P U for rows 16w .. 16w + 15
     {
+      const int io = 16 * w + l16;  // this lane's token
+      const float e = ex2(cb[io]);
       f32x4 acc[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = accO[nt];
-      const int i0 = 16 * w + 4 * g4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = ex2(cb[i0 + r]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
-      }
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = accO[nt] * e;
       // token k-steps up to the diagonal: rows 16w .. need tokens < 16w + 16
       for (int s2 = 0; s2 <= w / 2; ++s2) {
-        const u32x4 ap = lds_b128(cP, dswz<WCP>(16 * w + l16, 32 * s2 + 8 * g4));
+        const u32x4 ap = lds_b128(cP, dswz<WCP>(io, 32 * s2 + 8 * g4));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
-          acc[nt] = mfma16x16x32(ap, bu, acc[nt]);
+          acc[nt] = mfma16x16x32(bu, ap, acc[nt]);
         }
       }
+      if (io < n) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (i0 + r < n)
-            oh[(size_t)(t0 + i0 + r) * DV + 16 * nt + l16] = (uint16_t)(cvt2(acc[nt][r], 0.0f) & 0xffffu);
+        for (int nt = 0; nt < NT; ++nt)
+          *reinterpret_cast<uint2*>(oh + (size_t)(t0 + io) * DV + 16 * nt + 4 * g4) =
+              make_uint2(cvt2(acc[nt][0], acc[nt][1]), cvt2(acc[nt][2], acc[nt][3]));
+      }
     }
     // (2b) S = e^{b_last} S + K^T (e^{b_last - b} U) for the wave's state tiles
     {
