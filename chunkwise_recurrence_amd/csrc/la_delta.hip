@@ -373,8 +373,12 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   const int t0 = c * C, n = min(C, L - t0);
 
   constexpr int VS = 128 + 8;  // row stride of the V tile (d_v <= 128)
-  __shared__ __align__(16) uint16_t sK[C * QS];
-  __shared__ __align__(16) uint16_t sV[C * VS];
+  // K until W is formed, then V (which waits in registers until then): with
+  // the X blocks of the inverse inside T, the LDS then holds three
+  // workgroups per compute unit instead of two
+  __shared__ __align__(16) uint16_t sKV[C * (QS > VS ? QS : VS)];
+  uint16_t* const sK = sKV;
+  uint16_t* const sV = sKV;
   // N (fp32) is dead once T is known; its space then holds the split factor
   constexpr int NS = CS;  // row stride of N in fp32 words (C + 8)
   __shared__ __align__(16) float sNT[C * NS];
@@ -382,7 +386,6 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   uint16_t* sTh = reinterpret_cast<uint16_t*>(sNT);
   uint16_t* sTl = sTh + C * CS;
   __shared__ float sT[C][C + 1];
-  __shared__ float sX[3 * 16][17];
   __shared__ float sb[C], sbeta[C];
 
   const size_t rowk = (size_t)bh * L + t0;
@@ -412,13 +415,16 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   // the K and V tiles: every load issued before the first LDS store, so the
   // workgroup (which handles one chunk) waits for memory once.  A whole chunk
   // takes no row checks; the short last chunk of a sequence re-reads its last
-  // row and zeroes the rows past it.
+  // row and zeroes the rows past it.  V stays in registers until the LDS
+  // buffer it shares with K is free.
   constexpr int PK = C * NCH / 256;   // 16-byte pieces of K per thread
   constexpr int PV = C * 16 / 256;    // ... of V at most (d_v <= 128)
   static_assert(PK >= 1 && C * NCH % 256 == 0, "K tile pieces per thread");
   const int VCH = DV / 8;
+  const bool whole_chunk = n == C;
+  u32x4 xv[PV];
   auto stage = [&](bool whole) {
-    u32x4 xk[PK], xv[PV];
+    u32x4 xk[PK];
 #pragma unroll
     for (int p = 0; p < PK; ++p) {
       const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
@@ -435,16 +441,10 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
       const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
       *reinterpret_cast<u32x4*>(&sK[row * QS + 8 * ch]) = (whole || row < n) ? xk[p] : zero4;
     }
-#pragma unroll
-    for (int p = 0; p < PV; ++p) {
-      const int idx = min(tid + 256 * p, C * VCH - 1), row = idx / VCH, ch = idx % VCH;
-      *reinterpret_cast<u32x4*>(&sV[row * VS + 8 * ch]) = (whole || row < n) ? xv[p] : zero4;
-    }
   };
   if (n == C) stage(true);
   else stage(false);
   if (tid < C) sbeta[tid] = tid < n ? rbeta : 0.0f;
-  for (int idx = tid; idx < C * C; idx += 256) sT[idx / C][idx % C] = 0.0f;
   lds_barrier();  // the K tile is in LDS
 
   // The chunk's 20 score tiles: N = K K^T below and on the diagonal (10
@@ -546,7 +546,8 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   // wave J of block row I forms X = sum_{J <= M < I} N_IM T_MJ, passes it
   // through LDS (its rows become the k-runs of the next B operand) and writes
   // T_IJ = -T_II X.  Operand lanes: A[l16][g4], B[g4][l16]; result rows
-  // 4 g4 .. 4 g4 + 3 of column l16.
+  // 4 g4 .. 4 g4 + 3 of column l16.  X_J lives in T's block (J, 3), above the
+  // diagonal, which T never fills (its upper triangle is read as zero).
   for (int I = 1; I < C / 16; ++I) {
     if (w < I) {
       const int J = w;
@@ -558,22 +559,24 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
                                                     sT[16 * M + 4 * kk + g4][16 * J + l16], x, 0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sX[16 * J + 4 * g4 + r][l16] = x[r];
+      for (int r = 0; r < 4; ++r) sT[16 * J + 4 * g4 + r][48 + l16] = x[r];
       f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         y = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[16 * I + l16][16 * I + 4 * kk + g4],
-                                                  sX[16 * J + 4 * kk + g4][l16], y, 0, 0, 0);
+                                                  sT[16 * J + 4 * kk + g4][48 + l16], y, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) sT[16 * I + 4 * g4 + r][16 * J + l16] = -y[r];
     }
     lds_barrier();
   }
-  // left factor (T diag(f)) as bf16 high + remainder, row-major [C][CS]
+  // left factor (T diag(f)) as bf16 high + remainder, row-major [C][CS];
+  // T is lower triangular, and its LDS above the diagonal holds other data
   auto split = [&](bool with_decay) {
     for (int idx = tid; idx < C * C / 2; idx += 256) {
       const int i = idx / (C / 2), m = 2 * (idx % (C / 2));
-      float x0 = sT[i][m] * sbeta[m], x1 = sT[i][m + 1] * sbeta[m + 1];
+      float x0 = m <= i ? sT[i][m] * sbeta[m] : 0.0f;
+      float x1 = m + 1 <= i ? sT[i][m + 1] * sbeta[m + 1] : 0.0f;
       if (with_decay) {
         x0 *= ex2(sb[m]);
         x1 *= ex2(sb[m + 1]);
@@ -604,7 +607,12 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
       *reinterpret_cast<uint2*>(wo + (size_t)io * DK + 16 * nt + 4 * g4) =
           make_uint2(cvt2(acc[0], acc[1]), cvt2(acc[2], acc[3]));
   }
-  lds_barrier();
+  lds_barrier();  // W has read the K tile: V takes its place
+#pragma unroll
+  for (int p = 0; p < PV; ++p) {
+    const int idx = min(tid + 256 * p, C * VCH - 1), row = idx / VCH, ch = idx % VCH;
+    *reinterpret_cast<u32x4*>(&sV[row * VS + 8 * ch]) = (whole_chunk || row < n) ? xv[p] : zero4;
+  }
   split(false);
   lds_barrier();
   // U0 = (T diag(beta)) V, bf16 like W and formed transposed the same way
