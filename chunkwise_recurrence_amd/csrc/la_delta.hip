@@ -776,8 +776,15 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   }
   const int urow = (64 * w + lane) / WCU;
   const int uoff = urow * DV + 8 * ((64 * w + lane) % WCU);
-  // copies of chunk c into stage st (rows past the sequence re-read its last row)
-  auto issue = [&](int c, int st) {
+  // Copies of chunk c into stage st (rows past the sequence re-read its last
+  // row).  They pass through the compute unit's memory pipeline one 1 KB copy
+  // at a time (about 1100 cycles for a chunk's 68), and the waves of the
+  // second group, which issue behind the first on each SIMD, waited longest.
+  // With two groups, group 0 copies q, k, P and b and group 1 only W and the
+  // U0 tiles (10-11 copies per wave against 5); otherwise every wave copies
+  // an equal share.  The wait at the top of a chunk counts only the stores
+  // each wave issues after its copies, so the shares need not be equal.
+  auto issue_uniform = [&](int c, int st) {
     const int t0 = c * C, last = min(C, L - t0) - 1;
     const bool whole = last == C - 1;
     const size_t rq = (size_t)t0 * DK;
@@ -798,8 +805,50 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
       const int off = whole ? uoff : uoff - max(urow - last, 0) * DV;
       dma16(uh + (size_t)t0 * DV + off, sU0g[st][grp] + 1024 * w);
     }
-    // lane l of wave wg: prefix wg * BPER + l (one instruction per wave)
     if (lane < BPER) dma4(bhp + t0 + min(wg * BPER + lane, last), &sb[st][wg * BPER]);
+  };
+  auto issue_roles = [&](int c, int st) {
+    const int t0 = c * C, last = min(C, L - t0) - 1;
+    const size_t rq = (size_t)t0 * DK;
+    constexpr int QB4 = C * WCQ / 64 / 4;  // q/k/W blocks per wave of one group
+    constexpr int PB4 = C * WCP / 64 / 4;
+    if (grp == 0) {
+#pragma unroll
+      for (int i = 0; i < QB4; ++i) {
+        const int q = 64 * (w + 4 * i) + lane;
+        const int r = q / WCQ;
+        const int off = (min(r, last)) * DK + 8 * dswz_src_chunk<WCQ>(q);
+        dma16(qh + rq + off, sQ[st] + 1024 * (w + 4 * i));
+        dma16(kh + rq + off, sK[st] + 1024 * (w + 4 * i));
+      }
+#pragma unroll
+      for (int i = 0; i < PB4; ++i) {
+        const int q = 64 * (w + 4 * i) + lane;
+        const int r = q / WCP;
+        const int off = min(r, last) * C + 8 * dswz_src_chunk<WCP>(q);
+        dma16(ph + (size_t)t0 * C + off, sP[st] + 1024 * (w + 4 * i));
+      }
+      if (w == 0) dma4(bhp + t0 + min(lane, last), &sb[st][0]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < QB4; ++i) {
+        const int q = 64 * (w + 4 * i) + lane;
+        const int r = q / WCQ;
+        const int off = min(r, last) * DK + 8 * dswz_src_chunk<WCQ>(q);
+        dma16(wh + rq + off, sW[st] + 1024 * (w + 4 * i));
+      }
+      // block w % UBLK of group w / UBLK's U0 tile (UBLK = 2 here)
+      const int g2 = w / UBLK, b2 = w % UBLK;
+      const int q = 64 * b2 + lane;
+      const int r = q / WCU;
+      const int off = min(r, last) * DV + 8 * (q % WCU);
+      const uint16_t* uh2 = reinterpret_cast<const uint16_t*>(a.ws_U) + (size_t)bh * L * DV + (vt * NG + g2) * TV;
+      dma16(uh2 + (size_t)t0 * DV + off, sU0g[st][g2] + 1024 * b2);
+    }
+  };
+  auto issue = [&](int c, int st) {
+    if constexpr (NG == 2 && UBLK == 2) issue_roles(c, st);
+    else issue_uniform(c, st);
   };
 
   // ---- the state: own tiles (mt = w + 4 m, nt), lane rows 16 mt + 4 g4 + r, column 16 nt + l16
