@@ -162,6 +162,21 @@ def test_delta_workload_whole_output(gpu_lib):
     assert e_out <= 1e-2 and e_s <= 1e-2
 
 
+# Each layout of the matrix-core sequential pass: (B, H, d_k, d_v) and the layout
+# the launch picks for it (bf16, 64-token chunks): 32-column tiles in one group
+# once B*H*(d_v/32) >= 512, else two 16-column groups (d_k >= 64) or one
+# 16-column group (d_k = 32).  The two-group layout deals the tile copies by
+# group; the others give every wave an equal share.
+@pytest.mark.parametrize("B,H,dk,dv,layout", [
+    (1, 2, 128, 128, "two 16-column groups"), (1, 3, 64, 128, "two 16-column groups"),
+    (8, 32, 64, 64, "one 32-column group"), (8, 32, 32, 64, "one 32-column group"),
+    (1, 3, 32, 64, "one 16-column group"), (2, 2, 32, 32, "one 16-column group")])
+def test_delta_sequential_pass_layouts(gpu_lib, B, H, dk, dv, layout):
+    c = W.RandomCase(B, H, 64 * 2 + 13, dk, dv, torch.bfloat16, W.PHI_IDENTITY, W.DECAY_GATE,
+                     seed=680 + B + H + dk + dv, scale=1.0 / np.sqrt(dk), with_state=True)
+    _run(gpu_lib, c, 64, f"sequential pass, {layout}")
+
+
 def test_delta_many_heads_takes_the_32_column_pass(gpu_lib):
     """B*H*(d_v/32) >= 512 keeps 32-column workgroups in the MFMA pass; the
     smaller cases above run the 16-column ones."""
