@@ -203,10 +203,11 @@ const char* la_status_string(int status);
  * products are folded into a unit lower-triangular solve per chunk (the WY
  * idea of tutorial section 5.3): a chunk-parallel pass solves every chunk and
  * writes W = T diag(beta e^b) K and U0 = T diag(beta) V into the workspace
- * (for bf16 inputs with 64-token chunks also each chunk's causal scores
- * (q_i . k_j) e^{b_i - b_j}, j <= i), then a sequential pass per head computes
- * U = U0 - W S_c and the decayed linear-attention chunk with V replaced by U.
- * Accumulation is fp32 (bf16 inputs: bf16 matrix-core products).
+ * (for bf16 inputs with 64-token chunks as bf16, together with each chunk's
+ * causal scores (q_i . k_j) e^{b_i - b_j}, j <= i, and its in-chunk decay
+ * prefix b), then a sequential pass per head computes U = U0 - W S_c and the
+ * decayed linear-attention chunk with V replaced by U.  Accumulation is fp32
+ * (bf16 inputs: bf16 matrix-core products).
  *   q, k       : [B,H,L,d_k] (device, read), dtype LA_F32 or LA_BF16
  *   v          : [B,H,L,d_v] (device, read)
  *   beta       : [B,H,L] fp32 write strengths (device, read), 4-byte aligned
