@@ -59,8 +59,10 @@
 // into q~ k~^T, the inter-chunk term into q~ (diag(e^r) S) and the update into
 // S' = diag(e^{b_last - r}) (diag(e^r) S + k~^T V).  The prefix runs over
 // log a loaded straight into registers (each thread scans a run of tokens for
-// two channels, the runs combine through LDS), and q~, k~ replace q, k in
-// their LDS tiles, so everything after is the kernel's usual MFMA work.
+// four channels, two where runs of four would not tile the chunk; the runs of
+// a wave combine by lane shuffles and the waves' totals through LDS), and q~,
+// k~ replace q, k in their LDS tiles, so everything after is the kernel's
+// usual MFMA work.
 // The split stays in range while every channel's log2 decay over a chunk sums
 // to at least -kSplitMax (factors up to 2^96).  A workgroup that meets a chunk
 // beyond that flags itself, and a second launch (EXACT) recomputes exactly the
@@ -101,7 +103,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 // SO: the state-only pass, which stages no Q tile and needs no P~, partial
 // exchange or output staging (so it can prefetch deeper).  CH: the
-// per-channel decay, whose log a tile goes to registers (TPR tokens of two
+// per-channel decay, whose log a tile goes to registers (TPR tokens of CPT
 // channels per thread) instead of per-wave token weights to LDS.
 template <int DK, int NWV, int KH, int C, bool SO = false, bool CH = false>
 struct Geo {
@@ -126,8 +128,12 @@ struct Geo {
   static constexpr int QK_PER = (QK_BLK + NW - 1) / NW;  // per wave
   static constexpr int V_PER = (V_BLK + NW - 1) / NW;
   // per-channel decay: the workgroup's threads split into RUNS runs of TPR
-  // consecutive tokens, each thread taking two key channels of its run
-  static constexpr int RUNS = 128 * NW / DK;
+  // consecutive tokens, each thread taking CPT key channels of its run (four,
+  // one 16-byte load per token, where such runs tile the chunk; else two), a
+  // wave RPW runs of all DK channels
+  static constexpr int CPT = (256 * NW / DK <= C && C % (256 * NW / DK) == 0) ? 4 : 2;
+  static constexpr int RPW = 64 * CPT / DK;
+  static constexpr int RUNS = RPW * NW;
   static constexpr int TPR = RUNS > 0 && C % RUNS == 0 ? C / RUNS : 0;
   // vector memory instructions of one chunk per wave (at most)
   static constexpr int LOADS_MAX = (SO ? 1 : 2) * QK_PER + V_PER + (CH ? TPR : 1);
@@ -144,9 +150,9 @@ struct Geo {
   // the normalised form's z, denominator partials and row sums (counted for
   // every instance, so both forms run the same pipeline depth)
   static constexpr size_t NORM_BYTES = 2 * 4 * (size_t)DK + 4 * (size_t)C * (KH + NRB);
-  // per-wave token weights, or (per-channel decay) the run totals and the
-  // per-channel factors e^r, e^{b_last - r}
-  static constexpr size_t W_BYTES = CH ? 4 * (size_t)RUNS * DK + 2 * 4 * (size_t)DK
+  // per-wave token weights, or (per-channel decay) the waves' run totals and
+  // the per-channel factors e^r, e^{b_last - r}
+  static constexpr size_t W_BYTES = CH ? 4 * (size_t)NW * DK + 2 * 4 * (size_t)DK
                                        : 2 * 4 * (size_t)NW * C;
   static constexpr size_t stage_bytes(int n) {
     return SO ? (size_t)n * ((size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
@@ -154,8 +160,9 @@ struct Geo {
               : (size_t)n * (2 * (size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
                     2 * (size_t)C * C + W_BYTES + XU_BYTES + 2048 * (size_t)NW  + NORM_BYTES + 256;
   }
-  // the per-channel decay's prefetch registers stay bounded (TPR <= 16)
-  static constexpr bool CH_OK = !CH || (TPR >= 1 && TPR <= 16 && DK >= 32);
+  // the per-channel decay's prefetch registers stay bounded (at most 32 values
+  // per thread and stage)
+  static constexpr bool CH_OK = !CH || (TPR >= 1 && TPR * CPT <= 32 && DK >= 32);
   static constexpr int NSTG =
       (UNIFORM && stage_bytes(3) <= kMaxLds && 2 * STORES + LOADS_MAX < 64) ? 3 : 2;
   static constexpr size_t LDS = stage_bytes(NSTG);
@@ -257,6 +264,33 @@ __device__ __forceinline__ void lds_wave_sync() {
 }
 
 enum { kCatNone = 0, kCatHead = 1, kCatToken = 2, kCatChannel = 3 };
+
+// N (2 or 4) consecutive bf16 of an LDS tile, 4N-byte aligned, to fp32 and back
+template <int N>
+__device__ __forceinline__ void lds_bf16_get(const char* p, float* f) {
+  if constexpr (N == 4) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+    f[0] = bf16_to_f32(w[0] & 0xffffu);
+    f[1] = bf16_to_f32(w[0] >> 16);
+    f[2] = bf16_to_f32(w[1] & 0xffffu);
+    f[3] = bf16_to_f32(w[1] >> 16);
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    f[0] = bf16_to_f32(w & 0xffffu);
+    f[1] = bf16_to_f32(w >> 16);
+  }
+}
+template <int N>
+__device__ __forceinline__ void lds_bf16_put(char* p, const float* f) {
+  if constexpr (N == 4) {
+    u32x2 w;
+    w[0] = cvt2(f[0], f[1]);
+    w[1] = cvt2(f[2], f[3]);
+    *reinterpret_cast<u32x2*>(p) = w;
+  } else {
+    *reinterpret_cast<uint32_t*>(p) = cvt2(f[0], f[1]);
+  }
+}
 
 // Per-channel decay: the largest |log2 decay| of a chunk (per channel) the
 // split q e^{b - r}, k e^{r - b} takes (factors up to 2^96); beyond it the
@@ -395,9 +429,9 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   __shared__ int sBad;
   // per-wave weights of the current chunk: [0] e^{b_last - b_t}, [1] e^{b_t}
   __shared__ __align__(16) float sW[CHN ? 1 : NW][2][CHN ? 4 : C];
-  // per-channel decay: log2-decay totals of each run, then e^r and
+  // per-channel decay: log2-decay totals of each wave's runs, then e^r and
   // e^{b_last - r} per key channel
-  __shared__ __align__(16) float sTot[CHN ? G::RUNS : 1][CHN ? DK : 4];
+  __shared__ __align__(16) float sTot[CHN ? NW : 1][CHN ? DK : 4];
   __shared__ __align__(16) float sER[CHN ? DK : 4], sEL[CHN ? DK : 4];
   // normalised form: z (double-buffered by chunk parity), the denominators'
   // inter-chunk partials per key part and the score row sums per key block
@@ -434,9 +468,10 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   const float lg2 = CAT == kCatHead ? log2f(a.decay[hd]) : 0.0f;  // b_i = (i + 1) lg2
   float* wq = sW[CHN ? 0 : wave][0];
   float* eq = sW[CHN ? 0 : wave][1];
-  // per-channel decay: this thread's run of tokens and pair of key channels
+  // per-channel decay: this thread's run of tokens and its key channels
+  // CPT pq .. CPT pq + CPT - 1
   const float* dch = CHN ? a.decay + (size_t)bh * L * DK : nullptr;
-  const int pr = tid % (DK / 2), run = tid / (DK / 2);
+  const int pq = tid % (DK / G::CPT), run = tid / (DK / G::CPT);
 
   // ---- loop-invariant mask/decay weights of this wave's score blocks ------
   // block (I, J), register r: query row i = 32 I + l32, token
@@ -597,8 +632,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   auto chunk_of = [&](int it) { return (STATE_ONLY && !CHN) ? c_end - 1 - it : c_begin + it; };
 
   // per-channel decay: log a of this thread's tokens and channels, per stage
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  f32x2 lreg[CHN ? NS : 1][CHN ? G::TPR : 1];
+  typedef float fcv __attribute__((ext_vector_type(G::CPT)));
+  fcv lreg[CHN ? NS : 1][CHN ? G::TPR : 1];
 
   auto issue_loads = [&](auto BUF, int it) {
     const int c = chunk_of(it);
@@ -645,7 +680,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
       for (int i = 0; i < G::TPR; ++i) {
         const int t = min(t0 + run * G::TPR + i, L - 1);
-        lreg[buf][i] = *reinterpret_cast<const f32x2*>(dch + (size_t)t * DK + 2 * pr);
+        lreg[buf][i] = *reinterpret_cast<const fcv*>(dch + (size_t)t * DK + G::CPT * pq);
       }
     }
   };
@@ -653,7 +688,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   if (CHN && tid == 0) sBad = 0;
 
   float logA = 0.0f;
-  f32x2 logA2 = f32x2{0.0f, 0.0f};  // per-channel decay: totals of channels 2 pr, 2 pr + 1
+  fcv logAc = fcv{};  // per-channel decay: totals of this thread's channels
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
 
   auto body = [&](auto BUF, int it) {
@@ -710,18 +745,19 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     // count and does not see the tile copies, so a later wait would also
     // hold back the next chunk's copies
     constexpr float kLog2e = 1.4426950408889634f;
-    f32x2 bl[CHN ? G::TPR : 1];
-    f32x2 accb = f32x2{0.0f, 0.0f};
+    fcv bl[CHN ? G::TPR : 1];
+    fcv accb = fcv{};
     if constexpr (CHN) {
 #pragma unroll
       for (int i = 0; i < G::TPR; ++i) {
-        const f32x2 x = lreg[buf][i] * kLog2e;
-        accb += run * G::TPR + i < nvalid ? x : f32x2{0.0f, 0.0f};
+        const fcv x = lreg[buf][i] * kLog2e;
+        accb += run * G::TPR + i < nvalid ? x : fcv{};
         bl[i] = accb;
       }
       // the run total depends on every register: using it here keeps the
       // compiler's wait for them ahead of the copies below
-      asm volatile("" ::"v"(accb[0]), "v"(accb[1]));
+#pragma unroll
+      for (int e = 0; e < G::CPT; ++e) asm volatile("" ::"v"(accb[e]));
     }
     if (it + NS - 1 < n_it) issue_loads(std::integral_constant<int, (buf + NS - 1) % NS>{}, it + NS - 1);
 
@@ -737,60 +773,91 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     }
 
     if constexpr (CHN) {
-      // the runs' totals of the in-run prefixes through LDS
-      *reinterpret_cast<f32x2*>(&sTot[run][2 * pr]) = accb;
-      lds_barrier();
-      f32x2 off = f32x2{0.0f, 0.0f}, tot = f32x2{0.0f, 0.0f}, later = f32x2{0.0f, 0.0f};
+      // the run totals' exclusive prefix (pre) and suffix (suf) over the
+      // wave's RPW runs, LS lanes apart, by shuffles (a shifted Hillis-Steele
+      // scan: sums only, so log a = -inf stays -inf), then the waves' totals
+      // through LDS
+      constexpr int LS = DK / G::CPT;
+      const int rw = lane / LS;
+      fcv pre = fcv{}, suf = fcv{};
+      if constexpr (G::RPW > 1) {
 #pragma unroll
-      for (int r = 0; r < G::RUNS; ++r) {
-        const f32x2 x = *reinterpret_cast<const f32x2*>(&sTot[r][2 * pr]);
-        off += r < run ? x : f32x2{0.0f, 0.0f};
-        later += r > run ? x : f32x2{0.0f, 0.0f};
-        tot += x;
+        for (int e = 0; e < G::CPT; ++e) {
+          const float up = __shfl_up(accb[e], LS), dn = __shfl_down(accb[e], LS);
+          pre[e] = rw > 0 ? up : 0.0f;
+          suf[e] = rw < G::RPW - 1 ? dn : 0.0f;
+        }
+#pragma unroll
+        for (int d = 1; d < G::RPW - 1; d *= 2) {
+#pragma unroll
+          for (int e = 0; e < G::CPT; ++e) {
+            const float up = __shfl_up(pre[e], d * LS), dn = __shfl_down(suf[e], d * LS);
+            if (rw >= d) pre[e] += up;
+            if (rw + d < G::RPW) suf[e] += dn;
+          }
+        }
       }
+      if (rw == G::RPW - 1) *reinterpret_cast<fcv*>(&sTot[wave][G::CPT * pq]) = pre + accb;
+      lds_barrier();
+      // (wave is uniform: the partial sums loop over it, with no selects)
+      fcv off = pre, tot = fcv{}, later = suf;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) tot += *reinterpret_cast<const fcv*>(&sTot[w2][G::CPT * pq]);
+      for (int w2 = 0; w2 < wave; ++w2) off += *reinterpret_cast<const fcv*>(&sTot[w2][G::CPT * pq]);
+      if constexpr (XF)
+        for (int w2 = wave + 1; w2 < NW; ++w2) later += *reinterpret_cast<const fcv*>(&sTot[w2][G::CPT * pq]);
       if constexpr (!XF) {
         // the split below puts factors up to 2^{-tot/2} into q and k: a chunk
         // whose log2 decay sums below -kSplitMax in any channel (or is not a
         // number) flags the workgroup for the exact re-run
-        if (!(tot[0] >= -kSplitMax && tot[1] >= -kSplitMax)) sBad = 1;
-        const f32x2 rr = tot * 0.5f;  // r = b_last / 2
-        // q~ = phi(q) e^{b - r}, k~ = phi(k) e^{r - b}, in place
+        bool in_range = true;
 #pragma unroll
-        for (int i = 0; i < G::TPR; ++i) {
-          const f32x2 b = off + bl[i];
-          const int o = swz<G::WCK>(run * G::TPR + i, 2 * pr);
-          uint32_t* kp = reinterpret_cast<uint32_t*>(kb + o);
-          const uint32_t kw = *kp;
-          float k0 = bf16_to_f32(kw & 0xffffu), k1 = bf16_to_f32(kw >> 16);
-          if (elu) {
-            k0 = feature_elu1(k0);
-            k1 = feature_elu1(k1);
+        for (int e = 0; e < G::CPT; ++e) in_range = in_range && tot[e] >= -kSplitMax;
+        if (!in_range) sBad = 1;
+        const fcv rr = tot * 0.5f;  // r = b_last / 2
+        // q~ = phi(q) e^{b - r}, k~ = phi(k) e^{r - b}, in place
+        auto rescale = [&](auto ELU) {
+#pragma unroll
+          for (int i = 0; i < G::TPR; ++i) {
+            const fcv b = off + bl[i];
+            const int o = swz<G::WCK>(run * G::TPR + i, G::CPT * pq);
+            float kf[G::CPT], qf[G::CPT];
+            lds_bf16_get<G::CPT>(kb + o, kf);
+            lds_bf16_get<G::CPT>(qb + o, qf);
+#pragma unroll
+            for (int e = 0; e < G::CPT; ++e) {
+              if constexpr (decltype(ELU)::value) {
+                kf[e] = feature_elu1(kf[e]);
+                qf[e] = feature_elu1(qf[e]);
+              }
+              kf[e] *= __builtin_amdgcn_exp2f(rr[e] - b[e]);
+              qf[e] *= __builtin_amdgcn_exp2f(b[e] - rr[e]);
+            }
+            lds_bf16_put<G::CPT>(kb + o, kf);
+            lds_bf16_put<G::CPT>(qb + o, qf);
           }
-          *kp = cvt2(k0 * __builtin_amdgcn_exp2f(rr[0] - b[0]), k1 * __builtin_amdgcn_exp2f(rr[1] - b[1]));
-          uint32_t* qp = reinterpret_cast<uint32_t*>(qb + o);
-          const uint32_t qw = *qp;
-          float q0 = bf16_to_f32(qw & 0xffffu), q1 = bf16_to_f32(qw >> 16);
-          if (elu) {
-            q0 = feature_elu1(q0);
-            q1 = feature_elu1(q1);
-          }
-          *qp = cvt2(q0 * __builtin_amdgcn_exp2f(b[0] - rr[0]), q1 * __builtin_amdgcn_exp2f(b[1] - rr[1]));
-        }
+        };
+        if (elu) rescale(std::true_type{});
+        else rescale(std::false_type{});
         if (run == 0) {
-          *reinterpret_cast<f32x2*>(&sER[2 * pr]) =
-              f32x2{__builtin_amdgcn_exp2f(rr[0]), __builtin_amdgcn_exp2f(rr[1])};
-          *reinterpret_cast<f32x2*>(&sEL[2 * pr]) =
-              f32x2{__builtin_amdgcn_exp2f(tot[0] - rr[0]), __builtin_amdgcn_exp2f(tot[1] - rr[1])};
+          fcv er, el;
+#pragma unroll
+          for (int e = 0; e < G::CPT; ++e) {
+            er[e] = __builtin_amdgcn_exp2f(rr[e]);
+            el[e] = __builtin_amdgcn_exp2f(tot[e] - rr[e]);
+          }
+          *reinterpret_cast<fcv*>(&sER[G::CPT * pq]) = er;
+          *reinterpret_cast<fcv*>(&sEL[G::CPT * pq]) = el;
         }
       } else {
         // exact form: every factor is 2^(a direct sum of log2 a <= 0).  sf[i]:
         // the sum over the run's tokens after token i (exclusive suffix)
-        f32x2 sf[G::TPR];
-        f32x2 acs = f32x2{0.0f, 0.0f};
+        fcv sf[G::TPR];
+        fcv acs = fcv{};
 #pragma unroll
         for (int i = G::TPR - 1; i >= 0; --i) {
           sf[i] = acs;
-          acs += run * G::TPR + i < nvalid ? lreg[buf][i] * kLog2e : f32x2{0.0f, 0.0f};
+          acs += run * G::TPR + i < nvalid ? lreg[buf][i] * kLog2e : fcv{};
         }
         if constexpr (!STATE_ONLY) {
           // phi on this thread's q and k elements in place, its log2 a into the tile
@@ -798,49 +865,65 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
           for (int i = 0; i < G::TPR; ++i) {
             const int t = run * G::TPR + i;
-            const int o = swz<G::WCK>(t, 2 * pr);
+            const int o = swz<G::WCK>(t, G::CPT * pq);
             if (elu) {
-              uint32_t* kp = reinterpret_cast<uint32_t*>(kb + o);
-              uint32_t* qp = reinterpret_cast<uint32_t*>(qb + o);
-              const uint32_t kw = *kp, qw = *qp;
-              *kp = cvt2(feature_elu1(bf16_to_f32(kw & 0xffffu)), feature_elu1(bf16_to_f32(kw >> 16)));
-              *qp = cvt2(feature_elu1(bf16_to_f32(qw & 0xffffu)), feature_elu1(bf16_to_f32(qw >> 16)));
+              float kf[G::CPT], qf[G::CPT];
+              lds_bf16_get<G::CPT>(kb + o, kf);
+              lds_bf16_get<G::CPT>(qb + o, qf);
+#pragma unroll
+              for (int e = 0; e < G::CPT; ++e) {
+                kf[e] = feature_elu1(kf[e]);
+                qf[e] = feature_elu1(qf[e]);
+              }
+              lds_bf16_put<G::CPT>(kb + o, kf);
+              lds_bf16_put<G::CPT>(qb + o, qf);
             }
-            *reinterpret_cast<f32x2*>(&lat[t * DK + 2 * pr]) =
-                t < nvalid ? lreg[buf][i] * kLog2e : f32x2{0.0f, 0.0f};
+            *reinterpret_cast<fcv*>(&lat[t * DK + G::CPT * pq]) =
+                t < nvalid ? lreg[buf][i] * kLog2e : fcv{};
           }
           lds_barrier();
           exact_scores<DK, C, NW>(qb, kb, reinterpret_cast<const float*>(sX), sP, nvalid, tid);
           lds_barrier();  // the scores have read the tiles the rescaling below overwrites
         }
-        // q^ = phi(q) e^{b}, k^ = phi(k) e^{b_last - b}, in place
+        // q^ = phi(q) e^{b}, k^ = phi(k) e^{b_last - b}, in place (the state
+        // pass maps k here; the flag is tested once, not per element)
+        auto rescale = [&](auto ELU) {
 #pragma unroll
-        for (int i = 0; i < G::TPR; ++i) {
-          const int o = swz<G::WCK>(run * G::TPR + i, 2 * pr);
-          const f32x2 ek = sf[i] + later;
-          uint32_t* kp = reinterpret_cast<uint32_t*>(kb + o);
-          const uint32_t kw = *kp;
-          float k0 = bf16_to_f32(kw & 0xffffu), k1 = bf16_to_f32(kw >> 16);
-          if (STATE_ONLY && elu) {
-            k0 = feature_elu1(k0);
-            k1 = feature_elu1(k1);
+          for (int i = 0; i < G::TPR; ++i) {
+            const int o = swz<G::WCK>(run * G::TPR + i, G::CPT * pq);
+            const fcv ek = sf[i] + later;
+            float kf[G::CPT];
+            lds_bf16_get<G::CPT>(kb + o, kf);
+#pragma unroll
+            for (int e = 0; e < G::CPT; ++e) {
+              if constexpr (STATE_ONLY && decltype(ELU)::value) kf[e] = feature_elu1(kf[e]);
+              kf[e] *= __builtin_amdgcn_exp2f(ek[e]);
+            }
+            lds_bf16_put<G::CPT>(kb + o, kf);
+            if constexpr (!STATE_ONLY) {
+              const fcv eb = off + bl[i];
+              float qf[G::CPT];
+              lds_bf16_get<G::CPT>(qb + o, qf);
+#pragma unroll
+              for (int e = 0; e < G::CPT; ++e) qf[e] *= __builtin_amdgcn_exp2f(eb[e]);
+              lds_bf16_put<G::CPT>(qb + o, qf);
+            }
           }
-          *kp = cvt2(k0 * __builtin_amdgcn_exp2f(ek[0]), k1 * __builtin_amdgcn_exp2f(ek[1]));
-          if constexpr (!STATE_ONLY) {
-            const f32x2 eb = off + bl[i];
-            uint32_t* qp = reinterpret_cast<uint32_t*>(qb + o);
-            const uint32_t qw = *qp;
-            *qp = cvt2(bf16_to_f32(qw & 0xffffu) * __builtin_amdgcn_exp2f(eb[0]),
-                       bf16_to_f32(qw >> 16) * __builtin_amdgcn_exp2f(eb[1]));
-          }
-        }
+        };
+        if (STATE_ONLY && elu) rescale(std::true_type{});
+        else rescale(std::false_type{});
         if (run == 0) {
-          *reinterpret_cast<f32x2*>(&sER[2 * pr]) = f32x2{1.0f, 1.0f};
-          *reinterpret_cast<f32x2*>(&sEL[2 * pr]) =
-              f32x2{__builtin_amdgcn_exp2f(tot[0]), __builtin_amdgcn_exp2f(tot[1])};
+          fcv er, el;
+#pragma unroll
+          for (int e = 0; e < G::CPT; ++e) {
+            er[e] = 1.0f;
+            el[e] = __builtin_amdgcn_exp2f(tot[e]);
+          }
+          *reinterpret_cast<fcv*>(&sER[G::CPT * pq]) = er;
+          *reinterpret_cast<fcv*>(&sEL[G::CPT * pq]) = el;
         }
       }
-      logA2 += tot;
+      logAc += tot;
       lds_barrier();
     }
     // rows of this wave's state tiles scaled by a per-channel factor from LDS
@@ -1180,7 +1263,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     dst = a.ws_S + (unit0 + sigma) * DK * DV;
     if constexpr (CHN) {
       if (vt == 0 && run == 0)
-        *reinterpret_cast<f32x2*>(&a.ws_logA[(unit0 + sigma) * DK + 2 * pr]) = logA2;
+        *reinterpret_cast<fcv*>(&a.ws_logA[(unit0 + sigma) * DK + G::CPT * pq]) = logAc;
     } else {
       if (vt == 0 && tid == 0) a.ws_logA[unit0 + sigma] = logA;
     }
