@@ -633,7 +633,11 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 
   // per-channel decay: log a of this thread's tokens and channels, per stage
   typedef float fcv __attribute__((ext_vector_type(G::CPT)));
-  fcv lreg[CHN ? NS : 1][CHN ? G::TPR : 1];
+  // (the fast output pass with two stages reads a chunk's registers before
+  // the next chunk's loads are issued into them, so one set serves; the exact
+  // form reads them again after the issue)
+  constexpr int LB = (CHN && !XF && NS == 2) ? 1 : (CHN ? NS : 1);
+  fcv lreg[LB][CHN ? G::TPR : 1];
 
   auto issue_loads = [&](auto BUF, int it) {
     const int c = chunk_of(it);
@@ -680,7 +684,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
       for (int i = 0; i < G::TPR; ++i) {
         const int t = min(t0 + run * G::TPR + i, L - 1);
-        lreg[buf][i] = *reinterpret_cast<const fcv*>(dch + (size_t)t * DK + G::CPT * pq);
+        lreg[buf % LB][i] = *reinterpret_cast<const fcv*>(dch + (size_t)t * DK + G::CPT * pq);
       }
     }
   };
@@ -750,7 +754,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     if constexpr (CHN) {
 #pragma unroll
       for (int i = 0; i < G::TPR; ++i) {
-        const fcv x = lreg[buf][i] * kLog2e;
+        const fcv x = lreg[buf % LB][i] * kLog2e;
         accb += run * G::TPR + i < nvalid ? x : fcv{};
         bl[i] = accb;
       }
@@ -857,7 +861,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
         for (int i = G::TPR - 1; i >= 0; --i) {
           sf[i] = acs;
-          acs += run * G::TPR + i < nvalid ? lreg[buf][i] * kLog2e : fcv{};
+          acs += run * G::TPR + i < nvalid ? lreg[buf % LB][i] * kLog2e : fcv{};
         }
         if constexpr (!STATE_ONLY) {
           // phi on this thread's q and k elements in place, its log2 a into the tile
@@ -879,7 +883,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
               lds_bf16_put<G::CPT>(qb + o, qf);
             }
             *reinterpret_cast<fcv*>(&lat[t * DK + G::CPT * pq]) =
-                t < nvalid ? lreg[buf][i] * kLog2e : fcv{};
+                t < nvalid ? lreg[buf % LB][i] * kLog2e : fcv{};
           }
           lds_barrier();
           exact_scores<DK, C, NW>(qb, kb, reinterpret_cast<const float*>(sX), sP, nvalid, tid);
@@ -1056,10 +1060,18 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
           f32x16 pacc;
 #pragma unroll
           for (int r = 0; r < 16; ++r) pacc[r] = 0.0f;
+          // (per-channel decay: the lane's row and half re-derived each chunk, so
+          // the compiler forms these swizzled offsets here instead of holding
+          // them across the chunk loop, where that kernel's registers run out
+          // and they would be spilled -- a scratch reload's wait would also
+          // wait for the next chunk's tile copies)
+          int ln = lane;
+          if constexpr (CHN) asm volatile("" : "+v"(ln));
+          const int rl = ln & 31, rh = ln >> 5;
 #pragma unroll
           for (int s = 0; s < G::NKS; ++s) {
-            const u32x4 kA = lds_b128(kb, swz<G::WCK>(32 * J + l32, 16 * s + 8 * h));
-            const u32x4 qB = lds_b128(qb, swz<G::WCK>(32 * I + l32, 16 * s + 8 * h));
+            const u32x4 kA = lds_b128(kb, swz<G::WCK>(32 * J + rl, 16 * s + 8 * rh));
+            const u32x4 qB = lds_b128(qb, swz<G::WCK>(32 * I + rl, 16 * s + 8 * rh));
             pacc = mfma32(kA, qB, pacc);
           }
           // register r: token j = 32 J + 8 (r / 4) + 4 h + r % 4, row i = 32 I + l32
