@@ -58,11 +58,11 @@
 // (each exponent within half the chunk's total decay), which turns the scores
 // into q~ k~^T, the inter-chunk term into q~ (diag(e^r) S) and the update into
 // S' = diag(e^{b_last - r}) (diag(e^r) S + k~^T V).  The prefix runs over
-// log a loaded straight into registers (each thread scans a run of tokens for
-// four channels, two where runs of four would not tile the chunk; the runs of
-// a wave combine by lane shuffles and the waves' totals through LDS), and q~,
-// k~ replace q, k in their LDS tiles, so everything after is the kernel's
-// usual MFMA work.
+// log a loaded straight into registers (each wave scans its own key channels
+// over the whole chunk: a thread takes a run of tokens of four or two
+// channels, and the runs combine by lane shifts inside a 16-lane row, with no
+// exchange between waves), and q~, k~ replace q, k in their LDS tiles, so
+// everything after is the kernel's usual MFMA work.
 // The split stays in range while every channel's log2 decay over a chunk sums
 // to at least -kSplitMax (factors up to 2^96).  A workgroup that meets a chunk
 // beyond that flags itself, and a second launch (EXACT) recomputes exactly the
@@ -127,14 +127,15 @@ struct Geo {
   static constexpr int V_BLK = V_BYTES / 1024;
   static constexpr int QK_PER = (QK_BLK + NW - 1) / NW;  // per wave
   static constexpr int V_PER = (V_BLK + NW - 1) / NW;
-  // per-channel decay: the workgroup's threads split into RUNS runs of TPR
-  // consecutive tokens, each thread taking CPT key channels of its run (four,
-  // one 16-byte load per token, where such runs tile the chunk; else two), a
-  // wave RPW runs of all DK channels
-  static constexpr int CPT = (256 * NW / DK <= C && C % (256 * NW / DK) == 0) ? 4 : 2;
-  static constexpr int RPW = 64 * CPT / DK;
-  static constexpr int RUNS = RPW * NW;
-  static constexpr int TPR = RUNS > 0 && C % RUNS == 0 ? C / RUNS : 0;
+  // per-channel decay: wave w scans key channels CPW w .. CPW w + CPW - 1
+  // over the whole chunk.  Its lanes are CPW / CPT channel groups of CPT
+  // channels (four -- one 16-byte load per token -- unless that takes more
+  // than 16 runs, else two) times R runs of TPR consecutive tokens; a group's
+  // runs are R consecutive lanes of one 16-lane row
+  static constexpr int CPW = DK / NW;
+  static constexpr int CPT = (CPW % 4 == 0 && 256 / CPW <= 16) ? 4 : 2;
+  static constexpr int R = 64 * CPT / CPW;
+  static constexpr int TPR = R >= 1 && C % R == 0 ? C / R : 0;
   // vector memory instructions of one chunk per wave (at most)
   static constexpr int LOADS_MAX = (SO ? 1 : 2) * QK_PER + V_PER + (CH ? TPR : 1);
   static constexpr int STORES = SO ? 0 : 2 * RBW;
@@ -150,9 +151,9 @@ struct Geo {
   // the normalised form's z, denominator partials and row sums (counted for
   // every instance, so both forms run the same pipeline depth)
   static constexpr size_t NORM_BYTES = 2 * 4 * (size_t)DK + 4 * (size_t)C * (KH + NRB);
-  // per-wave token weights, or (per-channel decay) the waves' run totals and
-  // the per-channel factors e^r, e^{b_last - r}
-  static constexpr size_t W_BYTES = CH ? 4 * (size_t)NW * DK + 2 * 4 * (size_t)DK
+  // per-wave token weights, or (per-channel decay) the per-channel factors
+  // e^r, e^{b_last - r}
+  static constexpr size_t W_BYTES = CH ? 2 * 4 * (size_t)DK
                                        : 2 * 4 * (size_t)NW * C;
   static constexpr size_t stage_bytes(int n) {
     return SO ? (size_t)n * ((size_t)QK_BYTES + (size_t)V_BYTES + 4 * (size_t)C) +
@@ -162,7 +163,7 @@ struct Geo {
   }
   // the per-channel decay's prefetch registers stay bounded (at most 32 values
   // per thread and stage)
-  static constexpr bool CH_OK = !CH || (TPR >= 1 && TPR * CPT <= 32 && DK >= 32);
+  static constexpr bool CH_OK = !CH || (R <= 16 && TPR >= 1 && TPR * CPT <= 32 && DK >= 32);
   static constexpr int NSTG =
       (UNIFORM && stage_bytes(3) <= kMaxLds && 2 * STORES + LOADS_MAX < 64) ? 3 : 2;
   static constexpr size_t LDS = stage_bytes(NSTG);
@@ -264,6 +265,44 @@ __device__ __forceinline__ void lds_wave_sync() {
 }
 
 enum { kCatNone = 0, kCatHead = 1, kCatToken = 2, kCatChannel = 3 };
+
+// x of the lane D below (row_shr) or above (row_shl) in the same 16-lane row
+// (DPP); a lane with none in its row gets 0.  Every lane must be active.
+template <int D>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + D, 0xf, 0xf, false));
+}
+template <int D>
+__device__ __forceinline__ float dpp_row_shl(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + D, 0xf, 0xf, false));
+}
+// Over a group of R lanes (R <= 16 consecutive lanes of a 16-lane row,
+// r = lane % R): the sum of x over the group's lanes below r (prefix) or
+// above r (suffix) -- a Hillis-Steele scan of the group shifted by one lane;
+// its step d only matters when d < R - 1, the first lane's shifted value
+// being 0
+template <int R>
+__device__ __forceinline__ float group_excl_prefix(float x, int r) {
+  const float x1 = dpp_row_shr<1>(x);
+  float s = r >= 1 ? x1 : 0.0f;
+  if constexpr (R > 2) { const float y = dpp_row_shr<1>(s); if (r >= 1) s += y; }
+  if constexpr (R > 3) { const float y = dpp_row_shr<2>(s); if (r >= 2) s += y; }
+  if constexpr (R > 5) { const float y = dpp_row_shr<4>(s); if (r >= 4) s += y; }
+  if constexpr (R > 9) { const float y = dpp_row_shr<8>(s); if (r >= 8) s += y; }
+  return s;
+}
+template <int R>
+__device__ __forceinline__ float group_excl_suffix(float x, int r) {
+  const float x1 = dpp_row_shl<1>(x);
+  float s = r + 1 < R ? x1 : 0.0f;
+  if constexpr (R > 2) { const float y = dpp_row_shl<1>(s); if (r + 1 < R) s += y; }
+  if constexpr (R > 3) { const float y = dpp_row_shl<2>(s); if (r + 2 < R) s += y; }
+  if constexpr (R > 5) { const float y = dpp_row_shl<4>(s); if (r + 4 < R) s += y; }
+  if constexpr (R > 9) { const float y = dpp_row_shl<8>(s); if (r + 8 < R) s += y; }
+  return s;
+}
 
 // N (2 or 4) consecutive bf16 of an LDS tile, 4N-byte aligned, to fp32 and back
 template <int N>
@@ -429,9 +468,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   __shared__ int sBad;
   // per-wave weights of the current chunk: [0] e^{b_last - b_t}, [1] e^{b_t}
   __shared__ __align__(16) float sW[CHN ? 1 : NW][2][CHN ? 4 : C];
-  // per-channel decay: log2-decay totals of each wave's runs, then e^r and
-  // e^{b_last - r} per key channel
-  __shared__ __align__(16) float sTot[CHN ? NW : 1][CHN ? DK : 4];
+  // per-channel decay: e^r and e^{b_last - r} per key channel
   __shared__ __align__(16) float sER[CHN ? DK : 4], sEL[CHN ? DK : 4];
   // normalised form: z (double-buffered by chunk parity), the denominators'
   // inter-chunk partials per key part and the score row sums per key block
@@ -469,9 +506,10 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
   float* wq = sW[CHN ? 0 : wave][0];
   float* eq = sW[CHN ? 0 : wave][1];
   // per-channel decay: this thread's run of tokens and its key channels
-  // CPT pq .. CPT pq + CPT - 1
+  // ch0 .. ch0 + CPT - 1
   const float* dch = CHN ? a.decay + (size_t)bh * L * DK : nullptr;
-  const int pq = tid % (DK / G::CPT), run = tid / (DK / G::CPT);
+  const int run = CHN ? lane % G::R : 0;
+  const int ch0 = CHN ? G::CPW * wave + G::CPT * (lane / G::R) : 0;
 
   // ---- loop-invariant mask/decay weights of this wave's score blocks ------
   // block (I, J), register r: query row i = 32 I + l32, token
@@ -684,7 +722,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
       for (int i = 0; i < G::TPR; ++i) {
         const int t = min(t0 + run * G::TPR + i, L - 1);
-        lreg[buf % LB][i] = *reinterpret_cast<const fcv*>(dch + (size_t)t * DK + G::CPT * pq);
+        lreg[buf % LB][i] = *reinterpret_cast<const fcv*>(dch + (size_t)t * DK + ch0);
       }
     }
   };
@@ -777,39 +815,16 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     }
 
     if constexpr (CHN) {
-      // the run totals' exclusive prefix (pre) and suffix (suf) over the
-      // wave's RPW runs, LS lanes apart, by shuffles (a shifted Hillis-Steele
-      // scan: sums only, so log a = -inf stays -inf), then the waves' totals
-      // through LDS
-      constexpr int LS = DK / G::CPT;
-      const int rw = lane / LS;
-      fcv pre = fcv{}, suf = fcv{};
-      if constexpr (G::RPW > 1) {
+      // the run totals' exclusive prefix (off) and suffix (later) over the
+      // group's runs by row shifts (sums only, so log a = -inf stays -inf),
+      // and the group's total from its last run
+      fcv off, tot, later = fcv{};
 #pragma unroll
-        for (int e = 0; e < G::CPT; ++e) {
-          const float up = __shfl_up(accb[e], LS), dn = __shfl_down(accb[e], LS);
-          pre[e] = rw > 0 ? up : 0.0f;
-          suf[e] = rw < G::RPW - 1 ? dn : 0.0f;
-        }
-#pragma unroll
-        for (int d = 1; d < G::RPW - 1; d *= 2) {
-#pragma unroll
-          for (int e = 0; e < G::CPT; ++e) {
-            const float up = __shfl_up(pre[e], d * LS), dn = __shfl_down(suf[e], d * LS);
-            if (rw >= d) pre[e] += up;
-            if (rw + d < G::RPW) suf[e] += dn;
-          }
-        }
+      for (int e = 0; e < G::CPT; ++e) {
+        off[e] = group_excl_prefix<G::R>(accb[e], run);
+        tot[e] = __shfl(off[e] + accb[e], lane | (G::R - 1));
+        if constexpr (XF) later[e] = group_excl_suffix<G::R>(accb[e], run);
       }
-      if (rw == G::RPW - 1) *reinterpret_cast<fcv*>(&sTot[wave][G::CPT * pq]) = pre + accb;
-      lds_barrier();
-      // (wave is uniform: the partial sums loop over it, with no selects)
-      fcv off = pre, tot = fcv{}, later = suf;
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) tot += *reinterpret_cast<const fcv*>(&sTot[w2][G::CPT * pq]);
-      for (int w2 = 0; w2 < wave; ++w2) off += *reinterpret_cast<const fcv*>(&sTot[w2][G::CPT * pq]);
-      if constexpr (XF)
-        for (int w2 = wave + 1; w2 < NW; ++w2) later += *reinterpret_cast<const fcv*>(&sTot[w2][G::CPT * pq]);
       if constexpr (!XF) {
         // the split below puts factors up to 2^{-tot/2} into q and k: a chunk
         // whose log2 decay sums below -kSplitMax in any channel (or is not a
@@ -824,7 +839,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
           for (int i = 0; i < G::TPR; ++i) {
             const fcv b = off + bl[i];
-            const int o = swz<G::WCK>(run * G::TPR + i, G::CPT * pq);
+            const int o = swz<G::WCK>(run * G::TPR + i, ch0);
             float kf[G::CPT], qf[G::CPT];
             lds_bf16_get<G::CPT>(kb + o, kf);
             lds_bf16_get<G::CPT>(qb + o, qf);
@@ -850,8 +865,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
             er[e] = __builtin_amdgcn_exp2f(rr[e]);
             el[e] = __builtin_amdgcn_exp2f(tot[e] - rr[e]);
           }
-          *reinterpret_cast<fcv*>(&sER[G::CPT * pq]) = er;
-          *reinterpret_cast<fcv*>(&sEL[G::CPT * pq]) = el;
+          *reinterpret_cast<fcv*>(&sER[ch0]) = er;
+          *reinterpret_cast<fcv*>(&sEL[ch0]) = el;
         }
       } else {
         // exact form: every factor is 2^(a direct sum of log2 a <= 0).  sf[i]:
@@ -869,7 +884,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
           for (int i = 0; i < G::TPR; ++i) {
             const int t = run * G::TPR + i;
-            const int o = swz<G::WCK>(t, G::CPT * pq);
+            const int o = swz<G::WCK>(t, ch0);
             if (elu) {
               float kf[G::CPT], qf[G::CPT];
               lds_bf16_get<G::CPT>(kb + o, kf);
@@ -882,7 +897,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
               lds_bf16_put<G::CPT>(kb + o, kf);
               lds_bf16_put<G::CPT>(qb + o, qf);
             }
-            *reinterpret_cast<fcv*>(&lat[t * DK + G::CPT * pq]) =
+            *reinterpret_cast<fcv*>(&lat[t * DK + ch0]) =
                 t < nvalid ? lreg[buf % LB][i] * kLog2e : fcv{};
           }
           lds_barrier();
@@ -894,7 +909,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         auto rescale = [&](auto ELU) {
 #pragma unroll
           for (int i = 0; i < G::TPR; ++i) {
-            const int o = swz<G::WCK>(run * G::TPR + i, G::CPT * pq);
+            const int o = swz<G::WCK>(run * G::TPR + i, ch0);
             const fcv ek = sf[i] + later;
             float kf[G::CPT];
             lds_bf16_get<G::CPT>(kb + o, kf);
@@ -923,8 +938,8 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
             er[e] = 1.0f;
             el[e] = __builtin_amdgcn_exp2f(tot[e]);
           }
-          *reinterpret_cast<fcv*>(&sER[G::CPT * pq]) = er;
-          *reinterpret_cast<fcv*>(&sEL[G::CPT * pq]) = el;
+          *reinterpret_cast<fcv*>(&sER[ch0]) = er;
+          *reinterpret_cast<fcv*>(&sEL[ch0]) = el;
         }
       }
       logAc += tot;
@@ -1275,7 +1290,7 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
     dst = a.ws_S + (unit0 + sigma) * DK * DV;
     if constexpr (CHN) {
       if (vt == 0 && run == 0)
-        *reinterpret_cast<fcv*>(&a.ws_logA[(unit0 + sigma) * DK + G::CPT * pq]) = logAc;
+        *reinterpret_cast<fcv*>(&a.ws_logA[(unit0 + sigma) * DK + ch0]) = logAc;
     } else {
       if (vt == 0 && tid == 0) a.ws_logA[unit0 + sigma] = logA;
     }
