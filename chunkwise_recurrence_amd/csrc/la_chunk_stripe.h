@@ -266,18 +266,6 @@ __device__ __forceinline__ void lds_wave_sync() {
 
 enum { kCatNone = 0, kCatHead = 1, kCatToken = 2, kCatChannel = 3 };
 
-// x of the lane D below (row_shr) or above (row_shl) in the same 16-lane row
-// (DPP); a lane with none in its row gets 0.  Every lane must be active.
-template <int D>
-__device__ __forceinline__ float dpp_row_shr(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + D, 0xf, 0xf, false));
-}
-template <int D>
-__device__ __forceinline__ float dpp_row_shl(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + D, 0xf, 0xf, false));
-}
 // Over a group of R lanes (R <= 16 consecutive lanes of a 16-lane row,
 // r = lane % R): the sum of x over the group's lanes below r (prefix) or
 // above r (suffix) -- a Hillis-Steele scan of the group shifted by one lane;

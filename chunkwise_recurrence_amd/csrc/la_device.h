@@ -43,6 +43,19 @@ __device__ __forceinline__ float feature_elu1_accurate(float x) {
   return x > 0.0f ? x + 1.0f : expf(x);
 }
 
+// x of the lane D below (row_shr) or above (row_shl) in the same 16-lane row
+// (DPP); a lane with none in its row gets 0.  Every lane must be active.
+template <int D>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + D, 0xf, 0xf, false));
+}
+template <int D>
+__device__ __forceinline__ float dpp_row_shl(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + D, 0xf, 0xf, false));
+}
+
 // Smallest per-token log decay the kernels work with: ln of the smallest
 // normal fp32 (2^-126).  A decay below it, -inf included, is taken as 2^-126:
 // every factor that contains it is then below the fp32 normal range, as the
@@ -59,6 +72,21 @@ __device__ __forceinline__ float clamp_log_decay(float x) {
 __device__ __forceinline__ float token_log_decay(int kind, float x) {
   if (kind == kDecayLog) return clamp_log_decay(x);
   if (kind == kDecayGate) return clamp_log_decay(-(fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)))));
+  return 0.0f;
+}
+
+// The same from the hardware exp2 / log2 (a few ulp; for the bf16 paths):
+// log1p(y) = ln(u) - ((u - 1) - y) / u with u = 1 + y, the second term
+// undoing the rounding of u (so log1p(y) = y for tiny y).
+__device__ __forceinline__ float token_log_decay_fast(int kind, float x) {
+  if (kind == kDecayLog) return clamp_log_decay(x);
+  if (kind == kDecayGate) {
+    const float y = __builtin_amdgcn_exp2f(-fabsf(x * 1.4426950408889634f));
+    const float u = 1.0f + y;
+    const float l1p = __builtin_amdgcn_logf(u) * 0.6931471805599453f -
+                      ((u - 1.0f) - y) * __builtin_amdgcn_rcpf(u);
+    return clamp_log_decay(-(fmaxf(x, 0.0f) + l1p));
+  }
   return 0.0f;
 }
 
