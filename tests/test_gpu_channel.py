@@ -337,3 +337,41 @@ def test_channel_strong_decay_fp32_and_decode(gpu_lib):
                                        W.DECAY_CHANNEL, _np(ld), ref_S)
         assert oracle.rel_err(_np(o), ro) <= 1e-4
     assert oracle.rel_err(_np(Sd), ref_S) <= 1e-5
+
+
+# (d_k, value tile, key parts, C): every layout of the per-channel prefix scan
+# -- a wave's d_k / waves channels in groups of 4 (or 2) lanes' channels times
+# R runs of a 16-lane row, R = 2 .. 16 -- and both forms of the output pass
+@pytest.mark.parametrize("dk,tile,parts,C", [
+    (128, 128, 2, 64), (128, 128, 1, 64), (128, 64, 2, 64), (128, 64, 1, 32), (128, 32, 2, 32),
+    (64, 128, 2, 64), (64, 128, 1, 32), (64, 64, 1, 64), (64, 32, 2, 64),
+    (32, 32, 1, 64), (32, 64, 1, 32), (32, 128, 1, 64), (32, 128, 1, 128)])
+@pytest.mark.parametrize("strength", ["mild", "strong"])
+def test_channel_scan_layouts(gpu_lib, dk, tile, parts, C, strength):
+    """Each stripe layout's per-channel scan (waves x channel groups x runs),
+    with two segments so the state pass and its composition run too; "strong"
+    puts chunks beyond the split's range in, so the exact pass runs as well."""
+    la = gpu_lib
+    B, H, L, dv = 1, 2, 5 * C + 7, 128
+    c = W.RandomCase(B, H, L, dk, dv, torch.bfloat16, W.PHI_ELU1 if dk == 64 else 0,
+                     W.DECAY_CHANNEL, seed=600 + dk + tile + parts + C, scale=1.0 / np.sqrt(dk),
+                     channel_mean=0.3, with_state=True)
+    q, k, v, decay, S0 = W.random_inputs(c)
+    if strength == "strong":
+        decay = _strong_log_decay("mixed", B, H, L, dk, seed=601)
+        decay[:, 0, C:2 * C] = -9.0
+    print(f"[channel scan layout] dk={dk} tile={tile} parts={parts} C={C} {strength}", flush=True)
+    with la.using_plan(la.KERNEL_STRIPE, tile, 2, parts, 0):
+        got = la.plan(B, H, L, dk, dv, C, decay_kind=W.DECAY_CHANNEL)
+        assert got[:4] == (la.KERNEL_STRIPE, tile, 2, parts), got
+        S = S0.to(DEV).contiguous()
+        out = la.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), C=C, phi=c.phi,
+                           decay_kind=W.DECAY_CHANNEL, decay=decay.to(DEV).contiguous(), state=S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(S).all()
+    ref, ref_s = oracle.recurrent(_np(q), _np(k), _np(v), c.phi, W.DECAY_CHANNEL, _np(decay),
+                                  _np(S0))
+    e = (oracle.rel_err(_np(out), ref), oracle.rel_err(_np(S), ref_s))
+    print(f"[channel scan layout] dk={dk} tile={tile} parts={parts} C={C} {strength}: "
+          f"out/state rel err {e}", flush=True)
+    assert e[0] <= 1e-2 and e[1] <= 1e-2
