@@ -524,27 +524,21 @@ def main():
         "gated": dict(workload="gated_bf16: B=1, H=16, L=65536, d=128, a_t = exp(-softplus(g_t)), "
                                "C=64",
                       **leg_report(gt, gt["w"].B * gt["w"].L, "gated_bf16", gt["plan"])),
-        "normalized": {"workload": "retnet_bf16 shapes, normalised form, phi = elu+1",
-                       "ms_per_call": n["ms"], "tokens_per_s": tokens / (n["ms"] / 1000.0),
-                       "algorithmic_bytes": n["bytes"],
-                       "achieved_GBs": n["bytes"] / (n["ms"] / 1000.0) / 1e9,
-                       "hbm_frac": n["bytes"] / (n["ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS},
-        "gla": {"workload": "gla_bf16: retnet_bf16 shapes, per-channel gate, "
-                            "log a ~ -Exp(mean 0.8) per token, head and key channel",
-                "ms_per_call": g["ms"], "tokens_per_s": tokens / (g["ms"] / 1000.0),
-                "algorithmic_bytes": g["bytes"],
-                "achieved_GBs": g["bytes"] / (g["ms"] / 1000.0) / 1e9,
-                "hbm_frac": g["bytes"] / (g["ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS},
-        "delta": {"workload": "delta_bf16: Gated DeltaNet on the retnet_bf16 shapes, unit keys, "
-                              "beta ~ U(0,1), gate g ~ N(0,1), C = 64",
-                  "ms_per_call": dl["ms"], "tokens_per_s": tokens / (dl["ms"] / 1000.0),
-                  "algorithmic_bytes": dl["bytes"],
-                  "achieved_GBs": dl["bytes"] / (dl["ms"] / 1000.0) / 1e9,
-                  "hbm_frac": dl["bytes"] / (dl["ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS},
+        "normalized": dict(workload="retnet_bf16 shapes, normalised form, phi = elu+1",
+                           **leg_report(n, tokens, "norm_retnet_bf16")),
+        "gla": dict(workload="gla_bf16: retnet_bf16 shapes, per-channel gate, "
+                             "log a ~ -Exp(mean 0.8) per token, head and key channel",
+                    **leg_report(g, tokens, "gla_bf16")),
+        "delta": dict(workload="delta_bf16: Gated DeltaNet on the retnet_bf16 shapes, unit keys, "
+                               "beta ~ U(0,1), gate g ~ N(0,1), C = 64",
+                      **leg_report(dl, tokens, "delta_bf16")),
         "decode": {"workload": "decode_bf16", "N": d["w"].N, "H": d["w"].H, "d": d["w"].dk,
                    "steps": d["steps"], "steps_per_s": 1e6 / d["step_us"],
                    "us_per_step": d["step_us"], "bytes_per_step": d["bytes"],
-                   "achieved_GBs": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS},
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                                "algorithmic_bytes": d["bytes"],
+                                "traffic": profile_value(TRAFFIC_PROFILE, "hbm_bytes_decode_step")}},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(W)
