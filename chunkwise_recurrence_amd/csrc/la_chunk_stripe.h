@@ -41,11 +41,11 @@
 // NORM adds the normalised form (the tutorial's section 2.2, boxed
 // recurrence): z_t = a_t z_{t-1} + phi(k_t) is carried like one more value
 // column of ones and o_t = phi(q_t)^T S_t / phi(q_t)^T z_t.  Per chunk the
-// denominator is e^{b_i} phi(q_i).z_c (one more MFMA per key step with z in
-// the first row of the A operand, computed by the waves of stripe 0) plus the
-// row sums of the masked, decayed scores (taken where the score blocks are
-// made); z itself is updated by the waves of stripe 0 from the K^T operands
-// and token weights of the state update.
+// denominator is e^{b_i} phi(q_i).z_c (v_dot2_f32_bf16 over the inter term's
+// q operand pairs against z rounded to bf16 pairs, each row block on a stripe
+// other than 0) plus the row sums of the masked, decayed scores (taken where
+// the score blocks are made); z itself is updated by the waves of stripe 0
+// from the K^T operands and token weights of the state update.
 //
 // The per-channel decay (CAT kCatChannel; GLA's diagonal gate, the tutorial's
 // section 2.4: S_t = diag(a_t) S_{t-1} + k_t v_t^T with a_t a vector over the
