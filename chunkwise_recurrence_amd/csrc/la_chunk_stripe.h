@@ -823,25 +823,36 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         if (!in_range) sBad = 1;
         const fcv rr = tot * 0.5f;  // r = b_last / 2
         // q~ = phi(q) e^{b - r}, k~ = phi(k) e^{r - b}, in place
+        // (every read of the thread's q, k elements is issued before the
+        // first write back, so the reads' LDS latency overlaps; d = b - r, with
+        // the k factor 2^-d through v_exp_f32's negate modifier)
         auto rescale = [&](auto ELU) {
+          const fcv c0 = off - rr;
+          float kf[G::TPR][G::CPT], qf[G::TPR][G::CPT];
 #pragma unroll
           for (int i = 0; i < G::TPR; ++i) {
-            const fcv b = off + bl[i];
             const int o = swz<G::WCK>(run * G::TPR + i, ch0);
-            float kf[G::CPT], qf[G::CPT];
-            lds_bf16_get<G::CPT>(kb + o, kf);
-            lds_bf16_get<G::CPT>(qb + o, qf);
+            lds_bf16_get<G::CPT>(kb + o, kf[i]);
+            lds_bf16_get<G::CPT>(qb + o, qf[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < G::TPR; ++i) {
+            const fcv d = bl[i] + c0;
 #pragma unroll
             for (int e = 0; e < G::CPT; ++e) {
               if constexpr (decltype(ELU)::value) {
-                kf[e] = feature_elu1(kf[e]);
-                qf[e] = feature_elu1(qf[e]);
+                kf[i][e] = feature_elu1(kf[i][e]);
+                qf[i][e] = feature_elu1(qf[i][e]);
               }
-              kf[e] *= __builtin_amdgcn_exp2f(rr[e] - b[e]);
-              qf[e] *= __builtin_amdgcn_exp2f(b[e] - rr[e]);
+              kf[i][e] *= __builtin_amdgcn_exp2f(-d[e]);
+              qf[i][e] *= __builtin_amdgcn_exp2f(d[e]);
             }
-            lds_bf16_put<G::CPT>(kb + o, kf);
-            lds_bf16_put<G::CPT>(qb + o, qf);
+          }
+#pragma unroll
+          for (int i = 0; i < G::TPR; ++i) {
+            const int o = swz<G::WCK>(run * G::TPR + i, ch0);
+            lds_bf16_put<G::CPT>(kb + o, kf[i]);
+            lds_bf16_put<G::CPT>(qb + o, qf[i]);
           }
         };
         if (elu) rescale(std::true_type{});
@@ -894,27 +905,34 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
         }
         // q^ = phi(q) e^{b}, k^ = phi(k) e^{b_last - b}, in place (the state
         // pass maps k here; the flag is tested once, not per element)
+        // (reads first, as above)
         auto rescale = [&](auto ELU) {
+          float kf[G::TPR][G::CPT], qf[STATE_ONLY ? 1 : G::TPR][G::CPT];
 #pragma unroll
           for (int i = 0; i < G::TPR; ++i) {
             const int o = swz<G::WCK>(run * G::TPR + i, ch0);
+            lds_bf16_get<G::CPT>(kb + o, kf[i]);
+            if constexpr (!STATE_ONLY) lds_bf16_get<G::CPT>(qb + o, qf[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < G::TPR; ++i) {
             const fcv ek = sf[i] + later;
-            float kf[G::CPT];
-            lds_bf16_get<G::CPT>(kb + o, kf);
 #pragma unroll
             for (int e = 0; e < G::CPT; ++e) {
-              if constexpr (STATE_ONLY && decltype(ELU)::value) kf[e] = feature_elu1(kf[e]);
-              kf[e] *= __builtin_amdgcn_exp2f(ek[e]);
+              if constexpr (STATE_ONLY && decltype(ELU)::value) kf[i][e] = feature_elu1(kf[i][e]);
+              kf[i][e] *= __builtin_amdgcn_exp2f(ek[e]);
             }
-            lds_bf16_put<G::CPT>(kb + o, kf);
             if constexpr (!STATE_ONLY) {
               const fcv eb = off + bl[i];
-              float qf[G::CPT];
-              lds_bf16_get<G::CPT>(qb + o, qf);
 #pragma unroll
-              for (int e = 0; e < G::CPT; ++e) qf[e] *= __builtin_amdgcn_exp2f(eb[e]);
-              lds_bf16_put<G::CPT>(qb + o, qf);
+              for (int e = 0; e < G::CPT; ++e) qf[i][e] *= __builtin_amdgcn_exp2f(eb[e]);
             }
+          }
+#pragma unroll
+          for (int i = 0; i < G::TPR; ++i) {
+            const int o = swz<G::WCK>(run * G::TPR + i, ch0);
+            lds_bf16_put<G::CPT>(kb + o, kf[i]);
+            if constexpr (!STATE_ONLY) lds_bf16_put<G::CPT>(qb + o, qf[i]);
           }
         };
         if (STATE_ONLY && elu) rescale(std::true_type{});
