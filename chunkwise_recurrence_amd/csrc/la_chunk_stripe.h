@@ -810,7 +810,13 @@ __global__ __launch_bounds__(64 * NWV * KH) void chunk_stripe_kernel(const Chunk
 #pragma unroll
       for (int e = 0; e < G::CPT; ++e) {
         off[e] = group_excl_prefix<G::R>(accb[e], run);
-        tot[e] = __shfl(off[e] + accb[e], lane | (G::R - 1));
+        // (a group of 16 is a whole row: DPP row_share reads its last lane)
+        if constexpr (G::R == 16)
+          tot[e] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                 0, __builtin_bit_cast(int, off[e] + accb[e]),
+                                                 0x150 + 15, 0xf, 0xf, false));
+        else
+          tot[e] = __shfl(off[e] + accb[e], lane | (G::R - 1));
         if constexpr (XF) later[e] = group_excl_suffix<G::R>(accb[e], run);
       }
       if constexpr (!XF) {
