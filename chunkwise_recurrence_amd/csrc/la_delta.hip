@@ -572,15 +572,21 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   }
   // left factor (T diag(f)) as bf16 high + remainder, row-major [C][CS];
   // T is lower triangular, and its LDS above the diagonal holds other data
+  // (a thread keeps the column pair m, m + 1 in every row it takes, so its
+  // two column factors are formed once; the rows' reads unrolled together)
   auto split = [&](bool with_decay) {
-    for (int idx = tid; idx < C * C / 2; idx += 256) {
-      const int i = idx / (C / 2), m = 2 * (idx % (C / 2));
-      float x0 = m <= i ? sT[i][m] * sbeta[m] : 0.0f;
-      float x1 = m + 1 <= i ? sT[i][m + 1] * sbeta[m + 1] : 0.0f;
-      if (with_decay) {
-        x0 *= ex2(sb[m]);
-        x1 *= ex2(sb[m + 1]);
-      }
+    static_assert((C * C / 2) % 256 == 0 && 256 % (C / 2) == 0, "split: whole rows per pass");
+    const int m = 2 * (tid % (C / 2)), i0 = tid / (C / 2);
+    float f0 = sbeta[m], f1 = sbeta[m + 1];
+    if (with_decay) {
+      f0 *= ex2(sb[m]);
+      f1 *= ex2(sb[m + 1]);
+    }
+#pragma unroll
+    for (int p = 0; p < C * C / 2 / 256; ++p) {
+      const int i = i0 + p * (256 / (C / 2));
+      const float x0 = m <= i ? sT[i][m] * f0 : 0.0f;
+      const float x1 = m + 1 <= i ? sT[i][m + 1] * f1 : 0.0f;
       const uint32_t hi = cvt2(x0, x1);
       const float r0 = x0 - bf16_to_f32(hi & 0xffffu), r1 = x1 - bf16_to_f32(hi >> 16);
       *reinterpret_cast<uint32_t*>(&sTh[i * CS + m]) = hi;
