@@ -392,31 +392,22 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   const uint16_t* kc = static_cast<const uint16_t*>(a.k) + rowk * DK;
   const uint16_t* vc = static_cast<const uint16_t*>(a.v) + rowk * DV;
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-  // query row 16w + l16 as the B operand of the score tiles below, loaded
-  // first so that its latency hides behind the tile loads and G = K K^T
-  // (rows past the sequence re-read its last row, unconditionally, and are
-  // zeroed where the value is used: a load under a condition makes the
-  // compiler wait for it on the spot)
+  // (the query rows past the sequence re-read its last row, unconditionally,
+  // and are zeroed where the value is used: a load under a condition makes
+  // the compiler wait for it on the spot)
   const int iq = 16 * w + l16;
   u32x4 bq[KST];
-  {
-    const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (rowk + min(iq, n - 1)) * DK;
-#pragma unroll
-    for (int s = 0; s < KST; ++s) bq[s] = *reinterpret_cast<const u32x4*>(qr + 32 * s + 8 * g4);
-  }
-  // beta of token t0 + tid and (wave 0) the decay data of token t0 + lane
-  const float rbeta = a.beta[rowk + min(tid, n - 1)];
   const bool tok = a.decay_kind == kDecayLog || a.decay_kind == kDecayGate;
-  float rdec = 0.0f;
-  if (w == 0) {
-    if (tok) rdec = a.decay[rowk + min(lane, n - 1)];
-    else if (a.decay_kind == kDecayHead) rdec = logf(a.decay[h]);
-  }
-  // the K and V tiles: every load issued before the first LDS store, so the
-  // workgroup (which handles one chunk) waits for memory once.  A whole chunk
-  // takes no row checks; the short last chunk of a sequence re-reads its last
-  // row and zeroes the rows past it.  V stays in registers until the LDS
-  // buffer it shares with K is free.
+  float rbeta, rdec = 0.0f;
+  // The loads, in the order their data is needed: the K tile (the first
+  // barrier publishes it), beta and (wave 0) the decay data of token t0 + lane
+  // (stored before that barrier), the query row 16w + l16 as the B operand
+  // of the score tiles (used after it), and the V tile (used last; it stays
+  // in registers until the LDS buffer it shares with K is free).  Every load
+  // is issued before the first LDS store, so the workgroup (one chunk) waits
+  // for memory once, and each wait covers only the loads issued before what
+  // it waits for.  A whole chunk takes no row checks; the short last chunk of
+  // a sequence re-reads its last row and zeroes the rows past it.
   constexpr int PK = C * NCH / 256;   // 16-byte pieces of K per thread
   constexpr int PV = C * 16 / 256;    // ... of V at most (d_v <= 128)
   static_assert(PK >= 1 && C * NCH % 256 == 0, "K tile pieces per thread");
@@ -429,6 +420,16 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
     for (int p = 0; p < PK; ++p) {
       const int idx = tid + 256 * p, row = idx / NCH, ch = idx % NCH;
       xk[p] = *reinterpret_cast<const u32x4*>(kc + (size_t)(whole ? row : min(row, n - 1)) * DK + 8 * ch);
+    }
+    rbeta = a.beta[rowk + min(tid, n - 1)];
+    if (w == 0) {
+      if (tok) rdec = a.decay[rowk + min(lane, n - 1)];
+      else if (a.decay_kind == kDecayHead) rdec = logf(a.decay[h]);
+    }
+    {
+      const uint16_t* qr = static_cast<const uint16_t*>(a.q) + (rowk + min(iq, n - 1)) * DK;
+#pragma unroll
+      for (int s = 0; s < KST; ++s) bq[s] = *reinterpret_cast<const u32x4*>(qr + 32 * s + 8 * g4);
     }
     // (pieces past a narrower V tile repeat its last piece, load and store)
 #pragma unroll
