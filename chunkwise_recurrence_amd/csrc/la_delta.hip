@@ -681,13 +681,9 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // The sequential pass for bf16 inputs on v_mfma_f32_16x16x32_bf16: one
-// workgroup of NG groups of 4 waves per (head, NG x TV value columns), C = 64;
-// group g takes value columns [TV g, TV g + TV) of the workgroup, and the
-// groups share the chunk's q, k, W and P tiles in LDS (one copy per compute
-// unit instead of one per group: those tiles are the same for every value
-// column of a head, and filling LDS with them is what a chunk waits for).
-// Wave w of a group owns the chunk's query rows 16w .. 16w + 15 and the state
-// rows (keys) of 16-row tiles w, w + 4, ...; the state tile lives in its fp32
+// workgroup of 4 waves per (head, TV value columns), C = 64.  Wave w owns
+// the chunk's query rows 16w .. 16w + 15 and the state rows (keys) of 16-row
+// tiles w, w + 4, ...; the state tile lives in its fp32
 // accumulators, with a bf16 copy S^T in LDS (double-buffered by chunk parity)
 // as the B operand of W S and Q S.  Per chunk:
 //   (1) U = U0 - W S for the wave's rows -> U^T and (e^{b_last - b} U)^T in
@@ -706,37 +702,36 @@ __device__ __forceinline__ void wait_vm() {
 // output stores included; its one wait for memory counts instructions.  Rows
 // past a short last chunk are copies of its last row: they meet zero weights
 // in the state update and give outputs that are not stored.
-template <int DK, int TV, int NG>
-__global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaArgs a) {
+template <int DK, int TV>
+__global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a) {
   constexpr int C = 64;
-  constexpr int NT = TV / 16;       // 16-column tiles of a group's value columns
+  constexpr int NT = TV / 16;       // 16-column tiles of the value columns
   constexpr int QS = DK + 8;        // bf16 row stride of S^T
   constexpr int CS = C + 8;         // bf16 row stride of U^T
   constexpr int KST = DK / 32;      // 32-wide k-steps over the keys
   constexpr int NMT = DK / 16;      // 16-row tiles of the state
   constexpr int MTW = (NMT + 3) / 4;
-  constexpr int NWV = 4 * NG;       // waves of the workgroup
+  constexpr int NWV = 4;            // waves of the workgroup
   constexpr int WCQ = DK / 8;       // 16-byte chunks of a q / k / W row
   constexpr int WCP = C / 8;        // ... of a score row
-  constexpr int WCU = TV / 8;       // ... of a group's U0 row
+  constexpr int WCU = TV / 8;       // ... of a U0 row
   constexpr int QB = C * DK * 2, PB = C * C * 2, UB = C * TV * 2;  // tile bytes
   // 1 KB tile copies (64 lanes x 16 bytes) per wave and chunk: equal for every
   // wave, so the wait below can count them
   constexpr int QPER = C * WCQ / 64 / NWV;
   constexpr int PPER = C * WCP / 64 / NWV;
-  // (a group's U0 tile is 2 or 4 KB: its first UBLK waves copy one block each;
+  // (the U0 tile is 2 or 4 KB: the first UBLK waves copy one block each;
   // the wait counts only what a wave issues after its copies)
   constexpr int UBLK = C * WCU / 64;
   constexpr int BPER = C / NWV;     // decay prefixes each wave copies
   static_assert(QPER >= 1 && C * WCQ % (64 * NWV) == 0, "q/k/W copies per wave");
   static_assert(PPER >= 1 && C * WCP % (64 * NWV) == 0, "score copies per wave");
-  static_assert(UBLK >= 1 && UBLK <= 4 && C * WCU % 64 == 0, "U0 copies of a group");
+  static_assert(UBLK >= 1 && UBLK <= 4 && C * WCU % 64 == 0, "U0 tile copies");
   // vector memory instructions of one chunk per wave: copies, then stores
   constexpr int STORES = NT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave of the workgroup
-  const int grp = wg / 4;   // column group
-  const int w = wg % 4;     // wave of the group
+  const int w = wg;
   const int l16 = lane & 15, g4 = lane >> 4;
   // workgroup -> (head, value tile): the tiles of one head get workgroup ids
   // that are equal mod 8, so they run on one XCD and share q, k and W
@@ -747,17 +742,13 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   const int bh = (slot / a.n_v) * 8 + (f & 7);
   if (bh >= a.B * a.H) return;
   const int L = a.L, DV = a.DV;
-  const int dv0 = (vt * NG + grp) * TV;
+  const int dv0 = vt * TV;
   const int nch = (L + C - 1) / C;
 
-  __shared__ __align__(16) char sQ[2][QB], sK[2][QB], sW[2][QB], sP[2][PB];
-  __shared__ __align__(16) char sU0g[2][NG][UB];
+  __shared__ __align__(16) char sQ[2][QB], sK[2][QB], sW[2][QB], sP[2][PB], sU0t[2][UB];
   __shared__ __align__(16) float sb[2][C];
-  __shared__ __align__(16) uint16_t sSTg[NG][2][TV * QS];
-  __shared__ __align__(16) uint16_t sUTg[NG][TV * CS], sUwTg[NG][TV * CS];
-  auto& sST = sSTg[grp];
-  uint16_t* sUT = sUTg[grp];
-  uint16_t* sUwT = sUwTg[grp];
+  __shared__ __align__(16) uint16_t sST[2][TV * QS];
+  __shared__ __align__(16) uint16_t sUT[TV * CS], sUwT[TV * CS];
 
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * L * DK;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
@@ -784,14 +775,8 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   const int urow = (64 * w + lane) / WCU;
   const int uoff = urow * DV + 8 * ((64 * w + lane) % WCU);
   // Copies of chunk c into stage st (rows past the sequence re-read its last
-  // row).  They pass through the compute unit's memory pipeline one 1 KB copy
-  // at a time (about 1100 cycles for a chunk's 68), and the waves of the
-  // second group, which issue behind the first on each SIMD, waited longest.
-  // With two groups, group 0 copies q, k, P and b and group 1 only W and the
-  // U0 tiles (10-11 copies per wave against 5); otherwise every wave copies
-  // an equal share.  The wait at the top of a chunk counts only the stores
-  // each wave issues after its copies, so the shares need not be equal.
-  auto issue_uniform = [&](int c, int st) {
+  // row), an equal share per wave.
+  auto issue = [&](int c, int st) {
     const int t0 = c * C, last = min(C, L - t0) - 1;
     const bool whole = last == C - 1;
     const size_t rq = (size_t)t0 * DK;
@@ -810,54 +795,10 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
     }
     if (w < UBLK) {
       const int off = whole ? uoff : uoff - max(urow - last, 0) * DV;
-      dma16(uh + (size_t)t0 * DV + off, sU0g[st][grp] + 1024 * w);
+      dma16(uh + (size_t)t0 * DV + off, sU0t[st] + 1024 * w);
     }
     if (lane < BPER) dma4(bhp + t0 + min(wg * BPER + lane, last), &sb[st][wg * BPER]);
   };
-  auto issue_roles = [&](int c, int st) {
-    const int t0 = c * C, last = min(C, L - t0) - 1;
-    const size_t rq = (size_t)t0 * DK;
-    constexpr int QB4 = C * WCQ / 64 / 4;  // q/k/W blocks per wave of one group
-    constexpr int PB4 = C * WCP / 64 / 4;
-    if (grp == 0) {
-#pragma unroll
-      for (int i = 0; i < QB4; ++i) {
-        const int q = 64 * (w + 4 * i) + lane;
-        const int r = q / WCQ;
-        const int off = (min(r, last)) * DK + 8 * dswz_src_chunk<WCQ>(q);
-        dma16(qh + rq + off, sQ[st] + 1024 * (w + 4 * i));
-        dma16(kh + rq + off, sK[st] + 1024 * (w + 4 * i));
-      }
-#pragma unroll
-      for (int i = 0; i < PB4; ++i) {
-        const int q = 64 * (w + 4 * i) + lane;
-        const int r = q / WCP;
-        const int off = min(r, last) * C + 8 * dswz_src_chunk<WCP>(q);
-        dma16(ph + (size_t)t0 * C + off, sP[st] + 1024 * (w + 4 * i));
-      }
-      if (w == 0) dma4(bhp + t0 + min(lane, last), &sb[st][0]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < QB4; ++i) {
-        const int q = 64 * (w + 4 * i) + lane;
-        const int r = q / WCQ;
-        const int off = min(r, last) * DK + 8 * dswz_src_chunk<WCQ>(q);
-        dma16(wh + rq + off, sW[st] + 1024 * (w + 4 * i));
-      }
-      // block w % UBLK of group w / UBLK's U0 tile (UBLK = 2 here)
-      const int g2 = w / UBLK, b2 = w % UBLK;
-      const int q = 64 * b2 + lane;
-      const int r = q / WCU;
-      const int off = min(r, last) * DV + 8 * (q % WCU);
-      const uint16_t* uh2 = reinterpret_cast<const uint16_t*>(a.ws_U) + (size_t)bh * L * DV + (vt * NG + g2) * TV;
-      dma16(uh2 + (size_t)t0 * DV + off, sU0g[st][g2] + 1024 * b2);
-    }
-  };
-  auto issue = [&](int c, int st) {
-    if constexpr (NG == 2 && UBLK == 2) issue_roles(c, st);
-    else issue_uniform(c, st);
-  };
-
   // ---- the state: own tiles (mt = w + 4 m, nt), lane rows 16 mt + 4 g4 + r, column 16 nt + l16
   f32x4 accS[MTW][NT];
   auto put_state = [&](int buf) {
@@ -899,7 +840,7 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
     const char* cK = sK[sp];
     const char* cW = sW[sp];
     const char* cP = sP[sp];
-    const uint16_t* sU0 = reinterpret_cast<const uint16_t*>(sU0g[sp][grp]);
+    const uint16_t* sU0 = reinterpret_cast<const uint16_t*>(sU0t[sp]);
     const float* cb = sb[sp];
     const float bL = cb[n - 1];
     const uint16_t* st = sST[sp];
@@ -1006,22 +947,287 @@ __global__ __launch_bounds__(256 * NG) void delta_chunk_mfma_kernel(const DeltaA
   }
 }
 
+// The sequential pass with the waves in two roles, for 8-wave workgroups of
+// 32 value columns (d_k >= 64).  Waves 0-3 own the chunk's query rows
+// 16w .. 16w + 15 over all 32 columns: they form U = U0 - W S with Q S
+// beside it, then O.  Waves 4-7 move the tiles and hold the state: at the
+// top of chunk c they store chunk c + 1's tiles, loaded into registers a
+// chunk earlier, to the other LDS stage and issue the loads of chunk c + 2;
+// after U is published they update their state tiles (key tiles w, w + 4, ..
+// and both 16-column halves).  The U products so never queue behind tile
+// copies in a wave's instruction stream, each W and Q row tile is read from
+// LDS once per chunk instead of once per 16-column half, and a tile load has
+// a whole chunk to land.  Two barriers per chunk, as in the pass above: the
+// top one (tiles stored, the previous chunk done, S^T complete) and the one
+// that publishes U.
+template <int DK>
+__global__ __launch_bounds__(512) void delta_chunk_roles_kernel(const DeltaArgs a) {
+  constexpr int C = 64, TV = 32, NT = 2;
+  constexpr int QS = DK + 8;        // bf16 row stride of S^T
+  constexpr int CS = C + 8;         // bf16 row stride of U^T
+  constexpr int KST = DK / 32;      // 32-wide k-steps over the keys
+  constexpr int NMT = DK / 16;      // 16-row tiles of the state
+  constexpr int MTW = (NMT + 3) / 4;
+  constexpr int WCQ = DK / 8;       // 16-byte chunks of a q / k / W row
+  constexpr int WCP = C / 8;        // ... of a score row
+  constexpr int WCU = TV / 8;       // ... of a U0 row
+  constexpr int QB = C * DK * 2, PB = C * C * 2, UB = C * TV * 2;  // tile bytes
+  // 1 KB copies per copying wave and chunk, of each q / k / W tile, of the
+  // score tile and of the U0 tile
+  constexpr int QPER = C * WCQ / 64 / 4;
+  constexpr int PPER = C * WCP / 64 / 4;
+  constexpr int UPER = C * WCU / 64 / 4;
+  static_assert(DK >= 64 && QPER >= 1 && PPER >= 1 && UPER >= 1, "tile copies per copying wave");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wg = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool copier = wg >= 4;
+  const int w = wg & 3;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  // workgroup -> (head, value tile) as in the pass above
+  const int f = blockIdx.x;
+  const int slot = f >> 3;
+  const int vt = slot % a.n_v;
+  const int bh = (slot / a.n_v) * 8 + (f & 7);
+  if (bh >= a.B * a.H) return;
+  const int L = a.L, DV = a.DV;
+  const int dv0 = vt * TV;
+  const int nch = (L + C - 1) / C;
+
+  __shared__ __align__(16) char sQ[2][QB], sK[2][QB], sW[2][QB], sP[2][PB], sU0[2][UB];
+  __shared__ __align__(16) float sb[2][C];
+  __shared__ __align__(16) uint16_t sST[2][TV * QS];
+  __shared__ __align__(16) uint16_t sUT[TV * CS], sUwT[TV * CS];
+
+  const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * L * DK;
+  const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
+  const uint16_t* wh = reinterpret_cast<const uint16_t*>(a.ws_W) + (size_t)bh * L * DK;
+  const uint16_t* ph = static_cast<const uint16_t*>(a.ws_P) + (size_t)bh * L * C;
+  const uint16_t* uh = reinterpret_cast<const uint16_t*>(a.ws_U) + (size_t)bh * L * DV + dv0;
+  const float* bhp = a.ws_b + (size_t)bh * L;
+  uint16_t* oh = static_cast<uint16_t*>(a.out) + (size_t)bh * L * DV + dv0;
+
+  // Copying wave w's share of chunk c's tiles: 1 KB blocks w, w + 4, .. of
+  // each, loaded into registers (rows past the sequence re-read its last row)
+  // and stored to a tile stage a chunk later, each lane's 16 bytes at
+  // 16 lane.  These waves issue no stores to memory, so the waits for these
+  // loads cover nothing else.
+  u32x4 xw[QPER], xq[QPER], xk[QPER], xu[UPER], xp[PPER];
+  float xb = 0.0f;
+  auto fetch = [&](int c) {
+    const int t0 = c * C, last = min(C, L - t0) - 1;
+    const size_t rq = (size_t)t0 * DK;
+#pragma unroll
+    for (int i = 0; i < QPER; ++i) {
+      const int q = 64 * (w + 4 * i) + lane;
+      const int off = min(q / WCQ, last) * DK + 8 * dswz_src_chunk<WCQ>(q);
+      xw[i] = *reinterpret_cast<const u32x4*>(wh + rq + off);
+      xq[i] = *reinterpret_cast<const u32x4*>(qh + rq + off);
+      xk[i] = *reinterpret_cast<const u32x4*>(kh + rq + off);
+    }
+#pragma unroll
+    for (int i = 0; i < UPER; ++i) {
+      const int q = 64 * (w + 4 * i) + lane;
+      const int off = min(q / WCU, last) * DV + 8 * (q % WCU);
+      xu[i] = *reinterpret_cast<const u32x4*>(uh + (size_t)t0 * DV + off);
+    }
+#pragma unroll
+    for (int i = 0; i < PPER; ++i) {
+      const int q = 64 * (w + 4 * i) + lane;
+      const int off = min(q / WCP, last) * C + 8 * dswz_src_chunk<WCP>(q);
+      xp[i] = *reinterpret_cast<const u32x4*>(ph + (size_t)t0 * C + off);
+    }
+    xb = bhp[t0 + min(lane, last)];
+  };
+  auto stash = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < QPER; ++i) {
+      const int o = 1024 * (w + 4 * i) + 16 * lane;
+      *reinterpret_cast<u32x4*>(sW[st] + o) = xw[i];
+      *reinterpret_cast<u32x4*>(sQ[st] + o) = xq[i];
+      *reinterpret_cast<u32x4*>(sK[st] + o) = xk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < UPER; ++i)
+      *reinterpret_cast<u32x4*>(sU0[st] + 1024 * (w + 4 * i) + 16 * lane) = xu[i];
+#pragma unroll
+    for (int i = 0; i < PPER; ++i)
+      *reinterpret_cast<u32x4*>(sP[st] + 1024 * (w + 4 * i) + 16 * lane) = xp[i];
+    if (w == 0) sb[st][lane] = xb;
+  };
+
+  // ---- the state (copying waves): tiles (mt = w + 4 m, nt), lane rows
+  // 16 mt + 4 g4 + r, column 16 nt + l16
+  f32x4 accS[MTW][NT];
+  auto put_state = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      const int mt = w + 4 * m;
+      if (mt < NMT) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          *reinterpret_cast<uint2*>(&sST[buf][(16 * nt + l16) * QS + 16 * mt + 4 * g4]) =
+              make_uint2(cvt2(accS[m][nt][0], accS[m][nt][1]), cvt2(accS[m][nt][2], accS[m][nt][3]));
+      }
+    }
+  };
+  if (copier) {
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int mt = w + 4 * m, d = 16 * mt + 4 * g4 + r;
+          accS[m][nt][r] = (a.state && mt < NMT)
+                               ? a.state[((size_t)bh * DK + d) * DV + dv0 + 16 * nt + l16]
+                               : 0.0f;
+        }
+    put_state(0);
+    if (nch > 0) {
+      fetch(0);
+      stash(0);
+    }
+    if (nch > 1) fetch(1);
+  }
+
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = c * C, n = min(C, L - t0);
+    const int sp = c & 1;  // tile stage and S^T buffer of this chunk
+    lds_barrier();  // chunk c's tiles stored; the previous chunk is done; S^T[sp] complete
+    const char* cQ = sQ[sp];
+    const char* cK = sK[sp];
+    const char* cW = sW[sp];
+    const char* cP = sP[sp];
+    const uint16_t* cU0 = reinterpret_cast<const uint16_t*>(sU0[sp]);
+    const float* cb = sb[sp];
+    const float bL = cb[n - 1];
+    const uint16_t* st = sST[sp];
+
+    // (1) U = U0 - W S for rows 16w .. 16w + 15 and, sharing the S operand
+    // reads, Q S for the same rows (O formed transposed, as in the pass
+    // above); the copying waves meanwhile issue chunk c + 1's copies
+    f32x4 accO[NT];
+    if (!copier) {
+      f32x4 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accO[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int s = 0; s < KST; ++s) {
+        const u32x4 aw = lds_b128(cW, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
+        const u32x4 aq = lds_b128(cQ, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
+          acc[nt] = mfma16x16x32(aw, bs, acc[nt]);
+          accO[nt] = mfma16x16x32(bs, aq, accO[nt]);
+        }
+      }
+      const int i0 = 16 * w + 4 * g4;
+      float wt[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wt[r] = i0 + r < n ? ex2(bL - cb[i0 + r]) : 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = bf16_to_f32(cU0[(i0 + r) * TV + 16 * nt + l16]) - acc[nt][r];
+        const int o = (16 * nt + l16) * CS + i0;
+        *reinterpret_cast<uint2*>(&sUT[o]) = make_uint2(cvt2(u[0], u[1]), cvt2(u[2], u[3]));
+        *reinterpret_cast<uint2*>(&sUwT[o]) = make_uint2(cvt2(u[0] * wt[0], u[1] * wt[1]),
+                                                         cvt2(u[2] * wt[2], u[3] * wt[3]));
+      }
+    } else {
+      // chunk c + 1 from registers to the other stage (free since the
+      // barrier above), then the loads of chunk c + 2, which so have a whole
+      // chunk to land
+      if (c + 1 < nch) stash(sp ^ 1);
+      if (c + 2 < nch) fetch(c + 2);
+    }
+    lds_barrier();  // U^T and (wU)^T complete
+
+    if (!copier) {
+      // (2a) O = diag(e^b) Q S + P U for rows 16w .. 16w + 15
+      const int io = 16 * w + l16;  // this lane's token
+      const float e = ex2(cb[io]);
+      f32x4 acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = accO[nt] * e;
+      // token k-steps up to the diagonal: rows 16w .. need tokens < 16w + 16
+      for (int s2 = 0; s2 <= w / 2; ++s2) {
+        const u32x4 ap = lds_b128(cP, dswz<WCP>(io, 32 * s2 + 8 * g4));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
+          acc[nt] = mfma16x16x32(bu, ap, acc[nt]);
+        }
+      }
+      if (io < n) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          *reinterpret_cast<uint2*>(oh + (size_t)(t0 + io) * DV + 16 * nt + 4 * g4) =
+              make_uint2(cvt2(acc[nt][0], acc[nt][1]), cvt2(acc[nt][2], acc[nt][3]));
+      }
+    } else {
+      // (2b) S = e^{b_last} S + K^T (e^{b_last - b} U) for the wave's state
+      // tiles, then the new S^T to the other buffer
+      const float eL = ex2(bL);
+#pragma unroll
+      for (int m = 0; m < MTW; ++m) {
+        const int mt = w + 4 * m;
+        if (mt < NMT) {
+          f32x4 acc[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt] = accS[m][nt] * eL;
+#pragma unroll
+          for (int s2 = 0; s2 < C / 32; ++s2) {
+            const u32x4 ak = lds_tr8s<WCQ>(cK, 32 * s2 + 8 * g4, 16 * mt, l16);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUwT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
+              acc[nt] = mfma16x16x32(ak, bu, acc[nt]);
+            }
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) accS[m][nt] = acc[nt];
+        }
+      }
+      put_state(sp ^ 1);
+    }
+  }
+  if (copier && a.state) {
+#pragma unroll
+    for (int m = 0; m < MTW; ++m) {
+      const int mt = w + 4 * m;
+      if (mt < NMT) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            a.state[((size_t)bh * DK + 16 * mt + 4 * g4 + r) * DV + dv0 + 16 * nt + l16] = accS[m][nt][r];
+      }
+    }
+  }
+}
+
 // The sequential MFMA pass: 32 value columns per workgroup; where 4-wave
 // 32-column workgroups would leave fewer than two per compute unit of an
-// MI355X (256 of them), 8-wave workgroups of two 16-column groups instead
-// (d_k >= 64: the tiles then still split evenly over the 512 threads).
+// MI355X (256 of them), 8-wave ones with the waves in two roles instead
+// (d_k >= 64).
 template <int D>
 void launch_chunk_mfma(const DeltaArgs& a, dim3 grid, hipStream_t s) {
   if constexpr (D >= 64) {
     if ((long long)a.B * a.H * a.n_v < 512) {
-      hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16, 2>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((delta_chunk_roles_kernel<D>), grid, dim3(512), 0, s, a);
       return;
     }
   }
   if (a.n_v == a.DV / 16)
-    hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 16>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 32, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((delta_chunk_mfma_kernel<D, 32>), grid, dim3(256), 0, s, a);
 }
 
 template <bool BF16>
