@@ -947,41 +947,94 @@ __global__ __launch_bounds__(256) void delta_chunk_mfma_kernel(const DeltaArgs a
   }
 }
 
-// The sequential pass with the waves in two roles, for 8-wave workgroups of
-// 32 value columns (d_k >= 64).  Waves 0-3 own the chunk's query rows
-// 16w .. 16w + 15 over all 32 columns: they form U = U0 - W S with Q S
-// beside it, then O.  Waves 4-7 move the tiles and hold the state: at the
-// top of chunk c they store chunk c + 1's tiles, loaded into registers a
-// chunk earlier, to the other LDS stage and issue the loads of chunk c + 2;
-// after U is published they update their state tiles (key tiles w, w + 4, ..
-// and both 16-column halves).  The U products so never queue behind tile
-// copies in a wave's instruction stream, each W and Q row tile is read from
-// LDS once per chunk instead of once per 16-column half, and a tile load has
-// a whole chunk to land.  Two barriers per chunk, as in the pass above: the
-// top one (tiles stored, the previous chunk done, S^T complete) and the one
-// that publishes U.
+// The column pass below keeps its state and U as fp32 accumulator tiles and
+// feeds them to the next products as operands after rounding to bf16 alone,
+// with no exchange between lanes.  A 16x16x32 product sums over its 32 k
+// indices in any order both operands agree on, so the keys (of S) and the
+// tokens (of U) are numbered in the order in which two 16x16 accumulator
+// tiles hold their rows: within each 32-wide k-step (s or t), tile 2s + h row
+// 4a + b is index 8a + 4h + b (a, b < 4).  Lane (l16, g4) of a tile pair then
+// holds indices 8 g4 .. 8 g4 + 7 of the k-step, in order, as an operand wants
+// them; the row tiles read from LDS take the same numbering (row l16 of
+// tile 2t + h is token 32t + 8 (l16 / 4) + 4h + l16 % 4).
+__device__ __forceinline__ u32x4 pack_pair(const f32x4& t0, const f32x4& t1) {
+  return u32x4{cvt2(t0[0], t0[1]), cvt2(t0[2], t0[3]), cvt2(t1[0], t1[1]), cvt2(t1[2], t1[3])};
+}
+__device__ __forceinline__ int perm_index(int k0, int h, int l16) {
+  return k0 + 8 * (l16 >> 2) + 4 * h + (l16 & 3);
+}
+// 16-byte-chunk XOR swizzles of bf16 tiles with WC (8 or 16) chunks per row,
+// one per access pattern of that pass (physical chunk = logical chunk ^
+// swizzle(row)), each making the 16 lanes of a quarter-wave hit distinct
+// banks.  Rows: lanes read rows perm_index(.., l16) at one column (the q, W
+// and score tiles).  Cols: lanes (j, m) = (l16 / 4, l16 % 4) read row k0 + j
+// (k0 a multiple of 4) at chunk 4s + m (transpose reads of the k tile).
+template <int WC>
+__device__ __forceinline__ int swz_rows(int row) {
+  static_assert(WC == 8 || WC == 16, "8 or 16 chunks per row");
+  if constexpr (WC == 16) return (row & 3) | ((row >> 1) & 12);
+  else return ((row >> 1) & 1) | ((row >> 2) & 6);
+}
+template <int WC>
+__device__ __forceinline__ int swz_cols(int row) {
+  static_assert(WC == 8 || WC == 16, "8 or 16 chunks per row");
+  if constexpr (WC == 16) return (row & 3) << 2;
+  else return ((row >> 1) & 1) << 2;
+}
+// byte offset of element (row, col); the logical chunk a tile copy's slot q
+// (row q / WC, physical chunk q % WC) holds
+template <int WC, bool ROWS>
+__device__ __forceinline__ int off_sw(int row, int col) {
+  const int sw = ROWS ? swz_rows<WC>(row) : swz_cols<WC>(row);
+  return row * (WC * 16) + (((col >> 3) ^ sw) << 4) + ((col & 7) << 1);
+}
+template <int WC, bool ROWS>
+__device__ __forceinline__ int src_sw(int q) {
+  const int row = q / WC;
+  return (q % WC) ^ (ROWS ? swz_rows<WC>(row) : swz_cols<WC>(row));
+}
+// K^T as the A operand of key tile 2s + h over token step k0 + 8 g4 .. + 7:
+// lane (l16, g4) gets key perm_index(32 s, h, l16) at those 8 tokens
+template <int WC>
+__device__ __forceinline__ u32x4 lds_ktr(const char* base, int k0, int s, int h, int l16) {
+  const int j = l16 >> 2, m = l16 & 3, c = 32 * s + 8 * m + 4 * h;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_sw<WC, false>(k0 + j, c)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_sw<WC, false>(k0 + 4 + j, c)));
+  const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+  return u32x4{x[0], x[1], y[0], y[1]};
+}
+
+// The sequential pass by value columns, for workgroups of 32 value columns
+// (d_k >= 64).  The recurrence never mixes value columns: U = U0 - W S, O and
+// the update of S for columns j need only S's columns j.  Each of waves 0-1
+// so carries the whole chunk-to-chunk chain for its 16 columns in its own
+// registers, with no barrier between U and the state update: its state
+// tiles are fp32 accumulators (keys numbered as above), and the products
+// take the accumulators of S and U as operands.  Waves 2-5 move the tiles:
+// at the top of chunk c they store chunk c + 1's tiles (loaded into
+// registers a chunk earlier) to the other LDS stage and issue chunk c + 2's
+// loads.  One barrier per chunk (tiles stored, the previous chunk's tiles
+// free).
 template <int DK>
-__global__ __launch_bounds__(512) void delta_chunk_roles_kernel(const DeltaArgs a) {
-  constexpr int C = 64, TV = 32, NT = 2;
-  constexpr int QS = DK + 8;        // bf16 row stride of S^T
-  constexpr int CS = C + 8;         // bf16 row stride of U^T
+__global__ __launch_bounds__(384) void delta_chunk_cols_kernel(const DeltaArgs a) {
+  constexpr int C = 64, TV = 32;
   constexpr int KST = DK / 32;      // 32-wide k-steps over the keys
-  constexpr int NMT = DK / 16;      // 16-row tiles of the state
-  constexpr int MTW = (NMT + 3) / 4;
+  constexpr int NMT = DK / 16;      // 16-row key tiles of the state
   constexpr int WCQ = DK / 8;       // 16-byte chunks of a q / k / W row
   constexpr int WCP = C / 8;        // ... of a score row
   constexpr int WCU = TV / 8;       // ... of a U0 row
   constexpr int QB = C * DK * 2, PB = C * C * 2, UB = C * TV * 2;  // tile bytes
-  // 1 KB copies per copying wave and chunk, of each q / k / W tile, of the
+  // 1 KB blocks per copying wave and chunk, of each q / k / W tile, of the
   // score tile and of the U0 tile
   constexpr int QPER = C * WCQ / 64 / 4;
   constexpr int PPER = C * WCP / 64 / 4;
   constexpr int UPER = C * WCU / 64 / 4;
-  static_assert(DK >= 64 && QPER >= 1 && PPER >= 1 && UPER >= 1, "tile copies per copying wave");
+  static_assert(DK == 64 || DK == 128, "d_k of the column pass");
+  static_assert(QPER >= 1 && PPER >= 1 && UPER >= 1, "tile copies per copying wave");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wg = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool copier = wg >= 4;
-  const int w = wg & 3;
+  const bool copier = wg >= 2;
+  const int w = copier ? wg - 2 : wg;  // copying wave, or the compute wave's 16-column half
   const int l16 = lane & 15, g4 = lane >> 4;
   // workgroup -> (head, value tile) as in the pass above
   const int f = blockIdx.x;
@@ -995,8 +1048,6 @@ __global__ __launch_bounds__(512) void delta_chunk_roles_kernel(const DeltaArgs 
 
   __shared__ __align__(16) char sQ[2][QB], sK[2][QB], sW[2][QB], sP[2][PB], sU0[2][UB];
   __shared__ __align__(16) float sb[2][C];
-  __shared__ __align__(16) uint16_t sST[2][TV * QS];
-  __shared__ __align__(16) uint16_t sUT[TV * CS], sUwT[TV * CS];
 
   const uint16_t* qh = static_cast<const uint16_t*>(a.q) + (size_t)bh * L * DK;
   const uint16_t* kh = static_cast<const uint16_t*>(a.k) + (size_t)bh * L * DK;
@@ -1004,96 +1055,86 @@ __global__ __launch_bounds__(512) void delta_chunk_roles_kernel(const DeltaArgs 
   const uint16_t* ph = static_cast<const uint16_t*>(a.ws_P) + (size_t)bh * L * C;
   const uint16_t* uh = reinterpret_cast<const uint16_t*>(a.ws_U) + (size_t)bh * L * DV + dv0;
   const float* bhp = a.ws_b + (size_t)bh * L;
-  uint16_t* oh = static_cast<uint16_t*>(a.out) + (size_t)bh * L * DV + dv0;
 
-  // Copying wave w's share of chunk c's tiles: 1 KB blocks w, w + 4, .. of
-  // each, loaded into registers (rows past the sequence re-read its last row)
-  // and stored to a tile stage a chunk later, each lane's 16 bytes at
-  // 16 lane.  These waves issue no stores to memory, so the waits for these
-  // loads cover nothing else.
-  u32x4 xw[QPER], xq[QPER], xk[QPER], xu[UPER], xp[PPER];
-  float xb = 0.0f;
-  auto fetch = [&](int c) {
-    const int t0 = c * C, last = min(C, L - t0) - 1;
-    const size_t rq = (size_t)t0 * DK;
-#pragma unroll
-    for (int i = 0; i < QPER; ++i) {
-      const int q = 64 * (w + 4 * i) + lane;
-      const int off = min(q / WCQ, last) * DK + 8 * dswz_src_chunk<WCQ>(q);
-      xw[i] = *reinterpret_cast<const u32x4*>(wh + rq + off);
-      xq[i] = *reinterpret_cast<const u32x4*>(qh + rq + off);
-      xk[i] = *reinterpret_cast<const u32x4*>(kh + rq + off);
-    }
-#pragma unroll
-    for (int i = 0; i < UPER; ++i) {
-      const int q = 64 * (w + 4 * i) + lane;
-      const int off = min(q / WCU, last) * DV + 8 * (q % WCU);
-      xu[i] = *reinterpret_cast<const u32x4*>(uh + (size_t)t0 * DV + off);
-    }
-#pragma unroll
-    for (int i = 0; i < PPER; ++i) {
-      const int q = 64 * (w + 4 * i) + lane;
-      const int off = min(q / WCP, last) * C + 8 * dswz_src_chunk<WCP>(q);
-      xp[i] = *reinterpret_cast<const u32x4*>(ph + (size_t)t0 * C + off);
-    }
-    xb = bhp[t0 + min(lane, last)];
-  };
-  auto stash = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < QPER; ++i) {
-      const int o = 1024 * (w + 4 * i) + 16 * lane;
-      *reinterpret_cast<u32x4*>(sW[st] + o) = xw[i];
-      *reinterpret_cast<u32x4*>(sQ[st] + o) = xq[i];
-      *reinterpret_cast<u32x4*>(sK[st] + o) = xk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < UPER; ++i)
-      *reinterpret_cast<u32x4*>(sU0[st] + 1024 * (w + 4 * i) + 16 * lane) = xu[i];
-#pragma unroll
-    for (int i = 0; i < PPER; ++i)
-      *reinterpret_cast<u32x4*>(sP[st] + 1024 * (w + 4 * i) + 16 * lane) = xp[i];
-    if (w == 0) sb[st][lane] = xb;
-  };
-
-  // ---- the state (copying waves): tiles (mt = w + 4 m, nt), lane rows
-  // 16 mt + 4 g4 + r, column 16 nt + l16
-  f32x4 accS[MTW][NT];
-  auto put_state = [&](int buf) {
-#pragma unroll
-    for (int m = 0; m < MTW; ++m) {
-      const int mt = w + 4 * m;
-      if (mt < NMT) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          *reinterpret_cast<uint2*>(&sST[buf][(16 * nt + l16) * QS + 16 * mt + 4 * g4]) =
-              make_uint2(cvt2(accS[m][nt][0], accS[m][nt][1]), cvt2(accS[m][nt][2], accS[m][nt][3]));
-      }
-    }
-  };
   if (copier) {
+    // copying wave w's share of chunk c's tiles: 1 KB blocks w, w + 4, ..
+    // of each, loaded into registers (rows past the sequence re-read its
+    // last row) and stored to a tile stage a chunk later, each lane's 16
+    // bytes at 16 lane.  These waves issue no stores to memory, so the waits
+    // for these loads cover nothing else.
+    u32x4 xw[QPER], xq[QPER], xk[QPER], xu[UPER], xp[PPER];
+    float xb = 0.0f;
+    auto fetch = [&](int c) {
+      const int t0 = c * C, last = min(C, L - t0) - 1;
+      const size_t rq = (size_t)t0 * DK;
 #pragma unroll
-    for (int m = 0; m < MTW; ++m)
+      for (int i = 0; i < QPER; ++i) {
+        const int q = 64 * (w + 4 * i) + lane;
+        const int row = min(q / WCQ, last) * DK;
+        xw[i] = *reinterpret_cast<const u32x4*>(wh + rq + row + 8 * src_sw<WCQ, true>(q));
+        xq[i] = *reinterpret_cast<const u32x4*>(qh + rq + row + 8 * src_sw<WCQ, true>(q));
+        xk[i] = *reinterpret_cast<const u32x4*>(kh + rq + row + 8 * src_sw<WCQ, false>(q));
+      }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int i = 0; i < UPER; ++i) {
+        const int q = 64 * (w + 4 * i) + lane;
+        const int off = min(q / WCU, last) * DV + 8 * (q % WCU);
+        xu[i] = *reinterpret_cast<const u32x4*>(uh + (size_t)t0 * DV + off);
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int mt = w + 4 * m, d = 16 * mt + 4 * g4 + r;
-          accS[m][nt][r] = (a.state && mt < NMT)
-                               ? a.state[((size_t)bh * DK + d) * DV + dv0 + 16 * nt + l16]
-                               : 0.0f;
-        }
-    put_state(0);
+      for (int i = 0; i < PPER; ++i) {
+        const int q = 64 * (w + 4 * i) + lane;
+        const int off = min(q / WCP, last) * C + 8 * src_sw<WCP, true>(q);
+        xp[i] = *reinterpret_cast<const u32x4*>(ph + (size_t)t0 * C + off);
+      }
+      xb = bhp[t0 + min(lane, last)];
+    };
+    auto stash = [&](int st) {
+#pragma unroll
+      for (int i = 0; i < QPER; ++i) {
+        const int o = 1024 * (w + 4 * i) + 16 * lane;
+        *reinterpret_cast<u32x4*>(sW[st] + o) = xw[i];
+        *reinterpret_cast<u32x4*>(sQ[st] + o) = xq[i];
+        *reinterpret_cast<u32x4*>(sK[st] + o) = xk[i];
+      }
+#pragma unroll
+      for (int i = 0; i < UPER; ++i)
+        *reinterpret_cast<u32x4*>(sU0[st] + 1024 * (w + 4 * i) + 16 * lane) = xu[i];
+#pragma unroll
+      for (int i = 0; i < PPER; ++i)
+        *reinterpret_cast<u32x4*>(sP[st] + 1024 * (w + 4 * i) + 16 * lane) = xp[i];
+      if (w == 0) sb[st][lane] = xb;
+    };
     if (nch > 0) {
       fetch(0);
       stash(0);
     }
     if (nch > 1) fetch(1);
+    for (int c = 0; c < nch; ++c) {
+      lds_barrier();  // chunk c's tiles stored; chunk c - 1's stage is free
+      if (c + 1 < nch) stash((c & 1) ^ 1);
+      if (c + 2 < nch) fetch(c + 2);
+    }
+    return;
   }
+
+  // ---- compute wave w: value column dv0 + 16 w + l16 (the lane's column)
+  const int col = 16 * w + l16;  // within the workgroup's 32
+  // state tile 2s + h: lane rows are keys 32 s + 8 g4 + 4 h + r
+  f32x4 accS[NMT];
+#pragma unroll
+  for (int m = 0; m < NMT; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 32 * (m >> 1) + 8 * g4 + 4 * (m & 1) + r;
+      accS[m][r] = a.state ? a.state[((size_t)bh * DK + key) * DV + dv0 + col] : 0.0f;
+    }
+  uint16_t* oh = static_cast<uint16_t*>(a.out) + (size_t)bh * L * DV + dv0 + 16 * w;
 
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * C, n = min(C, L - t0);
-    const int sp = c & 1;  // tile stage and S^T buffer of this chunk
-    lds_barrier();  // chunk c's tiles stored; the previous chunk is done; S^T[sp] complete
+    const int sp = c & 1;
+    lds_barrier();  // chunk c's tiles stored
     const char* cQ = sQ[sp];
     const char* cK = sK[sp];
     const char* cW = sW[sp];
@@ -1101,126 +1142,149 @@ __global__ __launch_bounds__(512) void delta_chunk_roles_kernel(const DeltaArgs 
     const uint16_t* cU0 = reinterpret_cast<const uint16_t*>(sU0[sp]);
     const float* cb = sb[sp];
     const float bL = cb[n - 1];
-    const uint16_t* st = sST[sp];
 
-    // (1) U = U0 - W S for rows 16w .. 16w + 15 and, sharing the S operand
-    // reads, Q S for the same rows (O formed transposed, as in the pass
-    // above); the copying waves meanwhile issue chunk c + 1's copies
-    f32x4 accO[NT];
-    if (!copier) {
-      f32x4 acc[NT];
+    // The LDS reads are issued in batches ahead of the products that use
+    // them (scheduling barriers keep each batch ahead of the products of the
+    // batch before): with one wave per SIMD nothing else hides their
+    // latency, and left alone the compiler waits for each read right before
+    // its product.
+    // (a) what U, the state's weights and O's scaling need
+    uint32_t u0v[4][4];
+    f32x4 bt[4];
+    float bo[4];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accO[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int tk = 32 * (i >> 1) + 8 * g4 + 4 * (i & 1);  // + r: token of U row r
 #pragma unroll
-      for (int s = 0; s < KST; ++s) {
-        const u32x4 aw = lds_b128(cW, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
-        const u32x4 aq = lds_b128(cQ, dswz<WCQ>(16 * w + l16, 32 * s + 8 * g4));
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const u32x4 bs = *reinterpret_cast<const u32x4*>(&st[(16 * nt + l16) * QS + 32 * s + 8 * g4]);
-          acc[nt] = mfma16x16x32(aw, bs, acc[nt]);
-          accO[nt] = mfma16x16x32(bs, aq, accO[nt]);
-        }
-      }
-      const int i0 = 16 * w + 4 * g4;
-      float wt[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) wt[r] = i0 + r < n ? ex2(bL - cb[i0 + r]) : 0.0f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float u[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = bf16_to_f32(cU0[(i0 + r) * TV + 16 * nt + l16]) - acc[nt][r];
-        const int o = (16 * nt + l16) * CS + i0;
-        *reinterpret_cast<uint2*>(&sUT[o]) = make_uint2(cvt2(u[0], u[1]), cvt2(u[2], u[3]));
-        *reinterpret_cast<uint2*>(&sUwT[o]) = make_uint2(cvt2(u[0] * wt[0], u[1] * wt[1]),
-                                                         cvt2(u[2] * wt[2], u[3] * wt[3]));
-      }
-    } else {
-      // chunk c + 1 from registers to the other stage (free since the
-      // barrier above), then the loads of chunk c + 2, which so have a whole
-      // chunk to land
-      if (c + 1 < nch) stash(sp ^ 1);
-      if (c + 2 < nch) fetch(c + 2);
+      for (int r = 0; r < 4; ++r) u0v[i][r] = cU0[(tk + r) * TV + col];
+      bt[i] = *reinterpret_cast<const f32x4*>(&cb[tk]);
+      bo[i] = cb[perm_index(32 * (i >> 1), i & 1, l16)];
     }
-    lds_barrier();  // U^T and (wU)^T complete
+    // (1) W S for token tiles i (lane rows: tokens perm_index(32 (i / 2),
+    // i % 2, 4 g4 + r), the lane's column) and, sharing the S operand,
+    // (Q S)^T (value columns 4 g4 + r of the wave's 16, token
+    // perm_index(.., l16)), key step s's operands read a step ahead
+    u32x4 aw[2][4], aq[2][4];
+    auto read_wq = [&](int s, int buf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = off_sw<WCQ, true>(perm_index(32 * (i >> 1), i & 1, l16), 32 * s + 8 * g4);
+        aw[buf][i] = *reinterpret_cast<const u32x4*>(cW + o);
+        aq[buf][i] = *reinterpret_cast<const u32x4*>(cQ + o);
+      }
+    };
+    read_wq(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // S as operand over key step s
+    u32x4 bS[KST];
+#pragma unroll
+    for (int s = 0; s < KST; ++s) bS[s] = pack_pair(accS[2 * s], accS[2 * s + 1]);
+    f32x4 accU[4], accO[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      accU[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accO[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // the K^T operands of (2), key tiles m0 .. m0 + NMT/2 - 1
+    constexpr int MH = NMT / 2;
+    u32x4 ak[MH][2], ap[6];
+    auto read_k = [&](int m0) {
+#pragma unroll
+      for (int m = 0; m < MH; ++m)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          ak[m][t] = lds_ktr<WCQ>(cK, 32 * t + 8 * g4, (m0 + m) >> 1, (m0 + m) & 1, l16);
+    };
+#pragma unroll
+    for (int s = 0; s < KST; ++s) {
+      if (s + 1 < KST) read_wq(s + 1, (s + 1) & 1);
+      else read_k(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        accU[i] = mfma16x16x32(aw[s & 1][i], bS[s], accU[i]);
+        accO[i] = mfma16x16x32(bS[s], aq[s & 1][i], accO[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // U = U0 - W S and the state's weights e^{b_last - b} U (zero past the
+    // sequence), as operands over token step t (tiles 2t, 2t + 1)
+    u32x4 bU[2], bwU[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 u[2], uw[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = 2 * t + h, tk = 32 * t + 8 * g4 + 4 * h;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u[h][r] = bf16_to_f32(u0v[i][r]) - accU[i][r];
+          uw[h][r] = tk + r < n ? u[h][r] * ex2(bL - bt[i][r]) : 0.0f;
+        }
+      }
+      bU[t] = pack_pair(u[0], u[1]);
+      bwU[t] = pack_pair(uw[0], uw[1]);
+    }
 
-    if (!copier) {
-      // (2a) O = diag(e^b) Q S + P U for rows 16w .. 16w + 15
-      const int io = 16 * w + l16;  // this lane's token
-      const float e = ex2(cb[io]);
-      f32x4 acc[NT];
+    // (2) S = e^{b_last} S + K^T (e^{b_last - b} U), in two halves of the
+    // key tiles; the second half's operands and the score operands of (3)
+    // are read while the first half's products run
+    const float eL = ex2(bL);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = accO[nt] * e;
-      // token k-steps up to the diagonal: rows 16w .. need tokens < 16w + 16
-      for (int s2 = 0; s2 <= w / 2; ++s2) {
-        const u32x4 ap = lds_b128(cP, dswz<WCP>(io, 32 * s2 + 8 * g4));
+    for (int hf = 0; hf < 2; ++hf) {
+      if (hf == 1) {
+        read_k(MH);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
-          acc[nt] = mfma16x16x32(bu, ap, acc[nt]);
-        }
+        for (int i = 0, x = 0; i < 4; ++i)
+#pragma unroll
+          for (int t = 0; t <= i / 2; ++t, ++x)
+            ap[x] = *reinterpret_cast<const u32x4*>(
+                cP + off_sw<WCP, true>(perm_index(32 * (i >> 1), i & 1, l16), 32 * t + 8 * g4));
       }
-      if (io < n) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          *reinterpret_cast<uint2*>(oh + (size_t)(t0 + io) * DV + 16 * nt + 4 * g4) =
-              make_uint2(cvt2(acc[nt][0], acc[nt][1]), cvt2(acc[nt][2], acc[nt][3]));
+      for (int m = 0; m < MH; ++m) {
+        f32x4 acc = accS[MH * hf + m] * eL;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc = mfma16x16x32(ak[m][t], bwU[t], acc);
+        accS[MH * hf + m] = acc;
       }
-    } else {
-      // (2b) S = e^{b_last} S + K^T (e^{b_last - b} U) for the wave's state
-      // tiles, then the new S^T to the other buffer
-      const float eL = ex2(bL);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // (3) O^T = diag(e^b) (Q S)^T + U^T P^T: token perm_index(.., l16), value
+    // columns 4 g4 .. 4 g4 + 3 of the wave's 16 (one 8-byte store)
 #pragma unroll
-      for (int m = 0; m < MTW; ++m) {
-        const int mt = w + 4 * m;
-        if (mt < NMT) {
-          f32x4 acc[NT];
+    for (int i = 0, x = 0; i < 4; ++i) {
+      const int io = perm_index(32 * (i >> 1), i & 1, l16);
+      f32x4 acc = accO[i] * ex2(bo[i]);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[nt] = accS[m][nt] * eL;
-#pragma unroll
-          for (int s2 = 0; s2 < C / 32; ++s2) {
-            const u32x4 ak = lds_tr8s<WCQ>(cK, 32 * s2 + 8 * g4, 16 * mt, l16);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              const u32x4 bu = *reinterpret_cast<const u32x4*>(&sUwT[(16 * nt + l16) * CS + 32 * s2 + 8 * g4]);
-              acc[nt] = mfma16x16x32(ak, bu, acc[nt]);
-            }
-          }
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) accS[m][nt] = acc[nt];
-        }
-      }
-      put_state(sp ^ 1);
+      for (int t = 0; t <= i / 2; ++t, ++x) acc = mfma16x16x32(bU[t], ap[x], acc);
+      if (io < n)
+        *reinterpret_cast<uint2*>(oh + (size_t)(t0 + io) * DV + 4 * g4) =
+            make_uint2(cvt2(acc[0], acc[1]), cvt2(acc[2], acc[3]));
     }
   }
-  if (copier && a.state) {
+  if (a.state) {
 #pragma unroll
-    for (int m = 0; m < MTW; ++m) {
-      const int mt = w + 4 * m;
-      if (mt < NMT) {
+    for (int m = 0; m < NMT; ++m)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            a.state[((size_t)bh * DK + 16 * mt + 4 * g4 + r) * DV + dv0 + 16 * nt + l16] = accS[m][nt][r];
+      for (int r = 0; r < 4; ++r) {
+        const int key = 32 * (m >> 1) + 8 * g4 + 4 * (m & 1) + r;
+        a.state[((size_t)bh * DK + key) * DV + dv0 + col] = accS[m][r];
       }
-    }
   }
 }
 
 // The sequential MFMA pass: 32 value columns per workgroup; where 4-wave
 // 32-column workgroups would leave fewer than two per compute unit of an
-// MI355X (256 of them), 8-wave ones with the waves in two roles instead
-// (d_k >= 64).
+// MI355X (256 of them), the column pass instead (d_k >= 64: two waves that
+// each carry 16 columns' whole chain, four that move the tiles).
 template <int D>
 void launch_chunk_mfma(const DeltaArgs& a, dim3 grid, hipStream_t s) {
   if constexpr (D >= 64) {
     if ((long long)a.B * a.H * a.n_v < 512) {
-      hipLaunchKernelGGL((delta_chunk_roles_kernel<D>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((delta_chunk_cols_kernel<D>), grid, dim3(384), 0, s, a);
       return;
     }
   }

@@ -164,11 +164,11 @@ def test_delta_workload_whole_output(gpu_lib):
 
 # Each layout of the matrix-core sequential pass: (B, H, d_k, d_v) and the layout
 # the launch picks for it (bf16, 64-token chunks): 32-column tiles in one group
-# once B*H*(d_v/32) >= 512, else 8-wave 32-column workgroups whose waves take
-# two roles (d_k >= 64: products and outputs; tile loads and the state) or one
-# 16-column group (d_k = 32).
+# once B*H*(d_v/32) >= 512, else the column pass (d_k >= 64: 32-column
+# workgroups, two waves each carrying 16 columns' whole chain, four moving the
+# tiles) or one 16-column group (d_k = 32).
 @pytest.mark.parametrize("B,H,dk,dv,layout", [
-    (1, 2, 128, 128, "two roles"), (1, 3, 64, 128, "two roles"),
+    (1, 2, 128, 128, "column pass"), (1, 3, 64, 128, "column pass"),
     (8, 32, 64, 64, "one 32-column group"), (8, 32, 32, 64, "one 32-column group"),
     (1, 3, 32, 64, "one 16-column group"), (2, 2, 32, 32, "one 16-column group")])
 def test_delta_sequential_pass_layouts(gpu_lib, B, H, dk, dv, layout):
