@@ -177,6 +177,18 @@ def test_delta_sequential_pass_layouts(gpu_lib, B, H, dk, dv, layout):
     _run(gpu_lib, c, 64, f"sequential pass, {layout}")
 
 
+@pytest.mark.parametrize("dk,dv,L,with_state", [
+    (128, 128, 1, True), (128, 64, 37, False), (64, 32, 64, True), (128, 64, 65, False),
+    (64, 128, 128, True), (128, 32, 64 * 5 + 63, True)])
+def test_delta_column_pass_lengths(gpu_lib, dk, dv, L, with_state):
+    """The column pass (bf16, d_k >= 64, few heads) at one token, one partial
+    chunk, exactly one and two chunks, one chunk and a token, and a ragged tail;
+    with and without an initial state; 32 to 128 value columns."""
+    c = W.RandomCase(1, 2, L, dk, dv, torch.bfloat16, W.PHI_IDENTITY, W.DECAY_GATE,
+                     seed=900 + dk + dv + L, scale=1.0 / np.sqrt(dk), with_state=with_state)
+    _run(gpu_lib, c, 64, f"column pass L={L}")
+
+
 def test_delta_many_heads_takes_the_32_column_pass(gpu_lib):
     """B*H*(d_v/32) >= 512 keeps 32-column workgroups in the MFMA pass; the
     smaller cases above run the 16-column ones."""
