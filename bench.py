@@ -482,7 +482,7 @@ def main():
     gt = bench_forward_leg(la, torch, W, "gated_bf16", args.steps, args.warmup)
     n = bench_chunk_norm(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
     g = bench_chunk_gla(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
-    dl = bench_delta(la, torch, W, max(args.steps // 10, 1), max(args.warmup // 5, 1))
+    dl = bench_delta(la, torch, W, max(args.steps // 2, 1), max(args.warmup // 2, 1))
     d = bench_decode(la, torch, W, args.decode_steps)
     w = c["w"]
     tokens = w.B * w.L
