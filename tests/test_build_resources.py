@@ -1,10 +1,11 @@
-"""Register budget of the timed output passes (host only: compiles device code
-to assembly with hipcc, runs nothing).
+"""Register budget of the timed chunk loops (host only: compiles device code to
+assembly with hipcc, runs nothing).
 
 A spilled value that the compiler reloads inside a chunk loop comes with a
-`s_waitcnt vmcnt(0)`, which also waits for the next chunk's tile copies in
-flight: the per-channel gate's output pass once lost 6 % that way.  These
-instances must keep every value in registers (no scratch)."""
+`s_waitcnt vmcnt(0)`, which also waits for the next chunk's tile copies or the
+previous chunk's output stores in flight: the per-channel gate's output pass
+once lost 6 % that way.  These instances must keep every value in registers
+(no scratch)."""
 import os
 import re
 import shutil
@@ -18,10 +19,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "chunkwise_recurrence_amd", "csrc")
 
 # (translation unit, mangled-name fragment of the instance): the output passes
-# of the retnet_bf16 (per-head decay) and gla_bf16 (per-channel gate) workloads
+# of the retnet_bf16 (per-head decay) and gla_bf16 (per-channel gate) workloads,
+# and the delta rule's column pass (its compute waves hold 250 registers)
 INSTANCES = [
     ("la_chunk_stripe_dk128_c1", "chunk_stripe_kernelILi128ELi4ELi2ELi64ELi1ELb0ELb0ELb0E"),
     ("la_chunk_stripe_dk128_c3", "chunk_stripe_kernelILi128ELi4ELi2ELi64ELi3ELb0ELb0ELb0E"),
+    ("la_delta", "delta_chunk_cols_kernelILi128EE"),
+    ("la_delta", "delta_chunk_cols_kernelILi64EE"),
 ]
 
 
