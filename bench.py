@@ -99,7 +99,18 @@ def settle(torch, fn):
         torch.cuda.synchronize()
 
 
+def fresh_memory(torch):
+    """Return the blocks earlier legs freed to the device before a leg draws its
+    inputs, so that every leg's buffers come from fresh allocations as in a
+    process of its own: the delta leg ran 5 % slower (0.80 against 0.76 ms) in
+    some runs whose inputs and workspace reused the caching allocator's blocks
+    from the legs before it; the other legs time the same either way."""
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def bench_chunk(la, torch, W, steps, warmup):
+    fresh_memory(torch)
     w = W.WORKLOADS["retnet_bf16"]
     dev = torch.device("cuda:0")
     q, k, v, gamma = W.chunk_inputs(w)
@@ -154,6 +165,7 @@ def bench_forward_leg(la, torch, W, name, steps, warmup, cold=False):
     bracketed by HIP events on the launch stream.  cold: before every call a
     512 MiB buffer is written, so the inputs are not served from the memory-side
     cache (elu_bf16's 100 MB of inputs fit in it)."""
+    fresh_memory(torch)
     w = W.WORKLOADS[name]
     dev = torch.device("cuda:0")
     q, k, v, decay = W.chunk_inputs(w)
@@ -213,6 +225,7 @@ def leg_report(r, tokens, profile_key=None, plan=None):
 def bench_chunk_norm(la, torch, W, steps, warmup):
     """The normalised form (la_chunk_fwd_norm) on the timed workload's shapes,
     with phi = elu + 1 so that every denominator is positive."""
+    fresh_memory(torch)
     w = W.WORKLOADS["retnet_bf16"]
     dev = torch.device("cuda:0")
     q, k, v, gamma = W.chunk_inputs(w)
@@ -248,6 +261,7 @@ def bench_chunk_norm(la, torch, W, steps, warmup):
 def bench_chunk_gla(la, torch, W, steps, warmup):
     """The per-channel (GLA) gate on its workload: la_chunk_fwd with log a
     given per token, head and key channel."""
+    fresh_memory(torch)
     w = W.WORKLOADS["gla_bf16"]
     dev = torch.device("cuda:0")
     q, k, v, log_a = W.chunk_inputs(w)
@@ -279,6 +293,7 @@ def bench_chunk_gla(la, torch, W, steps, warmup):
 
 def bench_delta(la, torch, W, steps, warmup):
     """The delta rule (Gated DeltaNet) on delta_bf16: la_delta_fwd, both passes."""
+    fresh_memory(torch)
     w = W.DELTA
     dev = torch.device("cuda:0")
     q, k, v, beta, g = W.delta_inputs(w)
@@ -310,6 +325,7 @@ def bench_delta(la, torch, W, steps, warmup):
 
 
 def bench_decode(la, torch, W, steps, reps=3):
+    fresh_memory(torch)
     w = W.DECODE
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(w.seed)
