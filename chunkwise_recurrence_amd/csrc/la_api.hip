@@ -520,14 +520,30 @@ la_status la_decode_step_norm(const void* q, const void* k, const void* v, int d
 
 namespace {
 
-// W (fp32-sized; the matrix-core path keeps it in bf16), U0 in fp32, and on
-// the matrix-core path the chunks' bf16 score rows.
-size_t delta_ws_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
+// The delta rule's workspace: W and U0 (bf16 on the matrix-core path, fp32
+// otherwise), then on the matrix-core path the chunks' bf16 score rows and
+// the fp32 in-chunk decay prefix; byte offsets of U0, P and b, and the total.
+struct DeltaWsLayout {
+  size_t u_off = 0, p_off = 0, b_off = 0, bytes = 0;
+};
+DeltaWsLayout delta_ws_layout(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
   const size_t ht = (size_t)B * H * L;
-  size_t by = round256(ht * d_k * sizeof(float)) + round256(ht * d_v * sizeof(float));
-  if (la::delta_uses_mfma(dtype, C, d_k, d_v))
-    by += round256(ht * la::kDeltaMaxC * 2) + round256(ht * sizeof(float));
-  return by;
+  const bool mfma = la::delta_uses_mfma(dtype, C, d_k, d_v);
+  const size_t es = mfma ? 2 : sizeof(float);
+  DeltaWsLayout w;
+  w.u_off = round256(ht * d_k * es);
+  size_t off = w.u_off + round256(ht * d_v * es);
+  if (mfma) {
+    w.p_off = off;
+    off += round256(ht * la::kDeltaMaxC * 2);
+    w.b_off = off;
+    off += round256(ht * sizeof(float));
+  }
+  w.bytes = off;
+  return w;
+}
+size_t delta_ws_bytes(int B, int H, int L, int d_k, int d_v, int C, int dtype) {
+  return delta_ws_layout(B, H, L, d_k, d_v, C, dtype).bytes;
 }
 
 la_status check_delta_shape(int dtype, int B, int H, int L, int d_k, int d_v, int C) {
@@ -572,13 +588,12 @@ la_status la_delta_fwd(const void* q, const void* k, const void* v, const float*
   a.state = state;
   a.decay = decay_kind == LA_DECAY_NONE ? nullptr : decay_data;
   char* ws = static_cast<char*>(workspace);
+  const DeltaWsLayout lay = delta_ws_layout(B, H, L, d_k, d_v, C, dtype);
   a.ws_W = reinterpret_cast<float*>(ws);
-  a.ws_U = reinterpret_cast<float*>(ws + round256((size_t)B * H * L * d_k * sizeof(float)));
+  a.ws_U = reinterpret_cast<float*>(ws + lay.u_off);
   if (la::delta_uses_mfma(dtype, C, d_k, d_v)) {
-    const size_t ht = (size_t)B * H * L;
-    char* p = ws + round256(ht * d_k * sizeof(float)) + round256(ht * d_v * sizeof(float));
-    a.ws_P = p;
-    a.ws_b = reinterpret_cast<float*>(p + round256(ht * la::kDeltaMaxC * 2));
+    a.ws_P = ws + lay.p_off;
+    a.ws_b = reinterpret_cast<float*>(ws + lay.b_off);
   }
   a.B = B;
   a.H = H;

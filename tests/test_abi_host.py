@@ -330,10 +330,10 @@ def test_delta_zero_length_and_workspace_size():
     assert _delta(L=0, q=None, k=None, v=None, beta=None, out=None, ws=None) == OK
     B, H, L, dk, dv = 2, 3, 100, 32, 64
     r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    # W, U0, and on the matrix-core path (bf16, 64-token chunks) the chunks'
-    # bf16 score rows and the fp32 in-chunk decay prefix
+    # W and U0, bf16 on the matrix-core path (bf16, 64-token chunks) with the
+    # chunks' bf16 score rows and the fp32 in-chunk decay prefix, else fp32
     assert la.delta_fwd_workspace_bytes(B, H, L, dk, dv, 64, la.LA_BF16) == \
-        r256(B * H * L * dk * 4) + r256(B * H * L * dv * 4) + r256(B * H * L * 64 * 2) + \
+        r256(B * H * L * dk * 2) + r256(B * H * L * dv * 2) + r256(B * H * L * 64 * 2) + \
         r256(B * H * L * 4)
     assert la.delta_fwd_workspace_bytes(B, H, L, dk, dv, 32, la.LA_BF16) == \
         r256(B * H * L * dk * 4) + r256(B * H * L * dv * 4)
