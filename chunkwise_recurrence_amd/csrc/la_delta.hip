@@ -373,19 +373,17 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   const int t0 = c * C, n = min(C, L - t0);
 
   constexpr int VS = 128 + 8;  // row stride of the V tile (d_v <= 128)
-  // K until W is formed, then V (which waits in registers until then): with
-  // the X blocks of the inverse inside T, the LDS then holds three
-  // workgroups per compute unit instead of two
+  // K until W is formed, then V (which waits in registers until then).  T is
+  // formed in place of N (block row by block row: N's blocks of a row are
+  // dead once that row of T is known), the X blocks of the inverse sit in
+  // the upper triangle, which neither fills, and each wave splits its own
+  // rows of the left factor in registers: 34.5 KB at d_k = 128, four
+  // workgroups per compute unit
   __shared__ __align__(16) uint16_t sKV[C * (QS > VS ? QS : VS)];
   uint16_t* const sK = sKV;
   uint16_t* const sV = sKV;
-  // N (fp32) is dead once T is known; its space then holds the split factor
-  constexpr int NS = CS;  // row stride of N in fp32 words (C + 8)
-  __shared__ __align__(16) float sNT[C * NS];
-  float (*sN)[NS] = reinterpret_cast<float (*)[NS]>(sNT);
-  uint16_t* sTh = reinterpret_cast<uint16_t*>(sNT);
-  uint16_t* sTl = sTh + C * CS;
   __shared__ float sT[C][C + 1];
+  float (*const sN)[C + 1] = sT;
   __shared__ float sb[C], sbeta[C];
 
   const size_t rowk = (size_t)bh * L + t0;
@@ -546,9 +544,11 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
   // v_mfma_f32_16x16x4_f32 (fp32 operands and sums, like the substitution):
   // wave J of block row I forms X = sum_{J <= M < I} N_IM T_MJ, passes it
   // through LDS (its rows become the k-runs of the next B operand) and writes
-  // T_IJ = -T_II X.  Operand lanes: A[l16][g4], B[g4][l16]; result rows
-  // 4 g4 .. 4 g4 + 3 of column l16.  X_J lives in T's block (J, 3), above the
-  // diagonal, which T never fills (its upper triangle is read as zero).
+  // T_IJ = -T_II X over N_IJ, once every wave of the row has read its N
+  // blocks.  Operand lanes: A[l16][g4], B[g4][l16]; result rows
+  // 4 g4 .. 4 g4 + 3 of column l16.  X_J lives in block (J, 3), above the
+  // diagonal, which neither N nor T fills (T's upper triangle is read as
+  // zero).
   for (int I = 1; I < C / 16; ++I) {
     if (w < I) {
       const int J = w;
@@ -561,6 +561,10 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) sT[16 * J + 4 * g4 + r][48 + l16] = x[r];
+    }
+    lds_barrier();  // every N_IM of the row read
+    if (w < I) {
+      const int J = w;
       f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
@@ -571,44 +575,45 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
     }
     lds_barrier();
   }
-  // left factor (T diag(f)) as bf16 high + remainder, row-major [C][CS];
-  // T is lower triangular, and its LDS above the diagonal holds other data
-  // (a thread keeps the column pair m, m + 1 in every row it takes, so its
-  // two column factors are formed once; the rows' reads unrolled together)
-  auto split = [&](bool with_decay) {
-    static_assert((C * C / 2) % 256 == 0 && 256 % (C / 2) == 0, "split: whole rows per pass");
-    const int m = 2 * (tid % (C / 2)), i0 = tid / (C / 2);
-    float f0 = sbeta[m], f1 = sbeta[m + 1];
-    if (with_decay) {
-      f0 *= ex2(sb[m]);
-      f1 *= ex2(sb[m + 1]);
-    }
+  // The lane's row io = 16w + l16 of the left factor T diag(f) as bf16 high
+  // and remainder parts, over token steps s (the B operands of the W and U0
+  // products; T is lower triangular): columns 32s + 8 g4 .. + 7.
+  const int io = 16 * w + l16;  // the row this lane forms and stores
+  auto split_row = [&](bool with_decay, u32x4 (&th)[C / 32], u32x4 (&tl)[C / 32]) {
 #pragma unroll
-    for (int p = 0; p < C * C / 2 / 256; ++p) {
-      const int i = i0 + p * (256 / (C / 2));
-      const float x0 = m <= i ? sT[i][m] * f0 : 0.0f;
-      const float x1 = m + 1 <= i ? sT[i][m + 1] * f1 : 0.0f;
-      const uint32_t hi = cvt2(x0, x1);
-      const float r0 = x0 - bf16_to_f32(hi & 0xffffu), r1 = x1 - bf16_to_f32(hi >> 16);
-      *reinterpret_cast<uint32_t*>(&sTh[i * CS + m]) = hi;
-      *reinterpret_cast<uint32_t*>(&sTl[i * CS + m]) = cvt2(r0, r1);
+    for (int s = 0; s < C / 32; ++s) {
+      uint32_t hp[4], lp[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int m = 32 * s + 8 * g4 + e;
+        float f0 = sbeta[m], f1 = sbeta[m + 1];
+        if (with_decay) {
+          f0 *= ex2(sb[m]);
+          f1 *= ex2(sb[m + 1]);
+        }
+        const float x0 = m <= io ? sT[io][m] * f0 : 0.0f;
+        const float x1 = m + 1 <= io ? sT[io][m + 1] * f1 : 0.0f;
+        const uint32_t hi = cvt2(x0, x1);
+        hp[e / 2] = hi;
+        lp[e / 2] = cvt2(x0 - bf16_to_f32(hi & 0xffffu), x1 - bf16_to_f32(hi >> 16));
+      }
+      th[s] = u32x4{hp[0], hp[1], hp[2], hp[3]};
+      tl[s] = u32x4{lp[0], lp[1], lp[2], lp[3]};
     }
   };
-  split(true);
-  lds_barrier();
+  u32x4 th[C / 32], tl[C / 32];
+  split_row(true, th, tl);
   // W = (T diag(beta e^b)) K: wave w, rows 16w .., every 16-column tile of the
   // keys.  Formed transposed (K^T as the A operand): lane (l16, g4) then holds
   // columns 4 g4 .. 4 g4 + 3 of row 16w + l16, one 8-byte store.
   uint16_t* wo = reinterpret_cast<uint16_t*>(a.ws_W) + rowk * DK;
-  const int io = 16 * w + l16;  // the row this lane stores
   for (int nt = 0; nt < DK / 16; ++nt) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < C / 32; ++s) {
-      const int ao = io * CS + 32 * s + 8 * g4;
       const u32x4 ak = lds_tr8(sK, QS, 32 * s + 8 * g4, 16 * nt, l16);
-      acc = mfma16x16x32(ak, *reinterpret_cast<const u32x4*>(&sTh[ao]), acc);
-      acc = mfma16x16x32(ak, *reinterpret_cast<const u32x4*>(&sTl[ao]), acc);
+      acc = mfma16x16x32(ak, th[s], acc);
+      acc = mfma16x16x32(ak, tl[s], acc);
     }
     if (io < n)
       *reinterpret_cast<uint2*>(wo + (size_t)io * DK + 16 * nt + 4 * g4) =
@@ -620,18 +625,17 @@ __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a)
     const int idx = min(tid + 256 * p, C * VCH - 1), row = idx / VCH, ch = idx % VCH;
     *reinterpret_cast<u32x4*>(&sV[row * VS + 8 * ch]) = (whole_chunk || row < n) ? xv[p] : zero4;
   }
-  split(false);
-  lds_barrier();
+  split_row(false, th, tl);
+  lds_barrier();  // the V tile stored
   // U0 = (T diag(beta)) V, bf16 like W and formed transposed the same way
   uint16_t* uo = reinterpret_cast<uint16_t*>(a.ws_U) + rowk * DV;
   for (int nt = 0; nt < DV / 16; ++nt) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < C / 32; ++s) {
-      const int ao = io * CS + 32 * s + 8 * g4;
       const u32x4 av = lds_tr8(sV, VS, 32 * s + 8 * g4, 16 * nt, l16);
-      acc = mfma16x16x32(av, *reinterpret_cast<const u32x4*>(&sTh[ao]), acc);
-      acc = mfma16x16x32(av, *reinterpret_cast<const u32x4*>(&sTl[ao]), acc);
+      acc = mfma16x16x32(av, th[s], acc);
+      acc = mfma16x16x32(av, tl[s], acc);
     }
     if (io < n)
       *reinterpret_cast<uint2*>(uo + (size_t)io * DV + 16 * nt + 4 * g4) =
