@@ -348,18 +348,19 @@ __global__ __launch_bounds__(256) void delta_chunk_kernel(const DeltaArgs a) {
 // of 4 waves per (head, chunk).
 //   * G = K K^T on v_mfma_f32_16x16x32_bf16 (exact products of the bf16
 //     inputs, fp32 sums), N = diag(beta) (tril(G, -1) o e^{b_i - b_j}) in LDS.
-//   * T = (I + N)^-1: wave w inverts diagonal block w by forward substitution
-//     with its 16 columns in registers (lane j holds column j, no barriers);
-//     the blocks below the diagonal follow block row by block row,
-//     T_IJ = -T_II sum_{J <= M < I} N_IM T_MJ, on fp32 MFMA.
+//   * T = (I + N)^-1, formed in place of N: wave w inverts diagonal block w
+//     by forward substitution with its 16 columns in registers (lane j holds
+//     column j, no barriers); the blocks below the diagonal follow block row
+//     by block row, T_IJ = -T_II sum_{J <= M < I} N_IM T_MJ, on fp32 MFMA.
 //   * W = (T diag(beta e^b)) K and U0 = (T diag(beta)) V on MFMA, with the
 //     fp32 left factor split into a bf16 high part and a bf16 remainder (two
-//     MFMAs, ~16 significant bits); W and U0 leave as bf16.
+//     MFMAs, ~16 significant bits; each wave splits its own rows in
+//     registers); W and U0 leave as bf16.
 //   * the chunk's causal scores (q_i . k_j) e^{b_i - b_j} [j <= i] as bf16
 //     rows, computed here once per head and chunk instead of once per value
 //     tile in the sequential pass, and the in-chunk prefix b itself (fp32,
-//     log2 units): formed in the sequential pass, its gate logarithms and
-//     six-step scan sat on one wave before every chunk's second barrier.
+//     log2 units), whose gate logarithms and scan would otherwise sit on the
+//     sequential pass's chunk-to-chunk chain.
 template <int DK>
 __global__ __launch_bounds__(256) void delta_prep_mfma_kernel(const DeltaArgs a) {
   constexpr int C = 64, QS = DK + 8, CS = C + 8, KST = DK / 32, NCH = DK / 8;
