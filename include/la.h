@@ -220,8 +220,8 @@ const char* la_status_string(int status);
  *   workspace  : device scratch of at least la_delta_fwd_workspace_bytes(),
  *                16-byte aligned, owned by the caller; contents undefined after
  *                (per head-token: 2 (d_k + d_v + 64) + 4 bytes for bf16 inputs
- *                with 64-token chunks and d_v a multiple of 32, 4 (d_k + d_v)
- *                otherwise, each of its regions rounded up to 256 bytes)
+ *                with 64-token chunks, d_k >= 32 and d_v a multiple of 32,
+ *                4 (d_k + d_v) otherwise; each region rounded up to 256 bytes)
  * Shapes, alignment and errors as for la_chunk_fwd (LA_ERR_NULL for a NULL
  * beta, LA_ERR_WORKSPACE for a missing or small workspace).  Asynchronous on
  * `stream`.
